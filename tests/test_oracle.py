@@ -1,0 +1,333 @@
+"""Pins for the oracle (CPU only).
+
+The oracle is the token recurrence (``oracle.recurrence``).  Nothing here compares it with
+itself: every test checks it against a value fixed by hand, a closed form, an independent
+formulation (dense triangular solve; the page's seven chunk stages), a library routine or
+an invariant of the mathematics.  Each is chosen so that a plausible slip (dropped decay,
+wrong sign, transposed state, diagonal in the mask, wrong GQA grouping, wrong chunk
+restart) fails at least one test; the ``planted`` tests show that on mutated copies.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from oracle import chunked as ch
+from oracle import dense_form
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rand_case(seed, B=1, T=37, H=2, Hg=None, Dk=6, Dv=5, h0=True, normalise=True):
+    rng = np.random.default_rng(seed)
+    Hg = Hg or H
+    q = rng.standard_normal((B, T, Hg, Dk))
+    k = rng.standard_normal((B, T, Hg, Dk))
+    if normalise:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, Dv))
+    g = -np.log1p(np.exp(-(rng.standard_normal((B, T, H)) + 3.0)))  # logsigmoid(N(3,1))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))
+    hs = 0.1 * rng.standard_normal((B, H, Dk, Dv)) if h0 else None
+    return q, k, v, g, beta, hs
+
+
+def close(a, b, tol=1e-11):
+    a, b = np.asarray(a), np.asarray(b)
+    scale = max(1.0, float(np.abs(b).max()) if b.size else 1.0)
+    assert a.shape == b.shape
+    err = float(np.abs(a - b).max()) if a.size else 0.0
+    assert err <= tol * scale, "max abs err %g (scale %g)" % (err, scale)
+
+
+# --------------------------------------------------------------------------- hand-worked
+def test_hand_worked_golden():
+    with open(os.path.join(HERE, "golden", "hand_worked.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        T = len(c["g"])
+        q = np.array(c["q"]).reshape(1, T, 1, c["Dk"])
+        k = np.array(c["k"]).reshape(1, T, 1, c["Dk"])
+        v = np.array(c["v"]).reshape(1, T, 1, c["Dv"])
+        g = np.array(c["g"]).reshape(1, T, 1)
+        beta = np.array(c["beta"]).reshape(1, T, 1)
+        h0 = None if c["h0"] is None else np.array(c["h0"]).reshape(1, 1, c["Dk"], c["Dv"])
+        o, ht = oracle.recurrence(q, k, v, g, beta, h0, scale=c["scale"])
+        close(o.reshape(T, c["Dv"]), np.array(c["o"]), 1e-12)
+        close(ht.reshape(c["Dk"], c["Dv"]), np.array(c["ht"]), 1e-12)
+
+
+# --------------------------------------------------------------------------- closed forms
+def test_beta0_g0_keeps_state():
+    """beta = 0, g = 0: the state never changes, ht = h0 and o_t = scale h0^T q_t.
+    Dk != Dv and a non-symmetric h0 pin the state orientation."""
+    q, k, v, g, beta, h0 = rand_case(1, B=2, T=19, H=3, Dk=7, Dv=4)
+    o, ht = oracle.recurrence(q, k, v, 0 * g, 0 * beta, h0, scale=0.3)
+    close(ht, h0)
+    close(o, 0.3 * np.einsum("bhkv,bthk->bthv", h0, q))
+
+
+def test_beta0_pure_decay():
+    """beta = 0: ht = e^{G_T} h0 and o_t = scale e^{G_t} h0^T q_t, G the running sum of g."""
+    q, k, v, g, beta, h0 = rand_case(2, B=1, T=23, H=2, Dk=5, Dv=3)
+    o, ht = oracle.recurrence(q, k, v, g, 0 * beta, h0, scale=0.7)
+    G = np.cumsum(g, axis=1)                                    # [B, T, H]
+    close(ht, np.exp(G[:, -1])[:, :, None, None] * h0)
+    close(o, 0.7 * np.exp(G)[..., None] * np.einsum("bhkv,bthk->bthv", h0, q))
+
+
+def test_delta_rule_overwrites_orthonormal_keys():
+    """beta = 1, g = 0, orthonormal keys: each write replaces the value stored under its key
+    (S k_t = v_t right after token t) and leaves the other keys' values alone, so at the end
+    S k_i = v_i for all i, and o_t = scale v_t when q_t = k_t.  Holds for any h0."""
+    rng = np.random.default_rng(3)
+    Dk, Dv, T = 8, 5, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+    keys = Qm[:, :T].T                                           # T orthonormal rows
+    v = rng.standard_normal((1, T, 1, Dv))
+    h0 = rng.standard_normal((1, 1, Dk, Dv))
+    k = keys.reshape(1, T, 1, Dk)
+    o, ht = oracle.recurrence(k, k, v, np.zeros((1, T, 1)), np.ones((1, T, 1)), h0, scale=1.5)
+    close(o, 1.5 * v)
+    S = ht[0, 0].T                                               # Dv x Dk
+    close(keys @ S.T, v[0, :, 0])
+    # directions orthogonal to every key keep their h0 values
+    rest = Qm[:, T:].T
+    close(rest @ S.T, rest @ h0[0, 0])
+
+
+def test_single_token_from_zero_state():
+    """One token, h0 = 0: S = beta v k^T, so o = scale beta (k . q) v and ht = beta k v^T."""
+    q, k, v, g, beta, _ = rand_case(4, B=1, T=1, H=1, Dk=6, Dv=4, h0=False)
+    o, ht = oracle.recurrence(q, k, v, g, beta, None, scale=0.9)
+    b = beta[0, 0, 0]
+    close(o[0, 0, 0], 0.9 * b * (k[0, 0, 0] @ q[0, 0, 0]) * v[0, 0, 0])
+    close(ht[0, 0], b * np.outer(k[0, 0, 0], v[0, 0, 0]))
+
+
+# ----------------------------------------------------------------- independent formulations
+@pytest.mark.parametrize("T,H,Hg,Dk,Dv,h0", [(1, 1, 1, 4, 4, True), (2, 2, 1, 5, 3, True),
+                                             (17, 4, 2, 6, 6, False), (64, 2, 2, 8, 5, True),
+                                             (200, 2, 1, 16, 16, True)])
+def test_recurrence_equals_dense_solve(T, H, Hg, Dk, Dv, h0):
+    q, k, v, g, beta, hs = rand_case(10 + T, B=2, T=T, H=H, Hg=Hg, Dk=Dk, Dv=Dv, h0=h0)
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs)
+    od, htd = dense_form.dense(q, k, v, g, beta, hs)
+    close(o, od, 1e-10)
+    close(ht, htd, 1e-10)
+
+
+@pytest.mark.parametrize("C", [1, 2, 7, 16, 64, 97])
+def test_chunked_stages_equal_recurrence(C):
+    """The page's seven stages reach the recurrence at every chunk size, including a
+    ragged last chunk (T = 97 is not a multiple of 2, 7, 16 or 64)."""
+    q, k, v, g, beta, hs = rand_case(20 + C, B=2, T=97, H=4, Hg=2, Dk=6, Dv=5)
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs)
+    r = ch.chunked(q, k, v, g, beta, hs, C=C)
+    close(r["o"], o, 1e-10)
+    close(r["ht"], ht, 1e-10)
+
+
+def test_chunked_varlen_equals_recurrence():
+    rng = np.random.default_rng(5)
+    lens = [1, 63, 64, 65, 130, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, g, beta, _ = rand_case(6, B=1, T=int(cu[-1]), H=2, Dk=8, Dv=4, h0=False)
+    hs = 0.1 * rng.standard_normal((len(lens), 2, 8, 4))
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs, cu_seqlens=cu)
+    r = ch.chunked(q, k, v, g, beta, hs, cu_seqlens=cu, C=64)
+    close(r["o"], o, 1e-10)
+    close(r["ht"], ht, 1e-10)
+    # chunks restart at every sequence start
+    assert [(n, s, L) for n, s, L in r["table"]][:4] == [(0, 0, 1), (1, 1, 63), (2, 64, 64),
+                                                         (3, 128, 64)]
+
+
+def test_solve_stage_matches_library_and_inverts():
+    q, k, v, g, beta, hs = rand_case(7, B=1, T=128, H=2, Dk=16, Dv=8)
+    r = ch.chunked(q, k, v, g, beta, hs, C=64)
+    for _, s, L in r["table"]:
+        for h in range(2):
+            A = r["A"][s:s + L, h, :L]
+            assert np.all(np.triu(A) == 0.0)                     # strictly lower
+            Ti = r["Tinv"][s:s + L, h, :L]
+            close(Ti @ (np.eye(L) + A), np.eye(L), 1e-12)
+            ref = scipy.linalg.solve_triangular(np.eye(L) + A, np.eye(L), lower=True,
+                                                unit_diagonal=True)
+            close(Ti, ref, 1e-12)
+
+
+def test_cumsum_stage_matches_numpy_per_chunk():
+    q, k, v, g, beta, hs = rand_case(8, B=1, T=100, H=3, Dk=4, Dv=4)
+    r = ch.chunked(q, k, v, g, beta, hs, C=32)
+    gf = g.reshape(100, 3)
+    for _, s, L in r["table"]:
+        close(r["g_cum"][s:s + L], np.add.accumulate(gf[s:s + L], axis=0), 1e-14)
+    close(r["g_t"], r["g_cum"].T, 0)
+    close(r["beta_t"], beta.reshape(100, 3).T, 0)
+
+
+# --------------------------------------------------------------------------- invariants
+def test_varlen_equals_per_sequence_runs():
+    lens = [5, 70, 1, 33]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, g, beta, _ = rand_case(9, B=1, T=int(cu[-1]), H=2, Dk=6, Dv=4, h0=False)
+    hs = 0.1 * np.random.default_rng(9).standard_normal((4, 2, 6, 4))
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs, cu_seqlens=cu)
+    for n in range(4):
+        sl = slice(cu[n], cu[n + 1])
+        on, hn = oracle.recurrence(q[:, sl], k[:, sl], v[:, sl], g[:, sl], beta[:, sl],
+                                   hs[n:n + 1])
+        close(o[:, sl], on, 1e-14)
+        close(ht[n:n + 1], hn, 1e-14)
+
+
+def test_dense_batch_equals_packed():
+    q, k, v, g, beta, hs = rand_case(11, B=3, T=20, H=2, Dk=5, Dv=5)
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs)
+    flat = lambda x: x.reshape((1, 60) + x.shape[2:])
+    op, htp = oracle.recurrence(flat(q), flat(k), flat(v), flat(g), flat(beta), hs,
+                                cu_seqlens=[0, 20, 40, 60])
+    close(flat(o), op, 0)
+    close(ht, htp, 0)
+
+
+def test_gqa_equals_repeated_heads():
+    """Value head h reads q/k head h // (H / Hg) (contiguous groups, MegaGDN-PTO page
+    section 5.2) — a GQA run equals a plain run with q, k repeated along heads."""
+    q, k, v, g, beta, hs = rand_case(12, B=2, T=30, H=6, Hg=2, Dk=4, Dv=3)
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs)
+    rep = lambda x: np.repeat(x, 3, axis=2)
+    o2, ht2 = oracle.recurrence(rep(q), rep(k), v, g, beta, hs)
+    close(o, o2, 0)
+    close(ht, ht2, 0)
+
+
+def test_continuation_through_final_state():
+    """Feeding the final state of a prefix as h0 of the suffix equals one run."""
+    q, k, v, g, beta, hs = rand_case(13, B=2, T=50, H=2, Dk=5, Dv=4)
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs)
+    a, b = slice(0, 21), slice(21, 50)
+    o1, h1 = oracle.recurrence(q[:, a], k[:, a], v[:, a], g[:, a], beta[:, a], hs)
+    o2, h2 = oracle.recurrence(q[:, b], k[:, b], v[:, b], g[:, b], beta[:, b], h1)
+    close(np.concatenate([o1, o2], axis=1), o, 1e-14)
+    close(h2, ht, 1e-14)
+
+
+def test_linear_in_values_and_initial_state():
+    q, k, v, g, beta, hs = rand_case(14, B=1, T=40, H=2, Dk=5, Dv=4)
+    _, _, v2, _, _, hs2 = rand_case(15, B=1, T=40, H=2, Dk=5, Dv=4)
+    a = -1.7
+    o1, h1 = oracle.recurrence(q, k, v, g, beta, hs)
+    o2, h2 = oracle.recurrence(q, k, v2, g, beta, hs2)
+    o3, h3 = oracle.recurrence(q, k, v + a * v2, g, beta, hs + a * hs2)
+    close(o3, o1 + a * o2, 1e-12)
+    close(h3, h1 + a * h2, 1e-12)
+
+
+def test_value_columns_are_independent():
+    """Column j of v (and of h0) only reaches o[..., j] and ht[..., j]."""
+    q, k, v, g, beta, hs = rand_case(16, B=1, T=30, H=1, Dk=4, Dv=6)
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs)
+    o2, ht2 = oracle.recurrence(q, k, v[..., 2:4], g, beta, hs[..., 2:4])
+    close(o2, o[..., 2:4], 0)
+    close(ht2, ht[..., 2:4], 0)
+
+
+def test_pairs_subset_matches_full_run():
+    q, k, v, g, beta, hs = rand_case(17, B=2, T=12, H=3, Dk=4, Dv=4)
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs)
+    pairs = [1, 5]
+    os_, hts = oracle.recurrence(q, k, v, g, beta, hs, pairs=pairs)
+    for p in pairs:
+        n, h = divmod(p, 3)
+        close(os_[n, :, h], o[n, :, h], 0)
+        close(hts[n, h], ht[n, h], 0)
+    assert np.all(os_[0, :, 0] == 0)
+
+
+def test_empty_sequence_passes_state_through():
+    """A length-0 sequence writes no output and returns its h0 as the final state."""
+    q, k, v, g, beta, _ = rand_case(18, B=1, T=10, H=1, Dk=4, Dv=4, h0=False)
+    hs = np.random.default_rng(18).standard_normal((3, 1, 4, 4))
+    o, ht = oracle.recurrence(q, k, v, g, beta, hs, cu_seqlens=[0, 4, 4, 10])
+    close(ht[1], hs[1], 0)
+
+
+# --------------------------------------------------------------------- planted mistakes
+def _recurrence_py(q, k, v, g, beta, h0, scale, *, transpose_h0=False, decay_write=False,
+                   sign=-1.0, o_before=False, group_mod=False):
+    """A mutable pure-Python copy of the recurrence, used only to show that the pins above
+    catch each plausible mistake (the real oracle is the C one)."""
+    B, T, Hg, Dk = q.shape
+    H, Dv = v.shape[2], v.shape[3]
+    grp = H // Hg
+    o = np.zeros((B, T, H, Dv))
+    ht = np.zeros((B, H, Dk, Dv))
+    for b in range(B):
+        for h in range(H):
+            hk = h % Hg if group_mod else h // grp
+            S = np.zeros((Dv, Dk)) if h0 is None else (
+                h0[b, h].reshape(Dv, Dk) if transpose_h0 else h0[b, h].T.copy())
+            for t in range(T):
+                kt, qt, vt = k[b, t, hk], q[b, t, hk], v[b, t, h]
+                d, bt = np.exp(g[b, t, h]), beta[b, t, h]
+                if o_before:
+                    o[b, t, h] = scale * S @ qt
+                upd = S + sign * bt * np.outer(S @ kt, kt)
+                S = d * upd + (d if decay_write else 1.0) * bt * np.outer(vt, kt)
+                if not o_before:
+                    o[b, t, h] = scale * S @ qt
+            ht[b, h] = S.T
+    return o, ht
+
+
+@pytest.mark.parametrize("mutation", ["transpose_h0", "decay_write", "sign", "o_before",
+                                      "group_mod"])
+def test_planted_mistakes_are_caught(mutation):
+    q, k, v, g, beta, hs = rand_case(19, B=1, T=24, H=4, Hg=2, Dk=5, Dv=5)
+    kw = {"sign": {"sign": +1.0}}.get(mutation, {mutation: True})
+    # the unmutated copy agrees with the oracle ...
+    o, ht = _recurrence_py(q, k, v, g, beta, hs, 0.5)
+    od, htd = dense_form.dense(q, k, v, g, beta, hs, scale=0.5)
+    close(o, od, 1e-10)
+    close(ht, htd, 1e-10)
+    # ... and each mutation is caught by the independent dense formulation
+    om, htm = _recurrence_py(q, k, v, g, beta, hs, 0.5, **kw)
+    err = max(np.abs(om - od).max(), np.abs(htm - htd).max())
+    assert err > 1e-3, mutation
+
+
+def test_planted_diagonal_in_kkt_mask_is_caught(monkeypatch):
+    """Reading the KKT mask as lower *including* the diagonal breaks agreement with the
+    recurrence, which pins the strictly-lower reading."""
+    q, k, v, g, beta, hs = rand_case(21, B=1, T=64, H=2, Dk=8, Dv=8)
+    o, _ = oracle.recurrence(q, k, v, g, beta, hs)
+    orig = ch.stage_kkt
+
+    def kkt_with_diag(kf, g_t, beta_t, table, H, C):
+        A = orig(kf, g_t, beta_t, table, H, C)
+        for _, s, L in table:
+            for h in range(H):
+                kc = kf[s:s + L, h // (H // kf.shape[1])]
+                A[s:s + L, h, :L] += np.diag(beta_t[h, s:s + L] * np.sum(kc * kc, axis=1))
+        return A
+
+    def solve_general(A, table, H):
+        # the mistaken reading solves with the diagonal of A included (not unit-lower)
+        Tinv = np.zeros_like(A)
+        for _, s, L in table:
+            for h in range(H):
+                M = np.eye(L) + A[s:s + L, h, :L]
+                Tinv[s:s + L, h, :L] = scipy.linalg.solve_triangular(M, np.eye(L), lower=True)
+        return Tinv
+
+    monkeypatch.setattr(ch, "stage_kkt", kkt_with_diag)
+    monkeypatch.setattr(ch, "stage_solve_tril", solve_general)
+    r = ch.chunked(q, k, v, g, beta, hs, C=16)
+    rel = np.linalg.norm(r["o"] - o) / np.linalg.norm(o)
+    assert rel > 0.05
