@@ -1,0 +1,210 @@
+"""Benchmark of the chunked Gated DeltaNet forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload headline] [--variant auto]
+
+One step = one gdn_chunk_fwd call over the whole workload (all stages), inputs already
+resident in HBM.  Prints ONE JSON line: whole-job tokens/s, the roofline of the dominant
+kernel (algorithmic bytes per launch / measured launch time, against MI355X's 8 TB/s), and
+the fp64 oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gdn_inputs  # noqa: E402
+
+METRIC = "GDN chunk-fwd tokens/s at 1 MI355X (16×8192, H=32, D=128, bf16); % roofline"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+F32_PEAK_TFLOPS = 157.3
+
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the fused kernel on the headline workload
+# (KiB per dispatch), and the same counters for a plain copy of known size (calibration):
+# filled in from profiles/ once measured; None until then.
+PMC_TRAFFIC = None
+
+
+def algorithmic_work(inp):
+    """Bytes moved and flops a perfect implementation needs (per call).
+
+    Bytes: q and k once per q/k head, v, g, beta and h0 (if given) read once, o and ht
+    written once.  Flops (triangle-aware, per token and value head):
+    2 (3 C Dk / 2 + 2 C Dv / 2 + 3 Dk Dv) + C^2 / 3 — K K^T and Q K^T (half), T K and T V
+    (half), P v_new (half), W h, K^T v_new and Q h (full), plus the triangular inverse."""
+    q, v = inp["q"], inp["v"]
+    B, T, Hg, Dk = q.shape
+    H, Dv = v.shape[2], v.shape[3]
+    C = inp["C"]
+    el = q.element_size()
+    toks = B * T
+    nseq = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    by = toks * Hg * Dk * el * 2 + toks * H * Dv * el * 2 + toks * H * 4 + \
+        toks * H * inp["beta"].element_size() + nseq * H * Dk * Dv * 4
+    if inp["h0"] is not None:
+        by += nseq * H * Dk * Dv * 4
+    fl = toks * H * (2 * (3 * C * Dk / 2 + 2 * C * Dv / 2 + 3 * Dk * Dv) + C * C / 3)
+    return float(by), float(fl)
+
+
+def cpu_baseline(inp, o_gpu, ht_gpu, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a bounded sample of (sequence, head) pairs of
+    the same workload, scale to whole-job tokens/s, and check the sampled GPU outputs."""
+    import oracle
+    from tests.gdn_testlib import oracle_pairs, rel_l2
+    B, T = inp["q"].shape[:2]
+    H = inp["v"].shape[2]
+    nseq = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    cores = len(os.sched_getaffinity(0))
+    threads = oracle.max_threads(cores)
+    rng = np.random.default_rng(12345)
+    all_pairs = [(n, h) for n in range(nseq) for h in range(H)]
+    order = rng.permutation(len(all_pairs))
+    # calibrate on one pair per thread, then size the sample to the budget
+    t0 = time.perf_counter()
+    first = [all_pairs[i] for i in order[:threads]]
+    oracle_pairs(inp, first, nthreads=threads)
+    t_first = time.perf_counter() - t0
+    n_more = int(max(0, budget_s / max(t_first, 1e-3) - 1)) * threads
+    more = [all_pairs[i] for i in order[threads:threads + n_more]]
+    t0 = time.perf_counter()
+    res = oracle_pairs(inp, first + more, nthreads=threads)
+    t_sample = time.perf_counter() - t0
+    npairs = len(res)
+    # whole-job estimate: the oracle's time scales with (sequence, head) pairs
+    t_job = t_sample * len(all_pairs) / npairs
+    value = B * T / t_job
+    errs_o, errs_h = [], []
+    o64 = None
+    for (n, h), (o_ref, ht_ref) in res.items():
+        from tests.gdn_testlib import pair_slices
+        ts, b, _ = pair_slices(inp, n, h)
+        o64 = o_gpu[b, ts, h].double().cpu().numpy()
+        errs_o.append(rel_l2(o64, o_ref))
+        errs_h.append(rel_l2(ht_gpu[n, h].double().cpu().numpy(), ht_ref))
+    return {
+        "value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": "%d of %d (sequence, head) pairs at full length, fp64 token recurrence "
+                  "(C, OpenMP), %.1f s; scaled by pairs to the whole job" %
+                  (npairs, len(all_pairs), t_sample),
+        "sample_seconds": t_sample,
+        "parity_sampled": {"pairs": npairs, "o_rel_l2_max": max(errs_o),
+                           "ht_rel_l2_max": max(errs_h)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline", choices=sorted(gdn_inputs.WORKLOADS))
+    ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    import gated_deltanet_chunked_02_amd as gdn
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gdn_inputs.WORKLOADS[args.workload]
+    print("[bench] drawing %s on %s" % (w.name, dev), file=sys.stderr, flush=True)
+    inp = gdn_inputs.draw(w, device=dev)
+    q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))
+    h0, cu = inp["h0"], inp["cu_seqlens"]
+    desc = gdn.make_desc(q, v, beta, cu, w.C, args.variant)
+    o = torch.empty_like(v)
+    ht = torch.empty((desc.N, desc.H, desc.Dk, desc.Dv), device=dev, dtype=torch.float32)
+    ws_bytes = gdn.gdn_chunk_fwd_workspace_size(desc)
+    ws = None
+    if ws_bytes:
+        ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
+        desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+    variant = "fused" if ws_bytes == 0 else "staged"
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = gdn.gdn_chunk_fwd(desc, q, k, v, g, beta, h0, cu, inp["scale"], o, ht, stream)
+        if st != 0:
+            raise gdn.GdnError(st, "gdn_chunk_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done; timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = 1e3 * t_wall / args.steps
+    tokens = q.shape[0] * q.shape[1]
+    value = tokens / (ms_per_step * 1e-3)
+
+    by, fl = algorithmic_work(inp)
+    avg_ms = float(np.mean(launch_ms))
+    gbs = by / (avg_ms * 1e-3) / 1e9
+    tfl = fl / (avg_ms * 1e-3) / 1e12
+    peak_tf = F32_PEAK_TFLOPS if q.dtype == torch.float32 else BF16_PEAK_TFLOPS
+    bound = "hbm" if by / HBM_PEAK_GBS >= fl / (peak_tf * 1e3) else "mfma"
+    if variant == "staged":
+        kernel = "staged pipeline (8 launches; per-kernel split in profiles/)"
+    else:
+        kernel = "k_fused<%d,%d>" % (w.Dk, w.C)
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": tfl, "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": tfl / peak_tf}
+    roof["traffic"] = PMC_TRAFFIC
+    roof["kernel"] = kernel
+    roof["launch_ms"] = avg_ms
+    roof["algorithmic_bytes"] = by
+    roof["algorithmic_flops"] = fl
+    roof["mfma_tflops"] = tfl
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, o, ht, args.cpu_budget)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": int(q.shape[0]), "T": int(q.shape[1]),
+                   "H": w.H, "Hg": w.Hg, "Dk": w.Dk, "Dv": w.Dv, "C": w.C,
+                   "variant": variant, "h0": inp["h0"] is not None,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+"""Python binding of libgdn — the chunked Gated DeltaNet forward for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in libgdn's HIP kernels.
+PyTorch supplies device memory and the current stream.  The binding refuses to run when
+the library is missing; there is no fallback.
+
+Low level (same names as the C ABI in include/gdn.h):
+    gdn_chunk_fwd(desc, q, k, v, g, beta, h0, cu_seqlens, scale, o, ht, stream)
+    gdn_chunk_fwd_workspace_size(desc) / gdn_stage_buffer(desc, buf) / gdn_status_string(s)
+High level (the call shape of the FlashQLA how-to, step 5.2):
+    o, ht = chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
+                                   output_final_state=True, cu_seqlens=None, chunk_size=128)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GdnDesc", "GdnError", "load", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size",
+    "gdn_stage_buffer", "gdn_status_string", "gdn_version", "chunk_gated_delta_rule",
+    "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
+          3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_HIP"}
+F32, BF16 = 0, 1
+VARIANTS = {"auto": 0, "staged": 1, "fused": 2}
+BUFFERS = {"chunk_table": 0, "seq_chunks": 1, "g_cum": 2, "g_t": 3, "beta_t": 4, "A": 5,
+           "Tinv": 6, "W": 7, "U": 8, "h_c": 9, "v_new": 10}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__("%s%s (%s)" % (what + ": " if what else "", STATUS.get(status, status),
+                                        gdn_status_string(status) if _lib else "?"))
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("Hg", ctypes.c_int32), ("Dk", ctypes.c_int32),
+                ("Dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32), ("beta_dtype", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("stop_after", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libgdn.so (built by ``gated_deltanet_chunked_02_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libgdn.so not found at %s — build it with "
+                           "`python -m gated_deltanet_chunked_02_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    P, S = ctypes.c_void_p, ctypes.c_size_t
+    lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, P, P, ctypes.c_float,
+                                  P, P, P]
+    lib.gdn_chunk_fwd_workspace_size.restype = S
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(GdnDesc),
+                                                 ctypes.POINTER(ctypes.c_int)]
+    lib.gdn_stage_buffer.restype = ctypes.c_int
+    lib.gdn_stage_buffer.argtypes = [ctypes.POINTER(GdnDesc), ctypes.c_int32,
+                                     ctypes.POINTER(S), ctypes.POINTER(S)]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_version.restype = ctypes.c_int32
+    lib.gdn_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def gdn_status_string(status: int) -> str:
+    return load().gdn_status_string(int(status)).decode()
+
+
+def gdn_version() -> int:
+    return int(load().gdn_version())
+
+
+def gdn_chunk_fwd_workspace_size(desc: GdnDesc) -> int:
+    st = ctypes.c_int(0)
+    n = load().gdn_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(st))
+    if st.value != 0:
+        raise GdnError(st.value, "gdn_chunk_fwd_workspace_size")
+    return int(n)
+
+
+def gdn_stage_buffer(desc: GdnDesc, buf) -> tuple:
+    """(offset, bytes) of intermediate ``buf`` (name or id) inside the staged workspace."""
+    b = BUFFERS[buf] if isinstance(buf, str) else int(buf)
+    off, nb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = load().gdn_stage_buffer(ctypes.byref(desc), b, ctypes.byref(off), ctypes.byref(nb))
+    if st != 0:
+        raise GdnError(st, "gdn_stage_buffer")
+    return int(off.value), int(nb.value)
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def gdn_chunk_fwd(desc: GdnDesc, q, k, v, g, beta, h0, cu_seqlens, scale, o, ht,
+                  stream=None) -> int:
+    """Raw call: tensors (or integer device addresses / None) are passed as pointers.
+    Returns the status code (0 = ok) without raising."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return int(load().gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                    _ptr(beta), _ptr(h0), _ptr(cu_seqlens), float(scale),
+                                    _ptr(o), _ptr(ht), stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("libgdn takes bf16 or fp32 tensors, got %s" % t.dtype)
+
+
+def make_desc(q, v, beta, cu_seqlens=None, chunk_size=128, variant="auto", stop_after=0,
+              N=None) -> GdnDesc:
+    B, T, Hg, Dk = q.shape
+    H, Dv = v.shape[2], v.shape[3]
+    if N is None:
+        N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    return GdnDesc(B=B, T=T, N=N, H=H, Hg=Hg, Dk=Dk, Dv=Dv, chunk=chunk_size,
+                   qkv_dtype=_dtype_code(q), beta_dtype=_dtype_code(beta),
+                   variant=VARIANTS[variant] if isinstance(variant, str) else int(variant),
+                   stop_after=stop_after, workspace=None, workspace_bytes=0)
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
+                           output_final_state=True, cu_seqlens=None, chunk_size=128,
+                           variant="auto", workspace=None, stop_after=0):
+    """Chunked Gated DeltaNet forward on the current CUDA (HIP) stream.
+
+    q, k: [B, T, Hg, Dk]; v: [B, T, H, Dv]; g: [B, T, H] fp32 log-decay; beta: [B, T, H];
+    initial_state: [N, H, Dk, Dv] fp32 or None; cu_seqlens: int32 [N + 1] (B == 1) or None.
+    Returns (o [B, T, H, Dv] in q's dtype, final state [N, H, Dk, Dv] fp32 or None).
+    ``workspace``: optional uint8 device tensor for the staged variant (allocated here when
+    needed and not given).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    g, beta = g.contiguous(), beta.contiguous()
+    if g.dtype != torch.float32:
+        raise TypeError("g must be fp32")
+    if cu_seqlens is not None:
+        cu_seqlens = cu_seqlens.to(torch.int32).contiguous()
+    desc = make_desc(q, v, beta, cu_seqlens, chunk_size, variant, stop_after)
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    if initial_state is not None:
+        initial_state = initial_state.to(torch.float32).contiguous()
+    o = torch.empty_like(v)
+    ht = None
+    if output_final_state:
+        ht = torch.empty((desc.N, desc.H, desc.Dk, desc.Dv), device=q.device,
+                         dtype=torch.float32)
+    ws_bytes = gdn_chunk_fwd_workspace_size(desc)
+    if ws_bytes:
+        if workspace is None or workspace.numel() < ws_bytes:
+            workspace = torch.empty(ws_bytes, device=q.device, dtype=torch.uint8)
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel()
+    st = gdn_chunk_fwd(desc, q, k, v, g, beta, initial_state, cu_seqlens, scale, o, ht)
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_fwd")
+    return o, ht

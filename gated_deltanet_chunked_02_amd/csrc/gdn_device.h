@@ -1,0 +1,200 @@
+// Device-side building blocks shared by the staged and fused kernels (gfx950 / CDNA4).
+//
+// Matrix-core conventions used everywhere (v_mfma_f32_16x16x32_{bf16,f16} and
+// v_mfma_f32_16x16x4_f32, wave64):
+//   * an output tile is 16 x 16 fp32; lane l holds rows 4*(l/16) + i (i = 0..3) of column
+//     l % 16 ("accumulator layout");
+//   * the A operand of a 16 x 16 tile reads, in lane l, row l % 16 and KPL consecutive k
+//     values starting at k0 + KPL*(l/16); the B operand reads column l % 16 the same way.
+//     Operands staged in LDS are therefore stored "k-contiguous": A as [row][k], B as
+//     [col][k] (B transposed);
+//   * since A and B only need to agree on which k each (lane, element) slot carries, an
+//     accumulator tile can be fed back as a B operand whose k runs over the tile's rows:
+//     slot (lane, i < 4) carries k = 16*kb + 4*(l/16) + i of block kb and slot i + 4 the
+//     same row of block kb + 1.  The A operand then reads its two 4-element groups from
+//     LDS at those k.  This keeps state, residuals and new values in registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+template <typename E> __device__ __forceinline__ float to_f32(E x) { return (float)x; }
+template <typename E> __device__ __forceinline__ E from_f32(float x) { return (E)x; }
+
+// Operand traits for the three matrix-core shapes in use.
+template <typename E> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int KPL = 8;   // k values one lane supplies
+  static constexpr int KS = 32;   // k per instruction
+  typedef bf16x8 frag;
+  typedef bf16x4 half;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<f16> {
+  static constexpr int KPL = 8;
+  static constexpr int KS = 32;
+  typedef f16x8 frag;
+  typedef f16x4 half;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KPL = 1;
+  static constexpr int KS = 4;
+  typedef float frag;
+  static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row padding (elements) for k-contiguous LDS operands: 16 bytes, so that the 16 rows
+// a fragment load touches fall in different bank groups.
+template <typename E> constexpr int pad_of() { return 16 / (int)sizeof(E); }
+
+// Standard fragment load from a k-contiguous LDS matrix m[row][k] (leading dim ld).
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::frag frag_ld(const E* m, int ld, int row0, int k0) {
+  const int l = lane_id();
+  const E* p = m + (row0 + (l & 15)) * ld + k0 + Mma<E>::KPL * (l >> 4);
+  if constexpr (Mma<E>::KPL == 8) {
+    return *reinterpret_cast<const typename Mma<E>::frag*>(p);
+  } else {
+    return *p;
+  }
+}
+
+// acc += A[row0.., k] * B[col0.., k] over k in [k0, k1) (k1 - k0 a multiple of KS), both
+// operands k-contiguous in LDS.
+template <typename E>
+__device__ __forceinline__ void mma_lds(f32x4& acc, const E* A, int lda, int arow0,
+                                        const E* B, int ldb, int bcol0, int k0, int k1) {
+  for (int k = k0; k < k1; k += Mma<E>::KS)
+    acc = Mma<E>::mma(frag_ld<E>(A, lda, arow0, k), frag_ld<E>(B, ldb, bcol0, k), acc);
+}
+
+// ---------------------------------------------------------------------------------------
+// Contraction with the B operand taken from accumulator tiles (see the header comment).
+//   acc += sum over kb < nkb of  A[arow0 + r][16*kb + c] * Bt[kb][c][col]
+// where Bt[kb] is an accumulator tile whose rows run over k.  A is k-contiguous in LDS
+// (row-major [row][k], leading dim lda, k offset koff).  If `mask_upper` the A element is
+// taken as zero where its k exceeds its row index (row and k both offset by `diag`):
+// used to read a lower-triangular matrix out of a storage that holds other data above
+// the diagonal.
+template <typename E, int NKB, bool MaskUpper = false>
+__device__ __forceinline__ void mma_accB(f32x4& acc, const E* A, int lda, int arow0, int koff,
+                                         const f32x4* Bt, int nkb, int diag = 0) {
+  const int l = lane_id();
+  const int r = arow0 + (l & 15);
+  const int g4 = 4 * (l >> 4);
+  if constexpr (Mma<E>::KPL == 8) {
+    typedef typename Mma<E>::frag frag;
+    typedef typename Mma<E>::half half;
+#pragma unroll
+    for (int kb = 0; kb < NKB; kb += 2) {
+      if (kb < nkb) {
+        const bool two = (kb + 1 < NKB) && (kb + 1 < nkb);
+        const E* p0 = A + r * lda + koff + 16 * kb + g4;
+        half x0 = *reinterpret_cast<const half*>(p0);
+        half x1 = two ? *reinterpret_cast<const half*>(p0 + 16) : half{0, 0, 0, 0};
+        if constexpr (MaskUpper) {
+          const int row = r - diag;
+          const int k0 = 16 * kb + g4 + koff - diag;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (k0 + i > row) x0[i] = (E)0.f;
+            if (k0 + 16 + i > row) x1[i] = (E)0.f;
+          }
+        }
+        const half b0 = __builtin_convertvector(Bt[kb], half);
+        const half b1 = two ? __builtin_convertvector(Bt[kb + 1], half) : half{0, 0, 0, 0};
+        const frag a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const frag b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = Mma<E>::mma(a, b, acc);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (kb < nkb) {
+        const E* p0 = A + r * lda + koff + 16 * kb + g4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          E x = p0[i];
+          if constexpr (MaskUpper) {
+            if (16 * kb + g4 + i + koff - diag > r - diag) x = (E)0.f;
+          }
+          acc = Mma<E>::mma(x, Bt[kb][i], acc);
+        }
+      }
+    }
+  }
+}
+
+// Inclusive prefix sum across a wave.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const float y = __shfl_up(x, d, kWave);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_int(int x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d, kWave);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+
+// beta is bf16 or fp32 (runtime flag): read element i as fp32.
+__device__ __forceinline__ float load_beta(const void* beta, int f32, long i) {
+  return f32 ? static_cast<const float*>(beta)[i] : (float)static_cast<const bf16*>(beta)[i];
+}
+
+// Sequence span [start, start + len) of sequence n, clamped to [0, Ttot].
+__device__ __forceinline__ void seq_span(const int32_t* cu, int n, int T, int Ttot, int& start,
+                                         int& len) {
+  int s, e;
+  if (cu) {
+    s = cu[n];
+    e = cu[n + 1];
+  } else {
+    s = n * T;
+    e = s + T;
+  }
+  s = min(max(s, 0), Ttot);
+  e = min(max(e, s), Ttot);
+  start = s;
+  len = e - s;
+}
+
+}  // namespace gdn

@@ -1,0 +1,122 @@
+// Blocked inverse of the unit lower-triangular chunk matrix (I + A), A strictly lower:
+// the solve_tril stage of the MegaGDN-PTO page (section 4.4), which inverts the
+// lower-triangular chunk matrix recursively by sub-blocks on the matrix unit.
+//
+// gfx950 design: the 16 x 16 diagonal blocks are inverted in fp32 by forward
+// substitution, one column per lane (VALU); then blocks are merged pairwise
+// (16 -> 32 -> 64 -> C) with   T21 = -T22 (A21 T11)   on the matrix cores, one wave per
+// 16-column slice of T21.  A21 T11 stays in that wave's registers and is fed straight
+// back as the B operand of the second product (see gdn_device.h), so a level needs one
+// barrier.
+//
+// Storage (LDS):
+//   sA  [C][ldA] TS   A's off-diagonal 16 x 16 blocks, row-major (diagonal blocks unused)
+//   sAd [C/16][16][17] f32   A's diagonal blocks
+//   sM  [C][ldM] TS   result: M[i][j] = T[max(i,j)][min(i,j)], i.e. T = (I + A)^-1 below
+//                     and on the diagonal, T^T above it (both operand orientations in one
+//                     buffer; readers mask the half they do not want).
+#pragma once
+
+#include "gdn_device.h"
+
+namespace gdn {
+
+constexpr int kAdLd = 17;  // leading dim of a diagonal block in sAd
+
+template <int NW, int C, typename TS>
+__device__ __forceinline__ void solve_diag_blocks(const float* sAd, TS* sM, int ldM) {
+  const int t = threadIdx.x;
+  if (t < C) {
+    const int b = t >> 4, c = t & 15;
+    const float* Ab = sAd + b * 16 * kAdLd;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s = fmaf(-Ab[i * kAdLd + m], x[m], s);
+      x[i] = s;
+    }
+    const int base = 16 * b;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i >= c) {
+        sM[(base + i) * ldM + base + c] = (TS)x[i];
+        sM[(base + c) * ldM + base + i] = (TS)x[i];
+      }
+    }
+  }
+}
+
+template <int NW, int C, typename TS, int S>
+__device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int ldM) {
+  constexpr int NB = S / 16;                 // 16-blocks per half of a merged pair
+  constexpr int NJOBS = (C / (2 * S)) * NB;  // (pair, 16-column slice) jobs = C / 32
+  constexpr int KS = Mma<TS>::KS;
+  constexpr int KPL = Mma<TS>::KPL;
+  typedef typename Mma<TS>::frag frag;
+  const int w = wave_id(), l = lane_id();
+  for (int job = w; job < NJOBS; job += NW) {
+    const int p = job / NB, J = job % NB;
+    const int o = 2 * S * p;
+    // Y[:, J] = A21 T11[:, J]; T11 is lower, so k starts at the slice's first column.
+    f32x4 y[NB];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) y[kb] = zero4();
+    const int ncol = o + 16 * J + (l & 15);
+    for (int k = o + 16 * J; k < o + S; k += KS) {
+      const int kl = k + KPL * (l >> 4);
+      frag b = frag_ld<TS>(sM, ldM, o + 16 * J, k);  // row ncol of M: T^T above diagonal
+      if constexpr (KPL == 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kl + e < ncol || kl + e >= o + S) b[e] = (TS)0.f;
+      } else {
+        if (kl < ncol || kl >= o + S) b = 0.f;
+      }
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        frag a = frag_ld<TS>(sA, ldA, o + S + 16 * kb, k);
+        if constexpr (KPL == 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (kl + e >= o + S) a[e] = (TS)0.f;
+        } else {
+          if (kl >= o + S) a = 0.f;
+        }
+        y[kb] = Mma<TS>::mma(a, b, y[kb]);
+      }
+    }
+    // T21[I, J] = -sum_{kb <= I} T22[I, kb] Y[kb, J]; T22 is read from M's lower half.
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      f32x4 acc = zero4();
+      mma_accB<TS, NB, true>(acc, sM, ldM, o + S + 16 * I, o + S, y, I + 1, 0);
+      const int R0 = o + S + 16 * I + 4 * (l >> 4);
+      const int Cc = o + 16 * J + (l & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const TS val = (TS)(-acc[e]);
+        sM[(R0 + e) * ldM + Cc] = val;
+        sM[Cc * ldM + R0 + e] = val;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Full solve.  Precondition: sA / sAd written and visible (barrier done).  Ends with a
+// barrier, after which sM holds the result.
+template <int NW, int C, typename TS>
+__device__ __forceinline__ void solve_tril(const TS* sA, int ldA, const float* sAd, TS* sM,
+                                           int ldM) {
+  static_assert(C == 64 || C == 128, "chunk size");
+  static_assert(NW * kWave >= C, "one lane per diagonal-block column");
+  solve_diag_blocks<NW, C, TS>(sAd, sM, ldM);
+  __syncthreads();
+  solve_level<NW, C, TS, 16>(sA, ldA, sM, ldM);
+  solve_level<NW, C, TS, 32>(sA, ldA, sM, ldM);
+  if constexpr (C == 128) solve_level<NW, C, TS, 64>(sA, ldA, sM, ldM);
+}
+
+}  // namespace gdn

@@ -1,0 +1,606 @@
+// The seven chunk stages as separate launches (the staged execution mode of the
+// MegaGDN-PTO page, sections 1.1 and 7.4), written for gfx950.
+//
+//   stage 0  chunk table        cu_seqlens -> (sequence, first token, length, index)
+//   stage 1  chunk_cumsum       G = in-chunk prefix sum of g            (page section 4.1)
+//   stage 2  transpose          [T, H] -> [H, T] for G and beta         (page section 4.5)
+//   stage 3  scaled_dot_kkt     A = beta_i e^{G_i-G_j} k_i.k_j, i > j    (page section 4.2)
+//   stage 4  solve_tril         Tinv = (I + A)^-1                        (page section 4.4)
+//   stage 5  wy_fast            U = Tinv diag(beta) V, W = Tinv diag(beta e^G) K (4.3)
+//   stage 6  chunk_h            per chunk: h_c, v_new = U - W h_c,
+//                               h <- e^{G_last} h + K^T (e^{G_last-G} v_new)
+//                               (chunk_gated_delta_rule_fwd_h, TileLang x xLLM page)
+//   stage 7  chunk_o            o = scale (diag(e^G) Q h_c + (Q K^T * e^{G_i-G_j})_{i>=j} v_new)
+//
+// Every chunk-parallel stage runs one 256-thread workgroup (4 waves) per (chunk, head);
+// chunk_h runs one workgroup per (sequence, head, 64-column slice of the state).  Dense
+// products use the 16x16 matrix-core tiles described in gdn_device.h.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+#include "gdn_solve.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+template <typename T> struct Vec16 { static constexpr int n = 16 / (int)sizeof(T); };
+
+__device__ __forceinline__ int4 load_chunk(const int32_t* table, int c) {
+  return reinterpret_cast<const int4*>(table)[c];
+}
+
+// ------------------------------------------------------------------------- stage 0
+// One workgroup of 1024 threads scans the chunk counts of all sequences (wave scans +
+// a workgroup combine, repeated per 1024 sequences with a running carry).
+__global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* cu, int N, int T, int Ttot,
+                                                      int C, int max_chunks, int32_t* table,
+                                                      int32_t* seq_chunks) {
+  __shared__ int s_part[16];
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  int4* tab = reinterpret_cast<int4*>(table);
+  int carry = 0;
+  for (int base = 0; base < N; base += 1024) {
+    const int n = base + tid;
+    int start = 0, len = 0;
+    if (n < N) seq_span(cu, n, T, Ttot, start, len);
+    const int nc = (len + C - 1) / C;
+    const int incl = wave_incl_scan_int(nc);
+    if (l == kWave - 1) s_part[w] = incl;
+    __syncthreads();
+    int wbase = 0, total = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int x = s_part[i];
+      wbase += (i < w) ? x : 0;
+      total += x;
+    }
+    const int off = carry + wbase + incl - nc;
+    if (n < N) {
+      seq_chunks[n] = min(off, max_chunks);
+      for (int m = 0; m < nc; ++m) {
+        const int idx = off + m;
+        if (idx < max_chunks) tab[idx] = make_int4(n, start + m * C, min(C, len - m * C), m);
+      }
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) seq_chunks[N] = min(carry, max_chunks);
+  for (int i = carry + tid; i < max_chunks; i += 1024) tab[i] = make_int4(0, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------- stage 1
+// One workgroup per chunk.  The chunk's g block [len, H] is contiguous: stage it through
+// LDS (coalesced), scan each head's column with one wave (C/64 tokens per lane), store back.
+template <int C>
+__global__ __launch_bounds__(kThreads) void k_cumsum(const int32_t* table, const float* g,
+                                                     float* g_cum, int H) {
+  const int4 ci = load_chunk(table, blockIdx.x);
+  const int start = ci.y, len = ci.z;
+  if (len == 0) return;
+  constexpr int HB = 64;
+  __shared__ float tile[C][HB + 1];
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  for (int hb = 0; hb < H; hb += HB) {
+    const int nh = min(HB, H - hb);
+    for (int i = tid; i < len * nh; i += kThreads) {
+      const int t = i / nh, j = i - t * nh;
+      tile[t][j] = g[(long)(start + t) * H + hb + j];
+    }
+    __syncthreads();
+    for (int j = w; j < nh; j += kWaves) {
+      if constexpr (C == 128) {
+        const int t0 = 2 * l, t1 = 2 * l + 1;
+        const float a = t0 < len ? tile[t0][j] : 0.f;
+        const float b = t1 < len ? tile[t1][j] : 0.f;
+        const float incl = wave_incl_scan(a + b);
+        if (t0 < len) tile[t0][j] = incl - b;
+        if (t1 < len) tile[t1][j] = incl;
+      } else {
+        const float a = l < len ? tile[l][j] : 0.f;
+        const float incl = wave_incl_scan(a);
+        if (l < len) tile[l][j] = incl;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < len * nh; i += kThreads) {
+      const int t = i / nh, j = i - t * nh;
+      g_cum[(long)(start + t) * H + hb + j] = tile[t][j];
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------- stage 2
+// 64 x 64 tiles through LDS; both the read and the write side are row-contiguous.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_transpose(const T* in, T* out, int rows,
+                                                        int cols) {
+  __shared__ T tile[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += kThreads) {
+    const int r = i >> 6, c = i & 63;
+    if (r0 + r < rows && c0 + c < cols) tile[r][c] = in[(long)(r0 + r) * cols + c0 + c];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += kThreads) {
+    const int c = i >> 6, r = i & 63;
+    if (r0 + r < rows && c0 + c < cols) out[(long)(c0 + c) * rows + r0 + r] = tile[r][c];
+  }
+}
+
+// Copy `rows` rows of D elements (row stride `stride` elements in global memory) into a
+// k-contiguous LDS matrix [C][ld]; rows >= rows_valid are zero.  16-byte pieces.
+template <typename T, int D, int C>
+__device__ __forceinline__ void stage_rows(T* s, int ld, const T* src, long stride,
+                                           int rows_valid) {
+  constexpr int VE = Vec16<T>::n, VPR = D / VE;
+  for (int i = threadIdx.x; i < C * VPR; i += blockDim.x) {
+    const int t = i / VPR, pc = i - t * VPR;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t < rows_valid) val = *reinterpret_cast<const uint4*>(src + t * stride + pc * VE);
+    *reinterpret_cast<uint4*>(s + t * ld + pc * VE) = val;
+  }
+}
+
+// Same source, stored transposed: s[d][t] = scale_t * src[t][d0 + d] for d < W columns.
+template <typename T, int W, int C>
+__device__ __forceinline__ void stage_rows_T(T* s, int ld, const T* src, long stride,
+                                             int rows_valid, const float* scale_t) {
+  constexpr int VE = Vec16<T>::n, VPR = W / VE;
+  for (int i = threadIdx.x; i < C * VPR; i += blockDim.x) {
+    const int t = i / VPR, pc = i - t * VPR;
+    union {
+      uint4 u;
+      T e[VE];
+    } val;
+    val.u = make_uint4(0, 0, 0, 0);
+    if (t < rows_valid) val.u = *reinterpret_cast<const uint4*>(src + t * stride + pc * VE);
+    const float f = scale_t ? scale_t[t] : 1.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) s[(pc * VE + e) * ld + t] = (T)(f * (float)val.e[e]);
+  }
+}
+
+// ------------------------------------------------------------------------- stage 3
+template <typename TI, int D, int C>
+__global__ __launch_bounds__(kThreads) void k_kkt(const int32_t* table, const TI* k,
+                                                  const float* g_t, const void* beta_t,
+                                                  int beta_f32, float* A, int Ttot, int H,
+                                                  int Hg) {
+  const int4 ci = load_chunk(table, blockIdx.x);
+  const int start = ci.y, len = ci.z;
+  if (len == 0) return;
+  const int h = blockIdx.y, hk = h / (H / Hg);
+  constexpr int LD = D + pad_of<TI>();
+  extern __shared__ __align__(16) char smem[];
+  TI* sK = reinterpret_cast<TI*>(smem);
+  float* sG = reinterpret_cast<float*>(smem + C * LD * sizeof(TI));
+  float* sB = sG + C;
+  stage_rows<TI, D, C>(sK, LD, k + ((long)start * Hg + hk) * D, (long)Hg * D, len);
+  for (int t = threadIdx.x; t < C; t += kThreads) {
+    const long gi = (long)h * Ttot + start + t;
+    sG[t] = t < len ? g_t[gi] : 0.f;
+    sB[t] = t < len ? load_beta(beta_t, beta_f32, gi) : 0.f;
+  }
+  __syncthreads();
+  constexpr int NT = C / 16;
+  const int w = wave_id(), l = lane_id();
+  for (int tt = w; tt < NT * NT; tt += kWaves) {
+    const int ti = tt / NT, tj = tt % NT;
+    f32x4 acc = zero4();
+    if (ti >= tj) mma_lds<TI>(acc, sK, LD, ti * 16, sK, LD, tj * 16, 0, D);
+    const int j = tj * 16 + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = ti * 16 + 4 * (l >> 4) + e;
+      if (i < len) {
+        float val = 0.f;
+        if (i > j) val = sB[i] * __expf(sG[i] - sG[j]) * acc[e];
+        A[((long)(start + i) * H + h) * C + j] = val;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- stage 4
+template <typename TI> struct SolveType { typedef f16 type; };
+template <> struct SolveType<float> { typedef float type; };
+
+template <typename TI, int C>
+__global__ __launch_bounds__(kThreads) void k_solve(const int32_t* table, const float* A,
+                                                    TI* Tinv, int H) {
+  const int4 ci = load_chunk(table, blockIdx.x);
+  const int start = ci.y, len = ci.z;
+  if (len == 0) return;
+  const int h = blockIdx.y;
+  typedef typename SolveType<TI>::type TS;
+  constexpr int LD = C + pad_of<TS>();
+  extern __shared__ __align__(16) char smem[];
+  TS* sA = reinterpret_cast<TS*>(smem);
+  TS* sM = sA + C * LD;
+  float* sAd = reinterpret_cast<float*>(sM + C * LD);
+  constexpr int P4 = C / 4;
+  for (int i = threadIdx.x; i < C * P4; i += kThreads) {
+    const int t = i / P4, j0 = (i - t * P4) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < len) v = *reinterpret_cast<const float4*>(A + ((long)(start + t) * H + h) * C + j0);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = j0 + e;
+      if ((t >> 4) == (j >> 4))
+        sAd[(t >> 4) * 16 * kAdLd + (t & 15) * kAdLd + (j & 15)] = vv[e];
+      else
+        sA[t * LD + j] = (TS)vv[e];
+    }
+  }
+  __syncthreads();
+  solve_tril<kWaves, C, TS>(sA, LD, sAd, sM, LD);
+  for (int i = threadIdx.x; i < len * C; i += kThreads) {
+    const int t = i / C, j = i - t * C;
+    Tinv[((long)(start + t) * H + h) * C + j] = (TI)(j <= t ? (float)sM[t * LD + j] : 0.f);
+  }
+}
+
+// ------------------------------------------------------------------------- stage 5
+template <typename TI, int D, int C>
+__global__ __launch_bounds__(kThreads) void k_wy(const int32_t* table, const TI* Tinv,
+                                                 const TI* k, const TI* v, const float* g_t,
+                                                 const void* beta_t, int beta_f32, TI* W,
+                                                 TI* U, int Ttot, int H, int Hg) {
+  const int4 ci = load_chunk(table, blockIdx.x);
+  const int start = ci.y, len = ci.z;
+  if (len == 0) return;
+  const int h = blockIdx.y, hk = h / (H / Hg);
+  constexpr int LD = C + pad_of<TI>();
+  constexpr int PW = 64;  // output columns per panel
+  constexpr int KS = Mma<TI>::KS;
+  extern __shared__ __align__(16) char smem[];
+  TI* sT = reinterpret_cast<TI*>(smem);
+  TI* sP = sT + C * LD;
+  float* sB = reinterpret_cast<float*>(sP + PW * LD);
+  float* sEB = sB + C;
+  stage_rows<TI, C, C>(sT, LD, Tinv + ((long)start * H + h) * C, (long)H * C, len);
+  for (int t = threadIdx.x; t < C; t += kThreads) {
+    const long gi = (long)h * Ttot + start + t;
+    const float b = t < len ? load_beta(beta_t, beta_f32, gi) : 0.f;
+    sB[t] = b;
+    sEB[t] = t < len ? b * __expf(g_t[gi]) : 0.f;
+  }
+  const int w = wave_id(), l = lane_id();
+  for (int pass = 0; pass < 2; ++pass) {
+    const TI* src = pass ? k + ((long)start * Hg + hk) * D : v + ((long)start * H + h) * D;
+    const long sstride = pass ? (long)Hg * D : (long)H * D;
+    const float* scl = pass ? sEB : sB;
+    TI* dst = pass ? W : U;
+    for (int p0 = 0; p0 < D; p0 += PW) {
+      __syncthreads();  // sB/sEB/sT written; previous panel consumed
+      stage_rows_T<TI, PW, C>(sP, LD, src + p0, sstride, len, scl);
+      __syncthreads();
+      // wave w owns output columns [16w, 16w + 16) of the panel; T is lower-triangular,
+      // so row block ti only needs k < 16 (ti + 1).
+      for (int ti = 0; ti < C / 16; ++ti) {
+        f32x4 acc = zero4();
+        const int kend = ((ti + 1) * 16 + KS - 1) / KS * KS;
+        mma_lds<TI>(acc, sT, LD, ti * 16, sP, LD, w * 16, 0, kend);
+        const int col = p0 + w * 16 + (l & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = ti * 16 + 4 * (l >> 4) + e;
+          if (i < len) dst[((long)(start + i) * H + h) * D + col] = (TI)acc[e];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- stage 6
+// One workgroup per (sequence, head, 64-column slice).  Wave w owns state columns
+// [16w, 16w+16) of the slice for all Dk rows, kept in accumulator tiles; W h and the
+// K^T v_new update take the state / new values straight from registers.
+template <typename TI, int D, int C>
+__global__ __launch_bounds__(kThreads) void k_chunk_h(const int32_t* table,
+                                                      const int32_t* seq_chunks, const TI* k,
+                                                      const TI* W, const TI* U,
+                                                      const float* g_t, const float* h0,
+                                                      TI* h_c, TI* v_new, float* ht, int Ttot,
+                                                      int H, int Hg) {
+  const int n = blockIdx.x, h = blockIdx.y, hk = h / (H / Hg);
+  const int w = wave_id(), l = lane_id();
+  const int dv = blockIdx.z * 64 + 16 * w + (l & 15);
+  constexpr int NDK = D / 16, NT = C / 16;
+  constexpr int LDW = D + pad_of<TI>(), LDK = C + pad_of<TI>();
+  extern __shared__ __align__(16) char smem[];
+  TI* sW = reinterpret_cast<TI*>(smem);
+  TI* sKt = sW + C * LDW;
+  float* sG = reinterpret_cast<float*>(sKt + D * LDK);
+
+  f32x4 st[NDK];
+  const long hoff = ((long)n * H + h) * D * D;
+#pragma unroll
+  for (int db = 0; db < NDK; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int dk = 16 * db + 4 * (l >> 4) + e;
+      st[db][e] = h0 ? h0[hoff + (long)dk * D + dv] : 0.f;
+    }
+
+  const int c0 = seq_chunks[n], c1 = seq_chunks[n + 1];
+  for (int c = c0; c < c1; ++c) {
+    const int4 ci = load_chunk(table, c);
+    const int start = ci.y, len = ci.z;
+    const long coff = ((long)c * H + h) * D * D;
+#pragma unroll
+    for (int db = 0; db < NDK; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        h_c[coff + (long)(16 * db + 4 * (l >> 4) + e) * D + dv] = (TI)st[db][e];
+    stage_rows<TI, D, C>(sW, LDW, W + ((long)start * H + h) * D, (long)H * D, len);
+    stage_rows_T<TI, D, C>(sKt, LDK, k + ((long)start * Hg + hk) * D, (long)Hg * D, len,
+                           nullptr);
+    for (int t = threadIdx.x; t < C; t += kThreads)
+      sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
+    __syncthreads();
+    const float glast = sG[len - 1];
+    f32x4 vn[NT];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+      f32x4 x = zero4();
+      mma_accB<TI, NDK>(x, sW, LDW, tb * 16, 0, st, NDK);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = tb * 16 + 4 * (l >> 4) + e;
+        float val = 0.f;
+        if (t < len) {
+          const long gi = ((long)(start + t) * H + h) * D + dv;
+          val = (float)U[gi] - x[e];
+          v_new[gi] = (TI)val;
+          val *= __expf(glast - sG[t]);
+        }
+        vn[tb][e] = val;
+      }
+    }
+    const float eg = __expf(glast);
+#pragma unroll
+    for (int db = 0; db < NDK; ++db) {
+      st[db] *= eg;
+      mma_accB<TI, NT>(st[db], sKt, LDK, db * 16, 0, vn, NT);
+    }
+    __syncthreads();
+  }
+  if (ht) {
+#pragma unroll
+    for (int db = 0; db < NDK; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ht[hoff + (long)(16 * db + 4 * (l >> 4) + e) * D + dv] = st[db][e];
+  }
+}
+
+// ------------------------------------------------------------------------- stage 7
+// One workgroup per (chunk, head).  P = (Q K^T * decay) is built once in LDS (K streamed
+// in panels of at most 128 columns), then each 64-column panel of o is produced with
+// Q h_c and P v_new taking h_c and v_new straight from registers (wave w owns 16 columns).
+template <typename TI, int D, int C>
+__global__ __launch_bounds__(kThreads) void k_chunk_o(const int32_t* table, const TI* q,
+                                                      const TI* k, const TI* v_new,
+                                                      const TI* h_c, const float* g_t, TI* o,
+                                                      int Ttot, int H, int Hg, float scale) {
+  const int c = blockIdx.x;
+  const int4 ci = load_chunk(table, c);
+  const int start = ci.y, len = ci.z;
+  if (len == 0) return;
+  const int h = blockIdx.y, hk = h / (H / Hg);
+  const int w = wave_id(), l = lane_id();
+  constexpr int KP = D < 128 ? D : 128;
+  constexpr int NT = C / 16, NDK = D / 16;
+  constexpr int LDQ = D + pad_of<TI>(), LDKP = KP + pad_of<TI>(), LDP = C + pad_of<TI>();
+  constexpr int NLOW = NT * (NT + 1) / 2;
+  constexpr int MAXT = (NLOW + kWaves - 1) / kWaves;
+  extern __shared__ __align__(16) char smem[];
+  TI* sQ = reinterpret_cast<TI*>(smem);
+  TI* sK = sQ + C * LDQ;
+  TI* sP = sK + C * LDKP;
+  float* sG = reinterpret_cast<float*>(sP + C * LDP);
+
+  stage_rows<TI, D, C>(sQ, LDQ, q + ((long)start * Hg + hk) * D, (long)Hg * D, len);
+  for (int t = threadIdx.x; t < C; t += kThreads)
+    sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
+  for (int i = threadIdx.x; i < C * LDP; i += kThreads) sP[i] = (TI)0.f;
+
+  // P^T tiles (rows j, columns i, i >= j) accumulate over K panels.
+  f32x4 pacc[MAXT];
+#pragma unroll
+  for (int m = 0; m < MAXT; ++m) pacc[m] = zero4();
+  for (int kp = 0; kp < D; kp += KP) {
+    __syncthreads();
+    stage_rows<TI, KP, C>(sK, LDKP, k + ((long)start * Hg + hk) * D + kp, (long)Hg * D, len);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MAXT; ++m) {
+      const int u = w + kWaves * m;
+      if (u < NLOW) {
+        int ti = 0;
+        while ((ti + 1) * (ti + 2) / 2 <= u) ++ti;
+        const int tj = u - ti * (ti + 1) / 2;
+        mma_lds<TI>(pacc[m], sK, LDKP, tj * 16, sQ + kp, LDQ, ti * 16, 0, KP);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MAXT; ++m) {
+    const int u = w + kWaves * m;
+    if (u < NLOW) {
+      int ti = 0;
+      while ((ti + 1) * (ti + 2) / 2 <= u) ++ti;
+      const int tj = u - ti * (ti + 1) / 2;
+      const int i = ti * 16 + (l & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = tj * 16 + 4 * (l >> 4) + e;
+        const float val = (i >= j) ? __expf(sG[i] - sG[j]) * pacc[m][e] : 0.f;
+        sP[i * LDP + j] = (TI)val;
+      }
+    }
+  }
+  __syncthreads();
+
+  const long hcoff = ((long)c * H + h) * D * D;
+  for (int p0 = 0; p0 < D; p0 += 64) {
+    const int dv = p0 + 16 * w + (l & 15);
+    f32x4 hc[NDK];
+#pragma unroll
+    for (int db = 0; db < NDK; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hc[db][e] = (float)h_c[hcoff + (long)(16 * db + 4 * (l >> 4) + e) * D + dv];
+    f32x4 vt[NT];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = tb * 16 + 4 * (l >> 4) + e;
+        vt[tb][e] = t < len ? (float)v_new[((long)(start + t) * H + h) * D + dv] : 0.f;
+      }
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+      f32x4 acc = zero4();
+      mma_accB<TI, NDK>(acc, sQ, LDQ, tb * 16, 0, hc, NDK);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] *= __expf(sG[tb * 16 + 4 * (l >> 4) + e]);
+      mma_accB<TI, NT>(acc, sP, LDP, tb * 16, 0, vt, tb + 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = tb * 16 + 4 * (l >> 4) + e;
+        if (t < len) o[((long)(start + t) * H + h) * D + dv] = (TI)(scale * acc[e]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- launchers
+template <typename K>
+hipError_t set_smem(K kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+#define GDN_TRY(x)                          \
+  do {                                      \
+    hipError_t e_ = (x);                    \
+    if (e_ != hipSuccess) return e_;        \
+  } while (0)
+
+template <typename TI, int D, int C>
+hipError_t run_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st) {
+  const int MC = p.max_chunks;
+  const TI* q = static_cast<const TI*>(p.q);
+  const TI* k = static_cast<const TI*>(p.k);
+  const TI* v = static_cast<const TI*>(p.v);
+  TI* Tinv = static_cast<TI*>(s.Tinv);
+  TI* W = static_cast<TI*>(s.W);
+  TI* U = static_cast<TI*>(s.U);
+  TI* h_c = static_cast<TI*>(s.h_c);
+  TI* v_new = static_cast<TI*>(s.v_new);
+  const int bf = p.beta_f32 ? 1 : 0;
+
+  k_chunk_table<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.Ttot, C, MC, s.table, s.seq_chunks);
+  GDN_TRY(hipGetLastError());
+  if (MC == 0) return hipSuccess;
+
+  k_cumsum<C><<<MC, kThreads, 0, st>>>(s.table, p.g, s.g_cum, p.H);
+  GDN_TRY(hipGetLastError());
+  if (stop_after == 1) return hipSuccess;
+
+  if (p.Ttot > 0) {
+    dim3 grid((p.Ttot + 63) / 64, (p.H + 63) / 64);
+    k_transpose<float><<<grid, kThreads, 0, st>>>(s.g_cum, s.g_t, p.Ttot, p.H);
+    GDN_TRY(hipGetLastError());
+    if (p.beta_f32)
+      k_transpose<float><<<grid, kThreads, 0, st>>>(static_cast<const float*>(p.beta),
+                                                    static_cast<float*>(s.beta_t), p.Ttot, p.H);
+    else
+      k_transpose<uint16_t><<<grid, kThreads, 0, st>>>(static_cast<const uint16_t*>(p.beta),
+                                                       static_cast<uint16_t*>(s.beta_t),
+                                                       p.Ttot, p.H);
+    GDN_TRY(hipGetLastError());
+  }
+  if (stop_after == 2) return hipSuccess;
+
+  {
+    const size_t sm = C * (D + pad_of<TI>()) * sizeof(TI) + 2 * C * sizeof(float);
+    GDN_TRY(set_smem(k_kkt<TI, D, C>, sm));
+    k_kkt<TI, D, C><<<dim3(MC, p.H), kThreads, sm, st>>>(s.table, k, s.g_t, s.beta_t, bf, s.A,
+                                                         p.Ttot, p.H, p.Hg);
+    GDN_TRY(hipGetLastError());
+  }
+  if (stop_after == 3) return hipSuccess;
+
+  {
+    typedef typename SolveType<TI>::type TS;
+    const size_t sm = 2 * C * (C + pad_of<TS>()) * sizeof(TS) + (C / 16) * 16 * kAdLd * 4;
+    GDN_TRY(set_smem(k_solve<TI, C>, sm));
+    k_solve<TI, C><<<dim3(MC, p.H), kThreads, sm, st>>>(s.table, s.A, Tinv, p.H);
+    GDN_TRY(hipGetLastError());
+  }
+  if (stop_after == 4) return hipSuccess;
+
+  {
+    const size_t sm = (C + 64) * (C + pad_of<TI>()) * sizeof(TI) + 2 * C * sizeof(float);
+    GDN_TRY(set_smem(k_wy<TI, D, C>, sm));
+    k_wy<TI, D, C><<<dim3(MC, p.H), kThreads, sm, st>>>(s.table, Tinv, k, v, s.g_t, s.beta_t,
+                                                        bf, W, U, p.Ttot, p.H, p.Hg);
+    GDN_TRY(hipGetLastError());
+  }
+  if (stop_after == 5) return hipSuccess;
+
+  {
+    const size_t sm = (C * (D + pad_of<TI>()) + D * (C + pad_of<TI>())) * sizeof(TI) +
+                      C * sizeof(float);
+    GDN_TRY(set_smem(k_chunk_h<TI, D, C>, sm));
+    k_chunk_h<TI, D, C><<<dim3(p.N, p.H, D / 64), kThreads, sm, st>>>(
+        s.table, s.seq_chunks, k, W, U, s.g_t, p.h0, h_c, v_new, stop_after ? nullptr : p.ht,
+        p.Ttot, p.H, p.Hg);
+    GDN_TRY(hipGetLastError());
+  }
+  if (stop_after == 6) return hipSuccess;
+
+  {
+    constexpr int KP = D < 128 ? D : 128;
+    const size_t sm = (C * (D + pad_of<TI>()) + C * (KP + pad_of<TI>()) +
+                       C * (C + pad_of<TI>())) * sizeof(TI) + C * sizeof(float);
+    GDN_TRY(set_smem(k_chunk_o<TI, D, C>, sm));
+    k_chunk_o<TI, D, C><<<dim3(MC, p.H), kThreads, sm, st>>>(
+        s.table, q, k, v_new, h_c, s.g_t, static_cast<TI*>(p.o), p.Ttot, p.H, p.Hg, p.scale);
+    GDN_TRY(hipGetLastError());
+  }
+  return hipSuccess;
+}
+
+template <typename TI, int D>
+hipError_t run_staged_c(const Problem& p, const Stages& s, int stop_after, hipStream_t st) {
+  return p.C == 64 ? run_staged<TI, D, 64>(p, s, stop_after, st)
+                   : run_staged<TI, D, 128>(p, s, stop_after, st);
+}
+
+template <typename TI>
+hipError_t run_staged_d(const Problem& p, const Stages& s, int stop_after, hipStream_t st) {
+  switch (p.D) {
+    case 64: return run_staged_c<TI, 64>(p, s, stop_after, st);
+    case 128: return run_staged_c<TI, 128>(p, s, stop_after, st);
+    default: return run_staged_c<TI, 256>(p, s, stop_after, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st) {
+  return p.f32 ? run_staged_d<float>(p, s, stop_after, st)
+               : run_staged_d<bf16>(p, s, stop_after, st);
+}
+
+}  // namespace gdn

@@ -1,0 +1,122 @@
+/*
+ * libgdn — chunked Gated DeltaNet forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one call): for every sequence n and value head h, with q/k head
+ * hk = h / (H / Hg), starting from S = h0[n, h]^T (zero when h0 is NULL), for each token t
+ *
+ *     S   <- exp(g_t) S (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t <- scale S q_t
+ *
+ * and finally ht[n, h] = S^T.  It is evaluated chunk by chunk (chunk length C) through
+ * the seven stages of the MegaGDN-PTO page (section 1.1: cumsum, transpose,
+ * scaled_dot_kkt, solve_tril, wy_fast, chunk_h, chunk_o), either as seven launches
+ * (GDN_VARIANT_STAGED) or as one launch that keeps every intermediate on chip
+ * (GDN_VARIANT_FUSED; the megakernel idea of the page's section 1.3).  GQA (Hg q/k heads
+ * shared by H value heads in contiguous groups) follows the page's section 5.2, packed
+ * variable-length batches via cu_seqlens its section 5.3, and the user-level call shape
+ * (q, k, v, g, beta, scale, initial_state, output_final_state) the FlashQLA how-to, step 5.2.
+ *
+ * Layouts (all contiguous, row-major; the token axis of a packed batch is B = 1, T = total):
+ *   q, k    [B, T, Hg, Dk]   qkv_dtype (bf16 or f32)
+ *   v, o    [B, T, H,  Dv]   qkv_dtype
+ *   g       [B, T, H]        f32, the log-decay (g <= 0 in the intended use)
+ *   beta    [B, T, H]        beta_dtype (bf16 or f32)
+ *   h0, ht  [N, H, Dk, Dv]   f32 (the [B, H, K, V] state layout of the FlashQLA how-to,
+ *                            step 5.3): ht[n, h, a, b] = S[b, a]
+ *   cu_seqlens [N + 1]       int32, device memory, cu[0] = 0, non-decreasing, cu[N] <= B*T
+ *
+ * Ownership: the caller allocates and frees every buffer (device memory) and the optional
+ * workspace.  The library keeps no pointer after a call returns, allocates nothing, and
+ * has no mutable global state; calls are reentrant.  All work is enqueued on `stream`
+ * (NULL = the default stream) and nothing is synchronised: errors found on the host are
+ * returned before any launch; a launch failure returns GDN_ERR_HIP.  cu_seqlens is read
+ * only on the device: values outside [0, B*T] are clamped (a sequence never reads or
+ * writes outside the token range), but non-monotone values give unspecified results.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* null required pointer, bad shape, misaligned pointer */
+  GDN_ERR_UNSUPPORTED = 2, /* valid but not built: Dk != Dv, D not in {64,128,256}, ... */
+  GDN_ERR_WORKSPACE = 3,   /* staged variant without a large enough workspace */
+  GDN_ERR_HIP = 4          /* a HIP launch or attribute call failed */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_variant {
+  GDN_VARIANT_AUTO = 0,   /* fused when built for the shape, otherwise staged */
+  GDN_VARIANT_STAGED = 1, /* seven launches, intermediates in the workspace */
+  GDN_VARIANT_FUSED = 2   /* one launch, one workgroup per (sequence, head) */
+} gdn_variant;
+
+/* Intermediate buffers of the staged variant, readable through gdn_stage_buffer(). */
+typedef enum gdn_buffer {
+  GDN_BUF_CHUNK_TABLE = 0, /* int32 [max_chunks, 4]: (sequence, first token, length, index
+                              in sequence); unused rows have length 0                  */
+  GDN_BUF_SEQ_CHUNKS = 1,  /* int32 [N + 1]: first chunk of each sequence; [N] = total    */
+  GDN_BUF_G_CUM = 2,       /* f32 [B*T, H]: in-chunk inclusive prefix sum of g  (stage 1) */
+  GDN_BUF_G_T = 3,         /* f32 [H, B*T]: g_cum transposed                    (stage 2) */
+  GDN_BUF_BETA_T = 4,      /* beta_dtype [H, B*T]: beta transposed              (stage 2) */
+  GDN_BUF_A = 5,           /* f32 [B*T, H, C]: gated strictly-lower K K^T       (stage 3) */
+  GDN_BUF_TINV = 6,        /* qkv_dtype [B*T, H, C]: rows of (I + A)^-1         (stage 4) */
+  GDN_BUF_W = 7,           /* qkv_dtype [B*T, H, Dk]                            (stage 5) */
+  GDN_BUF_U = 8,           /* qkv_dtype [B*T, H, Dv]                            (stage 5) */
+  GDN_BUF_H_C = 9,         /* qkv_dtype [max_chunks, H, Dk, Dv]: state at chunk start (6) */
+  GDN_BUF_V_NEW = 10,      /* qkv_dtype [B*T, H, Dv]: U - W h_c                 (stage 6) */
+  GDN_BUF_COUNT = 11
+} gdn_buffer;
+
+typedef struct gdn_desc {
+  int32_t B, T;       /* dense batch [B, T, ...]; packed varlen: B = 1, T = total tokens */
+  int32_t N;          /* sequences: B when cu_seqlens is NULL, else len(cu_seqlens) - 1 */
+  int32_t H, Hg;      /* value heads, q/k heads; H % Hg == 0                              */
+  int32_t Dk, Dv;     /* head dims; this build supports Dk == Dv in {64, 128, 256}        */
+  int32_t chunk;      /* C in {64, 128}; 0 selects 128                                    */
+  int32_t qkv_dtype;  /* gdn_dtype of q, k, v, o                                          */
+  int32_t beta_dtype; /* gdn_dtype of beta                                                */
+  int32_t variant;    /* gdn_variant                                                      */
+  int32_t stop_after; /* staged only: 0 = all stages, k in 1..6 = stop after stage k      */
+  void* workspace;    /* device memory for the staged variant (may be NULL for fused)     */
+  size_t workspace_bytes;
+} gdn_desc;
+
+/* Bytes of workspace the variant chosen by d->variant needs (0 for the fused variant);
+ * host-only, no device work.  Returns 0 and sets *status on an invalid descriptor. */
+size_t gdn_chunk_fwd_workspace_size(const gdn_desc* d, gdn_status* status);
+
+/* The forward pass.  q, k, v, g, beta, o are required; h0 (zero state), cu_seqlens (dense
+ * batch) and ht (final state not written) may be NULL.  scale multiplies o (Dk^-0.5 is the
+ * usual choice).  Pointers must be device pointers aligned to 16 bytes (g, beta, cu_seqlens:
+ * 4 / 2 / 4 bytes).  With stop_after = k > 0 (staged only) o and ht are not written. */
+gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const void* v,
+                         const float* g, const void* beta, const float* h0,
+                         const int32_t* cu_seqlens, float scale, void* o, float* ht,
+                         hipStream_t stream);
+
+/* Where intermediate `buf` lives inside the staged workspace (offset and size in bytes),
+ * for stage-by-stage inspection (the page's section 7.4 debugging mode). */
+gdn_status gdn_stage_buffer(const gdn_desc* d, int32_t buf, size_t* offset, size_t* bytes);
+
+/* Static, human-readable text for a status code. */
+const char* gdn_status_string(gdn_status s);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

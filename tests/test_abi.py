@@ -1,0 +1,143 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every function the
+header declares, validates descriptors before any launch and lays out the workspace."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_chunked_02_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built (python -m gated_deltanet_chunked_02_amd.build)")
+    return gdn.load()
+
+
+def header_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert {"gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size", "gdn_stage_buffer",
+            "gdn_status_string", "gdn_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert len(gdn.gdn_status_string(s)) > 0
+    assert gdn.gdn_status_string(99) == "unknown status"
+    assert gdn.gdn_version() >= 100
+
+
+def desc(**kw):
+    base = dict(B=2, T=256, N=2, H=4, Hg=2, Dk=128, Dv=128, chunk=128, qkv_dtype=1,
+                beta_dtype=1, variant=0, stop_after=0, workspace=None, workspace_bytes=0)
+    base.update(kw)
+    return gdn.GdnDesc(**base)
+
+
+def ws_status(d):
+    st = ctypes.c_int(-1)
+    n = gdn.load().gdn_chunk_fwd_workspace_size(ctypes.byref(d), ctypes.byref(st))
+    return st.value, n
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(H=3, Hg=2), 1),
+    (dict(B=0), 1),
+    (dict(T=-1), 1),
+    (dict(Dk=128, Dv=64), 2),
+    (dict(Dk=96, Dv=96), 2),
+    (dict(chunk=32), 2),
+    (dict(qkv_dtype=7), 1),
+    (dict(variant=9), 1),
+    (dict(stop_after=7), 1),
+    (dict(qkv_dtype=0, beta_dtype=0, Dk=128, Dv=128, chunk=128), 2),
+    (dict(qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, chunk=64), 0),
+    (dict(variant=2, qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, chunk=64), 2),
+    (dict(variant=2, Dk=256, Dv=256), 2),
+    (dict(variant=2, stop_after=3), 2),
+])
+def test_descriptor_validation(lib, kw, status):
+    st, n = ws_status(desc(**kw))
+    assert st == status
+    if st != 0:
+        assert n == 0
+
+
+def test_fused_needs_no_workspace_and_staged_does(lib):
+    assert ws_status(desc(variant=2)) == (0, 0)
+    st, n = ws_status(desc(variant=1))
+    assert st == 0 and n > 0
+    # AUTO resolves to fused where it is built, to staged otherwise (D = 256)
+    assert ws_status(desc(variant=0))[1] == 0
+    assert ws_status(desc(variant=0, Dk=256, Dv=256))[1] > 0
+
+
+def test_staged_layout_is_aligned_and_disjoint(lib):
+    d = desc(variant=1, B=3, T=1000, N=3, H=6, Hg=3, Dk=64, Dv=64, chunk=64)
+    total = gdn.gdn_chunk_fwd_workspace_size(d)
+    spans = []
+    for name, b in gdn.BUFFERS.items():
+        off, nb = gdn.gdn_stage_buffer(d, b)
+        assert off % 256 == 0
+        assert off + nb <= total
+        spans.append((off, off + nb, name))
+    spans.sort()
+    for (a0, a1, _), (b0, b1, _) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    Ttot, H, C, D = 3000, 6, 64, 64
+    max_chunks = -(-Ttot // C) + 3
+    sizes = {n: gdn.gdn_stage_buffer(d, n)[1] for n in gdn.BUFFERS}
+    assert sizes["chunk_table"] == max_chunks * 16
+    assert sizes["A"] == Ttot * H * C * 4
+    assert sizes["Tinv"] == Ttot * H * C * 2
+    assert sizes["h_c"] == max_chunks * H * D * D * 2
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_stage_buffer(d, 11)
+
+
+def test_chunk_fwd_rejects_bad_arguments_before_any_launch(lib):
+    # Fake, well-aligned addresses: validation must fail before anything touches them.
+    A = 0x10000
+    d = desc(variant=2)
+
+    def call(dd=d, q=A, k=A, v=A, g=A, beta=A, h0=None, cu=None, o=A, ht=None):
+        return gdn.load().gdn_chunk_fwd(ctypes.byref(dd), q, k, v, g, beta, h0, cu, 1.0, o, ht,
+                                        None)
+
+    assert call(q=None) == 1
+    assert call(o=None) == 1
+    assert call(beta=None) == 1
+    assert call(q=A + 2) == 1             # misaligned q
+    assert call(g=A + 2) == 1             # misaligned g
+    assert call(h0=A + 8) == 1            # misaligned h0
+    assert call(dd=desc(variant=2, H=3, Hg=2)) == 1
+    assert call(dd=desc(variant=2, Dk=96, Dv=96)) == 2
+    assert call(dd=desc(variant=2, N=3)) == 1             # dense batch: N must equal B
+    assert call(dd=desc(variant=2, B=2), cu=A) == 1       # varlen needs B == 1
+    assert call(dd=desc(variant=1)) == 3                  # staged without workspace
+    assert call(dd=desc(variant=1, workspace=A, workspace_bytes=16)) == 3
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    g = torch.zeros(1, 4, 1)
+    with pytest.raises(ValueError):
+        gdn.chunk_gated_delta_rule(x, x, x, g, g.to(torch.bfloat16))

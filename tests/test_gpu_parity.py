@@ -1,0 +1,268 @@
+"""GPU parity: libgdn (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Sizes here are ones the oracle finishes in seconds while still spanning several chunks,
+several 16-row tiles and a ragged last chunk.  Tolerances: fp32 workloads max-abs <= 1e-4 on
+o and ht; bf16 workloads relative L2 <= 5e-3 on o and <= 1e-2 on ht.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs
+from gdn_testlib import (check_against_oracle, max_abs, oracle_full, rel_l2, run_gdn, to64)
+
+pytestmark = pytest.mark.gpu
+
+LOG = os.environ.get("GDN_PARITY_LOG")
+
+
+def log(**kw):
+    print(json.dumps(kw), flush=True)
+    if LOG:
+        with open(LOG, "a") as f:
+            f.write(json.dumps(kw) + "\n")
+
+
+def draw(**kw):
+    return gdn_inputs.draw(gdn_inputs.small(**kw), device="cpu")
+
+
+# ------------------------------------------------------------------ the fp32 workload
+@pytest.mark.parametrize("variant", ["auto", "staged"])
+def test_tiny_f32_workload(variant):
+    inp = gdn_inputs.draw(gdn_inputs.WORKLOADS["tiny_f32"], device="cpu")
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant=variant)
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "tiny_f32")
+    log(test="tiny_f32", variant=variant, o_maxabs=eo, ht_maxabs=eh)
+
+
+# ------------------------------------------------------------------ bf16, dense batches
+CASES = [
+    # D, C, H, Hg, B, T, h0
+    (128, 128, 4, 4, 2, 300, True),
+    (128, 128, 4, 2, 1, 517, False),
+    (128, 64, 2, 2, 2, 200, True),
+    (64, 64, 4, 4, 2, 333, True),
+    (64, 128, 2, 1, 1, 390, True),
+    (256, 128, 4, 1, 1, 290, True),
+    (256, 64, 2, 2, 1, 150, False),
+]
+
+
+@pytest.mark.parametrize("D,C,H,Hg,B,T,h0", CASES)
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+def test_bf16_dense(variant, D, C, H, Hg, B, T, h0):
+    if variant == "fused" and D == 256:
+        pytest.skip("fused variant is built for D in {64, 128}")
+    inp = draw(B=B, T=T, H=H, Hg=Hg, Dk=D, C=C, seed=D + C + T, h0_std=0.05 if h0 else None)
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant=variant)
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "%s D%d C%d" % (variant, D, C))
+    log(test="bf16_dense", variant=variant, D=D, C=C, H=H, Hg=Hg, B=B, T=T, o_rel=eo, ht_rel=eh)
+
+
+# ------------------------------------------------------------------ packed varlen
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+@pytest.mark.parametrize("C", [64, 128])
+def test_varlen_edge_lengths(variant, C):
+    lens = [1, C - 1, C, C + 1, 0, 3 * C + 17, 2]
+    w = gdn_inputs.small(H=4, Hg=2, Dk=128, C=C, seed=7, h0_std=0.05)
+    inp = gdn_inputs.draw(w.with_(B=1, T=sum(lens)), device="cpu")
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    inp["cu_seqlens"] = torch.from_numpy(cu)
+    inp["h0"] = torch.randn(len(lens), 4, 128, 128, generator=torch.Generator().manual_seed(3)) * 0.05
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant=variant)
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "varlen")
+    # the empty sequence passes its initial state through untouched
+    assert torch.equal(ht[4].cpu(), inp["h0"][4])
+    log(test="varlen_edges", variant=variant, C=C, o_rel=eo, ht_rel=eh)
+
+
+def test_varlen_workload_reduced():
+    """The varlen recipe (lengths U{1..max_len}) at a reduced size: 12 sequences up to 700."""
+    w = gdn_inputs.WORKLOADS["varlen"].with_(n_varlen=12, max_len=700, H=4, Hg=4)
+    inp = gdn_inputs.draw(w, device="cpu")
+    o_ref, ht_ref = oracle_full(inp)
+    for variant in ("staged", "fused"):
+        o, ht = run_gdn(inp, variant=variant)
+        eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "varlen " + variant)
+        log(test="varlen_reduced", variant=variant, o_rel=eo, ht_rel=eh)
+
+
+# ------------------------------------------------------------------ per-stage parity
+def staged_buffers(inp, C):
+    """Run the staged variant and return its workspace intermediates as float64 arrays."""
+    import gated_deltanet_chunked_02_amd as gdn
+    dev = torch.device("cuda")
+    q = inp["q"].to(dev)
+    desc = gdn.make_desc(q, inp["v"], inp["beta"], inp["cu_seqlens"], C, "staged")
+    ws = torch.zeros(gdn.gdn_chunk_fwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+    o, ht = run_gdn(inp, variant="staged", C=C, workspace=ws)
+    Ttot = q.shape[0] * q.shape[1]
+    H, D = inp["v"].shape[2], inp["v"].shape[3]
+    el = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    eb = torch.float32 if inp["beta"].dtype == torch.float32 else torch.bfloat16
+
+    def buf(name, dtype, shape):
+        off, nb = gdn.gdn_stage_buffer(desc, name)
+        t = ws[off:off + nb].view(dtype)
+        return t.reshape(shape)
+
+    MC = gdn.gdn_stage_buffer(desc, "chunk_table")[1] // 16
+    out = dict(
+        table=buf("chunk_table", torch.int32, (MC, 4)).cpu().numpy(),
+        seq_chunks=buf("seq_chunks", torch.int32, (-1,)).cpu().numpy(),
+        g_cum=to64(buf("g_cum", torch.float32, (Ttot, H))),
+        g_t=to64(buf("g_t", torch.float32, (H, Ttot))),
+        beta_t=to64(buf("beta_t", eb, (H, Ttot))),
+        A=to64(buf("A", torch.float32, (Ttot, H, C))),
+        Tinv=to64(buf("Tinv", el, (Ttot, H, C))),
+        W=to64(buf("W", el, (Ttot, H, D))),
+        U=to64(buf("U", el, (Ttot, H, D))),
+        h_c=to64(buf("h_c", el, (MC, H, D, D))),
+        v_new=to64(buf("v_new", el, (Ttot, H, D))),
+    )
+    return out, o, ht
+
+
+@pytest.mark.parametrize("wl", ["tiny_f32", "bf16_gqa_varlen"])
+def test_stage_by_stage(wl):
+    from oracle import chunked
+    if wl == "tiny_f32":
+        inp = gdn_inputs.draw(gdn_inputs.WORKLOADS["tiny_f32"], device="cpu")
+        tol = 1e-5
+    else:
+        lens = [70, 128, 1, 300]
+        w = gdn_inputs.small(H=4, Hg=2, Dk=128, C=128, seed=11, h0_std=0.05)
+        inp = gdn_inputs.draw(w.with_(B=1, T=sum(lens)), device="cpu")
+        inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+        inp["h0"] = torch.randn(4, 4, 128, 128, generator=torch.Generator().manual_seed(5)) * 0.05
+        tol = 1e-2
+    C = inp["C"]
+    got, o, ht = staged_buffers(inp, C)
+    ref = chunked.chunked(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), to64(inp["g"]),
+                          to64(inp["beta"]), to64(inp["h0"]), scale=inp["scale"],
+                          cu_seqlens=None if inp["cu_seqlens"] is None
+                          else inp["cu_seqlens"].numpy(), C=C)
+    NC = len(ref["table"])
+    # stage 0: integer work, bit-exact
+    exp_tab = np.array([(n, s, L) for n, s, L in ref["table"]], dtype=np.int64)
+    assert np.array_equal(got["table"][:NC, :3], exp_tab)
+    assert np.all(got["table"][NC:, 2] == 0)
+    errs = {}
+    # stage 1-2: fp32 sums and exact copies
+    errs["g_cum"] = max_abs(got["g_cum"], ref["g_cum"])
+    assert errs["g_cum"] <= 1e-5
+    assert np.array_equal(got["g_t"], got["g_cum"].T)
+    assert np.array_equal(got["beta_t"], to64(inp["beta"]).reshape(-1, inp["beta"].shape[-1]).T)
+    # stages 3-7: relative L2 per intermediate
+    for name in ("A", "Tinv", "W", "U", "v_new"):
+        errs[name] = rel_l2(got[name], ref[name])
+    errs["h_c"] = rel_l2(got["h_c"][:NC], ref["h_c"])
+    errs["o"] = rel_l2(to64(o).reshape(ref["o"].shape), ref["o"])
+    errs["ht"] = rel_l2(to64(ht), ref["ht"])
+    log(test="stage_by_stage", workload=wl, **errs)
+    assert errs["A"] <= 1e-5
+    for name in ("Tinv", "W", "U", "h_c", "v_new", "o", "ht"):
+        assert errs[name] <= tol, (name, errs[name])
+
+
+def test_stop_after_leaves_outputs_untouched():
+    import gated_deltanet_chunked_02_amd as gdn
+    inp = draw(B=1, T=200, H=2, Dk=64, C=64, seed=3)
+    dev = torch.device("cuda")
+    args = [inp[n].to(dev) for n in ("q", "k", "v", "g", "beta")]
+    o = torch.full_like(args[2], 7.0)
+    for k in range(1, 7):
+        desc = gdn.make_desc(args[0], args[2], args[4], None, 64, "staged", stop_after=k)
+        ws = torch.zeros(gdn.gdn_chunk_fwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+        desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+        st = gdn.gdn_chunk_fwd(desc, *args, None, None, inp["scale"], o, None)
+        torch.cuda.synchronize()
+        assert st == 0
+        assert torch.all(o == 7.0)
+
+
+# ------------------------------------------------------------------ invariants
+def test_fused_and_staged_agree_and_are_deterministic():
+    inp = draw(B=2, T=400, H=4, Hg=2, Dk=128, C=128, seed=21, h0_std=0.05)
+    o1, h1 = run_gdn(inp, variant="fused")
+    o2, h2 = run_gdn(inp, variant="fused")
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)          # bitwise rerun
+    o3, h3 = run_gdn(inp, variant="staged")
+    o4, h4 = run_gdn(inp, variant="staged")
+    assert torch.equal(o3, o4) and torch.equal(h3, h4)
+    e = rel_l2(to64(o1), to64(o3))
+    log(test="fused_vs_staged", o_rel=e, ht_rel=rel_l2(to64(h1), to64(h3)))
+    assert e <= 5e-3
+
+
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+def test_chunk_size_invariance(variant):
+    inp = draw(B=1, T=333, H=2, Dk=128, C=64, seed=22, h0_std=0.05)
+    o64, h64 = run_gdn(inp, variant=variant, C=64)
+    o128, h128 = run_gdn(inp, variant=variant, C=128)
+    assert rel_l2(to64(o64), to64(o128)) <= 5e-3
+    assert rel_l2(to64(h64), to64(h128)) <= 1e-2
+
+
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+def test_gqa_equals_repeated_heads_and_varlen_equals_dense(variant):
+    inp = draw(B=2, T=260, H=4, Hg=2, Dk=64, C=64, seed=23, h0_std=0.05)
+    o, ht = run_gdn(inp, variant=variant)
+    rep = dict(inp)
+    rep["q"] = inp["q"].repeat_interleave(2, dim=2)
+    rep["k"] = inp["k"].repeat_interleave(2, dim=2)
+    o2, ht2 = run_gdn(rep, variant=variant)
+    assert torch.equal(o, o2) and torch.equal(ht, ht2)
+    packed = dict(inp)
+    for n in ("q", "k", "v", "g", "beta"):
+        packed[n] = inp[n].reshape((1, 520) + tuple(inp[n].shape[2:]))
+    packed["cu_seqlens"] = torch.tensor([0, 260, 520], dtype=torch.int32)
+    o3, ht3 = run_gdn(packed, variant=variant)
+    assert torch.equal(o.reshape(o3.shape), o3) and torch.equal(ht, ht3)
+
+
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+def test_initial_state_none_equals_zeros_and_final_state_optional(variant):
+    inp = draw(B=1, T=150, H=2, Dk=64, C=64, seed=24, h0_std=None)
+    o, ht = run_gdn(inp, variant=variant)
+    z = dict(inp)
+    z["h0"] = torch.zeros(1, 2, 64, 64)
+    o2, ht2 = run_gdn(z, variant=variant)
+    assert torch.equal(o, o2) and torch.equal(ht, ht2)
+    o3, ht3 = run_gdn(inp, variant=variant, output_final_state=False)
+    assert ht3 is None and torch.equal(o, o3)
+
+
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+def test_continuation_through_final_state(variant):
+    inp = draw(B=1, T=384, H=2, Dk=128, C=128, seed=25, h0_std=0.05)
+    o, ht = run_gdn(inp, variant=variant)
+    a, b = dict(inp), dict(inp)
+    for n in ("q", "k", "v", "g", "beta"):
+        a[n] = inp[n][:, :256]
+        b[n] = inp[n][:, 256:].contiguous()
+    oa, hta = run_gdn(a, variant=variant)
+    b["h0"] = hta.cpu()
+    ob, htb = run_gdn(b, variant=variant)
+    # chunk boundaries coincide (256 = 2 C), so only the state handoff differs: exact in fp32
+    assert torch.equal(torch.cat([oa, ob], dim=1), o)
+    assert torch.equal(htb, ht)
+
+
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+def test_single_token_and_scale(variant):
+    inp = draw(B=3, T=1, H=2, Dk=64, C=64, seed=26, h0_std=0.1)
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant=variant)
+    check_against_oracle(inp, o, ht, o_ref, ht_ref, "T=1")
+    inp2 = dict(inp)
+    inp2["scale"] = 2.0 * inp["scale"]
+    o2, _ = run_gdn(inp2, variant=variant)
+    assert rel_l2(to64(o2), 2.0 * to64(o)) <= 1e-2
