@@ -102,6 +102,25 @@ def cpu_baseline(inp, o_gpu, ht_gpu, budget_s: float):
     }
 
 
+def copy_reference(args, dev):
+    """A plain copy of 1 GiB (bf16): 1 GiB read + 1 GiB written per launch."""
+    n = 1 << 29
+    a = torch.ones(n, device=dev, dtype=torch.bfloat16)
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    print(json.dumps({"mode": "copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                      "ms_per_copy": ms, "GBps": 4 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +130,9 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged"])
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--mode", default="gdn", choices=["gdn", "copy"],
+                    help="copy: time a plain 1 GiB device-to-device copy (the reference "
+                         "kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
@@ -123,6 +145,9 @@ def main():
     import gated_deltanet_chunked_02_amd as gdn
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "copy":
+        copy_reference(args, dev)
+        return
     w = gdn_inputs.WORKLOADS[args.workload]
     print("[bench] drawing %s on %s" % (w.name, dev), file=sys.stderr, flush=True)
     inp = gdn_inputs.draw(w, device=dev)
