@@ -28,6 +28,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -77,8 +78,8 @@ template <typename E> constexpr int pad_of() { return 16 / (int)sizeof(E); }
 
 // Standard fragment load from a k-contiguous LDS matrix m[row][k] (leading dim ld).
 template <typename E>
-__device__ __forceinline__ typename Mma<E>::frag frag_ld(const E* m, int ld, int row0, int k0) {
-  const int l = lane_id();
+__device__ __forceinline__ typename Mma<E>::frag frag_ld(const E* m, int ld, int row0, int k0,
+                                                         int l = lane_id()) {
   const E* p = m + (row0 + (l & 15)) * ld + k0 + Mma<E>::KPL * (l >> 4);
   if constexpr (Mma<E>::KPL == 8) {
     return *reinterpret_cast<const typename Mma<E>::frag*>(p);
@@ -91,9 +92,10 @@ __device__ __forceinline__ typename Mma<E>::frag frag_ld(const E* m, int ld, int
 // operands k-contiguous in LDS.
 template <typename E>
 __device__ __forceinline__ void mma_lds(f32x4& acc, const E* A, int lda, int arow0,
-                                        const E* B, int ldb, int bcol0, int k0, int k1) {
+                                        const E* B, int ldb, int bcol0, int k0, int k1,
+                                        int l = lane_id()) {
   for (int k = k0; k < k1; k += Mma<E>::KS)
-    acc = Mma<E>::mma(frag_ld<E>(A, lda, arow0, k), frag_ld<E>(B, ldb, bcol0, k), acc);
+    acc = Mma<E>::mma(frag_ld<E>(A, lda, arow0, k, l), frag_ld<E>(B, ldb, bcol0, k, l), acc);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -106,8 +108,8 @@ __device__ __forceinline__ void mma_lds(f32x4& acc, const E* A, int lda, int aro
 // the diagonal.
 template <typename E, int NKB, bool MaskUpper = false>
 __device__ __forceinline__ void mma_accB(f32x4& acc, const E* A, int lda, int arow0, int koff,
-                                         const f32x4* Bt, int nkb, int diag = 0) {
-  const int l = lane_id();
+                                         const f32x4* Bt, int nkb, int diag = 0,
+                                         int l = lane_id()) {
   const int r = arow0 + (l & 15);
   const int g4 = 4 * (l >> 4);
   if constexpr (Mma<E>::KPL == 8) {
@@ -153,6 +155,58 @@ __device__ __forceinline__ void mma_accB(f32x4& acc, const E* A, int lda, int ar
     }
   }
 }
+
+// B tiles may be held as fp32 accumulators (converted at use) or already as 16-bit
+// 4-vectors (the form they take as operands).
+template <typename H> __device__ __forceinline__ H as_half(const f32x4& x) {
+  return __builtin_convertvector(x, H);
+}
+template <typename H> __device__ __forceinline__ H as_half(const H& x) { return x; }
+
+// Same contraction for NJ outputs that share the A operand; one A fragment load feeds NJ
+// matrix-core instructions.
+//   acc[j * AJ] += A * B_j,  B_j block kb = Bt[j * BJ + kb * BK].
+template <typename E, int NKB, int NJ, bool MaskUpper = false, int AJ = 1, int BJ = NKB,
+          int BK = 1, typename BT = f32x4>
+__device__ __forceinline__ void mma_accB_n(f32x4* acc, const E* A, int lda, int arow0, int koff,
+                                           const BT* Bt, int nkb, int diag = 0,
+                                           int l = lane_id()) {
+  const int r = arow0 + (l & 15);
+  const int g4 = 4 * (l >> 4);
+  static_assert(Mma<E>::KPL == 8, "16-bit operands");
+  typedef typename Mma<E>::frag frag;
+  typedef typename Mma<E>::half half;
+#pragma unroll
+  for (int kb = 0; kb < NKB; kb += 2) {
+    if (kb < nkb) {
+      const bool two = (kb + 1 < NKB) && (kb + 1 < nkb);
+      const E* p0 = A + r * lda + koff + 16 * kb + g4;
+      half x0 = *reinterpret_cast<const half*>(p0);
+      half x1 = two ? *reinterpret_cast<const half*>(p0 + 16) : half{0, 0, 0, 0};
+      if constexpr (MaskUpper) {
+        const int row = r - diag;
+        const int k0 = 16 * kb + g4 + koff - diag;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (k0 + i > row) x0[i] = (E)0.f;
+          if (k0 + 16 + i > row) x1[i] = (E)0.f;
+        }
+      }
+      const frag a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const half b0 = as_half<half>(Bt[j * BJ + kb * BK]);
+        const half b1 = two ? as_half<half>(Bt[j * BJ + (kb + 1) * BK]) : half{0, 0, 0, 0};
+        acc[j * AJ] = Mma<E>::mma(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                  acc[j * AJ]);
+      }
+    }
+  }
+}
+
+// Make the compiler treat a value as changed here, so address arithmetic derived from it is
+// not hoisted out of a loop (and kept live across it).
+template <typename T> __device__ __forceinline__ void opaque(T& x) { asm volatile("" : "+v"(x)); }
 
 // Inclusive prefix sum across a wave.
 __device__ __forceinline__ float wave_incl_scan(float x) {

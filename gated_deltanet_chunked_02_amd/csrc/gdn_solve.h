@@ -24,8 +24,7 @@ namespace gdn {
 constexpr int kAdLd = 17;  // leading dim of a diagonal block in sAd
 
 template <int NW, int C, typename TS>
-__device__ __forceinline__ void solve_diag_blocks(const float* sAd, TS* sM, int ldM) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ void solve_diag_blocks(const float* sAd, TS* sM, int ldM, int t) {
   if (t < C) {
     const int b = t >> 4, c = t & 15;
     const float* Ab = sAd + b * 16 * kAdLd;
@@ -49,13 +48,13 @@ __device__ __forceinline__ void solve_diag_blocks(const float* sAd, TS* sM, int 
 }
 
 template <int NW, int C, typename TS, int S>
-__device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int ldM) {
+__device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int ldM, int w,
+                                            int l) {
   constexpr int NB = S / 16;                 // 16-blocks per half of a merged pair
   constexpr int NJOBS = (C / (2 * S)) * NB;  // (pair, 16-column slice) jobs = C / 32
   constexpr int KS = Mma<TS>::KS;
   constexpr int KPL = Mma<TS>::KPL;
   typedef typename Mma<TS>::frag frag;
-  const int w = wave_id(), l = lane_id();
   for (int job = w; job < NJOBS; job += NW) {
     const int p = job / NB, J = job % NB;
     const int o = 2 * S * p;
@@ -66,7 +65,7 @@ __device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int l
     const int ncol = o + 16 * J + (l & 15);
     for (int k = o + 16 * J; k < o + S; k += KS) {
       const int kl = k + KPL * (l >> 4);
-      frag b = frag_ld<TS>(sM, ldM, o + 16 * J, k);  // row ncol of M: T^T above diagonal
+      frag b = frag_ld<TS>(sM, ldM, o + 16 * J, k, l);  // row ncol of M: T^T above diagonal
       if constexpr (KPL == 8) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -76,7 +75,7 @@ __device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int l
       }
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb) {
-        frag a = frag_ld<TS>(sA, ldA, o + S + 16 * kb, k);
+        frag a = frag_ld<TS>(sA, ldA, o + S + 16 * kb, k, l);
         if constexpr (KPL == 8) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -91,7 +90,7 @@ __device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int l
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
       f32x4 acc = zero4();
-      mma_accB<TS, NB, true>(acc, sM, ldM, o + S + 16 * I, o + S, y, I + 1, 0);
+      mma_accB<TS, NB, true>(acc, sM, ldM, o + S + 16 * I, o + S, y, I + 1, 0, l);
       const int R0 = o + S + 16 * I + 4 * (l >> 4);
       const int Cc = o + 16 * J + (l & 15);
 #pragma unroll
@@ -107,16 +106,18 @@ __device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int l
 
 // Full solve.  Precondition: sA / sAd written and visible (barrier done).  Ends with a
 // barrier, after which sM holds the result.
+// tid / w / l: thread, wave and lane index (passed in so callers can keep them opaque).
 template <int NW, int C, typename TS>
 __device__ __forceinline__ void solve_tril(const TS* sA, int ldA, const float* sAd, TS* sM,
-                                           int ldM) {
+                                           int ldM, int tid = threadIdx.x, int w = wave_id(),
+                                           int l = lane_id()) {
   static_assert(C == 64 || C == 128, "chunk size");
   static_assert(NW * kWave >= C, "one lane per diagonal-block column");
-  solve_diag_blocks<NW, C, TS>(sAd, sM, ldM);
+  solve_diag_blocks<NW, C, TS>(sAd, sM, ldM, tid);
   __syncthreads();
-  solve_level<NW, C, TS, 16>(sA, ldA, sM, ldM);
-  solve_level<NW, C, TS, 32>(sA, ldA, sM, ldM);
-  if constexpr (C == 128) solve_level<NW, C, TS, 64>(sA, ldA, sM, ldM);
+  solve_level<NW, C, TS, 16>(sA, ldA, sM, ldM, w, l);
+  solve_level<NW, C, TS, 32>(sA, ldA, sM, ldM, w, l);
+  if constexpr (C == 128) solve_level<NW, C, TS, 64>(sA, ldA, sM, ldM, w, l);
 }
 
 }  // namespace gdn
