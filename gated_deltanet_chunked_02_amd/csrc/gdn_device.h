@@ -204,6 +204,54 @@ __device__ __forceinline__ void mma_accB_n(f32x4* acc, const E* A, int lda, int 
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Software-pipelined form of the accumulator-fed contraction, for a run of NR output row
+// blocks that share the B tiles: the A fragments of row block r + 1 are loaded from LDS
+// before the matrix-core work of row block r is issued, so a single wave per SIMD keeps
+// its LDS latency hidden.
+template <typename E, int NPAIR>
+struct ARow {
+  typename Mma<E>::frag f[NPAIR];
+};
+
+// A fragments of one 16-row block: pair p covers k blocks 2p and 2p + 1 (only the first
+// `nkb` k blocks are real; the rest read as zero).
+template <typename E, int NPAIR>
+__device__ __forceinline__ void load_arow(ARow<E, NPAIR>& a, const E* A, int lda, int row0,
+                                          int koff, int nkb, int l) {
+  typedef typename Mma<E>::half half;
+  const E* p0 = A + (row0 + (l & 15)) * lda + koff + 4 * (l >> 4);
+#pragma unroll
+  for (int p = 0; p < NPAIR; ++p) {
+    half x0 = half{0, 0, 0, 0}, x1 = half{0, 0, 0, 0};
+    if (2 * p < nkb) x0 = *reinterpret_cast<const half*>(p0 + 32 * p);
+    if (2 * p + 1 < nkb) x1 = *reinterpret_cast<const half*>(p0 + 32 * p + 16);
+    a.f[p] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+//   acc[j * AJ] += A_row * B_j,  B_j block kb = Bt[j * BJ + kb * BK] (16-bit 4-vectors).
+template <typename E, int NPAIR, int NJ, int AJ, int BJ, int BK>
+__device__ __forceinline__ void mma_arow(f32x4* acc, const ARow<E, NPAIR>& a,
+                                         const typename Mma<E>::half* Bt, int nkb) {
+  typedef typename Mma<E>::half half;
+#pragma unroll
+  for (int p = 0; p < NPAIR; ++p) {
+    if (2 * p < nkb) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const half b0 = Bt[j * BJ + 2 * p * BK];
+        const half b1 = (2 * p + 1 < nkb) ? Bt[j * BJ + (2 * p + 1) * BK] : half{0, 0, 0, 0};
+        acc[j * AJ] = Mma<E>::mma(a.f[p], __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6,
+                                                                  7), acc[j * AJ]);
+      }
+    }
+  }
+}
+
+// Keep the scheduler from moving instructions across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // Make the compiler treat a value as changed here, so address arithmetic derived from it is
 // not hoisted out of a loop (and kept live across it).
 template <typename T> __device__ __forceinline__ void opaque(T& x) { asm volatile("" : "+v"(x)); }

@@ -14,7 +14,9 @@
 //   sAd [C/16][16][17] f32   A's diagonal blocks
 //   sM  [C][ldM] TS   result: M[i][j] = T[max(i,j)][min(i,j)], i.e. T = (I + A)^-1 below
 //                     and on the diagonal, T^T above it (both operand orientations in one
-//                     buffer; readers mask the half they do not want).
+//                     buffer; readers mask the half they do not want).  sM may be sA itself
+//                     (in place): A's diagonal blocks are not read from sA, and each
+//                     off-diagonal block of A is read in the level that overwrites it.
 #pragma once
 
 #include "gdn_device.h"
@@ -28,13 +30,27 @@ __device__ __forceinline__ void solve_diag_blocks(const float* sAd, TS* sM, int 
   if (t < C) {
     const int b = t >> 4, c = t & 15;
     const float* Ab = sAd + b * 16 * kAdLd;
+    // Forward substitution down column c; row i's entries are loaded two rows ahead so
+    // the dependent FMA chain does not wait on LDS.
     float x[16];
+    float ra[16], rb[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int m = 0; m < 16; ++m) {
+      ra[m] = m < 1 ? Ab[1 * kAdLd + m] : 0.f;
+      rb[m] = m < 2 ? Ab[2 * kAdLd + m] : 0.f;
+    }
+    x[0] = (c == 0) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
       float s = (i == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < i; ++m) s = fmaf(-Ab[i * kAdLd + m], x[m], s);
+      for (int m = 0; m < i; ++m) s = fmaf(-ra[m], x[m], s);
       x[i] = s;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        ra[m] = rb[m];
+        rb[m] = (i + 2 < 16 && m < i + 2) ? Ab[(i + 2) * kAdLd + m] : 0.f;
+      }
     }
     const int base = 16 * b;
 #pragma unroll
@@ -47,57 +63,74 @@ __device__ __forceinline__ void solve_diag_blocks(const float* sAd, TS* sM, int 
   }
 }
 
-template <int NW, int C, typename TS, int S>
+// One merge level: pairs of S x S inverse blocks become 2S x 2S blocks.  InPlace: sA and
+// sM are the same storage (A's off-diagonal blocks are overwritten by T's), so every
+// wave first reads its A21 blocks, then a barrier, then T21 is written.
+template <int NW, int C, typename TS, int S, bool InPlace>
 __device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int ldM, int w,
                                             int l) {
   constexpr int NB = S / 16;                 // 16-blocks per half of a merged pair
   constexpr int NJOBS = (C / (2 * S)) * NB;  // (pair, 16-column slice) jobs = C / 32
+  constexpr int JPW = (NJOBS + NW - 1) / NW;
   constexpr int KS = Mma<TS>::KS;
   constexpr int KPL = Mma<TS>::KPL;
   typedef typename Mma<TS>::frag frag;
-  for (int job = w; job < NJOBS; job += NW) {
-    const int p = job / NB, J = job % NB;
-    const int o = 2 * S * p;
-    // Y[:, J] = A21 T11[:, J]; T11 is lower, so k starts at the slice's first column.
-    f32x4 y[NB];
+  f32x4 y[JPW][NB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) y[kb] = zero4();
-    const int ncol = o + 16 * J + (l & 15);
-    for (int k = o + 16 * J; k < o + S; k += KS) {
-      const int kl = k + KPL * (l >> 4);
-      frag b = frag_ld<TS>(sM, ldM, o + 16 * J, k, l);  // row ncol of M: T^T above diagonal
-      if constexpr (KPL == 8) {
+  for (int jj = 0; jj < JPW; ++jj) {
+    const int job = w + jj * NW;
+    if (job < NJOBS) {
+      const int p = job / NB, J = job % NB;
+      const int o = 2 * S * p;
+      // Y[:, J] = A21 T11[:, J]; T11 is lower, so k starts at the slice's first column.
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (kl + e < ncol || kl + e >= o + S) b[e] = (TS)0.f;
-      } else {
-        if (kl < ncol || kl >= o + S) b = 0.f;
-      }
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb) {
-        frag a = frag_ld<TS>(sA, ldA, o + S + 16 * kb, k, l);
+      for (int kb = 0; kb < NB; ++kb) y[jj][kb] = zero4();
+      const int ncol = o + 16 * J + (l & 15);
+      for (int k = o + 16 * J; k < o + S; k += KS) {
+        const int kl = k + KPL * (l >> 4);
+        frag b = frag_ld<TS>(sM, ldM, o + 16 * J, k, l);  // row ncol of M: T^T above diagonal
         if constexpr (KPL == 8) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (kl + e >= o + S) a[e] = (TS)0.f;
+            if (kl + e < ncol || kl + e >= o + S) b[e] = (TS)0.f;
         } else {
-          if (kl >= o + S) a = 0.f;
+          if (kl < ncol || kl >= o + S) b = 0.f;
         }
-        y[kb] = Mma<TS>::mma(a, b, y[kb]);
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+          frag a = frag_ld<TS>(sA, ldA, o + S + 16 * kb, k, l);
+          if constexpr (KPL == 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (kl + e >= o + S) a[e] = (TS)0.f;
+          } else {
+            if (kl >= o + S) a = 0.f;
+          }
+          y[jj][kb] = Mma<TS>::mma(a, b, y[jj][kb]);
+        }
       }
     }
-    // T21[I, J] = -sum_{kb <= I} T22[I, kb] Y[kb, J]; T22 is read from M's lower half.
+  }
+  if constexpr (InPlace) __syncthreads();
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      f32x4 acc = zero4();
-      mma_accB<TS, NB, true>(acc, sM, ldM, o + S + 16 * I, o + S, y, I + 1, 0, l);
-      const int R0 = o + S + 16 * I + 4 * (l >> 4);
-      const int Cc = o + 16 * J + (l & 15);
+  for (int jj = 0; jj < JPW; ++jj) {
+    const int job = w + jj * NW;
+    if (job < NJOBS) {
+      const int p = job / NB, J = job % NB;
+      const int o = 2 * S * p;
+      // T21[I, J] = -sum_{kb <= I} T22[I, kb] Y[kb, J]; T22 is read from M's lower half.
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const TS val = (TS)(-acc[e]);
-        sM[(R0 + e) * ldM + Cc] = val;
-        sM[Cc * ldM + R0 + e] = val;
+      for (int I = 0; I < NB; ++I) {
+        f32x4 acc = zero4();
+        mma_accB<TS, NB, true>(acc, sM, ldM, o + S + 16 * I, o + S, y[jj], I + 1, 0, l);
+        const int R0 = o + S + 16 * I + 4 * (l >> 4);
+        const int Cc = o + 16 * J + (l & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const TS val = (TS)(-acc[e]);
+          sM[(R0 + e) * ldM + Cc] = val;
+          sM[Cc * ldM + R0 + e] = val;
+        }
       }
     }
   }
@@ -105,9 +138,9 @@ __device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int l
 }
 
 // Full solve.  Precondition: sA / sAd written and visible (barrier done).  Ends with a
-// barrier, after which sM holds the result.
-// tid / w / l: thread, wave and lane index (passed in so callers can keep them opaque).
-template <int NW, int C, typename TS>
+// barrier, after which sM holds the result.  tid / w / l: thread, wave and lane index
+// (passed in so callers can keep them opaque).  InPlace: sM == sA.
+template <int NW, int C, typename TS, bool InPlace = false>
 __device__ __forceinline__ void solve_tril(const TS* sA, int ldA, const float* sAd, TS* sM,
                                            int ldM, int tid = threadIdx.x, int w = wave_id(),
                                            int l = lane_id()) {
@@ -115,9 +148,9 @@ __device__ __forceinline__ void solve_tril(const TS* sA, int ldA, const float* s
   static_assert(NW * kWave >= C, "one lane per diagonal-block column");
   solve_diag_blocks<NW, C, TS>(sAd, sM, ldM, tid);
   __syncthreads();
-  solve_level<NW, C, TS, 16>(sA, ldA, sM, ldM, w, l);
-  solve_level<NW, C, TS, 32>(sA, ldA, sM, ldM, w, l);
-  if constexpr (C == 128) solve_level<NW, C, TS, 64>(sA, ldA, sM, ldM, w, l);
+  solve_level<NW, C, TS, 16, InPlace>(sA, ldA, sM, ldM, w, l);
+  solve_level<NW, C, TS, 32, InPlace>(sA, ldA, sM, ldM, w, l);
+  if constexpr (C == 128) solve_level<NW, C, TS, 64, InPlace>(sA, ldA, sM, ldM, w, l);
 }
 
 }  // namespace gdn
