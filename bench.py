@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline", choices=sorted(gdn_inputs.WORKLOADS))
     ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged"])
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="override the workload's chunk size C (64 or 128)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--mode", default="gdn", choices=["gdn", "copy"],
@@ -149,6 +151,8 @@ def main():
         copy_reference(args, dev)
         return
     w = gdn_inputs.WORKLOADS[args.workload]
+    if args.chunk:
+        w = w.with_(C=args.chunk)
     print("[bench] drawing %s on %s" % (w.name, dev), file=sys.stderr, flush=True)
     inp = gdn_inputs.draw(w, device=dev)
     q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))

@@ -43,12 +43,14 @@ namespace gdn {
 
 namespace {
 
-// 16-column state blocks per wave: 1 -> D/16 waves (two per SIMD, so one wave's LDS
-// latency is hidden behind the other's work); 2 -> D/32 waves with twice the registers.
+// 16-column state blocks per wave: 2 -> D/32 waves, one per SIMD with up to 512
+// registers (spill-free; every A fragment feeds two matrix-core instructions); 1 -> D/16
+// waves, two per SIMD with 256 registers each.
 #ifndef GDN_FUSED_NJ
 #define GDN_FUSED_NJ 2
 #endif
 constexpr int kFusedNJ = GDN_FUSED_NJ;
+
 
 template <int D, int C, int NJ_>
 struct FusedCfg {
@@ -84,22 +86,30 @@ __device__ __forceinline__ int swz(int r, int k) {
   return r * D + ((((k >> 3) ^ r) & (CPR - 1)) << 3) + (k & 7);
 }
 
+// Within a 16-row block (row0 % 16 == 0) the swizzle key of lane l's row is l % 16, so
+// the in-row offset of a k chunk depends on the lane only: swz(row0 + l%16, k) =
+// row0 * D + swz(l%16, k).
+template <int D>
+__device__ __forceinline__ int swz_lane(int l, int k) {
+  return swz<D>(l & 15, k);
+}
+
 // Standard 16-byte fragment (rows row0 + l%16, k0 + 8 (l/16) ...) of a swizzled tile.
 template <int D>
 __device__ __forceinline__ bf16x8 frag_swz(const bf16* m, int row0, int k0, int l) {
-  return *reinterpret_cast<const bf16x8*>(m + swz<D>(row0 + (l & 15), k0 + 8 * (l >> 4)));
+  return *reinterpret_cast<const bf16x8*>(m + row0 * D + swz_lane<D>(l, k0 + 8 * (l >> 4)));
 }
 
 // A-row fragments (accumulator-fed contraction form, see gdn_device.h) of a swizzled tile.
 template <int D, int NPAIR>
 __device__ __forceinline__ void load_arow_swz(ARow<bf16, NPAIR>& a, const bf16* m, int row0,
                                               int l) {
-  const int r = row0 + (l & 15);
   const int g4 = 4 * (l >> 4);
+  const bf16* mr = m + row0 * D;
 #pragma unroll
   for (int p = 0; p < NPAIR; ++p) {
-    const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(m + swz<D>(r, 32 * p + g4));
-    const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(m + swz<D>(r, 32 * p + 16 + g4));
+    const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(mr + swz_lane<D>(l, 32 * p + g4));
+    const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(mr + swz_lane<D>(l, 32 * p + 16 + g4));
     a.f[p] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
@@ -362,14 +372,15 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) x[j] = zero4();
         mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(x, a[tb & 1], &stb[0][0], NDK);
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + tb * 16 + g4);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(sB + tb * 16 + g4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = tb * 16 + g4 + e;
           const bf16* vp = S2 + swz<D>(t, dvl);
-          const float eg = sEG[t], bt = sB[t];
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            R[tb][j][e] = (bf16)(bt * ((float)vp[j] - eg * x[j][e]));
+            R[tb][j][e] = (bf16)(bt[e] * ((float)vp[j] - eg[e] * x[j][e]));
         }
         sched_fence();
       }
@@ -500,19 +511,21 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         for (int j = 0; j < NJ; ++j) y[j] = z[j] = zero4();
         mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(y, aq[tb & 1], &stb[0][0], NDK);
         mma_arow<bf16, NT / 2, NJ, 1, 1, NJ>(z, ap[tb & 1], &vn[0][0], tb + 1);
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + tb * 16 + g4);
+        bf16* op = o + ((long)(cs + tb * 16 + g4) * H + h) * D + dvl;
+        const long ostride = (long)H * D;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = tb * 16 + g4 + e;
-          if (t < len) {
-            const float eg = sEG[t];
-            bf16* op = o + ((long)(cs + t) * H + h) * D + dvl;
+          // full chunks store unconditionally (a uniform branch); a partial last chunk
+          // stores its valid rows only
+          if (len == C || tb * 16 + g4 + e < len) {
             if constexpr (NJ == 2) {
               bf16x2_t ov;
-              ov[0] = (bf16)(scale * fmaf(eg, y[0][e], z[0][e]));
-              ov[1] = (bf16)(scale * fmaf(eg, y[1][e], z[1][e]));
-              *reinterpret_cast<bf16x2_t*>(op) = ov;
+              ov[0] = (bf16)(scale * fmaf(eg[e], y[0][e], z[0][e]));
+              ov[1] = (bf16)(scale * fmaf(eg[e], y[1][e], z[1][e]));
+              *reinterpret_cast<bf16x2_t*>(op + e * ostride) = ov;
             } else {
-              *op = (bf16)(scale * fmaf(eg, y[0][e], z[0][e]));
+              op[e * ostride] = (bf16)(scale * fmaf(eg[e], y[0][e], z[0][e]));
             }
           }
         }

@@ -26,8 +26,17 @@ namespace gdn {
 constexpr int kAdLd = 17;  // leading dim of a diagonal block in sAd
 
 template <int NW, int C, typename TS>
+__device__ __forceinline__ void solve_diag_column(const float* sAd, TS* sM, int ldM, int t);
+
+// Inverse of each 16 x 16 diagonal block, one column per thread t < C.
+template <int NW, int C, typename TS>
 __device__ __forceinline__ void solve_diag_blocks(const float* sAd, TS* sM, int ldM, int t) {
-  if (t < C) {
+  if (t < C) solve_diag_column<NW, C, TS>(sAd, sM, ldM, t);
+}
+
+template <int NW, int C, typename TS>
+__device__ __forceinline__ void solve_diag_column(const float* sAd, TS* sM, int ldM, int t) {
+  {
     const int b = t >> 4, c = t & 15;
     const float* Ab = sAd + b * 16 * kAdLd;
     // Forward substitution down column c; row i's entries are loaded two rows ahead so
@@ -111,7 +120,7 @@ __device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int l
       }
     }
   }
-  if constexpr (InPlace) __syncthreads();
+  if constexpr (InPlace && NW > 1) __syncthreads();
 #pragma unroll
   for (int jj = 0; jj < JPW; ++jj) {
     const int job = w + jj * NW;
@@ -134,7 +143,7 @@ __device__ __forceinline__ void solve_level(const TS* sA, int ldA, TS* sM, int l
       }
     }
   }
-  __syncthreads();
+  if constexpr (NW > 1) __syncthreads();
 }
 
 // Full solve.  Precondition: sA / sAd written and visible (barrier done).  Ends with a
