@@ -28,10 +28,42 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 F32_PEAK_TFLOPS = 157.3
 
-# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE for the fused kernel on the headline workload
-# (KiB per dispatch), and the same counters for a plain copy of known size (calibration):
-# filled in from profiles/ once measured; None until then.
-PMC_TRAFFIC = None
+# HBM bytes of the fused kernel on the 16x8192, H=32, D=128, C=128 workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+# same counter reads for a plain 1 GiB device copy (FETCH_SIZE reads 0.5 GiB there, so x2;
+# WRITE_SIZE reads 1 GiB, so x1).  The figures hold only for the kernel sources they were
+# taken on: SOURCES_SHA256 is checked against the current files and traffic reports null
+# once they differ.
+PMC_TRAFFIC = {
+    "workload": "bf16_16x8192_h32_d128_c128",
+    "fetch_kib": 1671541.85, "write_kib": 1081344.02,
+    "fetch_scale": 2.0, "write_scale": 1.0,
+    "sources_sha256": "dc273a6b5b2703d198b3e305538fc081eb41a36a17b7c79d114a6ad9c9721cab",
+}
+FUSED_SOURCES = ("fused.hip", "gdn_device.h", "gdn_solve.h")
+
+
+def fused_sources_sha256() -> str:
+    """sha256 over the sha256sum-style listing of the fused kernel's sources (the same
+    digest as `sha256sum fused.hip gdn_device.h gdn_solve.h | sha256sum` run from the
+    repository root with the package-relative paths)."""
+    import hashlib
+    lines = []
+    for fn in FUSED_SOURCES:
+        rel = "gated_deltanet_chunked_02_amd/csrc/" + fn
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            lines.append("%s  %s\n" % (hashlib.sha256(f.read()).hexdigest(), rel))
+    return hashlib.sha256("".join(lines).encode()).hexdigest()
+
+
+def pmc_traffic(workload: str, variant: str):
+    """Scaled HBM bytes per launch, or None when no counters match this kernel build."""
+    t = PMC_TRAFFIC
+    if t is None or variant != "fused" or workload != t["workload"]:
+        return None
+    if fused_sources_sha256() != t["sources_sha256"]:
+        return None
+    return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
 
 
 def algorithmic_work(inp):
@@ -208,7 +240,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": tfl, "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": tfl / peak_tf}
-    roof["traffic"] = PMC_TRAFFIC
+    roof["traffic"] = pmc_traffic(w.name, variant)
     roof["kernel"] = kernel
     roof["launch_ms"] = avg_ms
     roof["algorithmic_bytes"] = by

@@ -4,11 +4,22 @@
 
 Each translation unit is compiled separately (in parallel) into ``_build/`` and linked
 into ``gated_deltanet_chunked_02_amd/libgdn.so``, next to the binding that loads it.
+
+The gfx950 assembly of every HIP source is also generated and checked; two patterns fail
+the build because both were seen to give wrong sums on gfx950 while the compiler inserted
+no wait states for them:
+  * a matrix-core instruction whose destination registers partly overlap its accumulator
+    input (e.g. ``v_mfma_... a[2:5], ..., a[4:7]``): correct code accumulates in place or
+    into disjoint registers;
+  * an accumulator input produced a few instructions earlier by a matrix-core instruction
+    of a different shape (e.g. 16x16x32 then 16x16x16 on the same tile): accumulation
+    chains keep one instruction shape.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,7 +45,57 @@ def flags():
             "-Wno-unused-function",
             # keep packed-fp32 VALU forms out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # LLVM's iterative ILP scheduler: under it the register allocator gives every
+            # matrix-core accumulation either the same or disjoint destination registers
+            # (checked on the assembly below)
+            "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+_MFMA = re.compile(r"^\s*(v_mfma\S*)\s+([av])\[(\d+):(\d+)\],\s*[^,]+,\s*[^,]+,\s*"
+                   r"([av])\[(\d+):(\d+)\]")
+
+
+def mfma_partial_overlaps(asm: str):
+    """(line number, text) of every matrix-core instruction whose destination register range
+    partly overlaps its accumulator-input range (same register file, not identical)."""
+    bad = []
+    for n, line in enumerate(asm.splitlines(), 1):
+        m = _MFMA.match(line)
+        if not m:
+            continue
+        _, df, d0, d1, cf_, c0, c1 = m.groups()
+        d0, d1, c0, c1 = int(d0), int(d1), int(c0), int(c1)
+        if df == cf_ and (d0, d1) != (c0, c1) and d0 <= c1 and c0 <= d1:
+            bad.append((n, line.strip()))
+    return bad
+
+
+_MFMA_DST = re.compile(r"^\s*(v_mfma\S*)\s+([av])\[(\d+):(\d+)\],")
+
+
+def mfma_mixed_chains(asm: str, window: int = 16):
+    """(line number, text) of every matrix-core instruction whose accumulator input is the
+    destination of a matrix-core instruction of another opcode at most `window`
+    instructions earlier (labels, directives and comments not counted)."""
+    bad = []
+    last = {}
+    k = 0
+    for n, line in enumerate(asm.splitlines(), 1):
+        t = line.strip()
+        if not t or t.startswith((";", ".")) or t.endswith(":"):
+            continue
+        k += 1
+        m = _MFMA.match(line)
+        if m:
+            op, _, _, _, cf_, c0, c1 = m.groups()
+            prev = last.get((cf_, int(c0), int(c1)))
+            if prev is not None and k - prev[0] <= window and prev[1] != op:
+                bad.append((n, t))
+        d = _MFMA_DST.match(line)
+        if d:
+            last[(d.group(2), int(d.group(3)), int(d.group(4)))] = (k, d.group(1))
+    return bad
 
 
 def _compile(src: str) -> str:
@@ -43,6 +104,23 @@ def _compile(src: str) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))
+    if src.endswith(".hip"):
+        asm = os.path.join(BUILD, os.path.splitext(src)[0] + "." + ARCH + ".s")
+        cmd = [hipcc()] + flags() + ["--cuda-device-only", "-S", os.path.join(CSRC, src),
+                                     "-o", asm]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc -S failed for %s:\n%s" % (src, res.stderr))
+        with open(asm) as f:
+            text = f.read()
+        for check, what in ((mfma_partial_overlaps, "partly overlapping destination and "
+                             "accumulator registers"),
+                            (mfma_mixed_chains, "an accumulator input from a matrix-core "
+                             "instruction of another shape just before")):
+            bad = check(text)
+            if bad:
+                raise RuntimeError("%s: %d matrix-core instruction(s) with %s, e.g. %s:%d: %s"
+                                   % (src, len(bad), what, asm, bad[0][0], bad[0][1]))
     return obj
 
 

@@ -4,78 +4,72 @@
 //
 // One workgroup owns one (sequence, value head) and walks its chunks in order; nothing
 // crosses workgroups, so no grid barrier is needed (the page's all-core SyncAll barrier
-// has no counterpart here).  D/32 waves, one per SIMD with a 512-register budget; wave w
-// owns 32 state columns as two 16-wide matrix-core column blocks, for all Dk rows, kept as
-// fp32 accumulator tiles, so the recurrent chain K h -> R -> T R -> (o, h) never leaves
-// registers and every A-operand fragment feeds two matrix-core instructions.  Column c of
-// block j of wave w is state column dv = 32 w + 2 c + j, so each lane's two columns are
-// adjacent in memory (4-byte V / o and 8-byte h0 / ht accesses).  Per chunk, with G the
-// in-chunk prefix sum of g:
+// has no counterpart here).  D/32 waves, one per SIMD; wave w owns 32 state columns as two
+// 16-wide matrix-core column blocks, for all Dk rows, kept as fp32 accumulator tiles.
+// Column c of block j of wave w is state column dv = 32 w + 2 c + j, so each lane's two
+// columns are adjacent in memory (4-byte V / o and 8-byte h0 / ht accesses).  Per chunk,
+// with G the in-chunk prefix sum of g and h the state at the chunk start:
 //
-//   A    = (K K^T) * beta_i e^{G_i-G_j}, i > j            (scaled_dot_kkt, section 4.2)
-//   T    = (I + A)^-1                                      (solve_tril, section 4.4)
-//   R    = diag(beta) (V - diag(e^G) K h)                  (wy_fast + chunk_h, 4.3):
-//   v_new = T R  = U - W h                                  T applied once to V - e^G K h
-//   o    = scale (diag(e^G) Q h + (Q K^T * e^{G_i-G_j})_{i>=j} v_new)       (chunk_o)
-//   h    = e^{G_last} h + K^T (e^{G_last-G} v_new)          (chunk_h, TileLang page step 1)
+//   A     = (K K^T) * beta_i e^{G_i-G_j}, i > j             (scaled_dot_kkt, section 4.2)
+//   R     = diag(beta) (V - diag(e^G) K h)                   (wy_fast + chunk_h, 4.3)
+//   (I + A) v_new = R                                        (solve_tril, 4.4, applied)
+//   o     = scale (diag(e^G) Q h + (Q K^T * e^{G_i-G_j})_{i>=j} v_new)        (chunk_o)
+//   h     = e^{G_last} h + K^T (e^{G_last-G} v_new)          (chunk_h, TileLang page step 1)
 //
-// Applying T to (V - e^G K h) instead of forming W = T diag(beta e^G) K and U = T diag(beta)
-// V separately is exact algebra (v_new = U - W h) and saves the C x C x Dk product W.
+// (I + A) v_new = R is the same as v_new = U - W h with U = T diag(beta) V, W = T diag(beta
+// e^G) K and T = (I + A)^-1, but T is never formed: each wave solves for its own 32 columns
+// by blocked forward substitution over the C/16 token blocks,
 //
-// LDS: four slabs re-used by phase —
-//   S0: K            -> A (fp16, off-diagonal blocks) -> T (solved in place; bf16, lower)
-//   S1: Q                                (read again for Q h in the output phase)
-//   S2: V            -> P = gated, masked Q K^T (bf16)
-//   S3: K^T scaled by e^{G_last - G}
-// plus the fp32 diagonal blocks of A and the chunk's gate vectors (G, e^G, beta,
-// e^{G_last-G}), which wave 0 computes for the next chunk at the end of the current one
-// (double-buffered).  The next chunk's K, Q and V are copied from HBM straight into their
-// slabs (global_load_lds, no register staging) as soon as the current chunk is done with
-// each slab: K after T R, Q and V after the output.  K, Q, V rows are unpadded with the
-// 16-byte chunk index XOR-swizzled by the row, which keeps fragment reads conflict-free
-// and matches the lane order of the direct-to-LDS copy.  R and v_new live in registers in
-// the bf16 form in which they feed the matrix cores.
+//   v_i = T_ii (R_i - sum_{j<i} A_ij v_j),   T_ii = (I + A_ii)^-1,
+//
+// where the 16 x 16 diagonal inverses come from the nilpotent product
+// (I + A_ii)^-1 = (I - A_ii)(I + A_ii^2)(I + A_ii^4)(I + A_ii^8) on the matrix cores.  The
+// solve therefore needs no barrier and no cross-wave data beyond A, and each token block's
+// output and state-update contribution are issued as soon as its v_i is known.
+//
+// Two phases and three barriers per chunk:
+//   P1  lower tiles of K Q^T and K K^T -> P and -A in LDS (packed fp16 16 x 16 tiles; the
+//       owner of a diagonal tile replaces it with T_ii); R and Y = Q h for this wave's
+//       columns into registers (fp32).  Barrier.  Q and V are now dead: the next chunk's
+//       Q and V are copied HBM -> LDS directly (global_load_lds) and its K is loaded into
+//       registers, all landing while P2 runs.
+//   P2  substitution, o = scale (e^G Y + P v_new) and h += K^T (d v_new) block by block
+//       (K^T fragments by transposing LDS reads).  Barrier; the prefetched K is written to
+//       LDS, wave 0 prepares the next chunk's gate vectors; barrier.
+// K, Q, V rows are unpadded with the 16-byte chunk index XOR-swizzled by the row, which
+// keeps fragment reads conflict-free and matches the lane order of the direct-to-LDS copy.
 #include "gdn_device.h"
 #include "gdn_internal.h"
-#include "gdn_solve.h"
 
 namespace gdn {
 
 namespace {
 
-// 16-column state blocks per wave: 2 -> D/32 waves, one per SIMD with up to 512
-// registers (spill-free; every A fragment feeds two matrix-core instructions); 1 -> D/16
-// waves, two per SIMD with 256 registers each.
-#ifndef GDN_FUSED_NJ
-#define GDN_FUSED_NJ 2
-#endif
-constexpr int kFusedNJ = GDN_FUSED_NJ;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-
-template <int D, int C, int NJ_>
+template <int D, int C>
 struct FusedCfg {
-  static constexpr int NJ = NJ_;          // 16-column blocks per wave
+  static constexpr int NJ = 2;              // 16-column state blocks per wave
   static constexpr int NW = D / (16 * NJ);  // waves
-  static constexpr int NTH = NW * kWave;  // = 4 D / NJ (the launch bound)
-  static constexpr int NT = C / 16;       // token blocks per chunk
-  static constexpr int NDK = D / 16;      // key blocks
-  static constexpr int CPR = D / 8;       // 16-byte pieces per q/k/v row
-  static constexpr int LDC = C + 8;       // row of a [*][C] 16-bit operand (A, T, P)
-  static constexpr int LDT = C + 12;      // row of K^T (8-byte reads; spreads the writes)
-  static constexpr int SLAB_TILE = C * D;                                    // swizzled rows
-  static constexpr int SLAB_SQ = C * LDC;                                    // padded C x C
-  static constexpr int SLAB = SLAB_TILE > SLAB_SQ ? SLAB_TILE : SLAB_SQ;    // elements
-  static constexpr int KT = D * LDT;
-  static constexpr int RPI = 1024 / (2 * D);        // rows per direct-to-LDS instruction
-  static constexpr int NDMA = C / RPI / NW;         // such instructions per wave per tile
+  static constexpr int NTH = NW * kWave;    // = 2 D (the launch bound)
+  static constexpr int NT = C / 16;         // token blocks per chunk
+  static constexpr int NDK = D / 16;        // key blocks
+  static constexpr int CPR = D / 8;         // 16-byte pieces per q/k/v row
+  static constexpr int TILE = C * D;        // elements of a swizzled [C][D] bf16 tile
+  static constexpr int RS = 20;             // row stride (elements) of a packed fp16 tile
+  static constexpr int TE = 16 * RS;        // elements per packed 16 x 16 tile
   static constexpr int NLOW = NT * (NT + 1) / 2;
   static constexpr int MAXT = (NT == 2 * NW) ? NT + 1 : (NLOW + NW - 1) / NW;
+  static constexpr int RPI = 1024 / (2 * D);        // rows per direct-to-LDS instruction
+  static constexpr int NDMA = C / RPI / NW;         // such instructions per wave per tile
+  static constexpr int KPL = C * CPR / NTH;         // 16-byte pieces of K per lane
   static constexpr int TPL = C / kWave;             // tokens per lane in the gate scan
   static constexpr int GATES = 2 * 4 * C;           // [2][4][C] G, e^G, beta, e^{G_last-G}
+  static_assert(NT % 2 == 0, "token blocks pair up");
   static_assert(NDMA * NW * RPI == C, "tile covered by whole copy instructions");
+  static_assert(KPL * NTH == C * CPR, "K tile covered by whole 16-byte loads");
   static constexpr size_t lds_bytes() {
-    return (size_t)(3 * SLAB + KT) * 2 + (size_t)GATES * 4 + 2 * 4 +
-           (size_t)(C / 16) * 16 * kAdLd * 4 + 8;
+    return (size_t)3 * TILE * 2 + (size_t)2 * NLOW * TE * 2 + (size_t)GATES * 4 + 16;
   }
 };
 
@@ -220,20 +214,63 @@ __device__ __forceinline__ bool has_tile(int w, int u) {
   return w + NW * u < NLOW;
 }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)b) << 16);
+
+// Packed lower-triangular storage of 16 x 16 fp16 tiles: tile (ti, tj), tj <= ti, row r,
+// column c at tix(ti, tj) + r * RS + c.  RS = 20 puts the 16 rows that one 4-element
+// fragment access touches on distinct bank pairs.
+template <class F>
+__device__ __forceinline__ int tix(int ti, int tj) {
+  return (ti * (ti + 1) / 2 + tj) * F::TE;
 }
 
-template <int D, int C, int NJ_>
-__global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
+__device__ __forceinline__ f32x4 mma16h(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 cat8h(f16x4 a, f16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 mma32h(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// One 16-token block through the 32-deep instruction (upper half zero), so that an
+// accumulation chain never switches instruction shape between dependent steps.
+__device__ __forceinline__ f32x4 mma32h1(f16x4 a, f16x4 b, f32x4 c) {
+  const f16x4 z = {0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(cat8h(a, z), cat8h(b, z), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32b(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+template <typename V4>
+__device__ __forceinline__ auto cat8(V4 a, V4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f16x4 to_h(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+__device__ __forceinline__ bf16x4 to_b(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane c
+// receives element e = element c % 4 of the 8 bytes that lane 4 e + c / 4 of the group
+// addressed.  So if lane c of group g addresses row (R0 + 4 g + c / 4), columns
+// (C0 + 4 (c % 4)) .. + 3 of a row-major 16-bit matrix M, lane c receives
+// M[R0 + 4 g + e][C0 + c], e = 0..3: a column of M, the k-contiguous operand form of M^T.
+template <typename V4>
+__device__ __forceinline__ V4 read_tr(const void* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(V4, r);
+}
+
+// Order this wave's earlier LDS writes before its later LDS reads of the same data.
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int D, int C>
+__global__ __launch_bounds__(D * 2) void k_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const void* __restrict__ beta, int beta_f32,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, bf16* __restrict__ o,
     float* __restrict__ ht, int T, int Ttot, int H, int Hg, float scale) {
-  typedef FusedCfg<D, C, NJ_> F;
-  constexpr int NT = F::NT, NDK = F::NDK, NJ = F::NJ, LDC = F::LDC, LDT = F::LDT,
-                TPL = F::TPL, CPR = F::CPR;
+  typedef FusedCfg<D, C> F;
+  constexpr int NT = F::NT, NDK = F::NDK, NJ = F::NJ, RS = F::RS, CPR = F::CPR;
   const int n = blockIdx.x / H, h = blockIdx.x - n * H;
   const int hk = h / (H / Hg);
   const long qstride = (long)Hg * D, vstride = (long)H * D;
@@ -242,21 +279,19 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
   const bf16* vh = v + (long)h * D;
 
   extern __shared__ __align__(16) char smem[];
-  bf16* S0 = reinterpret_cast<bf16*>(smem);
-  bf16* S1 = S0 + F::SLAB;
-  bf16* S2 = S1 + F::SLAB;
-  bf16* S3 = S2 + F::SLAB;
-  float* sGates = reinterpret_cast<float*>(S3 + F::KT);  // [2][4][C]
-  float* sMisc = sGates + F::GATES;                       // [2]: e^{G_last}
-  float* sAd = sMisc + 2;
-  f16* A16 = reinterpret_cast<f16*>(S0);
+  bf16* SK = reinterpret_cast<bf16*>(smem);
+  bf16* SQ = SK + F::TILE;
+  bf16* SV = SQ + F::TILE;
+  f16* SA = reinterpret_cast<f16*>(SV + F::TILE);  // -A below the diagonal, T_ii on it
+  f16* SP = SA + F::NLOW * F::TE;                   // P = (Q K^T * e^{G_i-G_j})_{i>=j}
+  float* sGates = reinterpret_cast<float*>(SP + F::NLOW * F::TE);  // [2][4][C]
+  float* sMisc = sGates + F::GATES;                                  // [2]: e^{G_last}
 
   int cs0, L;
   seq_span(cu, n, T, Ttot, cs0, L);
   const int nchunks = (L + C - 1) / C;
 
-  // State: st[j][db] holds rows dk = 16 db + 4 (l/16) + e of column
-  // 16 NJ w + NJ (l%16) + j.
+  // State: st[j][db] holds rows dk = 16 db + 4 (l/16) + e of column 32 w + 2 (l%16) + j.
   f32x4 st[NJ][NDK];
   const long hoff = ((long)n * H + h) * D * D;
   {
@@ -276,20 +311,19 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
             st[j][db][e] = h0[hoff + (long)(16 * db + g4 + e) * D + dv0 + j];
     }
   }
-  // bf16 copy of the state in the B-operand form of the K h, Q h products, refreshed once
-  // per chunk after the state update.
+  // bf16 copy of the chunk-start state in the B-operand form of the K h and Q h products.
   bf16x4 stb[NJ][NDK];
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int db = 0; db < NDK; ++db) stb[j][db] = __builtin_convertvector(st[j][db], bf16x4);
+    for (int db = 0; db < NDK; ++db) stb[j][db] = to_b(st[j][db]);
 
-  float pg[TPL], pb[TPL];
+  float pg[F::TPL], pb[F::TPL];
   if (nchunks > 0) {
     const int len0 = min(C, L), l = lane_id(), w = wave_id();
-    dma_tile<F, D>(S0, kh + (long)cs0 * qstride, qstride, len0, w, l);
-    dma_tile<F, D>(S1, qh + (long)cs0 * qstride, qstride, len0, w, l);
-    dma_tile<F, D>(S2, vh + (long)cs0 * vstride, vstride, len0, w, l);
+    dma_tile<F, D>(SK, kh + (long)cs0 * qstride, qstride, len0, w, l);
+    dma_tile<F, D>(SQ, qh + (long)cs0 * qstride, qstride, len0, w, l);
+    dma_tile<F, D>(SV, vh + (long)cs0 * vstride, vstride, len0, w, l);
     if (w == 0) {
       load_gates<C>(pg, pb, g, beta, beta_f32, cs0, len0, h, H, l);
       chunk_gates<C>(sGates, sMisc, pg, pb, len0, l);
@@ -297,9 +331,9 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed
     if (len0 < C) {
       __syncthreads();
-      zero_tail<F, C>(S0, len0, threadIdx.x);
-      zero_tail<F, C>(S1, len0, threadIdx.x);
-      zero_tail<F, C>(S2, len0, threadIdx.x);
+      zero_tail<F, C>(SK, len0, threadIdx.x);
+      zero_tail<F, C>(SQ, len0, threadIdx.x);
+      zero_tail<F, C>(SV, len0, threadIdx.x);
     }
   }
   __syncthreads();
@@ -315,261 +349,243 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     // Lane / wave / thread ids are re-derived opaquely at every phase, so the compiler
     // computes each phase's many LDS addresses inside that phase instead of holding them
     // in registers across the chunk.
-    int tid, l, w, g4, dvl;
+    int tid, l, w, g4, r16, dvl;
     auto phase = [&]() {
       tid = threadIdx.x;
       opaque(tid);
       l = tid & 63;
       w = __builtin_amdgcn_readfirstlane(tid >> 6);
       g4 = 4 * (l >> 4);
-      dvl = 16 * NJ * w + NJ * (l & 15);  // this lane's first state column
+      r16 = l & 15;
+      dvl = 16 * NJ * w + NJ * r16;  // this lane's first state column
     };
     phase();
 
-    // (A) K^T scaled by e^{G_last - G} (the weight the state update gives v_new) into S3,
-    // from the K tile in S0; token pairs are packed into 4-byte writes.
-    for (int i = tid; i < (C / 2) * CPR; i += F::NTH) {
-      const int tp = i / CPR, c8 = (i - tp * CPR) * 8, t = 2 * tp;
-      const float d0 = sDec[t], d1 = sDec[t + 1];
-      union {
-        uint4 u;
-        bf16 e[8];
-      } k0, k1;
-      k0.u = *reinterpret_cast<const uint4*>(S0 + swz<D>(t, c8));
-      k1.u = *reinterpret_cast<const uint4*>(S0 + swz<D>(t + 1, c8));
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint32_t*>(S3 + (c8 + e) * LDT + t) =
-            pack2(d0 * (float)k0.e[e], d1 * (float)k1.e[e]);
-    }
-
-    phase();
-    // (D1) K Q^T lower tiles (transposed orientation: rows j, columns i) and
-    // R = beta (V - e^G K h) for this wave's columns, kept as the bf16 operand it becomes.
-    f32x4 pacc[F::MAXT];
+    // ---- P1 (a): this wave's lower 16 x 16 tiles of K Q^T and K K^T.  Tile (ti, tj) in
+    // accumulator form holds, in lane l, row i = 16 ti + l%16 and columns j = 16 tj + 4
+    // (l/16) + e: the k-contiguous operand form of that row of P and A.
 #pragma unroll
     for (int u = 0; u < F::MAXT; ++u) {
-      pacc[u] = zero4();
       if (has_tile<NT, F::NW>(w, u)) {
         int ti, tj;
         lower_tile<NT, F::NW>(w, u, ti, tj);
+        f32x4 pa = zero4(), aa = zero4();
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-          pacc[u] = Mma<bf16>::mma(frag_swz<D>(S0, tj * 16, 32 * kk, l),
-                                   frag_swz<D>(S1, ti * 16, 32 * kk, l), pacc[u]);
+        for (int kk = 0; kk < D / 32; ++kk) {
+          const bf16x8 kf = frag_swz<D>(SK, tj * 16, 32 * kk, l);
+          pa = Mma<bf16>::mma(kf, frag_swz<D>(SQ, ti * 16, 32 * kk, l), pa);
+          aa = Mma<bf16>::mma(kf, frag_swz<D>(SK, ti * 16, 32 * kk, l), aa);
+        }
+        const int i = ti * 16 + r16, j0 = tj * 16 + g4;
+        const float Gi = sG[i], nbi = -sB[i];
+        const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
+        f32x4 pf, nf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // masked entries use a clamped exponent, so they never overflow
+          const float dec = __expf(fminf(Gi - Gj[e], 0.f));
+          pf[e] = (i >= j0 + e ? dec : 0.f) * pa[e];
+          nf[e] = (i > j0 + e ? nbi * dec : 0.f) * aa[e];
+        }
+        *reinterpret_cast<f16x4*>(SP + tix<F>(ti, tj) + r16 * RS + g4) = to_h(pf);
+        f16* at = SA + tix<F>(ti, tj);
+        const f16x4 nt = to_h(nf);
+        *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = nt;
+        if (ti == tj) {
+          // T_ii = (I + N + N^2 + ... + N^15) = (I + N)(I + N^2)(I + N^4)(I + N^8) with
+          // N = -A_ii strictly lower.  nt is N^T in accumulator form; N itself is read back
+          // transposed.  A product X Y takes X^T and Y in accumulator form, so both
+          // orientations of each power are kept; the result is built as T^T, whose
+          // accumulator form is the row-major storage of T.
+          lds_fence();
+          const f16x4 nn = read_tr<f16x4>(at + (g4 + (r16 >> 2)) * RS + 4 * (r16 & 3));
+          f32x4 eye;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) eye[e] = (g4 + e == r16) ? 1.f : 0.f;
+          const f32x4 n2 = mma16h(nt, nn, zero4());     // N^2
+          const f32x4 n2t = mma16h(nn, nt, zero4());    // (N^2)^T
+          const f16x4 h2 = to_h(n2), h2t = to_h(n2t);
+          const f32x4 n4 = mma16h(h2t, h2, zero4());    // N^4
+          const f32x4 n4t = mma16h(h2, h2t, zero4());   // (N^4)^T
+          const f16x4 h4 = to_h(n4), h4t = to_h(n4t);
+          const f16x4 h8 = to_h(mma16h(h4t, h4, zero4()));  // N^8
+          // Y1 = (I + N^2)^T (I + N)^T = I + N^T + (N^2)^T + (N^2)^T N^T
+          const f32x4 y1 = mma16h(h2, nt, eye + nf + n2t);
+          const f32x4 y2 = mma16h(h4, to_h(y1), y1);    // (I + (N^4)^T) Y1
+          const f32x4 y3 = mma16h(h8, to_h(y2), y2);    // (I + (N^8)^T) Y2 = T_ii^T
+          *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(y3);
+        }
       }
       sched_fence();
     }
-    bf16x4 R[NT][NJ];
+
+    // ---- P1 (b): R = beta (V - e^G K h) and Y = Q h for this wave's columns (fp32).
+    phase();
+    f32x4 R[NT][NJ], Y[NT][NJ];
     {
-      ARow<bf16, NDK / 2> a[2];
-      load_arow_swz<D, NDK / 2>(a[0], S0, 0, l);
+      ARow<bf16, NDK / 2> ak[2], aq[2];
+      load_arow_swz<D, NDK / 2>(ak[0], SK, 0, l);
+      load_arow_swz<D, NDK / 2>(aq[0], SQ, 0, l);
 #pragma unroll
       for (int tb = 0; tb < NT; ++tb) {
-        if (tb + 1 < NT) load_arow_swz<D, NDK / 2>(a[(tb + 1) & 1], S0, (tb + 1) * 16, l);
+        if (tb + 1 < NT) {
+          load_arow_swz<D, NDK / 2>(ak[(tb + 1) & 1], SK, (tb + 1) * 16, l);
+          load_arow_swz<D, NDK / 2>(aq[(tb + 1) & 1], SQ, (tb + 1) * 16, l);
+        }
         sched_fence();
         f32x4 x[NJ];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) x[j] = zero4();
-        mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(x, a[tb & 1], &stb[0][0], NDK);
+        for (int j = 0; j < NJ; ++j) x[j] = Y[tb][j] = zero4();
+        mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(x, ak[tb & 1], &stb[0][0], NDK);
+        mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(Y[tb], aq[tb & 1], &stb[0][0], NDK);
         const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + tb * 16 + g4);
         const f32x4 bt = *reinterpret_cast<const f32x4*>(sB + tb * 16 + g4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = tb * 16 + g4 + e;
-          const bf16* vp = S2 + swz<D>(t, dvl);
+          const bf16* vp = SV + swz<D>(tb * 16 + g4 + e, dvl);
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            R[tb][j][e] = (bf16)(bt[e] * ((float)vp[j] - eg[e] * x[j][e]));
+          for (int j = 0; j < NJ; ++j) R[tb][j][e] = bt[e] * ((float)vp[j] - eg[e] * x[j][e]);
         }
         sched_fence();
       }
     }
-    __syncthreads();  // V consumed; K^T written
 
-    phase();
-    // (D2) P -> S2 (bf16); K K^T lower tiles.
-#pragma unroll
-    for (int u = 0; u < F::MAXT; ++u) {
-      if (has_tile<NT, F::NW>(w, u)) {
-        int ti, tj;
-        lower_tile<NT, F::NW>(w, u, ti, tj);
-        const int i = ti * 16 + (l & 15);
-        const int j0 = tj * 16 + g4;
-        const float Gi = sG[i];
-        const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
-        bf16x4 pv4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float dec = __expf(fminf(Gi - Gj[e], 0.f));
-          pv4[e] = (bf16)((i >= j0 + e) ? dec * pacc[u][e] : 0.f);
-        }
-        *reinterpret_cast<bf16x4*>(S2 + i * LDC + j0) = pv4;
-      }
-    }
-    f32x4 aacc[F::MAXT];
-#pragma unroll
-    for (int u = 0; u < F::MAXT; ++u) {
-      aacc[u] = zero4();
-      if (has_tile<NT, F::NW>(w, u)) {
-        int ti, tj;
-        lower_tile<NT, F::NW>(w, u, ti, tj);
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-          aacc[u] = Mma<bf16>::mma(frag_swz<D>(S0, tj * 16, 32 * kk, l),
-                                   frag_swz<D>(S0, ti * 16, 32 * kk, l), aacc[u]);
-      }
-      sched_fence();
-    }
-    __syncthreads();  // K consumed
-
-    phase();
-    // (E) A -> S0 (fp16; diagonal blocks fp32 in sAd).
-#pragma unroll
-    for (int u = 0; u < F::MAXT; ++u) {
-      if (has_tile<NT, F::NW>(w, u)) {
-        int ti, tj;
-        lower_tile<NT, F::NW>(w, u, ti, tj);
-        const int i = ti * 16 + (l & 15);
-        const int j0 = tj * 16 + g4;
-        const float Gi = sG[i], bi = sB[i];
-        const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
-        f32x4 a4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float dec = __expf(fminf(Gi - Gj[e], 0.f));
-          a4[e] = (i > j0 + e) ? bi * dec * aacc[u][e] : 0.f;
-        }
-        if (ti == tj) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sAd[ti * 16 * kAdLd + (i & 15) * kAdLd + ((j0 + e) & 15)] = a4[e];
-        } else {
-          *reinterpret_cast<f16x4*>(A16 + i * LDC + j0) = __builtin_convertvector(a4, f16x4);
-        }
-      }
-    }
-    __syncthreads();  // A written
-
-    phase();
-    // (F) T = (I + A)^-1 in place over A (fp16), then to bf16 with the T^T half zeroed, so
-    // S0 holds exactly the lower-triangular T.
-    solve_tril<F::NW, C, f16, true>(A16, LDC, sAd, A16, LDC, tid, w, l);
-    for (int i = tid; i < C * (C / 8); i += F::NTH) {
-      const int r = i / (C / 8), c8 = (i - r * (C / 8)) * 8;
-      const f16x8 hv = *reinterpret_cast<const f16x8*>(A16 + r * LDC + c8);
-      f32x8 fv = __builtin_convertvector(hv, f32x8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (c8 + e > r) fv[e] = 0.f;
-      *reinterpret_cast<bf16x8*>(S0 + r * LDC + c8) = __builtin_convertvector(fv, bf16x8);
-    }
-    __syncthreads();
-
-    phase();
-    // (G) v_new = T R, kept as its bf16 operand form (T lower: row block tb needs k < 16 (tb+1)).
-    bf16x4 vn[NT][NJ];
-    {
-      ARow<bf16, NT / 2> a[2];
-      load_arow<bf16, NT / 2>(a[0], S0, LDC, 0, 0, 1, l);
-#pragma unroll
-      for (int tb = 0; tb < NT; ++tb) {
-        if (tb + 1 < NT) load_arow<bf16, NT / 2>(a[(tb + 1) & 1], S0, LDC, (tb + 1) * 16, 0, tb + 2, l);
-        sched_fence();
-        f32x4 acc[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = zero4();
-        mma_arow<bf16, NT / 2, NJ, 1, 1, NJ>(acc, a[tb & 1], &R[0][0], tb + 1);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) vn[tb][j] = __builtin_convertvector(acc[j], bf16x4);
-        sched_fence();
-      }
-    }
     const bool more = m + 1 < nchunks;
     const int csn = cs + C, lenn = min(C, L - (m + 1) * C);
-    if (more && w == 0) load_gates<C>(pg, pb, g, beta, beta_f32, csn, lenn, h, H, l);
-    __syncthreads();  // T no longer read
-    // Next chunk's K straight into S0.
-    if (more) dma_tile<F, D>(S0, kh + (long)csn * qstride, qstride, lenn, w, l);
+    __syncthreads();  // P, -A, T_ii visible; Q and V consumed
+    // Next chunk: Q and V straight into their tiles, K into registers (its tile is read
+    // until the end of P2), g and beta into wave 0's registers.
+    uint4 kp[F::KPL];
+    if (more) {
+      dma_tile<F, D>(SQ, qh + (long)csn * qstride, qstride, lenn, w, l);
+      dma_tile<F, D>(SV, vh + (long)csn * vstride, vstride, lenn, w, l);
+#pragma unroll
+      for (int s = 0; s < F::KPL; ++s) {
+        const int idx = tid + F::NTH * s, r = idx / CPR, c = idx - r * CPR;
+        kp[s] = *reinterpret_cast<const uint4*>(kh + (long)(csn + min(r, lenn - 1)) * qstride +
+                                                c * 8);
+      }
+      if (w == 0) load_gates<C>(pg, pb, g, beta, beta_f32, csn, lenn, h, H, l);
+    }
+    sched_fence();
 
+    // ---- P2: forward substitution, output and state update, one token block at a time.
     phase();
-    // (H) o = scale (e^G Q h + P v_new) for this wave's columns, one token block at a time.
     {
-      ARow<bf16, NDK / 2> aq[2];
-      ARow<bf16, NT / 2> ap[2];
-      load_arow_swz<D, NDK / 2>(aq[0], S1, 0, l);
-      load_arow<bf16, NT / 2>(ap[0], S2, LDC, 0, 0, 1, l);
+      const float eglast = sMisc[buf];
 #pragma unroll
-      for (int tb = 0; tb < NT; ++tb) {
-        if (tb + 1 < NT) {
-          load_arow_swz<D, NDK / 2>(aq[(tb + 1) & 1], S1, (tb + 1) * 16, l);
-          load_arow<bf16, NT / 2>(ap[(tb + 1) & 1], S2, LDC, (tb + 1) * 16, 0, tb + 2, l);
-        }
-        sched_fence();
-        f32x4 y[NJ], z[NJ];
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) y[j] = z[j] = zero4();
-        mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(y, aq[tb & 1], &stb[0][0], NDK);
-        mma_arow<bf16, NT / 2, NJ, 1, 1, NJ>(z, ap[tb & 1], &vn[0][0], tb + 1);
-        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + tb * 16 + g4);
-        bf16* op = o + ((long)(cs + tb * 16 + g4) * H + h) * D + dvl;
+        for (int db = 0; db < NDK; ++db) st[j][db] *= eglast;
+    }
+    f16x4 vh16[NT][NJ];   // v_new, fp16 operand form (rows = tokens)
+    bf16x4 vb[NT][NJ];    // e^{G_last - G} v_new, bf16 operand form
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const f16* arow = SA + r16 * RS + g4;
+      const f16* prow = SP + r16 * RS + g4;
+      f32x4 acc[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = R[i][j];
+      // R_i - sum_{jb < i} A_{i,jb} v_jb: blocks before i - 1 first (pairs, then a single),
+      // the block the chain waits on last.
+#pragma unroll
+      for (int jb = 0; jb + 1 <= i - 2; jb += 2) {
+        const f16x8 a = cat8(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb)),
+                             *reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb + 1)));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, cat8(vh16[jb][j], vh16[jb + 1][j]), acc[j]);
+      }
+      if (i >= 2 && ((i - 1) & 1)) {
+        const f16x4 a = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 2));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h1(a, vh16[i - 2][j], acc[j]);
+      }
+      const f16x4 tf = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i));
+      if (i >= 1) {
+        const f16x4 a = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 1));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h1(a, vh16[i - 1][j], acc[j]);
+      }
+      f32x4 vn[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        vn[j] = mma16h(tf, to_h(acc[j]), zero4());
+        vh16[i][j] = to_h(vn[j]);
+      }
+      // o_i = scale (e^G Y_i + sum_{jb <= i} P_{i,jb} v_jb)
+      f32x4 z[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) z[j] = zero4();
+#pragma unroll
+      for (int jb = 0; jb + 1 <= i; jb += 2) {
+        const f16x8 a = cat8(*reinterpret_cast<const f16x4*>(prow + tix<F>(i, jb)),
+                             *reinterpret_cast<const f16x4*>(prow + tix<F>(i, jb + 1)));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) z[j] = mma32h(a, cat8(vh16[jb][j], vh16[jb + 1][j]), z[j]);
+      }
+      if ((i & 1) == 0) {
+        const f16x4 a = *reinterpret_cast<const f16x4*>(prow + tix<F>(i, i));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) z[j] = mma32h1(a, vh16[i][j], z[j]);
+      }
+      {
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
+        bf16* op = o + ((long)(cs + i * 16 + g4) * H + h) * D + dvl;
         const long ostride = (long)H * D;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // full chunks store unconditionally (a uniform branch); a partial last chunk
           // stores its valid rows only
-          if (len == C || tb * 16 + g4 + e < len) {
-            if constexpr (NJ == 2) {
-              bf16x2_t ov;
-              ov[0] = (bf16)(scale * fmaf(eg[e], y[0][e], z[0][e]));
-              ov[1] = (bf16)(scale * fmaf(eg[e], y[1][e], z[1][e]));
-              *reinterpret_cast<bf16x2_t*>(op + e * ostride) = ov;
-            } else {
-              op[e * ostride] = (bf16)(scale * fmaf(eg[e], y[0][e], z[0][e]));
-            }
+          if ((len == C || i * 16 + g4 + e < len)) {
+            bf16x2_t ov;
+            ov[0] = (bf16)(scale * fmaf(eg[e], Y[i][0][e], z[0][e]));
+            ov[1] = (bf16)(scale * fmaf(eg[e], Y[i][1][e], z[1][e]));
+            *reinterpret_cast<bf16x2_t*>(op + e * ostride) = ov;
           }
         }
-        sched_fence();
       }
-    }
-    __syncthreads();  // Q and P no longer read
-    // Next chunk's Q and V straight into S1 and S2.
-    if (more) {
-      dma_tile<F, D>(S1, qh + (long)csn * qstride, qstride, lenn, w, l);
-      dma_tile<F, D>(S2, vh + (long)csn * vstride, vstride, lenn, w, l);
-    }
-
-    phase();
-    // (I) h = e^{G_last} h + (K e^{G_last - G})^T v_new, then refresh the bf16 copy.
-    {
-      const float eglast = sMisc[buf];
-      ARow<bf16, NT / 2> a[2];
-      load_arow<bf16, NT / 2>(a[0], S3, LDT, 0, 0, NT, l);
+      // h += K^T (e^{G_last - G} v_new), two token blocks per step
+      {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDec + i * 16 + g4);
 #pragma unroll
-      for (int db = 0; db < NDK; ++db) {
-        if (db + 1 < NDK) load_arow<bf16, NT / 2>(a[(db + 1) & 1], S3, LDT, (db + 1) * 16, 0, NT, l);
-        sched_fence();
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) st[j][db] *= eglast;
-        mma_arow<bf16, NT / 2, NJ, NDK, 1, NJ>(&st[0][db], a[db & 1], &vn[0][0], NT);
-        sched_fence();
+        for (int j = 0; j < NJ; ++j) vb[i][j] = to_b(d4 * vn[j]);
       }
+      if (i & 1) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+        for (int db = 0; db < NDK; ++db) {
+          const int kc = 16 * db + 4 * (r16 & 3);
+          const bf16x8 a = cat8(read_tr<bf16x4>(SK + swz<D>(16 * (i - 1) + g4 + (r16 >> 2), kc)),
+                                read_tr<bf16x4>(SK + swz<D>(16 * i + g4 + (r16 >> 2), kc)));
 #pragma unroll
-        for (int db = 0; db < NDK; ++db) stb[j][db] = __builtin_convertvector(st[j][db], bf16x4);
+          for (int j = 0; j < NJ; ++j) st[j][db] = mma32b(a, cat8(vb[i - 1][j], vb[i][j]), st[j][db]);
+        }
+      }
+      sched_fence();
     }
+    __syncthreads();  // K, -A / T_ii and P no longer read
     if (more) {
+#pragma unroll
+      for (int s = 0; s < F::KPL; ++s) {
+        const int idx = tid + F::NTH * s, r = idx / CPR, c = idx - r * CPR;
+        const uint4 val = r < lenn ? kp[s] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(SK + r * D + (((c ^ r) & (CPR - 1)) << 3)) = val;
+      }
       if (w == 0) chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, lenn, l);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next chunk's copies have landed
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int db = 0; db < NDK; ++db) stb[j][db] = to_b(st[j][db]);
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next chunk's Q, V copies have landed
       if (lenn < C) {
         __syncthreads();
-        zero_tail<F, C>(S0, lenn, tid);
-        zero_tail<F, C>(S1, lenn, tid);
-        zero_tail<F, C>(S2, lenn, tid);
+        zero_tail<F, C>(SQ, lenn, tid);
+        zero_tail<F, C>(SV, lenn, tid);
       }
     }
-    __syncthreads();  // next chunk's tiles and gates visible; this chunk's reads done
+    __syncthreads();  // next chunk's tiles and gates visible
   }
 
   if (ht) {
@@ -587,15 +603,14 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
 
 template <int D, int C>
 hipError_t run_fused(const Problem& p, hipStream_t st) {
-  constexpr int NJ = kFusedNJ;
-  typedef FusedCfg<D, C, NJ> F;
+  typedef FusedCfg<D, C> F;
   const size_t sm = F::lds_bytes();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused<D, C, NJ>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused<D, C>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   const int grid = p.N * p.H;
   if (grid == 0) return hipSuccess;
-  k_fused<D, C, NJ><<<grid, F::NTH, sm, st>>>(
+  k_fused<D, C><<<grid, F::NTH, sm, st>>>(
       static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.v),
       p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot,
       p.H, p.Hg, p.scale);
