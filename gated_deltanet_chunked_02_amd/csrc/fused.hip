@@ -68,9 +68,6 @@ struct FusedCfg {
   static_assert(NT % 2 == 0, "token blocks pair up");
   static_assert(NDMA * NW * RPI == C, "tile covered by whole copy instructions");
   static_assert(KPL * NTH == C * CPR, "K tile covered by whole 16-byte loads");
-  static constexpr size_t lds_bytes() {
-    return (size_t)3 * TILE * 2 + (size_t)2 * NLOW * TE * 2 + (size_t)GATES * 4 + 16;
-  }
 };
 
 // Element offset of (r, k) in a swizzled [rows][D] bf16 tile.
@@ -134,9 +131,11 @@ __device__ __forceinline__ void zero_tail(bf16* tile, int len, int tid) {
     *reinterpret_cast<uint4*>(tile + i * 8) = make_uint4(0, 0, 0, 0);
 }
 
-// Wave 0: g and beta of a chunk, TPL consecutive tokens per lane (zero past len).
+// Wave 0: g and beta of a chunk, TPL consecutive tokens per lane (zero past len).  beta
+// is kept as raw bits (fp32, or bf16 in the high half) and widened only in chunk_gates,
+// so nothing waits for these loads until the chunk's other loads are waited for too.
 template <int C>
-__device__ __forceinline__ void load_gates(float* ga, float* be, const float* g,
+__device__ __forceinline__ void load_gates(float* ga, uint32_t* be, const float* g,
                                            const void* beta, int beta_f32, int cs, int len,
                                            int h, int H, int l) {
   constexpr int TPL = C / kWave;
@@ -144,11 +143,12 @@ __device__ __forceinline__ void load_gates(float* ga, float* be, const float* g,
   for (int r = 0; r < TPL; ++r) {
     const int t = TPL * l + r;
     ga[r] = 0.f;
-    be[r] = 0.f;
+    be[r] = 0u;
     if (t < len) {
       const long gi = (long)(cs + t) * H + h;
       ga[r] = g[gi];
-      be[r] = load_beta(beta, beta_f32, gi);
+      be[r] = beta_f32 ? static_cast<const uint32_t*>(beta)[gi]
+                       : (uint32_t) static_cast<const uint16_t*>(beta)[gi];
     }
   }
 }
@@ -157,7 +157,7 @@ __device__ __forceinline__ void load_gates(float* ga, float* be, const float* g,
 // e^{G_last - G} (zero past len) into sm[4][C], e^{G_last} into *misc.
 template <int C>
 __device__ __forceinline__ void chunk_gates(float* sm, float* misc, const float* ga,
-                                            const float* be, int len, int l) {
+                                            const uint32_t* be, int beta_f32, int len, int l) {
   constexpr int TPL = C / kWave;
   float G[TPL];
   float s = 0.f;
@@ -181,7 +181,7 @@ __device__ __forceinline__ void chunk_gates(float* sm, float* misc, const float*
     const int t = TPL * l + r;
     sm[t] = G[r];
     sm[C + t] = __expf(G[r]);
-    sm[2 * C + t] = be[r];
+    sm[2 * C + t] = __builtin_bit_cast(float, beta_f32 ? be[r] : be[r] << 16);
     sm[3 * C + t] = t < len ? __expf(glast - G[r]) : 0.f;
   }
   if (l == 0) *misc = __expf(glast);
@@ -278,14 +278,15 @@ __global__ __launch_bounds__(D * 2) void k_fused(
   const bf16* kh = k + (long)hk * D;
   const bf16* vh = v + (long)h * D;
 
-  extern __shared__ __align__(16) char smem[];
-  bf16* SK = reinterpret_cast<bf16*>(smem);
-  bf16* SQ = SK + F::TILE;
-  bf16* SV = SQ + F::TILE;
-  f16* SA = reinterpret_cast<f16*>(SV + F::TILE);  // -A below the diagonal, T_ii on it
-  f16* SP = SA + F::NLOW * F::TE;                   // P = (Q K^T * e^{G_i-G_j})_{i>=j}
-  float* sGates = reinterpret_cast<float*>(SP + F::NLOW * F::TE);  // [2][4][C]
-  float* sMisc = sGates + F::GATES;                                  // [2]: e^{G_last}
+  // Separate LDS objects, so the compiler can tell that reads of K, A and P never touch
+  // the Q and V tiles the direct-to-LDS copies are filling, and does not wait for them.
+  __shared__ __align__(16) bf16 SK[F::TILE];
+  __shared__ __align__(16) bf16 SQ[F::TILE];
+  __shared__ __align__(16) bf16 SV[F::TILE];
+  __shared__ __align__(16) f16 SA[F::NLOW * F::TE];  // -A below the diagonal, T_ii on it
+  __shared__ __align__(16) f16 SP[F::NLOW * F::TE];  // P = (Q K^T * e^{G_i-G_j})_{i>=j}
+  __shared__ __align__(16) float sGates[F::GATES];   // [2][4][C]
+  __shared__ float sMisc[2];                          // e^{G_last}, double-buffered
 
   int cs0, L;
   seq_span(cu, n, T, Ttot, cs0, L);
@@ -318,7 +319,8 @@ __global__ __launch_bounds__(D * 2) void k_fused(
 #pragma unroll
     for (int db = 0; db < NDK; ++db) stb[j][db] = to_b(st[j][db]);
 
-  float pg[F::TPL], pb[F::TPL];
+  float pg[F::TPL];
+  uint32_t pb[F::TPL];
   if (nchunks > 0) {
     const int len0 = min(C, L), l = lane_id(), w = wave_id();
     dma_tile<F, D>(SK, kh + (long)cs0 * qstride, qstride, len0, w, l);
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(D * 2) void k_fused(
     dma_tile<F, D>(SV, vh + (long)cs0 * vstride, vstride, len0, w, l);
     if (w == 0) {
       load_gates<C>(pg, pb, g, beta, beta_f32, cs0, len0, h, H, l);
-      chunk_gates<C>(sGates, sMisc, pg, pb, len0, l);
+      chunk_gates<C>(sGates, sMisc, pg, pb, beta_f32, len0, l);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed
     if (len0 < C) {
@@ -571,7 +573,8 @@ __global__ __launch_bounds__(D * 2) void k_fused(
         const uint4 val = r < lenn ? kp[s] : make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(SK + r * D + (((c ^ r) & (CPR - 1)) << 3)) = val;
       }
-      if (w == 0) chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, lenn, l);
+      if (w == 0)
+        chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -604,13 +607,9 @@ __global__ __launch_bounds__(D * 2) void k_fused(
 template <int D, int C>
 hipError_t run_fused(const Problem& p, hipStream_t st) {
   typedef FusedCfg<D, C> F;
-  const size_t sm = F::lds_bytes();
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused<D, C>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-  if (e != hipSuccess) return e;
   const int grid = p.N * p.H;
   if (grid == 0) return hipSuccess;
-  k_fused<D, C><<<grid, F::NTH, sm, st>>>(
+  k_fused<D, C><<<grid, F::NTH, 0, st>>>(
       static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.v),
       p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot,
       p.H, p.Hg, p.scale);
