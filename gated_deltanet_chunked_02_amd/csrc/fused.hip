@@ -46,12 +46,21 @@ namespace gdn {
 namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int D, int C>
+// 16-column state blocks per wave: 2 -> D/32 waves (one per SIMD at D = 128, up to 512
+// registers each, every operand fragment feeds two matrix-core instructions); 1 -> D/16
+// waves (two per SIMD, 256 registers each, one wave's latency hidden behind the other).
+#ifndef GDN_FUSED_NJ
+#define GDN_FUSED_NJ 2
+#endif
+constexpr int kFusedNJ = GDN_FUSED_NJ;
+
+template <int D, int C, int NJ_>
 struct FusedCfg {
-  static constexpr int NJ = 2;              // 16-column state blocks per wave
+  static constexpr int NJ = NJ_;            // 16-column state blocks per wave
   static constexpr int NW = D / (16 * NJ);  // waves
-  static constexpr int NTH = NW * kWave;    // = 2 D (the launch bound)
+  static constexpr int NTH = NW * kWave;    // = 4 D / NJ (the launch bound)
   static constexpr int NT = C / 16;         // token blocks per chunk
   static constexpr int NDK = D / 16;        // key blocks
   static constexpr int CPR = D / 8;         // 16-byte pieces per q/k/v row
@@ -153,7 +162,7 @@ __device__ __forceinline__ void load_gates(float* ga, uint32_t* be, const float*
   }
 }
 
-// Wave 0: G = in-chunk prefix sum of g (chunk_cumsum), then e^G, beta and
+// Wave 0: G = in-chunk prefix sum of g (chunk_cumsum), then G log2(e), e^G, beta and
 // e^{G_last - G} (zero past len) into sm[4][C], e^{G_last} into *misc.
 template <int C>
 __device__ __forceinline__ void chunk_gates(float* sm, float* misc, const float* ga,
@@ -179,7 +188,7 @@ __device__ __forceinline__ void chunk_gates(float* sm, float* misc, const float*
 #pragma unroll
   for (int r = 0; r < TPL; ++r) {
     const int t = TPL * l + r;
-    sm[t] = G[r];
+    sm[t] = G[r] * 1.4426950408889634f;  // G log2(e): decays are exp2 of differences
     sm[C + t] = __expf(G[r]);
     sm[2 * C + t] = __builtin_bit_cast(float, beta_f32 ? be[r] : be[r] << 16);
     sm[3 * C + t] = t < len ? __expf(glast - G[r]) : 0.f;
@@ -263,13 +272,13 @@ __device__ __forceinline__ V4 read_tr(const void* p) {
 // Order this wave's earlier LDS writes before its later LDS reads of the same data.
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int D, int C>
-__global__ __launch_bounds__(D * 2) void k_fused(
+template <int D, int C, int NJ_>
+__global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const void* __restrict__ beta, int beta_f32,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, bf16* __restrict__ o,
     float* __restrict__ ht, int T, int Ttot, int H, int Hg, float scale) {
-  typedef FusedCfg<D, C> F;
+  typedef FusedCfg<D, C, NJ_> F;
   constexpr int NT = F::NT, NDK = F::NDK, NJ = F::NJ, RS = F::RS, CPR = F::CPR;
   const int n = blockIdx.x / H, h = blockIdx.x - n * H;
   const int hk = h / (H / Hg);
@@ -363,7 +372,27 @@ __global__ __launch_bounds__(D * 2) void k_fused(
     };
     phase();
 
-    // ---- P1 (a): this wave's lower 16 x 16 tiles of K Q^T and K K^T.  Tile (ti, tj) in
+    // Next chunk's K, Q, V into registers now; they are written to LDS once this chunk
+    // is done with its tiles, so the loads have the whole chunk to land.  Wave 0 also
+    // loads the next chunk's g and beta.
+    const bool more = m + 1 < nchunks;
+    const int csn = cs + C, lenn = min(C, L - (m + 1) * C);
+    u32x4 kp[F::KPL], qp[F::KPL], vp[F::KPL];
+    if (more) {
+      // the small gate loads first: a wait for them then never waits for the tiles
+      if (w == 0) load_gates<C>(pg, pb, g, beta, beta_f32, csn, lenn, h, H, l);
+#pragma unroll
+      for (int s = 0; s < F::KPL; ++s) {
+        const int idx = tid + F::NTH * s, r = idx / CPR, c = idx - r * CPR;
+        const long row = csn + min(r, lenn - 1);
+        kp[s] = *reinterpret_cast<const u32x4*>(kh + row * qstride + c * 8);
+        qp[s] = *reinterpret_cast<const u32x4*>(qh + row * qstride + c * 8);
+        vp[s] = *reinterpret_cast<const u32x4*>(vh + row * vstride + c * 8);
+      }
+    }
+    sched_fence();
+
+    // ---- P1: this wave's lower 16 x 16 tiles of K Q^T and K K^T.  Tile (ti, tj) in
     // accumulator form holds, in lane l, row i = 16 ti + l%16 and columns j = 16 tj + 4
     // (l/16) + e: the k-contiguous operand form of that row of P and A.
 #pragma unroll
@@ -382,18 +411,29 @@ __global__ __launch_bounds__(D * 2) void k_fused(
         const float Gi = sG[i], nbi = -sB[i];
         const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
         f32x4 pf, nf;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // masked entries use a clamped exponent, so they never overflow
-          const float dec = __expf(fminf(Gi - Gj[e], 0.f));
-          pf[e] = (i >= j0 + e ? dec : 0.f) * pa[e];
-          nf[e] = (i > j0 + e ? nbi * dec : 0.f) * aa[e];
-        }
-        *reinterpret_cast<f16x4*>(SP + tix<F>(ti, tj) + r16 * RS + g4) = to_h(pf);
         f16* at = SA + tix<F>(ti, tj);
-        const f16x4 nt = to_h(nf);
-        *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = nt;
-        if (ti == tj) {
+        f16* pt = SP + tix<F>(ti, tj);
+        if (ti != tj) {
+          // below the diagonal every entry is kept (i > j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
+            pf[e] = dec * pa[e];
+            nf[e] = nbi * dec * aa[e];
+          }
+          *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
+          *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(nf);
+        } else {
+          // masked entries use a clamped exponent, so they never overflow
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
+            pf[e] = (i >= j0 + e ? dec : 0.f) * pa[e];
+            nf[e] = (i > j0 + e ? nbi * dec : 0.f) * aa[e];
+          }
+          *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
+          const f16x4 nt = to_h(nf);
+          *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = nt;
           // T_ii = (I + N + N^2 + ... + N^15) = (I + N)(I + N^2)(I + N^4)(I + N^8) with
           // N = -A_ii strictly lower.  nt is N^T in accumulator form; N itself is read back
           // transposed.  A product X Y takes X^T and Y in accumulator form, so both
@@ -420,58 +460,12 @@ __global__ __launch_bounds__(D * 2) void k_fused(
       }
       sched_fence();
     }
+    __syncthreads();  // P, -A, T_ii visible
 
-    // ---- P1 (b): R = beta (V - e^G K h) and Y = Q h for this wave's columns (fp32).
-    phase();
-    f32x4 R[NT][NJ], Y[NT][NJ];
-    {
-      ARow<bf16, NDK / 2> ak[2], aq[2];
-      load_arow_swz<D, NDK / 2>(ak[0], SK, 0, l);
-      load_arow_swz<D, NDK / 2>(aq[0], SQ, 0, l);
-#pragma unroll
-      for (int tb = 0; tb < NT; ++tb) {
-        if (tb + 1 < NT) {
-          load_arow_swz<D, NDK / 2>(ak[(tb + 1) & 1], SK, (tb + 1) * 16, l);
-          load_arow_swz<D, NDK / 2>(aq[(tb + 1) & 1], SQ, (tb + 1) * 16, l);
-        }
-        sched_fence();
-        f32x4 x[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) x[j] = Y[tb][j] = zero4();
-        mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(x, ak[tb & 1], &stb[0][0], NDK);
-        mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(Y[tb], aq[tb & 1], &stb[0][0], NDK);
-        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + tb * 16 + g4);
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(sB + tb * 16 + g4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16* vp = SV + swz<D>(tb * 16 + g4 + e, dvl);
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) R[tb][j][e] = bt[e] * ((float)vp[j] - eg[e] * x[j][e]);
-        }
-        sched_fence();
-      }
-    }
-
-    const bool more = m + 1 < nchunks;
-    const int csn = cs + C, lenn = min(C, L - (m + 1) * C);
-    __syncthreads();  // P, -A, T_ii visible; Q and V consumed
-    // Next chunk: Q and V straight into their tiles, K into registers (its tile is read
-    // until the end of P2), g and beta into wave 0's registers.
-    uint4 kp[F::KPL];
-    if (more) {
-      dma_tile<F, D>(SQ, qh + (long)csn * qstride, qstride, lenn, w, l);
-      dma_tile<F, D>(SV, vh + (long)csn * vstride, vstride, lenn, w, l);
-#pragma unroll
-      for (int s = 0; s < F::KPL; ++s) {
-        const int idx = tid + F::NTH * s, r = idx / CPR, c = idx - r * CPR;
-        kp[s] = *reinterpret_cast<const uint4*>(kh + (long)(csn + min(r, lenn - 1)) * qstride +
-                                                c * 8);
-      }
-      if (w == 0) load_gates<C>(pg, pb, g, beta, beta_f32, csn, lenn, h, H, l);
-    }
-    sched_fence();
-
-    // ---- P2: forward substitution, output and state update, one token block at a time.
+    // ---- P2: per token block i: R_i = beta (V_i - e^G K_i h) and Y_i = Q_i h, the
+    // forward substitution step, o_i = scale (e^G Y_i + sum_{j<=i} P_ij v_j) and
+    // h += K^T (e^{G_last - G} v_new) (two blocks per step).  The products for block i + 1
+    // are issued before block i's dependent chain, so they fill its latency.
     phase();
     {
       const float eglast = sMisc[buf];
@@ -482,13 +476,36 @@ __global__ __launch_bounds__(D * 2) void k_fused(
     }
     f16x4 vh16[NT][NJ];   // v_new, fp16 operand form (rows = tokens)
     bf16x4 vb[NT][NJ];    // e^{G_last - G} v_new, bf16 operand form
+    f32x4 xk[NJ], yq[NJ];  // K_i h and Q_i h of the next block
+    auto issue_kq = [&](int tb) {
+      ARow<bf16, NDK / 2> ak, aq;
+      load_arow_swz<D, NDK / 2>(ak, SK, tb * 16, l);
+      load_arow_swz<D, NDK / 2>(aq, SQ, tb * 16, l);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) xk[j] = yq[j] = zero4();
+      mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(xk, ak, &stb[0][0], NDK);
+      mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(yq, aq, &stb[0][0], NDK);
+    };
+    issue_kq(0);
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
+      f32x4 acc[NJ], Yi[NJ];
+      {
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(sB + i * 16 + g4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16* vrow = SV + swz<D>(i * 16 + g4 + e, dvl);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[j][e] = bt[e] * ((float)vrow[j] - eg[e] * xk[j][e]);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) Yi[j] = yq[j];
+      }
+      sched_fence();
+      if (i + 1 < NT) issue_kq(i + 1);
       const f16* arow = SA + r16 * RS + g4;
       const f16* prow = SP + r16 * RS + g4;
-      f32x4 acc[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[j] = R[i][j];
       // R_i - sum_{jb < i} A_{i,jb} v_jb: blocks before i - 1 first (pairs, then a single),
       // the block the chain waits on last.
 #pragma unroll
@@ -539,15 +556,18 @@ __global__ __launch_bounds__(D * 2) void k_fused(
         for (int e = 0; e < 4; ++e) {
           // full chunks store unconditionally (a uniform branch); a partial last chunk
           // stores its valid rows only
-          if ((len == C || i * 16 + g4 + e < len)) {
-            bf16x2_t ov;
-            ov[0] = (bf16)(scale * fmaf(eg[e], Y[i][0][e], z[0][e]));
-            ov[1] = (bf16)(scale * fmaf(eg[e], Y[i][1][e], z[1][e]));
-            *reinterpret_cast<bf16x2_t*>(op + e * ostride) = ov;
+          if (len == C || i * 16 + g4 + e < len) {
+            if constexpr (NJ == 2) {
+              bf16x2_t ov;
+              ov[0] = (bf16)(scale * fmaf(eg[e], Yi[0][e], z[0][e]));
+              ov[1] = (bf16)(scale * fmaf(eg[e], Yi[1][e], z[1][e]));
+              *reinterpret_cast<bf16x2_t*>(op + e * ostride) = ov;
+            } else {
+              op[e * ostride] = (bf16)(scale * fmaf(eg[e], Yi[0][e], z[0][e]));
+            }
           }
         }
       }
-      // h += K^T (e^{G_last - G} v_new), two token blocks per step
       {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDec + i * 16 + g4);
 #pragma unroll
@@ -565,13 +585,16 @@ __global__ __launch_bounds__(D * 2) void k_fused(
       }
       sched_fence();
     }
-    __syncthreads();  // K, -A / T_ii and P no longer read
+    __syncthreads();  // K, Q, V, -A / T_ii and P no longer read
     if (more) {
 #pragma unroll
       for (int s = 0; s < F::KPL; ++s) {
         const int idx = tid + F::NTH * s, r = idx / CPR, c = idx - r * CPR;
-        const uint4 val = r < lenn ? kp[s] : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(SK + r * D + (((c ^ r) & (CPR - 1)) << 3)) = val;
+        const int off = r * D + (((c ^ r) & (CPR - 1)) << 3);
+        const u32x4 keep = r < lenn ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(SK + off) = kp[s] & keep;
+        *reinterpret_cast<u32x4*>(SQ + off) = qp[s] & keep;
+        *reinterpret_cast<u32x4*>(SV + off) = vp[s] & keep;
       }
       if (w == 0)
         chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
@@ -580,14 +603,6 @@ __global__ __launch_bounds__(D * 2) void k_fused(
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int db = 0; db < NDK; ++db) stb[j][db] = to_b(st[j][db]);
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next chunk's Q, V copies have landed
-      if (lenn < C) {
-        __syncthreads();
-        zero_tail<F, C>(SQ, lenn, tid);
-        zero_tail<F, C>(SV, lenn, tid);
-      }
-    }
     __syncthreads();  // next chunk's tiles and gates visible
   }
 
@@ -606,10 +621,11 @@ __global__ __launch_bounds__(D * 2) void k_fused(
 
 template <int D, int C>
 hipError_t run_fused(const Problem& p, hipStream_t st) {
-  typedef FusedCfg<D, C> F;
+  constexpr int NJ = kFusedNJ;
+  typedef FusedCfg<D, C, NJ> F;
   const int grid = p.N * p.H;
   if (grid == 0) return hipSuccess;
-  k_fused<D, C><<<grid, F::NTH, 0, st>>>(
+  k_fused<D, C, NJ><<<grid, F::NTH, 0, st>>>(
       static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.v),
       p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot,
       p.H, p.Hg, p.scale);
