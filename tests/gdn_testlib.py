@@ -54,18 +54,31 @@ def pair_slices(inp, n, h):
 
 
 def oracle_pairs(inp, pairs, nthreads=0):
-    """Oracle for sampled (n, h) pairs only; copies just those slices to the host.
+    """Oracle for sampled (n, h) pairs only.  The pairs' tokens are copied to the host and
+    packed as one variable-length batch with a single head, so the oracle's parallel loop
+    over (sequence, head) runs them side by side.
     Returns {(n, h): (o [L, Dv], ht [Dk, Dv])}."""
-    out = {}
+    pairs = list(pairs)
+    if not pairs:
+        return {}
+    qs, ks, vs, gs, bs, h0s, lens = [], [], [], [], [], [], []
     for n, h in pairs:
         ts, b, hk = pair_slices(inp, n, h)
-        sel = lambda x, hh: x[b:b + 1, ts, hh:hh + 1].detach().cpu()
-        h0 = None if inp["h0"] is None else inp["h0"][n:n + 1, h:h + 1].detach().cpu()
-        o, ht = oracle.recurrence(sel(inp["q"], hk), sel(inp["k"], hk), sel(inp["v"], h),
-                                  sel(inp["g"], h), sel(inp["beta"], h), h0,
-                                  scale=inp["scale"], nthreads=nthreads)
-        out[(n, h)] = (o[0, :, 0], ht[0, 0])
-    return out
+        qs.append(inp["q"][b, ts, hk].detach().cpu())
+        ks.append(inp["k"][b, ts, hk].detach().cpu())
+        vs.append(inp["v"][b, ts, h].detach().cpu())
+        gs.append(inp["g"][b, ts, h].detach().cpu())
+        bs.append(inp["beta"][b, ts, h].detach().cpu())
+        if inp["h0"] is not None:
+            h0s.append(inp["h0"][n, h].detach().cpu())
+        lens.append(qs[-1].shape[0])
+    cat = lambda xs: torch.cat(xs, 0)[None, :, None]
+    cu = np.zeros(len(pairs) + 1, np.int64)
+    cu[1:] = np.cumsum(lens)
+    h0 = torch.stack(h0s)[:, None] if h0s else None
+    o, ht = oracle.recurrence(cat(qs), cat(ks), cat(vs), cat(gs), cat(bs), h0,
+                              scale=inp["scale"], cu_seqlens=cu, nthreads=nthreads)
+    return {p: (o[0, cu[i]:cu[i + 1], 0], ht[i, 0]) for i, p in enumerate(pairs)}
 
 
 def run_gdn(inp, variant="auto", C=None, output_final_state=True, **kw):

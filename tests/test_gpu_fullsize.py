@@ -1,0 +1,88 @@
+"""Full-size parity: each workload at its real size, run the way the benchmark runs it
+(variant AUTO, inputs drawn on the GPU), checked against the fp64 oracle on a seeded sample
+of (sequence, head) pairs: relative L2 per pair <= 5e-3 on o and <= 1e-2 on ht (the bf16
+tolerances).  The sample always includes the first and the last sequence (for a packed
+batch also the shortest and the longest one) and the first and the last head.  The head
+sweep of the packed batch and the prompt-length sweep of the long prefill are covered too.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs
+from gdn_testlib import TOL_BF16_HT, TOL_BF16_O, oracle_pairs, pair_slices, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+LOG = os.environ.get("GDN_PARITY_LOG")
+
+CASES = [
+    # workload, overrides, sampled pairs
+    ("headline", {}, 16),
+    ("gqa", {}, 8),
+    ("varlen", {}, 16),
+    ("varlen", {"H": 16, "Hg": 16}, 8),
+    ("varlen", {"H": 32, "Hg": 32}, 8),
+    ("varlen", {"H": 48, "Hg": 48}, 8),
+    ("long", {}, 4),
+    ("long", {"T": 512}, 8),
+    ("long", {"T": 4096}, 8),
+    ("long", {"T": 16384}, 8),
+]
+
+
+def sample_pairs(inp, count, seed):
+    H = inp["v"].shape[2]
+    cu = inp["cu_seqlens"]
+    if cu is None:
+        N = inp["q"].shape[0]
+        lens = np.full(N, inp["q"].shape[1])
+    else:
+        c = cu.cpu().numpy()
+        N = len(c) - 1
+        lens = np.diff(c)
+    fixed = [(0, 0), (N - 1, H - 1), (int(np.argmin(lens)), H // 2),
+             (int(np.argmax(lens)), H - 1)]
+    rng = np.random.default_rng(seed)
+    rest = [(int(rng.integers(N)), int(rng.integers(H))) for _ in range(4 * count)]
+    out = []
+    for p in fixed + rest:
+        if p not in out:
+            out.append(p)
+        if len(out) == count:
+            break
+    return out
+
+
+@pytest.mark.parametrize("name,over,count", CASES,
+                         ids=["%s%s" % (c[0], "".join("-%s%d" % kv for kv in c[1].items()))
+                              for c in CASES])
+def test_full_size_sampled(name, over, count):
+    import gated_deltanet_chunked_02_amd as gdn
+    w = gdn_inputs.WORKLOADS[name].with_(**over)
+    inp = gdn_inputs.draw(w, device="cuda")
+    print("[fullsize] %s drawn: q %s" % (w.name, tuple(inp["q"].shape)), flush=True)
+    o, ht = gdn.chunk_gated_delta_rule(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                       scale=inp["scale"], initial_state=inp["h0"],
+                                       cu_seqlens=inp["cu_seqlens"], chunk_size=w.C)
+    torch.cuda.synchronize()
+    pairs = sample_pairs(inp, count, w.seed)
+    ref = oracle_pairs(inp, pairs, nthreads=min(16, len(pairs)))
+    worst_o = worst_h = 0.0
+    for (n, h), (o_ref, ht_ref) in ref.items():
+        ts, b, _ = pair_slices(inp, n, h)
+        eo = rel_l2(o[b, ts, h].double().cpu().numpy(), o_ref)
+        eh = rel_l2(ht[n, h].double().cpu().numpy(), ht_ref)
+        assert np.isfinite(eo) and np.isfinite(eh)
+        assert eo <= TOL_BF16_O, "%s pair %s o rel-L2 %.3g" % (w.name, (n, h), eo)
+        assert eh <= TOL_BF16_HT, "%s pair %s ht rel-L2 %.3g" % (w.name, (n, h), eh)
+        worst_o, worst_h = max(worst_o, eo), max(worst_h, eh)
+    rec = dict(test="full_size", workload=w.name, over=over, pairs=len(ref),
+               o_rel_max=worst_o, ht_rel_max=worst_h)
+    print(json.dumps(rec), flush=True)
+    if LOG:
+        with open(LOG, "a") as f:
+            f.write(json.dumps(rec) + "\n")

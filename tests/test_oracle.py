@@ -331,3 +331,18 @@ def test_planted_diagonal_in_kkt_mask_is_caught(monkeypatch):
     r = ch.chunked(q, k, v, g, beta, hs, C=16)
     rel = np.linalg.norm(r["o"] - o) / np.linalg.norm(o)
     assert rel > 0.05
+
+
+def test_sampled_pairs_helper_matches_full_run():
+    import gdn_inputs
+    # the packed single-head form used for sampled full-size checks returns the same values
+    from gdn_testlib import oracle_full, oracle_pairs, pair_slices
+    inp = gdn_inputs.draw(gdn_inputs.small(T=0, n_varlen=5, max_len=90, H=4, Hg=2, Dk=16,
+                                           C=16, seed=11, h0_std=0.1), device="cpu")
+    o_ref, ht_ref = oracle_full(inp)
+    pairs = [(0, 0), (4, 3), (2, 1), (3, 2)]
+    got = oracle_pairs(inp, pairs, nthreads=2)
+    for (n, h), (o, ht) in got.items():
+        ts, b, _ = pair_slices(inp, n, h)
+        np.testing.assert_allclose(o, o_ref[b, ts, h], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(ht, ht_ref[n, h], rtol=0, atol=1e-14)
