@@ -372,93 +372,125 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     };
     phase();
 
-    // Next chunk's K, Q, V into registers now; they are written to LDS once this chunk
-    // is done with its tiles, so the loads have the whole chunk to land.  Wave 0 also
-    // loads the next chunk's g and beta.
+    // Next chunk's K, Q, V into registers, written to LDS once this chunk is done with its
+    // tiles.  The loads are spread over the chunk (K now, Q at the start of the second
+    // phase, V half-way through it) so the memory pipeline never holds all of them at
+    // once.  Wave 0 also loads the next chunk's g and beta.
     const bool more = m + 1 < nchunks;
     const int csn = cs + C, lenn = min(C, L - (m + 1) * C);
     u32x4 kp[F::KPL], qp[F::KPL], vp[F::KPL];
-    if (more) {
-      // the small gate loads first: a wait for them then never waits for the tiles
-      if (w == 0) load_gates<C>(pg, pb, g, beta, beta_f32, csn, lenn, h, H, l);
+    auto prefetch = [&](u32x4* dst, const bf16* base, long stride) {
 #pragma unroll
       for (int s = 0; s < F::KPL; ++s) {
         const int idx = tid + F::NTH * s, r = idx / CPR, c = idx - r * CPR;
-        const long row = csn + min(r, lenn - 1);
-        kp[s] = *reinterpret_cast<const u32x4*>(kh + row * qstride + c * 8);
-        qp[s] = *reinterpret_cast<const u32x4*>(qh + row * qstride + c * 8);
-        vp[s] = *reinterpret_cast<const u32x4*>(vh + row * vstride + c * 8);
+        dst[s] = *reinterpret_cast<const u32x4*>(base + (csn + min(r, lenn - 1)) * stride +
+                                                 c * 8);
       }
+    };
+    if (more) {
+      // the small gate loads first: a wait for them then never waits for the tiles
+      if (w == 0) load_gates<C>(pg, pb, g, beta, beta_f32, csn, lenn, h, H, l);
+      prefetch(kp, kh, qstride);
     }
     sched_fence();
 
     // ---- P1: this wave's lower 16 x 16 tiles of K Q^T and K K^T.  Tile (ti, tj) in
     // accumulator form holds, in lane l, row i = 16 ti + l%16 and columns j = 16 tj + 4
     // (l/16) + e: the k-contiguous operand form of that row of P and A.
+    // Gate, mask and store one tile (pa = its K Q^T part, aa = its K K^T part).
+    auto tile_out = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
+      const int i = ti * 16 + r16, j0 = tj * 16 + g4;
+      const float Gi = sG[i], nbi = -sB[i];
+      const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
+      f32x4 pf, nf;
+      f16* at = SA + tix<F>(ti, tj);
+      f16* pt = SP + tix<F>(ti, tj);
+      if (ti != tj) {
+        // below the diagonal every entry is kept (i > j)
 #pragma unroll
-    for (int u = 0; u < F::MAXT; ++u) {
-      if (has_tile<NT, F::NW>(w, u)) {
-        int ti, tj;
-        lower_tile<NT, F::NW>(w, u, ti, tj);
-        f32x4 pa = zero4(), aa = zero4();
+        for (int e = 0; e < 4; ++e) {
+          const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
+          pf[e] = dec * pa[e];
+          nf[e] = nbi * dec * aa[e];
+        }
+        *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
+        *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(nf);
+      } else {
+        // masked entries use a clamped exponent, so they never overflow
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
+          pf[e] = (i >= j0 + e ? dec : 0.f) * pa[e];
+          nf[e] = (i > j0 + e ? nbi * dec : 0.f) * aa[e];
+        }
+        *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
+        const f16x4 nt = to_h(nf);
+        *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = nt;
+        // T_ii = (I + N + N^2 + ... + N^15) = (I + N)(I + N^2)(I + N^4)(I + N^8) with
+        // N = -A_ii strictly lower.  nt is N^T in accumulator form; N itself is read back
+        // transposed.  A product X Y takes X^T and Y in accumulator form, so both
+        // orientations of each power are kept; the result is built as T^T, whose
+        // accumulator form is the row-major storage of T.
+        lds_fence();
+        const f16x4 nn = read_tr<f16x4>(at + (g4 + (r16 >> 2)) * RS + 4 * (r16 & 3));
+        f32x4 eye;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) eye[e] = (g4 + e == r16) ? 1.f : 0.f;
+        const f32x4 n2 = mma16h(nt, nn, zero4());     // N^2
+        const f32x4 n2t = mma16h(nn, nt, zero4());    // (N^2)^T
+        const f16x4 h2 = to_h(n2), h2t = to_h(n2t);
+        const f32x4 n4 = mma16h(h2t, h2, zero4());    // N^4
+        const f32x4 n4t = mma16h(h2, h2t, zero4());   // (N^4)^T
+        const f16x4 h4 = to_h(n4), h4t = to_h(n4t);
+        const f16x4 h8 = to_h(mma16h(h4t, h4, zero4()));  // N^8
+        // Y1 = (I + N^2)^T (I + N)^T = I + N^T + (N^2)^T + (N^2)^T N^T
+        const f32x4 y1 = mma16h(h2, nt, eye + nf + n2t);
+        const f32x4 y2 = mma16h(h4, to_h(y1), y1);    // (I + (N^4)^T) Y1
+        const f32x4 y3 = mma16h(h8, to_h(y2), y2);    // (I + (N^8)^T) Y2 = T_ii^T
+        *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(y3);
+      }
+    };
+    if constexpr (NT == 2 * F::NW) {
+      // Wave w owns block rows w and NT - 1 - w (NT + 1 tiles).  A row's Q and K fragments
+      // are loaded once and reused by all its tiles.
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int ti = rr == 0 ? w : NT - 1 - w;
+        bf16x8 qf[D / 32], kfi[D / 32];
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-          const bf16x8 kf = frag_swz<D>(SK, tj * 16, 32 * kk, l);
-          pa = Mma<bf16>::mma(kf, frag_swz<D>(SQ, ti * 16, 32 * kk, l), pa);
-          aa = Mma<bf16>::mma(kf, frag_swz<D>(SK, ti * 16, 32 * kk, l), aa);
+          qf[kk] = frag_swz<D>(SQ, ti * 16, 32 * kk, l);
+          kfi[kk] = frag_swz<D>(SK, ti * 16, 32 * kk, l);
         }
-        const int i = ti * 16 + r16, j0 = tj * 16 + g4;
-        const float Gi = sG[i], nbi = -sB[i];
-        const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
-        f32x4 pf, nf;
-        f16* at = SA + tix<F>(ti, tj);
-        f16* pt = SP + tix<F>(ti, tj);
-        if (ti != tj) {
-          // below the diagonal every entry is kept (i > j)
+        for (int tj = 0; tj <= ti; ++tj) {
+          f32x4 pa = zero4(), aa = zero4();
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
-            pf[e] = dec * pa[e];
-            nf[e] = nbi * dec * aa[e];
+          for (int kk = 0; kk < D / 32; ++kk) {
+            const bf16x8 kf = frag_swz<D>(SK, tj * 16, 32 * kk, l);
+            pa = Mma<bf16>::mma(kf, qf[kk], pa);
+            aa = Mma<bf16>::mma(kf, kfi[kk], aa);
           }
-          *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
-          *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(nf);
-        } else {
-          // masked entries use a clamped exponent, so they never overflow
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
-            pf[e] = (i >= j0 + e ? dec : 0.f) * pa[e];
-            nf[e] = (i > j0 + e ? nbi * dec : 0.f) * aa[e];
-          }
-          *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
-          const f16x4 nt = to_h(nf);
-          *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = nt;
-          // T_ii = (I + N + N^2 + ... + N^15) = (I + N)(I + N^2)(I + N^4)(I + N^8) with
-          // N = -A_ii strictly lower.  nt is N^T in accumulator form; N itself is read back
-          // transposed.  A product X Y takes X^T and Y in accumulator form, so both
-          // orientations of each power are kept; the result is built as T^T, whose
-          // accumulator form is the row-major storage of T.
-          lds_fence();
-          const f16x4 nn = read_tr<f16x4>(at + (g4 + (r16 >> 2)) * RS + 4 * (r16 & 3));
-          f32x4 eye;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) eye[e] = (g4 + e == r16) ? 1.f : 0.f;
-          const f32x4 n2 = mma16h(nt, nn, zero4());     // N^2
-          const f32x4 n2t = mma16h(nn, nt, zero4());    // (N^2)^T
-          const f16x4 h2 = to_h(n2), h2t = to_h(n2t);
-          const f32x4 n4 = mma16h(h2t, h2, zero4());    // N^4
-          const f32x4 n4t = mma16h(h2, h2t, zero4());   // (N^4)^T
-          const f16x4 h4 = to_h(n4), h4t = to_h(n4t);
-          const f16x4 h8 = to_h(mma16h(h4t, h4, zero4()));  // N^8
-          // Y1 = (I + N^2)^T (I + N)^T = I + N^T + (N^2)^T + (N^2)^T N^T
-          const f32x4 y1 = mma16h(h2, nt, eye + nf + n2t);
-          const f32x4 y2 = mma16h(h4, to_h(y1), y1);    // (I + (N^4)^T) Y1
-          const f32x4 y3 = mma16h(h8, to_h(y2), y2);    // (I + (N^8)^T) Y2 = T_ii^T
-          *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(y3);
+          tile_out(ti, tj, pa, aa);
         }
+        sched_fence();
       }
-      sched_fence();
+    } else {
+#pragma unroll
+      for (int u = 0; u < F::MAXT; ++u) {
+        if (has_tile<NT, F::NW>(w, u)) {
+          int ti, tj;
+          lower_tile<NT, F::NW>(w, u, ti, tj);
+          f32x4 pa = zero4(), aa = zero4();
+#pragma unroll
+          for (int kk = 0; kk < D / 32; ++kk) {
+            const bf16x8 kf = frag_swz<D>(SK, tj * 16, 32 * kk, l);
+            pa = Mma<bf16>::mma(kf, frag_swz<D>(SQ, ti * 16, 32 * kk, l), pa);
+            aa = Mma<bf16>::mma(kf, frag_swz<D>(SK, ti * 16, 32 * kk, l), aa);
+          }
+          tile_out(ti, tj, pa, aa);
+        }
+        sched_fence();
+      }
     }
     __syncthreads();  // P, -A, T_ii visible
 
@@ -467,6 +499,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     // h += K^T (e^{G_last - G} v_new) (two blocks per step).  The products for block i + 1
     // are issued before block i's dependent chain, so they fill its latency.
     phase();
+    if (more) prefetch(qp, qh, qstride);
+    sched_fence();
     {
       const float eglast = sMisc[buf];
 #pragma unroll
@@ -490,8 +524,10 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       f32x4 acc[NJ], Yi[NJ];
+      // e^G of this block's tokens (R and o both use it)
+      const f32x4 egs = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
       {
-        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
+        const f32x4 eg = egs;
         const f32x4 bt = *reinterpret_cast<const f32x4*>(sB + i * 16 + g4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -504,6 +540,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       }
       sched_fence();
       if (i + 1 < NT) issue_kq(i + 1);
+      if (i == NT / 2 - 1 && more) prefetch(vp, vh, vstride);
       const f16* arow = SA + r16 * RS + g4;
       const f16* prow = SP + r16 * RS + g4;
       // R_i - sum_{jb < i} A_{i,jb} v_jb: blocks before i - 1 first (pairs, then a single),
@@ -549,7 +586,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         for (int j = 0; j < NJ; ++j) z[j] = mma32h1(a, vh16[i][j], z[j]);
       }
       {
-        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
+        const f32x4 eg = egs;
         bf16* op = o + ((long)(cs + i * 16 + g4) * H + h) * D + dvl;
         const long ostride = (long)H * D;
 #pragma unroll
