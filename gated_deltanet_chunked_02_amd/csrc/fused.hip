@@ -378,7 +378,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     // once.  Wave 0 also loads the next chunk's g and beta.
     const bool more = m + 1 < nchunks;
     const int csn = cs + C, lenn = min(C, L - (m + 1) * C);
-    u32x4 kp[F::KPL], qp[F::KPL], vp[F::KPL];
+    u32x4 kp[F::KPL], qp[F::KPL], vp_next[F::KPL];
     auto prefetch = [&](u32x4* dst, const bf16* base, long stride) {
 #pragma unroll
       for (int s = 0; s < F::KPL; ++s) {
@@ -508,8 +508,36 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
 #pragma unroll
         for (int db = 0; db < NDK; ++db) st[j][db] *= eglast;
     }
-    f16x4 vh16[NT][NJ];   // v_new, fp16 operand form (rows = tokens)
-    bf16x4 vb[NT][NJ];    // e^{G_last - G} v_new, bf16 operand form
+    // Per-lane address parts, fixed for the chunk.  Within a 16-row block the swizzle key
+    // of a row depends only on the row's offset in the block, so every LDS access below is
+    // one of these lane offsets plus a compile-time block offset, and every output store a
+    // uniform block base plus one of ooff[].
+    int voff[4], koff[NDK];
+    uint32_t ooff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      voff[e] = swz<D>(g4 + e, dvl);
+      ooff[e] = (uint32_t)(((g4 + e) * H * D + dvl) * 2);
+    }
+#pragma unroll
+    for (int db = 0; db < NDK; ++db) koff[db] = swz<D>(g4 + (r16 >> 2), 16 * db + 4 * (r16 & 3));
+    const char* obase = reinterpret_cast<const char*>(o + ((long)cs * H + h) * D);
+    const long oblock = 16L * H * D * 2;  // bytes per 16-token block of o
+    const f16* arow = SA + r16 * RS + g4;
+    const f16* prow = SP + r16 * RS + g4;
+    const f16x4 z4 = {0, 0, 0, 0};
+    // A single 16-token block k against the pair register holding it: the A operand's
+    // other half is zero.
+    auto one = [&](f16x4 a, int k) { return (k & 1) ? cat8(z4, a) : cat8(a, z4); };
+
+    // v_new of token blocks 2p and 2p + 1 in one fp16 register octet (the B-operand form of
+    // a 32-deep product), zero until written; e^{G_last - G} v_new likewise in bf16.
+    f16x8 vp[NT / 2][NJ];
+    bf16x8 vbp[NT / 2][NJ];
+#pragma unroll
+    for (int p2 = 0; p2 < NT / 2; ++p2)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) vp[p2][j] = cat8(z4, z4);
     f32x4 xk[NJ], yq[NJ];  // K_i h and Q_i h of the next block
     auto issue_kq = [&](int tb) {
       ARow<bf16, NDK / 2> ak, aq;
@@ -527,22 +555,20 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       // e^G of this block's tokens (R and o both use it)
       const f32x4 egs = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
       {
-        const f32x4 eg = egs;
         const f32x4 bt = *reinterpret_cast<const f32x4*>(sB + i * 16 + g4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bf16* vrow = SV + swz<D>(i * 16 + g4 + e, dvl);
+          const bf16* vrow = SV + i * 16 * D + voff[e];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[j][e] = bt[e] * ((float)vrow[j] - eg[e] * xk[j][e]);
+          for (int j = 0; j < NJ; ++j)
+            acc[j][e] = bt[e] * ((float)vrow[j] - egs[e] * xk[j][e]);
         }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) Yi[j] = yq[j];
       }
       sched_fence();
       if (i + 1 < NT) issue_kq(i + 1);
-      if (i == NT / 2 - 1 && more) prefetch(vp, vh, vstride);
-      const f16* arow = SA + r16 * RS + g4;
-      const f16* prow = SP + r16 * RS + g4;
+      if (i == NT / 2 - 1 && more) prefetch(vp_next, vh, vstride);
       // R_i - sum_{jb < i} A_{i,jb} v_jb: blocks before i - 1 first (pairs, then a single),
       // the block the chain waits on last.
 #pragma unroll
@@ -550,24 +576,26 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         const f16x8 a = cat8(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb)),
                              *reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb + 1)));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, cat8(vh16[jb][j], vh16[jb + 1][j]), acc[j]);
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, vp[jb / 2][j], acc[j]);
       }
       if (i >= 2 && ((i - 1) & 1)) {
-        const f16x4 a = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 2));
+        const f16x8 a = one(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 2)), i - 2);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = mma32h1(a, vh16[i - 2][j], acc[j]);
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, vp[(i - 2) / 2][j], acc[j]);
       }
       const f16x4 tf = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i));
       if (i >= 1) {
-        const f16x4 a = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 1));
+        const f16x8 a = one(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 1)), i - 1);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = mma32h1(a, vh16[i - 1][j], acc[j]);
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, vp[(i - 1) / 2][j], acc[j]);
       }
       f32x4 vn[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         vn[j] = mma16h(tf, to_h(acc[j]), zero4());
-        vh16[i][j] = to_h(vn[j]);
+        const f16x4 hv = to_h(vn[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vp[i / 2][j][4 * (i & 1) + e] = hv[e];
       }
       // o_i = scale (e^G Y_i + sum_{jb <= i} P_{i,jb} v_jb)
       f32x4 z[NJ];
@@ -578,29 +606,28 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         const f16x8 a = cat8(*reinterpret_cast<const f16x4*>(prow + tix<F>(i, jb)),
                              *reinterpret_cast<const f16x4*>(prow + tix<F>(i, jb + 1)));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) z[j] = mma32h(a, cat8(vh16[jb][j], vh16[jb + 1][j]), z[j]);
+        for (int j = 0; j < NJ; ++j) z[j] = mma32h(a, vp[jb / 2][j], z[j]);
       }
       if ((i & 1) == 0) {
-        const f16x4 a = *reinterpret_cast<const f16x4*>(prow + tix<F>(i, i));
+        const f16x8 a = one(*reinterpret_cast<const f16x4*>(prow + tix<F>(i, i)), i);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) z[j] = mma32h1(a, vh16[i][j], z[j]);
+        for (int j = 0; j < NJ; ++j) z[j] = mma32h(a, vp[i / 2][j], z[j]);
       }
       {
-        const f32x4 eg = egs;
-        bf16* op = o + ((long)(cs + i * 16 + g4) * H + h) * D + dvl;
-        const long ostride = (long)H * D;
+        const char* ob = obase + i * oblock;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // full chunks store unconditionally (a uniform branch); a partial last chunk
           // stores its valid rows only
           if (len == C || i * 16 + g4 + e < len) {
+            bf16* op = reinterpret_cast<bf16*>(const_cast<char*>(ob) + ooff[e]);
             if constexpr (NJ == 2) {
               bf16x2_t ov;
-              ov[0] = (bf16)(scale * fmaf(eg[e], Yi[0][e], z[0][e]));
-              ov[1] = (bf16)(scale * fmaf(eg[e], Yi[1][e], z[1][e]));
-              *reinterpret_cast<bf16x2_t*>(op + e * ostride) = ov;
+              ov[0] = (bf16)(scale * fmaf(egs[e], Yi[0][e], z[0][e]));
+              ov[1] = (bf16)(scale * fmaf(egs[e], Yi[1][e], z[1][e]));
+              *reinterpret_cast<bf16x2_t*>(op) = ov;
             } else {
-              op[e * ostride] = (bf16)(scale * fmaf(eg[e], Yi[0][e], z[0][e]));
+              *op = (bf16)(scale * fmaf(egs[e], Yi[0][e], z[0][e]));
             }
           }
         }
@@ -608,16 +635,19 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(sDec + i * 16 + g4);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) vb[i][j] = to_b(d4 * vn[j]);
+        for (int j = 0; j < NJ; ++j) {
+          const bf16x4 b = to_b(d4 * vn[j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vbp[i / 2][j][4 * (i & 1) + e] = b[e];
+        }
       }
       if (i & 1) {
 #pragma unroll
         for (int db = 0; db < NDK; ++db) {
-          const int kc = 16 * db + 4 * (r16 & 3);
-          const bf16x8 a = cat8(read_tr<bf16x4>(SK + swz<D>(16 * (i - 1) + g4 + (r16 >> 2), kc)),
-                                read_tr<bf16x4>(SK + swz<D>(16 * i + g4 + (r16 >> 2), kc)));
+          const bf16x8 a = cat8(read_tr<bf16x4>(SK + (i - 1) * 16 * D + koff[db]),
+                                read_tr<bf16x4>(SK + i * 16 * D + koff[db]));
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) st[j][db] = mma32b(a, cat8(vb[i - 1][j], vb[i][j]), st[j][db]);
+          for (int j = 0; j < NJ; ++j) st[j][db] = mma32b(a, vbp[i / 2][j], st[j][db]);
         }
       }
       sched_fence();
@@ -631,7 +661,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         const u32x4 keep = r < lenn ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(SK + off) = kp[s] & keep;
         *reinterpret_cast<u32x4*>(SQ + off) = qp[s] & keep;
-        *reinterpret_cast<u32x4*>(SV + off) = vp[s] & keep;
+        *reinterpret_cast<u32x4*>(SV + off) = vp_next[s] & keep;
       }
       if (w == 0)
         chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
