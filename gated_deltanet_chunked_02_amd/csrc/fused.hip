@@ -56,6 +56,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kFusedNJ = GDN_FUSED_NJ;
 
+
 template <int D, int C, int NJ_>
 struct FusedCfg {
   static constexpr int NJ = NJ_;            // 16-column state blocks per wave
@@ -77,6 +78,7 @@ struct FusedCfg {
   static_assert(NT % 2 == 0, "token blocks pair up");
   static_assert(NDMA * NW * RPI == C, "tile covered by whole copy instructions");
   static_assert(KPL * NTH == C * CPR, "K tile covered by whole 16-byte loads");
+  static_assert((NTH / CPR) % CPR == 0, "row step of the loads is a multiple of the swizzle");
 };
 
 // Element offset of (r, k) in a swizzled [rows][D] bf16 tile.
@@ -328,6 +330,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
 #pragma unroll
     for (int db = 0; db < NDK; ++db) stb[j][db] = to_b(st[j][db]);
 
+  u32x4 vnext[F::KPL];  // next chunk's V, carried into it
   float pg[F::TPL];
   uint32_t pb[F::TPL];
   if (nchunks > 0) {
@@ -372,19 +375,43 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     };
     phase();
 
+    if (m > 0) {
+      // this chunk's V, loaded during the previous one: its tile is not read before the
+      // second phase, so it is written here, under the first phase's work
+      const uint32_t vr = (uint32_t)tid / CPR, vc = (uint32_t)tid % CPR;
+      const int lo = vr * D + (((vc ^ vr) & (CPR - 1)) << 3);
+#pragma unroll
+      for (int s = 0; s < F::KPL; ++s) {
+        const int r = vr + s * (F::NTH / CPR);
+        const u32x4 keep = r < len ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(SV + lo + s * (F::NTH / CPR) * D) = vnext[s] & keep;
+      }
+    }
     // Next chunk's K, Q, V into registers, written to LDS once this chunk is done with its
     // tiles.  The loads are spread over the chunk (K now, Q at the start of the second
     // phase, V half-way through it) so the memory pipeline never holds all of them at
     // once.  Wave 0 also loads the next chunk's g and beta.
     const bool more = m + 1 < nchunks;
     const int csn = cs + C, lenn = min(C, L - (m + 1) * C);
-    u32x4 kp[F::KPL], qp[F::KPL], vp_next[F::KPL];
+    u32x4 kp[F::KPL], qp[F::KPL];
+    // Lane tid loads rows tid / CPR + s RSTEP (s < KPL), 16-byte piece tid % CPR.  For a
+    // full chunk every load is a uniform row-block base plus one per-lane offset; a partial
+    // chunk re-reads its last row for the rows past its end (they are zeroed in LDS).
+    constexpr int RSTEP = F::NTH / CPR;
+    const uint32_t rl = (uint32_t)tid / CPR, cl = (uint32_t)tid % CPR;
     auto prefetch = [&](u32x4* dst, const bf16* base, long stride) {
+      const char* cb = reinterpret_cast<const char*>(base + (long)csn * stride);
+      if (lenn == C) {
+        const uint32_t lane = (uint32_t)((rl * stride + cl * 8) * 2);
 #pragma unroll
-      for (int s = 0; s < F::KPL; ++s) {
-        const int idx = tid + F::NTH * s, r = idx / CPR, c = idx - r * CPR;
-        dst[s] = *reinterpret_cast<const u32x4*>(base + (csn + min(r, lenn - 1)) * stride +
-                                                 c * 8);
+        for (int s = 0; s < F::KPL; ++s)
+          dst[s] = *reinterpret_cast<const u32x4*>(cb + (long)s * RSTEP * stride * 2 + lane);
+      } else {
+#pragma unroll
+        for (int s = 0; s < F::KPL; ++s) {
+          const long r = min((int)rl + s * RSTEP, lenn - 1);
+          dst[s] = *reinterpret_cast<const u32x4*>(cb + (r * stride + cl * 8) * 2);
+        }
       }
     };
     if (more) {
@@ -397,58 +424,70 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     // ---- P1: this wave's lower 16 x 16 tiles of K Q^T and K K^T.  Tile (ti, tj) in
     // accumulator form holds, in lane l, row i = 16 ti + l%16 and columns j = 16 tj + 4
     // (l/16) + e: the k-contiguous operand form of that row of P and A.
-    // Gate, mask and store one tile (pa = its K Q^T part, aa = its K K^T part).
-    auto tile_out = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
+    // Gate, mask and store one tile (pa = its K Q^T part, aa = its K K^T part): below the
+    // diagonal, and on it (masked, and replaced by T_ii).
+    auto tile_off = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
       const int i = ti * 16 + r16, j0 = tj * 16 + g4;
       const float Gi = sG[i], nbi = -sB[i];
       const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
       f32x4 pf, nf;
       f16* at = SA + tix<F>(ti, tj);
       f16* pt = SP + tix<F>(ti, tj);
-      if (ti != tj) {
-        // below the diagonal every entry is kept (i > j)
+      // below the diagonal every entry is kept (i > j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
-          pf[e] = dec * pa[e];
-          nf[e] = nbi * dec * aa[e];
-        }
-        *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
-        *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(nf);
-      } else {
-        // masked entries use a clamped exponent, so they never overflow
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
-          pf[e] = (i >= j0 + e ? dec : 0.f) * pa[e];
-          nf[e] = (i > j0 + e ? nbi * dec : 0.f) * aa[e];
-        }
-        *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
-        const f16x4 nt = to_h(nf);
-        *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = nt;
-        // T_ii = (I + N + N^2 + ... + N^15) = (I + N)(I + N^2)(I + N^4)(I + N^8) with
-        // N = -A_ii strictly lower.  nt is N^T in accumulator form; N itself is read back
-        // transposed.  A product X Y takes X^T and Y in accumulator form, so both
-        // orientations of each power are kept; the result is built as T^T, whose
-        // accumulator form is the row-major storage of T.
-        lds_fence();
-        const f16x4 nn = read_tr<f16x4>(at + (g4 + (r16 >> 2)) * RS + 4 * (r16 & 3));
-        f32x4 eye;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) eye[e] = (g4 + e == r16) ? 1.f : 0.f;
-        const f32x4 n2 = mma16h(nt, nn, zero4());     // N^2
-        const f32x4 n2t = mma16h(nn, nt, zero4());    // (N^2)^T
-        const f16x4 h2 = to_h(n2), h2t = to_h(n2t);
-        const f32x4 n4 = mma16h(h2t, h2, zero4());    // N^4
-        const f32x4 n4t = mma16h(h2, h2t, zero4());   // (N^4)^T
-        const f16x4 h4 = to_h(n4), h4t = to_h(n4t);
-        const f16x4 h8 = to_h(mma16h(h4t, h4, zero4()));  // N^8
-        // Y1 = (I + N^2)^T (I + N)^T = I + N^T + (N^2)^T + (N^2)^T N^T
-        const f32x4 y1 = mma16h(h2, nt, eye + nf + n2t);
-        const f32x4 y2 = mma16h(h4, to_h(y1), y1);    // (I + (N^4)^T) Y1
-        const f32x4 y3 = mma16h(h8, to_h(y2), y2);    // (I + (N^8)^T) Y2 = T_ii^T
-        *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(y3);
+      for (int e = 0; e < 4; ++e) {
+        const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
+        pf[e] = dec * pa[e];
+        nf[e] = nbi * dec * aa[e];
       }
+      *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
+      *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(nf);
+    };
+    auto tile_diag = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
+      const int i = ti * 16 + r16, j0 = tj * 16 + g4;
+      const float Gi = sG[i], nbi = -sB[i];
+      const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
+      f32x4 pf, nf;
+      f16* at = SA + tix<F>(ti, tj);
+      f16* pt = SP + tix<F>(ti, tj);
+      // masked entries use a clamped exponent, so they never overflow
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
+        pf[e] = (i >= j0 + e ? dec : 0.f) * pa[e];
+        nf[e] = (i > j0 + e ? nbi * dec : 0.f) * aa[e];
+      }
+      *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
+      const f16x4 nt = to_h(nf);
+      *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = nt;
+      // T_ii = (I + N + N^2 + ... + N^15) = (I + N)(I + N^2)(I + N^4)(I + N^8) with
+      // N = -A_ii strictly lower.  nt is N^T in accumulator form; N itself is read back
+      // transposed.  A product X Y takes X^T and Y in accumulator form, so both
+      // orientations of each power are kept; the result is built as T^T, whose
+      // accumulator form is the row-major storage of T.
+      lds_fence();
+      const f16x4 nn = read_tr<f16x4>(at + (g4 + (r16 >> 2)) * RS + 4 * (r16 & 3));
+      f32x4 eye;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) eye[e] = (g4 + e == r16) ? 1.f : 0.f;
+      const f32x4 n2 = mma16h(nt, nn, zero4());     // N^2
+      const f32x4 n2t = mma16h(nn, nt, zero4());    // (N^2)^T
+      const f16x4 h2 = to_h(n2), h2t = to_h(n2t);
+      const f32x4 n4 = mma16h(h2t, h2, zero4());    // N^4
+      const f32x4 n4t = mma16h(h2, h2t, zero4());   // (N^4)^T
+      const f16x4 h4 = to_h(n4), h4t = to_h(n4t);
+      const f16x4 h8 = to_h(mma16h(h4t, h4, zero4()));  // N^8
+      // Y1 = (I + N^2)^T (I + N)^T = I + N^T + (N^2)^T + (N^2)^T N^T
+      const f32x4 y1 = mma16h(h2, nt, eye + nf + n2t);
+      const f32x4 y2 = mma16h(h4, to_h(y1), y1);    // (I + (N^4)^T) Y1
+      const f32x4 y3 = mma16h(h8, to_h(y2), y2);    // (I + (N^8)^T) Y2 = T_ii^T
+      *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(y3);
+    };
+    auto tile_out = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
+      if (ti != tj)
+        tile_off(ti, tj, pa, aa);
+      else
+        tile_diag(ti, tj, pa, aa);
     };
     if constexpr (NT == 2 * F::NW) {
       // Wave w owns block rows w and NT - 1 - w (NT + 1 tiles).  A row's Q and K fragments
@@ -462,16 +501,27 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
           qf[kk] = frag_swz<D>(SQ, ti * 16, 32 * kk, l);
           kfi[kk] = frag_swz<D>(SK, ti * 16, 32 * kk, l);
         }
-        for (int tj = 0; tj <= ti; ++tj) {
-          f32x4 pa = zero4(), aa = zero4();
+        // the products of tile tj + 1 are issued before tile tj's epilogue; the diagonal
+        // tile comes last
+        auto prods = [&](int tj, f32x4& pa, f32x4& aa) {
+          pa = aa = zero4();
 #pragma unroll
           for (int kk = 0; kk < D / 32; ++kk) {
             const bf16x8 kf = frag_swz<D>(SK, tj * 16, 32 * kk, l);
             pa = Mma<bf16>::mma(kf, qf[kk], pa);
             aa = Mma<bf16>::mma(kf, kfi[kk], aa);
           }
-          tile_out(ti, tj, pa, aa);
+        };
+        f32x4 pa, aa;
+        prods(0, pa, aa);
+        for (int tj = 0; tj < ti; ++tj) {
+          f32x4 pn, an;
+          prods(tj + 1, pn, an);
+          tile_off(ti, tj, pa, aa);
+          pa = pn;
+          aa = an;
         }
+        tile_diag(ti, ti, pa, aa);
         sched_fence();
       }
     } else {
@@ -568,7 +618,11 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       }
       sched_fence();
       if (i + 1 < NT) issue_kq(i + 1);
-      if (i == NT / 2 - 1 && more) prefetch(vp_next, vh, vstride);
+      if (i == NT / 2 - 1 && more) prefetch(vnext, vh, vstride);
+      // wave 0 prepares the next chunk's gate vectors (the other buffer; its loads were
+      // issued at the start of the chunk)
+      if (i == NT / 2 && more && w == 0)
+        chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
       // R_i - sum_{jb < i} A_{i,jb} v_jb: blocks before i - 1 first (pairs, then a single),
       // the block the chain waits on last.
 #pragma unroll
@@ -654,17 +708,16 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     }
     __syncthreads();  // K, Q, V, -A / T_ii and P no longer read
     if (more) {
+      // RSTEP is a multiple of the swizzle period, so a lane's swizzle is the same for
+      // every s
+      const int lo = rl * D + (((cl ^ rl) & (CPR - 1)) << 3);
 #pragma unroll
       for (int s = 0; s < F::KPL; ++s) {
-        const int idx = tid + F::NTH * s, r = idx / CPR, c = idx - r * CPR;
-        const int off = r * D + (((c ^ r) & (CPR - 1)) << 3);
+        const int r = rl + s * RSTEP;
         const u32x4 keep = r < lenn ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(SK + off) = kp[s] & keep;
-        *reinterpret_cast<u32x4*>(SQ + off) = qp[s] & keep;
-        *reinterpret_cast<u32x4*>(SV + off) = vp_next[s] & keep;
+        *reinterpret_cast<u32x4*>(SK + lo + s * RSTEP * D) = kp[s] & keep;
+        *reinterpret_cast<u32x4*>(SQ + lo + s * RSTEP * D) = qp[s] & keep;
       }
-      if (w == 0)
-        chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
