@@ -52,7 +52,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // registers each, every operand fragment feeds two matrix-core instructions); 1 -> D/16
 // waves (two per SIMD, 256 registers each, one wave's latency hidden behind the other).
 #ifndef GDN_FUSED_NJ
-#define GDN_FUSED_NJ 2
+#define GDN_FUSED_NJ 1
 #endif
 constexpr int kFusedNJ = GDN_FUSED_NJ;
 
@@ -489,39 +489,62 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       else
         tile_diag(ti, tj, pa, aa);
     };
-    if constexpr (NT == 2 * F::NW) {
-      // Wave w owns block rows w and NT - 1 - w (NT + 1 tiles).  A row's Q and K fragments
-      // are loaded once and reused by all its tiles.
+    if constexpr (NT == 2 * F::NW || NT == F::NW) {
+      // Block rows pair up as (p, NT - 1 - p), NT + 1 tiles per pair.  With NT = 2 NW wave
+      // w owns pair w; with NT = NW waves 2p and 2p + 1 split pair p into 5 and 4 tiles.
+      // Each wave walks at most two row segments; a segment's Q and K fragments are loaded
+      // once, the products of tile tj + 1 are issued before tile tj's epilogue, and a
+      // diagonal tile is always a segment's last.
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int ti = rr == 0 ? w : NT - 1 - w;
-        bf16x8 qf[D / 32], kfi[D / 32];
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          qf[kk] = frag_swz<D>(SQ, ti * 16, 32 * kk, l);
-          kfi[kk] = frag_swz<D>(SK, ti * 16, 32 * kk, l);
+      for (int sg = 0; sg < 2; ++sg) {
+        int ti, t0, t1;
+        if constexpr (NT == 2 * F::NW) {
+          ti = sg == 0 ? w : NT - 1 - w;
+          t0 = 0;
+          t1 = ti;
+        } else {
+          const int pp = w >> 1, odd = w & 1;
+          const int split = NT / 2 - pp;  // tiles of row NT - 1 - p taken by the even wave
+          if (sg == 0) {
+            ti = odd ? NT - 1 - pp : pp;
+            t0 = odd ? split : 0;
+            t1 = ti;
+          } else {
+            ti = NT - 1 - pp;
+            t0 = 0;
+            t1 = odd ? -1 : split - 1;  // empty for the odd wave
+          }
         }
-        // the products of tile tj + 1 are issued before tile tj's epilogue; the diagonal
-        // tile comes last
-        auto prods = [&](int tj, f32x4& pa, f32x4& aa) {
-          pa = aa = zero4();
+        if (t1 >= t0) {
+          bf16x8 qf[D / 32], kfi[D / 32];
 #pragma unroll
           for (int kk = 0; kk < D / 32; ++kk) {
-            const bf16x8 kf = frag_swz<D>(SK, tj * 16, 32 * kk, l);
-            pa = Mma<bf16>::mma(kf, qf[kk], pa);
-            aa = Mma<bf16>::mma(kf, kfi[kk], aa);
+            qf[kk] = frag_swz<D>(SQ, ti * 16, 32 * kk, l);
+            kfi[kk] = frag_swz<D>(SK, ti * 16, 32 * kk, l);
           }
-        };
-        f32x4 pa, aa;
-        prods(0, pa, aa);
-        for (int tj = 0; tj < ti; ++tj) {
-          f32x4 pn, an;
-          prods(tj + 1, pn, an);
-          tile_off(ti, tj, pa, aa);
-          pa = pn;
-          aa = an;
+          auto prods = [&](int tj, f32x4& pa, f32x4& aa) {
+            pa = aa = zero4();
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+              const bf16x8 kf = frag_swz<D>(SK, tj * 16, 32 * kk, l);
+              pa = Mma<bf16>::mma(kf, qf[kk], pa);
+              aa = Mma<bf16>::mma(kf, kfi[kk], aa);
+            }
+          };
+          f32x4 pa, aa;
+          prods(t0, pa, aa);
+          for (int tj = t0; tj < t1; ++tj) {
+            f32x4 pn, an;
+            prods(tj + 1, pn, an);
+            tile_off(ti, tj, pa, aa);
+            pa = pn;
+            aa = an;
+          }
+          if (t1 == ti)
+            tile_diag(ti, ti, pa, aa);
+          else
+            tile_off(ti, t1, pa, aa);
         }
-        tile_diag(ti, ti, pa, aa);
         sched_fence();
       }
     } else {
