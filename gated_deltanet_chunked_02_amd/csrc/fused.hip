@@ -55,6 +55,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GDN_FUSED_NJ 1
 #endif
 constexpr int kFusedNJ = GDN_FUSED_NJ;
+constexpr int kGateWave = 1;  // the wave that builds the gate vectors
 
 
 template <int D, int C, int NJ_>
@@ -142,25 +143,31 @@ __device__ __forceinline__ void zero_tail(bf16* tile, int len, int tid) {
     *reinterpret_cast<uint4*>(tile + i * 8) = make_uint4(0, 0, 0, 0);
 }
 
-// Wave 0: g and beta of a chunk, TPL consecutive tokens per lane (zero past len).  beta
-// is kept as raw bits (fp32, or bf16 in the high half) and widened only in chunk_gates,
-// so nothing waits for these loads until the chunk's other loads are waited for too.
+// A raw buffer resource over [base, base + bytes): loads past the end return zero and
+// stores past it are dropped (word 3 selects 32-bit raw data on gfx950).  Bounding a
+// resource by a chunk's valid tokens makes a partial chunk zero-padded for free.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// g and beta of a chunk, TPL consecutive tokens per lane (zero past len).  beta is kept
+// as raw bits (fp32, or bf16 in the low half) and widened only in chunk_gates, so nothing
+// waits for these loads until the chunk's other loads are waited for too.
 template <int C>
 __device__ __forceinline__ void load_gates(float* ga, uint32_t* be, const float* g,
                                            const void* beta, int beta_f32, int cs, int len,
                                            int h, int H, int l) {
   constexpr int TPL = C / kWave;
+  const int bsz = beta_f32 ? 4 : 2;
+  const auto rg = buf_rsrc(g + (long)cs * H + h, (uint32_t)(len * H * 4));
+  const auto rb = buf_rsrc(static_cast<const char*>(beta) + ((long)cs * H + h) * bsz,
+                           (uint32_t)(len * H * bsz));
 #pragma unroll
   for (int r = 0; r < TPL; ++r) {
     const int t = TPL * l + r;
-    ga[r] = 0.f;
-    be[r] = 0u;
-    if (t < len) {
-      const long gi = (long)(cs + t) * H + h;
-      ga[r] = g[gi];
-      be[r] = beta_f32 ? static_cast<const uint32_t*>(beta)[gi]
-                       : (uint32_t) static_cast<const uint16_t*>(beta)[gi];
-    }
+    ga[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, t * H * 4, 0, 0));
+    be[r] = beta_f32 ? __builtin_amdgcn_raw_buffer_load_b32(rb, t * H * 4, 0, 0)
+                     : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, t * H * 2, 0, 0);
   }
 }
 
@@ -331,16 +338,20 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     for (int db = 0; db < NDK; ++db) stb[j][db] = to_b(st[j][db]);
 
   u32x4 vnext[F::KPL];  // next chunk's V, carried into it
-  float pg[F::TPL];
-  uint32_t pb[F::TPL];
+  // g and beta of the next chunk (loaded one chunk earlier) and of the one after it, in
+  // the registers of the wave that turns them into gate vectors
+  float pg[F::TPL], pg2[F::TPL];
+  uint32_t pb[F::TPL], pb2[F::TPL];
   if (nchunks > 0) {
     const int len0 = min(C, L), l = lane_id(), w = wave_id();
     dma_tile<F, D>(SK, kh + (long)cs0 * qstride, qstride, len0, w, l);
     dma_tile<F, D>(SQ, qh + (long)cs0 * qstride, qstride, len0, w, l);
     dma_tile<F, D>(SV, vh + (long)cs0 * vstride, vstride, len0, w, l);
-    if (w == 0) {
+    if (w == kGateWave) {
       load_gates<C>(pg, pb, g, beta, beta_f32, cs0, len0, h, H, l);
       chunk_gates<C>(sGates, sMisc, pg, pb, beta_f32, len0, l);
+      if (nchunks > 1)
+        load_gates<C>(pg, pb, g, beta, beta_f32, cs0 + C, min(C, L - C), h, H, l);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies have landed
     if (len0 < C) {
@@ -381,11 +392,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       const uint32_t vr = (uint32_t)tid / CPR, vc = (uint32_t)tid % CPR;
       const int lo = vr * D + (((vc ^ vr) & (CPR - 1)) << 3);
 #pragma unroll
-      for (int s = 0; s < F::KPL; ++s) {
-        const int r = vr + s * (F::NTH / CPR);
-        const u32x4 keep = r < len ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(SV + lo + s * (F::NTH / CPR) * D) = vnext[s] & keep;
-      }
+      for (int s = 0; s < F::KPL; ++s)
+        *reinterpret_cast<u32x4*>(SV + lo + s * (F::NTH / CPR) * D) = vnext[s];
     }
     // Next chunk's K, Q, V into registers, written to LDS once this chunk is done with its
     // tiles.  The loads are spread over the chunk (K now, Q at the start of the second
@@ -394,31 +402,24 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     const bool more = m + 1 < nchunks;
     const int csn = cs + C, lenn = min(C, L - (m + 1) * C);
     u32x4 kp[F::KPL], qp[F::KPL];
-    // Lane tid loads rows tid / CPR + s RSTEP (s < KPL), 16-byte piece tid % CPR.  For a
-    // full chunk every load is a uniform row-block base plus one per-lane offset; a partial
-    // chunk re-reads its last row for the rows past its end (they are zeroed in LDS).
+    // Lane tid loads rows tid / CPR + s RSTEP (s < KPL), 16-byte piece tid % CPR: a uniform
+    // row-block offset plus one per-lane offset.  The resource ends at the chunk's last
+    // token, so the rows of a partial chunk past its end load as zero.
     constexpr int RSTEP = F::NTH / CPR;
     const uint32_t rl = (uint32_t)tid / CPR, cl = (uint32_t)tid % CPR;
     auto prefetch = [&](u32x4* dst, const bf16* base, long stride) {
-      const char* cb = reinterpret_cast<const char*>(base + (long)csn * stride);
-      if (lenn == C) {
-        const uint32_t lane = (uint32_t)((rl * stride + cl * 8) * 2);
+      const auto rs = buf_rsrc(base + (long)csn * stride, (uint32_t)(lenn * stride * 2));
+      const int lane = (int)((rl * stride + cl * 8) * 2);
 #pragma unroll
-        for (int s = 0; s < F::KPL; ++s)
-          dst[s] = *reinterpret_cast<const u32x4*>(cb + (long)s * RSTEP * stride * 2 + lane);
-      } else {
-#pragma unroll
-        for (int s = 0; s < F::KPL; ++s) {
-          const long r = min((int)rl + s * RSTEP, lenn - 1);
-          dst[s] = *reinterpret_cast<const u32x4*>(cb + (r * stride + cl * 8) * 2);
-        }
-      }
+      for (int s = 0; s < F::KPL; ++s)
+        dst[s] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane, (int)(s * RSTEP * stride * 2), 0));
     };
-    if (more) {
-      // the small gate loads first: a wait for them then never waits for the tiles
-      if (w == 0) load_gates<C>(pg, pb, g, beta, beta_f32, csn, lenn, h, H, l);
-      prefetch(kp, kh, qstride);
-    }
+    // the small gate loads (two chunks ahead) first: a wait for them then never waits for
+    // the tiles
+    if (w == kGateWave && m + 2 < nchunks)
+      load_gates<C>(pg2, pb2, g, beta, beta_f32, cs + 2 * C, min(C, L - (m + 2) * C), h, H, l);
+    if (more) prefetch(kp, kh, qstride);
     sched_fence();
 
     // ---- P1: this wave's lower 16 x 16 tiles of K Q^T and K K^T.  Tile (ti, tj) in
@@ -565,6 +566,16 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         sched_fence();
       }
     }
+    // The gate wave (an odd wave, one tile fewer than its partner) builds the next
+    // chunk's gate vectors in the other buffer, whose last reader was the previous chunk.
+    if (w == kGateWave && more) {
+      chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
+#pragma unroll
+      for (int r = 0; r < F::TPL; ++r) {
+        pg[r] = pg2[r];
+        pb[r] = pb2[r];
+      }
+    }
     __syncthreads();  // P, -A, T_ii visible
 
     // ---- P2: per token block i: R_i = beta (V_i - e^G K_i h) and Y_i = Q_i h, the
@@ -584,7 +595,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     // Per-lane address parts, fixed for the chunk.  Within a 16-row block the swizzle key
     // of a row depends only on the row's offset in the block, so every LDS access below is
     // one of these lane offsets plus a compile-time block offset, and every output store a
-    // uniform block base plus one of ooff[].
+    // uniform block offset plus one of ooff[].
     int voff[4], koff[NDK];
     uint32_t ooff[4];
 #pragma unroll
@@ -594,8 +605,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     }
 #pragma unroll
     for (int db = 0; db < NDK; ++db) koff[db] = swz<D>(g4 + (r16 >> 2), 16 * db + 4 * (r16 & 3));
-    const char* obase = reinterpret_cast<const char*>(o + ((long)cs * H + h) * D);
-    const long oblock = 16L * H * D * 2;  // bytes per 16-token block of o
+    const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D, (uint32_t)(len * H * D * 2));
+    const int oblock = 16 * H * D * 2;  // bytes per 16-token block of o
     const f16* arow = SA + r16 * RS + g4;
     const f16* prow = SP + r16 * RS + g4;
     const f16x4 z4 = {0, 0, 0, 0};
@@ -642,10 +653,6 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       sched_fence();
       if (i + 1 < NT) issue_kq(i + 1);
       if (i == NT / 2 - 1 && more) prefetch(vnext, vh, vstride);
-      // wave 0 prepares the next chunk's gate vectors (the other buffer; its loads were
-      // issued at the start of the chunk)
-      if (i == NT / 2 && more && w == 0)
-        chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
       // R_i - sum_{jb < i} A_{i,jb} v_jb: blocks before i - 1 first (pairs, then a single),
       // the block the chain waits on last.
 #pragma unroll
@@ -690,23 +697,19 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) z[j] = mma32h(a, vp[i / 2][j], z[j]);
       }
-      {
-        const char* ob = obase + i * oblock;
+      // o rows past a partial chunk's end fall outside the output resource and are dropped
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // full chunks store unconditionally (a uniform branch); a partial last chunk
-          // stores its valid rows only
-          if (len == C || i * 16 + g4 + e < len) {
-            bf16* op = reinterpret_cast<bf16*>(const_cast<char*>(ob) + ooff[e]);
-            if constexpr (NJ == 2) {
-              bf16x2_t ov;
-              ov[0] = (bf16)(scale * fmaf(egs[e], Yi[0][e], z[0][e]));
-              ov[1] = (bf16)(scale * fmaf(egs[e], Yi[1][e], z[1][e]));
-              *reinterpret_cast<bf16x2_t*>(op) = ov;
-            } else {
-              *op = (bf16)(scale * fmaf(egs[e], Yi[0][e], z[0][e]));
-            }
-          }
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (NJ == 2) {
+          bf16x2_t ov;
+          ov[0] = (bf16)(scale * fmaf(egs[e], Yi[0][e], z[0][e]));
+          ov[1] = (bf16)(scale * fmaf(egs[e], Yi[1][e], z[1][e]));
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ov), orsrc,
+                                                (int)ooff[e], i * oblock, 0);
+        } else {
+          const bf16 ov = (bf16)(scale * fmaf(egs[e], Yi[0][e], z[0][e]));
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, ov), orsrc,
+                                                (int)ooff[e], i * oblock, 0);
         }
       }
       {
@@ -736,10 +739,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       const int lo = rl * D + (((cl ^ rl) & (CPR - 1)) << 3);
 #pragma unroll
       for (int s = 0; s < F::KPL; ++s) {
-        const int r = rl + s * RSTEP;
-        const u32x4 keep = r < lenn ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(SK + lo + s * RSTEP * D) = kp[s] & keep;
-        *reinterpret_cast<u32x4*>(SQ + lo + s * RSTEP * D) = qp[s] & keep;
+        *reinterpret_cast<u32x4*>(SK + lo + s * RSTEP * D) = kp[s];
+        *reinterpret_cast<u32x4*>(SQ + lo + s * RSTEP * D) = qp[s];
       }
     }
 #pragma unroll
