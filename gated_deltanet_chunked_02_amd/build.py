@@ -44,8 +44,6 @@ def flags():
             "-Wno-unused-function",
             # keep packed-fp32 VALU forms out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # LLVM's iterative ILP scheduler (fewer wait cycles in the fused kernel)
-            "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
@@ -72,27 +70,29 @@ _MFMA_DST = re.compile(r"^\s*(v_mfma\S*)\s+([av])\[(\d+):(\d+)\],")
 
 
 def mfma_mixed_chains(asm: str, window: int = 16):
-    """(line number, text) of every matrix-core instruction whose accumulator input overlaps
-    the destination of a matrix-core instruction of another opcode at most `window`
+    """(line number, text) of every matrix-core instruction with an accumulator-input register
+    last written by a matrix-core instruction of another opcode at most `window`
     instructions earlier (labels, directives and comments not counted)."""
     bad = []
-    recent = []  # (instruction index, opcode, register file, first, last) of matrix-core dsts
+    last = {}  # (register file, number) -> (instruction index, opcode) of its last writer
     k = 0
     for n, line in enumerate(asm.splitlines(), 1):
         t = line.strip()
         if not t or t.startswith((";", ".")) or t.endswith(":"):
             continue
         k += 1
-        recent = [r for r in recent if k - r[0] <= window]
         m = _MFMA.match(line)
         if m:
             op, _, _, _, cf_, c0, c1 = m.groups()
-            c0, c1 = int(c0), int(c1)
-            if any(r[1] != op and r[2] == cf_ and r[3] <= c1 and c0 <= r[4] for r in recent):
-                bad.append((n, t))
+            for r in range(int(c0), int(c1) + 1):
+                prev = last.get((cf_, r))
+                if prev is not None and k - prev[0] <= window and prev[1] != op:
+                    bad.append((n, t))
+                    break
         d = _MFMA_DST.match(line)
         if d:
-            recent.append((k, d.group(1), d.group(2), int(d.group(3)), int(d.group(4))))
+            for r in range(int(d.group(3)), int(d.group(4)) + 1):
+                last[(d.group(2), r)] = (k, d.group(1))
     return bad
 
 

@@ -103,18 +103,15 @@ __device__ __forceinline__ bf16x8 frag_swz(const bf16* m, int row0, int k0, int 
   return *reinterpret_cast<const bf16x8*>(m + row0 * D + swz_lane<D>(l, k0 + 8 * (l >> 4)));
 }
 
-// A-row fragments (accumulator-fed contraction form, see gdn_device.h) of a swizzled tile.
-template <int D, int NPAIR>
-__device__ __forceinline__ void load_arow_swz(ARow<bf16, NPAIR>& a, const bf16* m, int row0,
-                                              int l) {
-  const int g4 = 4 * (l >> 4);
-  const bf16* mr = m + row0 * D;
-#pragma unroll
-  for (int p = 0; p < NPAIR; ++p) {
-    const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(mr + swz_lane<D>(l, 32 * p + g4));
-    const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(mr + swz_lane<D>(l, 32 * p + 16 + g4));
-    a.f[p] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
+// Key row of the state held in row r (0..15) of key block db.  The pair of blocks
+// (2p, 2p + 1) covers keys 32p .. 32p + 31, interleaved in groups of four:
+//   row r of block 2p     -> key 32p + 8 (r / 4) + r % 4
+//   row r of block 2p + 1 -> key 32p + 8 (r / 4) + 4 + r % 4.
+// A 32-deep product takes its B operand from a block pair with lane group g holding rows
+// 4g .. 4g + 3 of both blocks, i.e. keys 32p + 8g .. 32p + 8g + 7: the A operand (K or Q
+// rows) is then the standard contiguous 16-byte fragment.
+__device__ __forceinline__ int state_dk(int db, int r) {
+  return 32 * (db >> 1) + 8 * (r >> 2) + 4 * (db & 1) + (r & 3);
 }
 
 // Issue this wave's share of the direct HBM -> LDS copy of one [C][D] tile (rows of one
@@ -310,7 +307,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
   seq_span(cu, n, T, Ttot, cs0, L);
   const int nchunks = (L + C - 1) / C;
 
-  // State: st[j][db] holds rows dk = 16 db + 4 (l/16) + e of column 32 w + 2 (l%16) + j.
+  // State: st[j][db] holds rows dk = state_dk(db, 4 (l/16) + e) of column
+  // 16 NJ w + NJ (l%16) + j.
   f32x4 st[NJ][NDK];
   const long hoff = ((long)n * H + h) * D * D;
   {
@@ -327,7 +325,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            st[j][db][e] = h0[hoff + (long)(16 * db + g4 + e) * D + dv0 + j];
+            st[j][db][e] = h0[hoff + (long)state_dk(db, g4 + e) * D + dv0 + j];
     }
   }
   // bf16 copy of the chunk-start state in the B-operand form of the K h and Q h products.
@@ -604,7 +602,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       ooff[e] = (uint32_t)(((g4 + e) * H * D + dvl) * 2);
     }
 #pragma unroll
-    for (int db = 0; db < NDK; ++db) koff[db] = swz<D>(g4 + (r16 >> 2), 16 * db + 4 * (r16 & 3));
+    for (int db = 0; db < NDK; ++db)
+      koff[db] = swz<D>(g4 + (r16 >> 2), state_dk(db, 4 * (r16 & 3)));
     const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D, (uint32_t)(len * H * D * 2));
     const int oblock = 16 * H * D * 2;  // bytes per 16-token block of o
     const f16* arow = SA + r16 * RS + g4;
@@ -625,8 +624,11 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     f32x4 xk[NJ], yq[NJ];  // K_i h and Q_i h of the next block
     auto issue_kq = [&](int tb) {
       ARow<bf16, NDK / 2> ak, aq;
-      load_arow_swz<D, NDK / 2>(ak, SK, tb * 16, l);
-      load_arow_swz<D, NDK / 2>(aq, SQ, tb * 16, l);
+#pragma unroll
+      for (int p = 0; p < NDK / 2; ++p) {
+        ak.f[p] = frag_swz<D>(SK, tb * 16, 32 * p, l);
+        aq.f[p] = frag_swz<D>(SQ, tb * 16, 32 * p, l);
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) xk[j] = yq[j] = zero4();
       mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(xk, ak, &stb[0][0], NDK);
@@ -759,7 +761,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          ht[hoff + (long)(16 * db + g4 + e) * D + dv0 + j] = st[j][db][e];
+          ht[hoff + (long)state_dk(db, g4 + e) * D + dv0 + j] = st[j][db][e];
   }
 }
 

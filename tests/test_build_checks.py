@@ -45,6 +45,16 @@ def test_mixed_shape_chain_detected():
            "  v_mfma_f32_16x16x16_f16 a[0:3], v[2:3], v[4:5], a[0:3]\n")
     assert len(mfma_mixed_chains(bad)) == 1
     assert mfma_mixed_chains(CHAIN_OK) == []
+    # an accumulator overwritten in between by the reader's own shape is not flagged
+    over = ("  v_mfma_f32_16x16x16_f16 a[20:23], v[10:11], v[6:7], 0\n"
+            "  v_mfma_f32_16x16x32_f16 a[20:23], v[40:43], v[14:17], 0\n"
+            "  v_mfma_f32_16x16x32_f16 a[20:23], v[2:5], v[6:9], a[20:23]\n")
+    assert mfma_mixed_chains(over) == []
+    # a partly overlapping input is checked register by register
+    part = ("  v_mfma_f32_16x16x16_f16 a[4:7], v[10:11], v[6:7], 0\n"
+            "  v_mfma_f32_16x16x32_f16 a[0:3], v[40:43], v[14:17], 0\n"
+            "  v_mfma_f32_16x16x32_f16 a[8:11], v[2:5], v[6:9], a[2:5]\n")
+    assert len(mfma_mixed_chains(part)) == 1
     # far enough apart (beyond the window) is not flagged
     far = bad.replace("  v_accvgpr_read_b32 v1, a4\n", "  v_nop\n" * 20)
     assert mfma_mixed_chains(far) == []
