@@ -69,12 +69,21 @@ def mfma_partial_overlaps(asm: str):
 _MFMA_DST = re.compile(r"^\s*(v_mfma\S*)\s+([av])\[(\d+):(\d+)\],")
 
 
+_FIRST_REG = re.compile(r"^\s*(\S+)\s+([av])(?:(\d+)\b|\[(\d+):(\d+)\])")
+_READS_FIRST = ("ds_write", "ds_store", "buffer_store", "global_store", "flat_store",
+                "scratch_store", "s_")
+
+
 def mfma_mixed_chains(asm: str, window: int = 16):
     """(line number, text) of every matrix-core instruction with an accumulator-input register
     last written by a matrix-core instruction of another opcode at most `window`
-    instructions earlier (labels, directives and comments not counted)."""
+    instructions earlier (labels, directives and comments not counted).  Any other
+    instruction whose first operand is a vector register (its destination; stores excepted)
+    counts as that register's last writer."""
     bad = []
-    last = {}  # (register file, number) -> (instruction index, opcode) of its last writer
+    # (register file, number) -> (instruction index, opcode) of its last writer; opcode None
+    # for a writer that is not a matrix-core instruction
+    last = {}
     k = 0
     for n, line in enumerate(asm.splitlines(), 1):
         t = line.strip()
@@ -86,13 +95,21 @@ def mfma_mixed_chains(asm: str, window: int = 16):
             op, _, _, _, cf_, c0, c1 = m.groups()
             for r in range(int(c0), int(c1) + 1):
                 prev = last.get((cf_, r))
-                if prev is not None and k - prev[0] <= window and prev[1] != op:
+                if prev is not None and prev[1] is not None and k - prev[0] <= window \
+                        and prev[1] != op:
                     bad.append((n, t))
                     break
         d = _MFMA_DST.match(line)
         if d:
             for r in range(int(d.group(3)), int(d.group(4)) + 1):
                 last[(d.group(2), r)] = (k, d.group(1))
+            continue
+        w = _FIRST_REG.match(line)
+        if w and not w.group(1).startswith(_READS_FIRST):
+            r0 = int(w.group(3) if w.group(3) is not None else w.group(4))
+            r1 = int(w.group(3) if w.group(3) is not None else w.group(5))
+            for r in range(r0, r1 + 1):
+                last[(w.group(2), r)] = (k, None)
     return bad
 
 

@@ -47,6 +47,7 @@ namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // 16-column state blocks per wave: 2 -> D/32 waves (one per SIMD at D = 128, up to 512
 // registers each, every operand fragment feeds two matrix-core instructions); 1 -> D/16
@@ -427,17 +428,17 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     // diagonal, and on it (masked, and replaced by T_ii).
     auto tile_off = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
       const int i = ti * 16 + r16, j0 = tj * 16 + g4;
-      const float Gi = sG[i], nbi = -sB[i];
+      const float Gi = sG[i];
       const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
       f32x4 pf, nf;
       f16* at = SA + tix<F>(ti, tj);
       f16* pt = SP + tix<F>(ti, tj);
-      // below the diagonal every entry is kept (i > j)
+      // below the diagonal every entry is kept (i > j); beta_i is left to T_ii
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
         pf[e] = dec * pa[e];
-        nf[e] = nbi * dec * aa[e];
+        nf[e] = -dec * aa[e];
       }
       *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
       *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(nf);
@@ -480,7 +481,9 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       const f32x4 y1 = mma16h(h2, nt, eye + nf + n2t);
       const f32x4 y2 = mma16h(h4, to_h(y1), y1);    // (I + (N^4)^T) Y1
       const f32x4 y3 = mma16h(h8, to_h(y2), y2);    // (I + (N^8)^T) Y2 = T_ii^T
-      *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(y3);
+      // stored: T_ii diag(beta), i.e. column c of T_ii times beta_c
+      const f32x4 bc = *reinterpret_cast<const f32x4*>(sB + j0);
+      *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(y3 * bc);
     };
     auto tile_out = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
       if (ti != tj)
@@ -609,9 +612,6 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     const f16* arow = SA + r16 * RS + g4;
     const f16* prow = SP + r16 * RS + g4;
     const f16x4 z4 = {0, 0, 0, 0};
-    // A single 16-token block k against the pair register holding it: the A operand's
-    // other half is zero.
-    auto one = [&](f16x4 a, int k) { return (k & 1) ? cat8(z4, a) : cat8(a, z4); };
 
     // v_new of token blocks 2p and 2p + 1 in one fp16 register octet (the B-operand form of
     // a 32-deep product), zero until written; e^{G_last - G} v_new likewise in bf16.
@@ -640,40 +640,33 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       f32x4 acc[NJ], Yi[NJ];
       // e^G of this block's tokens (R and o both use it)
       const f32x4 egs = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
-      {
-        const f32x4 bt = *reinterpret_cast<const f32x4*>(sB + i * 16 + g4);
+      // R_i / beta = V_i - e^G K_i h (beta is applied by the diagonal solve, T_ii diag(beta))
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16* vrow = SV + i * 16 * D + voff[e];
+      for (int e = 0; e < 4; ++e) {
+        const bf16* vrow = SV + i * 16 * D + voff[e];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[j][e] = bt[e] * ((float)vrow[j] - egs[e] * xk[j][e]);
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) Yi[j] = yq[j];
+        for (int j = 0; j < NJ; ++j) acc[j][e] = fmaf(-egs[e], xk[j][e], (float)vrow[j]);
       }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) Yi[j] = yq[j];
       sched_fence();
       if (i + 1 < NT) issue_kq(i + 1);
       if (i == NT / 2 - 1 && more) prefetch(vnext, vh, vstride);
-      // R_i - sum_{jb < i} A_{i,jb} v_jb: blocks before i - 1 first (pairs, then a single),
-      // the block the chain waits on last.
+      // R_i / beta - sum_{jb < i} (A_{i,jb} / beta_i) v_jb in pairs of blocks, the pair
+      // holding v_{i-1} last.  For odd i block i - 1 stands alone; its pair register's upper
+      // half (v_i) is still zero, so the A operand's upper half only has to be finite.
 #pragma unroll
-      for (int jb = 0; jb + 1 <= i - 2; jb += 2) {
+      for (int jb = 0; jb + 1 <= i - 1; jb += 2) {
         const f16x8 a = cat8(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb)),
                              *reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb + 1)));
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, vp[jb / 2][j], acc[j]);
       }
-      if (i >= 2 && ((i - 1) & 1)) {
-        const f16x8 a = one(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 2)), i - 2);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, vp[(i - 2) / 2][j], acc[j]);
-      }
       const f16x4 tf = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i));
-      if (i >= 1) {
-        const f16x8 a = one(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 1)), i - 1);
+      if (i & 1) {
+        const f16x4 a1 = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 1));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, vp[(i - 1) / 2][j], acc[j]);
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(cat8(a1, a1), vp[(i - 1) / 2][j], acc[j]);
       }
       f32x4 vn[NJ];
 #pragma unroll
@@ -683,7 +676,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
 #pragma unroll
         for (int e = 0; e < 4; ++e) vp[i / 2][j][4 * (i & 1) + e] = hv[e];
       }
-      // o_i = scale (e^G Y_i + sum_{jb <= i} P_{i,jb} v_jb)
+      // o_i = scale (e^G Y_i + sum_{jb <= i} P_{i,jb} v_jb); for even i block i stands
+      // alone against a pair register whose upper half is still zero
       f32x4 z[NJ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) z[j] = zero4();
@@ -695,9 +689,9 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         for (int j = 0; j < NJ; ++j) z[j] = mma32h(a, vp[jb / 2][j], z[j]);
       }
       if ((i & 1) == 0) {
-        const f16x8 a = one(*reinterpret_cast<const f16x4*>(prow + tix<F>(i, i)), i);
+        const f16x4 p1 = *reinterpret_cast<const f16x4*>(prow + tix<F>(i, i));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) z[j] = mma32h(a, vp[i / 2][j], z[j]);
+        for (int j = 0; j < NJ; ++j) z[j] = mma32h(cat8(p1, p1), vp[i / 2][j], z[j]);
       }
       // o rows past a partial chunk's end fall outside the output resource and are dropped
 #pragma unroll
@@ -708,10 +702,16 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
           ov[1] = (bf16)(scale * fmaf(egs[e], Yi[1][e], z[1][e]));
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ov), orsrc,
                                                 (int)ooff[e], i * oblock, 0);
-        } else {
-          const bf16 ov = (bf16)(scale * fmaf(egs[e], Yi[0][e], z[0][e]));
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, ov), orsrc,
-                                                (int)ooff[e], i * oblock, 0);
+        } else if ((e & 1) == 0) {
+          // rows e and e + 1 converted by one instruction and stored as its two halves.
+          // The pair is taken apart as a 32-bit word: this compiler turns an element read
+          // of a converted 16-bit vector into a read of element 0.
+          const f32x2_t o2 = {scale * fmaf(egs[e], Yi[0][e], z[0][e]),
+                              scale * fmaf(egs[e + 1], Yi[0][e + 1], z[0][e + 1])};
+          const uint32_t ov = __builtin_bit_cast(uint32_t, __builtin_convertvector(o2, bf16x2_t));
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ov, orsrc, (int)ooff[e], i * oblock, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(ov >> 16), orsrc, (int)ooff[e + 1],
+                                                i * oblock, 0);
         }
       }
       {

@@ -50,6 +50,19 @@ def test_mixed_shape_chain_detected():
             "  v_mfma_f32_16x16x32_f16 a[20:23], v[40:43], v[14:17], 0\n"
             "  v_mfma_f32_16x16x32_f16 a[20:23], v[2:5], v[6:9], a[20:23]\n")
     assert mfma_mixed_chains(over) == []
+    # ... and so is one rewritten by another instruction in between
+    moved = ("  v_mfma_f32_16x16x32_bf16 a[16:19], v[30:33], v[10:13], 0\n"
+             "  v_accvgpr_write_b32 a16, v69\n"
+             "  v_accvgpr_write_b32 a17, v74\n"
+             "  v_accvgpr_write_b32 a18, v75\n"
+             "  v_accvgpr_write_b32 a19, v76\n"
+             "  v_mfma_f32_16x16x32_f16 a[16:19], v[88:91], v[6:9], a[16:19]\n")
+    assert mfma_mixed_chains(moved) == []
+    # a store only reads its first operand
+    kept = ("  v_mfma_f32_16x16x32_bf16 v[16:19], v[30:33], v[10:13], 0\n"
+            "  ds_write_b128 v16, v[20:23]\n"
+            "  v_mfma_f32_16x16x32_f16 v[16:19], v[88:91], v[6:9], v[16:19]\n")
+    assert len(mfma_mixed_chains(kept)) == 1
     # a partly overlapping input is checked register by register
     part = ("  v_mfma_f32_16x16x16_f16 a[4:7], v[10:11], v[6:7], 0\n"
             "  v_mfma_f32_16x16x32_f16 a[0:3], v[40:43], v[14:17], 0\n"
