@@ -105,14 +105,17 @@ __device__ __forceinline__ bf16x8 frag_swz(const bf16* m, int row0, int k0, int 
 }
 
 // Key row of the state held in row r (0..15) of key block db.  The pair of blocks
-// (2p, 2p + 1) covers keys 32p .. 32p + 31, interleaved in groups of four:
-//   row r of block 2p     -> key 32p + 8 (r / 4) + r % 4
-//   row r of block 2p + 1 -> key 32p + 8 (r / 4) + 4 + r % 4.
-// A 32-deep product takes its B operand from a block pair with lane group g holding rows
-// 4g .. 4g + 3 of both blocks, i.e. keys 32p + 8g .. 32p + 8g + 7: the A operand (K or Q
-// rows) is then the standard contiguous 16-byte fragment.
+// (2p, 2p + 1) covers keys 32p .. 32p + 31 in groups of four: rows 4a .. 4a + 3 of the two
+// blocks hold keys 32p + 8a .. 32p + 8a + 7, block 2p the lower four when a is even and
+// the upper four when a is odd (block 2p + 1 the others):
+//   row r of block db -> key 32 (db / 2) + 8 (r / 4) + 4 ((db + r / 4) % 2) + r % 4.
+// A 32-deep K h or Q h product then reads each A operand (K or Q row, keys 32p + 8g ..
+// + 7 in lane group g) as one contiguous 16-byte fragment, with the B operand built from
+// the block pair in the order (2p, 2p + 1) for even g and (2p + 1, 2p) for odd g.  And
+// the transposing K^T reads of the state update, which address one group of four keys per
+// lane, touch both 8-byte halves of the swizzled 16-byte chunks, so every bank is used.
 __device__ __forceinline__ int state_dk(int db, int r) {
-  return 32 * (db >> 1) + 8 * (r >> 2) + 4 * (db & 1) + (r & 3);
+  return 32 * (db >> 1) + 8 * (r >> 2) + 4 * ((db ^ (r >> 2)) & 1) + (r & 3);
 }
 
 // Issue this wave's share of the direct HBM -> LDS copy of one [C][D] tile (rows of one
@@ -329,12 +332,20 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
             st[j][db][e] = h0[hoff + (long)state_dk(db, g4 + e) * D + dv0 + j];
     }
   }
-  // bf16 copy of the chunk-start state in the B-operand form of the K h and Q h products.
-  bf16x4 stb[NJ][NDK];
+  // bf16 copy of the chunk-start state as the B operands of the K h and Q h products: the
+  // pair of key blocks (2p, 2p + 1), swapped in odd lane groups (see state_dk).
+  bf16x8 stbo[NJ][NDK / 2];
+  auto make_stbo = [&]() {
+    const bool odd = (lane_id() >> 4) & 1;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int db = 0; db < NDK; ++db) stb[j][db] = to_b(st[j][db]);
+      for (int p = 0; p < NDK / 2; ++p) {
+        const bf16x4 lo = to_b(st[j][2 * p]), hi = to_b(st[j][2 * p + 1]);
+        stbo[j][p] = odd ? cat8(hi, lo) : cat8(lo, hi);
+      }
+  };
+  make_stbo();
 
   u32x4 vnext[F::KPL];  // next chunk's V, carried into it
   // g and beta of the next chunk (loaded one chunk earlier) and of the one after it, in
@@ -604,6 +615,9 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       voff[e] = swz<D>(g4 + e, dvl);
       ooff[e] = (uint32_t)(((g4 + e) * H * D + dvl) * 2);
     }
+    // one transposing read gives lane (r16, g) its column's V on rows 4g .. 4g + 3 of a
+    // token block (one state column per lane)
+    const int vtoff = swz<D>(g4 + (r16 >> 2), 16 * w + 4 * (r16 & 3));
 #pragma unroll
     for (int db = 0; db < NDK; ++db)
       koff[db] = swz<D>(g4 + (r16 >> 2), state_dk(db, 4 * (r16 & 3)));
@@ -631,8 +645,13 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) xk[j] = yq[j] = zero4();
-      mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(xk, ak, &stb[0][0], NDK);
-      mma_arow<bf16, NDK / 2, NJ, 1, NDK, 1>(yq, aq, &stb[0][0], NDK);
+#pragma unroll
+      for (int p = 0; p < NDK / 2; ++p)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          xk[j] = mma32b(ak.f[p], stbo[j][p], xk[j]);
+          yq[j] = mma32b(aq.f[p], stbo[j][p], yq[j]);
+        }
     };
     issue_kq(0);
 #pragma unroll
@@ -641,11 +660,17 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       // e^G of this block's tokens (R and o both use it)
       const f32x4 egs = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
       // R_i / beta = V_i - e^G K_i h (beta is applied by the diagonal solve, T_ii diag(beta))
+      if constexpr (NJ == 1) {
+        const bf16x4 vv = read_tr<bf16x4>(SV + i * 16 * D + vtoff);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16* vrow = SV + i * 16 * D + voff[e];
+        for (int e = 0; e < 4; ++e) acc[0][e] = fmaf(-egs[e], xk[0][e], (float)vv[e]);
+      } else {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j][e] = fmaf(-egs[e], xk[j][e], (float)vrow[j]);
+        for (int e = 0; e < 4; ++e) {
+          const bf16* vrow = SV + i * 16 * D + voff[e];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[j][e] = fmaf(-egs[e], xk[j][e], (float)vrow[j]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) Yi[j] = yq[j];
@@ -745,10 +770,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         *reinterpret_cast<u32x4*>(SQ + lo + s * RSTEP * D) = qp[s];
       }
     }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int db = 0; db < NDK; ++db) stb[j][db] = to_b(st[j][db]);
+    make_stbo();
     __syncthreads();  // next chunk's tiles and gates visible
   }
 
