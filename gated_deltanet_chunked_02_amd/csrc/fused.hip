@@ -235,8 +235,10 @@ __device__ __forceinline__ bool has_tile(int w, int u) {
 
 
 // Packed lower-triangular storage of 16 x 16 fp16 tiles: tile (ti, tj), tj <= ti, row r,
-// column c at tix(ti, tj) + r * RS + c.  RS = 20 puts the 16 rows that one 4-element
-// fragment access touches on distinct bank pairs.
+// column c at tix(ti, tj) + r * RS + c.  RS must be a multiple of 4 (8-byte accesses); of
+// 16, 20 and 24, RS = 20 measures fastest on gfx950: it staggers the rows of one 8-byte
+// access across the banks, and its 640-byte tile stride puts the two tiles of a paired
+// read on opposite halves of the banks.
 template <class F>
 __device__ __forceinline__ int tix(int ti, int tj) {
   return (ti * (ti + 1) / 2 + tj) * F::TE;
@@ -580,14 +582,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     }
     // The gate wave (an odd wave, one tile fewer than its partner) builds the next
     // chunk's gate vectors in the other buffer, whose last reader was the previous chunk.
-    if (w == kGateWave && more) {
+    if (w == kGateWave && more)
       chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
-#pragma unroll
-      for (int r = 0; r < F::TPL; ++r) {
-        pg[r] = pg2[r];
-        pb[r] = pb2[r];
-      }
-    }
     __syncthreads();  // P, -A, T_ii visible
 
     // ---- P2: per token block i: R_i = beta (V_i - e^G K_i h) and Y_i = Q_i h, the
@@ -760,6 +756,15 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       sched_fence();
     }
     __syncthreads();  // K, Q, V, -A / T_ii and P no longer read
+    if (w == kGateWave) {
+      // g and beta of the chunk after next move up; done here, long after their loads
+      // were issued, because the move waits for them
+#pragma unroll
+      for (int r = 0; r < F::TPL; ++r) {
+        pg[r] = pg2[r];
+        pb[r] = pb2[r];
+      }
+    }
     if (more) {
       // RSTEP is a multiple of the swizzle period, so a lane's swizzle is the same for
       // every s
