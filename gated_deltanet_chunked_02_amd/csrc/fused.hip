@@ -104,18 +104,26 @@ __device__ __forceinline__ bf16x8 frag_swz(const bf16* m, int row0, int k0, int 
   return *reinterpret_cast<const bf16x8*>(m + row0 * D + swz_lane<D>(l, k0 + 8 * (l >> 4)));
 }
 
-// Key row of the state held in row r (0..15) of key block db.  The pair of blocks
-// (2p, 2p + 1) covers keys 32p .. 32p + 31 in groups of four: rows 4a .. 4a + 3 of the two
-// blocks hold keys 32p + 8a .. 32p + 8a + 7, block 2p the lower four when a is even and
-// the upper four when a is odd (block 2p + 1 the others):
-//   row r of block db -> key 32 (db / 2) + 8 (r / 4) + 4 ((db + r / 4) % 2) + r % 4.
-// A 32-deep K h or Q h product then reads each A operand (K or Q row, keys 32p + 8g ..
-// + 7 in lane group g) as one contiguous 16-byte fragment, with the B operand built from
-// the block pair in the order (2p, 2p + 1) for even g and (2p + 1, 2p) for odd g.  And
-// the transposing K^T reads of the state update, which address one group of four keys per
-// lane, touch both 8-byte halves of the swizzled 16-byte chunks, so every bank is used.
+// Key row of the state held in row r (0..15) of key block db.  Row group a = r / 4 of the
+// block pair (2p, 2p + 1) covers the eight keys of 16-byte chunk
+//   kchunk(p, a) = 2p + a % 2 + (D/16) (a / 2)       (a bijection onto the D/8 chunks),
+// block 2p holding the lower four keys for even a and the upper four for odd a (block
+// 2p + 1 the others):
+//   row r of block db -> key 8 kchunk(db / 2, r / 4) + 4 ((db + r / 4) % 2) + r % 4.
+// A 32-deep K h or Q h product then reads each A operand (K or Q row, chunk kchunk(p, g)
+// in lane group g) as one contiguous 16-byte fragment, with the B operand built from the
+// block pair in the order (2p, 2p + 1) for even g and (2p + 1, 2p) for odd g.  The
+// transposing K^T reads of the state update address one group of four keys per lane;
+// served 32 lanes (eight token rows) at a time, they are conflict-free when the two key
+// groups in the same half of their chunks lie in chunks that differ in bit 3, which the
+// row-swizzle then spreads over all 16 chunk positions (D = 128).
+template <int D>
+__device__ __forceinline__ int kchunk(int p, int a) {
+  return 2 * p + (a & 1) + (D / 16) * (a >> 1);
+}
+template <int D>
 __device__ __forceinline__ int state_dk(int db, int r) {
-  return 32 * (db >> 1) + 8 * (r >> 2) + 4 * ((db ^ (r >> 2)) & 1) + (r & 3);
+  return 8 * kchunk<D>(db >> 1, r >> 2) + 4 * ((db ^ (r >> 2)) & 1) + (r & 3);
 }
 
 // Issue this wave's share of the direct HBM -> LDS copy of one [C][D] tile (rows of one
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
   seq_span(cu, n, T, Ttot, cs0, L);
   const int nchunks = (L + C - 1) / C;
 
-  // State: st[j][db] holds rows dk = state_dk(db, 4 (l/16) + e) of column
+  // State: st[j][db] holds rows dk = state_dk<D>(db, 4 (l/16) + e) of column
   // 16 NJ w + NJ (l%16) + j.
   f32x4 st[NJ][NDK];
   const long hoff = ((long)n * H + h) * D * D;
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            st[j][db][e] = h0[hoff + (long)state_dk(db, g4 + e) * D + dv0 + j];
+            st[j][db][e] = h0[hoff + (long)state_dk<D>(db, g4 + e) * D + dv0 + j];
     }
   }
   // bf16 copy of the chunk-start state as the B operands of the K h and Q h products: the
@@ -616,7 +624,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     const int vtoff = swz<D>(g4 + (r16 >> 2), 16 * w + 4 * (r16 & 3));
 #pragma unroll
     for (int db = 0; db < NDK; ++db)
-      koff[db] = swz<D>(g4 + (r16 >> 2), state_dk(db, 4 * (r16 & 3)));
+      koff[db] = swz<D>(g4 + (r16 >> 2), state_dk<D>(db, 4 * (r16 & 3)));
     const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D, (uint32_t)(len * H * D * 2));
     const int oblock = 16 * H * D * 2;  // bytes per 16-token block of o
     const f16* arow = SA + r16 * RS + g4;
@@ -636,8 +644,10 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       ARow<bf16, NDK / 2> ak, aq;
 #pragma unroll
       for (int p = 0; p < NDK / 2; ++p) {
-        ak.f[p] = frag_swz<D>(SK, tb * 16, 32 * p, l);
-        aq.f[p] = frag_swz<D>(SQ, tb * 16, 32 * p, l);
+        // chunk kchunk(p, l / 16) of row tb * 16 + l % 16
+        const int ko = tb * 16 * D + swz_lane<D>(l, 8 * kchunk<D>(p, l >> 4));
+        ak.f[p] = *reinterpret_cast<const bf16x8*>(SK + ko);
+        aq.f[p] = *reinterpret_cast<const bf16x8*>(SQ + ko);
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) xk[j] = yq[j] = zero4();
@@ -788,7 +798,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          ht[hoff + (long)state_dk(db, g4 + e) * D + dv0 + j] = st[j][db][e];
+          ht[hoff + (long)state_dk<D>(db, g4 + e) * D + dv0 + j] = st[j][db][e];
   }
 }
 
