@@ -446,11 +446,9 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     // accumulator form holds, in lane l, row i = 16 ti + l%16 and columns j = 16 tj + 4
     // (l/16) + e: the k-contiguous operand form of that row of P and A.
     // Gate, mask and store one tile (pa = its K Q^T part, aa = its K K^T part): below the
-    // diagonal, and on it (masked, and replaced by T_ii).
-    auto tile_off = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
-      const int i = ti * 16 + r16, j0 = tj * 16 + g4;
-      const float Gi = sG[i];
-      const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
+    // diagonal, and on it (masked, and replaced by T_ii).  Gi = G log2(e) of this lane's row
+    // and Gj of its four columns are read by the caller ahead of time.
+    auto tile_off = [&](int ti, int tj, f32x4 pa, f32x4 aa, float Gi, f32x4 Gj) {
       f32x4 pf, nf;
       f16* at = SA + tix<F>(ti, tj);
       f16* pt = SP + tix<F>(ti, tj);
@@ -464,10 +462,10 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
       *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(nf);
     };
-    auto tile_diag = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
+    auto tile_diag = [&](int ti, int tj, f32x4 pa, f32x4 aa, float Gi, f32x4 Gj) {
       const int i = ti * 16 + r16, j0 = tj * 16 + g4;
-      const float Gi = sG[i], nbi = -sB[i];
-      const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + j0);
+      const float nbi = -sB[i];
+      const f32x4 bc = *reinterpret_cast<const f32x4*>(sB + j0);
       f32x4 pf, nf;
       f16* at = SA + tix<F>(ti, tj);
       f16* pt = SP + tix<F>(ti, tj);
@@ -503,14 +501,15 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       const f32x4 y2 = mma16h(h4, to_h(y1), y1);    // (I + (N^4)^T) Y1
       const f32x4 y3 = mma16h(h8, to_h(y2), y2);    // (I + (N^8)^T) Y2 = T_ii^T
       // stored: T_ii diag(beta), i.e. column c of T_ii times beta_c
-      const f32x4 bc = *reinterpret_cast<const f32x4*>(sB + j0);
       *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = to_h(y3 * bc);
     };
     auto tile_out = [&](int ti, int tj, f32x4 pa, f32x4 aa) {
+      const float Gi = sG[ti * 16 + r16];
+      const f32x4 Gj = *reinterpret_cast<const f32x4*>(sG + tj * 16 + g4);
       if (ti != tj)
-        tile_off(ti, tj, pa, aa);
+        tile_off(ti, tj, pa, aa, Gi, Gj);
       else
-        tile_diag(ti, tj, pa, aa);
+        tile_diag(ti, tj, pa, aa, Gi, Gj);
     };
     if constexpr (NT == 2 * F::NW || NT == F::NW) {
       // Block rows pair up as (p, NT - 1 - p), NT + 1 tiles per pair.  With NT = 2 NW wave
@@ -545,7 +544,10 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
             qf[kk] = frag_swz<D>(SQ, ti * 16, 32 * kk, l);
             kfi[kk] = frag_swz<D>(SK, ti * 16, 32 * kk, l);
           }
-          auto prods = [&](int tj, f32x4& pa, f32x4& aa) {
+          const float Gi = sG[ti * 16 + r16];
+          // a tile's products and its column gates, issued one tile ahead
+          auto prods = [&](int tj, f32x4& pa, f32x4& aa, f32x4& Gj) {
+            Gj = *reinterpret_cast<const f32x4*>(sG + tj * 16 + g4);
             pa = aa = zero4();
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
@@ -554,19 +556,20 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
               aa = Mma<bf16>::mma(kf, kfi[kk], aa);
             }
           };
-          f32x4 pa, aa;
-          prods(t0, pa, aa);
+          f32x4 pa, aa, Gj;
+          prods(t0, pa, aa, Gj);
           for (int tj = t0; tj < t1; ++tj) {
-            f32x4 pn, an;
-            prods(tj + 1, pn, an);
-            tile_off(ti, tj, pa, aa);
+            f32x4 pn, an, Gn;
+            prods(tj + 1, pn, an, Gn);
+            tile_off(ti, tj, pa, aa, Gi, Gj);
             pa = pn;
             aa = an;
+            Gj = Gn;
           }
           if (t1 == ti)
-            tile_diag(ti, ti, pa, aa);
+            tile_diag(ti, ti, pa, aa, Gi, Gj);
           else
-            tile_off(ti, t1, pa, aa);
+            tile_off(ti, t1, pa, aa, Gi, Gj);
         }
         sched_fence();
       }
