@@ -289,9 +289,6 @@ __device__ __forceinline__ V4 read_tr(const void* p) {
   return __builtin_bit_cast(V4, r);
 }
 
-// Order this wave's earlier LDS writes before its later LDS reads of the same data.
-__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 template <int D, int C, int NJ_>
 __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -469,23 +466,27 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       f32x4 pf, nf;
       f16* at = SA + tix<F>(ti, tj);
       f16* pt = SP + tix<F>(ti, tj);
-      // masked entries use a clamped exponent, so they never overflow
+      // masked entries use a clamped exponent, so they never overflow.  The raw product
+      // k_i . k_j of a diagonal tile is symmetric (the same fp32 sum for (i, j) and (j, i)),
+      // so each lane also gates it for the mirrored position (row j0 + e, column i): nf
+      // holds N^T in accumulator form (N = -A_ii strictly lower) and nfm holds N itself,
+      // the two orientations the products below need, without a trip through LDS.
+      f32x4 nfm;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float dec = __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f));
+        const float decm = __builtin_amdgcn_exp2f(fminf(Gj[e] - Gi, 0.f));
         pf[e] = (i >= j0 + e ? dec : 0.f) * pa[e];
         nf[e] = (i > j0 + e ? nbi * dec : 0.f) * aa[e];
+        nfm[e] = (j0 + e > i ? -bc[e] * decm : 0.f) * aa[e];
       }
       *reinterpret_cast<f16x4*>(pt + r16 * RS + g4) = to_h(pf);
       const f16x4 nt = to_h(nf);
-      *reinterpret_cast<f16x4*>(at + r16 * RS + g4) = nt;
-      // T_ii = (I + N + N^2 + ... + N^15) = (I + N)(I + N^2)(I + N^4)(I + N^8) with
-      // N = -A_ii strictly lower.  nt is N^T in accumulator form; N itself is read back
-      // transposed.  A product X Y takes X^T and Y in accumulator form, so both
-      // orientations of each power are kept; the result is built as T^T, whose
-      // accumulator form is the row-major storage of T.
-      lds_fence();
-      const f16x4 nn = read_tr<f16x4>(at + (g4 + (r16 >> 2)) * RS + 4 * (r16 & 3));
+      const f16x4 nn = to_h(nfm);
+      // T_ii = (I + N + N^2 + ... + N^15) = (I + N)(I + N^2)(I + N^4)(I + N^8).  A product
+      // X Y takes X^T and Y in accumulator form, so both orientations of each power are
+      // kept; the result is built as T^T, whose accumulator form is the row-major storage
+      // of T.
       f32x4 eye;
 #pragma unroll
       for (int e = 0; e < 4; ++e) eye[e] = (g4 + e == r16) ? 1.f : 0.f;
