@@ -663,54 +663,12 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
           yq[j] = mma32b(aq.f[p], stbo[j][p], yq[j]);
         }
     };
-    issue_kq(0);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      f32x4 acc[NJ], Yi[NJ];
-      // e^G of this block's tokens (R and o both use it)
-      const f32x4 egs = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
-      // R_i / beta = V_i - e^G K_i h (beta is applied by the diagonal solve, T_ii diag(beta))
-      if constexpr (NJ == 1) {
-        const bf16x4 vv = read_tr<bf16x4>(SV + i * 16 * D + vtoff);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[0][e] = fmaf(-egs[e], xk[0][e], (float)vv[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16* vrow = SV + i * 16 * D + voff[e];
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[j][e] = fmaf(-egs[e], xk[j][e], (float)vrow[j]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) Yi[j] = yq[j];
-      sched_fence();
-      if (i + 1 < NT) issue_kq(i + 1);
-      if (i == NT / 2 - 1 && more) prefetch(vnext, vh, vstride);
-      // R_i / beta - sum_{jb < i} (A_{i,jb} / beta_i) v_jb in pairs of blocks, the pair
-      // holding v_{i-1} last.  For odd i block i - 1 stands alone; its pair register's upper
-      // half (v_i) is still zero, so the A operand's upper half only has to be finite.
-#pragma unroll
-      for (int jb = 0; jb + 1 <= i - 1; jb += 2) {
-        const f16x8 a = cat8(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb)),
-                             *reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb + 1)));
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, vp[jb / 2][j], acc[j]);
-      }
-      const f16x4 tf = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i));
-      if (i & 1) {
-        const f16x4 a1 = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 1));
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(cat8(a1, a1), vp[(i - 1) / 2][j], acc[j]);
-      }
-      f32x4 vn[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        vn[j] = mma16h(tf, to_h(acc[j]), zero4());
-        const f16x4 hv = to_h(vn[j]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vp[i / 2][j][4 * (i & 1) + e] = hv[e];
-      }
+    // Block i's output and state-update work (z, o, e^{G_last - G} v_i, and the update of
+    // the pair (i - 1, i) for odd i).  It runs one block late, inside block i + 1, where it
+    // is independent of that block's substitution chain and fills its latency.  It comes
+    // before block i + 1's solve in program order, so for even i the pair register of
+    // v_i still has a zero upper half.
+    auto tail = [&](int i, const f32x4* vn, const f32x4* Yi, f32x4 egs) {
       // o_i = scale (e^G Y_i + sum_{jb <= i} P_{i,jb} v_jb); for even i block i stands
       // alone against a pair register whose upper half is still zero
       f32x4 z[NJ];
@@ -767,8 +725,61 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
           for (int j = 0; j < NJ; ++j) st[j][db] = mma32b(a, vbp[i / 2][j], st[j][db]);
         }
       }
+    };
+    f32x4 vprev[NJ], yprev[NJ], egsprev;
+    issue_kq(0);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      f32x4 acc[NJ], Yi[NJ];
+      // e^G of this block's tokens (R and o both use it)
+      const f32x4 egs = *reinterpret_cast<const f32x4*>(sEG + i * 16 + g4);
+      // R_i / beta = V_i - e^G K_i h (beta is applied by the diagonal solve, T_ii diag(beta))
+      if constexpr (NJ == 1) {
+        const bf16x4 vv = read_tr<bf16x4>(SV + i * 16 * D + vtoff);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[0][e] = fmaf(-egs[e], xk[0][e], (float)vv[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16* vrow = SV + i * 16 * D + voff[e];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[j][e] = fmaf(-egs[e], xk[j][e], (float)vrow[j]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) Yi[j] = yq[j];
+      sched_fence();
+      if (i + 1 < NT) issue_kq(i + 1);
+      if (i == NT / 2 - 1 && more) prefetch(vnext, vh, vstride);
+      if (i >= 1) tail(i - 1, vprev, yprev, egsprev);
+      // R_i / beta - sum_{jb < i} (A_{i,jb} / beta_i) v_jb in pairs of blocks, the pair
+      // holding v_{i-1} last.  For odd i block i - 1 stands alone; its pair register's upper
+      // half (v_i) is still zero, so the A operand's upper half only has to be finite.
+#pragma unroll
+      for (int jb = 0; jb + 1 <= i - 1; jb += 2) {
+        const f16x8 a = cat8(*reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb)),
+                             *reinterpret_cast<const f16x4*>(arow + tix<F>(i, jb + 1)));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(a, vp[jb / 2][j], acc[j]);
+      }
+      const f16x4 tf = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i));
+      if (i & 1) {
+        const f16x4 a1 = *reinterpret_cast<const f16x4*>(arow + tix<F>(i, i - 1));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[j] = mma32h(cat8(a1, a1), vp[(i - 1) / 2][j], acc[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        vprev[j] = mma16h(tf, to_h(acc[j]), zero4());
+        const f16x4 hv = to_h(vprev[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vp[i / 2][j][4 * (i & 1) + e] = hv[e];
+        yprev[j] = Yi[j];
+      }
+      egsprev = egs;
       sched_fence();
     }
+    tail(NT - 1, vprev, yprev, egsprev);
     __syncthreads();  // K, Q, V, -A / T_ii and P no longer read
     if (w == kGateWave) {
       // g and beta of the chunk after next move up; done here, long after their loads
