@@ -780,6 +780,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       sched_fence();
     }
     tail(NT - 1, vprev, yprev, egsprev);
+    // the next chunk's B operands depend only on this wave's final state
+    make_stbo();
     __syncthreads();  // K, Q, V, -A / T_ii and P no longer read
     if (w == kGateWave) {
       // g and beta of the chunk after next move up; done here, long after their loads
@@ -800,7 +802,6 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         *reinterpret_cast<u32x4*>(SQ + lo + s * RSTEP * D) = qp[s];
       }
     }
-    make_stbo();
     __syncthreads();  // next chunk's tiles and gates visible
   }
 
