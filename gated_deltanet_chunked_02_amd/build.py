@@ -113,16 +113,22 @@ def mfma_mixed_chains(asm: str, window: int = 16):
     return bad
 
 
+# Per-source extra flags.  The fused kernel is scheduled with LLVM's max-ILP strategy
+# (measured about 0.7 % faster on gfx950 than the default); every source still passes
+# the assembly check below.
+EXTRA = {"fused.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))
     if src.endswith(".hip"):
         asm = os.path.join(BUILD, os.path.splitext(src)[0] + "." + ARCH + ".s")
-        cmd = [hipcc()] + flags() + ["--cuda-device-only", "-S", os.path.join(CSRC, src),
-                                     "-o", asm]
+        cmd = [hipcc()] + flags() + EXTRA.get(src, []) + ["--cuda-device-only", "-S",
+                                                          os.path.join(CSRC, src), "-o", asm]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError("hipcc -S failed for %s:\n%s" % (src, res.stderr))
