@@ -266,3 +266,38 @@ def test_single_token_and_scale(variant):
     inp2["scale"] = 2.0 * inp["scale"]
     o2, _ = run_gdn(inp2, variant=variant)
     assert rel_l2(to64(o2), 2.0 * to64(o)) <= 1e-2
+
+
+# ------------------------------------------------------------------ dtype and gate extremes
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+@pytest.mark.parametrize("C", [64, 128])
+def test_bf16_qkv_with_fp32_beta(variant, C):
+    """beta may be fp32 while q, k, v are bf16 (its own load and widening path)."""
+    inp = draw(B=2, T=2 * C + 37, H=4, Hg=2, Dk=128, C=C, seed=41 + C, h0_std=0.05,
+               beta_dtype="f32")
+    assert inp["beta"].dtype == torch.float32 and inp["q"].dtype == torch.bfloat16
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant=variant)
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "fp32 beta " + variant)
+    log(test="fp32_beta", variant=variant, C=C, o_rel=eo, ht_rel=eh)
+
+
+@pytest.mark.parametrize("variant", ["staged", "fused"])
+@pytest.mark.parametrize("regime", ["strong_decay", "no_decay_full_beta"])
+def test_gate_extremes(variant, regime):
+    """Strong decay (g about -5 per token: e^G underflows to zero inside a chunk, and the
+    masked exponents of the diagonal tiles are far out of range) and no decay with beta = 1
+    (the delta rule's full overwrite at every token)."""
+    inp = draw(B=2, T=300, H=4, Hg=4, Dk=128, C=128, seed=57, h0_std=0.05)
+    gen = torch.Generator().manual_seed(58)
+    if regime == "strong_decay":
+        x = torch.randn(inp["g"].shape, generator=gen) - 5.0
+        inp["g"] = torch.nn.functional.logsigmoid(x).to(inp["g"].dtype)
+    else:
+        inp["g"] = torch.zeros_like(inp["g"])
+        inp["beta"] = torch.ones_like(inp["beta"])
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant=variant)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(ht).all()
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, regime + " " + variant)
+    log(test="gate_extremes", regime=regime, variant=variant, o_rel=eo, ht_rel=eh)
