@@ -630,6 +630,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     for (int db = 0; db < NDK; ++db)
       koff[db] = swz<D>(g4 + (r16 >> 2), state_dk<D>(db, 4 * (r16 & 3)));
     const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D, (uint32_t)(len * H * D * 2));
+    // transposed output layout (one column block per wave): token r16, columns 16 w + 4 g ..
+    const uint32_t otoff = (uint32_t)((r16 * H * D + 16 * w + g4) * 2);
     const int oblock = 16 * H * D * 2;  // bytes per 16-token block of o
     const f16* arow = SA + r16 * RS + g4;
     const f16* prow = SP + r16 * RS + g4;
@@ -660,7 +662,11 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           xk[j] = mma32b(ak.f[p], stbo[j][p], xk[j]);
-          yq[j] = mma32b(aq.f[p], stbo[j][p], yq[j]);
+          // with one column block per wave Y is made transposed (token per lane), like z
+          if constexpr (NJ == 1)
+            yq[j] = mma32b(stbo[j][p], aq.f[p], yq[j]);
+          else
+            yq[j] = mma32b(aq.f[p], stbo[j][p], yq[j]);
         }
     };
     // Block i's output and state-update work (z, o, e^{G_last - G} v_i, and the update of
@@ -679,32 +685,38 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
         const f16x8 a = cat8(*reinterpret_cast<const f16x4*>(prow + tix<F>(i, jb)),
                              *reinterpret_cast<const f16x4*>(prow + tix<F>(i, jb + 1)));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) z[j] = mma32h(a, vp[jb / 2][j], z[j]);
+        for (int j = 0; j < NJ; ++j)
+          z[j] = NJ == 1 ? mma32h(vp[jb / 2][j], a, z[j]) : mma32h(a, vp[jb / 2][j], z[j]);
       }
       if ((i & 1) == 0) {
         const f16x4 p1 = *reinterpret_cast<const f16x4*>(prow + tix<F>(i, i));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) z[j] = mma32h(cat8(p1, p1), vp[i / 2][j], z[j]);
+        for (int j = 0; j < NJ; ++j)
+          z[j] = NJ == 1 ? mma32h(vp[i / 2][j], cat8(p1, p1), z[j])
+                         : mma32h(cat8(p1, p1), vp[i / 2][j], z[j]);
       }
       // o rows past a partial chunk's end fall outside the output resource and are dropped
+      if constexpr (NJ == 1) {
+        // z and Y are transposed: lane (r16, g) holds token 16 i + r16, columns
+        // 16 w + 4 g .. + 3, stored as one 8-byte word (pairs converted as 32-bit words:
+        // this compiler turns an element read of a converted 16-bit vector into a read of
+        // element 0)
+        const float egt = sEG[i * 16 + r16];
+        const f32x2_t o01 = {scale * fmaf(egt, Yi[0][0], z[0][0]), scale * fmaf(egt, Yi[0][1], z[0][1])};
+        const f32x2_t o23 = {scale * fmaf(egt, Yi[0][2], z[0][2]), scale * fmaf(egt, Yi[0][3], z[0][3])};
+        const uint32_t w01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(o01, bf16x2_t));
+        const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(o23, bf16x2_t));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 ow = {w01, w23};
+        __builtin_amdgcn_raw_buffer_store_b64(ow, orsrc, (int)otoff, i * oblock, 0);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (NJ == 2) {
+        for (int e = 0; e < 4; ++e) {
           bf16x2_t ov;
           ov[0] = (bf16)(scale * fmaf(egs[e], Yi[0][e], z[0][e]));
           ov[1] = (bf16)(scale * fmaf(egs[e], Yi[1][e], z[1][e]));
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ov), orsrc,
                                                 (int)ooff[e], i * oblock, 0);
-        } else if ((e & 1) == 0) {
-          // rows e and e + 1 converted by one instruction and stored as its two halves.
-          // The pair is taken apart as a 32-bit word: this compiler turns an element read
-          // of a converted 16-bit vector into a read of element 0.
-          const f32x2_t o2 = {scale * fmaf(egs[e], Yi[0][e], z[0][e]),
-                              scale * fmaf(egs[e + 1], Yi[0][e + 1], z[0][e + 1])};
-          const uint32_t ov = __builtin_bit_cast(uint32_t, __builtin_convertvector(o2, bf16x2_t));
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ov, orsrc, (int)ooff[e], i * oblock, 0);
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(ov >> 16), orsrc, (int)ooff[e + 1],
-                                                i * oblock, 0);
         }
       }
       {
