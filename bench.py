@@ -38,7 +38,7 @@ PMC_TRAFFIC = {
     "workload": "bf16_16x8192_h32_d128_c128",
     "fetch_kib": 1674206.58, "write_kib": 1081346.58,
     "fetch_scale": 2.0, "write_scale": 1.0,
-    "sources_sha256": "77fd06bb197f62fcfb27ad9ebaec4d7c0e7866f0adf3116e3aa0ca800d07cb54",
+    "sources_sha256": "17785ca016152a5049291c58bad055343e894af4ccb3b9d6789772c3526b09ce",
 }
 FUSED_SOURCES = ("fused.hip", "gdn_device.h", "gdn_solve.h")
 

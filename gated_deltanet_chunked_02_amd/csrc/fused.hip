@@ -4,11 +4,10 @@
 //
 // One workgroup owns one (sequence, value head) and walks its chunks in order; nothing
 // crosses workgroups, so no grid barrier is needed (the page's all-core SyncAll barrier
-// has no counterpart here).  D/32 waves, one per SIMD; wave w owns 32 state columns as two
-// 16-wide matrix-core column blocks, for all Dk rows, kept as fp32 accumulator tiles.
-// Column c of block j of wave w is state column dv = 32 w + 2 c + j, so each lane's two
-// columns are adjacent in memory (4-byte V / o and 8-byte h0 / ht accesses).  Per chunk,
-// with G the in-chunk prefix sum of g and h the state at the chunk start:
+// has no counterpart here).  With NJ = 1 (the default) there are D/16 waves, two per SIMD
+// at D = 128; wave w owns the 16 state columns 16 w .. 16 w + 15 for all Dk rows, kept as
+// fp32 accumulator tiles (NJ = 2: D/32 waves of two 16-column blocks).  Per chunk, with G
+// the in-chunk prefix sum of g and h the state at the chunk start:
 //
 //   A     = (K K^T) * beta_i e^{G_i-G_j}, i > j             (scaled_dot_kkt, section 4.2)
 //   R     = diag(beta) (V - diag(e^G) K h)                   (wy_fast + chunk_h, 4.3)
@@ -17,27 +16,32 @@
 //   h     = e^{G_last} h + K^T (e^{G_last-G} v_new)          (chunk_h, TileLang page step 1)
 //
 // (I + A) v_new = R is the same as v_new = U - W h with U = T diag(beta) V, W = T diag(beta
-// e^G) K and T = (I + A)^-1, but T is never formed: each wave solves for its own 32 columns
-// by blocked forward substitution over the C/16 token blocks,
+// e^G) K and T = (I + A)^-1, but T is never formed: each wave solves for its own columns
+// by blocked forward substitution over the C/16 token blocks.  Every row i of A carries
+// beta_i, so with A = diag(beta) A~ the step reads
 //
-//   v_i = T_ii (R_i - sum_{j<i} A_ij v_j),   T_ii = (I + A_ii)^-1,
+//   v_i = T_ii diag(beta_i) (R_i / beta_i - sum_{j<i} A~_ij v_j),   T_ii = (I + A_ii)^-1,
 //
 // where the 16 x 16 diagonal inverses come from the nilpotent product
-// (I + A_ii)^-1 = (I - A_ii)(I + A_ii^2)(I + A_ii^4)(I + A_ii^8) on the matrix cores.  The
-// solve therefore needs no barrier and no cross-wave data beyond A, and each token block's
-// output and state-update contribution are issued as soon as its v_i is known.
+// (I + A_ii)^-1 = (I - A_ii)(I + A_ii^2)(I + A_ii^4)(I + A_ii^8) on the matrix cores, and
+// R_i / beta_i = V_i - e^G K_i h needs no beta.  The solve needs no barrier and no
+// cross-wave data beyond A.
 //
 // Two phases and three barriers per chunk:
-//   P1  lower tiles of K Q^T and K K^T -> P and -A in LDS (packed fp16 16 x 16 tiles; the
-//       owner of a diagonal tile replaces it with T_ii); R and Y = Q h for this wave's
-//       columns into registers (fp32).  Barrier.  Q and V are now dead: the next chunk's
-//       Q and V are copied HBM -> LDS directly (global_load_lds) and its K is loaded into
-//       registers, all landing while P2 runs.
-//   P2  substitution, o = scale (e^G Y + P v_new) and h += K^T (d v_new) block by block
-//       (K^T fragments by transposing LDS reads).  Barrier; the prefetched K is written to
-//       LDS, wave 0 prepares the next chunk's gate vectors; barrier.
-// K, Q, V rows are unpadded with the 16-byte chunk index XOR-swizzled by the row, which
-// keeps fragment reads conflict-free and matches the lane order of the direct-to-LDS copy.
+//   P1  lower tiles of K Q^T and K K^T -> P and -A~ in LDS (packed fp16 16 x 16 tiles; the
+//       owner of a diagonal tile replaces it with T_ii diag(beta)); one wave also builds
+//       the next chunk's gate vectors.  Barrier.
+//   P2  per token block i: K_i h and Q_i h (issued one block ahead), R_i, the substitution
+//       step; block i - 1's output products, o store, and (per pair of blocks) the state
+//       update h += K^T (e^{G_last-G} v_new) run one block late, independent of block i's
+//       chain (K^T fragments by transposing LDS reads).  Barrier; the prefetched K and Q
+//       are written to LDS; barrier.
+// The next chunk's K, Q and V are loaded into registers during this one (K at its start,
+// Q at the start of P2, V half-way through P2, each bounded by the chunk's valid tokens so
+// a partial chunk reads zeros); V is written to LDS at the start of the next chunk, which
+// reads it only in P2; g and beta are loaded two chunks ahead.  K, Q, V rows are unpadded
+// with the 16-byte chunk index XOR-swizzled by the row, which keeps 16-byte fragment reads
+// conflict-free.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     // Next chunk's K, Q, V into registers, written to LDS once this chunk is done with its
     // tiles.  The loads are spread over the chunk (K now, Q at the start of the second
     // phase, V half-way through it) so the memory pipeline never holds all of them at
-    // once.  Wave 0 also loads the next chunk's g and beta.
+    // once.  The gate wave loads g and beta two chunks ahead.
     const bool more = m + 1 < nchunks;
     const int csn = cs + C, lenn = min(C, L - (m + 1) * C);
     u32x4 kp[F::KPL], qp[F::KPL];
@@ -598,10 +602,11 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
       chunk_gates<C>(sGates + (buf ^ 1) * 4 * C, sMisc + (buf ^ 1), pg, pb, beta_f32, lenn, l);
     __syncthreads();  // P, -A, T_ii visible
 
-    // ---- P2: per token block i: R_i = beta (V_i - e^G K_i h) and Y_i = Q_i h, the
-    // forward substitution step, o_i = scale (e^G Y_i + sum_{j<=i} P_ij v_j) and
-    // h += K^T (e^{G_last - G} v_new) (two blocks per step).  The products for block i + 1
-    // are issued before block i's dependent chain, so they fill its latency.
+    // ---- P2: per token block i: R_i / beta = V_i - e^G K_i h and Y_i = Q_i h, the forward
+    // substitution step, o_i = scale (e^G Y_i + sum_{j<=i} P_ij v_j) and
+    // h += K^T (e^{G_last - G} v_new) (two blocks per step).  The K h and Q h products for
+    // block i + 1 are issued before block i's dependent chain, and block i's output and
+    // update work runs inside block i + 1, so both fill the chain's latency.
     phase();
     if (more) prefetch(qp, qh, qstride);
     sched_fence();
@@ -638,7 +643,8 @@ __global__ __launch_bounds__(D * 4 / NJ_) void k_fused(
     const f16x4 z4 = {0, 0, 0, 0};
 
     // v_new of token blocks 2p and 2p + 1 in one fp16 register octet (the B-operand form of
-    // a 32-deep product), zero until written; e^{G_last - G} v_new likewise in bf16.
+    // a 32-deep product, or with one column block per wave the A-operand form of v_new^T
+    // in the output products), zero until written; e^{G_last - G} v_new likewise in bf16.
     f16x8 vp[NT / 2][NJ];
     bf16x8 vbp[NT / 2][NJ];
 #pragma unroll
