@@ -103,6 +103,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// An off-diagonal tile product of the side work: rows of block BI, columns of block BJ,
+// K K^T (KIND 0) or Q K^T (KIND 1).
+template <int BI, int BJ, int KIND>
+struct OffTile {
+  static constexpr int bi = BI, bj = BJ, kind = KIND;
+};
+
 // Packed lower-triangular storage of 16 x 16 fp16 tiles: tile (ti, tj), tj <= ti, row r,
 // column c at tix(ti, tj) + r * RS + c.
 template <class F>
@@ -157,10 +164,13 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   __shared__ __align__(16) bf16 SV[2][F::TILE];
   __shared__ __align__(16) f16 SA[2][F::NLOW * TE];  // -A~ below the diagonal, T_ii diag(beta) on it
   __shared__ __align__(16) f16 SP[2][F::NLOW * TE];  // scale (Q K^T * e^{Gc_i-Gc_j})_{i>=j}
-  __shared__ __align__(16) float SEF[2][CS];  // e^{Gc_t}
-  __shared__ __align__(16) float SEO[2][CS];  // scale e^{Gc_t}
-  __shared__ __align__(16) float SDC[2][CS];  // e^{Gc_end - Gc_t}
-  __shared__ float SGE[2];                    // e^{Gc_end}
+  // Gate vectors, made by one wave two chunks ahead (buffer = chunk % 3), per token t:
+  __shared__ __align__(16) float SGC[3][CS];  // Gc_t log2(e)
+  __shared__ __align__(16) float SBT[3][CS];  // beta_t
+  __shared__ __align__(16) float SEF[3][CS];  // e^{Gc_t}
+  __shared__ __align__(16) float SEO[3][CS];  // scale e^{Gc_t}
+  __shared__ __align__(16) float SDC[3][CS];  // e^{Gc_end - Gc_t}
+  __shared__ float SGE[3];                    // e^{Gc_end}
 
   int cs0, L;
   seq_span(cu, n, T, Ttot, cs0, L);
@@ -213,20 +223,32 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     for (int s = 0; s < F::KPL; ++s)
       *reinterpret_cast<u32x4*>(tile + lds_lo + s * F::RSTEP * D) = src[s];
   };
-  // g of token l (lane l, all CS = 64 tokens of a chunk) and beta of token 16 b + l%16,
-  // b = the diagonal block of this wave's side work (zero past the sequence end); beta kept
-  // as raw bits until used.
+  // g and beta of token l (lane l, all CS = 64 tokens of a chunk; zero past the sequence
+  // end), loaded by the gate wave, which turns them into the chunk's gate vectors.
   static_assert(CS == kWave, "one gate per lane");
-  const int sblk = w0 % NB;
+  constexpr int kGateWave = NW - 1;
   auto load_gate = [&](float& gv, uint32_t& bv, int cstart, int clen) {
     const int bsz = beta_f32 ? 4 : 2;
     const auto rg = buf_rsrc(g + (long)cstart * H + h, (uint32_t)(clen * H * 4));
     const auto rb = buf_rsrc(static_cast<const char*>(beta) + ((long)cstart * H + h) * bsz,
                              (uint32_t)(clen * H * bsz));
-    const int t = 16 * sblk + (lane_id() & 15);
-    gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, lane_id() * H * 4, 0, 0));
+    const int t = lane_id();
+    gv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, t * H * 4, 0, 0));
     bv = beta_f32 ? __builtin_amdgcn_raw_buffer_load_b32(rb, t * H * 4, 0, 0)
                   : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, t * H * 2, 0, 0);
+  };
+  // chunk_cumsum and the gate vectors of one chunk into gate buffer gb (gate wave only)
+  auto make_gates = [&](int gb, float gv, uint32_t bvr) {
+    const int t = lane_id();
+    const float Gc = wave_incl_scan(gv) * kLog2e;
+    const float gend = __shfl(Gc, CS - 1, kWave);
+    const float ef = __builtin_amdgcn_exp2f(Gc);
+    SGC[gb][t] = Gc;
+    SBT[gb][t] = __builtin_bit_cast(float, beta_f32 ? bvr : bvr << 16);
+    SEF[gb][t] = ef;
+    SEO[gb][t] = scale * ef;
+    SDC[gb][t] = __builtin_amdgcn_exp2f(gend - Gc);
+    if (t == 0) SGE[gb] = __builtin_amdgcn_exp2f(gend);
   };
 
   // Side work for one chunk (K/Q buffer kb, outputs in buffer ob).  Diagonal block b: the
@@ -234,30 +256,16 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   // -A~ (no beta: T_ii diag(beta) applies it) and P.  Tile (bi, bj) = K_bj (Q or K)_bi^T in
   // accumulator form holds, in lane l, row i = 16 bi + l%16 and columns j = 16 bj + 4 (l/16)
   // + e: the row-major storage of the tile.
-  auto side = [&](int kb, int ob, float gv, uint32_t bvr) {
+  auto side = [&](int kb, int gb, int ob) {
     const int l = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
     const int r16 = l & 15, g4 = 4 * (l >> 4);
-    const float Gc = wave_incl_scan(gv) * kLog2e;  // Gc log2(e) of token l
     const bf16* Kx = SK[kb];
     const bf16* Qx = SQ[kb];
+    const float* Gc = SGC[gb];
     auto diag = [&](int b) {
-      const float bv = __builtin_bit_cast(float, beta_f32 ? bvr : bvr << 16);
-      const float Gi = __shfl(Gc, 16 * b + r16, kWave);
-      f32x4 Gj, bc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Gj[e] = __shfl(Gc, 16 * b + g4 + e, kWave);
-        bc[e] = __shfl(bv, g4 + e, kWave);
-      }
-      const float gend = __shfl(Gc, CS - 1, kWave);
-      if (l < 16) {
-        const int t = 16 * b + l;
-        const float ef = __builtin_amdgcn_exp2f(Gi);
-        SEF[ob][t] = ef;
-        SEO[ob][t] = scale * ef;
-        SDC[ob][t] = __builtin_amdgcn_exp2f(gend - Gi);
-        if (t == 0) SGE[ob] = __builtin_amdgcn_exp2f(gend);
-      }
+      const float Gi = Gc[16 * b + r16], bv = SBT[gb][16 * b + r16];
+      const f32x4 Gj = *reinterpret_cast<const f32x4*>(Gc + 16 * b + g4);
+      const f32x4 bc = *reinterpret_cast<const f32x4*>(&SBT[gb][16 * b + g4]);
       bf16x8 kf[D / 32];
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) kf[kk] = frag_swz<D>(Kx, 16 * b, 32 * kk, l);
@@ -301,40 +309,56 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       const f32x4 y3 = mma16h(h8, to_h(y2), y2);         // (I + (N^8)^T) Y2 = T^T
       *reinterpret_cast<f16x4*>(&SA[ob][tix<F>(b, b) + r16 * RS + g4]) = to_h(y3 * bc);
     };
-    // Off-diagonal products: pair q = (bi, bj), bj < bi, in the order (1,0) (2,0) (2,1)
-    // (3,0) (3,1) (3,2); product u = 2 q + (0: K K^T -> -A~, 1: Q K^T -> P).
-    auto offdiag = [&](int u) {
-      const int qq = u >> 1, kind = u & 1;
-      const int bi = qq < 1 ? 1 : (qq < 3 ? 2 : 3);
-      const int bj = qq - bi * (bi - 1) / 2;
-      const float Gi = __shfl(Gc, 16 * bi + r16, kWave);
-      f32x4 Gj;
+    // Off-diagonal tile (bi, bj), bj < bi: K K^T -> -A~ (kind 0) or Q K^T -> P (kind 1).
+    // Each wave's products are fixed at compile time and all its fragment reads come before
+    // its tile stores, so fragments shared by its products are read once.
+    auto offdiag = [&](auto... prods) {
+      constexpr int NPR = sizeof...(prods);
+      constexpr int bi_[NPR] = {decltype(prods)::bi...};
+      constexpr int bj_[NPR] = {decltype(prods)::bj...};
+      constexpr int kd_[NPR] = {decltype(prods)::kind...};
+      f32x4 acc[NPR];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Gj[e] = __shfl(Gc, 16 * bj + g4 + e, kWave);
-      const bf16* Bx = kind ? Qx : Kx;
-      f32x4 acc = zero4();
+      for (int u = 0; u < NPR; ++u) acc[u] = zero4();
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk)
-        acc = mma32b(frag_swz<D>(Kx, 16 * bj, 32 * kk, l), frag_swz<D>(Bx, 16 * bi, 32 * kk, l), acc);
-      const float f = kind ? scale : -1.f;
-      f32x4 x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = f * __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f)) * acc[e];
-      f16* dst = kind ? SP[ob] : SA[ob];
-      *reinterpret_cast<f16x4*>(dst + tix<F>(bi, bj) + r16 * RS + g4) = to_h(x);
+        for (int u = 0; u < NPR; ++u)
+          acc[u] = mma32b(frag_swz<D>(Kx, 16 * bj_[u], 32 * kk, l),
+                          frag_swz<D>(kd_[u] ? Qx : Kx, 16 * bi_[u], 32 * kk, l), acc[u]);
+#pragma unroll
+      for (int u = 0; u < NPR; ++u) {
+        const float Gi = Gc[16 * bi_[u] + r16];
+        const f32x4 Gj = *reinterpret_cast<const f32x4*>(Gc + 16 * bj_[u] + g4);
+        const float f = kd_[u] ? scale : -1.f;
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[e] = f * __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f)) * acc[u][e];
+        f16* dst = kd_[u] ? SP[ob] : SA[ob];
+        *reinterpret_cast<f16x4*>(dst + tix<F>(bi_[u], bj_[u]) + r16 * RS + g4) = to_h(x);
+      }
+    };
+    // the twelve products, three per share, grouped so that each share reuses operands
+    auto offdiag_share = [&](int i) {
+      if (i == 0)
+        offdiag(OffTile<1, 0, 0>(), OffTile<1, 0, 1>(), OffTile<2, 0, 0>());
+      else if (i == 1)
+        offdiag(OffTile<2, 0, 1>(), OffTile<2, 1, 0>(), OffTile<2, 1, 1>());
+      else if (i == 2)
+        offdiag(OffTile<3, 0, 0>(), OffTile<3, 0, 1>(), OffTile<3, 1, 0>());
+      else
+        offdiag(OffTile<3, 1, 1>(), OffTile<3, 2, 0>(), OffTile<3, 2, 1>());
     };
     static_assert(F::NOFF == 12 && (NW == 2 * NB || NW == NB), "side work dealt evenly");
     if constexpr (NW == 2 * NB) {
-      if (w < NB) {
+      if (w < NB)
         diag(w);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 3; ++u) offdiag(3 * (w - NB) + u);
-      }
+      else
+        offdiag_share(w - NB);
     } else {
       diag(w);
-#pragma unroll
-      for (int u = 0; u < 3; ++u) offdiag(3 * w + u);
+      offdiag_share(w);
     }
   };
 
@@ -352,32 +376,36 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   const int oblock = 16 * H * D * 2;  // bytes per 16-token block of o
 
   u32x4 kp[F::KPL], qp[F::KPL], vp[F::KPL];
-  float gv1 = 0.f, gv2 = 0.f;
-  uint32_t bv1 = 0, bv2 = 0;
+  float gvn = 0.f;
+  uint32_t bvn = 0;
   if (nchunks > 0) {
     load_tile(kp, kh, qstride, cs0, min(CS, L));
     load_tile(qp, qh, qstride, cs0, min(CS, L));
     load_tile(vp, vh, vstride, cs0, min(CS, L));
-    float gv0;
-    uint32_t bv0;
-    load_gate(gv0, bv0, cs0, min(CS, L));
+    if (w0 == kGateWave) {
+      load_gate(gvn, bvn, cs0, min(CS, L));
+      make_gates(0, gvn, bvn);
+      if (nchunks > 1) {
+        load_gate(gvn, bvn, cs0 + CS, min(CS, L - CS));
+        make_gates(1, gvn, bvn);
+      }
+    }
     store_tile(SK[0], kp);
     store_tile(SQ[0], qp);
     store_tile(SV[0], vp);
     if (nchunks > 1) {
       load_tile(kp, kh, qstride, cs0 + CS, min(CS, L - CS));
       load_tile(qp, qh, qstride, cs0 + CS, min(CS, L - CS));
-      load_gate(gv1, bv1, cs0 + CS, min(CS, L - CS));
       store_tile(SK[1], kp);
       store_tile(SQ[1], qp);
     }
     __syncthreads();
-    side(0, 0, gv0, bv0);
+    side(0, 0, 0);
     make_stbo();
     __syncthreads();
   }
 
-  int kb = 0;  // K/Q buffer of chunk m (m % 3)
+  int kb = 0;  // K/Q and gate buffer of chunk m (m % 3)
   for (int m = 0; m < nchunks; ++m) {
     const int cs = cs0 + m * CS;
     const int len = min(CS, L - m * CS);
@@ -386,11 +414,11 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     const bool more1 = m + 1 < nchunks, more2 = m + 2 < nchunks;
     // the next chunk's side work first, then the loads of later chunks, so the side work
     // does not hold registers with loads in flight
-    if (more1) side(kb1, tb ^ 1, gv1, bv1);
+    if (more1) side(kb1, kb1, tb ^ 1);
     sched_fence();
     if (more2) {
       const int c2 = cs + 2 * CS, len2 = min(CS, L - (m + 2) * CS);
-      load_gate(gv2, bv2, c2, len2);
+      if (w0 == kGateWave) load_gate(gvn, bvn, c2, len2);
       load_tile(kp, kh, qstride, c2, len2);
       load_tile(qp, qh, qstride, c2, len2);
     }
@@ -404,9 +432,9 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     const bf16* vt = SV[tb] + vtoff;
     const f16* Ac = SA[tb] + r16 * RS + g4;
     const f16* Pc = SP[tb] + r16 * RS + g4;
-    const float* efp = SEF[tb] + g4;
-    const float* eop = SEO[tb] + r16;
-    const float* dcp = SDC[tb] + g4;
+    const float* efp = SEF[kb] + g4;
+    const float* eop = SEO[kb] + r16;
+    const float* dcp = SDC[kb] + g4;
     const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D, (uint32_t)(len * H * D * 2));
 
     // K h and Q h of every block with the chunk-start state; Y = Q h is made transposed
@@ -466,7 +494,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     // h = e^{Gc_end} h + K^T (e^{Gc_end-Gc} v_new), two blocks per 32-deep product (K^T
     // fragments by transposing LDS reads)
     {
-      const float ge = SGE[tb];
+      const float ge = SGE[kb];
 #pragma unroll
       for (int db = 0; db < NDK; ++db) st[db] *= ge;
 #pragma unroll
@@ -484,8 +512,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     if (more2) {
       store_tile(SK[kb2], kp);
       store_tile(SQ[kb2], qp);
-      gv1 = gv2;
-      bv1 = bv2;
+      if (w0 == kGateWave) make_gates(kb2, gvn, bvn);
     }
     if (more1) store_tile(SV[tb ^ 1], vp);
     __syncthreads();
