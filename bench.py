@@ -36,16 +36,16 @@ F32_PEAK_TFLOPS = 157.3
 # once they differ.
 PMC_TRAFFIC = {
     "workload": "bf16_16x8192_h32_d128_c128",
-    "fetch_kib": 1674206.58, "write_kib": 1081346.58,
+    "fetch_kib": 1674406.92, "write_kib": 1081380.03,
     "fetch_scale": 2.0, "write_scale": 1.0,
-    "sources_sha256": "17785ca016152a5049291c58bad055343e894af4ccb3b9d6789772c3526b09ce",
+    "sources_sha256": "d2ab46de292e51109e30167b018176f5a6464dcb22d47453bbdda6c093d0834b",
 }
-FUSED_SOURCES = ("fused.hip", "gdn_device.h", "gdn_solve.h")
+FUSED_SOURCES = ("fused.hip", "gdn_device.h", "gdn_internal.h")
 
 
 def fused_sources_sha256() -> str:
     """sha256 over the sha256sum-style listing of the fused kernel's sources (the same
-    digest as `sha256sum fused.hip gdn_device.h gdn_solve.h | sha256sum` run from the
+    digest as `sha256sum fused.hip gdn_device.h gdn_internal.h | sha256sum` run from the
     repository root with the package-relative paths)."""
     import hashlib
     lines = []
@@ -237,7 +237,7 @@ def main():
     if variant == "staged":
         kernel = "staged pipeline (8 launches; per-kernel split in profiles/)"
     else:
-        kernel = "k_fused (D=%d, C=%d)" % (w.Dk, w.C)
+        kernel = "k_fused (D=%d, 64-token chunks)" % w.Dk
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS}
