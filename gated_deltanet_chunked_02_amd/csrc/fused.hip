@@ -24,8 +24,8 @@
 // (I + A_ii)^-1 = (I - A_ii)(I + A_ii^2)(I + A_ii^4)(I + A_ii^8) on the matrix cores.
 //
 // The state-independent work of a chunk (its lower 16 x 16 tiles of K K^T and Q K^T, gated
-// and masked, the inverses T_ii and the gate vectors) is done one chunk ahead, split over
-// the waves, while the current chunk is solved; K and Q are therefore triple-buffered in
+// and masked, the inverses T_ii and the gate vectors) is done one chunk ahead, by waves 0-3
+// and one gate wave, while the current chunk is solved; K and Q are therefore triple-buffered in
 // LDS: chunk m is being solved, chunk m + 1's tiles are being made, chunk m + 2 is being
 // loaded (through registers, with buffer loads bounded at the sequence end, so a partial
 // chunk reads zeros).  One barrier per chunk.
@@ -339,7 +339,10 @@ __global__ __launch_bounds__(D * 4) void k_fused(
         *reinterpret_cast<f16x4*>(dst + tix<F>(bi_[u], bj_[u]) + r16 * RS + g4) = to_h(x);
       }
     };
-    // the twelve products, three per share, grouped so that each share reuses operands
+    // The twelve products in four shares of three, grouped so that each share reuses
+    // operands.  All tile work goes to waves 0 .. NB - 1: each SIMD issues its older wave
+    // first, so the younger waves NB .. 2 NB - 1, which only solve (and, for the last one,
+    // make the gate vectors), set the pace of the chunk.
     auto offdiag_share = [&](int i) {
       if (i == 0)
         offdiag(OffTile<1, 0, 0>(), OffTile<1, 0, 1>(), OffTile<2, 0, 0>());
@@ -351,12 +354,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
         offdiag(OffTile<3, 1, 1>(), OffTile<3, 2, 0>(), OffTile<3, 2, 1>());
     };
     static_assert(F::NOFF == 12 && (NW == 2 * NB || NW == NB), "side work dealt evenly");
-    if constexpr (NW == 2 * NB) {
-      if (w < NB)
-        diag(w);
-      else
-        offdiag_share(w - NB);
-    } else {
+    if (w < NB) {
       diag(w);
       offdiag_share(w);
     }
