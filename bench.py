@@ -163,7 +163,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="headline", choices=sorted(gdn_inputs.WORKLOADS))
-    ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged", "segmented"])
     ap.add_argument("--chunk", type=int, default=0,
                     help="override the workload's chunk size C (64 or 128)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -201,7 +201,7 @@ def main():
     if ws_bytes:
         ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
         desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
-    variant = "fused" if ws_bytes == 0 else "staged"
+    variant = gdn.gdn_resolved_variant(desc, cu)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -236,6 +236,8 @@ def main():
     bound = "hbm" if by / HBM_PEAK_GBS >= fl / (peak_tf * 1e3) else "mfma"
     if variant == "staged":
         kernel = "staged pipeline (8 launches; per-kernel split in profiles/)"
+    elif variant == "segmented":
+        kernel = "segmented: three k_fused passes over the segments and the segment scan"
     else:
         kernel = "k_fused (D=%d, 64-token chunks)" % w.Dk
     if bound == "hbm":

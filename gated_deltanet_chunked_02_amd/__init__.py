@@ -19,7 +19,7 @@ import os
 __all__ = [
     "GdnDesc", "GdnError", "load", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size",
     "gdn_stage_buffer", "gdn_status_string", "gdn_version", "chunk_gated_delta_rule",
-    "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH",
+    "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH", "gdn_resolved_variant",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_HIP"}
 F32, BF16 = 0, 1
-VARIANTS = {"auto": 0, "staged": 1, "fused": 2}
+VARIANTS = {"auto": 0, "staged": 1, "fused": 2, "segmented": 3}
 BUFFERS = {"chunk_table": 0, "seq_chunks": 1, "g_cum": 2, "g_t": 3, "beta_t": 4, "A": 5,
            "Tinv": 6, "W": 7, "U": 8, "h_c": 9, "v_new": 10}
 
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_version.restype = ctypes.c_int32
     lib.gdn_version.argtypes = []
+    lib.gdn_resolved_variant.restype = ctypes.c_int32
+    lib.gdn_resolved_variant.argtypes = [ctypes.POINTER(GdnDesc), P]
     _lib = lib
     return lib
 
@@ -84,6 +86,15 @@ def gdn_status_string(status: int) -> str:
 
 def gdn_version() -> int:
     return int(load().gdn_version())
+
+
+def gdn_resolved_variant(desc: GdnDesc, cu_seqlens=None) -> str:
+    """Name of the variant gdn_chunk_fwd runs with this descriptor (AUTO resolved)."""
+    v = int(load().gdn_resolved_variant(ctypes.byref(desc), _ptr(cu_seqlens)))
+    for name, code in VARIANTS.items():
+        if code == v and name != "auto":
+            return name
+    raise GdnError(1, "gdn_resolved_variant")
 
 
 def gdn_chunk_fwd_workspace_size(desc: GdnDesc) -> int:

@@ -28,7 +28,8 @@ gdn_status check_desc(const gdn_desc* d, gdn::Problem* p) {
   if (d->H % d->Hg != 0) return GDN_ERR_INVALID_ARG;
   if (d->qkv_dtype != GDN_F32 && d->qkv_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   if (d->beta_dtype != GDN_F32 && d->beta_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (d->variant < GDN_VARIANT_AUTO || d->variant > GDN_VARIANT_FUSED) return GDN_ERR_INVALID_ARG;
+  if (d->variant < GDN_VARIANT_AUTO || d->variant > GDN_VARIANT_SEGMENTED)
+    return GDN_ERR_INVALID_ARG;
   if (d->stop_after < 0 || d->stop_after > 6) return GDN_ERR_INVALID_ARG;
   const int C = d->chunk == 0 ? 128 : d->chunk;
   if (C != 64 && C != 128) return GDN_ERR_UNSUPPORTED;
@@ -55,13 +56,76 @@ gdn_status check_desc(const gdn_desc* d, gdn::Problem* p) {
   return GDN_OK;
 }
 
+// Segments of the segmented variant: S segments of Ls tokens (a multiple of the fused
+// kernel's 64-token chunk; the last may be shorter) per sequence of a dense batch.
+struct SegPlan {
+  int S = 1, Ls = 0;
+};
+
+constexpr int kFusedChunk = 64;
+constexpr int kTargetPairs = 256;    // (segment, head) pairs that fill the GPU: one per CU
+constexpr int kAutoMinSegments = 4;  // AUTO segments only when it gives at least 4 segments
+constexpr int kAutoMinSegLen = 1024; // of at least 1024 tokens (three passes over the data)
+
+SegPlan seg_plan(const gdn::Problem& p, bool forced) {
+  SegPlan sp;
+  const long pairs = (long)p.N * p.H;
+  if (pairs <= 0 || p.T <= 0) return sp;
+  const long want = (kTargetPairs + pairs - 1) / pairs;
+  const long maxs = (p.T + kFusedChunk - 1) / kFusedChunk;
+  long S = want < maxs ? want : maxs;
+  if (S < 1) S = 1;
+  long Ls = (p.T + S - 1) / S;
+  Ls = (Ls + kFusedChunk - 1) / kFusedChunk * kFusedChunk;
+  S = (p.T + Ls - 1) / Ls;
+  if (!forced && (S < kAutoMinSegments || Ls < kAutoMinSegLen)) return sp;
+  sp.S = (int)S;
+  sp.Ls = (int)Ls;
+  return sp;
+}
+
+// Workspace of the segmented variant: the segment table, then b, M and h_in per
+// (segment, head), each [N S, H, D, D] fp32.
+struct SegLayout {
+  size_t cu, b, M, h_in, total;
+};
+
+SegLayout seg_layout(const gdn::Problem& p, const SegPlan& sp) {
+  SegLayout L;
+  const size_t ns = (size_t)p.N * sp.S;
+  const size_t st = ns * p.H * (size_t)p.D * p.D * sizeof(float);
+  L.cu = 0;
+  L.b = align_up((ns + 1) * sizeof(int32_t));
+  L.M = L.b + align_up(st);
+  L.h_in = L.M + align_up(st);
+  L.total = L.h_in + align_up(st);
+  return L;
+}
+
+bool seg_ok(const gdn::Problem& p, const gdn_desc* d, bool dense) {
+  return dense && gdn::fused_supported(p) && d->stop_after == 0 &&
+         (long long)p.N * p.T <= (1LL << 30);
+}
+
 // Variant actually run (after AUTO resolution), or -1 if the request cannot be served.
-int resolve_variant(const gdn_desc* d, const gdn::Problem& p) {
+// `dense`: no cu_seqlens.  `ws`: the workspace the call brings (AUTO picks the segmented
+// variant only when it pays off and the workspace is large enough; else the fused one).
+int resolve_variant(const gdn_desc* d, const gdn::Problem& p, bool dense, bool ws_check) {
   const bool fused_ok = gdn::fused_supported(p) && d->stop_after == 0;
   switch (d->variant) {
     case GDN_VARIANT_FUSED: return fused_ok ? GDN_VARIANT_FUSED : -1;
     case GDN_VARIANT_STAGED: return GDN_VARIANT_STAGED;
-    default: return fused_ok ? GDN_VARIANT_FUSED : GDN_VARIANT_STAGED;
+    case GDN_VARIANT_SEGMENTED: return seg_ok(p, d, dense) ? GDN_VARIANT_SEGMENTED : -1;
+    default: {
+      if (!fused_ok) return GDN_VARIANT_STAGED;
+      if (seg_ok(p, d, dense) && seg_plan(p, false).S > 1) {
+        if (!ws_check) return GDN_VARIANT_SEGMENTED;
+        const size_t need = seg_layout(p, seg_plan(p, false)).total;
+        if (d->workspace && d->workspace_bytes >= need && aligned(d->workspace, kAlign))
+          return GDN_VARIANT_SEGMENTED;
+      }
+      return GDN_VARIANT_FUSED;
+    }
   }
 }
 
@@ -96,10 +160,15 @@ extern "C" {
 size_t gdn_chunk_fwd_workspace_size(const gdn_desc* d, gdn_status* status) {
   gdn::Problem p;
   gdn_status s = check_desc(d, &p);
-  if (s == GDN_OK && resolve_variant(d, p) < 0) s = GDN_ERR_UNSUPPORTED;
+  // the size query cannot see cu_seqlens: N other than 0 or B marks a packed batch
+  const bool dense = d && (d->N == 0 || d->N == d->B);
+  if (s == GDN_OK && resolve_variant(d, p, dense, false) < 0) s = GDN_ERR_UNSUPPORTED;
   if (status) *status = s;
   if (s != GDN_OK) return 0;
-  if (resolve_variant(d, p) == GDN_VARIANT_FUSED) return 0;
+  const int v = resolve_variant(d, p, dense, false);
+  if (v == GDN_VARIANT_FUSED) return 0;
+  if (v == GDN_VARIANT_SEGMENTED)
+    return seg_layout(p, seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED)).total;
   Layout L;
   staged_layout(p, &L);
   return L.total;
@@ -136,7 +205,7 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
   } else if (d->N != 0 && d->N != d->B) {
     return GDN_ERR_INVALID_ARG;
   }
-  const int variant = resolve_variant(d, p);
+  const int variant = resolve_variant(d, p, cu_seqlens == nullptr, true);
   if (variant < 0) return GDN_ERR_UNSUPPORTED;
   p.scale = scale;
   p.q = q;
@@ -153,6 +222,46 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
   hipError_t e;
   if (variant == GDN_VARIANT_FUSED) {
     e = gdn::launch_fused(p, stream);
+  } else if (variant == GDN_VARIANT_SEGMENTED) {
+    const SegPlan sp = seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED);
+    const SegLayout L = seg_layout(p, sp);
+    if (!d->workspace || d->workspace_bytes < L.total || !aligned(d->workspace, kAlign))
+      return GDN_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(d->workspace);
+    int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + L.cu);
+    float* bm = reinterpret_cast<float*>(ws + L.b);
+    float* mm = reinterpret_cast<float*>(ws + L.M);
+    float* hin = reinterpret_cast<float*>(ws + L.h_in);
+    // every segment is a sequence of a packed batch over the same tokens
+    gdn::Problem ps = p;
+    ps.N = p.N * sp.S;
+    ps.cu = cu_seg;
+    e = gdn::launch_segment_table(cu_seg, p.N, p.T, sp.S, sp.Ls, stream);
+    // b: each segment from a zero state; M: from the identity with v taken as zero
+    if (e == hipSuccess) {
+      gdn::Problem pb = ps;
+      pb.h0 = nullptr;
+      pb.ht = bm;
+      pb.fused_flags = gdn::kFusedNoOutput;
+      e = gdn::launch_fused(pb, stream);
+    }
+    if (e == hipSuccess) {
+      gdn::Problem pm = ps;
+      pm.h0 = nullptr;
+      pm.ht = mm;
+      pm.fused_flags = gdn::kFusedNoOutput | gdn::kFusedZeroV | gdn::kFusedH0Identity;
+      e = gdn::launch_fused(pm, stream);
+    }
+    // h_in of every segment, and the final state, by composing the maps in order
+    if (e == hipSuccess)
+      e = gdn::launch_segment_scan(mm, bm, p.h0, hin, p.ht, p.N, sp.S, p.H, p.D, stream);
+    // o of every segment from its true initial state
+    if (e == hipSuccess) {
+      gdn::Problem po = ps;
+      po.h0 = hin;
+      po.ht = nullptr;
+      e = gdn::launch_fused(po, stream);
+    }
   } else {
     Layout L;
     staged_layout(p, &L);
@@ -174,6 +283,18 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
     e = gdn::launch_staged(p, st, d->stop_after, stream);
   }
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int32_t gdn_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens) {
+  gdn::Problem p;
+  if (check_desc(d, &p) != GDN_OK) return -1;
+  if (cu_seqlens) {
+    if (d->B != 1 || d->N < 0) return -1;
+    p.N = d->N;
+  } else if (d->N != 0 && d->N != d->B) {
+    return -1;
+  }
+  return resolve_variant(d, p, cu_seqlens == nullptr, true);
 }
 
 const char* gdn_status_string(gdn_status s) {

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const void* __restrict__ beta, int beta_f32,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, bf16* __restrict__ o,
-    float* __restrict__ ht, int T, int Ttot, int H, int Hg, float scale) {
+    float* __restrict__ ht, int T, int Ttot, int H, int Hg, float scale, int flags) {
   typedef FusedCfg<D> F;
   constexpr int CS = F::CS, NB = F::NB, NDK = F::NDK, RS = F::RS, TE = F::TE, CPR = F::CPR;
   constexpr int NW = F::NW;
@@ -175,6 +175,8 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   int cs0, L;
   seq_span(cu, n, T, Ttot, cs0, L);
   const int nchunks = (L + CS - 1) / CS;
+  // rows of V a chunk reads (none when V is taken as zero)
+  auto vlen = [&](int len) { return (flags & kFusedZeroV) ? 0 : len; };
 
   const int l0 = lane_id(), w0 = __builtin_amdgcn_readfirstlane(wave_id());
   const int r16_0 = l0 & 15, g4_0 = 4 * (l0 >> 4);
@@ -186,7 +188,13 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     const int dv0 = 16 * w0 + r16_0;
 #pragma unroll
     for (int db = 0; db < NDK; ++db) st[db] = zero4();
-    if (h0) {
+    if (flags & kFusedH0Identity) {
+      // the identity as initial state: the final state is then the chunked map's matrix
+#pragma unroll
+      for (int db = 0; db < NDK; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[db][e] = state_dk<D>(db, g4_0 + e) == dv0 ? 1.f : 0.f;
+    } else if (h0) {
 #pragma unroll
       for (int db = 0; db < NDK; ++db)
 #pragma unroll
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   if (nchunks > 0) {
     load_tile(kp, kh, qstride, cs0, min(CS, L));
     load_tile(qp, qh, qstride, cs0, min(CS, L));
-    load_tile(vp, vh, vstride, cs0, min(CS, L));
+    load_tile(vp, vh, vstride, cs0, vlen(min(CS, L)));
     if (w0 == kGateWave) {
       load_gate(gvn, bvn, cs0, min(CS, L));
       make_gates(0, gvn, bvn);
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       load_tile(kp, kh, qstride, c2, len2);
       load_tile(qp, qh, qstride, c2, len2);
     }
-    if (more1) load_tile(vp, vh, vstride, cs + CS, min(CS, L - (m + 1) * CS));
+    if (more1) load_tile(vp, vh, vstride, cs + CS, vlen(min(CS, L - (m + 1) * CS)));
     sched_fence();
 
     const int l = lane_id();
@@ -433,7 +441,8 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     const float* efp = SEF[kb] + g4;
     const float* eop = SEO[kb] + r16;
     const float* dcp = SDC[kb] + g4;
-    const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D, (uint32_t)(len * H * D * 2));
+    const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D,
+                                (flags & kFusedNoOutput) ? 0u : (uint32_t)(len * H * D * 2));
 
     // K h and Q h of every block with the chunk-start state; Y = Q h is made transposed
     // (token per lane), like the output product below
@@ -534,7 +543,7 @@ hipError_t run_fused(const Problem& p, hipStream_t st) {
   k_fused<D><<<grid, FusedCfg<D>::NTH, 0, st>>>(
       static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.v),
       p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot,
-      p.H, p.Hg, p.scale);
+      p.H, p.Hg, p.scale, p.fused_flags);
   return hipGetLastError();
 }
 

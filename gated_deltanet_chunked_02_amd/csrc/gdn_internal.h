@@ -23,7 +23,13 @@ struct Problem {
   const int32_t* cu;
   void* o;
   float* ht;
+  int fused_flags = 0;  // kFused* bits, for the passes of the segmented variant
 };
+
+// Fused-kernel modes used by the segmented variant's passes.
+constexpr int kFusedZeroV = 1;       // v is read as zeros
+constexpr int kFusedH0Identity = 2;  // h0 is the identity (Dk == Dv), not read from memory
+constexpr int kFusedNoOutput = 4;    // o is not written
 
 // Intermediates of the staged variant (device pointers inside the caller's workspace).
 struct Stages {
@@ -43,5 +49,10 @@ struct Stages {
 hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st);
 bool fused_supported(const Problem& p);
 hipError_t launch_fused(const Problem& p, hipStream_t st);
+// Segmented variant: segment table (cu_seg[n S + s] = n T + min(s Ls, T), cu_seg[N S] =
+// N T) and the sequential composition of the segments' affine state maps.
+hipError_t launch_segment_table(int32_t* cu_seg, int N, int T, int S, int Ls, hipStream_t st);
+hipError_t launch_segment_scan(const float* M, const float* b, const float* h0, float* h_in,
+                               float* ht, int N, int S, int H, int D, hipStream_t st);
 
 }  // namespace gdn

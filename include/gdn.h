@@ -56,9 +56,19 @@ typedef enum gdn_status {
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 typedef enum gdn_variant {
-  GDN_VARIANT_AUTO = 0,   /* fused when built for the shape, otherwise staged */
-  GDN_VARIANT_STAGED = 1, /* seven launches, intermediates in the workspace */
-  GDN_VARIANT_FUSED = 2   /* one launch, one workgroup per (sequence, head) */
+  GDN_VARIANT_AUTO = 0,      /* fused when built for the shape, otherwise staged; segmented
+                                for a dense batch of few long sequences when the workspace
+                                for it is given (fused otherwise)                          */
+  GDN_VARIANT_STAGED = 1,    /* seven launches, intermediates in the workspace */
+  GDN_VARIANT_FUSED = 2,     /* one launch, one workgroup per (sequence, head) */
+  GDN_VARIANT_SEGMENTED = 3  /* dense batches only: every sequence split into S segments that
+                                run in parallel.  The state recurrence is affine in the
+                                initial state, h_end = M h_in + b; the fused kernel finds M
+                                (from h_in = I, v = 0) and b (from h_in = 0) of every segment,
+                                a scan composes h_in(s+1) = M_s h_in(s) + b_s (fp32), and a
+                                last fused pass writes o.  Three passes over the data, S-fold
+                                parallelism (the long-prompt case of the FlashQLA how-to,
+                                section 8.3).  Needs the workspace reported for it.        */
 } gdn_variant;
 
 /* Intermediate buffers of the staged variant, readable through gdn_stage_buffer(). */
@@ -88,13 +98,21 @@ typedef struct gdn_desc {
   int32_t beta_dtype; /* gdn_dtype of beta                                                */
   int32_t variant;    /* gdn_variant                                                      */
   int32_t stop_after; /* staged only: 0 = all stages, k in 1..6 = stop after stage k      */
-  void* workspace;    /* device memory for the staged variant (may be NULL for fused)     */
+  void* workspace;    /* device memory for the staged and segmented variants (256-byte
+                         aligned; may be NULL for fused)                                  */
   size_t workspace_bytes;
 } gdn_desc;
 
-/* Bytes of workspace the variant chosen by d->variant needs (0 for the fused variant);
- * host-only, no device work.  Returns 0 and sets *status on an invalid descriptor. */
+/* Bytes of workspace the variant chosen by d->variant needs (0 for the fused variant; for
+ * AUTO, what AUTO picks when given that much).  The query cannot see cu_seqlens: a
+ * descriptor with N == 0 or N == B is taken as a dense batch.  Host-only, no device work.
+ * Returns 0 and sets *status on an invalid descriptor. */
 size_t gdn_chunk_fwd_workspace_size(const gdn_desc* d, gdn_status* status);
+
+/* The gdn_variant that gdn_chunk_fwd(d, ..., cu_seqlens, ...) runs with this descriptor and
+ * workspace (AUTO resolved), or -1 if the call would be refused.  Only the nullness of
+ * cu_seqlens is used; host-only, no device work. */
+int32_t gdn_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens);
 
 /* The forward pass.  q, k, v, g, beta, o are required; h0 (zero state), cu_seqlens (dense
  * batch) and ht (final state not written) may be NULL.  scale multiplies o (Dk^-0.5 is the

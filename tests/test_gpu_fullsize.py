@@ -69,6 +69,14 @@ def test_full_size_sampled(name, over, count):
                                        scale=inp["scale"], initial_state=inp["h0"],
                                        cu_seqlens=inp["cu_seqlens"], chunk_size=w.C)
     torch.cuda.synchronize()
+    # the variant AUTO ran (chunk_gated_delta_rule gives it the workspace it asks for)
+    desc = gdn.make_desc(inp["q"], inp["v"], inp["beta"], inp["cu_seqlens"], w.C, "auto")
+    wsb = gdn.gdn_chunk_fwd_workspace_size(desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+    if ws is not None:
+        desc.workspace, desc.workspace_bytes = ws.data_ptr(), wsb
+    variant = gdn.gdn_resolved_variant(desc, inp["cu_seqlens"])
+    del ws
     pairs = sample_pairs(inp, count, w.seed)
     ref = oracle_pairs(inp, pairs, nthreads=min(16, len(pairs)))
     worst_o = worst_h = 0.0
@@ -80,7 +88,7 @@ def test_full_size_sampled(name, over, count):
         assert eo <= TOL_BF16_O, "%s pair %s o rel-L2 %.3g" % (w.name, (n, h), eo)
         assert eh <= TOL_BF16_HT, "%s pair %s ht rel-L2 %.3g" % (w.name, (n, h), eh)
         worst_o, worst_h = max(worst_o, eo), max(worst_h, eh)
-    rec = dict(test="full_size", workload=w.name, over=over, pairs=len(ref),
+    rec = dict(test="full_size", workload=w.name, over=over, variant=variant, pairs=len(ref),
                o_rel_max=worst_o, ht_rel_max=worst_h)
     print(json.dumps(rec), flush=True)
     if LOG:

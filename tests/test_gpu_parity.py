@@ -301,3 +301,68 @@ def test_gate_extremes(variant, regime):
     assert torch.isfinite(o.float()).all() and torch.isfinite(ht).all()
     eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, regime + " " + variant)
     log(test="gate_extremes", regime=regime, variant=variant, o_rel=eo, ht_rel=eh)
+
+
+# ------------------------------------------------------------------ segmented variant
+# Every sequence of a dense batch split into segments of a multiple of 64 tokens; the
+# segments' affine state maps (h_end = M h_in + b) are composed in order.  Segment counts
+# here follow the library's rule (enough (segment, head) pairs to fill the GPU, at most one
+# segment per 64 tokens), so these small cases use 64-token segments and a ragged last one.
+SEG_CASES = [
+    # D, H, Hg, B, T, h0
+    (128, 4, 4, 2, 300, True),
+    (128, 4, 2, 1, 517, False),
+    (64, 2, 1, 2, 333, True),
+]
+
+
+@pytest.mark.parametrize("D,H,Hg,B,T,h0", SEG_CASES)
+def test_segmented_matches_oracle_and_fused(D, H, Hg, B, T, h0):
+    inp = draw(B=B, T=T, H=H, Hg=Hg, Dk=D, C=64, seed=D + T + 11, h0_std=0.05 if h0 else None)
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant="segmented")
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "segmented D%d" % D)
+    of, htf = run_gdn(inp, variant="fused")
+    # the segmented passes round differently (segment maps in bf16 products); both agree
+    # with the oracle, and with each other to the same order
+    assert rel_l2(to64(o), to64(of)) <= 5e-3 and rel_l2(to64(ht), to64(htf)) <= 1e-2
+    log(test="segmented", D=D, H=H, Hg=Hg, B=B, T=T, o_rel=eo, ht_rel=eh)
+
+
+def test_segmented_strong_decay_and_no_final_state():
+    inp = draw(B=1, T=400, H=2, Hg=2, Dk=128, C=64, seed=91, h0_std=0.05)
+    gen = torch.Generator().manual_seed(92)
+    x = torch.randn(inp["g"].shape, generator=gen) - 5.0
+    inp["g"] = torch.nn.functional.logsigmoid(x).to(inp["g"].dtype)
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant="segmented")
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "segmented strong decay")
+    o2, ht2 = run_gdn(inp, variant="segmented", output_final_state=False)
+    assert ht2 is None and torch.equal(o, o2)
+    log(test="segmented_strong_decay", o_rel=eo, ht_rel=eh)
+
+
+def test_segmented_resolution():
+    """AUTO picks the segmented variant for a few long sequences when the workspace is there
+    (and the fused one without it); packed batches never segment."""
+    import gated_deltanet_chunked_02_amd as gdn
+    dev = torch.device("cuda")
+    q = torch.zeros(1, 65536, 16, 128, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros(1, 65536, 32, 128, dtype=torch.bfloat16, device=dev)
+    beta = torch.zeros(1, 65536, 32, dtype=torch.bfloat16, device=dev)
+    desc = gdn.make_desc(q, v, beta, None, 128, "auto")
+    assert gdn.gdn_resolved_variant(desc) == "fused"       # no workspace given
+    ws = gdn.gdn_chunk_fwd_workspace_size(desc)
+    assert ws > 0
+    buf = torch.empty(ws, dtype=torch.uint8, device=dev)
+    desc.workspace, desc.workspace_bytes = buf.data_ptr(), ws
+    assert gdn.gdn_resolved_variant(desc) == "segmented"
+    cu = torch.tensor([0, 65536], dtype=torch.int32, device=dev)
+    assert gdn.gdn_resolved_variant(desc, cu) == "fused"
+    # many pairs: the fused kernel already fills the GPU
+    q2 = torch.zeros(16, 8192, 32, 128, dtype=torch.bfloat16, device=dev)
+    v2 = torch.zeros(16, 8192, 32, 128, dtype=torch.bfloat16, device=dev)
+    b2 = torch.zeros(16, 8192, 32, dtype=torch.bfloat16, device=dev)
+    d2 = gdn.make_desc(q2, v2, b2, None, 128, "auto")
+    assert gdn.gdn_chunk_fwd_workspace_size(d2) == 0
+    assert gdn.gdn_resolved_variant(d2) == "fused"
