@@ -142,7 +142,9 @@ __device__ __forceinline__ V4 read_tr(const void* p) {
   return __builtin_bit_cast(V4, r);
 }
 
-template <int D>
+// OUT = false: the state-only form (no q read, no Q K^T tiles, no Q h, no o), for the
+// segmented variant's passes that only need final states.
+template <int D, bool OUT>
 __global__ __launch_bounds__(D * 4) void k_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const void* __restrict__ beta, int beta_f32,
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
         aa = mma32b(kf[kk], kf[kk], aa);
-        pa = mma32b(kf[kk], frag_swz<D>(Qx, 16 * b, 32 * kk, l), pa);
+        if constexpr (OUT) pa = mma32b(kf[kk], frag_swz<D>(Qx, 16 * b, 32 * kk, l), pa);
       }
       // N = -A_bb strictly lower.  The raw product k_i . k_j is symmetric, so each lane gates
       // it for both orientations: nf holds N^T in accumulator form, nfm holds N.  Masked
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
         nfm[e] = (j > r16 ? -bc[e] * decm : 0.f) * aa[e];
         pf[e] = (r16 >= j ? scale * dec : 0.f) * pa[e];
       }
-      *reinterpret_cast<f16x4*>(&SP[ob][tix<F>(b, b) + r16 * RS + g4]) = to_h(pf);
+      if constexpr (OUT) *reinterpret_cast<f16x4*>(&SP[ob][tix<F>(b, b) + r16 * RS + g4]) = to_h(pf);
       const f16x4 nt = to_h(nf), nn = to_h(nfm);
       // T = (I + N)(I + N^2)(I + N^4)(I + N^8): a product X Y takes X^T and Y in
       // accumulator form, so both orientations of each power are kept; T^T is built, whose
@@ -352,6 +354,18 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     // first, so the younger waves NB .. 2 NB - 1, which only solve (and, for the last one,
     // make the gate vectors), set the pace of the chunk.
     auto offdiag_share = [&](int i) {
+      if constexpr (!OUT) {
+        // the K K^T products only
+        if (i == 0)
+          offdiag(OffTile<1, 0, 0>(), OffTile<2, 0, 0>());
+        else if (i == 1)
+          offdiag(OffTile<2, 1, 0>(), OffTile<3, 0, 0>());
+        else if (i == 2)
+          offdiag(OffTile<3, 1, 0>());
+        else
+          offdiag(OffTile<3, 2, 0>());
+        return;
+      }
       if (i == 0)
         offdiag(OffTile<1, 0, 0>(), OffTile<1, 0, 1>(), OffTile<2, 0, 0>());
       else if (i == 1)
@@ -386,7 +400,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   uint32_t bvn = 0;
   if (nchunks > 0) {
     load_tile(kp, kh, qstride, cs0, min(CS, L));
-    load_tile(qp, qh, qstride, cs0, min(CS, L));
+    if constexpr (OUT) load_tile(qp, qh, qstride, cs0, min(CS, L));
     load_tile(vp, vh, vstride, cs0, vlen(min(CS, L)));
     if (w0 == kGateWave) {
       load_gate(gvn, bvn, cs0, min(CS, L));
@@ -397,13 +411,13 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       }
     }
     store_tile(SK[0], kp);
-    store_tile(SQ[0], qp);
+    if constexpr (OUT) store_tile(SQ[0], qp);
     store_tile(SV[0], vp);
     if (nchunks > 1) {
       load_tile(kp, kh, qstride, cs0 + CS, min(CS, L - CS));
-      load_tile(qp, qh, qstride, cs0 + CS, min(CS, L - CS));
+      if constexpr (OUT) load_tile(qp, qh, qstride, cs0 + CS, min(CS, L - CS));
       store_tile(SK[1], kp);
-      store_tile(SQ[1], qp);
+      if constexpr (OUT) store_tile(SQ[1], qp);
     }
     __syncthreads();
     side(0, 0, 0);
@@ -426,7 +440,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       const int c2 = cs + 2 * CS, len2 = min(CS, L - (m + 2) * CS);
       if (w0 == kGateWave) load_gate(gvn, bvn, c2, len2);
       load_tile(kp, kh, qstride, c2, len2);
-      load_tile(qp, qh, qstride, c2, len2);
+      if constexpr (OUT) load_tile(qp, qh, qstride, c2, len2);
     }
     if (more1) load_tile(vp, vh, vstride, cs + CS, vlen(min(CS, L - (m + 1) * CS)));
     sched_fence();
@@ -453,13 +467,15 @@ __global__ __launch_bounds__(D * 4) void k_fused(
 #pragma unroll
       for (int p = 0; p < NDK / 2; ++p) {
         kf[p] = *reinterpret_cast<const bf16x8*>(Kc + kqoff[p] + b * 16 * D);
-        qf[p] = *reinterpret_cast<const bf16x8*>(Qc + kqoff[p] + b * 16 * D);
+        if constexpr (OUT) qf[p] = *reinterpret_cast<const bf16x8*>(Qc + kqoff[p] + b * 16 * D);
       }
       xk[b] = yq[b] = zero4();
 #pragma unroll
       for (int p = 0; p < NDK / 2; ++p) xk[b] = mma32b(kf[p], stbo[p], xk[b]);
+      if constexpr (OUT) {
 #pragma unroll
-      for (int p = 0; p < NDK / 2; ++p) yq[b] = mma32b(stbo[p], qf[p], yq[b]);
+        for (int p = 0; p < NDK / 2; ++p) yq[b] = mma32b(stbo[p], qf[p], yq[b]);
+      }
     }
     // forward substitution, outputs and the update operands, block by block
     f16x4 vhh[NB];
@@ -484,16 +500,18 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       // 16 b + l%16, columns 16 w + 4 g .. + 3, stored as one 8-byte word (pairs converted
       // as 32-bit words: this compiler turns an element read of a converted 16-bit vector
       // into a read of element 0)
-      f32x4 z = zero4();
+      if constexpr (OUT) {
+        f32x4 z = zero4();
 #pragma unroll
-      for (int j = 0; j <= b; ++j)
-        z = mma16h(vhh[j], *reinterpret_cast<const f16x4*>(Pc + tix<F>(b, j)), z);
-      const float egt = eop[16 * b];
-      const f32x2_t o01 = {fmaf(egt, yq[b][0], z[0]), fmaf(egt, yq[b][1], z[1])};
-      const f32x2_t o23 = {fmaf(egt, yq[b][2], z[2]), fmaf(egt, yq[b][3], z[3])};
-      const u32x2 ow = {__builtin_bit_cast(uint32_t, __builtin_convertvector(o01, bf16x2_t)),
-                        __builtin_bit_cast(uint32_t, __builtin_convertvector(o23, bf16x2_t))};
-      __builtin_amdgcn_raw_buffer_store_b64(ow, orsrc, (int)otoff, b * oblock, 0);
+        for (int j = 0; j <= b; ++j)
+          z = mma16h(vhh[j], *reinterpret_cast<const f16x4*>(Pc + tix<F>(b, j)), z);
+        const float egt = eop[16 * b];
+        const f32x2_t o01 = {fmaf(egt, yq[b][0], z[0]), fmaf(egt, yq[b][1], z[1])};
+        const f32x2_t o23 = {fmaf(egt, yq[b][2], z[2]), fmaf(egt, yq[b][3], z[3])};
+        const u32x2 ow = {__builtin_bit_cast(uint32_t, __builtin_convertvector(o01, bf16x2_t)),
+                          __builtin_bit_cast(uint32_t, __builtin_convertvector(o23, bf16x2_t))};
+        __builtin_amdgcn_raw_buffer_store_b64(ow, orsrc, (int)otoff, b * oblock, 0);
+      }
       // e^{Gc_end - Gc} v_new, the update operand
       const f32x4 dc = *reinterpret_cast<const f32x4*>(dcp + 16 * b);
       vb[b] = to_b(dc * vn);
@@ -518,7 +536,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     make_stbo();
     if (more2) {
       store_tile(SK[kb2], kp);
-      store_tile(SQ[kb2], qp);
+      if constexpr (OUT) store_tile(SQ[kb2], qp);
       if (w0 == kGateWave) make_gates(kb2, gvn, bvn);
     }
     if (more1) store_tile(SV[tb ^ 1], vp);
@@ -536,11 +554,11 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   }
 }
 
-template <int D>
+template <int D, bool OUT>
 hipError_t run_fused(const Problem& p, hipStream_t st) {
   const int grid = p.N * p.H;
   if (grid == 0) return hipSuccess;
-  k_fused<D><<<grid, FusedCfg<D>::NTH, 0, st>>>(
+  k_fused<D, OUT><<<grid, FusedCfg<D>::NTH, 0, st>>>(
       static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.v),
       p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot,
       p.H, p.Hg, p.scale, p.fused_flags);
@@ -552,7 +570,9 @@ hipError_t run_fused(const Problem& p, hipStream_t st) {
 bool fused_supported(const Problem& p) { return !p.f32 && (p.D == 64 || p.D == 128); }
 
 hipError_t launch_fused(const Problem& p, hipStream_t st) {
-  return p.D == 64 ? run_fused<64>(p, st) : run_fused<128>(p, st);
+  if (p.fused_flags & kFusedNoOutput)
+    return p.D == 64 ? run_fused<64, false>(p, st) : run_fused<128, false>(p, st);
+  return p.D == 64 ? run_fused<64, true>(p, st) : run_fused<128, true>(p, st);
 }
 
 }  // namespace gdn
