@@ -27,10 +27,11 @@ __global__ void k_segment_table(int32_t* cu_seg, int N, int T, int S, int Ls) {
   }
 }
 
-// One workgroup per (sequence, head): h = h0 (zero when absent); for each segment s,
-// h_in[n S + s] = h and h <- M[n S + s] h + b[n S + s]; finally ht = h.  fp32 throughout;
-// thread (ty, tx) of a 16 x 16 grid owns rows ty R .. ty R + R - 1 and columns tx + 16 j
-// (R = D / 16, j < R) of the D x D state, kept in LDS between steps.
+// One workgroup per (sequence, head, 16-column slab of the state): the columns of
+// h_out = M h_in + b are independent, so each slab is composed on its own.  h = h0 (zero
+// when absent); for each segment s, h_in[n S + s] = h and h <- M[n S + s] h + b[n S + s];
+// finally ht = h.  fp32 throughout; thread (rg, c) owns column c of the slab and rows
+// rg R .. rg R + R - 1 (R = D / 16), M is staged in LDS per step, the slab kept there.
 template <int D>
 __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ M,
                                                       const float* __restrict__ b,
@@ -38,45 +39,50 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
                                                       float* __restrict__ h_in,
                                                       float* __restrict__ ht, int S, int H) {
   constexpr int R = D / 16;
-  __shared__ float hs[D * D];
-  __shared__ float ms[D * D];
-  const int n = blockIdx.x / H, h = blockIdx.x - n * H;
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  __shared__ float hs[D * 16];
+  constexpr int MS = D + 4;  // row stride of M in LDS (16-byte aligned rows, staggered banks)
+  __shared__ __align__(16) float ms[D * MS];
+  const int nh = blockIdx.x, slab = blockIdx.y;
+  const int n = nh / H, h = nh - n * H;
+  const int tid = threadIdx.x, c = tid % 16, rg = tid / 16;
+  const int col = 16 * slab + c;
   const long DD = (long)D * D;
-  for (int i = tid; i < D * D; i += 256) hs[i] = h0 ? h0[((long)n * H + h) * DD + i] : 0.f;
-  __syncthreads();
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    acc[r] = h0 ? h0[((long)n * H + h) * DD + (long)(rg * R + r) * D + col] : 0.f;
   for (int s = 0; s < S; ++s) {
     const long off = (((long)n * S + s) * H + h) * DD;
-    for (int i = tid; i < D * D; i += 256) {
-      h_in[off + i] = hs[i];
-      ms[i] = M[off + i];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = rg * R + r;
+      h_in[off + (long)row * D + col] = acc[r];
+      hs[row * 16 + c] = acc[r];
     }
+    for (int i = 4 * tid; i < D * D; i += 4 * 256)
+      *reinterpret_cast<float4*>(&ms[(i / D) * MS + i % D]) =
+          *reinterpret_cast<const float4*>(&M[off + i]);
     __syncthreads();
-    float acc[R][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) acc[r] = b[off + (long)(rg * R + r) * D + col];
+    for (int k = 0; k < D; k += 4) {
+      float x[4];
 #pragma unroll
-      for (int j = 0; j < R; ++j) acc[r][j] = b[off + (long)(ty * R + r) * D + tx + 16 * j];
-    for (int c = 0; c < D; ++c) {
-      float x[R];
-#pragma unroll
-      for (int j = 0; j < R; ++j) x[j] = hs[c * D + tx + 16 * j];
+      for (int u = 0; u < 4; ++u) x[u] = hs[(k + u) * 16 + c];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float mv = ms[(ty * R + r) * D + c];
-#pragma unroll
-        for (int j = 0; j < R; ++j) acc[r][j] = fmaf(mv, x[j], acc[r][j]);
+        const float4 mv = *reinterpret_cast<const float4*>(&ms[(rg * R + r) * MS + k]);
+        acc[r] = fmaf(mv.x, x[0], acc[r]);
+        acc[r] = fmaf(mv.y, x[1], acc[r]);
+        acc[r] = fmaf(mv.z, x[2], acc[r]);
+        acc[r] = fmaf(mv.w, x[3], acc[r]);
       }
     }
-    __syncthreads();  // every read of hs and ms for this step is done
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int j = 0; j < R; ++j) hs[(ty * R + r) * D + tx + 16 * j] = acc[r][j];
-    __syncthreads();
+    __syncthreads();  // hs and ms are rewritten by the next step
   }
   if (ht)
-    for (int i = tid; i < D * D; i += 256) ht[((long)n * H + h) * DD + i] = hs[i];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ht[((long)n * H + h) * DD + (long)(rg * R + r) * D + col] = acc[r];
 }
 
 }  // namespace
@@ -90,10 +96,11 @@ hipError_t launch_segment_table(int32_t* cu_seg, int N, int T, int S, int Ls, hi
 hipError_t launch_segment_scan(const float* M, const float* b, const float* h0, float* h_in,
                                float* ht, int N, int S, int H, int D, hipStream_t st) {
   if (N * H == 0) return hipSuccess;
+  const dim3 grid(N * H, D / 16);
   if (D == 64)
-    k_segment_scan<64><<<N * H, 256, 0, st>>>(M, b, h0, h_in, ht, S, H);
+    k_segment_scan<64><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, S, H);
   else
-    k_segment_scan<128><<<N * H, 256, 0, st>>>(M, b, h0, h_in, ht, S, H);
+    k_segment_scan<128><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, S, H);
   return hipGetLastError();
 }
 
