@@ -41,31 +41,40 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-template <int D>
+// DK: key dimension (= the value dimension of the tensors); DV: state columns of one
+// workgroup (DK / DV workgroups share a (sequence, head)).
+template <int DK, int DV>
 struct FusedCfg {
-  static constexpr int NW = D / 16;            // waves, one 16-column state block each
+  static constexpr int NW = DV / 16;           // waves, one 16-column state block each
   static constexpr int NTH = NW * kWave;       // threads (the launch bound)
-  static constexpr int CS = 64;                // tokens per chunk
+  static constexpr int SPLIT = DK / DV;        // workgroups per (sequence, head)
+  static constexpr int CS = DK > 128 ? 32 : 64;  // tokens per chunk (LDS holds 3 K/Q tiles)
   static constexpr int NB = CS / 16;           // 16-token blocks per chunk
-  static constexpr int NDK = D / 16;           // key blocks of the state
-  static constexpr int CPR = D / 8;            // 16-byte pieces per q/k/v row
-  static constexpr int TILE = CS * D;          // elements of one [CS][D] tile
-  static constexpr int KPL = CS * CPR / NTH;   // 16-byte pieces per lane per tile
+  static constexpr int NDK = DK / 16;          // key blocks of the state
+  static constexpr int CPR = DK / 8;           // 16-byte pieces per q/k row
+  static constexpr int CPRV = DV / 8;          // 16-byte pieces per row of this slice of v
+  static constexpr int TILE = CS * DK;         // elements of one [CS][DK] q/k tile
+  static constexpr int TILEV = CS * DV;        // elements of one [CS][DV] v tile
+  static constexpr int KPL = CS * CPR / NTH;   // 16-byte pieces per lane per q/k tile
   static constexpr int RSTEP = NTH / CPR;      // rows between one lane's pieces
+  static constexpr int KPLV = CS * CPRV / NTH; // the same for the v tile
+  static constexpr int RSTEPV = NTH / CPRV;
   static constexpr int RS = 20;                // row stride of a packed fp16 16 x 16 tile
   static constexpr int TE = 16 * RS;           // elements per packed tile
   static constexpr int NLOW = NB * (NB + 1) / 2;  // lower 16 x 16 tiles of a chunk
   static constexpr int NOFF = 2 * (NLOW - NB);     // off-diagonal tile products (K K^T, Q K^T)
-  static_assert(KPL * NTH == CS * CPR, "tile covered by whole 16-byte loads");
-  static_assert(RSTEP % CPR == 0, "a lane's pieces share one swizzle");
+  static_assert(KPL * NTH == CS * CPR && KPLV * NTH == CS * CPRV,
+                "tiles covered by whole 16-byte loads");
+  static_assert(RSTEP % 16 == 0 && RSTEPV % 16 == 0, "a lane's pieces share one swizzle");
 };
 
 // Element offset of (r, k) in a swizzled [rows][D] bf16 tile: the 16-byte piece index is
-// XOR-ed with the row, so 16-byte fragment reads of 16 rows are conflict-free.
+// XOR-ed with the row's position in its 16-row block, so 16-byte fragment reads of 16 rows
+// are conflict-free.
 template <int D>
 __device__ __forceinline__ int swz(int r, int k) {
   constexpr int CPR = D / 8;
-  return r * D + ((((k >> 3) ^ r) & (CPR - 1)) << 3) + (k & 7);
+  return r * D + ((((k >> 3) ^ (r & 15)) & (CPR - 1)) << 3) + (k & 7);
 }
 
 // Within a 16-row block the swizzle key of lane l's row is l % 16.
@@ -144,26 +153,29 @@ __device__ __forceinline__ V4 read_tr(const void* p) {
 
 // OUT = false: the state-only form (no q read, no Q K^T tiles, no Q h, no o), for the
 // segmented variant's passes that only need final states.
-template <int D, bool OUT>
-__global__ __launch_bounds__(D * 4) void k_fused(
+template <int DK, int DV, bool OUT>
+__global__ __launch_bounds__(DV * 4) void k_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const void* __restrict__ beta, int beta_f32,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, bf16* __restrict__ o,
     float* __restrict__ ht, int T, int Ttot, int H, int Hg, float scale, int flags) {
-  typedef FusedCfg<D> F;
+  typedef FusedCfg<DK, DV> F;
   constexpr int CS = F::CS, NB = F::NB, NDK = F::NDK, RS = F::RS, TE = F::TE, CPR = F::CPR;
-  constexpr int NW = F::NW;
+  constexpr int NW = F::NW, CPRV = F::CPRV;
+  constexpr int D = DK;  // row length of q, k, v and o
   constexpr float kLog2e = 1.4426950408889634f;
-  const int n = blockIdx.x / H, h = blockIdx.x - n * H;
+  const int nh = blockIdx.x / F::SPLIT, half = blockIdx.x - nh * F::SPLIT;
+  const int n = nh / H, h = nh - n * H;
   const int hk = h / (H / Hg);
+  const int col0 = half * DV;  // this workgroup's first state column
   const long qstride = (long)Hg * D, vstride = (long)H * D;
   const bf16* qh = q + (long)hk * D;
   const bf16* kh = k + (long)hk * D;
-  const bf16* vh = v + (long)h * D;
+  const bf16* vh = v + (long)h * D + col0;
 
   __shared__ __align__(16) bf16 SK[3][F::TILE];
   __shared__ __align__(16) bf16 SQ[3][F::TILE];
-  __shared__ __align__(16) bf16 SV[2][F::TILE];
+  __shared__ __align__(16) bf16 SV[2][F::TILEV];
   __shared__ __align__(16) f16 SA[2][F::NLOW * TE];  // -A~ below the diagonal, T_ii diag(beta) on it
   __shared__ __align__(16) f16 SP[2][F::NLOW * TE];  // scale (Q K^T * e^{Gc_i-Gc_j})_{i>=j}
   // Gate vectors, made by one wave two chunks ahead (buffer = chunk % 3), per token t:
@@ -183,11 +195,12 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   const int l0 = lane_id(), w0 = __builtin_amdgcn_readfirstlane(wave_id());
   const int r16_0 = l0 & 15, g4_0 = 4 * (l0 >> 4);
 
-  // State: st[db] holds rows dk = state_dk<D>(db, 4 (l/16) + e) of column 16 w + l%16.
+  // State: st[db] holds rows dk = state_dk<DK>(db, 4 (l/16) + e) of column
+  // col0 + 16 w + l%16.
   f32x4 st[NDK];
   const long hoff = ((long)n * H + h) * D * D;
   {
-    const int dv0 = 16 * w0 + r16_0;
+    const int dv0 = col0 + 16 * w0 + r16_0;
 #pragma unroll
     for (int db = 0; db < NDK; ++db) st[db] = zero4();
     if (flags & kFusedH0Identity) {
@@ -195,13 +208,13 @@ __global__ __launch_bounds__(D * 4) void k_fused(
 #pragma unroll
       for (int db = 0; db < NDK; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[db][e] = state_dk<D>(db, g4_0 + e) == dv0 ? 1.f : 0.f;
+        for (int e = 0; e < 4; ++e) st[db][e] = state_dk<DK>(db, g4_0 + e) == dv0 ? 1.f : 0.f;
     } else if (h0) {
 #pragma unroll
       for (int db = 0; db < NDK; ++db)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          st[db][e] = h0[hoff + (long)state_dk<D>(db, g4_0 + e) * D + dv0];
+          st[db][e] = h0[hoff + (long)state_dk<DK>(db, g4_0 + e) * D + dv0];
     }
   }
   // bf16 copy of the chunk-start state as the B operands of the K h and Q h products: the
@@ -218,8 +231,10 @@ __global__ __launch_bounds__(D * 4) void k_fused(
 
   // Loads of one staged tile into registers: lane tid holds rows tid / CPR + s RSTEP, piece
   // tid % CPR.  The resource ends at the chunk's last valid token.
+  // (q and k tiles: rows of D elements; the v tile: this workgroup's DV columns)
   const uint32_t rl = (uint32_t)threadIdx.x / CPR, cl = (uint32_t)threadIdx.x % CPR;
-  const int lds_lo = rl * D + (((cl ^ rl) & (CPR - 1)) << 3);
+  const uint32_t rlv = (uint32_t)threadIdx.x / CPRV, clv = (uint32_t)threadIdx.x % CPRV;
+  const int lds_lo = swz<D>(rl, cl * 8), lds_lov = swz<DV>(rlv, clv * 8);
   auto load_tile = [&](u32x4* dst, const bf16* base, long stride, int cstart, int clen) {
     const auto rs = buf_rsrc(base + (long)cstart * stride, (uint32_t)(clen * stride * 2));
     const int lane = (int)((rl * stride + cl * 8) * 2);
@@ -233,9 +248,23 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     for (int s = 0; s < F::KPL; ++s)
       *reinterpret_cast<u32x4*>(tile + lds_lo + s * F::RSTEP * D) = src[s];
   };
+  auto load_vtile = [&](u32x4* dst, int cstart, int clen) {
+    // the resource spans the rows' full width; only this workgroup's slice is read
+    const auto rs = buf_rsrc(vh + (long)cstart * vstride, (uint32_t)(clen * vstride * 2));
+    const int lane = (int)((rlv * vstride + clv * 8) * 2);
+#pragma unroll
+    for (int s = 0; s < F::KPLV; ++s)
+      dst[s] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane, (int)(s * F::RSTEPV * vstride * 2), 0));
+  };
+  auto store_vtile = [&](bf16* tile, const u32x4* src) {
+#pragma unroll
+    for (int s = 0; s < F::KPLV; ++s)
+      *reinterpret_cast<u32x4*>(tile + lds_lov + s * F::RSTEPV * DV) = src[s];
+  };
   // g and beta of token l (lane l, all CS = 64 tokens of a chunk; zero past the sequence
   // end), loaded by the gate wave, which turns them into the chunk's gate vectors.
-  static_assert(CS == kWave, "one gate per lane");
+  static_assert(CS <= kWave, "one gate per lane");
   constexpr int kGateWave = NW - 1;
   auto load_gate = [&](float& gv, uint32_t& bv, int cstart, int clen) {
     const int bsz = beta_f32 ? 4 : 2;
@@ -253,11 +282,13 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     const float Gc = wave_incl_scan(gv) * kLog2e;
     const float gend = __shfl(Gc, CS - 1, kWave);
     const float ef = __builtin_amdgcn_exp2f(Gc);
-    SGC[gb][t] = Gc;
-    SBT[gb][t] = __builtin_bit_cast(float, beta_f32 ? bvr : bvr << 16);
-    SEF[gb][t] = ef;
-    SEO[gb][t] = scale * ef;
-    SDC[gb][t] = __builtin_amdgcn_exp2f(gend - Gc);
+    if (t < CS) {
+      SGC[gb][t] = Gc;
+      SBT[gb][t] = __builtin_bit_cast(float, beta_f32 ? bvr : bvr << 16);
+      SEF[gb][t] = ef;
+      SEO[gb][t] = scale * ef;
+      SDC[gb][t] = __builtin_amdgcn_exp2f(gend - Gc);
+    }
     if (t == 0) SGE[gb] = __builtin_amdgcn_exp2f(gend);
   };
 
@@ -278,12 +309,12 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       const f32x4 bc = *reinterpret_cast<const f32x4*>(&SBT[gb][16 * b + g4]);
       bf16x8 kf[D / 32];
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) kf[kk] = frag_swz<D>(Kx, 16 * b, 32 * kk, l);
+      for (int kk = 0; kk < D / 32; ++kk) kf[kk] = frag_swz<DK>(Kx, 16 * b, 32 * kk, l);
       f32x4 aa = zero4(), pa = zero4();
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
         aa = mma32b(kf[kk], kf[kk], aa);
-        if constexpr (OUT) pa = mma32b(kf[kk], frag_swz<D>(Qx, 16 * b, 32 * kk, l), pa);
+        if constexpr (OUT) pa = mma32b(kf[kk], frag_swz<DK>(Qx, 16 * b, 32 * kk, l), pa);
       }
       // N = -A_bb strictly lower.  The raw product k_i . k_j is symmetric, so each lane gates
       // it for both orientations: nf holds N^T in accumulator form, nfm holds N.  Masked
@@ -334,8 +365,8 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
         for (int u = 0; u < NPR; ++u)
-          acc[u] = mma32b(frag_swz<D>(Kx, 16 * bj_[u], 32 * kk, l),
-                          frag_swz<D>(kd_[u] ? Qx : Kx, 16 * bi_[u], 32 * kk, l), acc[u]);
+          acc[u] = mma32b(frag_swz<DK>(Kx, 16 * bj_[u], 32 * kk, l),
+                          frag_swz<DK>(kd_[u] ? Qx : Kx, 16 * bi_[u], 32 * kk, l), acc[u]);
 #pragma unroll
       for (int u = 0; u < NPR; ++u) {
         const float Gi = Gc[16 * bi_[u] + r16];
@@ -354,6 +385,14 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     // first, so the younger waves NB .. 2 NB - 1, which only solve (and, for the last one,
     // make the gate vectors), set the pace of the chunk.
     auto offdiag_share = [&](int i) {
+      if constexpr (NB == 2) {
+        // one off-diagonal tile: K K^T on wave 0, Q K^T on wave 1
+        if (i == 0)
+          offdiag(OffTile<1, 0, 0>());
+        else if (OUT)
+          offdiag(OffTile<1, 0, 1>());
+        return;
+      }
       if constexpr (!OUT) {
         // the K K^T products only
         if (i == 0)
@@ -375,7 +414,9 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       else
         offdiag(OffTile<3, 1, 1>(), OffTile<3, 2, 0>(), OffTile<3, 2, 1>());
     };
-    static_assert(F::NOFF == 12 && (NW == 2 * NB || NW == NB), "side work dealt evenly");
+    static_assert((NB == 4 && F::NOFF == 12) || (NB == 2 && F::NOFF == 2),
+                  "side work dealt evenly");
+    static_assert(NW >= NB, "one wave per diagonal block");
     if (w < NB) {
       diag(w);
       offdiag_share(w);
@@ -385,23 +426,23 @@ __global__ __launch_bounds__(D * 4) void k_fused(
   // Per-lane LDS and output address parts (16-row blocks make every swizzle key a lane
   // constant): V by one transposing read per block (column 16 w + l%16, tokens 4 (l/16)..),
   // K^T of key block db by one transposing read per block, K and Q fragments of pair p.
-  const int vtoff = swz<D>(g4_0 + (r16_0 >> 2), 16 * w0 + 4 * (r16_0 & 3));
+  const int vtoff = swz<DV>(g4_0 + (r16_0 >> 2), 16 * w0 + 4 * (r16_0 & 3));
   int koff[NDK], kqoff[NDK / 2];
 #pragma unroll
   for (int db = 0; db < NDK; ++db)
-    koff[db] = swz<D>(g4_0 + (r16_0 >> 2), state_dk<D>(db, 4 * (r16_0 & 3)));
+    koff[db] = swz<DK>(g4_0 + (r16_0 >> 2), state_dk<DK>(db, 4 * (r16_0 & 3)));
 #pragma unroll
-  for (int p = 0; p < NDK / 2; ++p) kqoff[p] = swz_lane<D>(l0, 8 * kchunk<D>(p, l0 >> 4));
+  for (int p = 0; p < NDK / 2; ++p) kqoff[p] = swz_lane<DK>(l0, 8 * kchunk<DK>(p, l0 >> 4));
   const uint32_t otoff = (uint32_t)((r16_0 * H * D + 16 * w0 + g4_0) * 2);
   const int oblock = 16 * H * D * 2;  // bytes per 16-token block of o
 
-  u32x4 kp[F::KPL], qp[F::KPL], vp[F::KPL];
+  u32x4 kp[F::KPL], qp[F::KPL], vp[F::KPLV];
   float gvn = 0.f;
   uint32_t bvn = 0;
   if (nchunks > 0) {
     load_tile(kp, kh, qstride, cs0, min(CS, L));
     if constexpr (OUT) load_tile(qp, qh, qstride, cs0, min(CS, L));
-    load_tile(vp, vh, vstride, cs0, vlen(min(CS, L)));
+    load_vtile(vp, cs0, vlen(min(CS, L)));
     if (w0 == kGateWave) {
       load_gate(gvn, bvn, cs0, min(CS, L));
       make_gates(0, gvn, bvn);
@@ -412,7 +453,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     }
     store_tile(SK[0], kp);
     if constexpr (OUT) store_tile(SQ[0], qp);
-    store_tile(SV[0], vp);
+    store_vtile(SV[0], vp);
     if (nchunks > 1) {
       load_tile(kp, kh, qstride, cs0 + CS, min(CS, L - CS));
       if constexpr (OUT) load_tile(qp, qh, qstride, cs0 + CS, min(CS, L - CS));
@@ -442,7 +483,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       load_tile(kp, kh, qstride, c2, len2);
       if constexpr (OUT) load_tile(qp, qh, qstride, c2, len2);
     }
-    if (more1) load_tile(vp, vh, vstride, cs + CS, vlen(min(CS, L - (m + 1) * CS)));
+    if (more1) load_vtile(vp, cs + CS, vlen(min(CS, L - (m + 1) * CS)));
     sched_fence();
 
     const int l = lane_id();
@@ -455,7 +496,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     const float* efp = SEF[kb] + g4;
     const float* eop = SEO[kb] + r16;
     const float* dcp = SDC[kb] + g4;
-    const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D,
+    const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D + col0,
                                 (flags & kFusedNoOutput) ? 0u : (uint32_t)(len * H * D * 2));
 
     // K h and Q h of every block with the chunk-start state; Y = Q h is made transposed
@@ -484,7 +525,7 @@ __global__ __launch_bounds__(D * 4) void k_fused(
     for (int b = 0; b < NB; ++b) {
       // R / beta - sum_{j<b} A~_bj v_j = V - e^Gc (K h) + sum_{j<b} (-A~_bj) v_j: lane
       // (l%16, g) holds tokens 4 g + e of column 16 w + l%16
-      const bf16x4 vv = read_tr<bf16x4>(vt + b * 16 * D);
+      const bf16x4 vv = read_tr<bf16x4>(vt + b * 16 * DV);
       const f32x4 ef = *reinterpret_cast<const f32x4*>(efp + 16 * b);
       f32x4 acc;
 #pragma unroll
@@ -539,26 +580,26 @@ __global__ __launch_bounds__(D * 4) void k_fused(
       if constexpr (OUT) store_tile(SQ[kb2], qp);
       if (w0 == kGateWave) make_gates(kb2, gvn, bvn);
     }
-    if (more1) store_tile(SV[tb ^ 1], vp);
+    if (more1) store_vtile(SV[tb ^ 1], vp);
     __syncthreads();
     kb = kb1;
   }
 
   if (ht) {
-    const int dv0 = 16 * w0 + r16_0;
+    const int dv0 = col0 + 16 * w0 + r16_0;
 #pragma unroll
     for (int db = 0; db < NDK; ++db)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        ht[hoff + (long)state_dk<D>(db, g4_0 + e) * D + dv0] = st[db][e];
+        ht[hoff + (long)state_dk<DK>(db, g4_0 + e) * D + dv0] = st[db][e];
   }
 }
 
-template <int D, bool OUT>
+template <int DK, int DV, bool OUT>
 hipError_t run_fused(const Problem& p, hipStream_t st) {
-  const int grid = p.N * p.H;
+  const int grid = p.N * p.H * FusedCfg<DK, DV>::SPLIT;
   if (grid == 0) return hipSuccess;
-  k_fused<D, OUT><<<grid, FusedCfg<D>::NTH, 0, st>>>(
+  k_fused<DK, DV, OUT><<<grid, FusedCfg<DK, DV>::NTH, 0, st>>>(
       static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.v),
       p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot,
       p.H, p.Hg, p.scale, p.fused_flags);
@@ -567,12 +608,20 @@ hipError_t run_fused(const Problem& p, hipStream_t st) {
 
 }  // namespace
 
-bool fused_supported(const Problem& p) { return !p.f32 && (p.D == 64 || p.D == 128); }
+bool fused_supported(const Problem& p) {
+  return !p.f32 && (p.D == 64 || p.D == 128 || p.D == 256);
+}
 
 hipError_t launch_fused(const Problem& p, hipStream_t st) {
-  if (p.fused_flags & kFusedNoOutput)
-    return p.D == 64 ? run_fused<64, false>(p, st) : run_fused<128, false>(p, st);
-  return p.D == 64 ? run_fused<64, true>(p, st) : run_fused<128, true>(p, st);
+  // D = 256: two workgroups per (sequence, head), 128 state columns each
+  if (p.fused_flags & kFusedNoOutput) {
+    if (p.D == 64) return run_fused<64, 64, false>(p, st);
+    if (p.D == 128) return run_fused<128, 128, false>(p, st);
+    return run_fused<256, 128, false>(p, st);
+  }
+  if (p.D == 64) return run_fused<64, 64, true>(p, st);
+  if (p.D == 128) return run_fused<128, 128, true>(p, st);
+  return run_fused<256, 128, true>(p, st);
 }
 
 }  // namespace gdn

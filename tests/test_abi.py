@@ -70,7 +70,12 @@ def ws_status(d):
     (dict(qkv_dtype=0, beta_dtype=0, Dk=128, Dv=128, chunk=128), 2),
     (dict(qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, chunk=64), 0),
     (dict(variant=2, qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, chunk=64), 2),
-    (dict(variant=2, Dk=256, Dv=256), 2),
+    (dict(variant=2, Dk=256, Dv=256), 0),
+    (dict(variant=3), 0),
+    (dict(variant=3, Dk=256, Dv=256), 2),
+    (dict(variant=3, N=1, B=1), 0),
+    (dict(variant=3, B=1, N=3), 2),
+    (dict(variant=3, stop_after=3), 2),
     (dict(variant=2, stop_after=3), 2),
 ])
 def test_descriptor_validation(lib, kw, status):
@@ -84,9 +89,13 @@ def test_fused_needs_no_workspace_and_staged_does(lib):
     assert ws_status(desc(variant=2)) == (0, 0)
     st, n = ws_status(desc(variant=1))
     assert st == 0 and n > 0
-    # AUTO resolves to fused where it is built, to staged otherwise (D = 256)
+    # AUTO resolves to fused where it is built (bf16, D in {64, 128, 256}), to staged
+    # otherwise (fp32 operands), and to segmented for a few long sequences
     assert ws_status(desc(variant=0))[1] == 0
-    assert ws_status(desc(variant=0, Dk=256, Dv=256))[1] > 0
+    assert ws_status(desc(variant=0, Dk=256, Dv=256))[1] == 0
+    assert ws_status(desc(variant=0, qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, chunk=64))[1] > 0
+    assert ws_status(desc(variant=0, B=1, N=1, T=65536, H=8, Hg=8))[1] > 0
+    assert ws_status(desc(variant=3))[1] > 0
 
 
 def test_staged_layout_is_aligned_and_disjoint(lib):
