@@ -49,7 +49,7 @@ typedef enum gdn_status {
   GDN_OK = 0,
   GDN_ERR_INVALID_ARG = 1, /* null required pointer, bad shape, misaligned pointer */
   GDN_ERR_UNSUPPORTED = 2, /* valid but not built: Dk != Dv, D not in {64,128,256}, ... */
-  GDN_ERR_WORKSPACE = 3,   /* staged variant without a large enough workspace */
+  GDN_ERR_WORKSPACE = 3,   /* staged or segmented variant without the workspace it needs */
   GDN_ERR_HIP = 4          /* a HIP launch or attribute call failed */
 } gdn_status;
 
