@@ -346,3 +346,40 @@ def test_sampled_pairs_helper_matches_full_run():
         ts, b, _ = pair_slices(inp, n, h)
         np.testing.assert_allclose(o, o_ref[b, ts, h], rtol=0, atol=1e-14)
         np.testing.assert_allclose(ht, ht_ref[n, h], rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------ affine segment composition
+@pytest.mark.parametrize("bounds", [(0, 13, 37), (0, 1, 20, 21, 37), (0, 37)])
+def test_segments_compose_as_affine_maps(bounds):
+    """The segmented evaluation's algebra, on the oracle alone: the final state is affine in
+    the initial state, h_end = M h_in + b, with M the final state from h_in = I and v = 0
+    (M acts on the key index) and b the final state from h_in = 0.  Composing the segments'
+    maps in order gives the whole sequence's final state, and each segment run from its
+    composed h_in gives the whole sequence's outputs."""
+    q, k, v, g, beta, hs = rand_case(77, B=1, T=37, H=3, Hg=1, Dk=5, Dv=5)
+    o_full, ht_full = oracle.recurrence(q, k, v, g, beta, hs)
+    eye = np.broadcast_to(np.eye(5), (1, 3, 5, 5)).copy()
+    h = hs.copy()
+    for a, b_ in zip(bounds[:-1], bounds[1:]):
+        sl = (slice(None), slice(a, b_))
+        _, bseg = oracle.recurrence(q[sl], k[sl], v[sl], g[sl], beta[sl], None)
+        _, mseg = oracle.recurrence(q[sl], k[sl], 0 * v[sl], g[sl], beta[sl], eye)
+        oseg, _ = oracle.recurrence(q[sl], k[sl], v[sl], g[sl], beta[sl], h)
+        close(oseg, o_full[sl], 1e-11)
+        h = np.einsum("nhac,nhcb->nhab", mseg, h) + bseg
+    close(h, ht_full, 1e-11)
+
+
+def test_segment_map_orientation_is_pinned():
+    """A planted mistake: applying M on the value index (h M instead of M h) breaks the
+    composition, so the test above pins the orientation."""
+    q, k, v, g, beta, hs = rand_case(78, B=1, T=20, H=1, Dk=4, Dv=4)
+    _, ht_full = oracle.recurrence(q, k, v, g, beta, hs)
+    eye = np.eye(4)[None, None]
+    _, b1 = oracle.recurrence(q[:, :9], k[:, :9], v[:, :9], g[:, :9], beta[:, :9], None)
+    _, m1 = oracle.recurrence(q[:, :9], k[:, :9], 0 * v[:, :9], g[:, :9], beta[:, :9], eye)
+    _, b2 = oracle.recurrence(q[:, 9:], k[:, 9:], v[:, 9:], g[:, 9:], beta[:, 9:], None)
+    _, m2 = oracle.recurrence(q[:, 9:], k[:, 9:], 0 * v[:, 9:], g[:, 9:], beta[:, 9:], eye)
+    h1 = hs @ m1 + b1
+    wrong = h1 @ m2 + b2
+    assert np.abs(wrong - ht_full).max() > 1e-6
