@@ -504,18 +504,36 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
     f32x4 xk[NB], yq[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      bf16x8 kf[NDK / 2], qf[NDK / 2];
-#pragma unroll
-      for (int p = 0; p < NDK / 2; ++p) {
-        kf[p] = *reinterpret_cast<const bf16x8*>(Kc + kqoff[p] + b * 16 * D);
-        if constexpr (OUT) qf[p] = *reinterpret_cast<const bf16x8*>(Qc + kqoff[p] + b * 16 * D);
-      }
       xk[b] = yq[b] = zero4();
+      if constexpr (DK > 128) {
+        // 256 keys: the K fragments, then the Q fragments, so that only one set is live
+        bf16x8 f[NDK / 2];
 #pragma unroll
-      for (int p = 0; p < NDK / 2; ++p) xk[b] = mma32b(kf[p], stbo[p], xk[b]);
-      if constexpr (OUT) {
+        for (int p = 0; p < NDK / 2; ++p)
+          f[p] = *reinterpret_cast<const bf16x8*>(Kc + kqoff[p] + b * 16 * D);
 #pragma unroll
-        for (int p = 0; p < NDK / 2; ++p) yq[b] = mma32b(stbo[p], qf[p], yq[b]);
+        for (int p = 0; p < NDK / 2; ++p) xk[b] = mma32b(f[p], stbo[p], xk[b]);
+        if constexpr (OUT) {
+          sched_fence();
+#pragma unroll
+          for (int p = 0; p < NDK / 2; ++p)
+            f[p] = *reinterpret_cast<const bf16x8*>(Qc + kqoff[p] + b * 16 * D);
+#pragma unroll
+          for (int p = 0; p < NDK / 2; ++p) yq[b] = mma32b(stbo[p], f[p], yq[b]);
+        }
+      } else {
+        bf16x8 kf[NDK / 2], qf[NDK / 2];
+#pragma unroll
+        for (int p = 0; p < NDK / 2; ++p) {
+          kf[p] = *reinterpret_cast<const bf16x8*>(Kc + kqoff[p] + b * 16 * D);
+          if constexpr (OUT) qf[p] = *reinterpret_cast<const bf16x8*>(Qc + kqoff[p] + b * 16 * D);
+        }
+#pragma unroll
+        for (int p = 0; p < NDK / 2; ++p) xk[b] = mma32b(kf[p], stbo[p], xk[b]);
+        if constexpr (OUT) {
+#pragma unroll
+          for (int p = 0; p < NDK / 2; ++p) yq[b] = mma32b(stbo[p], qf[p], yq[b]);
+        }
       }
     }
     // forward substitution, outputs and the update operands, block by block
