@@ -32,6 +32,8 @@
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
+#include <type_traits>
+
 namespace gdn {
 
 namespace {
@@ -466,12 +468,12 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
     __syncthreads();
   }
 
-  int kb = 0;  // K/Q and gate buffer of chunk m (m % 3)
-  for (int m = 0; m < nchunks; ++m) {
+  // the loop body with compile-time buffer indices (kb = m % 3, tb = m % 2)
+  auto body = [&](int m, auto kbt, auto tbt) {
+    constexpr int kb = decltype(kbt)::value, tb = decltype(tbt)::value;
+    constexpr int kb1 = kb == 2 ? 0 : kb + 1, kb2 = kb1 == 2 ? 0 : kb1 + 1;
     const int cs = cs0 + m * CS;
     const int len = min(CS, L - m * CS);
-    const int tb = m & 1;
-    const int kb1 = kb == 2 ? 0 : kb + 1, kb2 = kb1 == 2 ? 0 : kb1 + 1;
     const bool more1 = m + 1 < nchunks, more2 = m + 2 < nchunks;
     // the next chunk's side work first, then the loads of later chunks, so the side work
     // does not hold registers with loads in flight
@@ -600,7 +602,14 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
     }
     if (more1) store_vtile(SV[tb ^ 1], vp);
     __syncthreads();
-    kb = kb1;
+  };
+  for (int m = 0; m < nchunks; m += 6) {
+    body(m, std::integral_constant<int, 0>(), std::integral_constant<int, 0>());
+    if (m + 1 < nchunks) body(m + 1, std::integral_constant<int, 1>(), std::integral_constant<int, 1>());
+    if (m + 2 < nchunks) body(m + 2, std::integral_constant<int, 2>(), std::integral_constant<int, 0>());
+    if (m + 3 < nchunks) body(m + 3, std::integral_constant<int, 0>(), std::integral_constant<int, 1>());
+    if (m + 4 < nchunks) body(m + 4, std::integral_constant<int, 1>(), std::integral_constant<int, 0>());
+    if (m + 5 < nchunks) body(m + 5, std::integral_constant<int, 2>(), std::integral_constant<int, 1>());
   }
 
   if (ht) {
