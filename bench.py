@@ -66,13 +66,15 @@ def pmc_traffic(workload: str, variant: str):
     return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
 
 
-def algorithmic_work(inp):
+def algorithmic_work(inp, variant="fused"):
     """Bytes moved and flops a perfect implementation needs (per call).
 
     Bytes: q and k once per q/k head, v, g, beta and h0 (if given) read once, o and ht
     written once.  Flops (triangle-aware, per token and value head):
     2 (3 C Dk / 2 + 2 C Dv / 2 + 3 Dk Dv) + C^2 / 3 — K K^T and Q K^T (half), T K and T V
-    (half), P v_new (half), W h, K^T v_new and Q h (full), plus the triangular inverse."""
+    (half), P v_new (half), W h, K^T v_new and Q h (full), plus the triangular inverse.
+    The recurrent variant does 6 Dk Dv per token and value head instead (k.H, q.H and the
+    rank-one update of the state)."""
     q, v = inp["q"], inp["v"]
     B, T, Hg, Dk = q.shape
     H, Dv = v.shape[2], v.shape[3]
@@ -85,6 +87,8 @@ def algorithmic_work(inp):
     if inp["h0"] is not None:
         by += nseq * H * Dk * Dv * 4
     fl = toks * H * (2 * (3 * C * Dk / 2 + 2 * C * Dv / 2 + 3 * Dk * Dv) + C * C / 3)
+    if variant == "recurrent":
+        fl = toks * H * 6 * Dk * Dv
     return float(by), float(fl)
 
 
@@ -163,7 +167,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="headline", choices=sorted(gdn_inputs.WORKLOADS))
-    ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged", "segmented"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged", "segmented", "recurrent"])
     ap.add_argument("--chunk", type=int, default=0,
                     help="override the workload's chunk size C (64 or 128)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -228,7 +232,7 @@ def main():
     tokens = q.shape[0] * q.shape[1]
     value = tokens / (ms_per_step * 1e-3)
 
-    by, fl = algorithmic_work(inp)
+    by, fl = algorithmic_work(inp, variant)
     avg_ms = float(np.mean(launch_ms))
     gbs = by / (avg_ms * 1e-3) / 1e9
     tfl = fl / (avg_ms * 1e-3) / 1e12
@@ -238,6 +242,8 @@ def main():
         kernel = "staged pipeline (8 launches; per-kernel split in profiles/)"
     elif variant == "segmented":
         kernel = "segmented: three k_fused passes over the segments and the segment scan"
+    elif variant == "recurrent":
+        kernel = "k_recurrent (D=%d, one wave per 32 state columns)" % w.Dk
     else:
         kernel = "k_fused (D=%d, 64-token chunks)" % w.Dk
     if bound == "hbm":

@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_HIP"}
 F32, BF16 = 0, 1
-VARIANTS = {"auto": 0, "staged": 1, "fused": 2, "segmented": 3}
+VARIANTS = {"auto": 0, "staged": 1, "fused": 2, "segmented": 3, "recurrent": 4}
 BUFFERS = {"chunk_table": 0, "seq_chunks": 1, "g_cum": 2, "g_t": 3, "beta_t": 4, "A": 5,
            "Tinv": 6, "W": 7, "U": 8, "h_c": 9, "v_new": 10}
 

@@ -28,7 +28,7 @@ gdn_status check_desc(const gdn_desc* d, gdn::Problem* p) {
   if (d->H % d->Hg != 0) return GDN_ERR_INVALID_ARG;
   if (d->qkv_dtype != GDN_F32 && d->qkv_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   if (d->beta_dtype != GDN_F32 && d->beta_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
-  if (d->variant < GDN_VARIANT_AUTO || d->variant > GDN_VARIANT_SEGMENTED)
+  if (d->variant < GDN_VARIANT_AUTO || d->variant > GDN_VARIANT_RECURRENT)
     return GDN_ERR_INVALID_ARG;
   if (d->stop_after < 0 || d->stop_after > 6) return GDN_ERR_INVALID_ARG;
   const int C = d->chunk == 0 ? 128 : d->chunk;
@@ -37,7 +37,6 @@ gdn_status check_desc(const gdn_desc* d, gdn::Problem* p) {
   const int D = d->Dk;
   if (D != 64 && D != 128 && D != 256) return GDN_ERR_UNSUPPORTED;
   const bool f32 = d->qkv_dtype == GDN_F32;
-  if (f32 && D * C > 8192) return GDN_ERR_UNSUPPORTED;  // fp32 operands: LDS budget
   const long long Ttot = (long long)d->B * d->T;
   if (Ttot > (1LL << 30)) return GDN_ERR_UNSUPPORTED;
   const int N = d->N == 0 ? d->B : d->N;
@@ -107,6 +106,22 @@ bool seg_ok(const gdn::Problem& p, const gdn_desc* d, bool dense) {
          (long long)p.N * p.T <= (1LL << 30);
 }
 
+// The staged kernels stage fp32 operands of at most 8192 elements per chunk row block in LDS.
+bool staged_ok(const gdn::Problem& p) { return !(p.f32 && p.D * p.C > 8192); }
+
+// The recurrent variant runs one token after another per (sequence, head): AUTO takes it
+// when a dense batch has at most kRecurrentMaxT tokens per sequence, or a packed batch at
+// most that many on average (decode).  Its grid is N H D / 32 single-wave workgroups.
+constexpr int kRecurrentMaxT = 8;
+
+bool recurrent_ok(const gdn::Problem& p, const gdn_desc* d) {
+  return d->stop_after == 0 && (long long)p.N * p.H * (p.D / 32) < (1LL << 31);
+}
+
+bool recurrent_pays(const gdn::Problem& p, bool dense) {
+  return dense ? p.T <= kRecurrentMaxT : (long long)p.Ttot <= (long long)kRecurrentMaxT * p.N;
+}
+
 // Variant actually run (after AUTO resolution), or -1 if the request cannot be served.
 // `dense`: no cu_seqlens.  `ws`: the workspace the call brings (AUTO picks the segmented
 // variant only when it pays off and the workspace is large enough; else the fused one).
@@ -114,10 +129,12 @@ int resolve_variant(const gdn_desc* d, const gdn::Problem& p, bool dense, bool w
   const bool fused_ok = gdn::fused_supported(p) && d->stop_after == 0;
   switch (d->variant) {
     case GDN_VARIANT_FUSED: return fused_ok ? GDN_VARIANT_FUSED : -1;
-    case GDN_VARIANT_STAGED: return GDN_VARIANT_STAGED;
+    case GDN_VARIANT_STAGED: return staged_ok(p) ? GDN_VARIANT_STAGED : -1;
     case GDN_VARIANT_SEGMENTED: return seg_ok(p, d, dense) ? GDN_VARIANT_SEGMENTED : -1;
+    case GDN_VARIANT_RECURRENT: return recurrent_ok(p, d) ? GDN_VARIANT_RECURRENT : -1;
     default: {
-      if (!fused_ok) return GDN_VARIANT_STAGED;
+      if (recurrent_ok(p, d) && recurrent_pays(p, dense)) return GDN_VARIANT_RECURRENT;
+      if (!fused_ok) return staged_ok(p) ? GDN_VARIANT_STAGED : -1;
       if (seg_ok(p, d, dense) && seg_plan(p, false).S > 1) {
         if (!ws_check) return GDN_VARIANT_SEGMENTED;
         const size_t need = seg_layout(p, seg_plan(p, false)).total;
@@ -166,7 +183,7 @@ size_t gdn_chunk_fwd_workspace_size(const gdn_desc* d, gdn_status* status) {
   if (status) *status = s;
   if (s != GDN_OK) return 0;
   const int v = resolve_variant(d, p, dense, false);
-  if (v == GDN_VARIANT_FUSED) return 0;
+  if (v == GDN_VARIANT_FUSED || v == GDN_VARIANT_RECURRENT) return 0;
   if (v == GDN_VARIANT_SEGMENTED)
     return seg_layout(p, seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED)).total;
   Layout L;
@@ -222,6 +239,8 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
   hipError_t e;
   if (variant == GDN_VARIANT_FUSED) {
     e = gdn::launch_fused(p, stream);
+  } else if (variant == GDN_VARIANT_RECURRENT) {
+    e = gdn::launch_recurrent(p, stream);
   } else if (variant == GDN_VARIANT_SEGMENTED) {
     const SegPlan sp = seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED);
     const SegLayout L = seg_layout(p, sp);

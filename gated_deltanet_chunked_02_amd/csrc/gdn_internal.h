@@ -49,6 +49,8 @@ struct Stages {
 hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st);
 bool fused_supported(const Problem& p);
 hipError_t launch_fused(const Problem& p, hipStream_t st);
+// Recurrent variant: token by token, one wave per (sequence, head, 32 state columns).
+hipError_t launch_recurrent(const Problem& p, hipStream_t st);
 // Segmented variant: segment table (cu_seg[n S + s] = n T + min(s Ls, T), cu_seg[N S] =
 // N T) and the sequential composition of the segments' affine state maps.
 hipError_t launch_segment_table(int32_t* cu_seg, int N, int T, int S, int Ls, hipStream_t st);

@@ -56,12 +56,14 @@ typedef enum gdn_status {
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 typedef enum gdn_variant {
-  GDN_VARIANT_AUTO = 0,      /* fused when built for the shape, otherwise staged; segmented
-                                for a dense batch of few long sequences when the workspace
-                                for it is given (fused otherwise)                          */
+  GDN_VARIANT_AUTO = 0,      /* recurrent for a few tokens per sequence (dense: T <= 8;
+                                packed: B*T <= 8 N); else fused when built for the shape,
+                                otherwise staged; segmented for a dense batch of few long
+                                sequences when the workspace for it is given (fused
+                                otherwise)                                                 */
   GDN_VARIANT_STAGED = 1,    /* seven launches, intermediates in the workspace */
   GDN_VARIANT_FUSED = 2,     /* one launch, one workgroup per (sequence, head) */
-  GDN_VARIANT_SEGMENTED = 3  /* dense batches only: every sequence split into S segments that
+  GDN_VARIANT_SEGMENTED = 3, /* dense batches only: every sequence split into S segments that
                                 run in parallel.  The state recurrence is affine in the
                                 initial state, h_end = M h_in + b; the fused kernel finds M
                                 (from h_in = I, v = 0) and b (from h_in = 0) of every segment,
@@ -69,6 +71,14 @@ typedef enum gdn_variant {
                                 last fused pass writes o.  Three passes over the data, S-fold
                                 parallelism (the long-prompt case of the FlashQLA how-to,
                                 section 8.3).  Needs the workspace reported for it.        */
+  GDN_VARIANT_RECURRENT = 4  /* token by token, the state kept in registers: one read and one
+                                write of each (sequence, head) state per call, whatever the
+                                number of tokens, and one dependent step per token.  For
+                                decode (one or a few tokens per sequence; the per-token
+                                delta-rule kernel of the Qwen3.5-on-Ascend page).  Any dtype
+                                and D the header lists; no workspace; chunk is ignored.
+                                ht may be the same buffer as h0 (state updated in place).
+                                The gates arrive as g and beta, as in every variant.       */
 } gdn_variant;
 
 /* Intermediate buffers of the staged variant, readable through gdn_stage_buffer(). */

@@ -77,6 +77,11 @@ def ws_status(d):
     (dict(variant=3, B=1, N=3), 2),
     (dict(variant=3, stop_after=3), 2),
     (dict(variant=2, stop_after=3), 2),
+    (dict(variant=4), 0),
+    (dict(variant=4, qkv_dtype=0, beta_dtype=0, Dk=256, Dv=256), 0),
+    (dict(variant=4, stop_after=3), 2),
+    (dict(variant=5), 1),
+    (dict(variant=1, qkv_dtype=0, beta_dtype=0, Dk=128, Dv=128, chunk=128), 2),
 ])
 def test_descriptor_validation(lib, kw, status):
     st, n = ws_status(desc(**kw))
@@ -96,6 +101,20 @@ def test_fused_needs_no_workspace_and_staged_does(lib):
     assert ws_status(desc(variant=0, qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, chunk=64))[1] > 0
     assert ws_status(desc(variant=0, B=1, N=1, T=65536, H=8, Hg=8))[1] > 0
     assert ws_status(desc(variant=3))[1] > 0
+
+
+def test_auto_takes_recurrent_for_few_tokens_per_sequence(lib):
+    A = 0x10000  # only the nullness of cu_seqlens is read
+    assert gdn.gdn_resolved_variant(desc(T=1)) == "recurrent"
+    assert gdn.gdn_resolved_variant(desc(T=8)) == "recurrent"
+    assert gdn.gdn_resolved_variant(desc(T=9)) == "fused"
+    assert gdn.gdn_resolved_variant(desc(T=8, qkv_dtype=0, beta_dtype=0)) == "recurrent"
+    # packed batches: the mean length decides (64 sequences in 512 tokens, then 513)
+    assert gdn.gdn_resolved_variant(desc(B=1, N=64, T=512), A) == "recurrent"
+    assert gdn.gdn_resolved_variant(desc(B=1, N=64, T=513), A) == "fused"
+    assert gdn.gdn_resolved_variant(desc(variant=4, T=4096)) == "recurrent"
+    assert ws_status(desc(variant=4)) == (0, 0)
+    assert ws_status(desc(T=8)) == (0, 0)
 
 
 def test_staged_layout_is_aligned_and_disjoint(lib):

@@ -31,6 +31,8 @@ CASES = [
     ("long", {"T": 512}, 8),
     ("long", {"T": 4096}, 8),
     ("long", {"T": 16384}, 8),
+    ("decode", {}, 32),
+    ("decode", {"T": 8}, 16),
 ]
 
 

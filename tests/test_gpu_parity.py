@@ -364,3 +364,85 @@ def test_segmented_resolution():
     d2 = gdn.make_desc(q2, v2, b2, None, 128, "auto")
     assert gdn.gdn_chunk_fwd_workspace_size(d2) == 0
     assert gdn.gdn_resolved_variant(d2) == "fused"
+
+
+# ------------------------------------------------------------------ recurrent (decode) variant
+REC_CASES = [
+    # D, dtype, H, Hg, B, T, h0
+    (128, "bf16", 4, 2, 8, 1, True),
+    (128, "bf16", 4, 4, 3, 16, True),
+    (64, "f32", 2, 2, 3, 5, True),
+    (64, "bf16", 4, 1, 2, 7, False),
+    (256, "bf16", 2, 1, 2, 3, True),
+    (256, "f32", 2, 2, 1, 4, True),
+    (128, "f32", 2, 1, 2, 40, False),
+]
+
+
+@pytest.mark.parametrize("D,dtype,H,Hg,B,T,h0", REC_CASES)
+def test_recurrent_matches_oracle(D, dtype, H, Hg, B, T, h0):
+    inp = draw(B=B, T=T, H=H, Hg=Hg, Dk=D, dtype=dtype, seed=11 + D + T,
+               h0_std=0.05 if h0 else None)
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant="recurrent")
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "recurrent D%d %s" % (D, dtype))
+    log(test="recurrent", D=D, dtype=dtype, H=H, Hg=Hg, B=B, T=T, o_err=eo, ht_err=eh)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_recurrent_varlen_edge_lengths(D):
+    lens = [1, 0, 3, 1, 17, 2]
+    w = gdn_inputs.small(H=4, Hg=2, Dk=D, seed=13, h0_std=0.05)
+    inp = gdn_inputs.draw(w.with_(B=1, T=sum(lens)), device="cpu")
+    inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    inp["h0"] = torch.randn(len(lens), 4, D, D, generator=torch.Generator().manual_seed(5)) * 0.05
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant="recurrent")
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "recurrent varlen")
+    assert torch.equal(ht[1].cpu(), inp["h0"][1])  # the empty sequence keeps its state
+    log(test="recurrent_varlen", D=D, o_rel=eo, ht_rel=eh)
+
+
+def test_recurrent_decode_loop_in_place_equals_one_call():
+    """Decode as a serving loop runs it: one token per call, the state updated in place
+    (ht is the h0 buffer).  After T calls, o and the state match one call over all T
+    tokens and the oracle."""
+    import gated_deltanet_chunked_02_amd as gdn
+    D, H, Hg, B, T = 128, 4, 2, 3, 6
+    inp = draw(B=B, T=T, H=H, Hg=Hg, Dk=D, seed=17, h0_std=0.05)
+    o_ref, ht_ref = oracle_full(inp)
+    dev = torch.device("cuda")
+    state = inp["h0"].clone().to(dev)
+    outs = []
+    for t in range(T):
+        sl = lambda x: x[:, t:t + 1].contiguous().to(dev)
+        q, k, v, g, beta = (sl(inp[n]) for n in ("q", "k", "v", "g", "beta"))
+        o = torch.empty_like(v)
+        desc = gdn.make_desc(q, v, beta, None, 128, "recurrent")
+        st = gdn.gdn_chunk_fwd(desc, q, k, v, g, beta, state, None, inp["scale"], o, state)
+        assert st == 0
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_loop = torch.cat(outs, dim=1)
+    check_against_oracle(inp, o_loop, state, o_ref, ht_ref, "decode loop")
+    o_one, ht_one = run_gdn(inp, variant="recurrent")
+    # the same per-token arithmetic in the same order: identical results
+    assert torch.equal(o_one, o_loop)
+    assert torch.equal(ht_one, state)
+
+
+def test_recurrent_without_final_state():
+    inp = draw(B=2, T=3, H=2, Hg=2, Dk=128, seed=19, h0_std=0.05)
+    o_ref, _ = oracle_full(inp)
+    o, ht = run_gdn(inp, variant="recurrent", output_final_state=False)
+    assert ht is None
+    assert rel_l2(to64(o), o_ref) <= 5e-3
+
+
+def test_auto_takes_recurrent_for_decode_shapes():
+    inp = draw(B=4, T=2, H=2, Hg=2, Dk=64, seed=23, h0_std=0.05)
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant="auto")
+    check_against_oracle(inp, o, ht, o_ref, ht_ref, "auto decode")
+    o_r, ht_r = run_gdn(inp, variant="recurrent")
+    assert torch.equal(o, o_r) and torch.equal(ht, ht_r)
