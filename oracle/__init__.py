@@ -15,6 +15,8 @@ Contents
   transpose, scaled_dot_kkt, solve_tril, wy_fast, chunk_h, chunk_o), in fp64 numpy, in the
   page's order; it yields every stage intermediate for per-stage parity of the staged GPU
   variant and is itself pinned to ``recurrence``.
+* ``conv1d`` — the causal depthwise convolution with its decode state that precedes the
+  gated delta rule (the Qwen3.5-on-Ascend page's causal_conv1d), in fp64 numpy.
 
 Every function here follows its cited passage; none is blocked, fused or reordered beyond
 what that passage states.

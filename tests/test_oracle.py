@@ -383,3 +383,98 @@ def test_segment_map_orientation_is_pinned():
     h1 = hs @ m1 + b1
     wrong = h1 @ m2 + b2
     assert np.abs(wrong - ht_full).max() > 1e-6
+
+
+# ------------------------------------------------------------------ causal conv1d oracle
+from oracle import conv1d as cv  # noqa: E402
+
+
+def conv_case(seed, T=23, C=6, W=4, B=1):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, T, C)), rng.standard_normal((C, W)),
+            rng.standard_normal(C))
+
+
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_conv1d_matches_numpy_convolution(W):
+    """With no state the causal convolution is numpy's full convolution with the reversed
+    taps, truncated to the first T outputs, plus the bias."""
+    x, w, b = conv_case(40 + W, W=W)
+    y, st = cv.causal_conv1d(x, w, b)
+    assert st is None
+    for c in range(x.shape[2]):
+        ref = np.convolve(x[0, :, c], w[c, ::-1])[:x.shape[1]] + b[c]
+        close(y[0, :, c], ref, 1e-12)
+
+
+def test_conv1d_impulse_response():
+    """A unit impulse at position p in channel c gives y[p + i, c] = weight[c, W - 1 - i]:
+    the last tap multiplies the current token, the first the oldest."""
+    W, T, C, p, c = 4, 12, 3, 5, 1
+    x = np.zeros((1, T, C))
+    x[0, p, c] = 1.0
+    w = np.arange(1.0, 1.0 + C * W).reshape(C, W)
+    y, _ = cv.causal_conv1d(x, w)
+    expect = np.zeros((1, T, C))
+    for i in range(W):
+        expect[0, p + i, c] = w[c, W - 1 - i]
+    close(y, expect, 0)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7])
+def test_conv1d_continues_across_calls(split):
+    """Two calls with the state carried (including a first piece shorter than W - 1) give
+    the outputs and final state of one call over the whole sequence."""
+    x, w, b = conv_case(50 + split, T=15, W=4)
+    rng = np.random.default_rng(9)
+    st0 = rng.standard_normal((1, 3, x.shape[2]))
+    y_all, st_all = cv.causal_conv1d(x, w, b, conv_state=st0, activation="silu")
+    y1, st1 = cv.causal_conv1d(x[:, :split], w, b, conv_state=st0, activation="silu")
+    y2, st2 = cv.causal_conv1d(x[:, split:], w, b, conv_state=st1, activation="silu")
+    close(np.concatenate([y1, y2], axis=1), y_all, 1e-12)
+    close(st2, st_all, 0)
+
+
+def test_conv1d_state_holds_the_last_inputs():
+    x, w, b = conv_case(61, T=9, W=4)
+    st0 = np.full((1, 3, x.shape[2]), 7.0)
+    _, st = cv.causal_conv1d(x, w, b, conv_state=st0)
+    close(st[0], x[0, -3:], 0)
+    # a sequence of one token shifts the old state by one
+    _, st = cv.causal_conv1d(x[:, :1], w, b, conv_state=st0)
+    close(st[0], np.concatenate([st0[0, 1:], x[0, :1]]), 0)
+
+
+def test_silu_values_and_odd_identity():
+    z = np.linspace(-30, 30, 121)
+    close(cv.silu(z) - cv.silu(-z), z, 1e-12)  # z s(z) + z s(-z) = z
+    assert cv.silu(0.0) == 0.0
+    close(cv.silu(1.0), 0.7310585786300049, 1e-15)  # the logistic function at 1
+    close(cv.silu(40.0), 40.0, 1e-12)
+    assert abs(cv.silu(-40.0)) < 1e-15
+
+
+def test_conv1d_packed_equals_per_sequence_runs():
+    """A packed batch with permuted cache lines, a sequence that starts from zeros and an
+    empty sequence equals per-sequence runs on the matching lines."""
+    rng = np.random.default_rng(71)
+    C, W = 5, 3
+    lens = [4, 0, 1, 6]
+    x = rng.standard_normal((1, sum(lens), C))
+    w, b = rng.standard_normal((C, W)), rng.standard_normal(C)
+    st0 = rng.standard_normal((6, W - 1, C))
+    idx = np.array([5, 0, 2, 3])
+    init = np.array([1, 1, 0, 1])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    y, st = cv.causal_conv1d(x, w, b, conv_state=st0, cache_indices=idx,
+                             has_initial_state=init, cu_seqlens=cu, activation="silu")
+    for n in range(len(lens)):
+        s, e = cu[n], cu[n + 1]
+        head = st0[idx[n]] if init[n] else np.zeros((W - 1, C))
+        yn, stn = cv.causal_conv1d(x[:, s:e], w, b, conv_state=head[None],
+                                   activation="silu")
+        close(y[0, s:e], yn[0], 0)
+        close(st[idx[n]], stn[0], 0)
+    close(st[1], st0[1], 0)  # an unused line is untouched
+    close(st[4], st0[4], 0)
+    close(st[0], st0[0], 0)  # the empty sequence leaves its line as it was
