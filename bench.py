@@ -158,6 +158,62 @@ def copy_reference(args, dev):
                       "ms_per_copy": ms, "GBps": 4 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def conv_bench(args, dev, gdn):
+    """Time gdn_causal_conv1d_fwd (both of its launches) on a conv workload.  Algorithmic
+    bytes: x read and y written once, weight and bias, and each sequence's state line read
+    and written once."""
+    w = gdn_inputs.CONV_WORKLOADS[args.workload]
+    print("[bench] drawing %s on %s" % (w.name, dev), file=sys.stderr, flush=True)
+    inp = gdn_inputs.draw_conv(w, device=dev)
+    x, wt, b, st, idx = (inp[n] for n in ("x", "weight", "bias", "conv_state", "cache_indices"))
+    y = torch.empty_like(x)
+    desc = gdn.GdnConvDesc(B=w.B, T=w.T, N=w.B, channels=w.channels, width=w.width,
+                           dtype=gdn._dtype_code(x), activation=gdn.ACTIVATIONS[w.activation],
+                           state_lines=w.lines)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = gdn.gdn_causal_conv1d_fwd(desc, x, wt, b, st, idx, None, None, y, stream)
+        if rc != 0:
+            raise gdn.GdnError(rc, "gdn_causal_conv1d_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    avg_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    ms_per_step = 1e3 * t_wall / args.steps
+    el = x.element_size()
+    toks = w.B * w.T
+    by = 2.0 * toks * w.channels * el + w.channels * (w.width + 1) * 4 + \
+        2.0 * w.B * (w.width - 1) * w.channels * el
+    gbs = by / (avg_ms * 1e-3) / 1e9
+    out = {
+        "metric": "causal conv1d tokens/s at 1 MI355X", "value": toks / (ms_per_step * 1e-3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if x.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "channels": w.channels,
+                   "width": w.width, "activation": w.activation, "state_lines": w.lines,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_conv1d + k_conv_state (W=%d)" % w.width,
+                     "launch_ms": avg_ms, "algorithmic_bytes": by},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,7 +222,9 @@ def main():
     # timed launches (about 0.25 s) average over it.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="headline", choices=sorted(gdn_inputs.WORKLOADS))
+    ap.add_argument("--workload", default="headline",
+                    choices=sorted(gdn_inputs.WORKLOADS) + sorted(gdn_inputs.CONV_WORKLOADS),
+                    help="conv_*: the causal conv1d before the delta rule")
     ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged", "segmented", "recurrent"])
     ap.add_argument("--chunk", type=int, default=0,
                     help="override the workload's chunk size C (64 or 128)")
@@ -189,6 +247,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.mode == "copy":
         copy_reference(args, dev)
+        return
+    if args.workload in gdn_inputs.CONV_WORKLOADS:
+        conv_bench(args, dev, gdn)
         return
     w = gdn_inputs.WORKLOADS[args.workload]
     if args.chunk:

@@ -10,6 +10,9 @@ Low level (same names as the C ABI in include/gdn.h):
 High level (the call shape of the FlashQLA how-to, step 5.2):
     o, ht = chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                                    output_final_state=True, cu_seqlens=None, chunk_size=128)
+The short convolution before it (low level gdn_causal_conv1d_fwd):
+    y = causal_conv1d(x, weight, bias=None, conv_state=None, cache_indices=None,
+                      has_initial_state=None, cu_seqlens=None, activation=None)
 """
 from __future__ import annotations
 
@@ -20,6 +23,7 @@ __all__ = [
     "GdnDesc", "GdnError", "load", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size",
     "gdn_stage_buffer", "gdn_status_string", "gdn_version", "chunk_gated_delta_rule",
     "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH", "gdn_resolved_variant",
+    "GdnConvDesc", "gdn_causal_conv1d_fwd", "causal_conv1d", "ACTIVATIONS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -28,6 +32,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_HIP"}
 F32, BF16 = 0, 1
 VARIANTS = {"auto": 0, "staged": 1, "fused": 2, "segmented": 3, "recurrent": 4}
+ACTIVATIONS = {None: 0, "none": 0, "silu": 1}
 BUFFERS = {"chunk_table": 0, "seq_chunks": 1, "g_cum": 2, "g_t": 3, "beta_t": 4, "A": 5,
            "Tinv": 6, "W": 7, "U": 8, "h_c": 9, "v_new": 10}
 
@@ -46,6 +51,13 @@ class GdnDesc(ctypes.Structure):
                 ("qkv_dtype", ctypes.c_int32), ("beta_dtype", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("stop_after", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class GdnConvDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("channels", ctypes.c_int32), ("width", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("state_lines", ctypes.c_int32)]
 
 
 _lib = None
@@ -76,6 +88,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_version.argtypes = []
     lib.gdn_resolved_variant.restype = ctypes.c_int32
     lib.gdn_resolved_variant.argtypes = [ctypes.POINTER(GdnDesc), P]
+    lib.gdn_causal_conv1d_fwd.restype = ctypes.c_int
+    lib.gdn_causal_conv1d_fwd.argtypes = [ctypes.POINTER(GdnConvDesc), P, P, P, P, P, P, P, P,
+                                          P]
     _lib = lib
     return lib
 
@@ -199,3 +214,53 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     if st != 0:
         raise GdnError(st, "gdn_chunk_fwd")
     return o, ht
+
+
+def gdn_causal_conv1d_fwd(desc: GdnConvDesc, x, weight, bias, conv_state, cache_indices,
+                          has_initial_state, cu_seqlens, y, stream=None) -> int:
+    """Raw call (tensors, integer device addresses or None); returns the status code."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return int(load().gdn_causal_conv1d_fwd(
+        ctypes.byref(desc), _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state),
+        _ptr(cache_indices), _ptr(has_initial_state), _ptr(cu_seqlens), _ptr(y), stream))
+
+
+def causal_conv1d(x, weight, bias=None, conv_state=None, cache_indices=None,
+                  has_initial_state=None, cu_seqlens=None, activation=None):
+    """Causal depthwise conv1d on the current stream; returns y and updates conv_state in
+    place.  x: [B, T, C] (packed: B = 1 with cu_seqlens int32 [N + 1]); weight [C, W] fp32;
+    bias [C] fp32; conv_state [lines, W - 1, C] in x's dtype; cache_indices and
+    has_initial_state int32 [N]; activation None or "silu"."""
+    import torch
+    for name, t in (("x", x), ("weight", weight)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if conv_state is not None and not conv_state.is_contiguous():
+        raise ValueError("conv_state must be contiguous (it is updated in place)")
+    if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise TypeError("weight and bias must be fp32")
+    if conv_state is not None and conv_state.dtype != x.dtype:
+        raise TypeError("conv_state must have x's dtype")
+    B, T, C = x.shape
+    weight = weight.contiguous()
+    if bias is not None:
+        if not bias.is_cuda:
+            raise ValueError("bias must be a device tensor")
+        bias = bias.contiguous()
+    i32 = lambda t: None if t is None else t.to(torch.int32).contiguous()
+    cu, idx, init = i32(cu_seqlens), i32(cache_indices), i32(has_initial_state)
+    N = B if cu is None else cu.numel() - 1
+    desc = GdnConvDesc(B=B, T=T, N=N, channels=C, width=weight.shape[1], dtype=_dtype_code(x),
+                       activation=ACTIVATIONS[activation],
+                       state_lines=0 if conv_state is None else conv_state.shape[0])
+    y = torch.empty_like(x)
+    st = gdn_causal_conv1d_fwd(desc, x, weight, bias, conv_state, idx, init, cu, y)
+    if st != 0:
+        raise GdnError(st, "gdn_causal_conv1d_fwd")
+    return y

@@ -304,6 +304,53 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_causal_conv1d_fwd(const gdn_conv_desc* d, const void* x, const float* weight,
+                                 const float* bias, void* conv_state,
+                                 const int32_t* cache_indices,
+                                 const int32_t* has_initial_state, const int32_t* cu_seqlens,
+                                 void* y, hipStream_t stream) {
+  if (!d || !weight) return GDN_ERR_INVALID_ARG;
+  if (d->B < 1 || d->T < 0 || d->N < 0 || d->channels < 1 || d->state_lines < 0)
+    return GDN_ERR_INVALID_ARG;
+  if ((long long)d->B * d->T > 0 && (!x || !y)) return GDN_ERR_INVALID_ARG;
+  if (d->dtype != GDN_F32 && d->dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (d->activation != GDN_ACT_NONE && d->activation != GDN_ACT_SILU) return GDN_ERR_INVALID_ARG;
+  if (d->width < 2 || d->width > 4 || d->channels % 8 != 0) return GDN_ERR_UNSUPPORTED;
+  const long long Ttot = (long long)d->B * d->T;
+  if (Ttot > (1LL << 30) || (long long)d->channels * 8 > (1LL << 30)) return GDN_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(conv_state, 16) || !aligned(weight, 4) ||
+      !aligned(bias, 4) || !aligned(cache_indices, 4) || !aligned(has_initial_state, 4) ||
+      !aligned(cu_seqlens, 4))
+    return GDN_ERR_INVALID_ARG;
+  if (conv_state && d->state_lines < 1) return GDN_ERR_INVALID_ARG;
+  int N = d->N;
+  if (cu_seqlens) {
+    if (d->B != 1) return GDN_ERR_INVALID_ARG;
+  } else {
+    if (d->N != 0 && d->N != d->B) return GDN_ERR_INVALID_ARG;
+    N = d->B;
+  }
+  if (N == 0) return GDN_OK;
+  gdn::ConvProblem p;
+  p.T = d->T;
+  p.Ttot = (int)Ttot;
+  p.N = N;
+  p.C = d->channels;
+  p.W = d->width;
+  p.lines = conv_state ? d->state_lines : 0;
+  p.f32 = d->dtype == GDN_F32;
+  p.silu = d->activation == GDN_ACT_SILU;
+  p.x = x;
+  p.weight = weight;
+  p.bias = bias;
+  p.state = conv_state;
+  p.cache_indices = cache_indices;
+  p.has_initial_state = has_initial_state;
+  p.cu = cu_seqlens;
+  p.y = y;
+  return gdn::launch_conv1d(p, stream) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 int32_t gdn_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens) {
   gdn::Problem p;
   if (check_desc(d, &p) != GDN_OK) return -1;

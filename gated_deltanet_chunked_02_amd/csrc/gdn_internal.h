@@ -49,6 +49,22 @@ struct Stages {
 hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st);
 bool fused_supported(const Problem& p);
 hipError_t launch_fused(const Problem& p, hipStream_t st);
+// Causal depthwise conv1d with a decode state (the step before the delta rule).
+struct ConvProblem {
+  int T, Ttot, N, C, W, lines;  // C channels (multiple of 8), W taps in {2, 3, 4}
+  bool f32;                     // x, y, state are fp32 (else bf16)
+  bool silu;
+  const void* x;
+  const float* weight;
+  const float* bias;
+  void* state;
+  const int32_t* cache_indices;
+  const int32_t* has_initial_state;
+  const int32_t* cu;
+  void* y;
+};
+hipError_t launch_conv1d(const ConvProblem& p, hipStream_t st);
+
 // Recurrent variant: token by token, one wave per (sequence, head, 32 state columns).
 hipError_t launch_recurrent(const Problem& p, hipStream_t st);
 // Segmented variant: segment table (cu_seg[n S + s] = n T + min(s Ls, T), cu_seg[N S] =

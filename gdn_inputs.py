@@ -115,3 +115,54 @@ def small(name="small", *, B=1, T=256, H=2, Hg=None, Dk=64, Dv=None, C=64, dtype
     return Workload(name, H=H, Hg=Hg or H, Dk=Dk, Dv=Dv or Dk, C=C, dtype=dtype, seed=seed,
                     B=B, T=T, n_varlen=n_varlen, max_len=max_len, h0_std=h0_std,
                     beta_dtype=beta_dtype)
+
+
+# ---------------------------------------------------------------- causal conv1d inputs
+@dataclasses.dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    channels: int
+    width: int
+    dtype: str
+    seed: int
+    B: int = 1
+    T: int = 0
+    lines: int = 0          # state lines (0: no state)
+    activation: str = "silu"
+
+    def with_(self, **kw) -> "ConvWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# The convolution runs over the concatenated q, k, v projections of a layer, so its channel
+# count is 2 Hg Dk + H Dv: 12288 for the 32-head, D = 128 shape of the prefill workload.
+CONV_WORKLOADS = {
+    "conv_prefill": ConvWorkload("conv_bf16_16x8192_c12288_w4_silu", channels=12288, width=4,
+                                 dtype="bf16", seed=6, B=16, T=8192, lines=16),
+    "conv_decode": ConvWorkload("conv_bf16_decode_256x1_c12288_w4_silu", channels=12288,
+                                width=4, dtype="bf16", seed=7, B=256, T=1, lines=256),
+}
+
+
+def draw_conv(w: ConvWorkload, device="cpu"):
+    """x ~ N(0, 1), weight ~ N(0, 1 / W), bias ~ N(0, 0.1^2), state lines ~ N(0, 1) cast to
+    the dtype; sequence n uses line (n * 7 + 3) mod lines when that is a permutation, else n;
+    every sequence starts from its line.  Draw order: x, weight, bias, state."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    dt = DTYPES[w.dtype]
+    x = torch.randn((w.B, w.T, w.channels), generator=gen, device=dev).to(dt)
+    weight = torch.randn((w.channels, w.width), generator=gen, device=dev) / w.width ** 0.5
+    bias = torch.randn((w.channels,), generator=gen, device=dev) * 0.1
+    state = idx = None
+    if w.lines:
+        state = torch.randn((w.lines, w.width - 1, w.channels), generator=gen,
+                            device=dev).to(dt)
+        import math
+        perm = math.gcd(7, w.lines) == 1 and w.lines >= w.B
+        idx = torch.tensor([(n * 7 + 3) % w.lines if perm else n for n in range(w.B)],
+                           dtype=torch.int32, device=dev)
+    return dict(x=x, weight=weight, bias=bias, conv_state=state, cache_indices=idx,
+                has_initial_state=None, cu_seqlens=None, activation=w.activation,
+                workload=w)

@@ -113,6 +113,49 @@ typedef struct gdn_desc {
   size_t workspace_bytes;
 } gdn_desc;
 
+/* Causal depthwise 1-D convolution with a decode state: the step before the gated delta
+ * rule (the causal_conv1d operator of the Qwen3.5-on-Ascend page).  For sequence n, channel
+ * c and position t of the sequence, with x~ = (the W - 1 inputs before the sequence, taken
+ * from the sequence's state line, or zeros) followed by the sequence's inputs,
+ *
+ *     y[t, c] = act(bias[c] + sum_{i < W} weight[c, i] x~[t + i, c])
+ *
+ * (weight[c, W - 1] multiplies the current token) and, when conv_state is given, the line
+ * afterwards holds the last W - 1 entries of x~ (part of the old line when the sequence is
+ * shorter than W - 1).  act is the identity or SiLU (z sigmoid(z)), in fp32.
+ *
+ * Layouts (contiguous, row-major; channels contiguous so that a token's row is one read):
+ *   x, y        [B, T, C]            dtype (bf16 or f32); packed: B = 1, T = total tokens
+ *   weight      [C, W]               f32
+ *   bias        [C]                  f32, or NULL (zero)
+ *   conv_state  [state_lines, W - 1, C]  dtype, or NULL (zeros in, nothing written); read
+ *                                    and written in place
+ *   cache_indices      [N] int32 or NULL (sequence n uses line n): an index outside
+ *                      [0, state_lines) gives a zero start and leaves every line untouched
+ *   has_initial_state  [N] int32 or NULL (all start from their line): 0 = start from zeros
+ *   cu_seqlens         [N + 1] int32 or NULL (dense batch), as for gdn_chunk_fwd
+ * C is a multiple of 8 and W is 2, 3 or 4; pointers are device pointers, x, y and conv_state
+ * 16-byte aligned; weight is required, x and y too unless B*T = 0.  Two sequences naming the same line give unspecified lines.  Errors are
+ * returned before any launch; the work is enqueued on `stream` (two launches: outputs, then
+ * the state lines). */
+typedef enum gdn_activation { GDN_ACT_NONE = 0, GDN_ACT_SILU = 1 } gdn_activation;
+
+typedef struct gdn_conv_desc {
+  int32_t B, T;        /* dense [B, T, C]; packed: B = 1, T = total tokens              */
+  int32_t N;           /* sequences: B (or 0) for a dense batch, len(cu_seqlens) - 1     */
+  int32_t channels;    /* C                                                             */
+  int32_t width;       /* W                                                             */
+  int32_t dtype;       /* gdn_dtype of x, y and conv_state                              */
+  int32_t activation;  /* gdn_activation                                                */
+  int32_t state_lines; /* lines in conv_state                                           */
+} gdn_conv_desc;
+
+gdn_status gdn_causal_conv1d_fwd(const gdn_conv_desc* d, const void* x, const float* weight,
+                                 const float* bias, void* conv_state,
+                                 const int32_t* cache_indices,
+                                 const int32_t* has_initial_state, const int32_t* cu_seqlens,
+                                 void* y, hipStream_t stream);
+
 /* Bytes of workspace the variant chosen by d->variant needs (0 for the fused variant; for
  * AUTO, what AUTO picks when given that much).  The query cannot see cu_seqlens: a
  * descriptor with N == 0 or N == B is taken as a dense batch.  Host-only, no device work.

@@ -169,3 +169,36 @@ def test_python_binding_refuses_cpu_tensors(lib):
     g = torch.zeros(1, 4, 1)
     with pytest.raises(ValueError):
         gdn.chunk_gated_delta_rule(x, x, x, g, g.to(torch.bfloat16))
+
+
+def conv_status(**kw):
+    base = dict(B=2, T=64, N=0, channels=64, width=4, dtype=1, activation=1, state_lines=2)
+    base.update({k: v for k, v in kw.items() if k in base})
+    d = gdn.GdnConvDesc(**base)
+    A = 0x10000  # fake, aligned: every case below must fail (or finish) before any launch
+    args = dict(x=A, weight=A, bias=None, state=A, idx=None, init=None, cu=None, y=A)
+    args.update({k: v for k, v in kw.items() if k in args})
+    return gdn.load().gdn_causal_conv1d_fwd(ctypes.byref(d), args["x"], args["weight"],
+                                            args["bias"], args["state"], args["idx"],
+                                            args["init"], args["cu"], args["y"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(width=1), 2),
+    (dict(width=5), 2),
+    (dict(channels=60), 2),
+    (dict(dtype=7), 1),
+    (dict(activation=5), 1),
+    (dict(x=None), 1),
+    (dict(y=None), 1),
+    (dict(weight=None), 1),
+    (dict(x=0x10000 + 8), 1),
+    (dict(state=0x10000 + 4), 1),
+    (dict(state_lines=0), 1),
+    (dict(N=3), 1),                       # dense: N must be B (or 0)
+    (dict(cu=0x10000), 1),                # packed needs B == 1
+    (dict(B=1, N=0, cu=0x10000), 0),      # no sequences: nothing to do, no launch
+    (dict(B=-1), 1),
+])
+def test_conv1d_rejects_bad_arguments_before_any_launch(lib, kw, status):
+    assert conv_status(**kw) == status
