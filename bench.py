@@ -228,6 +228,8 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "fused", "staged", "segmented", "recurrent"])
     ap.add_argument("--chunk", type=int, default=0,
                     help="override the workload's chunk size C (64 or 128)")
+    ap.add_argument("--set", action="append", default=[], metavar="FIELD=INT",
+                    help="override an integer field of the workload (e.g. H=16, T=4096)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--mode", default="gdn", choices=["gdn", "copy"],
@@ -254,6 +256,9 @@ def main():
     w = gdn_inputs.WORKLOADS[args.workload]
     if args.chunk:
         w = w.with_(C=args.chunk)
+    for kv in args.set:
+        field, val = kv.split("=", 1)
+        w = w.with_(**{field: int(val)})
     print("[bench] drawing %s on %s" % (w.name, dev), file=sys.stderr, flush=True)
     inp = gdn_inputs.draw(w, device=dev)
     q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))
