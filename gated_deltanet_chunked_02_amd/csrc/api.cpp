@@ -64,7 +64,7 @@ struct SegPlan {
 constexpr int kFusedChunk = 64;
 constexpr int kTargetPairs = 256;    // (segment, head) pairs that fill the GPU: one per CU
 constexpr int kAutoMinSegments = 4;  // AUTO segments only when it gives at least 4 segments
-constexpr int kAutoMinSegLen = 1024; // of at least 1024 tokens (three passes over the data)
+constexpr int kAutoMinSegLen = 512;  // of at least 512 tokens (three passes over the data)
 
 SegPlan seg_plan(const gdn::Problem& p, bool forced) {
   SegPlan sp;

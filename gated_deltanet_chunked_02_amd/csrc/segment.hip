@@ -30,59 +30,95 @@ __global__ void k_segment_table(int32_t* cu_seg, int N, int T, int S, int Ls) {
 // One workgroup per (sequence, head, 16-column slab of the state): the columns of
 // h_out = M h_in + b are independent, so each slab is composed on its own.  h = h0 (zero
 // when absent); for each segment s, h_in[n S + s] = h and h <- M[n S + s] h + b[n S + s];
-// finally ht = h.  fp32 throughout; thread (rg, c) owns column c of the slab and rows
-// rg R .. rg R + R - 1 (R = D / 16), M is staged in LDS per step, the slab kept there.
+// finally ht = h.  fp32 throughout.
+//
+// The product M h of a step is a D x D by D x 16 GEMM, done on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32): the slab is D / 16 output tiles of 16 x 16, spread over the four
+// waves and kept in registers in the accumulator layout (lane l: rows 4 (l / 16) + i of
+// column l % 16).  M is staged row-major in LDS and the slab column-major, both with a
+// padded stride, so one float4 read per lane supplies four consecutive k of one row or
+// column: matrix-core instruction j of a 16-wide k block takes k = k0 + 4 (l / 16) + j in
+// lane l for both operands (any assignment of k to slots works as long as A and B agree).
+// Step s + 1's M and b are loaded into registers while step s is composed.
 template <int D>
 __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ M,
                                                       const float* __restrict__ b,
                                                       const float* __restrict__ h0,
                                                       float* __restrict__ h_in,
                                                       float* __restrict__ ht, int S, int H) {
-  constexpr int R = D / 16;
-  __shared__ float hs[D * 16];
-  constexpr int MS = D + 4;  // row stride of M in LDS (16-byte aligned rows, staggered banks)
-  __shared__ __align__(16) float ms[D * MS];
+  constexpr int NT = D / 16;     // output tiles of the slab
+  static_assert(NT % 4 == 0, "the four waves take the same number of tiles");
+  constexpr int TPW = NT / 4;    // tiles per wave: wave w takes tiles w, w + 4, ...
+  constexpr int LD = D + 4;      // padded LDS stride (floats)
+  constexpr int NV = D * D / 4 / 256;  // float4 of M per thread and step
+  __shared__ __align__(16) float ms[D * LD];   // M[row][k]
+  __shared__ __align__(16) float hsT[16 * LD];  // h[k][col] stored as [col][k]
   const int nh = blockIdx.x, slab = blockIdx.y;
   const int n = nh / H, h = nh - n * H;
-  const int tid = threadIdx.x, c = tid % 16, rg = tid / 16;
-  const int col = 16 * slab + c;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lc = lane & 15, lg = lane >> 4;
+  const int col = 16 * slab + lc;
   const long DD = (long)D * D;
-  float acc[R];
+  const long hbase = ((long)n * H + h) * DD;
+  auto seg_off = [&](int s) { return (((long)n * S + s) * H + h) * DD; };
+  auto row_of = [&](int u, int i) { return 16 * (wave + 4 * u) + 4 * lg + i; };
+
+  f32x4 acc[TPW];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    acc[r] = h0 ? h0[((long)n * H + h) * DD + (long)(rg * R + r) * D + col] : 0.f;
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[u][i] = h0 ? h0[hbase + (long)row_of(u, i) * D + col] : 0.f;
+
+  // step s + 1's M and b are loaded while step s is composed
+  float4 mreg[NV];
+  f32x4 breg[TPW];
+  auto prefetch = [&](int s) {
+    const long off = seg_off(s);
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      mreg[v] = *reinterpret_cast<const float4*>(&M[off + 4 * (tid + 256 * v)]);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) breg[u][i] = b[off + (long)row_of(u, i) * D + col];
+  };
+  if (S > 0) prefetch(0);
   for (int s = 0; s < S; ++s) {
-    const long off = (((long)n * S + s) * H + h) * DD;
+    const long off = seg_off(s);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = rg * R + r;
-      h_in[off + (long)row * D + col] = acc[r];
-      hs[row * 16 + c] = acc[r];
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h_in[off + (long)row_of(u, i) * D + col] = acc[u][i];
+      *reinterpret_cast<f32x4*>(&hsT[lc * LD + 16 * (wave + 4 * u) + 4 * lg]) = acc[u];
+      acc[u] = breg[u];
     }
-    for (int i = 4 * tid; i < D * D; i += 4 * 256)
-      *reinterpret_cast<float4*>(&ms[(i / D) * MS + i % D]) =
-          *reinterpret_cast<const float4*>(&M[off + i]);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int i = 4 * (tid + 256 * v);
+      *reinterpret_cast<float4*>(&ms[(i / D) * LD + i % D]) = mreg[v];
+    }
     __syncthreads();
+    if (s + 1 < S) prefetch(s + 1);
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(&hsT[lc * LD + k0 + 4 * lg]);
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = b[off + (long)(rg * R + r) * D + col];
-    for (int k = 0; k < D; k += 4) {
-      float x[4];
+      for (int u = 0; u < TPW; ++u) {
+        const f32x4 av =
+            *reinterpret_cast<const f32x4*>(&ms[(16 * (wave + 4 * u) + lc) * LD + k0 + 4 * lg]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = hs[(k + u) * 16 + c];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float4 mv = *reinterpret_cast<const float4*>(&ms[(rg * R + r) * MS + k]);
-        acc[r] = fmaf(mv.x, x[0], acc[r]);
-        acc[r] = fmaf(mv.y, x[1], acc[r]);
-        acc[r] = fmaf(mv.z, x[2], acc[r]);
-        acc[r] = fmaf(mv.w, x[3], acc[r]);
+        for (int j = 0; j < 4; ++j)
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[u], 0, 0, 0);
       }
     }
-    __syncthreads();  // hs and ms are rewritten by the next step
+    __syncthreads();  // hsT and ms are rewritten by the next step
   }
-  if (ht)
+  if (ht) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) ht[((long)n * H + h) * DD + (long)(rg * R + r) * D + col] = acc[r];
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ht[hbase + (long)row_of(u, i) * D + col] = acc[u][i];
+  }
 }
 
 }  // namespace

@@ -117,6 +117,18 @@ def test_auto_takes_recurrent_for_few_tokens_per_sequence(lib):
     assert ws_status(desc(T=8)) == (0, 0)
 
 
+def test_auto_segments_from_four_segments_of_512_tokens(lib):
+    """One sequence, 32 heads: 8 segments wanted (256 pairs); AUTO segments when they are at
+    least 512 tokens long and the workspace is there (host-only, fake aligned address)."""
+    for T, expect in ((2048, "fused"), (4096, "segmented"), (65536, "segmented")):
+        d = desc(B=1, N=1, T=T, H=32, Hg=16)
+        need = gdn.gdn_chunk_fwd_workspace_size(d)
+        if expect == "fused":
+            assert need == 0
+        d.workspace, d.workspace_bytes = 0x10000, need
+        assert gdn.gdn_resolved_variant(d) == expect, T
+
+
 def test_staged_layout_is_aligned_and_disjoint(lib):
     d = desc(variant=1, B=3, T=1000, N=3, H=6, Hg=3, Dk=64, Dv=64, chunk=64)
     total = gdn.gdn_chunk_fwd_workspace_size(d)
