@@ -17,6 +17,8 @@ Contents
   variant and is itself pinned to ``recurrence``.
 * ``conv1d`` — the causal depthwise convolution with its decode state that precedes the
   gated delta rule (the Qwen3.5-on-Ascend page's causal_conv1d), in fp64 numpy.
+* ``backward`` — gradients of the forward recurrence (reverse pass through the token
+  steps, fp64 numpy), pinned by finite differences of ``recurrence``.
 
 Every function here follows its cited passage; none is blocked, fused or reordered beyond
 what that passage states.

@@ -478,3 +478,80 @@ def test_conv1d_packed_equals_per_sequence_runs():
     close(st[1], st0[1], 0)  # an unused line is untouched
     close(st[4], st0[4], 0)
     close(st[0], st0[0], 0)  # the empty sequence leaves its line as it was
+
+
+# ------------------------------------------------------------------ backward oracle
+from oracle import backward as bw  # noqa: E402
+
+
+def _loss_and_grads(case, scale, cu=None, seed=0):
+    """A random linear loss L = <Wo, o> + <Wh, ht> of the C forward oracle, its analytic
+    gradients from oracle.backward, and a central finite-difference check of each."""
+    q, k, v, g, beta, h0 = case
+    rng = np.random.default_rng(seed)
+    o, ht = oracle.recurrence(q, k, v, g, beta, h0, scale=scale, cu_seqlens=cu)
+    Wo, Wh = rng.standard_normal(o.shape), rng.standard_normal(ht.shape)
+
+    def loss(q_, k_, v_, g_, b_, h_):
+        o_, ht_ = oracle.recurrence(q_, k_, v_, g_, b_, h_, scale=scale, cu_seqlens=cu)
+        return float(np.sum(Wo * o_) + np.sum(Wh * ht_))
+
+    grads = bw.recurrence_backward(q, k, v, g, beta, h0, scale, Wo, Wh, cu_seqlens=cu)
+    inputs = [q, k, v, g, beta, h0]
+    eps = 1e-6
+    for which, (x, dx) in enumerate(zip(inputs, grads)):
+        if x is None:
+            continue
+        flat = x.reshape(-1)
+        idx = rng.choice(flat.size, size=min(flat.size, 12), replace=False)
+        for i in idx:
+            keep = flat[i]
+            flat[i] = keep + eps
+            lp = loss(*inputs)
+            flat[i] = keep - eps
+            lm = loss(*inputs)
+            flat[i] = keep
+            fd = (lp - lm) / (2 * eps)
+            an = dx.reshape(-1)[i]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (which, int(i), fd, an)
+    return grads
+
+
+@pytest.mark.parametrize("H,Hg", [(2, 2), (4, 2)])
+def test_backward_matches_finite_differences(H, Hg):
+    """Every input's gradient (q, k, v, g, beta, h0; GQA groups summing dq and dk) against
+    central differences of the forward oracle."""
+    case = rand_case(81 + H, B=2, T=9, H=H, Hg=Hg, Dk=4, Dv=3)
+    _loss_and_grads(case, scale=0.7, seed=H)
+
+
+def test_backward_packed_batch_matches_finite_differences():
+    case = rand_case(85, B=1, T=11, H=2, Dk=3, Dv=4, h0=False)
+    q, k, v, g, beta, _ = case
+    cu = np.array([0, 4, 4, 11])
+    h0 = 0.1 * np.random.default_rng(3).standard_normal((3, 2, 3, 4))
+    grads = _loss_and_grads((q, k, v, g, beta, h0), scale=0.5, cu=cu, seed=9)
+    # the empty sequence passes the ht gradient straight to h0
+    _, _, _, _, _, dh0 = grads
+    rng = np.random.default_rng(9)
+    o, ht = oracle.recurrence(q, k, v, g, beta, h0, scale=0.5, cu_seqlens=cu)
+    rng.standard_normal(o.shape)
+    Wh = rng.standard_normal(ht.shape)
+    close(dh0[1], Wh[1], 0)
+
+
+def test_backward_planted_sign_error_is_caught():
+    """A wrong sign in the decay gradient makes the finite-difference check fail."""
+    case = rand_case(87, B=1, T=6, H=1, Dk=3, Dv=3)
+    orig = bw._pair_backward
+
+    def planted(*a):
+        dq, dk, dv, dg, db, dH = orig(*a)
+        return dq, dk, dv, -dg, db, dH
+
+    bw._pair_backward = planted
+    try:
+        with pytest.raises(AssertionError):
+            _loss_and_grads(case, scale=1.0, seed=1)
+    finally:
+        bw._pair_backward = orig
