@@ -210,7 +210,8 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
   gdn::Problem p;
   gdn_status s = check_desc(d, &p);
   if (s != GDN_OK) return s;
-  if (!q || !k || !v || !g || !beta || !o) return GDN_ERR_INVALID_ARG;
+  // an empty token axis needs no token buffers (torch hands out null pointers for them)
+  if (p.Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(g, 4) || !aligned(beta, p.beta_f32 ? 4 : 2) || !aligned(h0, 16) ||
       !aligned(ht, 16) || !aligned(cu_seqlens, 4))
@@ -237,6 +238,14 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
   if (p.N == 0) return GDN_OK;
 
   hipError_t e;
+  if (p.Ttot == 0) {
+    // no tokens: every sequence is empty and its state passes through (ht = h0, or zeros);
+    // the recurrent kernel does exactly that without touching a token buffer
+    if (d->stop_after != 0 || !ht) return GDN_OK;
+    if ((long long)p.N * p.H * (p.D / 32) >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
+    e = gdn::launch_recurrent(p, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
   if (variant == GDN_VARIANT_FUSED) {
     e = gdn::launch_fused(p, stream);
   } else if (variant == GDN_VARIANT_RECURRENT) {

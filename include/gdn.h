@@ -167,8 +167,9 @@ size_t gdn_chunk_fwd_workspace_size(const gdn_desc* d, gdn_status* status);
  * cu_seqlens is used; host-only, no device work. */
 int32_t gdn_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens);
 
-/* The forward pass.  q, k, v, g, beta, o are required; h0 (zero state), cu_seqlens (dense
- * batch) and ht (final state not written) may be NULL.  scale multiplies o (Dk^-0.5 is the
+/* The forward pass.  q, k, v, g, beta, o are required unless B*T = 0 (then every sequence
+ * is empty: ht = h0, or zeros, and nothing else is touched, whatever the variant); h0 (zero
+ * state), cu_seqlens (dense batch) and ht (final state not written) may be NULL.  scale multiplies o (Dk^-0.5 is the
  * usual choice).  Pointers must be device pointers aligned to 16 bytes (g, beta, cu_seqlens:
  * 4 / 2 / 4 bytes).  With stop_after = k > 0 (staged only) o and ht are not written. */
 gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const void* v,

@@ -280,7 +280,7 @@ def test_bf16_qkv_with_fp32_beta(variant, C):
     log(test="fp32_beta", variant=variant, C=C, o_rel=eo, ht_rel=eh)
 
 
-@pytest.mark.parametrize("variant", ["staged", "fused"])
+@pytest.mark.parametrize("variant", ["staged", "fused", "recurrent"])
 @pytest.mark.parametrize("regime", ["strong_decay", "no_decay_full_beta"])
 def test_gate_extremes(variant, regime):
     """Strong decay (g about -5 per token: e^G underflows to zero inside a chunk, and the
@@ -446,3 +446,27 @@ def test_auto_takes_recurrent_for_decode_shapes():
     check_against_oracle(inp, o, ht, o_ref, ht_ref, "auto decode")
     o_r, ht_r = run_gdn(inp, variant="recurrent")
     assert torch.equal(o, o_r) and torch.equal(ht, ht_r)
+
+
+@pytest.mark.parametrize("variant", ["auto", "staged", "fused", "recurrent", "segmented"])
+@pytest.mark.parametrize("packed", [False, True])
+def test_empty_token_axis(variant, packed):
+    """No tokens at all (a dense batch with T = 0, or a packed batch of empty sequences):
+    every state passes through bit for bit, or is zero without h0, in every variant."""
+    from gated_deltanet_chunked_02_amd import chunk_gated_delta_rule
+    dev = torch.device("cuda")
+    B, N, H, D = (1, 3, 2, 64) if packed else (2, 2, 2, 64)
+    q = torch.empty(B, 0, H, D, dtype=torch.bfloat16, device=dev)
+    g = torch.empty(B, 0, H, dtype=torch.float32, device=dev)
+    beta = torch.empty(B, 0, H, dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(N + 1, dtype=torch.int32, device=dev) if packed else None
+    h0 = torch.randn(N, H, D, D, generator=torch.Generator().manual_seed(61)).to(dev)
+    if variant == "segmented" and packed:
+        pytest.skip("the segmented variant takes dense batches only")
+    o, ht = chunk_gated_delta_rule(q, q, q, g, beta, initial_state=h0, cu_seqlens=cu,
+                                   chunk_size=64, variant=variant)
+    o2, ht2 = chunk_gated_delta_rule(q, q, q, g, beta, cu_seqlens=cu, chunk_size=64,
+                                     variant=variant)
+    torch.cuda.synchronize()
+    assert o.shape == (B, 0, H, D) and torch.equal(ht, h0)
+    assert torch.equal(ht2, torch.zeros_like(ht2))
