@@ -5,6 +5,7 @@
 
 #include "gdn.h"
 #include "gdn_internal.h"
+#include "segment.h"
 
 namespace {
 
@@ -55,10 +56,14 @@ gdn_status check_desc(const gdn_desc* d, gdn::Problem* p) {
   return GDN_OK;
 }
 
-// Segments of the segmented variant: S segments of Ls tokens (a multiple of the fused
-// kernel's 64-token chunk; the last may be shorter) per sequence of a dense batch.
+// Segments of the segmented variant: segments of Ls tokens (a multiple of the fused kernel's
+// 64-token chunk; the last of a sequence may be shorter).  A dense batch has S per sequence
+// (nseg = N S); a packed batch has ceil(len / Ls) per sequence, at most nseg in total.
 struct SegPlan {
+  bool use = false;  // AUTO: segmenting pays off (a forced request always segments)
+  bool packed = false;
   int S = 1, Ls = 0;
+  long nseg = 0;
 };
 
 constexpr int kFusedChunk = 64;
@@ -66,8 +71,28 @@ constexpr int kTargetPairs = 256;    // (segment, head) pairs that fill the GPU:
 constexpr int kAutoMinSegments = 4;  // AUTO segments only when it gives at least 4 segments
 constexpr int kAutoMinSegLen = 512;  // of at least 512 tokens (three passes over the data)
 
-SegPlan seg_plan(const gdn::Problem& p, bool forced) {
+SegPlan seg_plan_packed(const gdn::Problem& p, bool forced) {
+  // about kTargetPairs (segment, head) pairs over the whole token axis
   SegPlan sp;
+  sp.packed = true;
+  const long pairs = (long)p.N * p.H;
+  long Ls = ((long)p.Ttot * p.H + kTargetPairs - 1) / kTargetPairs;
+  Ls = (Ls + kFusedChunk - 1) / kFusedChunk * kFusedChunk;
+  if (Ls < kFusedChunk) Ls = kFusedChunk;
+  sp.Ls = (int)Ls;
+  sp.nseg = ((long)p.Ttot + Ls - 1) / Ls + p.N;
+  // AUTO: the sequences do not fill the GPU, and they average at least kAutoMinSegments
+  // segments of at least kAutoMinSegLen tokens
+  sp.use = forced || (pairs < kTargetPairs && Ls >= kAutoMinSegLen &&
+                      (long)p.Ttot >= (long)kAutoMinSegments * p.N * Ls);
+  return sp;
+}
+
+SegPlan seg_plan(const gdn::Problem& p, bool forced, bool dense) {
+  if (!dense) return seg_plan_packed(p, forced);
+  SegPlan sp;
+  sp.use = forced;
+  sp.nseg = p.N;
   const long pairs = (long)p.N * p.H;
   if (pairs <= 0 || p.T <= 0) return sp;
   const long want = (kTargetPairs + pairs - 1) / pairs;
@@ -78,32 +103,35 @@ SegPlan seg_plan(const gdn::Problem& p, bool forced) {
   Ls = (Ls + kFusedChunk - 1) / kFusedChunk * kFusedChunk;
   S = (p.T + Ls - 1) / Ls;
   if (!forced && (S < kAutoMinSegments || Ls < kAutoMinSegLen)) return sp;
+  sp.use = true;
   sp.S = (int)S;
   sp.Ls = (int)Ls;
+  sp.nseg = (long)p.N * S;
   return sp;
 }
 
-// Workspace of the segmented variant: the segment table, then b, M and h_in per
-// (segment, head), each [N S, H, D, D] fp32.
+// Workspace of the segmented variant: the segment table [nseg + 1], each sequence's first
+// segment [N + 1], then b, M and h_in per (segment, head), each [nseg, H, D, D] fp32.
 struct SegLayout {
-  size_t cu, b, M, h_in, total;
+  size_t cu, first, b, M, h_in, total;
 };
 
 SegLayout seg_layout(const gdn::Problem& p, const SegPlan& sp) {
   SegLayout L;
-  const size_t ns = (size_t)p.N * sp.S;
+  const size_t ns = (size_t)sp.nseg;
   const size_t st = ns * p.H * (size_t)p.D * p.D * sizeof(float);
   L.cu = 0;
-  L.b = align_up((ns + 1) * sizeof(int32_t));
+  L.first = align_up((ns + 1) * sizeof(int32_t));
+  L.b = L.first + align_up(((size_t)p.N + 1) * sizeof(int32_t));
   L.M = L.b + align_up(st);
   L.h_in = L.M + align_up(st);
   L.total = L.h_in + align_up(st);
   return L;
 }
 
-bool seg_ok(const gdn::Problem& p, const gdn_desc* d, bool dense) {
-  return dense && gdn::fused_supported(p) && p.D <= 128 && d->stop_after == 0 &&
-         (long long)p.N * p.T <= (1LL << 30);
+bool seg_ok(const gdn::Problem& p, const gdn_desc* d) {
+  return gdn::fused_supported(p) && p.D <= 128 && d->stop_after == 0 &&
+         (long long)p.Ttot + p.N <= (1LL << 30);
 }
 
 // The staged kernels stage fp32 operands of at most 8192 elements per chunk row block in LDS.
@@ -130,14 +158,14 @@ int resolve_variant(const gdn_desc* d, const gdn::Problem& p, bool dense, bool w
   switch (d->variant) {
     case GDN_VARIANT_FUSED: return fused_ok ? GDN_VARIANT_FUSED : -1;
     case GDN_VARIANT_STAGED: return staged_ok(p) ? GDN_VARIANT_STAGED : -1;
-    case GDN_VARIANT_SEGMENTED: return seg_ok(p, d, dense) ? GDN_VARIANT_SEGMENTED : -1;
+    case GDN_VARIANT_SEGMENTED: return seg_ok(p, d) ? GDN_VARIANT_SEGMENTED : -1;
     case GDN_VARIANT_RECURRENT: return recurrent_ok(p, d) ? GDN_VARIANT_RECURRENT : -1;
     default: {
       if (recurrent_ok(p, d) && recurrent_pays(p, dense)) return GDN_VARIANT_RECURRENT;
       if (!fused_ok) return staged_ok(p) ? GDN_VARIANT_STAGED : -1;
-      if (seg_ok(p, d, dense) && seg_plan(p, false).S > 1) {
+      if (seg_ok(p, d) && seg_plan(p, false, dense).use) {
         if (!ws_check) return GDN_VARIANT_SEGMENTED;
-        const size_t need = seg_layout(p, seg_plan(p, false)).total;
+        const size_t need = seg_layout(p, seg_plan(p, false, dense)).total;
         if (d->workspace && d->workspace_bytes >= need && aligned(d->workspace, kAlign))
           return GDN_VARIANT_SEGMENTED;
       }
@@ -170,6 +198,17 @@ void staged_layout(const gdn::Problem& p, Layout* L) {
   L->total = off;
 }
 
+// Workspace of the variant a call resolves to, for one reading of the descriptor.
+size_t workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
+  const int v = resolve_variant(d, p, dense, false);
+  if (v == GDN_VARIANT_FUSED || v == GDN_VARIANT_RECURRENT || v < 0) return 0;
+  if (v == GDN_VARIANT_SEGMENTED)
+    return seg_layout(p, seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED, dense)).total;
+  Layout L;
+  staged_layout(p, &L);
+  return L.total;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,18 +216,20 @@ extern "C" {
 size_t gdn_chunk_fwd_workspace_size(const gdn_desc* d, gdn_status* status) {
   gdn::Problem p;
   gdn_status s = check_desc(d, &p);
-  // the size query cannot see cu_seqlens: N other than 0 or B marks a packed batch
+  // the size query cannot see cu_seqlens: N other than 0 or B marks a packed batch, and
+  // with B = 1 both readings are possible, so the larger need is reported
   const bool dense = d && (d->N == 0 || d->N == d->B);
   if (s == GDN_OK && resolve_variant(d, p, dense, false) < 0) s = GDN_ERR_UNSUPPORTED;
   if (status) *status = s;
   if (s != GDN_OK) return 0;
-  const int v = resolve_variant(d, p, dense, false);
-  if (v == GDN_VARIANT_FUSED || v == GDN_VARIANT_RECURRENT) return 0;
-  if (v == GDN_VARIANT_SEGMENTED)
-    return seg_layout(p, seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED)).total;
-  Layout L;
-  staged_layout(p, &L);
-  return L.total;
+  size_t need = workspace_for(d, p, dense);
+  if (dense && d->B == 1) {
+    gdn::Problem pp = p;
+    pp.N = d->N == 0 ? 1 : d->N;
+    const size_t packed = workspace_for(d, pp, false);
+    if (packed > need) need = packed;
+  }
+  return need;
 }
 
 gdn_status gdn_stage_buffer(const gdn_desc* d, int32_t buf, size_t* offset, size_t* bytes) {
@@ -251,20 +292,24 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
   } else if (variant == GDN_VARIANT_RECURRENT) {
     e = gdn::launch_recurrent(p, stream);
   } else if (variant == GDN_VARIANT_SEGMENTED) {
-    const SegPlan sp = seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED);
+    const bool dense = cu_seqlens == nullptr;
+    const SegPlan sp = seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED, dense);
     const SegLayout L = seg_layout(p, sp);
     if (!d->workspace || d->workspace_bytes < L.total || !aligned(d->workspace, kAlign))
       return GDN_ERR_WORKSPACE;
     char* ws = static_cast<char*>(d->workspace);
     int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + L.cu);
+    int32_t* seg_first = reinterpret_cast<int32_t*>(ws + L.first);
     float* bm = reinterpret_cast<float*>(ws + L.b);
     float* mm = reinterpret_cast<float*>(ws + L.M);
     float* hin = reinterpret_cast<float*>(ws + L.h_in);
     // every segment is a sequence of a packed batch over the same tokens
     gdn::Problem ps = p;
-    ps.N = p.N * sp.S;
+    ps.N = (int)sp.nseg;
     ps.cu = cu_seg;
-    e = gdn::launch_segment_table(cu_seg, p.N, p.T, sp.S, sp.Ls, stream);
+    e = dense ? gdn::launch_segment_table(cu_seg, p.N, p.T, sp.S, sp.Ls, stream)
+              : gdn::launch_segment_table_packed(p.cu, cu_seg, seg_first, p.N, p.Ttot, sp.Ls,
+                                                 (int)sp.nseg, stream);
     // b: each segment from a zero state; M: from the identity with v taken as zero
     if (e == hipSuccess) {
       gdn::Problem pb = ps;
@@ -282,7 +327,8 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
     }
     // h_in of every segment, and the final state, by composing the maps in order
     if (e == hipSuccess)
-      e = gdn::launch_segment_scan(mm, bm, p.h0, hin, p.ht, p.N, sp.S, p.H, p.D, stream);
+      e = gdn::launch_segment_scan_ranges(mm, bm, p.h0, hin, p.ht, dense ? nullptr : seg_first,
+                                          p.N, sp.S, p.H, p.D, stream);
     // o of every segment from its true initial state
     if (e == hipSuccess) {
       gdn::Problem po = ps;

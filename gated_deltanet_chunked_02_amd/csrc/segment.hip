@@ -11,6 +11,7 @@
 // segments, started from their true h_in, writes o.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "segment.h"
 
 namespace gdn {
 
@@ -40,12 +41,53 @@ __global__ void k_segment_table(int32_t* cu_seg, int N, int T, int S, int Ls) {
 // column: matrix-core instruction j of a 16-wide k block takes k = k0 + 4 (l / 16) + j in
 // lane l for both operands (any assignment of k to slots works as long as A and B agree).
 // Step s + 1's M and b are loaded into registers while step s is composed.
+// One workgroup of 256 threads: thread i counts the segments of a contiguous run of
+// sequences, a scan over the 256 partial sums gives every sequence's first segment, and
+// each thread then writes its sequences' segment starts.
+__global__ __launch_bounds__(256) void k_segment_table_packed(const int32_t* __restrict__ cu,
+                                                              int32_t* __restrict__ cu_seg,
+                                                              int32_t* __restrict__ seg_first,
+                                                              int N, int Ttot, int Ls,
+                                                              int nseg) {
+  __shared__ int part[257];
+  const int tid = threadIdx.x;
+  const int per = (N + 255) / 256;
+  const int n0 = min(tid * per, N), n1 = min(n0 + per, N);
+  auto bound = [&](int i) { return min(max(cu[i], 0), Ttot); };
+  int cnt = 0;
+  for (int n = n0; n < n1; ++n) {
+    const int bos = bound(n), eos = max(bound(n + 1), bos);
+    cnt += (eos - bos + Ls - 1) / Ls;
+  }
+  part[tid + 1] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    part[0] = 0;
+    for (int i = 1; i <= 256; ++i) part[i] += part[i - 1];
+  }
+  __syncthreads();
+  // every index is clamped to the planned nseg segments: a well-formed cu never reaches it,
+  // a non-monotone one (unspecified results) must not write past the table either
+  int first = min(part[tid], nseg);
+  for (int n = n0; n < n1; ++n) {
+    const int bos = bound(n), eos = max(bound(n + 1), bos);
+    seg_first[n] = first;
+    for (int t = bos; t < eos && first < nseg; t += Ls) cu_seg[first++] = t;
+  }
+  const int total = min(part[256], nseg);
+  const int end = N > 0 ? max(bound(N), bound(0)) : 0;
+  if (tid == 0) seg_first[N] = total;
+  for (int i = total + tid; i <= nseg; i += 256) cu_seg[i] = end;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ M,
                                                       const float* __restrict__ b,
                                                       const float* __restrict__ h0,
                                                       float* __restrict__ h_in,
-                                                      float* __restrict__ ht, int S, int H) {
+                                                      float* __restrict__ ht,
+                                                      const int32_t* __restrict__ seg_first,
+                                                      int S, int H) {
   constexpr int NT = D / 16;     // output tiles of the slab
   static_assert(NT % 4 == 0, "the four waves take the same number of tiles");
   constexpr int TPW = NT / 4;    // tiles per wave: wave w takes tiles w, w + 4, ...
@@ -60,7 +102,9 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
   const int col = 16 * slab + lc;
   const long DD = (long)D * D;
   const long hbase = ((long)n * H + h) * DD;
-  auto seg_off = [&](int s) { return (((long)n * S + s) * H + h) * DD; };
+  const int s0 = seg_first ? seg_first[n] : n * S;
+  const int ns = seg_first ? seg_first[n + 1] - s0 : S;  // this sequence's segments
+  auto seg_off = [&](int s) { return (((long)s0 + s) * H + h) * DD; };
   auto row_of = [&](int u, int i) { return 16 * (wave + 4 * u) + 4 * lg + i; };
 
   f32x4 acc[TPW];
@@ -82,8 +126,8 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) breg[u][i] = b[off + (long)row_of(u, i) * D + col];
   };
-  if (S > 0) prefetch(0);
-  for (int s = 0; s < S; ++s) {
+  if (ns > 0) prefetch(0);
+  for (int s = 0; s < ns; ++s) {
     const long off = seg_off(s);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -98,7 +142,7 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
       *reinterpret_cast<float4*>(&ms[(i / D) * LD + i % D]) = mreg[v];
     }
     __syncthreads();
-    if (s + 1 < S) prefetch(s + 1);
+    if (s + 1 < ns) prefetch(s + 1);
 #pragma unroll 4
     for (int k0 = 0; k0 < D; k0 += 16) {
       const f32x4 bv = *reinterpret_cast<const f32x4*>(&hsT[lc * LD + k0 + 4 * lg]);
@@ -129,14 +173,26 @@ hipError_t launch_segment_table(int32_t* cu_seg, int N, int T, int S, int Ls, hi
   return hipGetLastError();
 }
 
-hipError_t launch_segment_scan(const float* M, const float* b, const float* h0, float* h_in,
-                               float* ht, int N, int S, int H, int D, hipStream_t st) {
+hipError_t launch_segment_scan_ranges(const float* M, const float* b, const float* h0,
+                                      float* h_in, float* ht, const int32_t* seg_first, int N,
+                                      int S, int H, int D, hipStream_t st) {
   if (N * H == 0) return hipSuccess;
   const dim3 grid(N * H, D / 16);
   if (D == 64)
-    k_segment_scan<64><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, S, H);
+    k_segment_scan<64><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, seg_first, S, H);
   else
-    k_segment_scan<128><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, S, H);
+    k_segment_scan<128><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, seg_first, S, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_scan(const float* M, const float* b, const float* h0, float* h_in,
+                               float* ht, int N, int S, int H, int D, hipStream_t st) {
+  return launch_segment_scan_ranges(M, b, h0, h_in, ht, nullptr, N, S, H, D, st);
+}
+
+hipError_t launch_segment_table_packed(const int32_t* cu, int32_t* cu_seg, int32_t* seg_first,
+                                       int N, int Ttot, int Ls, int nseg, hipStream_t st) {
+  k_segment_table_packed<<<1, 256, 0, st>>>(cu, cu_seg, seg_first, N, Ttot, Ls, nseg);
   return hipGetLastError();
 }
 

@@ -58,19 +58,21 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 typedef enum gdn_variant {
   GDN_VARIANT_AUTO = 0,      /* recurrent for a few tokens per sequence (dense: T <= 8;
                                 packed: B*T <= 8 N); else fused when built for the shape,
-                                otherwise staged; segmented for a dense batch of few long
-                                sequences when the workspace for it is given (fused
-                                otherwise)                                                 */
+                                otherwise staged; segmented for a batch of few long
+                                sequences (dense or packed) when the workspace for it is
+                                given (fused otherwise)                                    */
   GDN_VARIANT_STAGED = 1,    /* seven launches, intermediates in the workspace */
   GDN_VARIANT_FUSED = 2,     /* one launch, one workgroup per (sequence, head) */
-  GDN_VARIANT_SEGMENTED = 3, /* dense batches only: every sequence split into S segments that
-                                run in parallel.  The state recurrence is affine in the
-                                initial state, h_end = M h_in + b; the fused kernel finds M
-                                (from h_in = I, v = 0) and b (from h_in = 0) of every segment,
-                                a scan composes h_in(s+1) = M_s h_in(s) + b_s (fp32), and a
-                                last fused pass writes o.  Three passes over the data, S-fold
-                                parallelism (the long-prompt case of the FlashQLA how-to,
-                                section 8.3).  Needs the workspace reported for it.        */
+  GDN_VARIANT_SEGMENTED = 3, /* every sequence split into segments that run in parallel
+                                (dense: S per sequence; packed: ceil(len / Ls) per sequence,
+                                the table built on the device).  The state recurrence is
+                                affine in the initial state, h_end = M h_in + b; the fused
+                                kernel finds M (from h_in = I, v = 0) and b (from h_in = 0)
+                                of every segment, a scan composes h_in(s+1) = M_s h_in(s) +
+                                b_s (fp32), and a last fused pass writes o.  Three passes over
+                                the data, many-fold parallelism (the long-prompt case of the
+                                FlashQLA how-to, section 8.3).  Needs the workspace reported
+                                for it.                                                    */
   GDN_VARIANT_RECURRENT = 4  /* token by token, the state kept in registers: one read and one
                                 write of each (sequence, head) state per call, whatever the
                                 number of tokens, and one dependent step per token.  For
@@ -158,7 +160,8 @@ gdn_status gdn_causal_conv1d_fwd(const gdn_conv_desc* d, const void* x, const fl
 
 /* Bytes of workspace the variant chosen by d->variant needs (0 for the fused variant; for
  * AUTO, what AUTO picks when given that much).  The query cannot see cu_seqlens: a
- * descriptor with N == 0 or N == B is taken as a dense batch.  Host-only, no device work.
+ * descriptor with N other than 0 or B is a packed batch, one with B == 1 may be either and
+ * gets the larger of the two needs, any other is a dense batch.  Host-only, no device work.
  * Returns 0 and sets *status on an invalid descriptor. */
 size_t gdn_chunk_fwd_workspace_size(const gdn_desc* d, gdn_status* status);
 

@@ -74,7 +74,7 @@ def ws_status(d):
     (dict(variant=3), 0),
     (dict(variant=3, Dk=256, Dv=256), 2),
     (dict(variant=3, N=1, B=1), 0),
-    (dict(variant=3, B=1, N=3), 2),
+    (dict(variant=3, B=1, N=3), 0),      # packed batches segment too
     (dict(variant=3, stop_after=3), 2),
     (dict(variant=2, stop_after=3), 2),
     (dict(variant=4), 0),
@@ -127,6 +127,24 @@ def test_auto_segments_from_four_segments_of_512_tokens(lib):
             assert need == 0
         d.workspace, d.workspace_bytes = 0x10000, need
         assert gdn.gdn_resolved_variant(d) == expect, T
+
+
+def test_packed_batches_segment_when_few_long_sequences(lib):
+    A = 0x10000  # only the nullness of cu_seqlens is read; fake aligned workspace
+    # one packed 65536-token sequence over 32 heads: segments of 8192 tokens
+    d = desc(B=1, N=1, T=65536, H=32, Hg=16)
+    need = gdn.gdn_chunk_fwd_workspace_size(d)  # covers the dense and the packed reading
+    d.workspace, d.workspace_bytes = A, need
+    assert gdn.gdn_resolved_variant(d, A) == "segmented"
+    assert gdn.gdn_resolved_variant(d) == "segmented"
+    # 64 packed sequences already give 2048 pairs: fused
+    d2 = desc(B=1, N=64, T=65536, H=32, Hg=16)
+    d2.workspace, d2.workspace_bytes = A, 1 << 40
+    assert gdn.gdn_resolved_variant(d2, A) == "fused"
+    # a few sequences averaging under four 512-token segments each: fused
+    d3 = desc(B=1, N=4, T=4096, H=32, Hg=16)
+    d3.workspace, d3.workspace_bytes = A, 1 << 40
+    assert gdn.gdn_resolved_variant(d3, A) == "fused"
 
 
 def test_staged_layout_is_aligned_and_disjoint(lib):

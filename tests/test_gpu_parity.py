@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import gdn_inputs
-from gdn_testlib import (check_against_oracle, max_abs, oracle_full, rel_l2, run_gdn, to64)
+from gdn_testlib import (check_against_oracle, max_abs, oracle_full, oracle_pairs, pair_slices,
+                         rel_l2, run_gdn, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -342,7 +343,7 @@ def test_segmented_strong_decay_and_no_final_state():
 
 def test_segmented_resolution():
     """AUTO picks the segmented variant for a few long sequences when the workspace is there
-    (and the fused one without it); packed batches never segment."""
+    (and the fused one without it), dense or packed."""
     import gated_deltanet_chunked_02_amd as gdn
     dev = torch.device("cuda")
     q = torch.zeros(1, 65536, 16, 128, dtype=torch.bfloat16, device=dev)
@@ -356,7 +357,7 @@ def test_segmented_resolution():
     desc.workspace, desc.workspace_bytes = buf.data_ptr(), ws
     assert gdn.gdn_resolved_variant(desc) == "segmented"
     cu = torch.tensor([0, 65536], dtype=torch.int32, device=dev)
-    assert gdn.gdn_resolved_variant(desc, cu) == "fused"
+    assert gdn.gdn_resolved_variant(desc, cu) == "segmented"  # the same prompt, packed
     # many pairs: the fused kernel already fills the GPU
     q2 = torch.zeros(16, 8192, 32, 128, dtype=torch.bfloat16, device=dev)
     v2 = torch.zeros(16, 8192, 32, 128, dtype=torch.bfloat16, device=dev)
@@ -461,8 +462,6 @@ def test_empty_token_axis(variant, packed):
     beta = torch.empty(B, 0, H, dtype=torch.bfloat16, device=dev)
     cu = torch.zeros(N + 1, dtype=torch.int32, device=dev) if packed else None
     h0 = torch.randn(N, H, D, D, generator=torch.Generator().manual_seed(61)).to(dev)
-    if variant == "segmented" and packed:
-        pytest.skip("the segmented variant takes dense batches only")
     o, ht = chunk_gated_delta_rule(q, q, q, g, beta, initial_state=h0, cu_seqlens=cu,
                                    chunk_size=64, variant=variant)
     o2, ht2 = chunk_gated_delta_rule(q, q, q, g, beta, cu_seqlens=cu, chunk_size=64,
@@ -470,3 +469,64 @@ def test_empty_token_axis(variant, packed):
     torch.cuda.synchronize()
     assert o.shape == (B, 0, H, D) and torch.equal(ht, h0)
     assert torch.equal(ht2, torch.zeros_like(ht2))
+
+
+# ------------------------------------------------------------------ segmented, packed batches
+PACKED_SEG = [
+    # D, H, Hg, lengths
+    (128, 4, 4, [300, 0, 517, 64, 1]),
+    (64, 2, 1, [200, 133]),
+]
+
+
+@pytest.mark.parametrize("D,H,Hg,lens", PACKED_SEG)
+def test_segmented_packed_matches_oracle(D, H, Hg, lens):
+    """Packed sequences cut into 64-token segments (ragged ends, an empty sequence)."""
+    w = gdn_inputs.small(H=H, Hg=Hg, Dk=D, C=64, seed=D + sum(lens), h0_std=0.05)
+    inp = gdn_inputs.draw(w.with_(B=1, T=sum(lens)), device="cpu")
+    inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    inp["h0"] = torch.randn(len(lens), H, D, D, generator=torch.Generator().manual_seed(7)) * 0.05
+    o_ref, ht_ref = oracle_full(inp)
+    o, ht = run_gdn(inp, variant="segmented")
+    eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "packed segmented D%d" % D)
+    of, htf = run_gdn(inp, variant="fused")
+    assert rel_l2(to64(o), to64(of)) <= 5e-3 and rel_l2(to64(ht), to64(htf)) <= 1e-2
+    if 0 in lens:
+        i = lens.index(0)
+        assert torch.equal(ht[i].cpu(), inp["h0"][i])
+    log(test="segmented_packed", D=D, lens=lens, o_rel=eo, ht_rel=eh)
+
+
+def test_segmented_packed_long_prompt_equals_dense():
+    """The 65536-token prompt as a packed batch of one sequence segments exactly like the
+    dense batch (same 8192-token segments): identical o and ht."""
+    w = gdn_inputs.WORKLOADS["long"]
+    inp = gdn_inputs.draw(w, device="cuda")
+    from gated_deltanet_chunked_02_amd import chunk_gated_delta_rule
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    o_d, ht_d = chunk_gated_delta_rule(*args, scale=inp["scale"], variant="segmented")
+    cu = torch.tensor([0, w.T], dtype=torch.int32, device="cuda")
+    o_p, ht_p = chunk_gated_delta_rule(*args, scale=inp["scale"], cu_seqlens=cu, variant="auto")
+    torch.cuda.synchronize()
+    assert torch.equal(o_d, o_p) and torch.equal(ht_d, ht_p)
+
+
+def test_segmented_packed_few_long_sequences_sampled():
+    """Three packed sequences (one empty) of a long prompt, forced segmented, against the
+    oracle on sampled (sequence, head) pairs."""
+    w = gdn_inputs.WORKLOADS["long"].with_(T=40000)
+    inp = gdn_inputs.draw(w, device="cuda")
+    inp["cu_seqlens"] = torch.tensor([0, 23000, 23000, 40000], dtype=torch.int32, device="cuda")
+    from gated_deltanet_chunked_02_amd import chunk_gated_delta_rule
+    o, ht = chunk_gated_delta_rule(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                   scale=inp["scale"], cu_seqlens=inp["cu_seqlens"],
+                                   variant="segmented")
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (2, 31), (0, 17), (1, 5)]
+    ref = oracle_pairs(inp, pairs, nthreads=4)
+    for (n, h), (o_ref, ht_ref) in ref.items():
+        ts, b, _ = pair_slices(inp, n, h)
+        if o_ref.size:
+            assert rel_l2(o[b, ts, h].double().cpu().numpy(), o_ref) <= 5e-3
+        assert rel_l2(ht[n, h].double().cpu().numpy(), ht_ref) <= 1e-2 or not np.any(ht_ref)
+    assert torch.equal(ht[1], torch.zeros_like(ht[1]))  # the empty sequence, no h0
