@@ -12,7 +12,7 @@
 // and afterwards the line holds the last W - 1 entries of x~.  act is the identity or SiLU.
 //
 // Two launches.  k_conv1d: one thread per 8 consecutive channels (16 bytes of bf16) and a
-// block of up to 32 consecutive tokens of the packed axis (fewer when that is needed to give
+// block of up to 64 consecutive tokens of the packed axis (fewer when that is needed to give
 // the GPU enough workgroups), walked in order with the W - 1 previous inputs in registers;
 // a wave reads 1 KiB of contiguous channels per token.  It only reads the state.
 // k_conv_state then rewrites each sequence's line (one thread per 8 channels of a line), so
@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kVec = 8;         // channels per thread
 constexpr int kThreads = 256;   // threads per workgroup: 2048 channels
-constexpr int kMaxTokens = 32;  // tokens per thread, at most (fewer when that fills the GPU)
+constexpr int kMaxTokens = 64;  // tokens per thread, at most (fewer when that fills the GPU)
 constexpr int kGroup = 8;       // tokens whose loads are issued together
 constexpr int kFillGroups = 512;  // workgroups that keep 256 CUs busy (measured on decode)
 
