@@ -167,7 +167,8 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
   constexpr int D = DK;  // row length of q, k, v and o
   constexpr float kLog2e = 1.4426950408889634f;
   const int nh = blockIdx.x / F::SPLIT, half = blockIdx.x - nh * F::SPLIT;
-  const int n = nh / H, h = nh - n * H;
+  int n = nh / H;  // for a packed batch, a rank that is mapped to a sequence below
+  const int h = nh - n * H;
   const int hk = h / (H / Hg);
   const int col0 = half * DV;  // this workgroup's first state column
   const long qstride = (long)Hg * D, vstride = (long)H * D;
@@ -188,6 +189,35 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
   __shared__ __align__(16) float SDC[3][CS];  // e^{Gc_end - Gc_t}
   __shared__ float SGE[3];                    // e^{Gc_end}
 
+  if (cu) {
+    // Packed batch: the workgroups take the sequences longest first (workgroup rank n gets
+    // the sequence of rank n by length, ties by index), so the last workgroups to start are
+    // the shortest and the batch ends with little imbalance.  The lengths are staged in the
+    // first K buffer, which the pipeline has not used yet.
+    const int N = gridDim.x / (F::SPLIT * H);
+    if (N > 1 && N <= F::TILE / 2) {
+      __shared__ int sel;
+      int* lens = reinterpret_cast<int*>(&SK[0][0]);
+      for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        int s0, l0;
+        seq_span(cu, i, T, Ttot, s0, l0);
+        lens[i] = l0;
+      }
+      __syncthreads();
+      for (int m = threadIdx.x; m < N; m += blockDim.x) {
+        const int lm = lens[m];
+        int r = 0;
+        for (int j = 0; j < N; ++j) {
+          const int lj = lens[j];
+          r += (lj > lm) || (lj == lm && j < m);
+        }
+        if (r == n) sel = m;  // the ranks are a permutation: exactly one m matches
+      }
+      __syncthreads();
+      n = sel;
+      __syncthreads();  // every wave has read sel and lens before SK is filled
+    }
+  }
   int cs0, L;
   seq_span(cu, n, T, Ttot, cs0, L);
   const int nchunks = (L + CS - 1) / CS;
