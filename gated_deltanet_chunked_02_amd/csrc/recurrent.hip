@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64) void k_recurrent(const E* __restrict__ q,
                                     scale * fmaf(e, r2, qk * u2), scale * fmaf(e, r3, qk * u3));
       Vec4<E>::store(o + v_off(t), ot);
     }
-    cur = nxt;
+    if (t + 1 < eos) cur = nxt;  // nxt was loaded only when a next token exists
   }
 
   if (ht) {
