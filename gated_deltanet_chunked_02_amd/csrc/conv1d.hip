@@ -1,5 +1,5 @@
 // Causal depthwise 1-D convolution with a decode state, the step before the gated delta
-// rule (the causal_conv1d operator of the Qwen3.5-on-Ascend page: each output depends on the
+// rule (the causal_conv1d operator of the TileLang × xLLM page: each output depends on the
 // current and earlier tokens only, a per-sequence state line carries the last inputs from
 // one call to the next, cache indices select the line, and a per-sequence flag says whether
 // a sequence starts from its line or from zeros).

@@ -1,5 +1,5 @@
 // Recurrent variant: the gated delta rule evaluated token by token, for batches with few
-// tokens per sequence (decode, where the Qwen3.5-on-Ascend page runs its fused sigmoid-gating
+// tokens per sequence (decode, where the TileLang × xLLM page runs its fused sigmoid-gating
 // delta-rule kernel once per token).  The chunked form's block work buys nothing there: each
 // (sequence, head) costs one read and one write of its Dk x Dv fp32 state whatever the
 // number of tokens, so the kernel is bound by HBM on the state and keeps it in registers

@@ -65,7 +65,7 @@ WORKLOADS = {
     "long": Workload("bf16_long_1x65536_h32_hg16_d128_c128", H=32, Hg=16, Dk=128, Dv=128,
                      C=128, dtype="bf16", seed=4, B=1, T=65536),
     # Decode: one new token for each of 256 sequences, each with a carried state
-    # (the per-token delta-rule kernel of the Qwen3.5-on-Ascend page), same head layout.
+    # (the per-token delta-rule kernel of the TileLang × xLLM page), same head layout.
     "decode": Workload("bf16_decode_256x1_h32_hg16_d128", H=32, Hg=16, Dk=128, Dv=128,
                        C=128, dtype="bf16", seed=5, B=256, T=1, h0_std=0.05),
 }

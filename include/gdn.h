@@ -77,7 +77,7 @@ typedef enum gdn_variant {
                                 write of each (sequence, head) state per call, whatever the
                                 number of tokens, and one dependent step per token.  For
                                 decode (one or a few tokens per sequence; the per-token
-                                delta-rule kernel of the Qwen3.5-on-Ascend page).  Any dtype
+                                delta-rule kernel of the TileLang × xLLM page).  Any dtype
                                 and D the header lists; no workspace; chunk is ignored.
                                 ht may be the same buffer as h0 (state updated in place).
                                 The gates arrive as g and beta, as in every variant.       */
@@ -116,7 +116,7 @@ typedef struct gdn_desc {
 } gdn_desc;
 
 /* Causal depthwise 1-D convolution with a decode state: the step before the gated delta
- * rule (the causal_conv1d operator of the Qwen3.5-on-Ascend page).  For sequence n, channel
+ * rule (the causal_conv1d operator of the TileLang × xLLM page).  For sequence n, channel
  * c and position t of the sequence, with x~ = (the W - 1 inputs before the sequence, taken
  * from the sequence's state line, or zeros) followed by the sequence's inputs,
  *

@@ -16,7 +16,7 @@ Contents
   page's order; it yields every stage intermediate for per-stage parity of the staged GPU
   variant and is itself pinned to ``recurrence``.
 * ``conv1d`` — the causal depthwise convolution with its decode state that precedes the
-  gated delta rule (the Qwen3.5-on-Ascend page's causal_conv1d), in fp64 numpy.
+  gated delta rule (the TileLang × xLLM page's causal_conv1d operator), in fp64 numpy.
 * ``backward`` — gradients of the forward recurrence (reverse pass through the token
   steps, fp64 numpy), pinned by finite differences of ``recurrence``.
 

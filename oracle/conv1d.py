@@ -1,7 +1,7 @@
 """Oracle for the causal 1-D convolution that precedes the gated delta rule — TEST
 INFRASTRUCTURE ONLY (the same import rules as the rest of ``oracle/``).
 
-The Qwen3.5-on-Ascend page (the section on its three operators, "causal_conv1d") describes
+The TileLang × xLLM page (the section on its three operators, "causal_conv1d") describes
 a causal convolution over the sequence: each output depends only on the current and the
 earlier tokens; a convolution state carries the last inputs from one call to the next for
 incremental decode; per-sequence cache indices select which state line a sequence uses;
