@@ -130,7 +130,7 @@ SegLayout seg_layout(const gdn::Problem& p, const SegPlan& sp) {
 }
 
 bool seg_ok(const gdn::Problem& p, const gdn_desc* d) {
-  return gdn::fused_supported(p) && p.D <= 128 && d->stop_after == 0 &&
+  return gdn::fused_supported(p) && d->stop_after == 0 &&
          (long long)p.Ttot + p.N <= (1LL << 30);
 }
 

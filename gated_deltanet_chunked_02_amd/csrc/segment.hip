@@ -40,7 +40,8 @@ __global__ void k_segment_table(int32_t* cu_seg, int N, int T, int S, int Ls) {
 // padded stride, so one float4 read per lane supplies four consecutive k of one row or
 // column: matrix-core instruction j of a 16-wide k block takes k = k0 + 4 (l / 16) + j in
 // lane l for both operands (any assignment of k to slots works as long as A and B agree).
-// Step s + 1's M and b are loaded into registers while step s is composed.
+// M is staged in row blocks of at most 128 rows (two for D = 256); the next row block, or
+// the next step's first one and its b, is loaded into registers while a block is composed.
 // One workgroup of 256 threads: thread i counts the segments of a contiguous run of
 // sequences, a scan over the 256 partial sums gives every sequence's first segment, and
 // each thread then writes its sequences' segment starts.
@@ -88,12 +89,15 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
                                                       float* __restrict__ ht,
                                                       const int32_t* __restrict__ seg_first,
                                                       int S, int H) {
-  constexpr int NT = D / 16;     // output tiles of the slab
-  static_assert(NT % 4 == 0, "the four waves take the same number of tiles");
-  constexpr int TPW = NT / 4;    // tiles per wave: wave w takes tiles w, w + 4, ...
-  constexpr int LD = D + 4;      // padded LDS stride (floats)
-  constexpr int NV = D * D / 4 / 256;  // float4 of M per thread and step
-  __shared__ __align__(16) float ms[D * LD];   // M[row][k]
+  constexpr int RB = D > 128 ? 128 : D;  // rows of M staged in LDS at a time
+  constexpr int NBLK = D / RB;           // row blocks per step (2 for D = 256)
+  constexpr int NTB = RB / 16;           // output tiles per row block
+  static_assert(NTB % 4 == 0, "the four waves take the same number of tiles");
+  constexpr int TPB = NTB / 4;           // tiles per wave and row block
+  constexpr int TPW = NBLK * TPB;        // tiles per wave
+  constexpr int LD = D + 4;              // padded LDS stride (floats)
+  constexpr int NV = RB * D / 4 / 256;   // float4 of a row block of M per thread
+  __shared__ __align__(16) float ms[RB * LD];   // a row block of M: [row][k]
   __shared__ __align__(16) float hsT[16 * LD];  // h[k][col] stored as [col][k]
   const int nh = blockIdx.x, slab = blockIdx.y;
   const int n = nh / H, h = nh - n * H;
@@ -105,7 +109,9 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
   const int s0 = seg_first ? seg_first[n] : n * S;
   const int ns = seg_first ? seg_first[n + 1] - s0 : S;  // this sequence's segments
   auto seg_off = [&](int s) { return (((long)s0 + s) * H + h) * DD; };
-  auto row_of = [&](int u, int i) { return 16 * (wave + 4 * u) + 4 * lg + i; };
+  // accumulator u of a wave: row block u / TPB, tile wave + 4 (u % TPB) within it
+  auto tile_of = [&](int u) { return (u / TPB) * NTB + wave + 4 * (u % TPB); };
+  auto row_of = [&](int u, int i) { return 16 * tile_of(u) + 4 * lg + i; };
 
   f32x4 acc[TPW];
 #pragma unroll
@@ -113,49 +119,65 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[u][i] = h0 ? h0[hbase + (long)row_of(u, i) * D + col] : 0.f;
 
-  // step s + 1's M and b are loaded while step s is composed
+  // the next row block of M (of this step, or the first of the next step) and the next
+  // step's b are loaded into registers while the current row block is composed
   float4 mreg[NV];
   f32x4 breg[TPW];
-  auto prefetch = [&](int s) {
-    const long off = seg_off(s);
+  auto load_block = [&](int s, int bk) {
+    const long off = seg_off(s) + (long)bk * RB * D;
 #pragma unroll
     for (int v = 0; v < NV; ++v)
       mreg[v] = *reinterpret_cast<const float4*>(&M[off + 4 * (tid + 256 * v)]);
+  };
+  auto load_b = [&](int s) {
+    const long off = seg_off(s);
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) breg[u][i] = b[off + (long)row_of(u, i) * D + col];
   };
-  if (ns > 0) prefetch(0);
+  if (ns > 0) {
+    load_block(0, 0);
+    load_b(0);
+  }
   for (int s = 0; s < ns; ++s) {
     const long off = seg_off(s);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) h_in[off + (long)row_of(u, i) * D + col] = acc[u][i];
-      *reinterpret_cast<f32x4*>(&hsT[lc * LD + 16 * (wave + 4 * u) + 4 * lg]) = acc[u];
+      *reinterpret_cast<f32x4*>(&hsT[lc * LD + 16 * tile_of(u) + 4 * lg]) = acc[u];
       acc[u] = breg[u];
     }
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int i = 4 * (tid + 256 * v);
-      *reinterpret_cast<float4*>(&ms[(i / D) * LD + i % D]) = mreg[v];
-    }
-    __syncthreads();
-    if (s + 1 < ns) prefetch(s + 1);
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&hsT[lc * LD + k0 + 4 * lg]);
+    for (int bk = 0; bk < NBLK; ++bk) {
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        const f32x4 av =
-            *reinterpret_cast<const f32x4*>(&ms[(16 * (wave + 4 * u) + lc) * LD + k0 + 4 * lg]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc[u], 0, 0, 0);
+      for (int v = 0; v < NV; ++v) {
+        const int i = 4 * (tid + 256 * v);
+        *reinterpret_cast<float4*>(&ms[(i / D) * LD + i % D]) = mreg[v];
       }
+      __syncthreads();
+      if (bk + 1 < NBLK) {
+        load_block(s, bk + 1);
+      } else if (s + 1 < ns) {
+        load_block(s + 1, 0);
+        load_b(s + 1);
+      }
+#pragma unroll 4
+      for (int k0 = 0; k0 < D; k0 += 16) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(&hsT[lc * LD + k0 + 4 * lg]);
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) {
+          const int u = bk * TPB + j;
+          const f32x4 av =
+              *reinterpret_cast<const f32x4*>(&ms[(16 * (wave + 4 * j) + lc) * LD + k0 + 4 * lg]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc[u], 0, 0, 0);
+        }
+      }
+      __syncthreads();  // ms (and, after the last block, hsT) is rewritten next
     }
-    __syncthreads();  // hsT and ms are rewritten by the next step
   }
   if (ht) {
 #pragma unroll
@@ -180,8 +202,10 @@ hipError_t launch_segment_scan_ranges(const float* M, const float* b, const floa
   const dim3 grid(N * H, D / 16);
   if (D == 64)
     k_segment_scan<64><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, seg_first, S, H);
-  else
+  else if (D == 128)
     k_segment_scan<128><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, seg_first, S, H);
+  else
+    k_segment_scan<256><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, seg_first, S, H);
   return hipGetLastError();
 }
 

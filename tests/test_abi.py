@@ -72,7 +72,7 @@ def ws_status(d):
     (dict(variant=2, qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, chunk=64), 2),
     (dict(variant=2, Dk=256, Dv=256), 0),
     (dict(variant=3), 0),
-    (dict(variant=3, Dk=256, Dv=256), 2),
+    (dict(variant=3, Dk=256, Dv=256), 0),
     (dict(variant=3, N=1, B=1), 0),
     (dict(variant=3, B=1, N=3), 0),      # packed batches segment too
     (dict(variant=3, stop_after=3), 2),

@@ -31,6 +31,7 @@ CASES = [
     ("long", {"T": 512}, 8),
     ("long", {"T": 4096}, 8),
     ("long", {"T": 16384}, 8),
+    ("gqa", {"B": 1, "T": 32768}, 4),
     ("decode", {}, 32),
     ("decode", {"T": 8}, 16),
 ]

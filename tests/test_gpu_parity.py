@@ -312,6 +312,7 @@ SEG_CASES = [
     (128, 4, 4, 2, 300, True),
     (128, 4, 2, 1, 517, False),
     (64, 2, 1, 2, 333, True),
+    (256, 2, 1, 1, 300, True),
 ]
 
 
@@ -476,6 +477,7 @@ PACKED_SEG = [
     # D, H, Hg, lengths
     (128, 4, 4, [300, 0, 517, 64, 1]),
     (64, 2, 1, [200, 133]),
+    (256, 2, 2, [150, 0, 90]),
 ]
 
 
