@@ -14,6 +14,9 @@ Recipe (fixed draw order: lengths -> q -> k -> v -> g_pre -> beta_pre -> h0):
   * beta = sigmoid(N(0, 1)), cast to the beta dtype;
   * h0 ~ N(0, std^2) fp32 when the workload has an initial state;
   * packed varlen: lengths ~ U{1 .. max_len}, B = 1, cu_seqlens int32 on the same device.
+The causal conv1d workloads (``draw_conv``) draw, in order: x ~ N(0, 1) cast to the dtype,
+weight ~ N(0, 1 / W), bias ~ N(0, 0.1^2), state lines ~ N(0, 1) cast; sequence n uses state
+line (7 n + 3) mod lines when that is a permutation.
 "N(mu, s)" is read as mean mu and standard deviation s.
 """
 from __future__ import annotations
