@@ -93,13 +93,13 @@ def test_conv1d_dense_matches_oracle(B, T, C, W, dtype, lines, act, bias):
     print(json.dumps(dict(test="conv1d_dense", B=B, T=T, C=C, W=W, dtype=dtype, err=err)))
 
 
-@pytest.mark.parametrize("W", [2, 4])
-def test_conv1d_packed_edges(W):
+@pytest.mark.parametrize("W,dtype", [(2, "bf16"), (4, "bf16"), (3, "f32")])
+def test_conv1d_packed_edges(W, dtype):
     """Ragged packed batch: empty sequences, sequences shorter than W - 1, block-crossing
     boundaries, permuted lines, a zero start, and a cache index outside the state."""
     lens = [1, 0, 2, 45, 3, 0, 33, 1]
     C = 136
-    inp = conv_inputs(1, sum(lens), C, W, "bf16", 10, seed=5 + W)
+    inp = conv_inputs(1, sum(lens), C, W, dtype, 10, seed=5 + W)
     inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
     inp["cache_indices"] = torch.tensor([9, 0, 3, 4, 1, 7, 2, -1], dtype=torch.int32)
     inp["has_initial_state"] = torch.tensor([1, 1, 0, 1, 1, 0, 1, 1], dtype=torch.int32)
