@@ -24,6 +24,22 @@ sys.path.insert(0, ROOT)
 import gdn_inputs  # noqa: E402
 
 METRIC = "GDN chunk-fwd tokens/s at 1 MI355X (16×8192, H=32, D=128, bf16); % roofline"
+
+
+def metric_for(w) -> str:
+    """The metric's name for workload ``w``: the headline's own string for the 16 x 8192
+    workload, the same form with the workload's shape otherwise."""
+    if w == gdn_inputs.WORKLOADS["headline"]:
+        return METRIC
+    heads = "H=%d" % w.H if w.Hg == w.H else "H=%d, Hg=%d" % (w.H, w.Hg)
+    if w.n_varlen:
+        shape = "varlen %d seqs U{1..%d}" % (w.n_varlen, w.max_len)
+    else:
+        shape = "%d×%d" % (w.B, w.T)
+    return "GDN chunk-fwd tokens/s at 1 MI355X (%s, %s, D=%d, %s); %% roofline" % (
+        shape, heads, w.Dk, w.dtype)
+
+
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 F32_PEAK_TFLOPS = 157.3
@@ -66,19 +82,19 @@ def pmc_traffic(workload: str, variant: str):
     return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
 
 
-def algorithmic_work(inp, variant="fused"):
+def algorithmic_work(inp, variant="fused", C=None):
     """Bytes moved and flops a perfect implementation needs (per call).
 
     Bytes: q and k once per q/k head, v, g, beta and h0 (if given) read once, o and ht
-    written once.  Flops (triangle-aware, per token and value head):
-    2 (3 C Dk / 2 + 2 C Dv / 2 + 3 Dk Dv) + C^2 / 3 — K K^T and Q K^T (half), T K and T V
-    (half), P v_new (half), W h, K^T v_new and Q h (full), plus the triangular inverse.
-    The recurrent variant does 6 Dk Dv per token and value head instead (k.H, q.H and the
-    rank-one update of the state)."""
+    written once.  Flops (triangle-aware, per token and value head, at the chunk length C
+    the kernel runs): 2 (3 C Dk / 2 + 2 C Dv / 2 + 3 Dk Dv) + C^2 / 3 — K K^T and Q K^T
+    (half), T K and T V (half), P v_new (half), W h, K^T v_new and Q h (full), plus the
+    triangular inverse.  The recurrent variant does 6 Dk Dv per token and value head instead
+    (k.H, q.H and the rank-one update of the state)."""
     q, v = inp["q"], inp["v"]
     B, T, Hg, Dk = q.shape
     H, Dv = v.shape[2], v.shape[3]
-    C = inp["C"]
+    C = inp["C"] if C is None else C
     el = q.element_size()
     toks = B * T
     nseq = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
@@ -101,6 +117,7 @@ def cpu_baseline(inp, o_gpu, ht_gpu, budget_s: float):
     H = inp["v"].shape[2]
     nseq = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
     cores = len(os.sched_getaffinity(0))
+    oracle.use_native()  # the same C source, -O3 -march=native for this host
     threads = oracle.max_threads(cores)
     rng = np.random.default_rng(12345)
     all_pairs = [(n, h) for n in range(nseq) for h in range(H)]
@@ -131,8 +148,9 @@ def cpu_baseline(inp, o_gpu, ht_gpu, budget_s: float):
         # the oracle's parallel loop runs over the sampled pairs
         "value": value, "unit": "tokens/s", "cores": min(threads, npairs), "kind": "oracle",
         "sample": "%d of %d (sequence, head) pairs at full length, fp64 token recurrence "
-                  "(C, OpenMP), %.1f s; scaled by pairs to the whole job" %
-                  (npairs, len(all_pairs), t_sample),
+                  "(C, gcc -O3 -march=native, OpenMP), %.1f s; scaled by pairs to the "
+                  "whole job" % (npairs, len(all_pairs), t_sample),
+        "cpu_model": oracle.cpu_model(), "host_threads_available": cores,
         "sample_seconds": t_sample,
         "parity_sampled": {"pairs": npairs, "o_rel_l2_max": max(errs_o),
                            "ht_rel_l2_max": max(errs_h)},
@@ -272,6 +290,7 @@ def main():
         ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
         desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
     variant = gdn.gdn_resolved_variant(desc, cu)
+    c_run = gdn.gdn_resolved_chunk(desc, cu)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -298,7 +317,7 @@ def main():
     tokens = q.shape[0] * q.shape[1]
     value = tokens / (ms_per_step * 1e-3)
 
-    by, fl = algorithmic_work(inp, variant)
+    by, fl = algorithmic_work(inp, variant, c_run)
     avg_ms = float(np.mean(launch_ms))
     gbs = by / (avg_ms * 1e-3) / 1e9
     tfl = fl / (avg_ms * 1e-3) / 1e12
@@ -311,7 +330,7 @@ def main():
     elif variant == "recurrent":
         kernel = "k_recurrent (D=%d, one wave per 32 state columns)" % w.Dk
     else:
-        kernel = "k_fused (D=%d, 64-token chunks)" % w.Dk
+        kernel = "k_fused (D=%d, %d-token chunks)" % (w.Dk, c_run)
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": gbs / HBM_PEAK_GBS}
@@ -331,12 +350,13 @@ def main():
         cpu = cpu_baseline(inp, o, ht, args.cpu_budget)
 
     out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "metric": metric_for(w), "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": int(q.shape[0]), "T": int(q.shape[1]),
-                   "H": w.H, "Hg": w.Hg, "Dk": w.Dk, "Dv": w.Dv, "C": w.C,
+                   "H": w.H, "Hg": w.Hg, "Dk": w.Dk, "Dv": w.Dv, "C": c_run,
+                   "C_requested": w.C,
                    "variant": variant, "h0": inp["h0"] is not None,
                    "parallelism": "single GPU"},
         "roofline": roof,

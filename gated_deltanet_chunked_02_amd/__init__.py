@@ -23,6 +23,7 @@ __all__ = [
     "GdnDesc", "GdnError", "load", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size",
     "gdn_stage_buffer", "gdn_status_string", "gdn_version", "chunk_gated_delta_rule",
     "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH", "gdn_resolved_variant",
+    "gdn_resolved_chunk",
     "GdnConvDesc", "gdn_causal_conv1d_fwd", "causal_conv1d", "ACTIVATIONS",
 ]
 
@@ -88,6 +89,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_version.argtypes = []
     lib.gdn_resolved_variant.restype = ctypes.c_int32
     lib.gdn_resolved_variant.argtypes = [ctypes.POINTER(GdnDesc), P]
+    lib.gdn_resolved_chunk.restype = ctypes.c_int32
+    lib.gdn_resolved_chunk.argtypes = [ctypes.POINTER(GdnDesc), P]
     lib.gdn_causal_conv1d_fwd.restype = ctypes.c_int
     lib.gdn_causal_conv1d_fwd.argtypes = [ctypes.POINTER(GdnConvDesc), P, P, P, P, P, P, P, P,
                                           P]
@@ -110,6 +113,15 @@ def gdn_resolved_variant(desc: GdnDesc, cu_seqlens=None) -> str:
         if code == v and name != "auto":
             return name
     raise GdnError(1, "gdn_resolved_variant")
+
+
+def gdn_resolved_chunk(desc: GdnDesc, cu_seqlens=None) -> int:
+    """Chunk length the variant gdn_chunk_fwd runs with this descriptor evaluates (the
+    staged variant's C, the fused kernel's own chunk, 1 for token by token)."""
+    c = int(load().gdn_resolved_chunk(ctypes.byref(desc), _ptr(cu_seqlens)))
+    if c < 0:
+        raise GdnError(1, "gdn_resolved_chunk")
+    return c
 
 
 def gdn_chunk_fwd_workspace_size(desc: GdnDesc) -> int:
@@ -172,6 +184,112 @@ def make_desc(q, v, beta, cu_seqlens=None, chunk_size=128, variant="auto", stop_
                    variant=VARIANTS[variant] if isinstance(variant, str) else int(variant),
                    stop_after=stop_after, workspace=None, workspace_bytes=0)
 
+_INT_DTYPES = ("torch.int32", "torch.int64", "torch.int16", "torch.int8", "torch.uint8")
+
+
+def _need(cond, exc, msg):
+    if not cond:
+        raise exc(msg)
+
+
+def _check_devices(named, ref):
+    """Every tensor of ``named`` (name -> tensor or None) on ``ref``, a CUDA (HIP) device.
+    Run after the shape and dtype checks, so those also run on a host without a GPU."""
+    _need(ref.type == "cuda", ValueError,
+          "the tensors must be device tensors (got %s)" % ref)
+    for name, t in named.items():
+        if t is not None:
+            _need(t.device == ref, ValueError,
+                  "%s must be on %s like the other tensors (got %s)" % (name, ref, t.device))
+
+
+def _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace):
+    """Shapes, dtypes and devices of chunk_gated_delta_rule's tensors, checked before any
+    pointer reaches the library (a host pointer or a short buffer read by a kernel would
+    fault the GPU instead of raising)."""
+    import torch
+    named = dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state,
+                 cu_seqlens=cu_seqlens, workspace=workspace)
+    for name, t in named.items():
+        _need(t is None or isinstance(t, torch.Tensor), TypeError,
+              "%s must be a torch tensor" % name)
+    for name in ("q", "k", "v"):
+        _need(named[name].dim() == 4, ValueError, "%s must be 4-D [B, T, heads, D]" % name)
+    _need(q.dtype in (torch.bfloat16, torch.float32), TypeError,
+          "q must be bf16 or fp32, got %s" % q.dtype)
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, TypeError,
+          "q, k and v must share one dtype (got %s, %s, %s)" % (q.dtype, k.dtype, v.dtype))
+    _need(k.shape == q.shape, ValueError, "k %s must have q's shape %s" % (tuple(k.shape),
+                                                                          tuple(q.shape)))
+    B, T, Hg, Dk = q.shape
+    _need(tuple(v.shape[:2]) == (B, T), ValueError, "v must be [B, T, H, Dv] with q's B, T")
+    H, Dv = v.shape[2], v.shape[3]
+    _need(Hg > 0 and H % Hg == 0, ValueError, "v heads (%d) must be a multiple of q/k heads "
+          "(%d)" % (H, Hg))
+    _need(g.dtype == torch.float32, TypeError, "g must be fp32, got %s" % g.dtype)
+    _need(tuple(g.shape) == (B, T, H), ValueError, "g must be [B, T, H] = %s" % ((B, T, H),))
+    _need(beta.dtype in (torch.bfloat16, torch.float32), TypeError,
+          "beta must be bf16 or fp32, got %s" % beta.dtype)
+    _need(tuple(beta.shape) == (B, T, H), ValueError,
+          "beta must be [B, T, H] = %s" % ((B, T, H),))
+    N = B
+    if cu_seqlens is not None:
+        _need(str(cu_seqlens.dtype) in _INT_DTYPES, TypeError, "cu_seqlens must be integer")
+        _need(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 1, ValueError,
+              "cu_seqlens must be 1-D [N + 1]")
+        _need(B == 1, ValueError, "a packed batch (cu_seqlens) needs B == 1")
+        N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state.is_floating_point(), TypeError, "initial_state must be floating")
+        _need(tuple(initial_state.shape) == (N, H, Dk, Dv), ValueError,
+              "initial_state must be [N, H, Dk, Dv] = %s" % ((N, H, Dk, Dv),))
+    if workspace is not None:
+        _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(), TypeError,
+              "workspace must be a contiguous uint8 tensor")
+    _check_devices(named, q.device)
+
+
+def _validate_conv(x, weight, bias, conv_state, cache_indices, has_initial_state,
+                   cu_seqlens):
+    """Shapes, dtypes and devices of causal_conv1d's tensors (see _validate_gdn)."""
+    import torch
+    named = dict(x=x, weight=weight, bias=bias, conv_state=conv_state,
+                 cache_indices=cache_indices, has_initial_state=has_initial_state,
+                 cu_seqlens=cu_seqlens)
+    for name, t in named.items():
+        _need(t is None or isinstance(t, torch.Tensor), TypeError,
+              "%s must be a torch tensor" % name)
+    _need(x.dim() == 3, ValueError, "x must be 3-D [B, T, C]")
+    _need(x.dtype in (torch.bfloat16, torch.float32), TypeError, "x must be bf16 or fp32")
+    _need(x.is_contiguous(), ValueError, "x must be contiguous")
+    B, T, C = x.shape
+    _need(weight.dtype == torch.float32, TypeError, "weight must be fp32")
+    _need(weight.dim() == 2 and weight.shape[0] == C, ValueError, "weight must be [C, W]")
+    W = weight.shape[1]
+    if bias is not None:
+        _need(bias.dtype == torch.float32, TypeError, "bias must be fp32")
+        _need(tuple(bias.shape) == (C,), ValueError, "bias must be [C]")
+    N = B
+    if cu_seqlens is not None:
+        _need(str(cu_seqlens.dtype) in _INT_DTYPES, TypeError, "cu_seqlens must be integer")
+        _need(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 1, ValueError,
+              "cu_seqlens must be 1-D [N + 1]")
+        _need(B == 1, ValueError, "a packed batch (cu_seqlens) needs B == 1")
+        N = cu_seqlens.numel() - 1
+    if conv_state is not None:
+        _need(conv_state.dtype == x.dtype, TypeError, "conv_state must have x's dtype")
+        _need(conv_state.dim() == 3 and tuple(conv_state.shape[1:]) == (W - 1, C), ValueError,
+              "conv_state must be [lines, W - 1, C] = [lines, %d, %d]" % (W - 1, C))
+        _need(conv_state.is_contiguous(), ValueError,
+              "conv_state must be contiguous (it is updated in place)")
+    for name in ("cache_indices", "has_initial_state"):
+        t = named[name]
+        if t is not None:
+            _need(str(t.dtype) in _INT_DTYPES or t.dtype == torch.bool, TypeError,
+                  "%s must be integer" % name)
+            _need(tuple(t.shape) == (N,), ValueError, "%s must be [N] = [%d]" % (name, N))
+    _check_devices(named, x.device)
+
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                            output_final_state=True, cu_seqlens=None, chunk_size=128,
@@ -185,13 +303,9 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     needed and not given).
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
-        if not t.is_cuda:
-            raise ValueError("%s must be a device tensor" % name)
+    _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace)
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     g, beta = g.contiguous(), beta.contiguous()
-    if g.dtype != torch.float32:
-        raise TypeError("g must be fp32")
     if cu_seqlens is not None:
         cu_seqlens = cu_seqlens.to(torch.int32).contiguous()
     desc = make_desc(q, v, beta, cu_seqlens, chunk_size, variant, stop_after)
@@ -236,22 +350,10 @@ def causal_conv1d(x, weight, bias=None, conv_state=None, cache_indices=None,
     bias [C] fp32; conv_state [lines, W - 1, C] in x's dtype; cache_indices and
     has_initial_state int32 [N]; activation None or "silu"."""
     import torch
-    for name, t in (("x", x), ("weight", weight)):
-        if not t.is_cuda:
-            raise ValueError("%s must be a device tensor" % name)
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
-    if conv_state is not None and not conv_state.is_contiguous():
-        raise ValueError("conv_state must be contiguous (it is updated in place)")
-    if weight.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
-        raise TypeError("weight and bias must be fp32")
-    if conv_state is not None and conv_state.dtype != x.dtype:
-        raise TypeError("conv_state must have x's dtype")
+    _validate_conv(x, weight, bias, conv_state, cache_indices, has_initial_state, cu_seqlens)
     B, T, C = x.shape
     weight = weight.contiguous()
     if bias is not None:
-        if not bias.is_cuda:
-            raise ValueError("bias must be a device tensor")
         bias = bias.contiguous()
     i32 = lambda t: None if t is None else t.to(torch.int32).contiguous()
     cu, idx, init = i32(cu_seqlens), i32(cache_indices), i32(has_initial_state)

@@ -198,10 +198,22 @@ void staged_layout(const gdn::Problem& p, Layout* L) {
   L->total = off;
 }
 
+// The fused variant on a packed batch runs its sequences longest first when the workspace
+// holds their order (4 bytes per sequence): the order kernel's O(N^2) compares are cheap up
+// to this many sequences.  Without it, or beyond, they run in index order (same results).
+constexpr int kLptMaxN = 65536;
+
+bool lpt_wanted(const gdn::Problem& p, bool dense) {
+  return !dense && p.N > 1 && p.N <= kLptMaxN;
+}
+
+size_t lpt_bytes(const gdn::Problem& p) { return align_up((size_t)p.N * sizeof(int32_t)); }
+
 // Workspace of the variant a call resolves to, for one reading of the descriptor.
 size_t workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
   const int v = resolve_variant(d, p, dense, false);
-  if (v == GDN_VARIANT_FUSED || v == GDN_VARIANT_RECURRENT || v < 0) return 0;
+  if (v == GDN_VARIANT_FUSED) return lpt_wanted(p, dense) ? lpt_bytes(p) : 0;
+  if (v == GDN_VARIANT_RECURRENT || v < 0) return 0;
   if (v == GDN_VARIANT_SEGMENTED)
     return seg_layout(p, seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED, dense)).total;
   Layout L;
@@ -288,7 +300,14 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   }
   if (variant == GDN_VARIANT_FUSED) {
-    e = gdn::launch_fused(p, stream);
+    e = hipSuccess;
+    if (lpt_wanted(p, cu_seqlens == nullptr) && d->workspace &&
+        d->workspace_bytes >= lpt_bytes(p) && aligned(d->workspace, kAlign)) {
+      int32_t* order = static_cast<int32_t*>(d->workspace);
+      e = gdn::launch_lpt_order(p.cu, order, p.N, p.T, p.Ttot, stream);
+      p.order = order;
+    }
+    if (e == hipSuccess) e = gdn::launch_fused(p, stream);
   } else if (variant == GDN_VARIANT_RECURRENT) {
     e = gdn::launch_recurrent(p, stream);
   } else if (variant == GDN_VARIANT_SEGMENTED) {
@@ -416,6 +435,14 @@ int32_t gdn_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens) {
     return -1;
   }
   return resolve_variant(d, p, cu_seqlens == nullptr, true);
+}
+
+int32_t gdn_resolved_chunk(const gdn_desc* d, const int32_t* cu_seqlens) {
+  const int32_t v = gdn_resolved_variant(d, cu_seqlens);
+  if (v < 0) return -1;
+  if (v == GDN_VARIANT_RECURRENT) return 1;
+  if (v == GDN_VARIANT_STAGED) return d->chunk == 0 ? 128 : d->chunk;
+  return d->Dk > 128 ? 32 : kFusedChunk;  // the fused kernel's own chunk (also segmented)
 }
 
 const char* gdn_status_string(gdn_status s) {

@@ -23,6 +23,12 @@
 // where the 16 x 16 diagonal inverses come from the nilpotent product
 // (I + A_ii)^-1 = (I - A_ii)(I + A_ii^2)(I + A_ii^4)(I + A_ii^8) on the matrix cores.
 //
+// The tiles (A~, T_ii diag(beta), the gated Q K^T) are fp16: they depend on q, k, g and beta
+// only and are bounded for keys with beta |k|^2 <= 2 and |q| |k| scale < 2^15 (L2-normalised
+// q and k).  The substitution operands R and v_new are fp16 too, but scale with v and h0, so
+// each wave carries them multiplied by a power of two chosen per chunk from its largest |R|
+// (exact, undone in fp32): any bf16 magnitude of v and h0 keeps the fp16 precision.
+//
 // The state-independent work of a chunk (its lower 16 x 16 tiles of K K^T and Q K^T, gated
 // and masked, the inverses T_ii and the gate vectors) is done one chunk ahead, by waves 0-3
 // and one gate wave, while the current chunk is solved; K and Q are therefore triple-buffered in
@@ -159,8 +165,9 @@ template <int DK, int DV, bool OUT>
 __global__ __launch_bounds__(DV * 4) void k_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const void* __restrict__ beta, int beta_f32,
-    const float* __restrict__ h0, const int32_t* __restrict__ cu, bf16* __restrict__ o,
-    float* __restrict__ ht, int T, int Ttot, int H, int Hg, float scale, int flags) {
+    const float* __restrict__ h0, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ order, bf16* __restrict__ o, float* __restrict__ ht, int T,
+    int Ttot, int H, int Hg, float scale, int flags) {
   typedef FusedCfg<DK, DV> F;
   constexpr int CS = F::CS, NB = F::NB, NDK = F::NDK, RS = F::RS, TE = F::TE, CPR = F::CPR;
   constexpr int NW = F::NW, CPRV = F::CPRV;
@@ -189,35 +196,10 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
   __shared__ __align__(16) float SDC[3][CS];  // e^{Gc_end - Gc_t}
   __shared__ float SGE[3];                    // e^{Gc_end}
 
-  if (cu) {
-    // Packed batch: the workgroups take the sequences longest first (workgroup rank n gets
-    // the sequence of rank n by length, ties by index), so the last workgroups to start are
-    // the shortest and the batch ends with little imbalance.  The lengths are staged in the
-    // first K buffer, which the pipeline has not used yet.
-    const int N = gridDim.x / (F::SPLIT * H);
-    if (N > 1 && N <= F::TILE / 2) {
-      __shared__ int sel;
-      int* lens = reinterpret_cast<int*>(&SK[0][0]);
-      for (int i = threadIdx.x; i < N; i += blockDim.x) {
-        int s0, l0;
-        seq_span(cu, i, T, Ttot, s0, l0);
-        lens[i] = l0;
-      }
-      __syncthreads();
-      for (int m = threadIdx.x; m < N; m += blockDim.x) {
-        const int lm = lens[m];
-        int r = 0;
-        for (int j = 0; j < N; ++j) {
-          const int lj = lens[j];
-          r += (lj > lm) || (lj == lm && j < m);
-        }
-        if (r == n) sel = m;  // the ranks are a permutation: exactly one m matches
-      }
-      __syncthreads();
-      n = sel;
-      __syncthreads();  // every wave has read sel and lens before SK is filled
-    }
-  }
+  // Packed batch with a longest-first order (k_lpt_order): workgroup rank n takes the
+  // sequence of rank n by length, so the last workgroups to start are the shortest and the
+  // batch ends with little imbalance.
+  if (order) n = order[n];
   int cs0, L;
   seq_span(cu, n, T, Ttot, cs0, L);
   const int nchunks = (L + CS - 1) / CS;
@@ -568,22 +550,45 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
         }
       }
     }
+    // R / beta = V - e^Gc (K h) of every block, in place of K h: lane (l%16, g) holds
+    // tokens 4 g + e of column 16 w + l%16
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const bf16x4 vv = read_tr<bf16x4>(vt + b * 16 * DV);
+      const f32x4 ef = *reinterpret_cast<const f32x4*>(efp + 16 * b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xk[b][e] = fmaf(-ef[e], xk[b][e], (float)vv[e]);
+    }
+    // The substitution and output operands are fp16 (range 2^-14 .. 65504), while v and h0
+    // may hold any bf16 magnitude.  The value side of the chunk (R, v_new) is therefore
+    // carried scaled by a power of two s, one per wave and chunk, that brings the largest
+    // |R| of the wave's 16 columns into [1, 2): exact (no rounding) and undone in fp32
+    // before o and the state update.  Every quantity of the value side is linear in
+    // (v, h0), so the scaled chunk stays a bounded multiple of that largest |R|.
+    float vs, vsi;
+    {
+      uint32_t m = 0;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = max(m, __builtin_bit_cast(uint32_t, fabsf(xk[b][e])));
+      // biased exponent of the largest |R|, clamped so that s and 1 / s are normal floats
+      // (zero or denormal R: s = 2^126, where every scaled value is still below 1)
+      const int ex = min(max((int)(wave_max_u32(m) >> 23), 1), 253);
+      vs = __builtin_bit_cast(float, (uint32_t)(254 - ex) << 23);   // 2^(127 - ex)
+      vsi = __builtin_bit_cast(float, (uint32_t)ex << 23);          // 2^(ex - 127)
+    }
     // forward substitution, outputs and the update operands, block by block
     f16x4 vhh[NB];
     bf16x4 vb[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      // R / beta - sum_{j<b} A~_bj v_j = V - e^Gc (K h) + sum_{j<b} (-A~_bj) v_j: lane
-      // (l%16, g) holds tokens 4 g + e of column 16 w + l%16
-      const bf16x4 vv = read_tr<bf16x4>(vt + b * 16 * DV);
-      const f32x4 ef = *reinterpret_cast<const f32x4*>(efp + 16 * b);
-      f32x4 acc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(-ef[e], xk[b][e], (float)vv[e]);
+      // s (R / beta - sum_{j<b} A~_bj v_j) = s R / beta + sum_{j<b} (-A~_bj) (s v_j)
+      f32x4 acc = xk[b] * vs;
 #pragma unroll
       for (int j = 0; j < b; ++j)
         acc = mma16h(*reinterpret_cast<const f16x4*>(Ac + tix<F>(b, j)), vhh[j], acc);
-      // v_b = T_bb diag(beta) (...)
+      // s v_b = T_bb diag(beta) (...)
       const f32x4 vn =
           mma16h(*reinterpret_cast<const f16x4*>(Ac + tix<F>(b, b)), to_h(acc), zero4());
       vhh[b] = to_h(vn);
@@ -597,15 +602,15 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
         for (int j = 0; j <= b; ++j)
           z = mma16h(vhh[j], *reinterpret_cast<const f16x4*>(Pc + tix<F>(b, j)), z);
         const float egt = eop[16 * b];
-        const f32x2_t o01 = {fmaf(egt, yq[b][0], z[0]), fmaf(egt, yq[b][1], z[1])};
-        const f32x2_t o23 = {fmaf(egt, yq[b][2], z[2]), fmaf(egt, yq[b][3], z[3])};
+        const f32x2_t o01 = {fmaf(egt, yq[b][0], z[0] * vsi), fmaf(egt, yq[b][1], z[1] * vsi)};
+        const f32x2_t o23 = {fmaf(egt, yq[b][2], z[2] * vsi), fmaf(egt, yq[b][3], z[3] * vsi)};
         const u32x2 ow = {__builtin_bit_cast(uint32_t, __builtin_convertvector(o01, bf16x2_t)),
                           __builtin_bit_cast(uint32_t, __builtin_convertvector(o23, bf16x2_t))};
         __builtin_amdgcn_raw_buffer_store_b64(ow, orsrc, (int)otoff, b * oblock, 0);
       }
-      // e^{Gc_end - Gc} v_new, the update operand
+      // e^{Gc_end - Gc} v_new, the update operand (the scale undone)
       const f32x4 dc = *reinterpret_cast<const f32x4*>(dcp + 16 * b);
-      vb[b] = to_b(dc * vn);
+      vb[b] = to_b(dc * (vn * vsi));
     }
     // h = e^{Gc_end} h + K^T (e^{Gc_end-Gc} v_new), two blocks per 32-deep product (K^T
     // fragments by transposing LDS reads)
@@ -658,12 +663,51 @@ hipError_t run_fused(const Problem& p, hipStream_t st) {
   if (grid == 0) return hipSuccess;
   k_fused<DK, DV, OUT><<<grid, FusedCfg<DK, DV>::NTH, 0, st>>>(
       static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.v),
-      p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot,
-      p.H, p.Hg, p.scale, p.fused_flags);
+      p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, p.cu ? p.order : nullptr,
+      static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot, p.H, p.Hg, p.scale, p.fused_flags);
   return hipGetLastError();
 }
 
+// Longest-processing-time-first order of a packed batch: order[rank] = m, where the rank of
+// sequence m counts the sequences longer than m, and those of equal length before it.  One
+// thread per sequence, the lengths staged through LDS in blocks; O(N^2) compares over the
+// whole grid (about 10 us at N = 4096), and the ranks are a permutation.
+__global__ __launch_bounds__(256) void k_lpt_order(const int32_t* __restrict__ cu,
+                                                   int32_t* __restrict__ order, int N, int T,
+                                                   int Ttot) {
+  __shared__ int lens[1024];
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  int lm = 0;
+  if (m < N) {
+    int s0;
+    seq_span(cu, m, T, Ttot, s0, lm);
+  }
+  int r = 0;
+  for (int j0 = 0; j0 < N; j0 += 1024) {
+    const int nj = min(1024, N - j0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nj; i += 256) {
+      int s0, l0;
+      seq_span(cu, j0 + i, T, Ttot, s0, l0);
+      lens[i] = l0;
+    }
+    __syncthreads();
+    for (int i = 0; i < nj; ++i) {
+      const int lj = lens[i];
+      r += (lj > lm) || (lj == lm && j0 + i < m);
+    }
+  }
+  if (m < N) order[r] = m;
+}
+
 }  // namespace
+
+hipError_t launch_lpt_order(const int32_t* cu, int32_t* order, int N, int T, int Ttot,
+                            hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  k_lpt_order<<<(N + 255) / 256, 256, 0, st>>>(cu, order, N, T, Ttot);
+  return hipGetLastError();
+}
 
 bool fused_supported(const Problem& p) {
   return !p.f32 && (p.D == 64 || p.D == 128 || p.D == 256);

@@ -24,6 +24,7 @@ struct Problem {
   void* o;
   float* ht;
   int fused_flags = 0;  // kFused* bits, for the passes of the segmented variant
+  const int32_t* order = nullptr;  // packed batch: sequence of each workgroup rank, or NULL
 };
 
 // Fused-kernel modes used by the segmented variant's passes.
@@ -49,6 +50,10 @@ struct Stages {
 hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st);
 bool fused_supported(const Problem& p);
 hipError_t launch_fused(const Problem& p, hipStream_t st);
+// Longest-first order of a packed batch's sequences (order[rank] = sequence), for the fused
+// kernel's workgroup ranks.
+hipError_t launch_lpt_order(const int32_t* cu, int32_t* order, int N, int T, int Ttot,
+                            hipStream_t st);
 // Causal depthwise conv1d with a decode state (the step before the delta rule).
 struct ConvProblem {
   int T, Ttot, N, C, W, lines;  // C channels (multiple of 8), W taps in {2, 3, 4}

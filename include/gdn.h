@@ -105,13 +105,19 @@ typedef struct gdn_desc {
   int32_t N;          /* sequences: B when cu_seqlens is NULL, else len(cu_seqlens) - 1 */
   int32_t H, Hg;      /* value heads, q/k heads; H % Hg == 0                              */
   int32_t Dk, Dv;     /* head dims; this build supports Dk == Dv in {64, 128, 256}        */
-  int32_t chunk;      /* C in {64, 128}; 0 selects 128                                    */
+  int32_t chunk;      /* C in {64, 128} (0 selects 128): the chunk length of the staged
+                         variant.  The fused and segmented variants run their own chunk
+                         (64 tokens, 32 at D = 256: what three K/Q buffers allow in LDS) and
+                         the recurrent one goes token by token, whatever C asks for; the
+                         result is the same up to rounding (the chunked form is exact for
+                         any chunk length).  gdn_resolved_chunk() reports the length run.  */
   int32_t qkv_dtype;  /* gdn_dtype of q, k, v, o                                          */
   int32_t beta_dtype; /* gdn_dtype of beta                                                */
   int32_t variant;    /* gdn_variant                                                      */
   int32_t stop_after; /* staged only: 0 = all stages, k in 1..6 = stop after stage k      */
-  void* workspace;    /* device memory for the staged and segmented variants (256-byte
-                         aligned; may be NULL for fused)                                  */
+  void* workspace;    /* device memory for the staged and segmented variants and the fused
+                         variant's longest-first order (256-byte aligned; may be NULL for
+                         fused, see gdn_chunk_fwd_workspace_size)                         */
   size_t workspace_bytes;
 } gdn_desc;
 
@@ -158,8 +164,11 @@ gdn_status gdn_causal_conv1d_fwd(const gdn_conv_desc* d, const void* x, const fl
                                  const int32_t* has_initial_state, const int32_t* cu_seqlens,
                                  void* y, hipStream_t stream);
 
-/* Bytes of workspace the variant chosen by d->variant needs (0 for the fused variant; for
- * AUTO, what AUTO picks when given that much).  The query cannot see cu_seqlens: a
+/* Bytes of workspace the variant chosen by d->variant needs (for AUTO, what AUTO picks when
+ * given that much).  The fused variant needs none on a dense batch; on a packed batch of
+ * 2 .. 65536 sequences it asks for 4 bytes per sequence (256-byte aligned) to run them
+ * longest first (an order kernel ranks them by length; the last workgroups to start are then
+ * the shortest).  Given less, it runs them in index order: the same results, bit for bit.  The query cannot see cu_seqlens: a
  * descriptor with N other than 0 or B is a packed batch, one with B == 1 may be either and
  * gets the larger of the two needs, any other is a dense batch.  Host-only, no device work.
  * Returns 0 and sets *status on an invalid descriptor. */
@@ -169,6 +178,11 @@ size_t gdn_chunk_fwd_workspace_size(const gdn_desc* d, gdn_status* status);
  * workspace (AUTO resolved), or -1 if the call would be refused.  Only the nullness of
  * cu_seqlens is used; host-only, no device work. */
 int32_t gdn_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens);
+
+/* The chunk length gdn_chunk_fwd(d, ..., cu_seqlens, ...) runs with this descriptor: C for
+ * the staged variant, the fused kernel's own chunk for the fused and segmented ones, 1 for
+ * the recurrent one; -1 if the call would be refused.  Host-only, no device work. */
+int32_t gdn_resolved_chunk(const gdn_desc* d, const int32_t* cu_seqlens);
 
 /* The forward pass.  q, k, v, g, beta, o are required unless B*T = 0 (then every sequence
  * is empty: ht = h0, or zeros, and nothing else is touched, whatever the variant); h0 (zero

@@ -48,12 +48,42 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
-def _load():
+def use_native() -> str:
+    """Switch this process to a copy of the same C source built with -O3 -march=native for
+    the host it runs on (the CPU-baseline timing; the tests use the portable -O2 build,
+    which can travel between machines).  Built in a temporary directory, never shipped.
+    Returns the library path."""
+    global _lib
+    import tempfile
+    path = os.path.join(tempfile.gettempdir(), "libgdn_oracle_native_%d.so" % os.getpid())
+    subprocess.check_call(
+        ["gcc", "-O3", "-march=native", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+         "-o", path, _SRC, "-lm"])
+    _lib = None
+    _load(path)
+    return path
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _load(path=None):
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        if path is None:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=False)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         lib.gdn_oracle_fwd.restype = ctypes.c_int
         lib.gdn_oracle_fwd.argtypes = [

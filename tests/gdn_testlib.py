@@ -2,10 +2,23 @@
 pairs, and running the HIP path through the C ABI binding."""
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
 import oracle
+
+
+def log(**kw):
+    """Print one JSON record; also append it to $GDN_PARITY_LOG when that is set (pytest
+    captures the output of passing tests)."""
+    print(json.dumps(kw), flush=True)
+    path = os.environ.get("GDN_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(kw) + "\n")
 
 # Tolerances (stated for the workloads): fp32 max-abs on o and ht; bf16 relative L2 error
 # over the whole tensor.

@@ -232,3 +232,130 @@ def conv_status(**kw):
 ])
 def test_conv1d_rejects_bad_arguments_before_any_launch(lib, kw, status):
     assert conv_status(**kw) == status
+
+
+# ------------------------------------------------------------------ binding validation
+# Each case has one defect; shapes and dtypes are checked before devices, so every case is
+# caught here on the host, before any pointer reaches the library.
+def gdn_args(**over):
+    import torch
+    B, T, Hg, H, D = 1, 8, 2, 4, 64
+    a = dict(q=torch.zeros(B, T, Hg, D, dtype=torch.bfloat16),
+             k=torch.zeros(B, T, Hg, D, dtype=torch.bfloat16),
+             v=torch.zeros(B, T, H, D, dtype=torch.bfloat16),
+             g=torch.zeros(B, T, H), beta=torch.zeros(B, T, H, dtype=torch.bfloat16),
+             initial_state=None, cu_seqlens=None, workspace=None)
+    a.update(over)
+    return a
+
+
+def _bad_gdn_cases():
+    import torch
+    bf = torch.bfloat16
+    return [
+        (dict(k=torch.zeros(1, 8, 2, 64, dtype=torch.float32)), TypeError),   # k dtype
+        (dict(v=torch.zeros(1, 8, 4, 64, dtype=torch.float32)), TypeError),   # v dtype
+        (dict(q=torch.zeros(1, 8, 2, 64, dtype=torch.float16),
+              k=torch.zeros(1, 8, 2, 64, dtype=torch.float16),
+              v=torch.zeros(1, 8, 4, 64, dtype=torch.float16)), TypeError),   # fp16
+        (dict(k=torch.zeros(1, 8, 2, 32, dtype=bf)), ValueError),             # k shape
+        (dict(v=torch.zeros(1, 7, 4, 64, dtype=bf)), ValueError),             # v tokens
+        (dict(v=torch.zeros(1, 8, 3, 64, dtype=bf)), ValueError),             # H % Hg
+        (dict(q=torch.zeros(8, 2, 64, dtype=bf)), ValueError),                # q rank
+        (dict(g=torch.zeros(1, 8, 4, dtype=bf)), TypeError),                  # g dtype
+        (dict(g=torch.zeros(1, 8, 2)), ValueError),                           # g shape
+        (dict(beta=torch.zeros(1, 8, 4, dtype=torch.float16)), TypeError),    # beta dtype
+        (dict(beta=torch.zeros(1, 8, 4, 1, dtype=bf)), ValueError),           # beta shape
+        (dict(initial_state=torch.zeros(1, 4, 64, 32)), ValueError),          # h0 shape
+        (dict(initial_state=torch.zeros(2, 4, 64, 64)), ValueError),          # h0: N != B
+        (dict(initial_state=torch.zeros(1, 4, 64, 64, dtype=torch.int32)), TypeError),
+        (dict(cu_seqlens=torch.zeros(3)), TypeError),                         # float cu
+        (dict(cu_seqlens=torch.zeros(1, 3, dtype=torch.int32)), ValueError),  # 2-D cu
+        (dict(q=torch.zeros(2, 4, 2, 64, dtype=bf), k=torch.zeros(2, 4, 2, 64, dtype=bf),
+              v=torch.zeros(2, 4, 4, 64, dtype=bf), g=torch.zeros(2, 4, 4),
+              beta=torch.zeros(2, 4, 4, dtype=bf),
+              cu_seqlens=torch.tensor([0, 4, 8], dtype=torch.int32)), ValueError),  # B != 1
+        (dict(cu_seqlens=torch.tensor([0, 3, 8], dtype=torch.int32),
+              initial_state=torch.zeros(1, 4, 64, 64)), ValueError),          # h0: N = 2
+        (dict(workspace=torch.zeros(16)), TypeError),                         # not uint8
+        (dict(), ValueError),                                                 # host tensors
+        (dict(cu_seqlens=torch.tensor([0, 8], dtype=torch.int32)), ValueError),
+        (dict(initial_state=torch.zeros(1, 4, 64, 64)), ValueError),
+    ]
+
+
+@pytest.mark.parametrize("case", range(22))
+def test_binding_validates_every_tensor(lib, case):
+    over, exc = _bad_gdn_cases()[case]
+    a = gdn_args(**over)
+    with pytest.raises(exc):
+        gdn.chunk_gated_delta_rule(a["q"], a["k"], a["v"], a["g"], a["beta"],
+                                   initial_state=a["initial_state"],
+                                   cu_seqlens=a["cu_seqlens"], workspace=a["workspace"])
+
+
+def test_binding_case_count():
+    assert len(_bad_gdn_cases()) == 22
+
+
+def _bad_conv_cases():
+    import torch
+    bf = torch.bfloat16
+    x = torch.zeros(2, 8, 16, dtype=bf)
+    w = torch.zeros(16, 4)
+    return [
+        (dict(x=torch.zeros(2, 8, 16, dtype=torch.float16)), TypeError),
+        (dict(x=torch.zeros(16, 8, dtype=bf)), ValueError),
+        (dict(x=torch.zeros(2, 16, 8, dtype=bf).transpose(1, 2)), ValueError),  # strided
+        (dict(weight=torch.zeros(16, 4, dtype=bf)), TypeError),
+        (dict(weight=torch.zeros(8, 4)), ValueError),
+        (dict(bias=torch.zeros(16, dtype=bf)), TypeError),
+        (dict(bias=torch.zeros(8)), ValueError),
+        (dict(conv_state=torch.zeros(2, 3, 16)), TypeError),                  # state dtype
+        (dict(conv_state=torch.zeros(2, 2, 16, dtype=bf)), ValueError),       # W - 1 rows
+        (dict(conv_state=torch.zeros(2, 16, 3, dtype=bf).transpose(1, 2)), ValueError),
+        (dict(cache_indices=torch.zeros(3, dtype=torch.int32)), ValueError),  # [N]
+        (dict(cache_indices=torch.zeros(2)), TypeError),
+        (dict(has_initial_state=torch.zeros(1, 2, dtype=torch.int32)), ValueError),
+        (dict(cu_seqlens=torch.tensor([0, 8], dtype=torch.int32)), ValueError),  # B != 1
+        (dict(), ValueError),                                                 # host tensors
+    ], x, w
+
+
+@pytest.mark.parametrize("case", range(15))
+def test_conv_binding_validates_every_tensor(lib, case):
+    cases, x, w = _bad_conv_cases()
+    over, exc = cases[case]
+    a = dict(x=x, weight=w, bias=None, conv_state=None, cache_indices=None,
+             has_initial_state=None, cu_seqlens=None)
+    a.update(over)
+    with pytest.raises(exc):
+        gdn.causal_conv1d(a["x"], a["weight"], bias=a["bias"], conv_state=a["conv_state"],
+                          cache_indices=a["cache_indices"],
+                          has_initial_state=a["has_initial_state"], cu_seqlens=a["cu_seqlens"])
+
+
+def test_resolved_chunk_reports_what_runs(lib):
+    A = 0x10000
+    assert gdn.load().gdn_resolved_chunk(ctypes.byref(desc(variant=1, chunk=64)), None) == 64
+    assert gdn.load().gdn_resolved_chunk(ctypes.byref(desc(variant=1, chunk=0)), None) == 128
+    assert gdn.gdn_resolved_chunk(desc(variant=2, chunk=128)) == 64
+    assert gdn.gdn_resolved_chunk(desc(variant=2, chunk=128, Dk=256, Dv=256)) == 32
+    assert gdn.gdn_resolved_chunk(desc(variant=2, Dk=64, Dv=64)) == 64
+    assert gdn.gdn_resolved_chunk(desc(variant=4)) == 1
+    assert gdn.gdn_resolved_chunk(desc(T=4)) == 1                      # AUTO: recurrent
+    assert gdn.gdn_resolved_chunk(desc(variant=3, B=1, N=1, T=65536)) == 64
+    assert gdn.load().gdn_resolved_chunk(ctypes.byref(desc(Dk=96, Dv=96)), None) == -1
+    assert gdn.load().gdn_resolved_chunk(ctypes.byref(desc(B=1, N=5, T=4096)), A) == 64
+
+
+def test_fused_packed_batch_asks_for_its_order(lib):
+    # a packed batch (N other than B): 4 bytes per sequence, 256-byte aligned
+    assert gdn.gdn_chunk_fwd_workspace_size(desc(B=1, N=64, T=200000, variant=2)) == 256
+    assert gdn.gdn_chunk_fwd_workspace_size(desc(B=1, N=100, T=200000, variant=2)) == 512
+    assert gdn.gdn_chunk_fwd_workspace_size(desc(B=1, N=4096, T=1 << 20, variant=2)) == 16384
+    # a dense batch needs nothing, and neither does one packed sequence
+    assert gdn.gdn_chunk_fwd_workspace_size(desc(variant=2)) == 0
+    assert gdn.gdn_chunk_fwd_workspace_size(desc(B=1, N=1, T=4096, variant=2)) == 0
+    # beyond 65536 sequences they run in index order, without workspace
+    assert gdn.gdn_chunk_fwd_workspace_size(desc(B=1, N=70000, T=1 << 22, variant=2)) == 0

@@ -1,5 +1,6 @@
 """Full-size parity: each workload at its real size, run the way the benchmark runs it
-(variant AUTO, inputs drawn on the GPU), checked against the fp64 oracle on a seeded sample
+(variant AUTO, inputs drawn on the GPU; the headline also through the staged variant, the
+seven stage kernels a0-a7 at their real size), checked against the fp64 oracle on a seeded sample
 of (sequence, head) pairs: relative L2 per pair <= 5e-3 on o and <= 1e-2 on ht (the bf16
 tolerances).  The sample always includes the first and the last sequence (for a packed
 batch also the shortest and the longest one) and the first and the last head.  The head
@@ -20,8 +21,9 @@ pytestmark = pytest.mark.gpu
 LOG = os.environ.get("GDN_PARITY_LOG")
 
 CASES = [
-    # workload, overrides, sampled pairs
+    # workload, overrides, sampled pairs[, variant]
     ("headline", {}, 16),
+    ("headline", {}, 16, "staged"),
     ("gqa", {}, 8),
     ("varlen", {}, 16),
     ("varlen", {"H": 16, "Hg": 16}, 8),
@@ -60,20 +62,24 @@ def sample_pairs(inp, count, seed):
     return out
 
 
-@pytest.mark.parametrize("name,over,count", CASES,
-                         ids=["%s%s" % (c[0], "".join("-%s%d" % kv for kv in c[1].items()))
-                              for c in CASES])
-def test_full_size_sampled(name, over, count):
+@pytest.mark.parametrize("case", CASES,
+                         ids=["%s%s%s" % (c[0], "".join("-%s%d" % kv for kv in c[1].items()),
+                                          "-" + c[3] if len(c) > 3 else "") for c in CASES])
+def test_full_size_sampled(case):
     import gated_deltanet_chunked_02_amd as gdn
+    name, over, count = case[:3]
+    req = case[3] if len(case) > 3 else "auto"
     w = gdn_inputs.WORKLOADS[name].with_(**over)
     inp = gdn_inputs.draw(w, device="cuda")
-    print("[fullsize] %s drawn: q %s" % (w.name, tuple(inp["q"].shape)), flush=True)
+    print("[fullsize] %s drawn: q %s, variant %s" % (w.name, tuple(inp["q"].shape), req),
+          flush=True)
     o, ht = gdn.chunk_gated_delta_rule(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                        scale=inp["scale"], initial_state=inp["h0"],
-                                       cu_seqlens=inp["cu_seqlens"], chunk_size=w.C)
+                                       cu_seqlens=inp["cu_seqlens"], chunk_size=w.C,
+                                       variant=req)
     torch.cuda.synchronize()
-    # the variant AUTO ran (chunk_gated_delta_rule gives it the workspace it asks for)
-    desc = gdn.make_desc(inp["q"], inp["v"], inp["beta"], inp["cu_seqlens"], w.C, "auto")
+    # the variant that ran (chunk_gated_delta_rule gives it the workspace it asks for)
+    desc = gdn.make_desc(inp["q"], inp["v"], inp["beta"], inp["cu_seqlens"], w.C, req)
     wsb = gdn.gdn_chunk_fwd_workspace_size(desc)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
     if ws is not None:

@@ -31,6 +31,28 @@ def draw(**kw):
     return gdn_inputs.draw(gdn_inputs.small(**kw), device="cpu")
 
 
+def check_per_pair(inp, o, ht, o_ref, ht_ref, label=""):
+    """The bf16 tolerances per (sequence, head) pair, so that one wrong short sequence is
+    not diluted by the rest of a packed batch.  Returns the worst pair errors."""
+    o64, ht64 = to64(o), to64(ht)
+    H = inp["v"].shape[2]
+    N = ht64.shape[0]
+    worst_o = worst_h = 0.0
+    for n in range(N):
+        for h in range(H):
+            ts, b, _ = pair_slices(inp, n, h)
+            ref = o_ref[b, ts, h]
+            if ref.size and np.any(ref):
+                eo = rel_l2(o64[b, ts, h], ref)
+                assert eo <= 5e-3, "%s pair %s o rel-L2 %.3g" % (label, (n, h), eo)
+                worst_o = max(worst_o, eo)
+            if np.any(ht_ref[n, h]):
+                eh = rel_l2(ht64[n, h], ht_ref[n, h])
+                assert eh <= 1e-2, "%s pair %s ht rel-L2 %.3g" % (label, (n, h), eh)
+                worst_h = max(worst_h, eh)
+    return worst_o, worst_h
+
+
 # ------------------------------------------------------------------ the fp32 workload
 @pytest.mark.parametrize("variant", ["auto", "staged"])
 def test_tiny_f32_workload(variant):
@@ -77,9 +99,11 @@ def test_varlen_edge_lengths(variant, C):
     o_ref, ht_ref = oracle_full(inp)
     o, ht = run_gdn(inp, variant=variant)
     eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "varlen")
+    po, ph = check_per_pair(inp, o, ht, o_ref, ht_ref, "varlen %s C%d" % (variant, C))
     # the empty sequence passes its initial state through untouched
     assert torch.equal(ht[4].cpu(), inp["h0"][4])
-    log(test="varlen_edges", variant=variant, C=C, o_rel=eo, ht_rel=eh)
+    log(test="varlen_edges", variant=variant, C=C, o_rel=eo, ht_rel=eh, pair_o_max=po,
+        pair_ht_max=ph)
 
 
 def test_varlen_workload_reduced():
@@ -87,10 +111,12 @@ def test_varlen_workload_reduced():
     w = gdn_inputs.WORKLOADS["varlen"].with_(n_varlen=12, max_len=700, H=4, Hg=4)
     inp = gdn_inputs.draw(w, device="cpu")
     o_ref, ht_ref = oracle_full(inp)
-    for variant in ("staged", "fused"):
+    for variant in ("staged", "fused", "segmented"):
         o, ht = run_gdn(inp, variant=variant)
         eo, eh = check_against_oracle(inp, o, ht, o_ref, ht_ref, "varlen " + variant)
-        log(test="varlen_reduced", variant=variant, o_rel=eo, ht_rel=eh)
+        po, ph = check_per_pair(inp, o, ht, o_ref, ht_ref, "varlen reduced " + variant)
+        log(test="varlen_reduced", variant=variant, o_rel=eo, ht_rel=eh, pair_o_max=po,
+            pair_ht_max=ph)
 
 
 # ------------------------------------------------------------------ per-stage parity
@@ -167,8 +193,14 @@ def test_stage_by_stage(wl):
     errs["ht"] = rel_l2(to64(ht), ref["ht"])
     log(test="stage_by_stage", workload=wl, **errs)
     assert errs["A"] <= 1e-5
-    for name in ("Tinv", "W", "U", "h_c", "v_new", "o", "ht"):
+    for name in ("Tinv", "W", "U", "h_c", "v_new"):
         assert errs[name] <= tol, (name, errs[name])
+    # the outputs at the stated tolerances (fp32: max-abs 1e-4 on o and ht)
+    if wl == "tiny_f32":
+        assert max_abs(to64(o).reshape(ref["o"].shape), ref["o"]) <= 1e-4
+        assert max_abs(to64(ht), ref["ht"]) <= 1e-4
+    else:
+        assert errs["o"] <= 5e-3 and errs["ht"] <= 1e-2, (errs["o"], errs["ht"])
 
 
 def test_stop_after_leaves_outputs_untouched():
@@ -201,13 +233,27 @@ def test_fused_and_staged_agree_and_are_deterministic():
     assert e <= 5e-3
 
 
-@pytest.mark.parametrize("variant", ["staged", "fused"])
-def test_chunk_size_invariance(variant):
-    inp = draw(B=1, T=333, H=2, Dk=128, C=64, seed=22, h0_std=0.05)
-    o64, h64 = run_gdn(inp, variant=variant, C=64)
-    o128, h128 = run_gdn(inp, variant=variant, C=128)
-    assert rel_l2(to64(o64), to64(o128)) <= 5e-3
-    assert rel_l2(to64(h64), to64(h128)) <= 1e-2
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_chunk_size_invariance(D):
+    """The staged variant runs the requested C (64 or 128); the fused kernel runs its own
+    chunk (64 tokens, 32 at D = 256), whatever C asks for.  All of them, and the oracle,
+    agree: the chunked form is exact for any chunk size."""
+    import gated_deltanet_chunked_02_amd as gdn
+    inp = draw(B=1, T=333, H=2, Dk=D, C=64, seed=22, h0_std=0.05)
+    o_ref, ht_ref = oracle_full(inp)
+    runs = {}
+    for variant, C in (("staged", 64), ("staged", 128), ("fused", 128)):
+        o, ht = run_gdn(inp, variant=variant, C=C)
+        check_against_oracle(inp, o, ht, o_ref, ht_ref, "%s C%d D%d" % (variant, C, D))
+        desc = gdn.make_desc(inp["q"], inp["v"], inp["beta"], None, C, variant)
+        runs[(variant, gdn.gdn_resolved_chunk(desc))] = (to64(o), to64(ht))
+    assert ("staged", 64) in runs and ("staged", 128) in runs
+    assert ("fused", 32 if D == 256 else 64) in runs
+    vals = list(runs.values())
+    for oa, ha in vals[1:]:
+        assert rel_l2(oa, vals[0][0]) <= 5e-3 and rel_l2(ha, vals[0][1]) <= 1e-2
+    # the staged runs at C = 64 and 128 differ in their rounding, so C was honoured
+    assert not np.array_equal(runs[("staged", 64)][0], runs[("staged", 128)][0])
 
 
 @pytest.mark.parametrize("variant", ["staged", "fused"])
@@ -532,3 +578,30 @@ def test_segmented_packed_few_long_sequences_sampled():
             assert rel_l2(o[b, ts, h].double().cpu().numpy(), o_ref) <= 5e-3
         assert rel_l2(ht[n, h].double().cpu().numpy(), ht_ref) <= 1e-2 or not np.any(ht_ref)
     assert torch.equal(ht[1], torch.zeros_like(ht[1]))  # the empty sequence, no h0
+
+
+# ------------------------------------------------------------------ longest-first order
+@pytest.mark.parametrize("N,max_len", [(600, 40), (5000, 12)])
+def test_packed_many_short_sequences_longest_first(N, max_len):
+    """Packed batches of many short sequences (more than the 512 threads of a fused
+    workgroup, and more than 4096): the fused kernel runs them longest first when the
+    workspace holds their order, in index order without it.  The two give the same bits and
+    match the oracle per (sequence, head)."""
+    import gated_deltanet_chunked_02_amd as gdn
+    w = gdn_inputs.small(H=2, Hg=1, Dk=64, C=64, seed=N, h0_std=0.05, n_varlen=N,
+                         max_len=max_len)
+    inp = gdn_inputs.draw(w, device="cpu")
+    o_ref, ht_ref = oracle_full(inp)
+    o1, ht1 = run_gdn(inp, variant="fused")          # the binding brings the order workspace
+    dev = torch.device("cuda")
+    t = {n: inp[n].to(dev) for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")}
+    desc = gdn.make_desc(t["q"], t["v"], t["beta"], t["cu_seqlens"], 64, "fused")
+    assert gdn.gdn_chunk_fwd_workspace_size(desc) >= 4 * N
+    o2, ht2 = torch.empty_like(t["v"]), torch.empty_like(t["h0"])
+    st = gdn.gdn_chunk_fwd(desc, t["q"], t["k"], t["v"], t["g"], t["beta"], t["h0"],
+                           t["cu_seqlens"], inp["scale"], o2, ht2)   # no workspace
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+    po, ph = check_per_pair(inp, o1, ht1, o_ref, ht_ref, "many short N=%d" % N)
+    log(test="many_short", N=N, max_len=max_len, pair_o_max=po, pair_ht_max=ph)
