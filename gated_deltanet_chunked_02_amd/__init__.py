@@ -23,7 +23,7 @@ __all__ = [
     "GdnDesc", "GdnError", "load", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size",
     "gdn_stage_buffer", "gdn_status_string", "gdn_version", "chunk_gated_delta_rule",
     "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH", "gdn_resolved_variant",
-    "gdn_resolved_chunk",
+    "gdn_resolved_chunk", "gdn_chunk_fwd_noalloc",
     "GdnConvDesc", "gdn_causal_conv1d_fwd", "causal_conv1d", "ACTIVATIONS",
 ]
 
@@ -91,6 +91,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_resolved_variant.argtypes = [ctypes.POINTER(GdnDesc), P]
     lib.gdn_resolved_chunk.restype = ctypes.c_int32
     lib.gdn_resolved_chunk.argtypes = [ctypes.POINTER(GdnDesc), P]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = lib.gdn_chunk_fwd.argtypes
     lib.gdn_causal_conv1d_fwd.restype = ctypes.c_int
     lib.gdn_causal_conv1d_fwd.argtypes = [ctypes.POINTER(GdnConvDesc), P, P, P, P, P, P, P, P,
                                           P]
@@ -162,6 +164,20 @@ def gdn_chunk_fwd(desc: GdnDesc, q, k, v, g, beta, h0, cu_seqlens, scale, o, ht,
     return int(load().gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                     _ptr(beta), _ptr(h0), _ptr(cu_seqlens), float(scale),
                                     _ptr(o), _ptr(ht), stream))
+
+
+def gdn_chunk_fwd_noalloc(desc: GdnDesc, q, k, v, g, beta, h0, cu_seqlens, scale, o, ht,
+                          stream=None) -> int:
+    """Raw call of the allocation-free entry point: the library's own per-GPU device
+    scratch is the workspace (desc.workspace is ignored).  Returns the status code."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return int(load().gdn_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(g), _ptr(beta), _ptr(h0), _ptr(cu_seqlens),
+                                            float(scale), _ptr(o), _ptr(ht), stream))
 
 
 def _dtype_code(t) -> int:

@@ -28,7 +28,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["api.cpp", "stages.hip", "fused.hip", "segment.hip", "recurrent.hip", "conv1d.hip"]
+SOURCES = ["api.cpp", "stages.hip", "fused.hip", "segment.hip", "recurrent.hip", "conv1d.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

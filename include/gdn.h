@@ -194,6 +194,24 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
                          const int32_t* cu_seqlens, float scale, void* o, float* ht,
                          hipStream_t stream);
 
+/* Bytes of device scratch the library holds on each GPU for gdn_chunk_fwd_noalloc. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* gdn_chunk_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid it.  Same
+ * arguments, checks and results as gdn_chunk_fwd, except that d->workspace and
+ * d->workspace_bytes are ignored: the workspace is the library's own scratch, a static
+ * device array of GDN_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends (its address is looked up on the first call on a device).  A variant
+ * that needs more returns GDN_ERR_WORKSPACE; AUTO picks among what fits, as it does for
+ * any workspace.  Nothing is allocated and nothing needs clearing between calls.  Every
+ * call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other streams,
+ * other host threads) race and give unspecified results. */
+gdn_status gdn_chunk_fwd_noalloc(const gdn_desc* d, const void* q, const void* k,
+                                 const void* v, const float* g, const void* beta,
+                                 const float* h0, const int32_t* cu_seqlens, float scale,
+                                 void* o, float* ht, hipStream_t stream);
+
 /* Where intermediate `buf` lives inside the staged workspace (offset and size in bytes),
  * for stage-by-stage inspection (the page's section 7.4 debugging mode). */
 gdn_status gdn_stage_buffer(const gdn_desc* d, int32_t buf, size_t* offset, size_t* bytes);
