@@ -10,6 +10,9 @@ Low level (same names as the C ABI in include/gdn.h):
 High level (the call shape of the FlashQLA how-to, step 5.2):
     o, ht = chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
                                    output_final_state=True, cu_seqlens=None, chunk_size=128)
+The decode operator with its gates made in the kernel (low level
+gdn_fused_sigmoid_gating_delta_rule):
+    o, ht = fused_sigmoid_gating_delta_rule(q, k, v, a, b, A_log, dt_bias=None, ...)
 The short convolution before it (low level gdn_causal_conv1d_fwd):
     y = causal_conv1d(x, weight, bias=None, conv_state=None, cache_indices=None,
                       has_initial_state=None, cu_seqlens=None, activation=None)
@@ -23,7 +26,8 @@ __all__ = [
     "GdnDesc", "GdnError", "load", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size",
     "gdn_stage_buffer", "gdn_status_string", "gdn_version", "chunk_gated_delta_rule",
     "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH", "gdn_resolved_variant",
-    "gdn_resolved_chunk", "gdn_chunk_fwd_noalloc",
+    "gdn_resolved_chunk", "gdn_chunk_fwd_noalloc", "gdn_fused_sigmoid_gating_delta_rule",
+    "fused_sigmoid_gating_delta_rule",
     "GdnConvDesc", "gdn_causal_conv1d_fwd", "causal_conv1d", "ACTIVATIONS",
 ]
 
@@ -93,6 +97,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_resolved_chunk.argtypes = [ctypes.POINTER(GdnDesc), P]
     lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_chunk_fwd_noalloc.argtypes = lib.gdn_chunk_fwd.argtypes
+    lib.gdn_fused_sigmoid_gating_delta_rule.restype = ctypes.c_int
+    lib.gdn_fused_sigmoid_gating_delta_rule.argtypes = [
+        ctypes.POINTER(GdnDesc), P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P]
     lib.gdn_causal_conv1d_fwd.restype = ctypes.c_int
     lib.gdn_causal_conv1d_fwd.argtypes = [ctypes.POINTER(GdnConvDesc), P, P, P, P, P, P, P, P,
                                           P]
@@ -180,6 +187,19 @@ def gdn_chunk_fwd_noalloc(desc: GdnDesc, q, k, v, g, beta, h0, cu_seqlens, scale
                                             float(scale), _ptr(o), _ptr(ht), stream))
 
 
+def gdn_fused_sigmoid_gating_delta_rule(desc: GdnDesc, q, k, v, a, b, A_log, dt_bias, h0,
+                                        cu_seqlens, scale, o, ht, stream=None) -> int:
+    """Raw call of the decode operator with in-kernel gates; returns the status code."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return int(load().gdn_fused_sigmoid_gating_delta_rule(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+        _ptr(dt_bias), _ptr(h0), _ptr(cu_seqlens), float(scale), _ptr(o), _ptr(ht), stream))
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -219,7 +239,7 @@ def _check_devices(named, ref):
                   "%s must be on %s like the other tensors (got %s)" % (name, ref, t.device))
 
 
-def _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace):
+def _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace, devices=True):
     """Shapes, dtypes and devices of chunk_gated_delta_rule's tensors, checked before any
     pointer reaches the library (a host pointer or a short buffer read by a kernel would
     fault the GPU instead of raising)."""
@@ -242,8 +262,10 @@ def _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace):
     H, Dv = v.shape[2], v.shape[3]
     _need(Hg > 0 and H % Hg == 0, ValueError, "v heads (%d) must be a multiple of q/k heads "
           "(%d)" % (H, Hg))
-    _need(g.dtype == torch.float32, TypeError, "g must be fp32, got %s" % g.dtype)
-    _need(tuple(g.shape) == (B, T, H), ValueError, "g must be [B, T, H] = %s" % ((B, T, H),))
+    if g is not None:  # None: the decode operator, whose gates are made in the kernel
+        _need(g.dtype == torch.float32, TypeError, "g must be fp32, got %s" % g.dtype)
+        _need(tuple(g.shape) == (B, T, H), ValueError,
+              "g must be [B, T, H] = %s" % ((B, T, H),))
     _need(beta.dtype in (torch.bfloat16, torch.float32), TypeError,
           "beta must be bf16 or fp32, got %s" % beta.dtype)
     _need(tuple(beta.shape) == (B, T, H), ValueError,
@@ -262,7 +284,8 @@ def _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace):
     if workspace is not None:
         _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(), TypeError,
               "workspace must be a contiguous uint8 tensor")
-    _check_devices(named, q.device)
+    if devices:
+        _check_devices(named, q.device)
 
 
 def _validate_conv(x, weight, bias, conv_state, cache_indices, has_initial_state,
@@ -343,6 +366,60 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     st = gdn_chunk_fwd(desc, q, k, v, g, beta, initial_state, cu_seqlens, scale, o, ht)
     if st != 0:
         raise GdnError(st, "gdn_chunk_fwd")
+    return o, ht
+
+
+def fused_sigmoid_gating_delta_rule(q, k, v, a, b, A_log, dt_bias=None, scale=None,
+                                    initial_state=None, output_final_state=True,
+                                    cu_seqlens=None, inplace_final_state=False):
+    """The decode operator (token by token, gates made in the kernel) on the current stream:
+    g = -exp(A_log) softplus(a + dt_bias) and beta = sigmoid(b), then the gated delta rule.
+
+    q, k: [B, T, Hg, Dk]; v: [B, T, H, Dv]; a, b: [B, T, H] (bf16 or fp32, one dtype);
+    A_log, dt_bias: [H] fp32 (dt_bias may be None); initial_state [N, H, Dk, Dv] or None.
+    ``inplace_final_state``: write the final state into ``initial_state`` (fp32, contiguous)
+    instead of a new tensor, as a decode loop does.  Returns (o, final state or None)."""
+    import torch
+    _validate_gdn(q, k, v, None, b, initial_state, cu_seqlens, None, devices=False)
+    _need(isinstance(a, torch.Tensor) and a.dtype == b.dtype, TypeError,
+          "a must be a tensor of b's dtype")
+    _need(a.shape == b.shape, ValueError, "a must have b's shape [B, T, H]")
+    H = v.shape[2]
+    _need(isinstance(A_log, torch.Tensor) and A_log.dtype == torch.float32, TypeError,
+          "A_log must be an fp32 tensor")
+    _need(tuple(A_log.shape) == (H,), ValueError, "A_log must be [H] = [%d]" % H)
+    if dt_bias is not None:
+        _need(isinstance(dt_bias, torch.Tensor) and dt_bias.dtype == torch.float32, TypeError,
+              "dt_bias must be an fp32 tensor")
+        _need(tuple(dt_bias.shape) == (H,), ValueError, "dt_bias must be [H] = [%d]" % H)
+    if inplace_final_state:
+        _need(initial_state is not None and initial_state.dtype == torch.float32 and
+              initial_state.is_contiguous(), ValueError,
+              "inplace_final_state needs a contiguous fp32 initial_state")
+    _check_devices(dict(q=q, k=k, v=v, a=a, b=b, A_log=A_log, dt_bias=dt_bias,
+                        initial_state=initial_state, cu_seqlens=cu_seqlens), q.device)
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    a, b, A_log = a.contiguous(), b.contiguous(), A_log.contiguous()
+    if dt_bias is not None:
+        dt_bias = dt_bias.contiguous()
+    if cu_seqlens is not None:
+        cu_seqlens = cu_seqlens.to(torch.int32).contiguous()
+    desc = make_desc(q, v, b, cu_seqlens, 0, "recurrent")
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    if initial_state is not None and not inplace_final_state:
+        initial_state = initial_state.to(torch.float32).contiguous()
+    o = torch.empty_like(v)
+    ht = None
+    if inplace_final_state:
+        ht = initial_state
+    elif output_final_state:
+        ht = torch.empty((desc.N, desc.H, desc.Dk, desc.Dv), device=q.device,
+                         dtype=torch.float32)
+    st = gdn_fused_sigmoid_gating_delta_rule(desc, q, k, v, a, b, A_log, dt_bias,
+                                             initial_state, cu_seqlens, scale, o, ht)
+    if st != 0:
+        raise GdnError(st, "gdn_fused_sigmoid_gating_delta_rule")
     return o, ht
 
 

@@ -378,6 +378,54 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+gdn_status gdn_fused_sigmoid_gating_delta_rule(const gdn_desc* d, const void* q, const void* k,
+                                               const void* v, const void* a, const void* b,
+                                               const float* A_log, const float* dt_bias,
+                                               const float* h0, const int32_t* cu_seqlens,
+                                               float scale, void* o, float* ht,
+                                               hipStream_t stream) {
+  gdn::Problem p;
+  gdn_status s = check_desc(d, &p);
+  if (s != GDN_OK) return s;
+  if (d->variant != GDN_VARIANT_AUTO && d->variant != GDN_VARIANT_RECURRENT)
+    return GDN_ERR_UNSUPPORTED;
+  if (d->stop_after != 0) return GDN_ERR_INVALID_ARG;
+  if (!A_log) return GDN_ERR_INVALID_ARG;
+  if (p.Ttot > 0 && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARG;
+  const size_t ab = p.beta_f32 ? 4 : 2;  // a and b share beta's dtype
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(a, ab) || !aligned(b, ab) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
+      !aligned(h0, 16) || !aligned(ht, 16) || !aligned(cu_seqlens, 4))
+    return GDN_ERR_INVALID_ARG;
+  if (cu_seqlens) {
+    if (d->B != 1 || d->N < 0) return GDN_ERR_INVALID_ARG;
+    p.N = d->N;
+  } else if (d->N != 0 && d->N != d->B) {
+    return GDN_ERR_INVALID_ARG;
+  }
+  if (!recurrent_ok(p, d)) return GDN_ERR_UNSUPPORTED;
+  p.scale = scale;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = nullptr;
+  p.beta = b;
+  p.gate_a = a;
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.h0 = h0;
+  p.cu = cu_seqlens;
+  p.o = o;
+  p.ht = ht;
+  if (p.N == 0) return GDN_OK;
+  if (p.Ttot == 0) {
+    // no tokens: the states pass through (ht = h0, or zeros), as in gdn_chunk_fwd
+    if (!ht) return GDN_OK;
+    p.gate_a = nullptr;
+  }
+  return gdn::launch_recurrent(p, stream) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 gdn_status gdn_causal_conv1d_fwd(const gdn_conv_desc* d, const void* x, const float* weight,
                                  const float* bias, void* conv_state,
                                  const int32_t* cache_indices,

@@ -25,6 +25,12 @@ struct Problem {
   float* ht;
   int fused_flags = 0;  // kFused* bits, for the passes of the segmented variant
   const int32_t* order = nullptr;  // packed batch: sequence of each workgroup rank, or NULL
+  // Recurrent variant with the gates made in the kernel (the decode operator): raw per-token
+  // inputs a (in place of g) and b (in beta, same dtype) and per-head A_log, dt_bias (fp32;
+  // dt_bias may be NULL).  gate_a == NULL: g and beta are used as given.
+  const void* gate_a = nullptr;
+  const float* A_log = nullptr;
+  const float* dt_bias = nullptr;
 };
 
 // Fused-kernel modes used by the segmented variant's passes.

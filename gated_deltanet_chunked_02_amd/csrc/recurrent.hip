@@ -16,6 +16,11 @@
 // which is S <- e S (I - beta k k^T) + beta v k^T followed by o = scale S q, the gated
 // delta rule of the MegaGDN-PTO page's section 1.1, written per column of H.
 //
+// GATED: the decode operator of the TileLang × xLLM page (fused_sigmoid_gating_delta_rule)
+// also makes the gates in the kernel, from the raw per-token inputs a and b and the per-head
+// A_log and dt_bias: g = -exp(A_log) softplus(a + dt_bias) and beta = sigmoid(b), in fp32,
+// with softplus(x) = max(x, 0) + log1p(e^-|x|) (no overflow).
+//
 // Mapping: one wave per (sequence, head, 32-column slab of H).  Lane l = 8 rg + cg holds the
 // four columns 4 cg .. 4 cg + 3 of the slab for the R = D / 8 rows rg R .. rg R + R - 1, so a
 // row's 32 columns are 128 contiguous bytes read by 8 lanes.  The sums over the key index
@@ -57,13 +62,13 @@ template <> struct Vec4<bf16> {
 };
 
 // The inputs of one token as one lane needs them: its R rows of k and q, its four columns
-// of v, and the token's gate and beta.
-template <int R, typename E> struct TokenIn {
+// of v, and the token's gate and beta (GATED: the raw inputs a and b, in beta's dtype).
+template <int R, typename E, bool GATED> struct TokenIn {
   typename Vec4<E>::raw k[R / 4], q[R / 4], v;
   float g, b;
 
   __device__ __forceinline__ void load(const E* __restrict__ qp, const E* __restrict__ kp,
-                                       const E* __restrict__ vp, const float* __restrict__ gp,
+                                       const E* __restrict__ vp, const void* __restrict__ gp,
                                        const void* __restrict__ bp, int beta_f32, long qk_off,
                                        long v_off, long gi) {
 #pragma unroll
@@ -72,8 +77,8 @@ template <int R, typename E> struct TokenIn {
       q[i] = Vec4<E>::load(qp + qk_off + 4 * i);
     }
     v = Vec4<E>::load(vp + v_off);
-    g = gp[gi];
-    b = beta_f32 ? static_cast<const float*>(bp)[gi] : (float)static_cast<const bf16*>(bp)[gi];
+    g = GATED ? load_beta(gp, beta_f32, gi) : static_cast<const float*>(gp)[gi];
+    b = load_beta(bp, beta_f32, gi);
   }
 };
 
@@ -85,12 +90,14 @@ __device__ __forceinline__ float row_group_sum(float x) {
   return x;
 }
 
-template <int D, typename E>
+template <int D, typename E, bool GATED>
 __global__ __launch_bounds__(64) void k_recurrent(const E* __restrict__ q,
                                                   const E* __restrict__ k,
                                                   const E* __restrict__ v,
-                                                  const float* __restrict__ g,
+                                                  const void* __restrict__ g,
                                                   const void* __restrict__ beta, int beta_f32,
+                                                  const float* __restrict__ A_log,
+                                                  const float* __restrict__ dt_bias,
                                                   const float* __restrict__ h0,
                                                   const int32_t* __restrict__ cu,
                                                   E* __restrict__ o, float* __restrict__ ht,
@@ -106,6 +113,13 @@ __global__ __launch_bounds__(64) void k_recurrent(const E* __restrict__ q,
   const int rg = lane >> 3, cg = lane & 7;
   const int row0 = rg * R;
   const int col = slab * kSlab + 4 * cg;
+
+  // GATED: the head's decay rate exp(A_log) and step-size bias
+  float rate = 0.f, dtb = 0.f;
+  if constexpr (GATED) {
+    rate = __expf(A_log[h]);
+    if (dt_bias) dtb = dt_bias[h];
+  }
 
   int bos, eos;
   if (cu) {
@@ -129,10 +143,10 @@ __global__ __launch_bounds__(64) void k_recurrent(const E* __restrict__ q,
   // token t's inputs are in `cur`; token t + 1's are loaded while t is computed
   auto qk_off = [&](int t) { return ((long)t * Hg + hk) * D + row0; };
   auto v_off = [&](int t) { return ((long)t * H + h) * D + col; };
-  TokenIn<R, E> cur;
+  TokenIn<R, E, GATED> cur;
   if (bos < eos) cur.load(q, k, v, g, beta, beta_f32, qk_off(bos), v_off(bos), (long)bos * H + h);
   for (int t = bos; t < eos; ++t) {
-    TokenIn<R, E> nxt;
+    TokenIn<R, E, GATED> nxt;
     if (t + 1 < eos)
       nxt.load(q, k, v, g, beta, beta_f32, qk_off(t + 1), v_off(t + 1), (long)(t + 1) * H + h);
     float kr[R], qr[R];
@@ -144,8 +158,13 @@ __global__ __launch_bounds__(64) void k_recurrent(const E* __restrict__ q,
       qr[4 * i] = b.x; qr[4 * i + 1] = b.y; qr[4 * i + 2] = b.z; qr[4 * i + 3] = b.w;
     }
     const float4 vt = Vec4<E>::wide(cur.v);
-    const float e = __builtin_amdgcn_exp2f(cur.g * 1.4426950408889634f);  // exp(g)
-    const float bt = cur.b;
+    float gl = cur.g, bt = cur.b;
+    if constexpr (GATED) {
+      const float x = cur.g + dtb;
+      gl = -rate * (fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));  // -exp(A_log) softplus(x)
+      bt = 1.f / (1.f + __expf(-cur.b));                         // sigmoid(b)
+    }
+    const float e = __builtin_amdgcn_exp2f(gl * 1.4426950408889634f);  // exp(g)
 
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f, qk = 0.f;
@@ -196,14 +215,19 @@ __global__ __launch_bounds__(64) void k_recurrent(const E* __restrict__ q,
   }
 }
 
+template <int D, typename E, bool GATED>
+hipError_t launch_g(const Problem& p, hipStream_t st) {
+  const long waves = (long)p.N * p.H * (D / kSlab);
+  k_recurrent<D, E, GATED><<<dim3((unsigned)waves), dim3(64), 0, st>>>(
+      static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v),
+      GATED ? p.gate_a : static_cast<const void*>(p.g), p.beta, p.beta_f32 ? 1 : 0, p.A_log,
+      p.dt_bias, p.h0, p.cu, static_cast<E*>(p.o), p.ht, p.T, p.Ttot, p.H, p.Hg, p.scale);
+  return hipGetLastError();
+}
+
 template <int D, typename E>
 hipError_t launch_d(const Problem& p, hipStream_t st) {
-  const long waves = (long)p.N * p.H * (D / kSlab);
-  k_recurrent<D, E><<<dim3((unsigned)waves), dim3(64), 0, st>>>(
-      static_cast<const E*>(p.q), static_cast<const E*>(p.k), static_cast<const E*>(p.v), p.g,
-      p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, static_cast<E*>(p.o), p.ht, p.T, p.Ttot, p.H,
-      p.Hg, p.scale);
-  return hipGetLastError();
+  return p.gate_a ? launch_g<D, E, true>(p, st) : launch_g<D, E, false>(p, st);
 }
 
 template <typename E>

@@ -169,3 +169,24 @@ def draw_conv(w: ConvWorkload, device="cpu"):
     return dict(x=x, weight=weight, bias=bias, conv_state=state, cache_indices=idx,
                 has_initial_state=None, cu_seqlens=None, activation=w.activation,
                 workload=w)
+
+
+# ---------------------------------------------------------------- decode gate inputs
+def draw_gating(w: Workload, B: int, T: int, device="cpu"):
+    """Raw gate inputs of the decode operator with the sigmoid-gate parametrisation, for a
+    [B, T] token layout (that of ``draw(w)``'s g: a packed batch has B = 1 and T = its total)
+    and the heads of workload ``w``.  Own generator (seed + 1000), draw order a, b, A_log,
+    dt_bias:
+      * a ~ N(0, 1) and b ~ N(0, 1) per token and value head, cast to the beta dtype;
+      * A_log = log(U(1, 16)) per value head (decay rates spread over a decade), fp32;
+      * dt_bias ~ N(-4, 0.5^2) per value head, fp32 (small step sizes, so the per-token
+        decay is mild, like the log-decays of the chunked workloads)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 1000)
+    bdt = DTYPES[w.beta_dtype or w.dtype]
+    a = torch.randn((B, T, w.H), generator=gen, device=dev).to(bdt)
+    b = torch.randn((B, T, w.H), generator=gen, device=dev).to(bdt)
+    A_log = torch.log(torch.rand((w.H,), generator=gen, device=dev) * 15.0 + 1.0)
+    dt_bias = torch.randn((w.H,), generator=gen, device=dev) * 0.5 - 4.0
+    return dict(a=a, b=b, A_log=A_log, dt_bias=dt_bias)

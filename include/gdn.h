@@ -194,6 +194,30 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
                          const int32_t* cu_seqlens, float scale, void* o, float* ht,
                          hipStream_t stream);
 
+/* The decode operator with its gates made in the kernel (fused_sigmoid_gating_delta_rule,
+ * the TileLang × xLLM page's section on the three core operators: the sigmoid activation,
+ * the gate computation from A_log, the decay rate, and the delta-rule state update in one
+ * kernel).  The page prints no formula; the reading is, per token t and value head h,
+ *
+ *     g_t    = -exp(A_log[h]) * softplus(a_t + dt_bias[h]),   softplus(x) = log(1 + e^x)
+ *     beta_t = sigmoid(b_t) = 1 / (1 + e^-b_t)
+ *
+ * followed by exactly the recurrence of gdn_chunk_fwd with these g and beta, token by token
+ * (the recurrent variant's kernel, the gates made in fp32 in the same kernel).
+ *   a, b        [B, T, H]   d->beta_dtype (bf16 or f32): raw gate and beta inputs
+ *   A_log       [H] f32     log of each head's decay rate (required)
+ *   dt_bias     [H] f32     added to a before softplus, or NULL (zero)
+ * Every other argument, layout and rule as for gdn_chunk_fwd (h0 and ht may be the same
+ * buffer: the state is then updated in place, as a decode loop wants).  d->variant must be
+ * GDN_VARIANT_AUTO or GDN_VARIANT_RECURRENT (else GDN_ERR_UNSUPPORTED); d->chunk is
+ * ignored; no workspace. */
+gdn_status gdn_fused_sigmoid_gating_delta_rule(const gdn_desc* d, const void* q, const void* k,
+                                               const void* v, const void* a, const void* b,
+                                               const float* A_log, const float* dt_bias,
+                                               const float* h0, const int32_t* cu_seqlens,
+                                               float scale, void* o, float* ht,
+                                               hipStream_t stream);
+
 /* Bytes of device scratch the library holds on each GPU for gdn_chunk_fwd_noalloc. */
 #define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

@@ -359,3 +359,61 @@ def test_fused_packed_batch_asks_for_its_order(lib):
     assert gdn.gdn_chunk_fwd_workspace_size(desc(B=1, N=1, T=4096, variant=2)) == 0
     # beyond 65536 sequences they run in index order, without workspace
     assert gdn.gdn_chunk_fwd_workspace_size(desc(B=1, N=70000, T=1 << 22, variant=2)) == 0
+
+
+def test_gating_entry_rejects_bad_arguments_before_any_launch(lib):
+    A = 0x10000  # fake, aligned: every case below must fail before any launch
+
+    def call(dd=None, **kw):
+        args = dict(q=A, k=A, v=A, a=A, b=A, A_log=A, dt_bias=None, h0=None, cu=None, o=A,
+                    ht=None)
+        args.update(kw)
+        return lib.gdn_fused_sigmoid_gating_delta_rule(
+            ctypes.byref(dd or desc()), args["q"], args["k"], args["v"], args["a"], args["b"],
+            args["A_log"], args["dt_bias"], args["h0"], args["cu"], 0.1, args["o"],
+            args["ht"], None)
+
+    assert call(desc(variant=2)) == 2                     # only AUTO or RECURRENT
+    assert call(desc(variant=1)) == 2
+    assert call(desc(stop_after=1)) == 1
+    assert call(A_log=None) == 1
+    assert call(a=None) == 1 and call(b=None) == 1 and call(q=None) == 1
+    assert call(a=A + 1) == 1                             # bf16 a needs 2-byte alignment
+    assert call(desc(beta_dtype=0), b=A + 2) == 1         # fp32 b needs 4 bytes
+    assert call(dt_bias=A + 2) == 1
+    assert call(desc(N=3)) == 1                           # dense: N must equal B
+    assert call(desc(B=2, N=2), cu=A) == 1                # packed needs B == 1
+    assert call(desc(Dk=96, Dv=96)) == 2
+    assert call(desc(B=1, N=0, T=0), cu=A) == 0           # no sequences: nothing to do
+
+
+def _gating_args(**over):
+    import torch
+    a = gdn_args()
+    a.update(a=torch.zeros(1, 8, 4, dtype=torch.bfloat16), A_log=torch.zeros(4),
+             dt_bias=None)
+    a.update(over)
+    return a
+
+
+def test_gating_binding_validates_its_tensors(lib):
+    import torch
+    bad = [
+        (dict(a=torch.zeros(1, 8, 4)), TypeError),                      # a dtype != b dtype
+        (dict(a=torch.zeros(1, 8, 2, dtype=torch.bfloat16)), ValueError),  # a shape
+        (dict(A_log=torch.zeros(4, dtype=torch.float64)), TypeError),
+        (dict(A_log=torch.zeros(3)), ValueError),
+        (dict(dt_bias=torch.zeros(4, dtype=torch.bfloat16)), TypeError),
+        (dict(dt_bias=torch.zeros(2)), ValueError),
+        (dict(beta=torch.zeros(1, 8, 4, dtype=torch.float16)), TypeError),
+        (dict(), ValueError),                                           # host tensors
+    ]
+    for over, exc in bad:
+        a = _gating_args(**over)
+        with pytest.raises(exc):
+            gdn.fused_sigmoid_gating_delta_rule(a["q"], a["k"], a["v"], a["a"], a["beta"],
+                                                a["A_log"], a["dt_bias"])
+    a = _gating_args()
+    with pytest.raises(ValueError):
+        gdn.fused_sigmoid_gating_delta_rule(a["q"], a["k"], a["v"], a["a"], a["beta"],
+                                            a["A_log"], inplace_final_state=True)

@@ -555,3 +555,104 @@ def test_backward_planted_sign_error_is_caught():
             _loss_and_grads(case, scale=1.0, seed=1)
     finally:
         bw._pair_backward = orig
+
+
+# ------------------------------------------------------------------ decode gating (f2)
+from oracle import gating  # noqa: E402
+
+
+def test_gating_functions_match_library_routines_everywhere():
+    import scipy.special
+    x = np.concatenate([np.linspace(-800, 800, 4001), [-1e-300, 0.0, 1e-300, 35.0, -35.0]])
+    # softplus(x) = log(e^0 + e^x): numpy's logaddexp; sigmoid: scipy's expit
+    assert np.allclose(gating.softplus(x), np.logaddexp(0.0, x), rtol=1e-14, atol=0)
+    assert np.allclose(gating.sigmoid(x), scipy.special.expit(x), rtol=1e-14, atol=1e-300)
+    assert np.all(np.isfinite(gating.softplus(x))) and np.all(np.isfinite(gating.sigmoid(x)))
+
+
+def test_gating_identities():
+    x = np.linspace(-30, 30, 601)
+    close(gating.softplus(x) - gating.softplus(-x), x, 1e-12)   # softplus is x + s(-x)
+    close(gating.sigmoid(x) + gating.sigmoid(-x), np.ones_like(x), 1e-15)
+    h = 1e-6                                                             # d softplus = sigmoid
+    close((gating.softplus(x + h) - gating.softplus(x - h)) / (2 * h), gating.sigmoid(x), 1e-8)
+    assert gating.softplus(0.0) == np.log(2.0) and gating.sigmoid(0.0) == 0.5
+
+
+def test_gates_closed_forms():
+    z = np.zeros((1, 3, 2))
+    g, beta = gating.gates(z, z, np.zeros(2))
+    close(g, np.full_like(g, -np.log(2.0)), 1e-15)
+    close(beta, np.full_like(beta, 0.5), 1e-15)
+    # the rate exp(A_log) multiplies; dt_bias shifts a; both per head
+    A_log = np.array([np.log(3.0), 0.0])
+    dt_bias = np.array([0.0, 2.0])
+    a = np.full((1, 1, 2), -2.0)
+    g, _ = gating.gates(a, np.zeros((1, 1, 2)), A_log, dt_bias)
+    close(g[0, 0], np.array([-3.0 * np.log1p(np.exp(-2.0)), -np.log(2.0)]), 1e-15)
+    # a vanishing rate gives no decay whatever a is; the decay e^g always lies in (0, 1]
+    g, _ = gating.gates(np.full((1, 4, 1), 40.0), np.zeros((1, 4, 1)), np.array([-800.0]))
+    assert np.all(g == 0.0)
+    rng = np.random.default_rng(3)
+    g, beta = gating.gates(rng.standard_normal((2, 50, 4)) * 5, rng.standard_normal((2, 50, 4)),
+                           rng.standard_normal(4), rng.standard_normal(4))
+    assert np.all(g < 0) and np.all((beta > 0) & (beta < 1))
+
+
+def test_gated_recurrence_hand_worked_token():
+    """One token, Dk = Dv = 2, h0 = I, k = (1, 0), q = (0, 1), v = (2, 3), scale 1,
+    A_log = a = dt_bias = b = 0: e^g = exp(-ln 2) = 1/2 and beta = 1/2, so
+    S1 = 1/2 I (I - 1/2 k k^T) + 1/2 v k^T = [[1/4 + 1, 0], [3/2, 1/2]],
+    o = S1 q = (0, 1/2) and ht = S1^T."""
+    q = np.array([0.0, 1.0]).reshape(1, 1, 1, 2)
+    k = np.array([1.0, 0.0]).reshape(1, 1, 1, 2)
+    v = np.array([2.0, 3.0]).reshape(1, 1, 1, 2)
+    z = np.zeros((1, 1, 1))
+    h0 = np.eye(2).reshape(1, 1, 2, 2)
+    o, ht = gating.gated_recurrence(q, k, v, z, z, np.zeros(1), np.zeros(1), h0, scale=1.0)
+    close(o[0, 0, 0], np.array([0.0, 0.5]), 1e-15)
+    close(ht[0, 0], np.array([[1.25, 1.5], [0.0, 0.5]]), 1e-15)
+
+
+@pytest.mark.parametrize("mutation", ["rate_not_exponentiated", "beta_not_activated",
+                                      "bias_ignored", "decay_sign"])
+def test_gating_planted_mistakes_are_caught(mutation):
+    """Copies of the gate map with one plausible slip each disagree with the closed forms."""
+    def wrong(a, b, A_log, dt_bias):
+        x = a + dt_bias
+        if mutation == "rate_not_exponentiated":
+            return -A_log * gating.softplus(x), gating.sigmoid(b)
+        if mutation == "beta_not_activated":
+            return -np.exp(A_log) * gating.softplus(x), b
+        if mutation == "bias_ignored":
+            return -np.exp(A_log) * gating.softplus(a), gating.sigmoid(b)
+        return np.exp(A_log) * gating.softplus(x), gating.sigmoid(b)
+    A_log = np.array([np.log(3.0)])
+    dt_bias = np.array([2.0])
+    a = np.full((1, 1, 1), -2.0)
+    b = np.full((1, 1, 1), 0.7)
+    g_ok, b_ok = gating.gates(a, b, A_log, dt_bias)
+    close(g_ok, np.full_like(g_ok, -3.0 * np.log(2.0)), 1e-15)       # softplus(0) = ln 2
+    close(b_ok, np.full_like(b_ok, 1.0 / (1.0 + np.exp(-0.7))), 1e-15)
+    g_bad, b_bad = wrong(a, b, A_log, dt_bias)
+    assert not (np.allclose(g_bad, g_ok) and np.allclose(b_bad, b_ok))
+
+
+def test_gated_recurrence_is_the_recurrence_with_mapped_gates():
+    """With g and beta from the gate map given directly, the plain recurrence agrees, and a
+    vanishing rate with b -> +inf is the undecayed full-overwrite delta rule."""
+    q, k, v, _, _, h0 = rand_case(31, B=2, T=9, H=4, Hg=2)
+    rng = np.random.default_rng(32)
+    a, b = rng.standard_normal((2, 9, 4)), rng.standard_normal((2, 9, 4))
+    A_log, dt_bias = np.log(rng.uniform(1, 16, 4)), rng.standard_normal(4)
+    o, ht = gating.gated_recurrence(q, k, v, a, b, A_log, dt_bias, h0)
+    g = -np.exp(A_log) * np.logaddexp(0.0, a + dt_bias)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    o2, ht2 = oracle.recurrence(q, k, v, g, beta, h0)
+    close(o, o2, 1e-13)
+    close(ht, ht2, 1e-13)
+    big = np.full_like(b, 800.0)
+    o3, ht3 = gating.gated_recurrence(q, k, v, a, big, np.full(4, -800.0), None, h0)
+    o4, ht4 = oracle.recurrence(q, k, v, np.zeros_like(a), np.ones_like(b), h0)
+    close(o3, o4, 1e-13)
+    close(ht3, ht4, 1e-13)
