@@ -133,8 +133,10 @@ def cpu_baseline(inp, o_gpu, ht_gpu, budget_s: float):
     res = oracle_pairs(inp, first + more, nthreads=threads)
     t_sample = time.perf_counter() - t0
     npairs = len(res)
-    # whole-job estimate: the oracle's time scales with (sequence, head) pairs
-    t_job = t_sample * len(all_pairs) / npairs
+    # whole-job estimate: the oracle's time scales with the token-heads it steps through
+    # (the pairs of a packed batch differ in length)
+    sampled_th = sum(o_ref.shape[0] for o_ref, _ in res.values())
+    t_job = t_sample * (B * T * H) / max(sampled_th, 1)
     value = B * T / t_job
     errs_o, errs_h = [], []
     o64 = None
@@ -148,7 +150,7 @@ def cpu_baseline(inp, o_gpu, ht_gpu, budget_s: float):
         # the oracle's parallel loop runs over the sampled pairs
         "value": value, "unit": "tokens/s", "cores": min(threads, npairs), "kind": "oracle",
         "sample": "%d of %d (sequence, head) pairs at full length, fp64 token recurrence "
-                  "(C, gcc -O3 -march=native, OpenMP), %.1f s; scaled by pairs to the "
+                  "(C, gcc -O3 -march=native, OpenMP), %.1f s; scaled by token-heads to the "
                   "whole job" % (npairs, len(all_pairs), t_sample),
         "cpu_model": oracle.cpu_model(), "host_threads_available": cores,
         "sample_seconds": t_sample,
@@ -250,6 +252,9 @@ def main():
                     help="override an integer field of the workload (e.g. H=16, T=4096)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--gated", action="store_true",
+                    help="time the decode operator with in-kernel gates "
+                         "(gdn_fused_sigmoid_gating_delta_rule) on the workload's tokens")
     ap.add_argument("--mode", default="gdn", choices=["gdn", "copy"],
                     help="copy: time a plain 1 GiB device-to-device copy (the reference "
                          "kernel for scaling HBM byte counters)")
@@ -281,6 +286,10 @@ def main():
     inp = gdn_inputs.draw(w, device=dev)
     q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))
     h0, cu = inp["h0"], inp["cu_seqlens"]
+    gate_in = None
+    if args.gated:
+        gate_in = gdn_inputs.draw_gating(w, g.shape[0], g.shape[1], device=dev)
+        args.variant = "recurrent"
     desc = gdn.make_desc(q, v, beta, cu, w.C, args.variant)
     o = torch.empty_like(v)
     ht = torch.empty((desc.N, desc.H, desc.Dk, desc.Dv), device=dev, dtype=torch.float32)
@@ -294,7 +303,12 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        st = gdn.gdn_chunk_fwd(desc, q, k, v, g, beta, h0, cu, inp["scale"], o, ht, stream)
+        if gate_in is not None:
+            st = gdn.gdn_fused_sigmoid_gating_delta_rule(
+                desc, q, k, v, gate_in["a"], gate_in["b"], gate_in["A_log"],
+                gate_in["dt_bias"], h0, cu, inp["scale"], o, ht, stream)
+        else:
+            st = gdn.gdn_chunk_fwd(desc, q, k, v, g, beta, h0, cu, inp["scale"], o, ht, stream)
         if st != 0:
             raise gdn.GdnError(st, "gdn_chunk_fwd")
 
@@ -318,6 +332,8 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
 
     by, fl = algorithmic_work(inp, variant, c_run)
+    if gate_in is not None:  # a and b replace g and beta; A_log and dt_bias per head
+        by += (gate_in["a"].element_size() - 4) * gate_in["a"].numel() + 8 * w.H
     avg_ms = float(np.mean(launch_ms))
     gbs = by / (avg_ms * 1e-3) / 1e9
     tfl = fl / (avg_ms * 1e-3) / 1e12
@@ -328,7 +344,8 @@ def main():
     elif variant == "segmented":
         kernel = "segmented: three k_fused passes over the segments and the segment scan"
     elif variant == "recurrent":
-        kernel = "k_recurrent (D=%d, one wave per 32 state columns)" % w.Dk
+        kernel = "k_recurrent%s (D=%d, one wave per 32 state columns)" % (
+            "<gated>" if gate_in is not None else "", w.Dk)
     else:
         kernel = "k_fused (D=%d, %d-token chunks)" % (w.Dk, c_run)
     if bound == "hbm":
@@ -347,10 +364,18 @@ def main():
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        if gate_in is not None:
+            # the oracle's gate map first (fp64), then the same timed token recurrence
+            from oracle import gating
+            gg, bb = gating.gates(gate_in["a"].cpu(), gate_in["b"].cpu(),
+                                  gate_in["A_log"].cpu(), gate_in["dt_bias"].cpu())
+            inp = dict(inp, g=torch.from_numpy(gg), beta=torch.from_numpy(bb))
         cpu = cpu_baseline(inp, o, ht, args.cpu_budget)
 
     out = {
-        "metric": metric_for(w), "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "metric": ("GDN gated decode (sigmoid gating in the kernel) tokens/s at 1 MI355X "
+                   "(%d×%d, H=%d, Hg=%d, D=%d, %s)" % (w.B, w.T, w.H, w.Hg, w.Dk, w.dtype)
+                   if gate_in is not None else metric_for(w)), "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32", "data": "synthetic",

@@ -23,11 +23,11 @@
 // where the 16 x 16 diagonal inverses come from the nilpotent product
 // (I + A_ii)^-1 = (I - A_ii)(I + A_ii^2)(I + A_ii^4)(I + A_ii^8) on the matrix cores.
 //
-// The tiles (A~, T_ii diag(beta), the gated Q K^T) are fp16: they depend on q, k, g and beta
-// only and are bounded for keys with beta |k|^2 <= 2 and |q| |k| scale < 2^15 (L2-normalised
-// q and k).  The substitution operands R and v_new are fp16 too, but scale with v and h0, so
-// each wave carries them multiplied by a power of two chosen per chunk from its largest |R|
-// (exact, undone in fp32): any bf16 magnitude of v and h0 keeps the fp16 precision.
+// The matrix-core operands of the substitution and the output (the tiles -A~, T_ii diag(beta)
+// and the gated Q K^T, the right-hand sides and v_new) are bf16, whose exponent range is
+// fp32's: they hold any magnitude of v and h0 that bf16 inputs can carry.  Only the power
+// series of T_ii, whose factors are bounded for keys with beta |k|^2 <= 2 (L2-normalised
+// keys), runs in fp16 for its three extra mantissa bits.
 //
 // The state-independent work of a chunk (its lower 16 x 16 tiles of K K^T and Q K^T, gated
 // and masked, the inverses T_ii and the gate vectors) is done one chunk ahead, by waves 0-3
@@ -137,6 +137,9 @@ __device__ __forceinline__ constexpr int tix(int ti, int tj) {
 __device__ __forceinline__ f32x4 mma16h(f16x4 a, f16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mma16b(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mma32b(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -186,8 +189,8 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
   __shared__ __align__(16) bf16 SK[3][F::TILE];
   __shared__ __align__(16) bf16 SQ[3][F::TILE];
   __shared__ __align__(16) bf16 SV[2][F::TILEV];
-  __shared__ __align__(16) f16 SA[2][F::NLOW * TE];  // -A~ below the diagonal, T_ii diag(beta) on it
-  __shared__ __align__(16) f16 SP[2][F::NLOW * TE];  // scale (Q K^T * e^{Gc_i-Gc_j})_{i>=j}
+  __shared__ __align__(16) bf16 SA[2][F::NLOW * TE];  // -A~ below the diagonal, T_ii diag(beta) on it
+  __shared__ __align__(16) bf16 SP[2][F::NLOW * TE];  // scale (Q K^T * e^{Gc_i-Gc_j})_{i>=j}
   // Gate vectors, made by one wave two chunks ahead (buffer = chunk % 3), per token t:
   __shared__ __align__(16) float SGC[3][CS];  // Gc_t log2(e)
   __shared__ __align__(16) float SBT[3][CS];  // beta_t
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
         nfm[e] = (j > r16 ? -bc[e] * decm : 0.f) * aa[e];
         pf[e] = (r16 >= j ? scale * dec : 0.f) * pa[e];
       }
-      if constexpr (OUT) *reinterpret_cast<f16x4*>(&SP[ob][tix<F>(b, b) + r16 * RS + g4]) = to_h(pf);
+      if constexpr (OUT) *reinterpret_cast<bf16x4*>(&SP[ob][tix<F>(b, b) + r16 * RS + g4]) = to_b(pf);
       const f16x4 nt = to_h(nf), nn = to_h(nfm);
       // T = (I + N)(I + N^2)(I + N^4)(I + N^8): a product X Y takes X^T and Y in
       // accumulator form, so both orientations of each power are kept; T^T is built, whose
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
       const f32x4 y1 = mma16h(h2, nt, eye + nf + n2t);   // (I + N^2)^T (I + N)^T
       const f32x4 y2 = mma16h(h4, to_h(y1), y1);         // (I + (N^4)^T) Y1
       const f32x4 y3 = mma16h(h8, to_h(y2), y2);         // (I + (N^8)^T) Y2 = T^T
-      *reinterpret_cast<f16x4*>(&SA[ob][tix<F>(b, b) + r16 * RS + g4]) = to_h(y3 * bc);
+      *reinterpret_cast<bf16x4*>(&SA[ob][tix<F>(b, b) + r16 * RS + g4]) = to_b(y3 * bc);
     };
     // Off-diagonal tile (bi, bj), bj < bi: K K^T -> -A~ (kind 0) or Q K^T -> P (kind 1).
     // Each wave's products are fixed at compile time and all its fragment reads come before
@@ -390,8 +393,8 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           x[e] = f * __builtin_amdgcn_exp2f(fminf(Gi - Gj[e], 0.f)) * acc[u][e];
-        f16* dst = kd_[u] ? SP[ob] : SA[ob];
-        *reinterpret_cast<f16x4*>(dst + tix<F>(bi_[u], bj_[u]) + r16 * RS + g4) = to_h(x);
+        bf16* dst = kd_[u] ? SP[ob] : SA[ob];
+        *reinterpret_cast<bf16x4*>(dst + tix<F>(bi_[u], bj_[u]) + r16 * RS + g4) = to_b(x);
       }
     };
     // The twelve products in four shares of three, grouped so that each share reuses
@@ -505,8 +508,8 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
     const bf16* Kc = SK[kb];
     const bf16* Qc = SQ[kb];
     const bf16* vt = SV[tb] + vtoff;
-    const f16* Ac = SA[tb] + r16 * RS + g4;
-    const f16* Pc = SP[tb] + r16 * RS + g4;
+    const bf16* Ac = SA[tb] + r16 * RS + g4;
+    const bf16* Pc = SP[tb] + r16 * RS + g4;
     const float* efp = SEF[kb] + g4;
     const float* eop = SEO[kb] + r16;
     const float* dcp = SDC[kb] + g4;
@@ -550,48 +553,27 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
         }
       }
     }
-    // R / beta = V - e^Gc (K h) of every block, in place of K h: lane (l%16, g) holds
-    // tokens 4 g + e of column 16 w + l%16
+    // forward substitution, outputs and the update operands, block by block.  The tiles
+    // and v_new enter the matrix cores as bf16, whose exponent range is fp32's: any magnitude
+    // of v and h0 that bf16 holds stays representable (and each value keeps its own
+    // exponent, so large and small values side by side keep their relative precision).
+    bf16x4 vnb[NB], vb[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+      // R / beta - sum_{j<b} A~_bj v_j = V - e^Gc (K h) + sum_{j<b} (-A~_bj) v_j: lane
+      // (l%16, g) holds tokens 4 g + e of column 16 w + l%16
       const bf16x4 vv = read_tr<bf16x4>(vt + b * 16 * DV);
       const f32x4 ef = *reinterpret_cast<const f32x4*>(efp + 16 * b);
+      f32x4 acc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) xk[b][e] = fmaf(-ef[e], xk[b][e], (float)vv[e]);
-    }
-    // The substitution and output operands are fp16 (range 2^-14 .. 65504), while v and h0
-    // may hold any bf16 magnitude.  The value side of the chunk (R, v_new) is therefore
-    // carried scaled by a power of two s, one per wave and chunk, that brings the largest
-    // |R| of the wave's 16 columns into [1, 2): exact (no rounding) and undone in fp32
-    // before o and the state update.  Every quantity of the value side is linear in
-    // (v, h0), so the scaled chunk stays a bounded multiple of that largest |R|.
-    float vs, vsi;
-    {
-      uint32_t m = 0;
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m = max(m, __builtin_bit_cast(uint32_t, fabsf(xk[b][e])));
-      // biased exponent of the largest |R|, clamped so that s and 1 / s are normal floats
-      // (zero or denormal R: s = 2^126, where every scaled value is still below 1)
-      const int ex = min(max((int)(wave_max_u32(m) >> 23), 1), 253);
-      vs = __builtin_bit_cast(float, (uint32_t)(254 - ex) << 23);   // 2^(127 - ex)
-      vsi = __builtin_bit_cast(float, (uint32_t)ex << 23);          // 2^(ex - 127)
-    }
-    // forward substitution, outputs and the update operands, block by block
-    f16x4 vhh[NB];
-    bf16x4 vb[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      // s (R / beta - sum_{j<b} A~_bj v_j) = s R / beta + sum_{j<b} (-A~_bj) (s v_j)
-      f32x4 acc = xk[b] * vs;
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(-ef[e], xk[b][e], (float)vv[e]);
 #pragma unroll
       for (int j = 0; j < b; ++j)
-        acc = mma16h(*reinterpret_cast<const f16x4*>(Ac + tix<F>(b, j)), vhh[j], acc);
-      // s v_b = T_bb diag(beta) (...)
+        acc = mma16b(*reinterpret_cast<const bf16x4*>(Ac + tix<F>(b, j)), vnb[j], acc);
+      // v_b = T_bb diag(beta) (...)
       const f32x4 vn =
-          mma16h(*reinterpret_cast<const f16x4*>(Ac + tix<F>(b, b)), to_h(acc), zero4());
-      vhh[b] = to_h(vn);
+          mma16b(*reinterpret_cast<const bf16x4*>(Ac + tix<F>(b, b)), to_b(acc), zero4());
+      vnb[b] = to_b(vn);
       // o^T = scale e^Gc Y^T + sum_{j<=b} v_j^T (scale P_bj)^T: lane (l%16, g) holds token
       // 16 b + l%16, columns 16 w + 4 g .. + 3, stored as one 8-byte word (pairs converted
       // as 32-bit words: this compiler turns an element read of a converted 16-bit vector
@@ -600,17 +582,17 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
         f32x4 z = zero4();
 #pragma unroll
         for (int j = 0; j <= b; ++j)
-          z = mma16h(vhh[j], *reinterpret_cast<const f16x4*>(Pc + tix<F>(b, j)), z);
+          z = mma16b(vnb[j], *reinterpret_cast<const bf16x4*>(Pc + tix<F>(b, j)), z);
         const float egt = eop[16 * b];
-        const f32x2_t o01 = {fmaf(egt, yq[b][0], z[0] * vsi), fmaf(egt, yq[b][1], z[1] * vsi)};
-        const f32x2_t o23 = {fmaf(egt, yq[b][2], z[2] * vsi), fmaf(egt, yq[b][3], z[3] * vsi)};
+        const f32x2_t o01 = {fmaf(egt, yq[b][0], z[0]), fmaf(egt, yq[b][1], z[1])};
+        const f32x2_t o23 = {fmaf(egt, yq[b][2], z[2]), fmaf(egt, yq[b][3], z[3])};
         const u32x2 ow = {__builtin_bit_cast(uint32_t, __builtin_convertvector(o01, bf16x2_t)),
                           __builtin_bit_cast(uint32_t, __builtin_convertvector(o23, bf16x2_t))};
         __builtin_amdgcn_raw_buffer_store_b64(ow, orsrc, (int)otoff, b * oblock, 0);
       }
-      // e^{Gc_end - Gc} v_new, the update operand (the scale undone)
+      // e^{Gc_end - Gc} v_new, the update operand
       const f32x4 dc = *reinterpret_cast<const f32x4*>(dcp + 16 * b);
-      vb[b] = to_b(dc * (vn * vsi));
+      vb[b] = to_b(dc * vn);
     }
     // h = e^{Gc_end} h + K^T (e^{Gc_end-Gc} v_new), two blocks per 32-deep product (K^T
     // fragments by transposing LDS reads)

@@ -256,25 +256,6 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // not hoisted out of a loop (and kept live across it).
 template <typename T> __device__ __forceinline__ void opaque(T& x) { asm volatile("" : "+v"(x)); }
 
-// One DPP move of x (the moved value in lanes of the rows `RowMask` enables, x elsewhere).
-template <int Ctrl, int RowMask>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, Ctrl, RowMask, 0xF, false);
-}
-
-// Maximum of x over the wave, as a wave-uniform value: DPP steps within each row of 16
-// lanes (quad permutations, then the half-row and row mirrors), the two row broadcasts
-// (lane 15 into the next row, lane 31 into the upper half), then lane 63.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  x = max(x, dpp_u32<0xB1, 0xF>(x));   // quad_perm [1, 0, 3, 2]
-  x = max(x, dpp_u32<0x4E, 0xF>(x));   // quad_perm [2, 3, 0, 1]
-  x = max(x, dpp_u32<0x141, 0xF>(x));  // row_half_mirror
-  x = max(x, dpp_u32<0x140, 0xF>(x));  // row_mirror: every lane holds its row's maximum
-  x = max(x, dpp_u32<0x142, 0xA>(x));  // row_bcast:15 into rows 1 and 3
-  x = max(x, dpp_u32<0x143, 0xC>(x));  // row_bcast:31 into rows 2 and 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-}
-
 // Inclusive prefix sum across a wave.
 __device__ __forceinline__ float wave_incl_scan(float x) {
   const int l = lane_id();

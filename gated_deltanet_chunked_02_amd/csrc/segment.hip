@@ -121,24 +121,17 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
 
   // the next row block of M (of this step, or the first of the next step) and the next
   // step's b are loaded into registers while the current row block is composed
-  float4 mreg[NV];
+  f32x4 mreg[NV];  // native vectors: HIP's float4 struct is copied through memory
   f32x4 breg[TPW];
-  auto load_block = [&](int s, int bk) {
-    const long off = seg_off(s) + (long)bk * RB * D;
+  if (ns > 0) {
+    const long off = seg_off(0);
 #pragma unroll
     for (int v = 0; v < NV; ++v)
-      mreg[v] = *reinterpret_cast<const float4*>(&M[off + 4 * (tid + 256 * v)]);
-  };
-  auto load_b = [&](int s) {
-    const long off = seg_off(s);
+      mreg[v] = *reinterpret_cast<const f32x4*>(&M[off + 4 * (tid + 256 * v)]);
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) breg[u][i] = b[off + (long)row_of(u, i) * D + col];
-  };
-  if (ns > 0) {
-    load_block(0, 0);
-    load_b(0);
   }
   for (int s = 0; s < ns; ++s) {
     const long off = seg_off(s);
@@ -154,14 +147,22 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int i = 4 * (tid + 256 * v);
-        *reinterpret_cast<float4*>(&ms[(i / D) * LD + i % D]) = mreg[v];
+        *reinterpret_cast<f32x4*>(&ms[(i / D) * LD + i % D]) = mreg[v];
       }
       __syncthreads();
-      if (bk + 1 < NBLK) {
-        load_block(s, bk + 1);
-      } else if (s + 1 < ns) {
-        load_block(s + 1, 0);
-        load_b(s + 1);
+      const bool next_step = bk + 1 == NBLK && s + 1 < ns;
+      if (bk + 1 < NBLK || next_step) {
+        const long moff = next_step ? seg_off(s + 1) : off + (long)(bk + 1) * RB * D;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          mreg[v] = *reinterpret_cast<const f32x4*>(&M[moff + 4 * (tid + 256 * v)]);
+      }
+      if (next_step) {
+        const long boff = seg_off(s + 1);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) breg[u][i] = b[boff + (long)row_of(u, i) * D + col];
       }
 #pragma unroll 4
       for (int k0 = 0; k0 < D; k0 += 16) {
