@@ -176,7 +176,22 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
   constexpr int NW = F::NW, CPRV = F::CPRV;
   constexpr int D = DK;  // row length of q, k, v and o
   constexpr float kLog2e = 1.4426950408889634f;
-  const int nh = blockIdx.x / F::SPLIT, half = blockIdx.x - nh * F::SPLIT;
+  // XCD-aware order.  The workgroups that read the same q/k rows (the H / Hg value heads of a
+  // q/k head, times SPLIT column halves: gsz consecutive indices) should share one XCD's L2,
+  // but the hardware deals consecutive workgroups round-robin to the 8 XCDs.  Workgroup p
+  // runs on XCD p % 8 at slot p / 8, so it takes member m of group R = (slot / gsz) 8 + XCD:
+  // each group's members run on one XCD in consecutive slots, and the groups still start in
+  // their global order (a packed batch's longest-first order is kept).  A grid that is not a
+  // multiple of 8 gsz keeps the plain order.
+  int bid = blockIdx.x;
+  {
+    const int gsz = F::SPLIT * (H / Hg);
+    if (gsz > 1 && gridDim.x % (8 * gsz) == 0) {
+      const int xcd = bid & 7, slot = bid >> 3;
+      bid = ((slot / gsz) * 8 + xcd) * gsz + slot % gsz;
+    }
+  }
+  const int nh = bid / F::SPLIT, half = bid - nh * F::SPLIT;
   int n = nh / H;  // for a packed batch, a rank that is mapped to a sequence below
   const int h = nh - n * H;
   const int hk = h / (H / Hg);
