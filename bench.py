@@ -234,6 +234,142 @@ def conv_bench(args, dev, gdn):
     print(json.dumps(out), flush=True)
 
 
+def bwd_algorithmic_bytes(inp):
+    """Bytes a perfect backward moves: the forward's inputs (q, k, v, g, beta, h0) and the
+    upstream gradients (do, dht) read once; dq, dk, dv, dg, dbeta (fp32) and dh0 written
+    once."""
+    q, v = inp["q"], inp["v"]
+    B, T, Hg, Dk = q.shape
+    H, Dv = v.shape[2], v.shape[3]
+    el = q.element_size()
+    toks = B * T
+    nseq = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    state = nseq * H * Dk * Dv * 4
+    rd = toks * (2 * Hg * Dk + 2 * H * Dv) * el + toks * H * (4 + inp["beta"].element_size())
+    wr = toks * (2 * Hg * Dk + H * Dv) * 4 + toks * H * 8
+    if inp["h0"] is not None:
+        rd += state
+        wr += state
+    if inp.get("dht") is not None:
+        rd += state
+    return float(rd + wr)
+
+
+def bwd_cpu_baseline(inp, grads_gpu, budget_s: float):
+    """Time the fp64 oracle's backward (reverse-mode through the token recurrence, numpy) on
+    a bounded sample of (sequence, head) pairs, scale to whole-job tokens/s, and check the
+    sampled GPU gradients (the workload's q/k heads are not shared: a pair's dq, dk are its
+    own)."""
+    from oracle import backward
+    from tests.gdn_testlib import pair_slices, rel_l2
+    B, T = inp["q"].shape[:2]
+    H = inp["v"].shape[2]
+    nseq = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    rng = np.random.default_rng(12345)
+    pairs = [(n, h) for n in range(nseq) for h in range(H)]
+    order = rng.permutation(len(pairs))
+    f = lambda x: x.double().cpu().numpy()
+    t_sample, th, errs, used = 0.0, 0, [], 0
+    for i in order:
+        if t_sample >= budget_s:
+            break
+        n, h = pairs[i]
+        ts, b, hk = pair_slices(inp, n, h)
+        sl = lambda x, j: f(x[b:b + 1, ts, j:j + 1])
+        args = [sl(inp["q"], hk), sl(inp["k"], hk), sl(inp["v"], h), sl(inp["g"], h),
+                sl(inp["beta"], h)]
+        h0 = None if inp["h0"] is None else f(inp["h0"][n:n + 1, h:h + 1])
+        dht = None if inp.get("dht") is None else f(inp["dht"][n:n + 1, h:h + 1])
+        do = sl(inp["do"], h)
+        t0 = time.perf_counter()
+        ref = backward.recurrence_backward(*args, h0, inp["scale"], do, dht)
+        t_sample += time.perf_counter() - t0
+        th += args[0].shape[1]
+        used += 1
+        for j, idx in enumerate((hk, hk, h, h, h)):
+            x = grads_gpu[j][b:b + 1, ts, idx:idx + 1]
+            errs.append(rel_l2(f(x), ref[j]))
+    t_job = t_sample * (B * T * H) / max(th, 1)
+    return {
+        "value": B * T / t_job, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": "%d of %d (sequence, head) pairs at full length, fp64 reverse-mode "
+                  "through the token recurrence (numpy, one thread), %.1f s; scaled by "
+                  "token-heads to the whole job" % (used, len(pairs), t_sample),
+        "sample_seconds": t_sample,
+        "parity_sampled": {"pairs": used, "grad_rel_l2_max": max(errs) if errs else None},
+    }
+
+
+def bwd_bench(args, dev, gdn, w, inp):
+    """Time gdn_chunk_bwd: the staged recompute of the forward's chunk quantities (C = 64)
+    and the two backward kernels, one call per step."""
+    q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))
+    h0, cu = inp["h0"], inp["cu_seqlens"]
+    N = q.shape[0] if cu is None else cu.numel() - 1
+    inp.update(gdn_inputs.draw_grads(w, q.shape[0], q.shape[1], N, device=dev,
+                                     dht_std=None if h0 is None else 0.1))
+    do, dht = inp["do"], inp["dht"]
+    desc = gdn.make_desc(q, v, beta, cu, 64, "staged")
+    ws = torch.empty(gdn.gdn_chunk_bwd_workspace_size(desc), device=dev, dtype=torch.uint8)
+    desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+    f = dict(device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty(q.shape, **f), torch.empty(k.shape, **f), torch.empty(v.shape, **f)
+    dg, dbeta = torch.empty(g.shape, **f), torch.empty(g.shape, **f)
+    dh0 = None if h0 is None else torch.empty(h0.shape, **f)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = gdn.gdn_chunk_bwd(desc, q, k, v, g, beta, h0, cu, inp["scale"], do, dht, dq, dk,
+                               dv, dg, dbeta, dh0, stream)
+        if st != 0:
+            raise gdn.GdnError(st, "gdn_chunk_bwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done; timing %d backward steps" % args.steps, file=sys.stderr,
+          flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_wall = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    avg_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    ms_per_step = 1e3 * t_wall / args.steps
+    tokens = q.shape[0] * q.shape[1]
+    by = bwd_algorithmic_bytes(inp)
+    gbs = by / (avg_ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] timing the oracle's backward on the host", file=sys.stderr, flush=True)
+        cpu = bwd_cpu_baseline(inp, (dq, dk, dv, dg, dbeta), args.cpu_budget)
+    heads = "H=%d" % w.H if w.Hg == w.H else "H=%d, Hg=%d" % (w.H, w.Hg)
+    shape = ("varlen %d seqs U{1..%d}" % (w.n_varlen, w.max_len) if w.n_varlen
+             else "%d×%d" % (w.B, w.T))
+    out = {
+        "metric": "GDN chunk-bwd tokens/s at 1 MI355X (%s, %s, D=%d, %s); %% roofline" % (
+            shape, heads, w.Dk, w.dtype),
+        "value": tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "B": int(q.shape[0]),
+                   "T": int(q.shape[1]), "H": w.H, "Hg": w.Hg, "Dk": w.Dk, "Dv": w.Dv,
+                   "C": 64, "h0": h0 is not None, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gdn_chunk_bwd whole call (staged stages 0-6, k_bwd_dh, "
+                               "k_bwd_chunk%s)" % (", k_bwd_group_sum" if w.H != w.Hg else ""),
+                     "launch_ms": avg_ms, "algorithmic_bytes": by},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +391,8 @@ def main():
     ap.add_argument("--gated", action="store_true",
                     help="time the decode operator with in-kernel gates "
                          "(gdn_fused_sigmoid_gating_delta_rule) on the workload's tokens")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (gdn_chunk_bwd) on the workload")
     ap.add_argument("--mode", default="gdn", choices=["gdn", "copy"],
                     help="copy: time a plain 1 GiB device-to-device copy (the reference "
                          "kernel for scaling HBM byte counters)")
@@ -284,6 +422,9 @@ def main():
         w = w.with_(**{field: int(val)})
     print("[bench] drawing %s on %s" % (w.name, dev), file=sys.stderr, flush=True)
     inp = gdn_inputs.draw(w, device=dev)
+    if args.bwd:
+        bwd_bench(args, dev, gdn, w, inp)
+        return
     q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))
     h0, cu = inp["h0"], inp["cu_seqlens"]
     gate_in = None

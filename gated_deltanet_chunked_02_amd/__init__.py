@@ -27,7 +27,8 @@ __all__ = [
     "gdn_stage_buffer", "gdn_status_string", "gdn_version", "chunk_gated_delta_rule",
     "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH", "gdn_resolved_variant",
     "gdn_resolved_chunk", "gdn_chunk_fwd_noalloc", "gdn_fused_sigmoid_gating_delta_rule",
-    "fused_sigmoid_gating_delta_rule",
+    "fused_sigmoid_gating_delta_rule", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_size",
+    "chunk_gated_delta_rule_bwd",
     "GdnConvDesc", "gdn_causal_conv1d_fwd", "causal_conv1d", "ACTIVATIONS",
 ]
 
@@ -100,6 +101,11 @@ def load(path: str = LIB_PATH):
     lib.gdn_fused_sigmoid_gating_delta_rule.restype = ctypes.c_int
     lib.gdn_fused_sigmoid_gating_delta_rule.argtypes = [
         ctypes.POINTER(GdnDesc), P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P]
+    lib.gdn_chunk_bwd_workspace_size.restype = S
+    lib.gdn_chunk_bwd_workspace_size.argtypes = lib.gdn_chunk_fwd_workspace_size.argtypes
+    lib.gdn_chunk_bwd.restype = ctypes.c_int
+    lib.gdn_chunk_bwd.argtypes = [ctypes.POINTER(GdnDesc), P, P, P, P, P, P, P, ctypes.c_float,
+                                  P, P, P, P, P, P, P, P, P]
     lib.gdn_causal_conv1d_fwd.restype = ctypes.c_int
     lib.gdn_causal_conv1d_fwd.argtypes = [ctypes.POINTER(GdnConvDesc), P, P, P, P, P, P, P, P,
                                           P]
@@ -198,6 +204,28 @@ def gdn_fused_sigmoid_gating_delta_rule(desc: GdnDesc, q, k, v, a, b, A_log, dt_
     return int(load().gdn_fused_sigmoid_gating_delta_rule(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
         _ptr(dt_bias), _ptr(h0), _ptr(cu_seqlens), float(scale), _ptr(o), _ptr(ht), stream))
+
+
+def gdn_chunk_bwd_workspace_size(desc: GdnDesc) -> int:
+    st = ctypes.c_int(0)
+    n = load().gdn_chunk_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(st))
+    if st.value != 0:
+        raise GdnError(st.value, "gdn_chunk_bwd_workspace_size")
+    return int(n)
+
+
+def gdn_chunk_bwd(desc: GdnDesc, q, k, v, g, beta, h0, cu_seqlens, scale, do, dht, dq, dk, dv,
+                  dg, dbeta, dh0, stream=None) -> int:
+    """Raw call of the backward pass; returns the status code (0 = ok) without raising."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return int(load().gdn_chunk_bwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+        _ptr(cu_seqlens), float(scale), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dg), _ptr(dbeta), _ptr(dh0), stream))
 
 
 def _dtype_code(t) -> int:
@@ -367,6 +395,57 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
     if st != 0:
         raise GdnError(st, "gdn_chunk_fwd")
     return o, ht
+
+
+def chunk_gated_delta_rule_bwd(q, k, v, g, beta, do, dht=None, scale=None,
+                               initial_state=None, cu_seqlens=None, workspace=None):
+    """Gradients of chunk_gated_delta_rule's inputs on the current stream, given the
+    gradient ``do`` of o [B, T, H, Dv] (q's dtype) and ``dht`` of the final state
+    [N, H, Dk, Dv] (or None: zero).  Forward inputs as for chunk_gated_delta_rule.
+    Returns fp32 (dq, dk [B, T, Hg, Dk], dv [B, T, H, Dv], dg, dbeta [B, T, H],
+    dh0 [N, H, Dk, Dv] or None when initial_state is None)."""
+    import torch
+    _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace, devices=False)
+    _need(isinstance(do, torch.Tensor) and do.dtype == q.dtype, TypeError,
+          "do must be a tensor of q's dtype")
+    _need(do.shape == v.shape, ValueError, "do must have v's shape [B, T, H, Dv]")
+    B, T, Hg, Dk = q.shape
+    H, Dv = v.shape[2], v.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if dht is not None:
+        _need(isinstance(dht, torch.Tensor) and dht.is_floating_point(), TypeError,
+              "dht must be a floating tensor")
+        _need(tuple(dht.shape) == (N, H, Dk, Dv), ValueError,
+              "dht must be [N, H, Dk, Dv] = %s" % ((N, H, Dk, Dv),))
+    _check_devices(dict(q=q, k=k, v=v, g=g, beta=beta, do=do, dht=dht,
+                        initial_state=initial_state, cu_seqlens=cu_seqlens,
+                        workspace=workspace), q.device)
+    q, k, v, do = q.contiguous(), k.contiguous(), v.contiguous(), do.contiguous()
+    g, beta = g.contiguous(), beta.contiguous()
+    if cu_seqlens is not None:
+        cu_seqlens = cu_seqlens.to(torch.int32).contiguous()
+    if initial_state is not None:
+        initial_state = initial_state.to(torch.float32).contiguous()
+    if dht is not None:
+        dht = dht.to(torch.float32).contiguous()
+    desc = make_desc(q, v, beta, cu_seqlens, 64, "staged")
+    if scale is None:
+        scale = Dk ** -0.5
+    f = dict(device=q.device, dtype=torch.float32)
+    dq, dk = torch.empty(q.shape, **f), torch.empty(k.shape, **f)
+    dv = torch.empty(v.shape, **f)
+    dg, dbeta = torch.empty(B, T, H, **f), torch.empty(B, T, H, **f)
+    dh0 = torch.empty(N, H, Dk, Dv, **f) if initial_state is not None else None
+    ws_bytes = gdn_chunk_bwd_workspace_size(desc)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), device=q.device, dtype=torch.uint8)
+    desc.workspace = workspace.data_ptr()
+    desc.workspace_bytes = workspace.numel()
+    st = gdn_chunk_bwd(desc, q, k, v, g, beta, initial_state, cu_seqlens, scale, do, dht, dq,
+                       dk, dv, dg, dbeta, dh0)
+    if st != 0:
+        raise GdnError(st, "gdn_chunk_bwd")
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def fused_sigmoid_gating_delta_rule(q, k, v, a, b, A_log, dt_bias=None, scale=None,

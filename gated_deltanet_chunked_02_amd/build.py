@@ -29,7 +29,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["api.cpp", "stages.hip", "fused.hip", "segment.hip", "recurrent.hip", "conv1d.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

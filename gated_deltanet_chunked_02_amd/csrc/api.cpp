@@ -221,6 +221,65 @@ size_t workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
   return L.total;
 }
 
+// The backward pass recomputes the staged forward's stages 0-6 at C = 64 into the front of
+// its workspace, then keeps dDelta [Ttot, H, D] and each chunk's end-state gradient
+// [max_chunks, H, D, D] in the q/k/v dtype and (H != Hg) per-value-head dq and dk
+// [Ttot, H, D] in fp32.
+constexpr int kBwdChunk = 64;
+
+struct BwdLayout {
+  Layout st;
+  size_t dD, dH, dqh, dkh, total;
+};
+
+// Shape part of a backward call: the forward's checks with the chunk set to 64 and N as the
+// call reads it (cu_seqlens: d->N; else B).
+gdn_status bwd_problem(const gdn_desc* d, bool packed, gdn::Problem* p) {
+  const gdn_status s = check_desc(d, p);
+  if (s != GDN_OK) return s;
+  if (packed) {
+    if (d->B != 1 || d->N < 0) return GDN_ERR_INVALID_ARG;
+    p->N = d->N;
+  } else if (d->N != 0 && d->N != d->B) {
+    return GDN_ERR_INVALID_ARG;
+  }
+  p->C = kBwdChunk;
+  p->max_chunks = (int)(((long long)p->Ttot + kBwdChunk - 1) / kBwdChunk) + p->N;
+  if (!gdn::bwd_supported(*p)) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+BwdLayout bwd_layout(const gdn::Problem& p) {
+  BwdLayout L;
+  staged_layout(p, &L.st);
+  const size_t e = p.f32 ? 4 : 2;
+  const size_t tok = (size_t)p.Ttot * p.H * p.D * sizeof(float);
+  L.dD = L.st.total;
+  L.dH = L.dD + align_up((size_t)p.Ttot * p.H * p.D * e);
+  const size_t hb = (size_t)p.max_chunks * p.H * p.D * p.D * e;
+  L.dqh = L.dH + align_up(hb);
+  const bool grouped = p.H != p.Hg;
+  L.dkh = L.dqh + (grouped ? align_up(tok) : 0);
+  L.total = L.dkh + (grouped ? align_up(tok) : 0);
+  return L;
+}
+
+gdn::Stages stages_at(char* ws, const Layout& L) {
+  gdn::Stages st;
+  st.table = reinterpret_cast<int32_t*>(ws + L.off[GDN_BUF_CHUNK_TABLE]);
+  st.seq_chunks = reinterpret_cast<int32_t*>(ws + L.off[GDN_BUF_SEQ_CHUNKS]);
+  st.g_cum = reinterpret_cast<float*>(ws + L.off[GDN_BUF_G_CUM]);
+  st.g_t = reinterpret_cast<float*>(ws + L.off[GDN_BUF_G_T]);
+  st.beta_t = ws + L.off[GDN_BUF_BETA_T];
+  st.A = reinterpret_cast<float*>(ws + L.off[GDN_BUF_A]);
+  st.Tinv = ws + L.off[GDN_BUF_TINV];
+  st.W = ws + L.off[GDN_BUF_W];
+  st.U = ws + L.off[GDN_BUF_U];
+  st.h_c = ws + L.off[GDN_BUF_H_C];
+  st.v_new = ws + L.off[GDN_BUF_V_NEW];
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,19 +419,7 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
     staged_layout(p, &L);
     if (!d->workspace || d->workspace_bytes < L.total || !aligned(d->workspace, kAlign))
       return GDN_ERR_WORKSPACE;
-    char* ws = static_cast<char*>(d->workspace);
-    gdn::Stages st;
-    st.table = reinterpret_cast<int32_t*>(ws + L.off[GDN_BUF_CHUNK_TABLE]);
-    st.seq_chunks = reinterpret_cast<int32_t*>(ws + L.off[GDN_BUF_SEQ_CHUNKS]);
-    st.g_cum = reinterpret_cast<float*>(ws + L.off[GDN_BUF_G_CUM]);
-    st.g_t = reinterpret_cast<float*>(ws + L.off[GDN_BUF_G_T]);
-    st.beta_t = ws + L.off[GDN_BUF_BETA_T];
-    st.A = reinterpret_cast<float*>(ws + L.off[GDN_BUF_A]);
-    st.Tinv = ws + L.off[GDN_BUF_TINV];
-    st.W = ws + L.off[GDN_BUF_W];
-    st.U = ws + L.off[GDN_BUF_U];
-    st.h_c = ws + L.off[GDN_BUF_H_C];
-    st.v_new = ws + L.off[GDN_BUF_V_NEW];
+    const gdn::Stages st = stages_at(static_cast<char*>(d->workspace), L);
     e = gdn::launch_staged(p, st, d->stop_after, stream);
   }
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
@@ -424,6 +471,77 @@ gdn_status gdn_fused_sigmoid_gating_delta_rule(const gdn_desc* d, const void* q,
     p.gate_a = nullptr;
   }
   return gdn::launch_recurrent(p, stream) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+size_t gdn_chunk_bwd_workspace_size(const gdn_desc* d, gdn_status* status) {
+  gdn::Problem p;
+  // N other than 0 or B is read as a packed batch; else the dense reading, whose chunk bound
+  // ceil(B T / 64) + B also covers a packed batch of B = 1 and N = 1
+  const bool packed = d && d->N != 0 && d->N != d->B;
+  const gdn_status s = bwd_problem(d, packed, &p);
+  if (status) *status = s;
+  if (s != GDN_OK) return 0;
+  return bwd_layout(p).total;
+}
+
+gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const void* v,
+                         const float* g, const void* beta, const float* h0,
+                         const int32_t* cu_seqlens, float scale, const void* dout,
+                         const float* dht, float* dq, float* dk, float* dv, float* dg,
+                         float* dbeta, float* dh0, hipStream_t stream) {
+  gdn::Problem p;
+  const gdn_status s = bwd_problem(d, cu_seqlens != nullptr, &p);
+  if (s != GDN_OK) return s;
+  if (p.Ttot > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg ||
+                     !dbeta))
+    return GDN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+      !aligned(g, 4) || !aligned(beta, p.beta_f32 ? 4 : 2) || !aligned(h0, 16) ||
+      !aligned(cu_seqlens, 4) || !aligned(dht, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(dg, 4) || !aligned(dbeta, 4) || !aligned(dh0, 16))
+    return GDN_ERR_INVALID_ARG;
+  p.scale = scale;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.beta = beta;
+  p.h0 = h0;
+  p.cu = cu_seqlens;
+  p.o = nullptr;
+  p.ht = nullptr;
+  if (p.N == 0) return GDN_OK;
+  if (p.Ttot == 0) {
+    // no tokens: the final state is the initial one, so dh0 = dht (or zeros); the recurrent
+    // kernel's pass-through writes exactly that
+    if (!dh0) return GDN_OK;
+    if ((long long)p.N * p.H * (p.D / 32) >= (1LL << 31)) return GDN_ERR_UNSUPPORTED;
+    gdn::Problem pp = p;
+    pp.h0 = dht;
+    pp.ht = dh0;
+    return gdn::launch_recurrent(pp, stream) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
+  const BwdLayout L = bwd_layout(p);
+  if (!d->workspace || d->workspace_bytes < L.total || !aligned(d->workspace, kAlign))
+    return GDN_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(d->workspace);
+  gdn::BwdBuffers b;
+  b.st = stages_at(ws, L.st);
+  b.dO = dout;
+  b.dht = dht;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dg = dg;
+  b.dbeta = dbeta;
+  b.dh0 = dh0;
+  b.dD = ws + L.dD;
+  b.dH = ws + L.dH;
+  b.dqh = p.H != p.Hg ? reinterpret_cast<float*>(ws + L.dqh) : nullptr;
+  b.dkh = p.H != p.Hg ? reinterpret_cast<float*>(ws + L.dkh) : nullptr;
+  hipError_t e = gdn::launch_staged(p, b.st, 6, stream);
+  if (e == hipSuccess) e = gdn::launch_bwd(p, b, stream);
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 gdn_status gdn_causal_conv1d_fwd(const gdn_conv_desc* d, const void* x, const float* weight,

@@ -1,0 +1,736 @@
+// Backward pass of the chunked gated delta rule (the FlashQLA how-to cites forward and
+// backward speed-ups of the chunked operator; no page prints its formulas).  Written for
+// gfx950 from the chunked forward's algebra.
+//
+// Per chunk (C = 64 tokens), with h the state at the chunk start (Dk x Dv), Gc the in-chunk
+// prefix sum of g, gam_t = e^{Gc_t}, gC = gam at the chunk's last token, Gam_ij =
+// e^{Gc_i - Gc_j}, T = (I + A)^-1 with A = strictly_lower(diag(beta) (K K^T * Gam)), and
+//   R = diag(beta) (V - diag(gam) K h),   Delta = T R   (v_new),
+//   O = scale (diag(gam) Q h + (Q K^T * Gam)_{i>=j} Delta),
+//   h' = gC h + K^T diag(gC / gam) Delta,
+// the gradients given dO and dh' (the gradient of the chunk-end state) are
+//   dDelta = P^T dO + diag(gC / gam) K dh',        P = scale (Q K^T * Gam)_{i>=j}
+//   dh     = gC dh' + scale Q^T diag(gam) dO - W^T dDelta,   W = T diag(beta gam) K
+//   dR     = T^T dDelta,   dA = -(dR Delta^T)_{i>j},   dV = diag(beta) dR
+//   dQ     = scale diag(gam) dO h^T + Mi K,            Mi = scale (dO Delta^T * Gam)_{i>=j}
+//   dK     = Mi^T Q + (DB + DB^T) K + diag(gC / gam) Delta dh'^T - diag(beta gam) dR h^T,
+//            DB = diag(beta) dA * Gam
+//   dbeta  = rowsum(dR * (V - diag(gam) K h)) + rowsum(dA * K K^T * Gam)
+//   dGc    = scale gam rowsum(dO * Q h) - (gC / gam) rowsum(Delta * K dh')
+//            - beta gam rowsum(dR * K h) + rowsum(E) - colsum(E),
+//            E = Mi * Q K^T + DB * K K^T,
+//            and at the last token also sum_t (gC / gam_t) rowsum(Delta * K dh')_t
+//            + gC <dh', h>;  dg = the in-chunk suffix sum of dGc.
+//
+// Two kernels follow the staged forward's recomputation (chunk table, Gc, T, W, the chunk-start
+// states and v_new in the workspace):
+//   k_bwd_dh     one workgroup per (sequence, head, 64-column slab of the state): the chunks
+//                in reverse, dh kept in accumulator tiles; writes dh' of every chunk, dDelta,
+//                and dh0;
+//   k_bwd_chunk  one workgroup per (chunk, head): everything else, in phases that stage their
+//                operands in LDS (each product C = A B^T with both operands k-contiguous).
+// Value heads that share a q/k head write their dq and dk to a per-head buffer that a last
+// kernel sums (no float atomics: the results do not depend on scheduling).
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kBT = 256;   // threads of the dh workgroup (4 waves)
+constexpr int kBT2 = 512;  // threads of the chunk workgroup (8 waves)
+constexpr int kBC = 64;   // chunk length of the backward
+
+__device__ __forceinline__ int4 chunk_of(const int32_t* table, int c) {
+  return reinterpret_cast<const int4*>(table)[c];
+}
+
+// One workgroup's copy of a ROWS x COLS block of TI (row r at src + r * stride; rows
+// r >= len read as zero, len >= 1) in RB x V sub-blocks, V = 16 / sizeof(TI) and RB chosen
+// so that every thread holds one: RB rows of one 16-byte vector each.  Eight lanes cover
+// 128 contiguous bytes of a source row.  The loads are unconditional (rows past len read
+// the last valid row) and nothing touches their results until a store zeroes the rows past
+// len, so a load issued phases ahead stays in flight until its data is stored.  Stored
+// natural (dst[r * ld + c], 16-byte LDS stores) or transposed in registers (dst[c * ld + r],
+// RB-element stores).
+template <typename TI, int ROWS, int COLS, int NTH = kBT>
+struct Blk {
+  static constexpr int V = 16 / (int)sizeof(TI), BC = COLS / V;
+  static constexpr int RB = ROWS * BC / NTH < V ? ROWS * BC / NTH : V;
+  static constexpr int BR = ROWS / RB, NB = BR * BC;
+  static_assert(RB >= 1 && ROWS % RB == 0 && BR % 8 == 0 && BC % 8 == 0 && NB == NTH,
+                "block shape");
+  union Vec {
+    uint4 u;
+    TI e[V];
+  };
+  typedef TI Col __attribute__((ext_vector_type(RB > 1 ? RB : 2)));
+  Vec in[RB];
+  int r0, c0, len;
+
+  __device__ __forceinline__ void load(const TI* src, long stride, int len_) {
+    const int lo = threadIdx.x & 63, hi = threadIdx.x >> 6;
+    const int bc = (lo & 7) + 8 * (hi % (BC / 8)), br = (lo >> 3) + 8 * (hi / (BC / 8));
+    r0 = RB * br;
+    c0 = V * bc;
+    len = len_;
+#pragma unroll
+    for (int a = 0; a < RB; ++a)
+      in[a].u = *reinterpret_cast<const uint4*>(src + (long)min(r0 + a, len - 1) * stride + c0);
+  }
+  __device__ __forceinline__ Vec row(int a) const {
+    Vec x;
+    x.u = r0 + a < len ? in[a].u : make_uint4(0, 0, 0, 0);
+    return x;
+  }
+  __device__ __forceinline__ void store_nat(TI* dst, int ld) const {
+#pragma unroll
+    for (int a = 0; a < RB; ++a) *reinterpret_cast<uint4*>(dst + (r0 + a) * ld + c0) = row(a).u;
+  }
+  __device__ __forceinline__ void store_trn(TI* dst, int ld) const {
+    Vec x[RB];
+#pragma unroll
+    for (int a = 0; a < RB; ++a) x[a] = row(a);
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+      if constexpr (RB == 1) {
+        dst[(c0 + b) * ld + r0] = x[0].e[b];
+      } else {
+        Col o;
+#pragma unroll
+        for (int a = 0; a < RB; ++a) o[a] = x[a].e[b];
+        *reinterpret_cast<Col*>(dst + (c0 + b) * ld + r0) = o;
+      }
+    }
+  }
+  // sum over the held elements of x * other[r][c] (other natural, leading dimension ld)
+  __device__ __forceinline__ float dot_nat(const TI* other, int ld) const {
+    float s = 0.f;
+#pragma unroll
+    for (int a = 0; a < RB; ++a) {
+      const Vec x = row(a);
+      Vec o;
+      o.u = *reinterpret_cast<const uint4*>(other + (r0 + a) * ld + c0);
+#pragma unroll
+      for (int b = 0; b < V; ++b) s += (float)x.e[b] * (float)o.e[b];
+    }
+    return s;
+  }
+};
+
+template <typename TI, int ROWS, int COLS, int NTH = kBT>
+__device__ __forceinline__ void ld_nat(TI* dst, int ld, const TI* src, long stride, int len) {
+  Blk<TI, ROWS, COLS, NTH> b;
+  b.load(src, stride, len);
+  b.store_nat(dst, ld);
+}
+
+template <typename TI, int ROWS, int COLS, int NTH = kBT>
+__device__ __forceinline__ void ld_tr(TI* dst, int ld, const TI* src, long stride, int len) {
+  Blk<TI, ROWS, COLS, NTH> b;
+  b.load(src, stride, len);
+  b.store_trn(dst, ld);
+}
+
+// Sum over the 16 lanes of a lane group (one accumulator row, its 16 columns).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
+// Sum over the 4 lane groups (one accumulator column, 16 of its rows with the 4 elements).
+__device__ __forceinline__ float sum4g(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// ------------------------------------------------------------------------- dh pass
+// LDS: R0 [C][LDD] holds Q and then P^T ([C][LDC]); K [C][LDD]; Q^T, W^T [D][LDC]; this
+// slab of dO transposed [64][LDC]; the chunk's Gc [C].  (About 80 KB at D = 128 in bf16:
+// two workgroups per CU.)
+template <typename TI, int D>
+constexpr size_t dh_smem() {
+  constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>();
+  return (2 * kBC * LDD + 2 * D * LDC + 64 * LDC) * sizeof(TI) + kBC * sizeof(float);
+}
+
+template <typename TI, int D>
+__global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ table,
+                                                const int32_t* __restrict__ seq_chunks,
+                                                const TI* __restrict__ q,
+                                                const TI* __restrict__ k,
+                                                const TI* __restrict__ W,
+                                                const TI* __restrict__ dO,
+                                                const float* __restrict__ g_t,
+                                                const float* __restrict__ dht,
+                                                TI* __restrict__ dH, TI* __restrict__ dD,
+                                                float* __restrict__ dh0, int Ttot, int H,
+                                                int Hg, float scale) {
+  constexpr int C = kBC, NDK = D / 16, NT = C / 16;
+  constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>();
+  static_assert(C * LDC <= C * LDD, "P^T fits where Q was");
+  const int n = blockIdx.x, h = blockIdx.y, hk = h / (H / Hg);
+  const int w = wave_id(), l = lane_id();
+  const int scol = 16 * w + (l & 15);           // column within the 64-column slab
+  const int col = blockIdx.z * 64 + scol;       // state column
+  extern __shared__ __align__(16) char smem[];
+  TI* sQ = reinterpret_cast<TI*>(smem);  // [C][LDD]
+  TI* sPt = sQ;                          // [C][LDC]  P^T, once P is in registers
+  TI* sK = sQ + C * LDD;                 // [C][LDD]
+  TI* sQt = sK + C * LDD;                // [D][LDC]  Q^T
+  TI* sWt = sQt + D * LDC;               // [D][LDC]  W^T
+  TI* sOt = sWt + D * LDC;               // [64][LDC] this slab of dO, transposed
+  float* sG = reinterpret_cast<float*>(sOt + 64 * LDC);
+
+  // dh tile db: rows (key index) 16 db + 4 (l/16) + e, column col
+  f32x4 dh[NDK];
+  const long hoff = ((long)n * H + h) * D * D;
+#pragma unroll
+  for (int db = 0; db < NDK; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dh[db][e] = dht ? dht[hoff + (long)(16 * db + 4 * (l >> 4) + e) * D + col] : 0.f;
+
+  // the chunk's operands are loaded one chunk ahead (into registers) while the previous one
+  // is computed
+  const int c0 = seq_chunks[n], c1 = seq_chunks[n + 1];
+  Blk<TI, C, D> bq, bk, bw;
+  Blk<TI, C, 64> bo;
+  float gt = 0.f;
+  int glen = 0;
+  auto fetch = [&](int c) {
+    const int4 ci = chunk_of(table, c);
+    const int start = ci.y, len = ci.z;
+    const long qk0 = ((long)start * Hg + hk) * D, v0 = ((long)start * H + h) * D;
+    bq.load(q + qk0, (long)Hg * D, len);
+    bk.load(k + qk0, (long)Hg * D, len);
+    bw.load(W + v0, (long)H * D, len);
+    bo.load(dO + v0 + blockIdx.z * 64, (long)H * D, len);
+    gt = g_t[(long)h * Ttot + start + min((int)threadIdx.x, len - 1)];
+    glen = len;
+  };
+  if (c1 > c0) fetch(c1 - 1);
+  for (int c = c1 - 1; c >= c0; --c) {
+    const int4 ci = chunk_of(table, c);
+    const int start = ci.y, len = ci.z;
+    const long v0 = ((long)start * H + h) * D;
+    __syncthreads();  // the previous chunk is done with the LDS tiles
+    bq.store_nat(sQ, LDD);
+    bq.store_trn(sQt, LDC);
+    bk.store_nat(sK, LDD);
+    bw.store_trn(sWt, LDC);
+    bo.store_trn(sOt, LDC);
+    if (threadIdx.x < C) sG[threadIdx.x] = (int)threadIdx.x < glen ? gt : 0.f;
+    if (c > c0) fetch(c - 1);
+    __syncthreads();
+    // P[i][j] = scale (q_i . k_j) e^{Gc_i - Gc_j} for j <= i < len (wave w: 4 of the 16 tiles)
+    f32x4 pt[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int u = w + 4 * m, ti = u >> 2, tj = u & 3;
+      pt[m] = zero4();
+      if (ti >= tj) mma_lds<TI>(pt[m], sQ, LDD, 16 * ti, sK, LDD, 16 * tj, 0, D);
+      const int j = 16 * tj + (l & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * ti + 4 * (l >> 4) + e;
+        pt[m][e] = (i >= j && i < len) ? scale * pt[m][e] * __expf(sG[i] - sG[j]) : 0.f;
+      }
+    }
+    __syncthreads();  // Q (natural) is read: P^T takes its place
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int u = w + 4 * m, ti = u >> 2, tj = u & 3;
+      const int j = 16 * tj + (l & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sPt[j * LDC + 16 * ti + 4 * (l >> 4) + e] = (TI)pt[m][e];
+    }
+    __syncthreads();
+    const float gC = sG[len - 1], eC = __expf(gC);
+    // dDelta (rows t, this lane's column) = P^T dO + (gC / gam_t) (K dh')
+    f32x4 dd[NT];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+      f32x4 a = zero4(), x = zero4();
+      mma_lds<TI>(a, sPt, LDC, 16 * tb, sOt, LDC, 16 * w, 0, C);
+      mma_accB<TI, NDK>(x, sK, LDD, 16 * tb, 0, dh, NDK);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tb + 4 * (l >> 4) + e;
+        dd[tb][e] = t < len ? a[e] + __expf(gC - sG[t]) * x[e] : 0.f;
+      }
+    }
+    // the chunk-end gradient dh' and dDelta, for the chunk-parallel kernel
+    const long coff = ((long)c * H + h) * D * D;
+#pragma unroll
+    for (int db = 0; db < NDK; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dH[coff + (long)(16 * db + 4 * (l >> 4) + e) * D + col] = (TI)dh[db][e];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tb + 4 * (l >> 4) + e;
+        if (t < len) dD[v0 + (long)t * H * D + col] = (TI)dd[tb][e];
+      }
+    // dh = gC dh' + scale Q^T diag(gam) dO - W^T dDelta
+    f32x4 go[NT], nd[NT];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tb + 4 * (l >> 4) + e;
+        go[tb][e] = t < len ? scale * __expf(sG[t]) * (float)sOt[scol * LDC + t] : 0.f;
+        nd[tb][e] = -dd[tb][e];
+      }
+#pragma unroll
+    for (int db = 0; db < NDK; ++db) {
+      dh[db] *= eC;
+      mma_accB<TI, NT>(dh[db], sQt, LDC, 16 * db, 0, go, NT);
+      mma_accB<TI, NT>(dh[db], sWt, LDC, 16 * db, 0, nd, NT);
+    }
+  }
+  if (dh0) {
+#pragma unroll
+    for (int db = 0; db < NDK; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dh0[hoff + (long)(16 * db + 4 * (l >> 4) + e) * D + col] = dh[db][e];
+  }
+}
+
+// ------------------------------------------------------------------------- chunk gradients
+// One workgroup of 8 waves per (chunk, head).  Wave w = 4 rh + cw: in the C x D products it
+// owns the row blocks 2 rh, 2 rh + 1 and the column blocks cw + 4 m (m < D / 64); in the
+// C x C products the row block cw and the column blocks 2 rh, 2 rh + 1.
+template <typename TI, int D>
+struct ChunkLds {
+  static constexpr int C = kBC;
+  static constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>();
+  static constexpr int MAT = (C * LDD > D * LDC ? C * LDD : D * LDC);  // a C x D or D x C panel
+  static constexpr int BIG = D * LDD;                                  // a D x D matrix
+  static constexpr int CC = C * LDC;                                   // a C x C matrix
+  static_assert(C * LDD <= 2 * CC, "V fits in the first two C x C tiles");
+  static constexpr size_t bytes =
+      (3 * MAT + BIG + C * LDD + 4 * CC) * sizeof(TI) + (2 + 16 + 4 + 4) * C * sizeof(float);
+};
+
+template <typename TI, int D>
+__global__ __launch_bounds__(kBT2) void k_bwd_chunk(
+    const int32_t* __restrict__ table, const TI* __restrict__ q, const TI* __restrict__ k,
+    const TI* __restrict__ v, const void* __restrict__ beta, int beta_f32,
+    const float* __restrict__ g_t, const TI* __restrict__ Tinv, const TI* __restrict__ h_c,
+    const TI* __restrict__ v_new, const TI* __restrict__ dD, const TI* __restrict__ dH,
+    const TI* __restrict__ dO, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta, int qk_rows,
+    int Ttot, int H, int Hg, float scale) {
+  typedef ChunkLds<TI, D> L;
+  constexpr int C = kBC, CBW = D / 64, N2 = kBT2;  // column blocks per wave (C x D outputs)
+  constexpr int LDD = L::LDD, LDC = L::LDC;
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int4 ci = chunk_of(table, c);
+  const int start = ci.y, len = ci.z;
+  if (len == 0) return;
+  const int hk = h / (H / Hg);
+  const int hq = qk_rows == H ? h : hk;  // the q/k row of dq and dk this head writes
+  const int w = wave_id(), l = lane_id(), lg = l >> 4, lc = l & 15;
+  const int cw = w & 3, rh = w >> 2;
+  extern __shared__ __align__(16) char smem[];
+  TI* sA = reinterpret_cast<TI*>(smem);
+  TI* sB = sA + L::MAT;
+  TI* sC = sB + L::MAT;
+  TI* sBig = sC + L::MAT;
+  TI* sDl = sBig + L::BIG;       // Delta, [C][LDD]
+  TI* sCC1 = sDl + C * LDD;      // T^T, then V ([C][LDD] over the first two tiles), then Mi
+  TI* sCC2 = sCC1 + L::CC;       // Mi^T
+  TI* sCC3 = sCC2 + L::CC;       // DB
+  TI* sCC4 = sCC3 + L::CC;       // DB^T
+  TI* sV = sCC1;
+  float* sG = reinterpret_cast<float*>(sCC4 + L::CC);
+  float* sBeta = sG + C;
+  // sPart [16 C]: the row dots' parts [quantity x][column wave][C] (x = 1..3 in phase B,
+  // x = 0 in phase D); later, over the consumed parts: <dh', h> per wave at 4 C, the last
+  // token's shares at 5 C, dGc at 6 C, rowsum(E) per row half at 8 C, rowsum(dA * KK * Gam)
+  // per row half at 10 C
+  float* sPart = sBeta + C;
+  float* sRD = sPart + 16 * C;   // [4][C] the row dots (1: Delta.K dh', 2: dR.K h, 3: dR.V)
+  float* sColE = sRD + 4 * C;    // [4 row blocks][C] partial colsum(E)
+  float* sHdh = sPart + 4 * C;
+  float* sShare = sPart + 5 * C;
+  float* sDgc = sPart + 6 * C;
+  float* sRowE = sPart + 8 * C;
+  float* sRowB = sPart + 10 * C;
+
+  const long qk0 = ((long)start * Hg + hk) * D, v0 = ((long)start * H + h) * D;
+  const long hcoff = ((long)c * H + h) * D * D;
+  if (threadIdx.x < C) {
+    const int t = threadIdx.x;
+    sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
+    sBeta[t] = t < len ? load_beta(beta, beta_f32, (long)(start + t) * H + h) : 0.f;
+  }
+
+  // Global loads are issued a phase or more ahead of their LDS stores (each thread holds its
+  // share of a block in registers meanwhile).
+  Blk<TI, C, C, N2> bT;
+  Blk<TI, C, D, N2> bdD, bk, bq, bdl, bv;
+  Blk<TI, D, D, N2> bhT;
+  bT.load(Tinv + ((long)start * H + h) * C, (long)H * C, len);
+  bdD.load(dD + v0, (long)H * D, len);
+  bk.load(k + qk0, (long)Hg * D, len);
+  bq.load(q + qk0, (long)Hg * D, len);
+  bdl.load(v_new + v0, (long)H * D, len);
+  bv.load(v + v0, (long)H * D, len);
+  bhT.load(h_c + hcoff, D, D);
+
+  // ---- phase A: dR = T^T dDelta
+  bT.store_trn(sCC1, LDC);
+  bdD.store_trn(sBig, LDC);  // [D][LDC]
+  __syncthreads();
+  f32x4 dR[2][CBW];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) {
+      dR[b][m] = zero4();
+      mma_lds<TI>(dR[b][m], sCC1, LDC, 16 * (2 * rh + b), sBig, LDC, 16 * (cw + 4 * m), 0, C);
+    }
+  // dV = diag(beta) dR, and dR kept in LDS for the later products (rows past len are zero:
+  // T's columns past len are)
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) {
+      const int colx = 16 * (cw + 4 * m) + lc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        sC[t * LDD + colx] = (TI)dR[b][m][e];
+        if (t < len) dv[v0 + (long)t * H * D + colx] = sBeta[t] * dR[b][m][e];
+      }
+    }
+  __syncthreads();
+
+  // ---- phase B: K h and K dh' and three row dots
+  Blk<TI, D, D, N2> bdT;
+  Blk<TI, C, D, N2> bo;
+  bdT.load(dH + hcoff, D, D);
+  bo.load(dO + v0, (long)H * D, len);
+  bk.store_nat(sA, LDD);
+  bq.store_nat(sB, LDD);
+  bdl.store_nat(sDl, LDD);
+  bv.store_nat(sV, LDD);
+  bhT.store_trn(sBig, LDD);  // h^T
+  __syncthreads();
+  f32x4 Kh[2][CBW], Kd[2][CBW];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) {
+      Kh[b][m] = zero4();
+      mma_lds<TI>(Kh[b][m], sA, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);
+    }
+  Blk<TI, D, D, N2> bh;
+  bh.load(h_c + hcoff, D, D);
+  __syncthreads();
+  bdT.store_trn(sBig, LDD);  // dh'^T
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) {
+      Kd[b][m] = zero4();
+      mma_lds<TI>(Kd[b][m], sA, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);
+    }
+  // row dots over the wave's columns: Delta.K dh', dR.K h, dR.V (operands from LDS)
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * (2 * rh + b) + 4 * lg + e;
+      float p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+      for (int m = 0; m < CBW; ++m) {
+        const int gi = t * LDD + 16 * (cw + 4 * m) + lc;
+        const float r = (float)sC[gi];
+        p1 += (float)sDl[gi] * Kd[b][m][e];
+        p2 += r * Kh[b][m][e];
+        p3 += r * (float)sV[gi];
+      }
+      p1 = sum16(p1);
+      p2 = sum16(p2);
+      p3 = sum16(p3);
+      if (lc == 0) {
+        sPart[(4 + cw) * C + t] = p1;
+        sPart[(8 + cw) * C + t] = p2;
+        sPart[(12 + cw) * C + t] = p3;
+      }
+    }
+  __syncthreads();
+  if (threadIdx.x < 3 * C) {
+    const int x = 1 + threadIdx.x / C, t = threadIdx.x % C;
+    sRD[x * C + t] = sPart[(4 * x) * C + t] + sPart[(4 * x + 1) * C + t] +
+                     sPart[(4 * x + 2) * C + t] + sPart[(4 * x + 3) * C + t];
+  }
+
+  // ---- phase C: the C x C products and their elementwise terms
+  f32x4 KK[2], QK[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    KK[b] = QK[b] = zero4();
+    mma_lds<TI>(KK[b], sA, LDD, 16 * cw, sA, LDD, 16 * (2 * rh + b), 0, D);
+    mma_lds<TI>(QK[b], sB, LDD, 16 * cw, sA, LDD, 16 * (2 * rh + b), 0, D);
+  }
+  Blk<TI, D, D, N2> bd;
+  bd.load(dH + hcoff, D, D);
+  __syncthreads();  // (also: the row dots' parts are summed)
+  bo.store_nat(sA, LDD);  // dO
+  __syncthreads();
+  f32x4 E1[2], RD[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    E1[b] = RD[b] = zero4();
+    mma_lds<TI>(E1[b], sA, LDD, 16 * cw, sDl, LDD, 16 * (2 * rh + b), 0, D);
+    mma_lds<TI>(RD[b], sC, LDD, 16 * cw, sDl, LDD, 16 * (2 * rh + b), 0, D);
+  }
+  float rowE[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int j = 16 * (2 * rh + b) + lc;
+    float colE = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * cw + 4 * lg + e;
+      const bool in = i < len && j < len;
+      const float gam = (in && i >= j) ? __expf(sG[i] - sG[j]) : 0.f;
+      const float mi = (i >= j) ? scale * E1[b][e] * gam : 0.f;
+      const float da = (in && i > j) ? -RD[b][e] : 0.f;
+      const float db = sBeta[i] * da * gam;
+      const float ee = mi * QK[b][e] + db * KK[b][e];
+      rowE[e] += ee;
+      rowB[e] += da * KK[b][e] * gam;
+      colE += ee;
+      sCC1[i * LDC + j] = (TI)mi;
+      sCC2[j * LDC + i] = (TI)mi;
+      sCC3[i * LDC + j] = (TI)db;
+      sCC4[j * LDC + i] = (TI)db;
+    }
+    colE = sum4g(colE);
+    if (lg == 0) sColE[cw * C + j] = colE;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float re = sum16(rowE[e]), rb = sum16(rowB[e]);
+    if (lc == 0) {
+      sRowE[rh * C + 16 * cw + 4 * lg + e] = re;
+      sRowB[rh * C + 16 * cw + 4 * lg + e] = rb;
+    }
+  }
+
+  // ---- phase D: dQ and dK
+  f32x4 aq[2][CBW], ak[2][CBW];
+  Blk<TI, C, D, N2> bkt, bqt;
+  bkt.load(k + qk0, (long)Hg * D, len);
+  bqt.load(q + qk0, (long)Hg * D, len);
+  __syncthreads();
+  bh.store_nat(sBig, LDD);  // h
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) {
+      f32x4 x = zero4(), y = zero4();
+      mma_lds<TI>(x, sA, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);  // dO h^T
+      mma_lds<TI>(y, sC, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);  // dR h^T
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        aq[b][m][e] = x[e];  // scaled below, once Q . (dO h^T) is taken
+        ak[b][m][e] = -sBeta[t] * __expf(sG[t]) * y[e];
+      }
+    }
+    // rowsum(dO * Q h) = rowsum(Q * dO h^T), Q natural in sB
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * (2 * rh + b) + 4 * lg + e;
+      float p0 = 0.f;
+#pragma unroll
+      for (int m = 0; m < CBW; ++m)
+        p0 += (float)sB[t * LDD + 16 * (cw + 4 * m) + lc] * aq[b][m][e];
+      p0 = sum16(p0);
+      if (lc == 0) sPart[cw * C + t] = p0;
+      const float sg = scale * __expf(sG[t]);
+#pragma unroll
+      for (int m = 0; m < CBW; ++m) aq[b][m][e] *= sg;
+    }
+  }
+  {
+    // dh' (natural) over h, and <dh', h> from the h it replaces (parts per wave, in order)
+    const float part = sum4g(sum16(bd.dot_nat(sBig, LDD)));
+    if (l == 0) sHdh[w] = part;
+    __syncthreads();
+    bd.store_nat(sBig, LDD);
+  }
+  __syncthreads();
+  const float gC = sG[len - 1];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) {
+      f32x4 x = zero4();
+      mma_lds<TI>(x, sDl, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);  // Delta dh'^T
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        ak[b][m][e] += __expf(gC - sG[t]) * x[e];
+      }
+    }
+  bkt.store_trn(sB, LDC);  // K^T (Q natural in sB was last read before the barrier above)
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) {
+      const int r0 = 16 * (2 * rh + b), c0 = 16 * (cw + 4 * m);
+      mma_lds<TI>(aq[b][m], sCC1, LDC, r0, sB, LDC, c0, 0, C);  // Mi K
+      mma_lds<TI>(ak[b][m], sCC3, LDC, r0, sB, LDC, c0, 0, C);  // DB K
+      mma_lds<TI>(ak[b][m], sCC4, LDC, r0, sB, LDC, c0, 0, C);  // DB^T K
+    }
+  __syncthreads();
+  bqt.store_trn(sB, LDC);  // Q^T
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m)
+      mma_lds<TI>(ak[b][m], sCC2, LDC, 16 * (2 * rh + b), sB, LDC, 16 * (cw + 4 * m), 0, C);  // Mi^T Q
+  const long dq0 = ((long)start * qk_rows + hq) * D;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        if (t < len) {
+          const long gi = dq0 + (long)t * qk_rows * D + 16 * (cw + 4 * m) + lc;
+          dq[gi] = aq[b][m][e];
+          dk[gi] = ak[b][m][e];
+        }
+      }
+
+  // ---- dbeta and dg (one thread per token; dg is the suffix sum of dGc in the chunk)
+  if (threadIdx.x < C) {
+    const int t = threadIdx.x;
+    float dgc = 0.f, db = 0.f;
+    if (t < len) {
+      const float gam = __expf(sG[t]), r = __expf(gC - sG[t]);
+      const float colE = sColE[t] + sColE[C + t] + sColE[2 * C + t] + sColE[3 * C + t];
+      const float rq = sPart[t] + sPart[C + t] + sPart[2 * C + t] + sPart[3 * C + t];
+      db = sRD[3 * C + t] - gam * sRD[2 * C + t] + sRowB[t] + sRowB[C + t];
+      dgc = scale * gam * rq - r * sRD[C + t] - sBeta[t] * gam * sRD[2 * C + t] +
+            sRowE[t] + sRowE[C + t] - colE;
+      sShare[t] = r * sRD[C + t];  // the last token's share of h' = gC h + ...
+    }
+    sDgc[t] = dgc;
+    if (t < len) dbeta[(long)(start + t) * H + h] = db;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // the last token: + sum_t (gC / gam_t) rowsum(Delta * K dh')_t + gC <dh', h>, then the
+    // suffix sums in token order (fixed order: deterministic)
+    float hdh = 0.f;
+    for (int i = 0; i < kBT2 / 64; ++i) hdh += sHdh[i];
+    float s = 0.f;
+    for (int t = 0; t < len; ++t) s += sShare[t];
+    sDgc[len - 1] += s + __expf(gC) * hdh;
+    float acc = 0.f;
+    for (int t = len - 1; t >= 0; --t) {
+      acc += sDgc[t];
+      dg[(long)(start + t) * H + h] = acc;
+    }
+  }
+}
+
+// dq[t][hk] = sum of the value heads' dq[t][hk G .. hk G + G - 1] (and dk the same).
+__global__ __launch_bounds__(256) void k_bwd_group_sum(const float* __restrict__ dqh,
+                                                       const float* __restrict__ dkh,
+                                                       float* __restrict__ dq,
+                                                       float* __restrict__ dk, long rows,
+                                                       int Hg, int G, int D) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // over rows * Hg * D
+  const long total = rows * Hg * D;
+  if (i >= total) return;
+  const long t = i / ((long)Hg * D);
+  const int rem = (int)(i - t * Hg * D), hk = rem / D, d = rem - hk * D;
+  float sq = 0.f, sk = 0.f;
+  for (int r = 0; r < G; ++r) {
+    const long j = (t * Hg * G + (long)hk * G + r) * D + d;
+    sq += dqh[j];
+    sk += dkh[j];
+  }
+  dq[i] = sq;
+  dk[i] = sk;
+}
+
+template <typename F>
+hipError_t set_lds(F f, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(f),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+#define GDN_BTRY(x)                     \
+  do {                                  \
+    hipError_t e_ = (x);                \
+    if (e_ != hipSuccess) return e_;    \
+  } while (0)
+
+template <typename TI, int D>
+hipError_t run_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st) {
+  const TI* q = static_cast<const TI*>(p.q);
+  const TI* k = static_cast<const TI*>(p.k);
+  const TI* v = static_cast<const TI*>(p.v);
+  const TI* dO = static_cast<const TI*>(b.dO);
+  const size_t sm1 = dh_smem<TI, D>();
+  GDN_BTRY(set_lds(k_bwd_dh<TI, D>, sm1));
+  k_bwd_dh<TI, D><<<dim3(p.N, p.H, D / 64), kBT, sm1, st>>>(
+      b.st.table, b.st.seq_chunks, q, k, static_cast<const TI*>(b.st.W),
+      dO, b.st.g_t, b.dht, static_cast<TI*>(b.dH), static_cast<TI*>(b.dD), b.dh0, p.Ttot,
+      p.H, p.Hg, p.scale);
+  GDN_BTRY(hipGetLastError());
+  const bool grouped = p.H != p.Hg;
+  const size_t sm2 = ChunkLds<TI, D>::bytes;
+  GDN_BTRY(set_lds(k_bwd_chunk<TI, D>, sm2));
+  k_bwd_chunk<TI, D><<<dim3(p.max_chunks, p.H), kBT2, sm2, st>>>(
+      b.st.table, q, k, v, p.beta, p.beta_f32 ? 1 : 0, b.st.g_t,
+      static_cast<const TI*>(b.st.Tinv), static_cast<const TI*>(b.st.h_c),
+      static_cast<const TI*>(b.st.v_new), static_cast<const TI*>(b.dD),
+      static_cast<const TI*>(b.dH), dO, grouped ? b.dqh : b.dq,
+      grouped ? b.dkh : b.dk, b.dv, b.dg, b.dbeta, grouped ? p.H : p.Hg, p.Ttot, p.H, p.Hg,
+      p.scale);
+  GDN_BTRY(hipGetLastError());
+  if (grouped) {
+    const long total = (long)p.Ttot * p.Hg * D;
+    k_bwd_group_sum<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
+        b.dqh, b.dkh, b.dq, b.dk, p.Ttot, p.Hg, p.H / p.Hg, D);
+    GDN_BTRY(hipGetLastError());
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+bool bwd_supported(const Problem& p) {
+  return p.f32 ? p.D == 64 : (p.D == 64 || p.D == 128);
+}
+
+hipError_t launch_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st) {
+  if (p.f32) return run_bwd<float, 64>(p, b, st);
+  return p.D == 64 ? run_bwd<bf16, 64>(p, b, st) : run_bwd<bf16, 128>(p, b, st);
+}
+
+}  // namespace gdn

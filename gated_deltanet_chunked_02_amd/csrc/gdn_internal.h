@@ -54,6 +54,29 @@ struct Stages {
 };
 
 hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st);
+
+// Backward pass: the staged forward's intermediates (stages 0-6 at C = 64) plus the
+// gradient buffers.  dq, dk: [Ttot, Hg, D]; dv: [Ttot, H, D]; dg, dbeta: [Ttot, H];
+// dh0: [N, H, D, D] or NULL; all fp32.  dD [Ttot, H, D] and dH [max_chunks, H, D, D] (the
+// gradient of each chunk's end state), in the q/k/v dtype, are workspace; dqh, dkh
+// [Ttot, H, D] fp32 too when H != Hg (per value head, summed over the group afterwards).
+struct BwdBuffers {
+  Stages st;
+  const void* dO;
+  const float* dht;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;
+  void* dD;
+  void* dH;
+  float* dqh;
+  float* dkh;
+};
+bool bwd_supported(const Problem& p);
+hipError_t launch_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st);
 bool fused_supported(const Problem& p);
 hipError_t launch_fused(const Problem& p, hipStream_t st);
 // Longest-first order of a packed batch's sequences (order[rank] = sequence), for the fused

@@ -190,3 +190,19 @@ def draw_gating(w: Workload, B: int, T: int, device="cpu"):
     A_log = torch.log(torch.rand((w.H,), generator=gen, device=dev) * 15.0 + 1.0)
     dt_bias = torch.randn((w.H,), generator=gen, device=dev) * 0.5 - 4.0
     return dict(a=a, b=b, A_log=A_log, dt_bias=dt_bias)
+
+
+# ---------------------------------------------------------------- backward inputs
+def draw_grads(w: Workload, B: int, T: int, N: int, device="cpu", dht_std=0.1):
+    """Upstream gradients for the backward pass, for a [B, T] token layout and N sequences
+    (those of ``draw(w)``).  Own generator (seed + 2000), draw order do, dht:
+      * do ~ N(0, 1) per output element, cast to the q/k/v dtype;
+      * dht ~ N(0, dht_std^2) fp32 [N, H, Dk, Dv] (None when dht_std is None)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 2000)
+    do = torch.randn((B, T, w.H, w.Dv), generator=gen, device=dev).to(DTYPES[w.dtype])
+    dht = None
+    if dht_std is not None:
+        dht = torch.randn((N, w.H, w.Dk, w.Dv), generator=gen, device=dev) * dht_std
+    return dict(do=do, dht=dht)

@@ -218,6 +218,37 @@ gdn_status gdn_fused_sigmoid_gating_delta_rule(const gdn_desc* d, const void* q,
                                                float scale, void* o, float* ht,
                                                hipStream_t stream);
 
+/* Bytes of workspace gdn_chunk_bwd needs for this descriptor (N other than 0 or B reads as a
+ * packed batch of N sequences, anything else as B dense sequences).  Host-only, no device
+ * work.  Returns 0 and sets *status on an invalid or unsupported descriptor. */
+size_t gdn_chunk_bwd_workspace_size(const gdn_desc* d, gdn_status* status);
+
+/* The backward pass of gdn_chunk_fwd (the FlashQLA how-to reports forward and backward
+ * speed-ups of the chunked operator, section 4.3; none of the pages prints the backward's
+ * formulas).  Given the forward's inputs and the gradients of its outputs, it writes the
+ * gradients of its inputs: the exact derivative of the recurrence, computed chunk by chunk
+ * (C = 64) from the WY form's quantities, which it recomputes into the workspace with the
+ * staged forward's stages 0-6 (nothing of a forward call is kept).
+ *   dout  [B, T, H, Dv]   qkv_dtype   gradient of o (required)
+ *   dht   [N, H, Dk, Dv]  f32         gradient of ht, or NULL (zero)
+ *   dq, dk [B, T, Hg, Dk] f32         the q/k heads' gradients (summed over the value heads
+ *                                     that share them)
+ *   dv    [B, T, H, Dv]   f32
+ *   dg, dbeta [B, T, H]   f32
+ *   dh0   [N, H, Dk, Dv]  f32         gradient of h0, or NULL (not written)
+ * Inputs, scale, cu_seqlens and their layouts as for gdn_chunk_fwd (h0 NULL = zero state).
+ * Supported: bf16 with Dk = Dv in {64, 128}; f32 with Dk = Dv = 64 (else
+ * GDN_ERR_UNSUPPORTED).  d->variant, d->chunk and d->stop_after are ignored.  The workspace
+ * (d->workspace, 256-byte aligned, gdn_chunk_bwd_workspace_size bytes) is required when
+ * B*T > 0, else GDN_ERR_WORKSPACE.  Results do not depend on scheduling (no atomics).
+ * Pointers are device pointers aligned to 16 bytes (g, beta, dg, dbeta, cu_seqlens: 4 / 2 /
+ * 4 / 4 / 4).  With B*T = 0 only dh0 is written (= dht, or zeros). */
+gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const void* v,
+                         const float* g, const void* beta, const float* h0,
+                         const int32_t* cu_seqlens, float scale, const void* dout,
+                         const float* dht, float* dq, float* dk, float* dv, float* dg,
+                         float* dbeta, float* dh0, hipStream_t stream);
+
 /* Bytes of device scratch the library holds on each GPU for gdn_chunk_fwd_noalloc. */
 #define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

@@ -417,3 +417,87 @@ def test_gating_binding_validates_its_tensors(lib):
     with pytest.raises(ValueError):
         gdn.fused_sigmoid_gating_delta_rule(a["q"], a["k"], a["v"], a["a"], a["beta"],
                                             a["A_log"], inplace_final_state=True)
+
+
+# ------------------------------------------------------------------ backward entry
+def bwd_ws(d):
+    st = ctypes.c_int(-1)
+    n = gdn.load().gdn_chunk_bwd_workspace_size(ctypes.byref(d), ctypes.byref(st))
+    return st.value, n
+
+
+def test_bwd_workspace_covers_the_staged_stages_and_its_gradient_buffers(lib):
+    # bf16 D = 128, dense B = 2, T = 256, H = 4, Hg = 2: the staged layout at C = 64, then
+    # dDelta [Ttot, H, D] and the chunk-end state gradients [max_chunks, H, D, D] in bf16,
+    # and (grouped heads) per-value-head dq and dk [Ttot, H, D] fp32
+    d = desc(chunk=128)
+    st, n = bwd_ws(d)
+    assert st == 0
+    staged = gdn.gdn_chunk_fwd_workspace_size(desc(chunk=64, variant=1))
+    Ttot, H, D = 512, 4, 128
+    max_chunks = Ttot // 64 + 2
+    tok = Ttot * H * D * 4
+    # dDelta and dh' in bf16, the rest fp32
+    assert n == staged + tok // 2 + 2 * tok + max_chunks * H * D * D * 2
+    # without grouped heads no per-value-head buffers
+    st, n2 = bwd_ws(desc(Hg=4))
+    assert st == 0 and n2 == gdn.gdn_chunk_fwd_workspace_size(
+        desc(Hg=4, chunk=64, variant=1)) + tok // 2 + max_chunks * H * D * D * 2
+    # supported: bf16 D 64 / 128, fp32 D 64
+    assert bwd_ws(desc(Dk=256, Dv=256))[0] == 2
+    assert bwd_ws(desc(qkv_dtype=0, Dk=128, Dv=128))[0] == 2
+    assert bwd_ws(desc(qkv_dtype=0, Dk=64, Dv=64))[0] == 0
+    assert bwd_ws(desc(Dk=64, Dv=64))[0] == 0
+    # the chunk, variant and stop_after fields do not change it
+    assert bwd_ws(desc(chunk=64, variant=2))[1] == n
+    # a packed batch of N sequences bounds its chunks by ceil(Ttot / 64) + N
+    st, npk = bwd_ws(desc(B=1, T=512, N=5))
+    assert st == 0 and npk > n
+
+
+def test_bwd_rejects_bad_arguments_before_any_launch(lib):
+    A = 0x10000  # fake, aligned: every case below must fail (or finish) before any launch
+
+    def call(dd=None, **kw):
+        args = dict(q=A, k=A, v=A, g=A, beta=A, h0=None, cu=None, do=A, dht=None, dq=A, dk=A,
+                    dv=A, dg=A, dbeta=A, dh0=None)
+        args.update(kw)
+        return lib.gdn_chunk_bwd(
+            ctypes.byref(dd or desc()), args["q"], args["k"], args["v"], args["g"],
+            args["beta"], args["h0"], args["cu"], 0.1, args["do"], args["dht"], args["dq"],
+            args["dk"], args["dv"], args["dg"], args["dbeta"], args["dh0"], None)
+
+    for name in ("q", "do", "dq", "dk", "dv", "dg", "dbeta"):
+        assert call(**{name: None}) == 1, name
+    assert call(do=A + 2) == 1                            # misaligned dout
+    assert call(dg=A + 2) == 1                            # misaligned dg
+    assert call(dh0=A + 8) == 1
+    assert call(desc(Dk=256, Dv=256)) == 2
+    assert call(desc(qkv_dtype=0)) == 2                   # fp32 only at D = 64
+    assert call(desc(N=3)) == 1                           # dense: N must equal B
+    assert call(desc(B=2, N=2), cu=A) == 1                # packed needs B == 1
+    assert call() == 3                                    # no workspace
+    assert call(desc(workspace=A, workspace_bytes=4096)) == 3
+    assert call(desc(workspace=A + 16, workspace_bytes=1 << 40)) == 3  # misaligned
+    assert call(desc(B=1, N=0, T=0), cu=A) == 0           # no sequences: nothing to do
+    assert call(desc(T=0)) == 0                           # no tokens and no dh0: nothing
+
+
+def test_bwd_binding_validates_its_tensors(lib):
+    import torch
+    bf = torch.bfloat16
+    bad = [
+        (dict(do=torch.zeros(1, 8, 4, 64)), TypeError),                 # do dtype
+        (dict(do=torch.zeros(1, 8, 2, 64, dtype=bf)), ValueError),      # do shape
+        (dict(dht=torch.zeros(1, 4, 64, 32)), ValueError),              # dht shape
+        (dict(dht=torch.zeros(1, 4, 64, 64, dtype=torch.int32)), TypeError),
+        (dict(g=torch.zeros(1, 8, 4, dtype=bf)), TypeError),            # forward checks too
+        (dict(), ValueError),                                           # host tensors
+    ]
+    for over, exc in bad:
+        a = gdn_args()
+        a.update(do=torch.zeros(1, 8, 4, 64, dtype=bf), dht=None)
+        a.update(over)
+        with pytest.raises(exc):
+            gdn.chunk_gated_delta_rule_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["do"],
+                                           dht=a["dht"], initial_state=a["initial_state"])

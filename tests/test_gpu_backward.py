@@ -1,0 +1,190 @@
+"""GPU parity of the backward pass (gdn_chunk_bwd) against the fp64 oracle's reverse-mode
+derivative of the token recurrence (oracle.backward, itself pinned by finite differences),
+through the C ABI.  Every gradient is compared over the whole tensor by relative L2 error:
+fp32 inputs at 1e-5 (fp32 matrix-core products throughout), bf16 inputs at 1e-2 (the
+backward rounds its matrix-core operands and its stored intermediates to bf16, as the
+forward does: a relative error of about 2^-9 per rounding, a few roundings deep).  Sizes
+span several 64-token chunks and a ragged tail; varlen batches hold empty and one-token
+sequences; the full-size case samples (sequence, head) pairs of the 16 x 8192 workload."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs
+from gdn_testlib import log, rel_l2, to64
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def tol(dtype, name):
+    return 1e-5 if dtype == "f32" else 1e-2
+
+
+def draw(B=1, T=200, H=4, Hg=2, D=128, dtype="bf16", seed=0, h0=True, dht=True, lens=None,
+         beta_dtype=""):
+    w = gdn_inputs.small(B=B, T=T, H=H, Hg=Hg, Dk=D, dtype=dtype, seed=seed,
+                         h0_std=0.05 if h0 else None, beta_dtype=beta_dtype)
+    N = B
+    if lens is not None:
+        w = w.with_(B=1, T=int(sum(lens)))
+        N = len(lens)
+    inp = gdn_inputs.draw(w, device="cpu")
+    if lens is not None:
+        inp["cu_seqlens"] = torch.from_numpy(
+            np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+        if h0:
+            inp["h0"] = torch.randn(N, H, D, D, generator=torch.Generator().manual_seed(seed)) * 0.05
+    Bx, Tx = inp["g"].shape[:2]
+    inp.update(gdn_inputs.draw_grads(w, Bx, Tx, N, dht_std=0.1 if dht else None))
+    return inp
+
+
+def oracle_bwd(inp):
+    from oracle import backward
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy()
+    h0 = None if inp["h0"] is None else inp["h0"].double().numpy()
+    dht = None if inp["dht"] is None else inp["dht"].double().numpy()
+    f = lambda x: x.double().numpy()
+    return backward.recurrence_backward(f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["g"]),
+                                        f(inp["beta"]), h0, inp["scale"], f(inp["do"]), dht,
+                                        cu_seqlens=cu)
+
+
+def run_bwd(inp):
+    from gated_deltanet_chunked_02_amd import chunk_gated_delta_rule_bwd
+    dev = torch.device("cuda")
+    mv = lambda t: None if t is None else t.to(dev)
+    out = chunk_gated_delta_rule_bwd(
+        mv(inp["q"]), mv(inp["k"]), mv(inp["v"]), mv(inp["g"]), mv(inp["beta"]),
+        mv(inp["do"]), dht=mv(inp["dht"]), scale=inp["scale"], initial_state=mv(inp["h0"]),
+        cu_seqlens=mv(inp["cu_seqlens"]))
+    torch.cuda.synchronize()
+    return out
+
+
+def compare(inp, got, ref, dtype, label):
+    errs = {}
+    for name, x, r in zip(NAMES, got, ref):
+        if name == "dh0" and inp["h0"] is None:
+            assert x is None
+            continue
+        x = to64(x)
+        assert np.isfinite(x).all(), (label, name)
+        errs[name] = rel_l2(x, r)
+    log(test="backward", case=label, **errs)
+    for name, e in errs.items():
+        assert e <= tol(dtype, name), (label, name, e, errs)
+    return errs
+
+
+CASES = [
+    # B, T, H, Hg, D, dtype, h0, dht
+    (2, 200, 4, 2, 128, "bf16", True, True),
+    (2, 130, 2, 2, 64, "bf16", False, False),
+    (1, 150, 4, 1, 64, "bf16", True, True),
+    (1, 256, 2, 2, 64, "f32", True, True),
+    (2, 77, 2, 1, 64, "f32", False, True),
+    (3, 64, 2, 2, 128, "bf16", True, False),
+]
+
+
+@pytest.mark.parametrize("B,T,H,Hg,D,dtype,h0,dht", CASES)
+def test_backward_matches_oracle(B, T, H, Hg, D, dtype, h0, dht):
+    inp = draw(B=B, T=T, H=H, Hg=Hg, D=D, dtype=dtype, seed=B * 7 + T + D, h0=h0, dht=dht)
+    compare(inp, run_bwd(inp), oracle_bwd(inp), dtype,
+            "B%d T%d H%d Hg%d D%d %s" % (B, T, H, Hg, D, dtype))
+
+
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "bf16"), (64, "f32")])
+def test_backward_varlen_with_empty_and_short_sequences(D, dtype):
+    lens = [70, 0, 1, 64, 129, 5]
+    inp = draw(H=4, Hg=2, D=D, dtype=dtype, seed=31, lens=lens)
+    got = run_bwd(inp)
+    ref = oracle_bwd(inp)
+    compare(inp, got, ref, dtype, "varlen D%d %s" % (D, dtype))
+    # the empty sequence's state passes through: its dh0 is its dht, exactly
+    assert torch.equal(got[5][1].cpu(), inp["dht"][1])
+    # per-sequence errors (a short sequence must not hide behind the long ones)
+    cu = inp["cu_seqlens"].numpy()
+    for n in range(len(lens)):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        if s1 == s0:
+            continue
+        e = rel_l2(to64(got[2])[:, s0:s1], ref[2][:, s0:s1])
+        assert e <= tol(dtype, "dv"), (n, e)
+
+
+def test_backward_fp32_beta_with_bf16_inputs():
+    inp = draw(B=1, T=100, H=2, Hg=2, D=128, seed=41, beta_dtype="f32")
+    assert inp["beta"].dtype == torch.float32 and inp["q"].dtype == torch.bfloat16
+    compare(inp, run_bwd(inp), oracle_bwd(inp), "bf16", "bf16 fp32-beta")
+
+
+def test_backward_beta_zero_closed_form():
+    """beta = 0: the state only decays (h_t = e^{G_t} h0), so o_t = scale e^{G_t} h0^T q_t;
+    then dq_t = scale e^{G_t} h0 do_t, dk = dv = 0 and dh0 = sum_t scale e^{G_t} q_t do_t^T +
+    e^{G_T} dht, in closed form (fp32 inputs)."""
+    inp = draw(B=1, T=90, H=2, Hg=2, D=64, dtype="f32", seed=43)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    dq, dk, dv, dg, dbeta, dh0 = run_bwd(inp)
+    G = np.cumsum(inp["g"].double().numpy()[0], axis=0)  # [T, H]
+    q, do = inp["q"].double().numpy()[0], inp["do"].double().numpy()[0]
+    h0, dht = inp["h0"].double().numpy()[0], inp["dht"].double().numpy()[0]
+    s = inp["scale"]
+    for h in range(2):
+        e = np.exp(G[:, h])
+        dq_ref = s * e[:, None] * (do[:, h] @ h0[h].T)
+        dh0_ref = s * (q[:, h] * e[:, None]).T @ do[:, h] + e[-1] * dht[h]
+        assert rel_l2(to64(dq)[0, :, h], dq_ref) <= 1e-5
+        assert rel_l2(to64(dh0)[0, h], dh0_ref) <= 1e-5
+    assert float(dk.abs().max()) == 0.0
+    assert float(dv.abs().max()) == 0.0
+
+
+def test_backward_empty_token_axis_passes_dht():
+    from gated_deltanet_chunked_02_amd import chunk_gated_delta_rule_bwd
+    dev = torch.device("cuda")
+    q = torch.empty(2, 0, 2, 64, dtype=torch.bfloat16, device=dev)
+    g = torch.empty(2, 0, 2, device=dev)
+    h0 = torch.zeros(2, 2, 64, 64, device=dev)
+    dht = torch.randn(2, 2, 64, 64, generator=torch.Generator().manual_seed(3)).to(dev)
+    out = chunk_gated_delta_rule_bwd(q, q, q, g, g.to(torch.bfloat16), q, dht=dht,
+                                     initial_state=h0)
+    torch.cuda.synchronize()
+    assert out[0].shape == (2, 0, 2, 64) and torch.equal(out[5], dht)
+    out = chunk_gated_delta_rule_bwd(q, q, q, g, g.to(torch.bfloat16), q, initial_state=h0)
+    torch.cuda.synchronize()
+    assert float(out[5].abs().max()) == 0.0
+
+
+def test_backward_is_deterministic():
+    inp = draw(B=2, T=300, H=4, Hg=1, D=128, seed=47)
+    a = run_bwd(inp)
+    b = run_bwd(inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_full_size_sampled_pairs():
+    """16 x 8192, H = 32, D = 128, bf16, no initial state: the whole backward on the GPU,
+    two (sequence, head) pairs checked against the oracle (dq, dk, dv, dg, dbeta of the
+    pair's tokens; q/k heads are not shared here, so a pair's dq and dk are its own)."""
+    from oracle import backward
+    w = gdn_inputs.WORKLOADS["headline"]
+    inp = gdn_inputs.draw(w, device="cpu")
+    inp.update(gdn_inputs.draw_grads(w, w.B, w.T, w.B, dht_std=None))
+    got = run_bwd(inp)
+    f = lambda x: x.double().numpy()
+    for n, h in ((0, 0), (15, 31)):
+        sl = lambda x: f(x[n:n + 1, :, h:h + 1])
+        ref = backward.recurrence_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]),
+                                           sl(inp["g"]), sl(inp["beta"]), None, inp["scale"],
+                                           sl(inp["do"]), None)
+        errs = {}
+        for name, x, r in zip(NAMES[:5], got[:5], ref[:5]):
+            errs[name] = rel_l2(to64(x[n:n + 1, :, h:h + 1]), r)
+        log(test="backward_fullsize", pair=[n, h], **errs)
+        for name, e in errs.items():
+            assert e <= tol("bf16", name), (n, h, name, e)
