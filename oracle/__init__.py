@@ -65,15 +65,23 @@ def use_native() -> str:
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    """The host CPU's model name as lscpu reports it (from /proc/cpuinfo), with its x86
+    family and model numbers, which identify the generation when the name is generic."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.lower().startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    key, val = line.split(":", 1)
+                    info.setdefault(key.strip().lower(), val.strip())
+                if line.strip() == "":
+                    break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    if "cpu family" in info and "model" in info:
+        name += " (x86 family %s, model %s)" % (info["cpu family"], info["model"])
+    return name
 
 
 def _load(path=None):
