@@ -221,15 +221,16 @@ size_t workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
   return L.total;
 }
 
-// The backward pass recomputes the staged forward's stages 0-6 at C = 64 into the front of
-// its workspace, then keeps dDelta [Ttot, H, D] and each chunk's end-state gradient
-// [max_chunks, H, D, D] in the q/k/v dtype and (H != Hg) per-value-head dq and dk
-// [Ttot, H, D] in fp32.
+// The backward pass recomputes the forward's chunk quantities at C = 64 into the staged
+// layout at the front of its workspace (stages 0-4, then the chunk-start states and v_new
+// from the fused kernel's store mode in bf16, or from stages 5-6 in fp32), then keeps dR
+// [Ttot, H, D] and each chunk's end-state gradient [max_chunks, H, D, D] in the q/k/v dtype
+// and (H != Hg) per-value-head dq and dk [Ttot, H, D] in fp32.
 constexpr int kBwdChunk = 64;
 
 struct BwdLayout {
   Layout st;
-  size_t dD, dH, dqh, dkh, total;
+  size_t dR, dH, dqh, dkh, total;
 };
 
 // Shape part of a backward call: the forward's checks with the chunk set to 64 and N as the
@@ -254,8 +255,8 @@ BwdLayout bwd_layout(const gdn::Problem& p) {
   staged_layout(p, &L.st);
   const size_t e = p.f32 ? 4 : 2;
   const size_t tok = (size_t)p.Ttot * p.H * p.D * sizeof(float);
-  L.dD = L.st.total;
-  L.dH = L.dD + align_up((size_t)p.Ttot * p.H * p.D * e);
+  L.dR = L.st.total;
+  L.dH = L.dR + align_up((size_t)p.Ttot * p.H * p.D * e);
   const size_t hb = (size_t)p.max_chunks * p.H * p.D * p.D * e;
   L.dqh = L.dH + align_up(hb);
   const bool grouped = p.H != p.Hg;
@@ -535,11 +536,25 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
   b.dg = dg;
   b.dbeta = dbeta;
   b.dh0 = dh0;
-  b.dD = ws + L.dD;
+  b.dR = ws + L.dR;
   b.dH = ws + L.dH;
   b.dqh = p.H != p.Hg ? reinterpret_cast<float*>(ws + L.dqh) : nullptr;
   b.dkh = p.H != p.Hg ? reinterpret_cast<float*>(ws + L.dkh) : nullptr;
-  hipError_t e = gdn::launch_staged(p, b.st, 6, stream);
+  hipError_t e;
+  if (gdn::fused_supported(p)) {
+    // stages 0-4 (chunk table, Gc, T), then h_c and v_new from the fused kernel
+    e = gdn::launch_staged(p, b.st, 4, stream);
+    if (e == hipSuccess) {
+      gdn::Problem pf = p;
+      pf.fused_flags = gdn::kFusedNoOutput;
+      pf.seq_chunks = b.st.seq_chunks;
+      pf.hc_out = b.st.h_c;
+      pf.vnew_out = b.st.v_new;
+      e = gdn::launch_fused(pf, stream);
+    }
+  } else {
+    e = gdn::launch_staged(p, b.st, 6, stream);
+  }
   if (e == hipSuccess) e = gdn::launch_bwd(p, b, stream);
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

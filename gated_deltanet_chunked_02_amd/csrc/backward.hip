@@ -150,13 +150,15 @@ __device__ __forceinline__ float sum4g(float x) {
 }
 
 // ------------------------------------------------------------------------- dh pass
-// LDS: R0 [C][LDD] holds Q and then P^T ([C][LDC]); K [C][LDD]; Q^T, W^T [D][LDC]; this
-// slab of dO transposed [64][LDC]; the chunk's Gc [C].  (About 80 KB at D = 128 in bf16:
-// two workgroups per CU.)
+// With W = T diag(beta gam) K, the update's W^T dDelta is K^T diag(beta gam) dR, dR = T^T
+// dDelta: the pass reads rows of T (C x C) instead of W (C x D), and hands dR to the chunk
+// kernel.  LDS: R0 [C][LDD] holds Q and then P^T ([C][LDC]); K [C][LDD]; Q^T, K^T [D][LDC];
+// T^T [C][LDC]; this slab of dO transposed [64][LDC]; Gc and beta [C].
 template <typename TI, int D>
 constexpr size_t dh_smem() {
   constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>();
-  return (2 * kBC * LDD + 2 * D * LDC + 64 * LDC) * sizeof(TI) + kBC * sizeof(float);
+  return (2 * kBC * LDD + 2 * D * LDC + kBC * LDC + 64 * LDC) * sizeof(TI) +
+         2 * kBC * sizeof(float);
 }
 
 template <typename TI, int D>
@@ -164,11 +166,12 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
                                                 const int32_t* __restrict__ seq_chunks,
                                                 const TI* __restrict__ q,
                                                 const TI* __restrict__ k,
-                                                const TI* __restrict__ W,
+                                                const TI* __restrict__ Tinv,
+                                                const void* __restrict__ beta, int beta_f32,
                                                 const TI* __restrict__ dO,
                                                 const float* __restrict__ g_t,
                                                 const float* __restrict__ dht,
-                                                TI* __restrict__ dH, TI* __restrict__ dD,
+                                                TI* __restrict__ dH, TI* __restrict__ dRo,
                                                 float* __restrict__ dh0, int Ttot, int H,
                                                 int Hg, float scale) {
   constexpr int C = kBC, NDK = D / 16, NT = C / 16;
@@ -183,9 +186,11 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
   TI* sPt = sQ;                          // [C][LDC]  P^T, once P is in registers
   TI* sK = sQ + C * LDD;                 // [C][LDD]
   TI* sQt = sK + C * LDD;                // [D][LDC]  Q^T
-  TI* sWt = sQt + D * LDC;               // [D][LDC]  W^T
-  TI* sOt = sWt + D * LDC;               // [64][LDC] this slab of dO, transposed
+  TI* sKt = sQt + D * LDC;               // [D][LDC]  K^T
+  TI* sTt = sKt + D * LDC;               // [C][LDC]  T^T
+  TI* sOt = sTt + C * LDC;               // [64][LDC] this slab of dO, transposed
   float* sG = reinterpret_cast<float*>(sOt + 64 * LDC);
+  float* sBeta = sG + C;
 
   // dh tile db: rows (key index) 16 db + 4 (l/16) + e, column col
   f32x4 dh[NDK];
@@ -199,9 +204,10 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
   // the chunk's operands are loaded one chunk ahead (into registers) while the previous one
   // is computed
   const int c0 = seq_chunks[n], c1 = seq_chunks[n + 1];
-  Blk<TI, C, D> bq, bk, bw;
+  Blk<TI, C, D> bq, bk;
+  Blk<TI, C, C> bt;
   Blk<TI, C, 64> bo;
-  float gt = 0.f;
+  float gt = 0.f, bet = 0.f;
   int glen = 0;
   auto fetch = [&](int c) {
     const int4 ci = chunk_of(table, c);
@@ -209,9 +215,11 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
     const long qk0 = ((long)start * Hg + hk) * D, v0 = ((long)start * H + h) * D;
     bq.load(q + qk0, (long)Hg * D, len);
     bk.load(k + qk0, (long)Hg * D, len);
-    bw.load(W + v0, (long)H * D, len);
+    bt.load(Tinv + ((long)start * H + h) * C, (long)H * C, len);
     bo.load(dO + v0 + blockIdx.z * 64, (long)H * D, len);
-    gt = g_t[(long)h * Ttot + start + min((int)threadIdx.x, len - 1)];
+    const int tt = min((int)threadIdx.x, len - 1);
+    gt = g_t[(long)h * Ttot + start + tt];
+    bet = load_beta(beta, beta_f32, (long)(start + tt) * H + h);
     glen = len;
   };
   if (c1 > c0) fetch(c1 - 1);
@@ -223,9 +231,14 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
     bq.store_nat(sQ, LDD);
     bq.store_trn(sQt, LDC);
     bk.store_nat(sK, LDD);
-    bw.store_trn(sWt, LDC);
+    bk.store_trn(sKt, LDC);
+    bt.store_trn(sTt, LDC);
     bo.store_trn(sOt, LDC);
-    if (threadIdx.x < C) sG[threadIdx.x] = (int)threadIdx.x < glen ? gt : 0.f;
+    if (threadIdx.x < C) {
+      const bool in = (int)threadIdx.x < glen;
+      sG[threadIdx.x] = in ? gt : 0.f;
+      sBeta[threadIdx.x] = in ? bet : 0.f;
+    }
     if (c > c0) fetch(c - 1);
     __syncthreads();
     // P[i][j] = scale (q_i . k_j) e^{Gc_i - Gc_j} for j <= i < len (wave w: 4 of the 16 tiles)
@@ -265,7 +278,14 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
         dd[tb][e] = t < len ? a[e] + __expf(gC - sG[t]) * x[e] : 0.f;
       }
     }
-    // the chunk-end gradient dh' and dDelta, for the chunk-parallel kernel
+    // dR = T^T dDelta
+    f32x4 dr[NT];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+      dr[tb] = zero4();
+      mma_accB<TI, NT>(dr[tb], sTt, LDC, 16 * tb, 0, dd, NT);
+    }
+    // the chunk-end gradient dh' and dR, for the chunk-parallel kernel
     const long coff = ((long)c * H + h) * D * D;
 #pragma unroll
     for (int db = 0; db < NDK; ++db)
@@ -277,23 +297,24 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * tb + 4 * (l >> 4) + e;
-        if (t < len) dD[v0 + (long)t * H * D + col] = (TI)dd[tb][e];
+        if (t < len) dRo[v0 + (long)t * H * D + col] = (TI)dr[tb][e];
       }
-    // dh = gC dh' + scale Q^T diag(gam) dO - W^T dDelta
+    // dh = gC dh' + scale Q^T diag(gam) dO - K^T diag(beta gam) dR
     f32x4 go[NT], nd[NT];
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * tb + 4 * (l >> 4) + e;
-        go[tb][e] = t < len ? scale * __expf(sG[t]) * (float)sOt[scol * LDC + t] : 0.f;
-        nd[tb][e] = -dd[tb][e];
+        const float gam = t < len ? __expf(sG[t]) : 0.f;
+        go[tb][e] = scale * gam * (float)sOt[scol * LDC + t];
+        nd[tb][e] = -sBeta[t] * gam * dr[tb][e];
       }
 #pragma unroll
     for (int db = 0; db < NDK; ++db) {
       dh[db] *= eC;
       mma_accB<TI, NT>(dh[db], sQt, LDC, 16 * db, 0, go, NT);
-      mma_accB<TI, NT>(dh[db], sWt, LDC, 16 * db, 0, nd, NT);
+      mma_accB<TI, NT>(dh[db], sKt, LDC, 16 * db, 0, nd, NT);
     }
   }
   if (dh0) {
@@ -324,8 +345,8 @@ template <typename TI, int D>
 __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
     const int32_t* __restrict__ table, const TI* __restrict__ q, const TI* __restrict__ k,
     const TI* __restrict__ v, const void* __restrict__ beta, int beta_f32,
-    const float* __restrict__ g_t, const TI* __restrict__ Tinv, const TI* __restrict__ h_c,
-    const TI* __restrict__ v_new, const TI* __restrict__ dD, const TI* __restrict__ dH,
+    const float* __restrict__ g_t, const TI* __restrict__ h_c,
+    const TI* __restrict__ v_new, const TI* __restrict__ dR, const TI* __restrict__ dH,
     const TI* __restrict__ dO, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta, int qk_rows,
     int Ttot, int H, int Hg, float scale) {
@@ -346,7 +367,7 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   TI* sC = sB + L::MAT;
   TI* sBig = sC + L::MAT;
   TI* sDl = sBig + L::BIG;       // Delta, [C][LDD]
-  TI* sCC1 = sDl + C * LDD;      // T^T, then V ([C][LDD] over the first two tiles), then Mi
+  TI* sCC1 = sDl + C * LDD;      // V ([C][LDD] over the first two tiles), then Mi
   TI* sCC2 = sCC1 + L::CC;       // Mi^T
   TI* sCC3 = sCC2 + L::CC;       // DB
   TI* sCC4 = sCC3 + L::CC;       // DB^T
@@ -376,44 +397,34 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
 
   // Global loads are issued a phase or more ahead of their LDS stores (each thread holds its
   // share of a block in registers meanwhile).
-  Blk<TI, C, C, N2> bT;
-  Blk<TI, C, D, N2> bdD, bk, bq, bdl, bv;
+  Blk<TI, C, D, N2> bdr, bk, bq, bdl, bv;
   Blk<TI, D, D, N2> bhT;
-  bT.load(Tinv + ((long)start * H + h) * C, (long)H * C, len);
-  bdD.load(dD + v0, (long)H * D, len);
+  bdr.load(dR + v0, (long)H * D, len);
   bk.load(k + qk0, (long)Hg * D, len);
   bq.load(q + qk0, (long)Hg * D, len);
   bdl.load(v_new + v0, (long)H * D, len);
   bv.load(v + v0, (long)H * D, len);
   bhT.load(h_c + hcoff, D, D);
+  __syncthreads();  // Gc and beta
 
-  // ---- phase A: dR = T^T dDelta
-  bT.store_trn(sCC1, LDC);
-  bdD.store_trn(sBig, LDC);  // [D][LDC]
-  __syncthreads();
-  f32x4 dR[2][CBW];
+  // ---- dR (from the reverse pass) and dV = diag(beta) dR
+  bdr.store_nat(sC, LDD);
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int a = 0; a < bdr.RB; ++a) {
+    const int t = bdr.r0 + a;
+    if (t < len) {
+      const typename Blk<TI, C, D, N2>::Vec x = bdr.row(a);
+      const float bt = sBeta[t];
+      float* dst = dv + v0 + (long)t * H * D + bdr.c0;
 #pragma unroll
-    for (int m = 0; m < CBW; ++m) {
-      dR[b][m] = zero4();
-      mma_lds<TI>(dR[b][m], sCC1, LDC, 16 * (2 * rh + b), sBig, LDC, 16 * (cw + 4 * m), 0, C);
-    }
-  // dV = diag(beta) dR, and dR kept in LDS for the later products (rows past len are zero:
-  // T's columns past len are)
+      for (int q4 = 0; q4 < bdr.V / 4; ++q4) {
+        f32x4 o;
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int m = 0; m < CBW; ++m) {
-      const int colx = 16 * (cw + 4 * m) + lc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * (2 * rh + b) + 4 * lg + e;
-        sC[t * LDD + colx] = (TI)dR[b][m][e];
-        if (t < len) dv[v0 + (long)t * H * D + colx] = sBeta[t] * dR[b][m][e];
+        for (int e = 0; e < 4; ++e) o[e] = bt * (float)x.e[4 * q4 + e];
+        *reinterpret_cast<f32x4*>(dst + 4 * q4) = o;
       }
     }
-  __syncthreads();
+  }
 
   // ---- phase B: K h and K dh' and three row dots
   Blk<TI, D, D, N2> bdT;
@@ -698,17 +709,17 @@ hipError_t run_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st) {
   const size_t sm1 = dh_smem<TI, D>();
   GDN_BTRY(set_lds(k_bwd_dh<TI, D>, sm1));
   k_bwd_dh<TI, D><<<dim3(p.N, p.H, D / 64), kBT, sm1, st>>>(
-      b.st.table, b.st.seq_chunks, q, k, static_cast<const TI*>(b.st.W),
-      dO, b.st.g_t, b.dht, static_cast<TI*>(b.dH), static_cast<TI*>(b.dD), b.dh0, p.Ttot,
-      p.H, p.Hg, p.scale);
+      b.st.table, b.st.seq_chunks, q, k, static_cast<const TI*>(b.st.Tinv), p.beta,
+      p.beta_f32 ? 1 : 0, dO, b.st.g_t, b.dht, static_cast<TI*>(b.dH), static_cast<TI*>(b.dR),
+      b.dh0, p.Ttot, p.H, p.Hg, p.scale);
   GDN_BTRY(hipGetLastError());
   const bool grouped = p.H != p.Hg;
   const size_t sm2 = ChunkLds<TI, D>::bytes;
   GDN_BTRY(set_lds(k_bwd_chunk<TI, D>, sm2));
   k_bwd_chunk<TI, D><<<dim3(p.max_chunks, p.H), kBT2, sm2, st>>>(
       b.st.table, q, k, v, p.beta, p.beta_f32 ? 1 : 0, b.st.g_t,
-      static_cast<const TI*>(b.st.Tinv), static_cast<const TI*>(b.st.h_c),
-      static_cast<const TI*>(b.st.v_new), static_cast<const TI*>(b.dD),
+      static_cast<const TI*>(b.st.h_c),
+      static_cast<const TI*>(b.st.v_new), static_cast<const TI*>(b.dR),
       static_cast<const TI*>(b.dH), dO, grouped ? b.dqh : b.dq,
       grouped ? b.dkh : b.dk, b.dv, b.dg, b.dbeta, grouped ? p.H : p.Hg, p.Ttot, p.H, p.Hg,
       p.scale);

@@ -163,14 +163,18 @@ __device__ __forceinline__ V4 read_tr(const void* p) {
 }
 
 // OUT = false: the state-only form (no q read, no Q K^T tiles, no Q h, no o), for the
-// segmented variant's passes that only need final states.
-template <int DK, int DV, bool OUT>
+// segmented variant's passes that only need final states.  STORE = true also writes every
+// chunk's start state (bf16, hc[chunk][h][Dk][Dv] with chunk = seq_chunks[n] + m, the
+// staged variant's chunk numbering at C = 64) and v_new (bf16, [Ttot][H][Dv]): the
+// quantities the backward pass recomputes.
+template <int DK, int DV, bool OUT, bool STORE = false>
 __global__ __launch_bounds__(DV * 4) void k_fused(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const void* __restrict__ beta, int beta_f32,
     const float* __restrict__ h0, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ order, bf16* __restrict__ o, float* __restrict__ ht, int T,
-    int Ttot, int H, int Hg, float scale, int flags) {
+    const int32_t* __restrict__ order, const int32_t* __restrict__ seq_chunks,
+    bf16* __restrict__ hc, bf16* __restrict__ vnew, bf16* __restrict__ o,
+    float* __restrict__ ht, int T, int Ttot, int H, int Hg, float scale, int flags) {
   typedef FusedCfg<DK, DV> F;
   constexpr int CS = F::CS, NB = F::NB, NDK = F::NDK, RS = F::RS, TE = F::TE, CPR = F::CPR;
   constexpr int NW = F::NW, CPRV = F::CPRV;
@@ -530,6 +534,16 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
     const float* dcp = SDC[kb] + g4;
     const auto orsrc = buf_rsrc(o + ((long)cs * H + h) * D + col0,
                                 (flags & kFusedNoOutput) ? 0u : (uint32_t)(len * H * D * 2));
+    if constexpr (STORE) {
+      // the chunk-start state, for the backward
+      const long cb = ((long)(seq_chunks[n] + m) * H + h) * D * D;
+      const int dv0 = col0 + 16 * w0 + r16;
+#pragma unroll
+      for (int db = 0; db < NDK; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          hc[cb + (long)state_dk<DK>(db, g4 + e) * D + dv0] = (bf16)st[db][e];
+    }
 
     // K h and Q h of every block with the chunk-start state; Y = Q h is made transposed
     // (token per lane), like the output product below
@@ -589,6 +603,13 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
       const f32x4 vn =
           mma16b(*reinterpret_cast<const bf16x4*>(Ac + tix<F>(b, b)), to_b(acc), zero4());
       vnb[b] = to_b(vn);
+      if constexpr (STORE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * b + g4 + e;
+          if (t < len) vnew[((long)(cs + t) * H + h) * D + col0 + 16 * w0 + r16] = (bf16)vn[e];
+        }
+      }
       // o^T = scale e^Gc Y^T + sum_{j<=b} v_j^T (scale P_bj)^T: lane (l%16, g) holds token
       // 16 b + l%16, columns 16 w + 4 g .. + 3, stored as one 8-byte word (pairs converted
       // as 32-bit words: this compiler turns an element read of a converted 16-bit vector
@@ -654,14 +675,15 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
   }
 }
 
-template <int DK, int DV, bool OUT>
+template <int DK, int DV, bool OUT, bool STORE = false>
 hipError_t run_fused(const Problem& p, hipStream_t st) {
   const int grid = p.N * p.H * FusedCfg<DK, DV>::SPLIT;
   if (grid == 0) return hipSuccess;
-  k_fused<DK, DV, OUT><<<grid, FusedCfg<DK, DV>::NTH, 0, st>>>(
+  k_fused<DK, DV, OUT, STORE><<<grid, FusedCfg<DK, DV>::NTH, 0, st>>>(
       static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), static_cast<const bf16*>(p.v),
-      p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, p.cu ? p.order : nullptr,
-      static_cast<bf16*>(p.o), p.ht, p.T, p.Ttot, p.H, p.Hg, p.scale, p.fused_flags);
+      p.g, p.beta, p.beta_f32 ? 1 : 0, p.h0, p.cu, p.cu ? p.order : nullptr, p.seq_chunks,
+      static_cast<bf16*>(p.hc_out), static_cast<bf16*>(p.vnew_out), static_cast<bf16*>(p.o),
+      p.ht, p.T, p.Ttot, p.H, p.Hg, p.scale, p.fused_flags);
   return hipGetLastError();
 }
 
@@ -711,6 +733,12 @@ bool fused_supported(const Problem& p) {
 }
 
 hipError_t launch_fused(const Problem& p, hipStream_t st) {
+  if (p.hc_out) {
+    // the backward's recompute: state-only, storing the chunk-start states and v_new
+    if (p.D == 64) return run_fused<64, 64, false, true>(p, st);
+    if (p.D == 128) return run_fused<128, 128, false, true>(p, st);
+    return hipErrorInvalidValue;
+  }
   // D = 256: two workgroups per (sequence, head), 128 state columns each
   if (p.fused_flags & kFusedNoOutput) {
     if (p.D == 64) return run_fused<64, 64, false>(p, st);

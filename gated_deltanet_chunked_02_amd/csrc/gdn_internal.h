@@ -31,6 +31,12 @@ struct Problem {
   const void* gate_a = nullptr;
   const float* A_log = nullptr;
   const float* dt_bias = nullptr;
+  // Fused variant, D <= 128: also write each chunk's start state (bf16 [chunks][H][D][D],
+  // chunk = seq_chunks[n] + m at 64-token chunks) and v_new (bf16 [Ttot][H][D]), for the
+  // backward; hc_out == NULL: not written.
+  const int32_t* seq_chunks = nullptr;
+  void* hc_out = nullptr;
+  void* vnew_out = nullptr;
 };
 
 // Fused-kernel modes used by the segmented variant's passes.
@@ -55,11 +61,12 @@ struct Stages {
 
 hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st);
 
-// Backward pass: the staged forward's intermediates (stages 0-6 at C = 64) plus the
-// gradient buffers.  dq, dk: [Ttot, Hg, D]; dv: [Ttot, H, D]; dg, dbeta: [Ttot, H];
-// dh0: [N, H, D, D] or NULL; all fp32.  dD [Ttot, H, D] and dH [max_chunks, H, D, D] (the
-// gradient of each chunk's end state), in the q/k/v dtype, are workspace; dqh, dkh
-// [Ttot, H, D] fp32 too when H != Hg (per value head, summed over the group afterwards).
+// Backward pass: the forward's chunk quantities (chunk table, Gc, T at C = 64, each chunk's
+// start state h_c and v_new; the staged layout) plus the gradient buffers.  dq, dk:
+// [Ttot, Hg, D]; dv: [Ttot, H, D]; dg, dbeta: [Ttot, H]; dh0: [N, H, D, D] or NULL; all
+// fp32.  dR [Ttot, H, D] and dH [max_chunks, H, D, D] (the gradient of each chunk's end
+// state), in the q/k/v dtype, are workspace; dqh, dkh [Ttot, H, D] fp32 too when H != Hg
+// (per value head, summed over the group afterwards).
 struct BwdBuffers {
   Stages st;
   const void* dO;
@@ -70,7 +77,7 @@ struct BwdBuffers {
   float* dg;
   float* dbeta;
   float* dh0;
-  void* dD;
+  void* dR;
   void* dH;
   float* dqh;
   float* dkh;
