@@ -149,6 +149,22 @@ __device__ __forceinline__ float sum4g(float x) {
   return x;
 }
 
+// A block of matrix-core products sharing fragment reads: per k-step over [0, K), the NA
+// A fragments fa(i, k) and NB B fragments fb(j, k) are read once, then fm(a, b) issues the
+// products (each fragment serves several tiles: fewer LDS reads per product).
+template <typename E, int K, int NA, int NB, typename FA, typename FB, typename FM>
+__device__ __forceinline__ void mma_steps(FA fa, FB fb, FM fm) {
+#pragma unroll
+  for (int k = 0; k < K; k += Mma<E>::KS) {
+    typename Mma<E>::frag a[NA], b[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) a[i] = fa(i, k);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b[j] = fb(j, k);
+    fm(a, b);
+  }
+}
+
 // ------------------------------------------------------------------------- dh pass
 // With W = T diag(beta gam) K, the update's W^T dDelta is K^T diag(beta gam) dR, dR = T^T
 // dDelta: the pass reads rows of T (C x C) instead of W (C x D), and hands dR to the chunk
@@ -437,26 +453,43 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   bv.store_nat(sV, LDD);
   bhT.store_trn(sBig, LDD);  // h^T
   __syncthreads();
+  typedef Mma<TI> MM;
+  // fragment readers: rows 32 rh + 16 i of a [C][LDD] panel; columns 16 (cw + 4 j) of a
+  // [.][LDD] B panel; the C-deep forms over [.][LDC] panels
+  auto rowsD = [&](const TI* P) {
+    return [=](int i, int kk) { return frag_ld<TI>(P, LDD, 32 * rh + 16 * i, kk); };
+  };
+  auto colsD = [&](const TI* P) {
+    return [=](int j, int kk) { return frag_ld<TI>(P, LDD, 16 * (cw + 4 * j), kk); };
+  };
+  auto rowsC = [&](const TI* P) {
+    return [=](int i, int kk) { return frag_ld<TI>(P, LDC, 32 * rh + 16 * i, kk); };
+  };
+  auto colsC = [&](const TI* P) {
+    return [=](int j, int kk) { return frag_ld<TI>(P, LDC, 16 * (cw + 4 * j), kk); };
+  };
   f32x4 Kh[2][CBW], Kd[2][CBW];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int m = 0; m < CBW; ++m) {
-      Kh[b][m] = zero4();
-      mma_lds<TI>(Kh[b][m], sA, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);
-    }
+    for (int m = 0; m < CBW; ++m) Kh[b][m] = Kd[b][m] = zero4();
+  mma_steps<TI, D, 2, CBW>(rowsD(sA), colsD(sBig), [&](auto& fa, auto& fb) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int m = 0; m < CBW; ++m) Kh[b][m] = MM::mma(fa[b], fb[m], Kh[b][m]);
+  });
   Blk<TI, D, D, N2> bh;
   bh.load(h_c + hcoff, D, D);
   __syncthreads();
   bdT.store_trn(sBig, LDD);  // dh'^T
   __syncthreads();
+  mma_steps<TI, D, 2, CBW>(rowsD(sA), colsD(sBig), [&](auto& fa, auto& fb) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int m = 0; m < CBW; ++m) {
-      Kd[b][m] = zero4();
-      mma_lds<TI>(Kd[b][m], sA, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);
-    }
+      for (int m = 0; m < CBW; ++m) Kd[b][m] = MM::mma(fa[b], fb[m], Kd[b][m]);
+  });
   // row dots over the wave's columns: Delta.K dh', dR.K h, dR.V (operands from LDS)
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -490,24 +523,34 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
 
   // ---- phase C: the C x C products and their elementwise terms
   f32x4 KK[2], QK[2];
+  KK[0] = KK[1] = QK[0] = QK[1] = zero4();
+  mma_steps<TI, D, 2, 2>(
+      [&](int i, int kk) { return frag_ld<TI>(i ? sB : sA, LDD, 16 * cw, kk); },
+      [&](int j, int kk) { return frag_ld<TI>(sA, LDD, 32 * rh + 16 * j, kk); },
+      [&](auto& fa, auto& fb) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    KK[b] = QK[b] = zero4();
-    mma_lds<TI>(KK[b], sA, LDD, 16 * cw, sA, LDD, 16 * (2 * rh + b), 0, D);
-    mma_lds<TI>(QK[b], sB, LDD, 16 * cw, sA, LDD, 16 * (2 * rh + b), 0, D);
-  }
+        for (int b = 0; b < 2; ++b) {
+          KK[b] = MM::mma(fa[0], fb[b], KK[b]);
+          QK[b] = MM::mma(fa[1], fb[b], QK[b]);
+        }
+      });
   Blk<TI, D, D, N2> bd;
   bd.load(dH + hcoff, D, D);
   __syncthreads();  // (also: the row dots' parts are summed)
   bo.store_nat(sA, LDD);  // dO
   __syncthreads();
   f32x4 E1[2], RD[2];
+  E1[0] = E1[1] = RD[0] = RD[1] = zero4();
+  mma_steps<TI, D, 2, 2>(
+      [&](int i, int kk) { return frag_ld<TI>(i ? sC : sA, LDD, 16 * cw, kk); },
+      [&](int j, int kk) { return frag_ld<TI>(sDl, LDD, 32 * rh + 16 * j, kk); },
+      [&](auto& fa, auto& fb) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    E1[b] = RD[b] = zero4();
-    mma_lds<TI>(E1[b], sA, LDD, 16 * cw, sDl, LDD, 16 * (2 * rh + b), 0, D);
-    mma_lds<TI>(RD[b], sC, LDD, 16 * cw, sDl, LDD, 16 * (2 * rh + b), 0, D);
-  }
+        for (int b = 0; b < 2; ++b) {
+          E1[b] = MM::mma(fa[0], fb[b], E1[b]);
+          RD[b] = MM::mma(fa[1], fb[b], RD[b]);
+        }
+      });
   float rowE[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -550,20 +593,31 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   __syncthreads();
   bh.store_nat(sBig, LDD);  // h
   __syncthreads();
+  // dO h^T into aq and dR h^T into ak, one pass over h's fragments
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) aq[b][m] = ak[b][m] = zero4();
+  mma_steps<TI, D, 4, CBW>(
+      [&](int i, int kk) { return frag_ld<TI>(i < 2 ? sA : sC, LDD, 32 * rh + 16 * (i & 1), kk); },
+      colsD(sBig), [&](auto& fa, auto& fb) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int m = 0; m < CBW; ++m) {
+            aq[b][m] = MM::mma(fa[b], fb[m], aq[b][m]);
+            ak[b][m] = MM::mma(fa[2 + b], fb[m], ak[b][m]);
+          }
+      });
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
-    for (int m = 0; m < CBW; ++m) {
-      f32x4 x = zero4(), y = zero4();
-      mma_lds<TI>(x, sA, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);  // dO h^T
-      mma_lds<TI>(y, sC, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);  // dR h^T
+    for (int m = 0; m < CBW; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * (2 * rh + b) + 4 * lg + e;
-        aq[b][m][e] = x[e];  // scaled below, once Q . (dO h^T) is taken
-        ak[b][m][e] = -sBeta[t] * __expf(sG[t]) * y[e];
+        ak[b][m][e] *= -sBeta[t] * __expf(sG[t]);  // aq is scaled below, once Q . (dO h^T) is taken
       }
-    }
     // rowsum(dO * Q h) = rowsum(Q * dO h^T), Q natural in sB
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -588,37 +642,54 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   }
   __syncthreads();
   const float gC = sG[len - 1];
+  {
+    f32x4 x[2][CBW];  // Delta dh'^T
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int m = 0; m < CBW; ++m) {
-      f32x4 x = zero4();
-      mma_lds<TI>(x, sDl, LDD, 16 * (2 * rh + b), sBig, LDD, 16 * (cw + 4 * m), 0, D);  // Delta dh'^T
+      for (int m = 0; m < CBW; ++m) x[b][m] = zero4();
+    mma_steps<TI, D, 2, CBW>(rowsD(sDl), colsD(sBig), [&](auto& fa, auto& fb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * (2 * rh + b) + 4 * lg + e;
-        ak[b][m][e] += __expf(gC - sG[t]) * x[e];
-      }
-    }
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int m = 0; m < CBW; ++m) x[b][m] = MM::mma(fa[b], fb[m], x[b][m]);
+    });
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int m = 0; m < CBW; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * (2 * rh + b) + 4 * lg + e;
+          ak[b][m][e] += __expf(gC - sG[t]) * x[b][m][e];
+        }
+  }
   bkt.store_trn(sB, LDC);  // K^T (Q natural in sB was last read before the barrier above)
   __syncthreads();
+  // Mi K into aq, (DB + DB^T) K into ak
+  mma_steps<TI, C, 6, CBW>(
+      [&](int i, int kk) {
+        return frag_ld<TI>(i < 2 ? sCC1 : (i < 4 ? sCC3 : sCC4), LDC, 32 * rh + 16 * (i & 1), kk);
+      },
+      colsC(sB), [&](auto& fa, auto& fb) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int m = 0; m < CBW; ++m) {
-      const int r0 = 16 * (2 * rh + b), c0 = 16 * (cw + 4 * m);
-      mma_lds<TI>(aq[b][m], sCC1, LDC, r0, sB, LDC, c0, 0, C);  // Mi K
-      mma_lds<TI>(ak[b][m], sCC3, LDC, r0, sB, LDC, c0, 0, C);  // DB K
-      mma_lds<TI>(ak[b][m], sCC4, LDC, r0, sB, LDC, c0, 0, C);  // DB^T K
-    }
+          for (int m = 0; m < CBW; ++m) {
+            aq[b][m] = MM::mma(fa[b], fb[m], aq[b][m]);
+            ak[b][m] = MM::mma(fa[2 + b], fb[m], ak[b][m]);
+            ak[b][m] = MM::mma(fa[4 + b], fb[m], ak[b][m]);
+          }
+      });
   __syncthreads();
   bqt.store_trn(sB, LDC);  // Q^T
   __syncthreads();
+  mma_steps<TI, C, 2, CBW>(rowsC(sCC2), colsC(sB), [&](auto& fa, auto& fb) {  // Mi^T Q
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int m = 0; m < CBW; ++m)
-      mma_lds<TI>(ak[b][m], sCC2, LDC, 16 * (2 * rh + b), sB, LDC, 16 * (cw + 4 * m), 0, C);  // Mi^T Q
+      for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
+  });
   const long dq0 = ((long)start * qk_rows + hq) * D;
 #pragma unroll
   for (int b = 0; b < 2; ++b)

@@ -131,17 +131,32 @@ __global__ __launch_bounds__(kThreads) void k_transpose(const T* in, T* out, int
   }
 }
 
-// Copy `rows` rows of D elements (row stride `stride` elements in global memory) into a
-// k-contiguous LDS matrix [C][ld]; rows >= rows_valid are zero.  16-byte pieces.
+// Copy C rows of D elements (row stride `stride` elements in global memory) into a
+// k-contiguous LDS matrix [C][ld]; rows >= rows_valid (>= 1) are zero.  16-byte pieces,
+// up to eight loads in flight per thread: the loads are unconditional (rows past the end
+// read the last valid row) and the zeroing is a select at the store.
 template <typename T, int D, int C>
 __device__ __forceinline__ void stage_rows(T* s, int ld, const T* src, long stride,
                                            int rows_valid) {
-  constexpr int VE = Vec16<T>::n, VPR = D / VE;
-  for (int i = threadIdx.x; i < C * VPR; i += blockDim.x) {
-    const int t = i / VPR, pc = i - t * VPR;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (t < rows_valid) val = *reinterpret_cast<const uint4*>(src + t * stride + pc * VE);
-    *reinterpret_cast<uint4*>(s + t * ld + pc * VE) = val;
+  constexpr int VE = Vec16<T>::n, VPR = D / VE, TOTAL = C * VPR;
+  constexpr int ITER = (TOTAL + kThreads - 1) / kThreads, BATCH = ITER < 8 ? ITER : 8;
+  static_assert(TOTAL % kThreads == 0 && ITER % BATCH == 0, "whole batches");
+#pragma unroll
+  for (int b0 = 0; b0 < ITER; b0 += BATCH) {
+    uint4 val[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int i = threadIdx.x + (b0 + j) * kThreads;
+      const int t = i / VPR, pc = i - t * VPR;
+      val[j] = *reinterpret_cast<const uint4*>(src + min(t, rows_valid - 1) * stride + pc * VE);
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int i = threadIdx.x + (b0 + j) * kThreads;
+      const int t = i / VPR, pc = i - t * VPR;
+      *reinterpret_cast<uint4*>(s + t * ld + pc * VE) =
+          t < rows_valid ? val[j] : make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
@@ -149,18 +164,30 @@ __device__ __forceinline__ void stage_rows(T* s, int ld, const T* src, long stri
 template <typename T, int W, int C>
 __device__ __forceinline__ void stage_rows_T(T* s, int ld, const T* src, long stride,
                                              int rows_valid, const float* scale_t) {
-  constexpr int VE = Vec16<T>::n, VPR = W / VE;
-  for (int i = threadIdx.x; i < C * VPR; i += blockDim.x) {
-    const int t = i / VPR, pc = i - t * VPR;
-    union {
-      uint4 u;
-      T e[VE];
-    } val;
-    val.u = make_uint4(0, 0, 0, 0);
-    if (t < rows_valid) val.u = *reinterpret_cast<const uint4*>(src + t * stride + pc * VE);
-    const float f = scale_t ? scale_t[t] : 1.f;
+  constexpr int VE = Vec16<T>::n, VPR = W / VE, TOTAL = C * VPR;
+  constexpr int ITER = (TOTAL + kThreads - 1) / kThreads, BATCH = ITER < 8 ? ITER : 8;
+  static_assert(TOTAL % kThreads == 0 && ITER % BATCH == 0, "whole batches");
+  union Piece {
+    uint4 u;
+    T e[VE];
+  };
 #pragma unroll
-    for (int e = 0; e < VE; ++e) s[(pc * VE + e) * ld + t] = (T)(f * (float)val.e[e]);
+  for (int b0 = 0; b0 < ITER; b0 += BATCH) {
+    Piece val[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int i = threadIdx.x + (b0 + j) * kThreads;
+      const int t = i / VPR, pc = i - t * VPR;
+      val[j].u = *reinterpret_cast<const uint4*>(src + min(t, rows_valid - 1) * stride + pc * VE);
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int i = threadIdx.x + (b0 + j) * kThreads;
+      const int t = i / VPR, pc = i - t * VPR;
+      const float f = t < rows_valid ? (scale_t ? scale_t[t] : 1.f) : 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s[(pc * VE + e) * ld + t] = (T)(f * (float)val[j].e[e]);
+    }
   }
 }
 
@@ -353,14 +380,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_h(const int32_t* table,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = tb * 16 + 4 * (l >> 4) + e;
-        float val = 0.f;
-        if (t < len) {
-          const long gi = ((long)(start + t) * H + h) * D + dv;
-          val = (float)U[gi] - x[e];
-          v_new[gi] = (TI)val;
-          val *= __expf(glast - sG[t]);
-        }
-        vn[tb][e] = val;
+        const long gi = ((long)(start + min(t, len - 1)) * H + h) * D + dv;
+        float val = (float)U[gi] - x[e];
+        if (t < len) v_new[gi] = (TI)val;
+        vn[tb][e] = t < len ? val * __expf(glast - sG[t]) : 0.f;
       }
     }
     const float eg = __expf(glast);
@@ -409,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_o(const int32_t* table, cons
   stage_rows<TI, D, C>(sQ, LDQ, q + ((long)start * Hg + hk) * D, (long)Hg * D, len);
   for (int t = threadIdx.x; t < C; t += kThreads)
     sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
-  for (int i = threadIdx.x; i < C * LDP; i += kThreads) sP[i] = (TI)0.f;
+  // (every lower tile of P is written below, and only those are read)
 
   // P^T tiles (rows j, columns i, i >= j) accumulate over K panels.
   f32x4 pacc[MAXT];
@@ -463,7 +486,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_o(const int32_t* table, cons
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = tb * 16 + 4 * (l >> 4) + e;
-        vt[tb][e] = t < len ? (float)v_new[((long)(start + t) * H + h) * D + dv] : 0.f;
+        const float x = (float)v_new[((long)(start + min(t, len - 1)) * H + h) * D + dv];
+        vt[tb][e] = t < len ? x : 0.f;
       }
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb) {
