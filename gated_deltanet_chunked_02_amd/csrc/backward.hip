@@ -46,78 +46,8 @@ __device__ __forceinline__ int4 chunk_of(const int32_t* table, int c) {
   return reinterpret_cast<const int4*>(table)[c];
 }
 
-// One workgroup's copy of a ROWS x COLS block of TI (row r at src + r * stride; rows
-// r >= len read as zero, len >= 1) in RB x V sub-blocks, V = 16 / sizeof(TI) and RB chosen
-// so that every thread holds one: RB rows of one 16-byte vector each.  Eight lanes cover
-// 128 contiguous bytes of a source row.  The loads are unconditional (rows past len read
-// the last valid row) and nothing touches their results until a store zeroes the rows past
-// len, so a load issued phases ahead stays in flight until its data is stored.  Stored
-// natural (dst[r * ld + c], 16-byte LDS stores) or transposed in registers (dst[c * ld + r],
-// RB-element stores).
 template <typename TI, int ROWS, int COLS, int NTH = kBT>
-struct Blk {
-  static constexpr int V = 16 / (int)sizeof(TI), BC = COLS / V;
-  static constexpr int RB = ROWS * BC / NTH < V ? ROWS * BC / NTH : V;
-  static constexpr int BR = ROWS / RB, NB = BR * BC;
-  static_assert(RB >= 1 && ROWS % RB == 0 && BR % 8 == 0 && BC % 8 == 0 && NB == NTH,
-                "block shape");
-  union Vec {
-    uint4 u;
-    TI e[V];
-  };
-  typedef TI Col __attribute__((ext_vector_type(RB > 1 ? RB : 2)));
-  Vec in[RB];
-  int r0, c0, len;
-
-  __device__ __forceinline__ void load(const TI* src, long stride, int len_) {
-    const int lo = threadIdx.x & 63, hi = threadIdx.x >> 6;
-    const int bc = (lo & 7) + 8 * (hi % (BC / 8)), br = (lo >> 3) + 8 * (hi / (BC / 8));
-    r0 = RB * br;
-    c0 = V * bc;
-    len = len_;
-#pragma unroll
-    for (int a = 0; a < RB; ++a)
-      in[a].u = *reinterpret_cast<const uint4*>(src + (long)min(r0 + a, len - 1) * stride + c0);
-  }
-  __device__ __forceinline__ Vec row(int a) const {
-    Vec x;
-    x.u = r0 + a < len ? in[a].u : make_uint4(0, 0, 0, 0);
-    return x;
-  }
-  __device__ __forceinline__ void store_nat(TI* dst, int ld) const {
-#pragma unroll
-    for (int a = 0; a < RB; ++a) *reinterpret_cast<uint4*>(dst + (r0 + a) * ld + c0) = row(a).u;
-  }
-  __device__ __forceinline__ void store_trn(TI* dst, int ld) const {
-    Vec x[RB];
-#pragma unroll
-    for (int a = 0; a < RB; ++a) x[a] = row(a);
-#pragma unroll
-    for (int b = 0; b < V; ++b) {
-      if constexpr (RB == 1) {
-        dst[(c0 + b) * ld + r0] = x[0].e[b];
-      } else {
-        Col o;
-#pragma unroll
-        for (int a = 0; a < RB; ++a) o[a] = x[a].e[b];
-        *reinterpret_cast<Col*>(dst + (c0 + b) * ld + r0) = o;
-      }
-    }
-  }
-  // sum over the held elements of x * other[r][c] (other natural, leading dimension ld)
-  __device__ __forceinline__ float dot_nat(const TI* other, int ld) const {
-    float s = 0.f;
-#pragma unroll
-    for (int a = 0; a < RB; ++a) {
-      const Vec x = row(a);
-      Vec o;
-      o.u = *reinterpret_cast<const uint4*>(other + (r0 + a) * ld + c0);
-#pragma unroll
-      for (int b = 0; b < V; ++b) s += (float)x.e[b] * (float)o.e[b];
-    }
-    return s;
-  }
-};
+using Blk = TileCopy<TI, ROWS, COLS, NTH>;
 
 template <typename TI, int ROWS, int COLS, int NTH = kBT>
 __device__ __forceinline__ void ld_nat(TI* dst, int ld, const TI* src, long stride, int len) {

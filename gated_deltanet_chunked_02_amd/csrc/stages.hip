@@ -327,7 +327,9 @@ __global__ __launch_bounds__(kThreads) void k_wy(const int32_t* table, const TI*
 // ------------------------------------------------------------------------- stage 6
 // One workgroup per (sequence, head, 64-column slice).  Wave w owns state columns
 // [16w, 16w+16) of the slice for all Dk rows, kept in accumulator tiles; W h and the
-// K^T v_new update take the state / new values straight from registers.
+// K^T v_new update take the state / new values straight from registers.  Where each
+// thread can hold one sub-block of the W, K and U tiles, the next chunk's tiles are loaded
+// into registers while the current chunk is computed.
 template <typename TI, int D, int C>
 __global__ __launch_bounds__(kThreads) void k_chunk_h(const int32_t* table,
                                                       const int32_t* seq_chunks, const TI* k,
@@ -337,13 +339,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk_h(const int32_t* table,
                                                       int H, int Hg) {
   const int n = blockIdx.x, h = blockIdx.y, hk = h / (H / Hg);
   const int w = wave_id(), l = lane_id();
-  const int dv = blockIdx.z * 64 + 16 * w + (l & 15);
+  const int scol = 16 * w + (l & 15);
+  const int dv = blockIdx.z * 64 + scol;
   constexpr int NDK = D / 16, NT = C / 16;
-  constexpr int LDW = D + pad_of<TI>(), LDK = C + pad_of<TI>();
+  constexpr int LDW = D + pad_of<TI>(), LDK = C + pad_of<TI>(), LDU = 64 + pad_of<TI>();
+  constexpr bool PRE = tile_copy_fits<TI, C, D, kThreads>() &&
+                       tile_copy_fits<TI, C, 64, kThreads>();
   extern __shared__ __align__(16) char smem[];
   TI* sW = reinterpret_cast<TI*>(smem);
   TI* sKt = sW + C * LDW;
-  float* sG = reinterpret_cast<float*>(sKt + D * LDK);
+  TI* sU = sKt + D * LDK;  // [C][LDU], this slice of U (prefetching form only)
+  float* sG = reinterpret_cast<float*>(sU + (PRE ? C * LDU : 0));
 
   f32x4 st[NDK];
   const long hoff = ((long)n * H + h) * D * D;
@@ -356,6 +362,26 @@ __global__ __launch_bounds__(kThreads) void k_chunk_h(const int32_t* table,
     }
 
   const int c0 = seq_chunks[n], c1 = seq_chunks[n + 1];
+  // the prefetching form's register tiles (unused otherwise)
+  struct Pre {
+    TileCopy<TI, (PRE ? C : 64), (PRE ? D : 64), kThreads> w, k;
+    TileCopy<TI, (PRE ? C : 64), 64, kThreads> u;
+  };
+  Pre pre;
+  float gt = 0.f;
+  int glen = 0;
+  auto fetch = [&](int c) {
+    const int4 ci = load_chunk(table, c);
+    const int start = ci.y, len = ci.z;
+    pre.w.load(W + ((long)start * H + h) * D, (long)H * D, len);
+    pre.k.load(k + ((long)start * Hg + hk) * D, (long)Hg * D, len);
+    pre.u.load(U + ((long)start * H + h) * D + blockIdx.z * 64, (long)H * D, len);
+    gt = g_t[(long)h * Ttot + start + min((int)threadIdx.x, len - 1)];
+    glen = len;
+  };
+  if constexpr (PRE) {
+    if (c1 > c0) fetch(c0);
+  }
   for (int c = c0; c < c1; ++c) {
     const int4 ci = load_chunk(table, c);
     const int start = ci.y, len = ci.z;
@@ -365,11 +391,19 @@ __global__ __launch_bounds__(kThreads) void k_chunk_h(const int32_t* table,
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         h_c[coff + (long)(16 * db + 4 * (l >> 4) + e) * D + dv] = (TI)st[db][e];
-    stage_rows<TI, D, C>(sW, LDW, W + ((long)start * H + h) * D, (long)H * D, len);
-    stage_rows_T<TI, D, C>(sKt, LDK, k + ((long)start * Hg + hk) * D, (long)Hg * D, len,
-                           nullptr);
-    for (int t = threadIdx.x; t < C; t += kThreads)
-      sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
+    if constexpr (PRE) {
+      pre.w.store_nat(sW, LDW);
+      pre.k.store_trn(sKt, LDK);
+      pre.u.store_nat(sU, LDU);
+      if (threadIdx.x < C) sG[threadIdx.x] = (int)threadIdx.x < glen ? gt : 0.f;
+      if (c + 1 < c1) fetch(c + 1);
+    } else {
+      stage_rows<TI, D, C>(sW, LDW, W + ((long)start * H + h) * D, (long)H * D, len);
+      stage_rows_T<TI, D, C>(sKt, LDK, k + ((long)start * Hg + hk) * D, (long)Hg * D, len,
+                             nullptr);
+      for (int t = threadIdx.x; t < C; t += kThreads)
+        sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
+    }
     __syncthreads();
     const float glast = sG[len - 1];
     f32x4 vn[NT];
@@ -381,7 +415,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_h(const int32_t* table,
       for (int e = 0; e < 4; ++e) {
         const int t = tb * 16 + 4 * (l >> 4) + e;
         const long gi = ((long)(start + min(t, len - 1)) * H + h) * D + dv;
-        float val = (float)U[gi] - x[e];
+        const float u = PRE ? (float)sU[t * LDU + scol] : (float)U[gi];
+        const float val = u - x[e];
         if (t < len) v_new[gi] = (TI)val;
         vn[tb][e] = t < len ? val * __expf(glast - sG[t]) : 0.f;
       }
@@ -583,8 +618,10 @@ hipError_t run_staged(const Problem& p, const Stages& s, int stop_after, hipStre
   if (stop_after == 5) return hipSuccess;
 
   {
-    const size_t sm = (C * (D + pad_of<TI>()) + D * (C + pad_of<TI>())) * sizeof(TI) +
-                      C * sizeof(float);
+    constexpr bool pre = tile_copy_fits<TI, C, D, kThreads>() &&
+                         tile_copy_fits<TI, C, 64, kThreads>();
+    const size_t sm = (C * (D + pad_of<TI>()) + D * (C + pad_of<TI>()) +
+                       (pre ? C * (64 + pad_of<TI>()) : 0)) * sizeof(TI) + C * sizeof(float);
     GDN_TRY(set_smem(k_chunk_h<TI, D, C>, sm));
     k_chunk_h<TI, D, C><<<dim3(p.N, p.H, D / 64), kThreads, sm, st>>>(
         s.table, s.seq_chunks, k, W, U, s.g_t, p.h0, h_c, v_new, stop_after ? nullptr : p.ht,
