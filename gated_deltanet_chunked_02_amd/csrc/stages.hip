@@ -249,26 +249,53 @@ __global__ __launch_bounds__(kThreads) void k_solve(const int32_t* table, const 
   TS* sA = reinterpret_cast<TS*>(smem);
   TS* sM = sA + C * LD;
   float* sAd = reinterpret_cast<float*>(sM + C * LD);
-  constexpr int P4 = C / 4;
-  for (int i = threadIdx.x; i < C * P4; i += kThreads) {
-    const int t = i / P4, j0 = (i - t * P4) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < len) v = *reinterpret_cast<const float4*>(A + ((long)(start + t) * H + h) * C + j0);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
+  // A's rows in unrolled batches of eight 16-byte loads, all in flight together (rows past
+  // the chunk's end read its last row and are zeroed at the store)
+  constexpr int P4 = C / 4, ITER = C * P4 / kThreads, BATCH = ITER < 8 ? ITER : 8;
+  static_assert(C * P4 % kThreads == 0 && ITER % BATCH == 0, "whole batches");
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = j0 + e;
-      if ((t >> 4) == (j >> 4))
-        sAd[(t >> 4) * 16 * kAdLd + (t & 15) * kAdLd + (j & 15)] = vv[e];
-      else
-        sA[t * LD + j] = (TS)vv[e];
+  for (int b0 = 0; b0 < ITER; b0 += BATCH) {
+    f32x4 v[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int i = threadIdx.x + (b0 + q) * kThreads;
+      const int t = i / P4, j0 = (i - t * P4) * 4;
+      v[q] = *reinterpret_cast<const f32x4*>(A + ((long)(start + min(t, len - 1)) * H + h) * C + j0);
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int i = threadIdx.x + (b0 + q) * kThreads;
+      const int t = i / P4, j0 = (i - t * P4) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        const float x = t < len ? v[q][e] : 0.f;
+        if ((t >> 4) == (j >> 4))
+          sAd[(t >> 4) * 16 * kAdLd + (t & 15) * kAdLd + (j & 15)] = x;
+        else
+          sA[t * LD + j] = (TS)x;
+      }
     }
   }
   __syncthreads();
   solve_tril<kWaves, C, TS>(sA, LD, sAd, sM, LD);
-  for (int i = threadIdx.x; i < len * C; i += kThreads) {
-    const int t = i / C, j = i - t * C;
-    Tinv[((long)(start + t) * H + h) * C + j] = (TI)(j <= t ? (float)sM[t * LD + j] : 0.f);
+  // rows of T, eight elements per store
+  constexpr int P8 = C / 8, OITER = (C * P8 + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int it = 0; it < OITER; ++it) {
+    const int i = threadIdx.x + it * kThreads;
+    const int t = i / P8, j0 = (i - t * P8) * 8;
+    if (i < C * P8 && t < len) {
+      union {
+        uint4 u[2];
+        TI e[8];
+      } o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o.e[e] = (TI)(j0 + e <= t ? (float)sM[t * LD + j0 + e] : 0.f);
+      uint4* dst = reinterpret_cast<uint4*>(Tinv + ((long)(start + t) * H + h) * C + j0);
+#pragma unroll
+      for (int q = 0; q < (int)sizeof(TI) / 2; ++q) dst[q] = o.u[q];
+    }
   }
 }
 
