@@ -96,19 +96,82 @@ __device__ __forceinline__ void mma_steps(FA fa, FB fb, FM fm) {
 }
 
 // ------------------------------------------------------------------------- dh pass
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16): within each group of 16 lanes,
+// if lane c of group g addresses row R0 + 4 g + c / 4, columns C0 + 4 (c % 4) .. + 3 of a
+// row-major matrix M, lane c receives M[R0 + 4 g + e][C0 + c], e = 0..3.
+__device__ __forceinline__ bf16x4 read_tr4(const bf16* p) {
+  const s16x4 r =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// acc += M^T[col0 .. col0 + 15][k] * Bt[k][.] over k < 16 NKB, with M row-major [k][col] in
+// LDS and Bt accumulator tiles whose rows run over k (the k order of mma_accB: 4 consecutive
+// k per lane group and half).  bf16: M^T's fragments by transposing reads; fp32: strided
+// reads.
+template <typename TI, int NKB>
+__device__ __forceinline__ void mma_accB_T(f32x4& acc, const TI* M, int ld, int col0,
+                                           const f32x4* Bt) {
+  const int l = lane_id(), c = l & 15, g = l >> 4;
+  if constexpr (sizeof(TI) == 2) {
+    static_assert(NKB % 2 == 0, "pairs of k blocks");
+    const TI* p = M + (4 * g + (c >> 2)) * ld + col0 + 4 * (c & 3);
+#pragma unroll
+    for (int kb = 0; kb < NKB; kb += 2) {
+      const bf16x4 a0 = read_tr4(p + 16 * kb * ld), a1 = read_tr4(p + (16 * kb + 16) * ld);
+      const bf16x4 b0 = __builtin_convertvector(Bt[kb], bf16x4);
+      const bf16x4 b1 = __builtin_convertvector(Bt[kb + 1], bf16x4);
+      acc = Mma<bf16>::mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                           __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc = Mma<TI>::mma(M[(16 * kb + 4 * g + i) * ld + col0 + c], Bt[kb][i], acc);
+  }
+}
+
+// acc += A[arow0 .. + 15][k] * M[k][n0 .. n0 + 15] over k < K: A row-major in LDS (k
+// contiguous), M row-major [k][n] in LDS, read by transposing reads (bf16) or strided reads.
+template <typename TI, int K>
+__device__ __forceinline__ void mma_lds_Bn(f32x4& acc, const TI* A, int lda, int arow0,
+                                           const TI* M, int ldm, int n0) {
+  const int l = lane_id(), c = l & 15, g = l >> 4;
+  if constexpr (sizeof(TI) == 2) {
+    const TI* pa = A + (arow0 + c) * lda + 4 * g;
+    const TI* pm = M + (4 * g + (c >> 2)) * ldm + n0 + 4 * (c & 3);
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+      const bf16x4 a0 = *reinterpret_cast<const bf16x4*>(pa + k);
+      const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(pa + k + 16);
+      const bf16x4 b0 = read_tr4(pm + k * ldm), b1 = read_tr4(pm + (k + 16) * ldm);
+      acc = Mma<bf16>::mma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                           __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), acc);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; k += 4)
+      acc = Mma<TI>::mma(A[(arow0 + c) * lda + k + g], M[(k + g) * ldm + n0 + c], acc);
+  }
+}
+
 // With W = T diag(beta gam) K, the update's W^T dDelta is K^T diag(beta gam) dR, dR = T^T
 // dDelta: the pass reads rows of T (C x C) instead of W (C x D), and hands dR to the chunk
-// kernel.  LDS: R0 [C][LDD] holds Q and then P^T ([C][LDC]); K [C][LDD]; Q^T, K^T [D][LDC];
-// T^T [C][LDC]; this slab of dO transposed [64][LDC]; Gc and beta [C].
+// kernel.  Every tile sits in LDS in its natural layout (Q, K [C][LDD]; T, P^T [C][LDC];
+// this slab of dO [C][LDO]); the transposed operands Q^T, K^T, T^T and dO^T are read from
+// them directly.  About 63 KB at D = 128 in bf16.
 template <typename TI, int D>
 constexpr size_t dh_smem() {
-  constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>();
-  return (2 * kBC * LDD + 2 * D * LDC + kBC * LDC + 64 * LDC) * sizeof(TI) +
-         2 * kBC * sizeof(float);
+  constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>(), LDO = 64 + pad_of<TI>();
+  return (2 * kBC * LDD + 2 * kBC * LDC + kBC * LDO) * sizeof(TI) + 2 * kBC * sizeof(float);
 }
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ table,
+__global__ __launch_bounds__(kBT, 2) void k_bwd_dh(const int32_t* __restrict__ table,
                                                 const int32_t* __restrict__ seq_chunks,
                                                 const TI* __restrict__ q,
                                                 const TI* __restrict__ k,
@@ -121,21 +184,18 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
                                                 float* __restrict__ dh0, int Ttot, int H,
                                                 int Hg, float scale) {
   constexpr int C = kBC, NDK = D / 16, NT = C / 16;
-  constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>();
-  static_assert(C * LDC <= C * LDD, "P^T fits where Q was");
+  constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>(), LDO = 64 + pad_of<TI>();
   const int n = blockIdx.x, h = blockIdx.y, hk = h / (H / Hg);
   const int w = wave_id(), l = lane_id();
   const int scol = 16 * w + (l & 15);           // column within the 64-column slab
   const int col = blockIdx.z * 64 + scol;       // state column
   extern __shared__ __align__(16) char smem[];
   TI* sQ = reinterpret_cast<TI*>(smem);  // [C][LDD]
-  TI* sPt = sQ;                          // [C][LDC]  P^T, once P is in registers
   TI* sK = sQ + C * LDD;                 // [C][LDD]
-  TI* sQt = sK + C * LDD;                // [D][LDC]  Q^T
-  TI* sKt = sQt + D * LDC;               // [D][LDC]  K^T
-  TI* sTt = sKt + D * LDC;               // [C][LDC]  T^T
-  TI* sOt = sTt + C * LDC;               // [64][LDC] this slab of dO, transposed
-  float* sG = reinterpret_cast<float*>(sOt + 64 * LDC);
+  TI* sT = sK + C * LDD;                 // [C][LDC]  rows of T
+  TI* sPt = sT + C * LDC;                // [C][LDC]  P^T
+  TI* sO = sPt + C * LDC;                // [C][LDO]  this slab of dO
+  float* sG = reinterpret_cast<float*>(sO + C * LDO);
   float* sBeta = sG + C;
 
   // dh tile db: rows (key index) 16 db + 4 (l/16) + e, column col
@@ -175,11 +235,9 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
     const long v0 = ((long)start * H + h) * D;
     __syncthreads();  // the previous chunk is done with the LDS tiles
     bq.store_nat(sQ, LDD);
-    bq.store_trn(sQt, LDC);
     bk.store_nat(sK, LDD);
-    bk.store_trn(sKt, LDC);
-    bt.store_trn(sTt, LDC);
-    bo.store_trn(sOt, LDC);
+    bt.store_nat(sT, LDC);
+    bo.store_nat(sO, LDO);
     if (threadIdx.x < C) {
       const bool in = (int)threadIdx.x < glen;
       sG[threadIdx.x] = in ? gt : 0.f;
@@ -187,27 +245,20 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
     }
     if (c > c0) fetch(c - 1);
     __syncthreads();
-    // P[i][j] = scale (q_i . k_j) e^{Gc_i - Gc_j} for j <= i < len (wave w: 4 of the 16 tiles)
-    f32x4 pt[4];
+    // P^T: P[i][j] = scale (q_i . k_j) e^{Gc_i - Gc_j} for j <= i < len, stored at [j][i]
+    // (wave w: 4 of the 16 tiles)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int u = w + 4 * m, ti = u >> 2, tj = u & 3;
-      pt[m] = zero4();
-      if (ti >= tj) mma_lds<TI>(pt[m], sQ, LDD, 16 * ti, sK, LDD, 16 * tj, 0, D);
+      f32x4 acc = zero4();
+      if (ti >= tj) mma_lds<TI>(acc, sQ, LDD, 16 * ti, sK, LDD, 16 * tj, 0, D);
       const int j = 16 * tj + (l & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * ti + 4 * (l >> 4) + e;
-        pt[m][e] = (i >= j && i < len) ? scale * pt[m][e] * __expf(sG[i] - sG[j]) : 0.f;
+        sPt[j * LDC + i] =
+            (TI)((i >= j && i < len) ? scale * acc[e] * __expf(sG[i] - sG[j]) : 0.f);
       }
-    }
-    __syncthreads();  // Q (natural) is read: P^T takes its place
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int u = w + 4 * m, ti = u >> 2, tj = u & 3;
-      const int j = 16 * tj + (l & 15);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sPt[j * LDC + 16 * ti + 4 * (l >> 4) + e] = (TI)pt[m][e];
     }
     __syncthreads();
     const float gC = sG[len - 1], eC = __expf(gC);
@@ -216,7 +267,7 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb) {
       f32x4 a = zero4(), x = zero4();
-      mma_lds<TI>(a, sPt, LDC, 16 * tb, sOt, LDC, 16 * w, 0, C);
+      mma_lds_Bn<TI, C>(a, sPt, LDC, 16 * tb, sO, LDO, 16 * w);
       mma_accB<TI, NDK>(x, sK, LDD, 16 * tb, 0, dh, NDK);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -229,7 +280,7 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb) {
       dr[tb] = zero4();
-      mma_accB<TI, NT>(dr[tb], sTt, LDC, 16 * tb, 0, dd, NT);
+      mma_accB_T<TI, NT>(dr[tb], sT, LDC, 16 * tb, dd);
     }
     // the chunk-end gradient dh' and dR, for the chunk-parallel kernel
     const long coff = ((long)c * H + h) * D * D;
@@ -253,14 +304,14 @@ __global__ __launch_bounds__(kBT) void k_bwd_dh(const int32_t* __restrict__ tabl
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * tb + 4 * (l >> 4) + e;
         const float gam = t < len ? __expf(sG[t]) : 0.f;
-        go[tb][e] = scale * gam * (float)sOt[scol * LDC + t];
+        go[tb][e] = scale * gam * (float)sO[t * LDO + scol];
         nd[tb][e] = -sBeta[t] * gam * dr[tb][e];
       }
 #pragma unroll
     for (int db = 0; db < NDK; ++db) {
       dh[db] *= eC;
-      mma_accB<TI, NT>(dh[db], sQt, LDC, 16 * db, 0, go, NT);
-      mma_accB<TI, NT>(dh[db], sKt, LDC, 16 * db, 0, nd, NT);
+      mma_accB_T<TI, NT>(dh[db], sQ, LDD, 16 * db, go);
+      mma_accB_T<TI, NT>(dh[db], sK, LDD, 16 * db, nd);
     }
   }
   if (dh0) {
