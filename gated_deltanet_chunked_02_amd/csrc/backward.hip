@@ -323,19 +323,36 @@ __global__ __launch_bounds__(kBT, 2) void k_bwd_dh(const int32_t* __restrict__ t
 }
 
 // ------------------------------------------------------------------------- chunk gradients
+// The k-contiguous operand fragment of M^T (rows n0 + l%16, k = k0 + 8 (l/16) + 0..7; the
+// layout of frag_ld) from row-major M [k][n] in LDS: two transposing reads in bf16, a
+// strided read in fp32.
+template <typename TI>
+__device__ __forceinline__ typename Mma<TI>::frag frag_tr(const TI* M, int ld, int n0, int k0) {
+  const int l = lane_id(), c = l & 15, g = l >> 4;
+  if constexpr (sizeof(TI) == 2) {
+    const TI* p = M + (k0 + 8 * g + (c >> 2)) * ld + n0 + 4 * (c & 3);
+    const bf16x4 a = read_tr4(p), b = read_tr4(p + 4 * ld);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    return M[(k0 + g) * ld + n0 + c];
+  }
+}
+
 // One workgroup of 8 waves per (chunk, head).  Wave w = 4 rh + cw: in the C x D products it
 // owns the row blocks 2 rh, 2 rh + 1 and the column blocks cw + 4 m (m < D / 64); in the
-// C x C products the row block cw and the column blocks 2 rh, 2 rh + 1.
+// C x C products the row block cw and the column blocks 2 rh, 2 rh + 1.  Every tile sits in
+// LDS in its natural layout and the transposed operands are read from it (frag_tr), so h
+// and dh' are each loaded once and every product that needs them runs while they are
+// resident.
 template <typename TI, int D>
 struct ChunkLds {
   static constexpr int C = kBC;
   static constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>();
-  static constexpr int MAT = (C * LDD > D * LDC ? C * LDD : D * LDC);  // a C x D or D x C panel
-  static constexpr int BIG = D * LDD;                                  // a D x D matrix
-  static constexpr int CC = C * LDC;                                   // a C x C matrix
-  static_assert(C * LDD <= 2 * CC, "V fits in the first two C x C tiles");
-  static constexpr size_t bytes =
-      (3 * MAT + BIG + C * LDD + 4 * CC) * sizeof(TI) + (2 + 16 + 4 + 4) * C * sizeof(float);
+  static constexpr int P = C * LDD;   // a C x D panel
+  static constexpr int BIG = D * LDD; // a D x D matrix
+  static constexpr int CC = C * LDC;  // a C x C matrix
+  static_assert(P <= 2 * CC, "V fits in the two C x C tiles");
+  static constexpr size_t bytes = (5 * P + BIG + 2 * CC) * sizeof(TI) + 26 * C * sizeof(float);
 };
 
 template <typename TI, int D>
@@ -348,6 +365,7 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
     float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta, int qk_rows,
     int Ttot, int H, int Hg, float scale) {
   typedef ChunkLds<TI, D> L;
+  typedef Mma<TI> MM;
   constexpr int C = kBC, CBW = D / 64, N2 = kBT2;  // column blocks per wave (C x D outputs)
   constexpr int LDD = L::LDD, LDC = L::LDC;
   const int c = blockIdx.x, h = blockIdx.y;
@@ -359,26 +377,25 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   const int w = wave_id(), l = lane_id(), lg = l >> 4, lc = l & 15;
   const int cw = w & 3, rh = w >> 2;
   extern __shared__ __align__(16) char smem[];
-  TI* sA = reinterpret_cast<TI*>(smem);
-  TI* sB = sA + L::MAT;
-  TI* sC = sB + L::MAT;
-  TI* sBig = sC + L::MAT;
-  TI* sDl = sBig + L::BIG;       // Delta, [C][LDD]
-  TI* sCC1 = sDl + C * LDD;      // V ([C][LDD] over the first two tiles), then Mi
-  TI* sCC2 = sCC1 + L::CC;       // Mi^T
-  TI* sCC3 = sCC2 + L::CC;       // DB
-  TI* sCC4 = sCC3 + L::CC;       // DB^T
-  TI* sV = sCC1;
-  float* sG = reinterpret_cast<float*>(sCC4 + L::CC);
+  TI* sK = reinterpret_cast<TI*>(smem);
+  TI* sQ = sK + L::P;
+  TI* sC = sQ + L::P;            // dR
+  TI* sO = sC + L::P;            // dO
+  TI* sDl = sO + L::P;           // Delta
+  TI* sBig = sDl + L::P;         // h, then dh'
+  TI* sMi = sBig + L::BIG;       // V ([C][LDD] over both C x C tiles) in phase B, then Mi
+  TI* sDB = sMi + L::CC;         // DB
+  TI* sV = sMi;
+  float* sG = reinterpret_cast<float*>(sDB + L::CC);
   float* sBeta = sG + C;
-  // sPart [16 C]: the row dots' parts [quantity x][column wave][C] (x = 1..3 in phase B,
-  // x = 0 in phase D); later, over the consumed parts: <dh', h> per wave at 4 C, the last
-  // token's shares at 5 C, dGc at 6 C, rowsum(E) per row half at 8 C, rowsum(dA * KK * Gam)
-  // per row half at 10 C
+  // sPart [16 C]: the row dots' parts [quantity x][column wave][C] (x = 0..3); after they
+  // are summed: the last token's shares at 5 C, dGc at 6 C, rowsum(E) per row half at 8 C,
+  // rowsum(dA * KK * Gam) per row half at 10 C
   float* sPart = sBeta + C;
-  float* sRD = sPart + 16 * C;   // [4][C] the row dots (1: Delta.K dh', 2: dR.K h, 3: dR.V)
+  float* sRD = sPart + 16 * C;   // [4][C] the row dots (1: Delta.K dh', 2: dR.K h, 3: dR.V);
+                                 // its first C floats hold the parts of <dh', h>
   float* sColE = sRD + 4 * C;    // [4 row blocks][C] partial colsum(E)
-  float* sHdh = sPart + 4 * C;
+  float* sHdh = sRD;
   float* sShare = sPart + 5 * C;
   float* sDgc = sPart + 6 * C;
   float* sRowE = sPart + 8 * C;
@@ -391,21 +408,26 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
     sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
     sBeta[t] = t < len ? load_beta(beta, beta_f32, (long)(start + t) * H + h) : 0.f;
   }
-
-  // Global loads are issued a phase or more ahead of their LDS stores (each thread holds its
-  // share of a block in registers meanwhile).
-  Blk<TI, C, D, N2> bdr, bk, bq, bdl, bv;
-  Blk<TI, D, D, N2> bhT;
+  // every operand tile, loaded together (each thread holds its share in registers)
+  Blk<TI, C, D, N2> bdr, bk, bq, bdl, bv, bo;
+  Blk<TI, D, D, N2> bh, bd;
   bdr.load(dR + v0, (long)H * D, len);
   bk.load(k + qk0, (long)Hg * D, len);
   bq.load(q + qk0, (long)Hg * D, len);
   bdl.load(v_new + v0, (long)H * D, len);
   bv.load(v + v0, (long)H * D, len);
-  bhT.load(h_c + hcoff, D, D);
+  bo.load(dO + v0, (long)H * D, len);
+  bh.load(h_c + hcoff, D, D);
   __syncthreads();  // Gc and beta
-
-  // ---- dR (from the reverse pass) and dV = diag(beta) dR
   bdr.store_nat(sC, LDD);
+  bk.store_nat(sK, LDD);
+  bq.store_nat(sQ, LDD);
+  bdl.store_nat(sDl, LDD);
+  bv.store_nat(sV, LDD);
+  bo.store_nat(sO, LDD);
+  bh.store_nat(sBig, LDD);
+  bd.load(dH + hcoff, D, D);
+  // dV = diag(beta) dR, from the registers that hold dR
 #pragma unroll
   for (int a = 0; a < bdr.RB; ++a) {
     const int t = bdr.r0 + a;
@@ -422,80 +444,122 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
       }
     }
   }
+  __syncthreads();
 
-  // ---- phase B: K h and K dh' and three row dots
-  Blk<TI, D, D, N2> bdT;
-  Blk<TI, C, D, N2> bo;
-  bdT.load(dH + hcoff, D, D);
-  bo.load(dO + v0, (long)H * D, len);
-  bk.store_nat(sA, LDD);
-  bq.store_nat(sB, LDD);
-  bdl.store_nat(sDl, LDD);
-  bv.store_nat(sV, LDD);
-  bhT.store_trn(sBig, LDD);  // h^T
-  __syncthreads();
-  typedef Mma<TI> MM;
-  // fragment readers: rows 32 rh + 16 i of a [C][LDD] panel; columns 16 (cw + 4 j) of a
-  // [.][LDD] B panel; the C-deep forms over [.][LDC] panels
-  auto rowsD = [&](const TI* P) {
-    return [=](int i, int kk) { return frag_ld<TI>(P, LDD, 32 * rh + 16 * i, kk); };
+  // fragment readers of the C x D products: rows 32 rh + 16 i of a [C][LD] panel; the
+  // B operands of columns 16 (cw + 4 j): natural rows of a [.][LD] matrix, or M^T from M
+  auto rows = [&](const TI* Pm, int ld) {
+    return [=](int i, int kk) { return frag_ld<TI>(Pm, ld, 32 * rh + 16 * i, kk); };
   };
-  auto colsD = [&](const TI* P) {
-    return [=](int j, int kk) { return frag_ld<TI>(P, LDD, 16 * (cw + 4 * j), kk); };
+  auto cols = [&](const TI* Pm, int ld) {
+    return [=](int j, int kk) { return frag_ld<TI>(Pm, ld, 16 * (cw + 4 * j), kk); };
   };
-  auto rowsC = [&](const TI* P) {
-    return [=](int i, int kk) { return frag_ld<TI>(P, LDC, 32 * rh + 16 * i, kk); };
+  auto colsT = [&](const TI* Pm, int ld) {
+    return [=](int j, int kk) { return frag_tr<TI>(Pm, ld, 16 * (cw + 4 * j), kk); };
   };
-  auto colsC = [&](const TI* P) {
-    return [=](int j, int kk) { return frag_ld<TI>(P, LDC, 16 * (cw + 4 * j), kk); };
-  };
-  f32x4 Kh[2][CBW], Kd[2][CBW];
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int m = 0; m < CBW; ++m) Kh[b][m] = Kd[b][m] = zero4();
-  mma_steps<TI, D, 2, CBW>(rowsD(sA), colsD(sBig), [&](auto& fa, auto& fb) {
+
+  // ---- phase B, h resident: K h, dO h^T (into aq), dR h^T (into ak), row dots
+  f32x4 aq[2][CBW], ak[2][CBW];
+  {
+    f32x4 Kh[2][CBW];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int m = 0; m < CBW; ++m) Kh[b][m] = MM::mma(fa[b], fb[m], Kh[b][m]);
-  });
-  Blk<TI, D, D, N2> bh;
-  bh.load(h_c + hcoff, D, D);
-  __syncthreads();
-  bdT.store_trn(sBig, LDD);  // dh'^T
-  __syncthreads();
-  mma_steps<TI, D, 2, CBW>(rowsD(sA), colsD(sBig), [&](auto& fa, auto& fb) {
+      for (int m = 0; m < CBW; ++m) Kh[b][m] = aq[b][m] = ak[b][m] = zero4();
+    mma_steps<TI, D, 2, CBW>(rows(sK, LDD), colsT(sBig, LDD), [&](auto& fa, auto& fb) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int m = 0; m < CBW; ++m) Kh[b][m] = MM::mma(fa[b], fb[m], Kh[b][m]);
+    });
+    mma_steps<TI, D, 4, CBW>(
+        [&](int i, int kk) { return frag_ld<TI>(i < 2 ? sO : sC, LDD, 32 * rh + 16 * (i & 1), kk); },
+        cols(sBig, LDD), [&](auto& fa, auto& fb) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int m = 0; m < CBW; ++m) {
+              aq[b][m] = MM::mma(fa[b], fb[m], aq[b][m]);
+              ak[b][m] = MM::mma(fa[2 + b], fb[m], ak[b][m]);
+            }
+        });
+    // row dots over the wave's columns: dR.K h, dR.V, Q.(dO h^T) = dO.Q h
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int m = 0; m < CBW; ++m) Kd[b][m] = MM::mma(fa[b], fb[m], Kd[b][m]);
-  });
-  // row dots over the wave's columns: Delta.K dh', dR.K h, dR.V (operands from LDS)
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        float p0 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+        for (int m = 0; m < CBW; ++m) {
+          const int gi = t * LDD + 16 * (cw + 4 * m) + lc;
+          const float r = (float)sC[gi];
+          p2 += r * Kh[b][m][e];
+          p3 += r * (float)sV[gi];
+          p0 += (float)sQ[gi] * aq[b][m][e];
+        }
+        p0 = sum16(p0);
+        p2 = sum16(p2);
+        p3 = sum16(p3);
+        if (lc == 0) {
+          sPart[cw * C + t] = p0;
+          sPart[(8 + cw) * C + t] = p2;
+          sPart[(12 + cw) * C + t] = p3;
+        }
+        const float gam = __expf(sG[t]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * (2 * rh + b) + 4 * lg + e;
-      float p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-      for (int m = 0; m < CBW; ++m) {
-        const int gi = t * LDD + 16 * (cw + 4 * m) + lc;
-        const float r = (float)sC[gi];
-        p1 += (float)sDl[gi] * Kd[b][m][e];
-        p2 += r * Kh[b][m][e];
-        p3 += r * (float)sV[gi];
+        for (int m = 0; m < CBW; ++m) {
+          aq[b][m][e] *= scale * gam;
+          ak[b][m][e] *= -sBeta[t] * gam;
+        }
       }
-      p1 = sum16(p1);
-      p2 = sum16(p2);
-      p3 = sum16(p3);
-      if (lc == 0) {
-        sPart[(4 + cw) * C + t] = p1;
-        sPart[(8 + cw) * C + t] = p2;
-        sPart[(12 + cw) * C + t] = p3;
-      }
-    }
+  }
+  {
+    // <dh', h> from the held dh' blocks and the resident h (parts per wave, in order)
+    const float part = sum4g(sum16(bd.dot_nat(sBig, LDD)));
+    if (l == 0) sHdh[w] = part;
+  }
   __syncthreads();
+  bd.store_nat(sBig, LDD);  // dh'
+  __syncthreads();
+
+  // ---- phase B', dh' resident: K dh' (row dot with Delta) and Delta dh'^T (into ak)
+  const float gC = sG[len - 1];
+  {
+    f32x4 Kd[2][CBW], X[2][CBW];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int m = 0; m < CBW; ++m) Kd[b][m] = X[b][m] = zero4();
+    mma_steps<TI, D, 2, CBW>(rows(sK, LDD), colsT(sBig, LDD), [&](auto& fa, auto& fb) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int m = 0; m < CBW; ++m) Kd[b][m] = MM::mma(fa[b], fb[m], Kd[b][m]);
+    });
+    mma_steps<TI, D, 2, CBW>(rows(sDl, LDD), cols(sBig, LDD), [&](auto& fa, auto& fb) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int m = 0; m < CBW; ++m) X[b][m] = MM::mma(fa[b], fb[m], X[b][m]);
+    });
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        float p1 = 0.f;
+        const float r = __expf(gC - sG[t]);
+#pragma unroll
+        for (int m = 0; m < CBW; ++m) {
+          p1 += (float)sDl[t * LDD + 16 * (cw + 4 * m) + lc] * Kd[b][m][e];
+          ak[b][m][e] += r * X[b][m][e];
+        }
+        p1 = sum16(p1);
+        if (lc == 0) sPart[(4 + cw) * C + t] = p1;
+      }
+  }
+  __syncthreads();  // row-dot parts complete; V read for the last time
   if (threadIdx.x < 3 * C) {
     const int x = 1 + threadIdx.x / C, t = threadIdx.x % C;
     sRD[x * C + t] = sPart[(4 * x) * C + t] + sPart[(4 * x + 1) * C + t] +
@@ -503,11 +567,11 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   }
 
   // ---- phase C: the C x C products and their elementwise terms
-  f32x4 KK[2], QK[2];
-  KK[0] = KK[1] = QK[0] = QK[1] = zero4();
+  f32x4 KK[2], QK[2], E1[2], RD[2];
+  KK[0] = KK[1] = QK[0] = QK[1] = E1[0] = E1[1] = RD[0] = RD[1] = zero4();
   mma_steps<TI, D, 2, 2>(
-      [&](int i, int kk) { return frag_ld<TI>(i ? sB : sA, LDD, 16 * cw, kk); },
-      [&](int j, int kk) { return frag_ld<TI>(sA, LDD, 32 * rh + 16 * j, kk); },
+      [&](int i, int kk) { return frag_ld<TI>(i ? sQ : sK, LDD, 16 * cw, kk); },
+      [&](int j, int kk) { return frag_ld<TI>(sK, LDD, 32 * rh + 16 * j, kk); },
       [&](auto& fa, auto& fb) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -515,15 +579,8 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
           QK[b] = MM::mma(fa[1], fb[b], QK[b]);
         }
       });
-  Blk<TI, D, D, N2> bd;
-  bd.load(dH + hcoff, D, D);
-  __syncthreads();  // (also: the row dots' parts are summed)
-  bo.store_nat(sA, LDD);  // dO
-  __syncthreads();
-  f32x4 E1[2], RD[2];
-  E1[0] = E1[1] = RD[0] = RD[1] = zero4();
   mma_steps<TI, D, 2, 2>(
-      [&](int i, int kk) { return frag_ld<TI>(i ? sC : sA, LDD, 16 * cw, kk); },
+      [&](int i, int kk) { return frag_ld<TI>(i ? sC : sO, LDD, 16 * cw, kk); },
       [&](int j, int kk) { return frag_ld<TI>(sDl, LDD, 32 * rh + 16 * j, kk); },
       [&](auto& fa, auto& fb) {
 #pragma unroll
@@ -532,6 +589,7 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
           RD[b] = MM::mma(fa[1], fb[b], RD[b]);
         }
       });
+  __syncthreads();  // the row-dot parts are summed before sRowE / sRowB reuse their space
   float rowE[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -549,10 +607,8 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
       rowE[e] += ee;
       rowB[e] += da * KK[b][e] * gam;
       colE += ee;
-      sCC1[i * LDC + j] = (TI)mi;
-      sCC2[j * LDC + i] = (TI)mi;
-      sCC3[i * LDC + j] = (TI)db;
-      sCC4[j * LDC + i] = (TI)db;
+      sMi[i * LDC + j] = (TI)mi;
+      sDB[i * LDC + j] = (TI)db;
     }
     colE = sum4g(colE);
     if (lg == 0) sColE[cw * C + j] = colE;
@@ -565,112 +621,39 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
       sRowB[rh * C + 16 * cw + 4 * lg + e] = rb;
     }
   }
+  __syncthreads();
 
-  // ---- phase D: dQ and dK
-  f32x4 aq[2][CBW], ak[2][CBW];
-  Blk<TI, C, D, N2> bkt, bqt;
-  bkt.load(k + qk0, (long)Hg * D, len);
-  bqt.load(q + qk0, (long)Hg * D, len);
-  __syncthreads();
-  bh.store_nat(sBig, LDD);  // h
-  __syncthreads();
-  // dO h^T into aq and dR h^T into ak, one pass over h's fragments
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int m = 0; m < CBW; ++m) aq[b][m] = ak[b][m] = zero4();
-  mma_steps<TI, D, 4, CBW>(
-      [&](int i, int kk) { return frag_ld<TI>(i < 2 ? sA : sC, LDD, 32 * rh + 16 * (i & 1), kk); },
-      colsD(sBig), [&](auto& fa, auto& fb) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int m = 0; m < CBW; ++m) {
-            aq[b][m] = MM::mma(fa[b], fb[m], aq[b][m]);
-            ak[b][m] = MM::mma(fa[2 + b], fb[m], ak[b][m]);
-          }
-      });
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-#pragma unroll
-    for (int m = 0; m < CBW; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * (2 * rh + b) + 4 * lg + e;
-        ak[b][m][e] *= -sBeta[t] * __expf(sG[t]);  // aq is scaled below, once Q . (dO h^T) is taken
-      }
-    // rowsum(dO * Q h) = rowsum(Q * dO h^T), Q natural in sB
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * (2 * rh + b) + 4 * lg + e;
-      float p0 = 0.f;
-#pragma unroll
-      for (int m = 0; m < CBW; ++m)
-        p0 += (float)sB[t * LDD + 16 * (cw + 4 * m) + lc] * aq[b][m][e];
-      p0 = sum16(p0);
-      if (lc == 0) sPart[cw * C + t] = p0;
-      const float sg = scale * __expf(sG[t]);
-#pragma unroll
-      for (int m = 0; m < CBW; ++m) aq[b][m][e] *= sg;
-    }
-  }
-  {
-    // dh' (natural) over h, and <dh', h> from the h it replaces (parts per wave, in order)
-    const float part = sum4g(sum16(bd.dot_nat(sBig, LDD)));
-    if (l == 0) sHdh[w] = part;
-    __syncthreads();
-    bd.store_nat(sBig, LDD);
-  }
-  __syncthreads();
-  const float gC = sG[len - 1];
-  {
-    f32x4 x[2][CBW];  // Delta dh'^T
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int m = 0; m < CBW; ++m) x[b][m] = zero4();
-    mma_steps<TI, D, 2, CBW>(rowsD(sDl), colsD(sBig), [&](auto& fa, auto& fb) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int m = 0; m < CBW; ++m) x[b][m] = MM::mma(fa[b], fb[m], x[b][m]);
-    });
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int m = 0; m < CBW; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * (2 * rh + b) + 4 * lg + e;
-          ak[b][m][e] += __expf(gC - sG[t]) * x[b][m][e];
-        }
-  }
-  bkt.store_trn(sB, LDC);  // K^T (Q natural in sB was last read before the barrier above)
-  __syncthreads();
-  // Mi K into aq, (DB + DB^T) K into ak
-  mma_steps<TI, C, 6, CBW>(
+  // ---- phase D: Mi K into aq; (DB + DB^T) K and Mi^T Q into ak
+  mma_steps<TI, C, 4, CBW>(
       [&](int i, int kk) {
-        return frag_ld<TI>(i < 2 ? sCC1 : (i < 4 ? sCC3 : sCC4), LDC, 32 * rh + 16 * (i & 1), kk);
+        const TI* Pm = (i & 2) ? sDB : sMi;
+        return frag_ld<TI>(Pm, LDC, 32 * rh + 16 * (i & 1), kk);
       },
-      colsC(sB), [&](auto& fa, auto& fb) {
+      colsT(sK, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int m = 0; m < CBW; ++m) {
             aq[b][m] = MM::mma(fa[b], fb[m], aq[b][m]);
             ak[b][m] = MM::mma(fa[2 + b], fb[m], ak[b][m]);
-            ak[b][m] = MM::mma(fa[4 + b], fb[m], ak[b][m]);
           }
       });
-  __syncthreads();
-  bqt.store_trn(sB, LDC);  // Q^T
-  __syncthreads();
-  mma_steps<TI, C, 2, CBW>(rowsC(sCC2), colsC(sB), [&](auto& fa, auto& fb) {  // Mi^T Q
+  mma_steps<TI, C, 2, CBW>(
+      [&](int i, int kk) { return frag_tr<TI>(sDB, LDC, 32 * rh + 16 * i, kk); },  // DB^T
+      colsT(sK, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
-  });
+          for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
+      });
+  mma_steps<TI, C, 2, CBW>(
+      [&](int i, int kk) { return frag_tr<TI>(sMi, LDC, 32 * rh + 16 * i, kk); },  // Mi^T
+      colsT(sQ, LDD), [&](auto& fa, auto& fb) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
+      });
   const long dq0 = ((long)start * qk_rows + hq) * D;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
