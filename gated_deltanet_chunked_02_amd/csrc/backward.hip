@@ -33,6 +33,7 @@
 // kernel sums (no float atomics: the results do not depend on scheduling).
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_operands.h"
 
 namespace gdn {
 
@@ -79,34 +80,8 @@ __device__ __forceinline__ float sum4g(float x) {
   return x;
 }
 
-// A block of matrix-core products sharing fragment reads: per k-step over [0, K), the NA
-// A fragments fa(i, k) and NB B fragments fb(j, k) are read once, then fm(a, b) issues the
-// products (each fragment serves several tiles: fewer LDS reads per product).
-template <typename E, int K, int NA, int NB, typename FA, typename FB, typename FM>
-__device__ __forceinline__ void mma_steps(FA fa, FB fb, FM fm) {
-#pragma unroll
-  for (int k = 0; k < K; k += Mma<E>::KS) {
-    typename Mma<E>::frag a[NA], b[NB];
-#pragma unroll
-    for (int i = 0; i < NA; ++i) a[i] = fa(i, k);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) b[j] = fb(j, k);
-    fm(a, b);
-  }
-}
 
 // ------------------------------------------------------------------------- dh pass
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16): within each group of 16 lanes,
-// if lane c of group g addresses row R0 + 4 g + c / 4, columns C0 + 4 (c % 4) .. + 3 of a
-// row-major matrix M, lane c receives M[R0 + 4 g + e][C0 + c], e = 0..3.
-__device__ __forceinline__ bf16x4 read_tr4(const bf16* p) {
-  const s16x4 r =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(bf16x4, r);
-}
-
 // acc += M^T[col0 .. col0 + 15][k] * Bt[k][.] over k < 16 NKB, with M row-major [k][col] in
 // LDS and Bt accumulator tiles whose rows run over k (the k order of mma_accB: 4 consecutive
 // k per lane group and half).  bf16: M^T's fragments by transposing reads; fp32: strided
@@ -323,21 +298,6 @@ __global__ __launch_bounds__(kBT, 2) void k_bwd_dh(const int32_t* __restrict__ t
 }
 
 // ------------------------------------------------------------------------- chunk gradients
-// The k-contiguous operand fragment of M^T (rows n0 + l%16, k = k0 + 8 (l/16) + 0..7; the
-// layout of frag_ld) from row-major M [k][n] in LDS: two transposing reads in bf16, a
-// strided read in fp32.
-template <typename TI>
-__device__ __forceinline__ typename Mma<TI>::frag frag_tr(const TI* M, int ld, int n0, int k0) {
-  const int l = lane_id(), c = l & 15, g = l >> 4;
-  if constexpr (sizeof(TI) == 2) {
-    const TI* p = M + (k0 + 8 * g + (c >> 2)) * ld + n0 + 4 * (c & 3);
-    const bf16x4 a = read_tr4(p), b = read_tr4(p + 4 * ld);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  } else {
-    return M[(k0 + g) * ld + n0 + c];
-  }
-}
-
 // One workgroup of 8 waves per (chunk, head).  Wave w = 4 rh + cw: in the C x D products it
 // owns the row blocks 2 rh, 2 rh + 1 and the column blocks cw + 4 m (m < D / 64); in the
 // C x C products the row block cw and the column blocks 2 rh, 2 rh + 1.  Every tile sits in

@@ -17,6 +17,7 @@
 // products use the 16x16 matrix-core tiles described in gdn_device.h.
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_operands.h"
 #include "gdn_solve.h"
 
 namespace gdn {
@@ -567,6 +568,128 @@ __global__ __launch_bounds__(kThreads) void k_chunk_o(const int32_t* table, cons
   }
 }
 
+// The same stage with every operand staged in LDS by 16-byte loads issued together at the
+// start (Q, K, h_c, v_new; v_new takes K's place once P is built) and the transposed
+// operands of Q h_c and P v_new read from the natural tiles (frag_tr).  For the shapes whose
+// tiles give every thread one sub-block and fit in LDS; wave w makes the row blocks w, w + 4,
+// ... of o, all D columns.
+template <typename TI, int D, int C>
+constexpr bool chunk_o_tiled() {
+  constexpr int LDQ = D + pad_of<TI>(), LDP = C + pad_of<TI>();
+  return tile_copy_fits<TI, C, D, kThreads>() && tile_copy_fits<TI, D, D, kThreads>() &&
+         (2 * C * LDQ + C * LDP + D * LDQ) * (int)sizeof(TI) + C * 4 <= 160 * 1024 &&
+         C % 64 == 0 && D % 64 == 0;
+}
+
+template <typename TI, int D, int C>
+constexpr size_t chunk_o_tiled_smem() {
+  constexpr int LDQ = D + pad_of<TI>(), LDP = C + pad_of<TI>();
+  return (size_t)(2 * C * LDQ + C * LDP + D * LDQ) * sizeof(TI) + C * sizeof(float);
+}
+
+template <typename TI, int D, int C>
+__global__ __launch_bounds__(kThreads) void k_chunk_o_tiled(const int32_t* table, const TI* q,
+                                                            const TI* k, const TI* v_new,
+                                                            const TI* h_c, const float* g_t,
+                                                            TI* o, int Ttot, int H, int Hg,
+                                                            float scale) {
+  const int c = blockIdx.x;
+  const int4 ci = load_chunk(table, c);
+  const int start = ci.y, len = ci.z;
+  if (len == 0) return;
+  const int h = blockIdx.y, hk = h / (H / Hg);
+  const int w = wave_id(), l = lane_id(), lg = l >> 4, lc = l & 15;
+  typedef Mma<TI> MM;
+  constexpr int NT = C / 16, NDK = D / 16, RPW = NT / kWaves;  // row blocks per wave
+  constexpr int LDQ = D + pad_of<TI>(), LDP = C + pad_of<TI>();
+  extern __shared__ __align__(16) char smem[];
+  TI* sQ = reinterpret_cast<TI*>(smem);
+  TI* sK = sQ + C * LDQ;  // K, then v_new
+  TI* sV = sK;
+  TI* sP = sK + C * LDQ;
+  TI* sH = sP + C * LDP;
+  float* sG = reinterpret_cast<float*>(sH + D * LDQ);
+
+  TileCopy<TI, C, D, kThreads> bq, bk, bv;
+  TileCopy<TI, D, D, kThreads> bh;
+  const long qk0 = ((long)start * Hg + hk) * D, v0 = ((long)start * H + h) * D;
+  bq.load(q + qk0, (long)Hg * D, len);
+  bk.load(k + qk0, (long)Hg * D, len);
+  bh.load(h_c + ((long)c * H + h) * D * D, D, D);
+  bv.load(v_new + v0, (long)H * D, len);
+  if (threadIdx.x < C) sG[threadIdx.x] = (int)threadIdx.x < len ? g_t[(long)h * Ttot + start + threadIdx.x] : 0.f;
+  bq.store_nat(sQ, LDQ);
+  bk.store_nat(sK, LDQ);
+  bh.store_nat(sH, LDQ);
+  // the tiles just above the diagonal of even block rows are read by the 32-deep P v
+  // products and never written below: zero them
+  for (int i = threadIdx.x; i < (NT / 2) * 16 * 2; i += kThreads) {
+    const int p = i / 32, r = (i >> 1) & 15, half = i & 1;
+    *reinterpret_cast<uint4*>(sP + (32 * p + r) * LDP + 32 * p + 16 + 8 * half) =
+        make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+
+  // P[i][j] = (q_i . k_j) e^{Gc_i - Gc_j} for j <= i (lower tiles, dealt round robin)
+  constexpr int NLOW = NT * (NT + 1) / 2, MAXT = (NLOW + kWaves - 1) / kWaves;
+#pragma unroll
+  for (int m = 0; m < MAXT; ++m) {
+    const int u = w + kWaves * m;
+    if (u < NLOW) {
+      int ti = 0;
+      while ((ti + 1) * (ti + 2) / 2 <= u) ++ti;
+      const int tj = u - ti * (ti + 1) / 2;
+      f32x4 acc = zero4();
+      mma_lds<TI>(acc, sQ, LDQ, 16 * ti, sK, LDQ, 16 * tj, 0, D);
+      const int j = 16 * tj + lc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * ti + 4 * lg + e;
+        sP[i * LDP + j] = (TI)((i >= j) ? __expf(sG[i] - sG[j]) * acc[e] : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+  bv.store_nat(sV, LDQ);  // v_new where K was
+  __syncthreads();
+
+  // o = scale (diag(e^Gc) Q h_c + P v_new), row blocks w + 4 r of this wave
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int tb = w + kWaves * r;
+    f32x4 acc[NDK];
+#pragma unroll
+    for (int cb = 0; cb < NDK; ++cb) acc[cb] = zero4();
+    mma_steps<TI, D, 1, NDK>(
+        [&](int, int kk) { return frag_ld<TI>(sQ, LDQ, 16 * tb, kk); },
+        [&](int cb, int kk) { return frag_tr<TI>(sH, LDQ, 16 * cb, kk); },
+        [&](auto& fa, auto& fb) {
+#pragma unroll
+          for (int cb = 0; cb < NDK; ++cb) acc[cb] = MM::mma(fa[0], fb[cb], acc[cb]);
+        });
+#pragma unroll
+    for (int cb = 0; cb < NDK; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[cb][e] *= __expf(sG[16 * tb + 4 * lg + e]);
+    const int kend = ((tb + 1) * 16 + MM::KS - 1) / MM::KS * MM::KS;
+    for (int kk = 0; kk < kend; kk += MM::KS) {
+      const auto fa = frag_ld<TI>(sP, LDP, 16 * tb, kk);
+#pragma unroll
+      for (int cb = 0; cb < NDK; ++cb)
+        acc[cb] = MM::mma(fa, frag_tr<TI>(sV, LDQ, 16 * cb, kk), acc[cb]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * tb + 4 * lg + e;
+      if (t < len) {
+#pragma unroll
+        for (int cb = 0; cb < NDK; ++cb)
+          o[v0 + (long)t * H * D + 16 * cb + lc] = (TI)(scale * acc[cb][e]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------- launchers
 template <typename K>
 hipError_t set_smem(K kernel, size_t bytes) {
@@ -657,7 +780,13 @@ hipError_t run_staged(const Problem& p, const Stages& s, int stop_after, hipStre
   }
   if (stop_after == 6) return hipSuccess;
 
-  {
+  if constexpr (chunk_o_tiled<TI, D, C>()) {
+    const size_t sm = chunk_o_tiled_smem<TI, D, C>();
+    GDN_TRY(set_smem(k_chunk_o_tiled<TI, D, C>, sm));
+    k_chunk_o_tiled<TI, D, C><<<dim3(MC, p.H), kThreads, sm, st>>>(
+        s.table, q, k, v_new, h_c, s.g_t, static_cast<TI*>(p.o), p.Ttot, p.H, p.Hg, p.scale);
+    GDN_TRY(hipGetLastError());
+  } else {
     constexpr int KP = D < 128 ? D : 128;
     const size_t sm = (C * (D + pad_of<TI>()) + C * (KP + pad_of<TI>()) +
                        C * (C + pad_of<TI>())) * sizeof(TI) + C * sizeof(float);
