@@ -368,8 +368,9 @@ def bwd_bench(args, dev, gdn, w, inp):
                    "C": 64, "h0": h0 is not None, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gdn_chunk_bwd whole call (staged stages 0-6, k_bwd_dh, "
-                               "k_bwd_chunk%s)" % (", k_bwd_group_sum" if w.H != w.Hg else ""),
+                     "kernel": "gdn_chunk_bwd whole call (%s, k_bwd_dh, k_bwd_chunk%s)" % (
+                         "staged stages 0-4, k_fused store mode" if q.dtype == torch.bfloat16
+                         else "staged stages 0-6", ", k_bwd_group_sum" if w.H != w.Hg else ""),
                      "launch_ms": avg_ms, "algorithmic_bytes": by},
         "cpu_baseline": cpu,
     }
