@@ -129,6 +129,26 @@ SegLayout seg_layout(const gdn::Problem& p, const SegPlan& sp) {
   return L;
 }
 
+// Stage stop of the fused variant (the page's section 7.4 debugging mode): the fused kernel
+// keeps every stage on chip and forms only the chunk-start states h_c and v_new, which its
+// store mode writes out.  stop_after = 6 (after chunk_h) is therefore the one stop it
+// offers, at its own 64-token chunk (bf16, D = 64 or 128: the store mode's instances).
+constexpr int kFusedStop = 6;
+
+bool fused_stop(const gdn_desc* d) {
+  return d->variant == GDN_VARIANT_FUSED && d->stop_after != 0;
+}
+
+bool fused_stop_ok(const gdn::Problem& p, const gdn_desc* d) {
+  return d->stop_after == kFusedStop && gdn::fused_supported(p) && p.D <= 128;
+}
+
+// The shape a fused stage stop lays its buffers out for: the fused kernel's chunk.
+void fused_stop_chunk(gdn::Problem* p) {
+  p->C = kFusedChunk;
+  p->max_chunks = (int)(((long long)p->Ttot + kFusedChunk - 1) / kFusedChunk) + p->N;
+}
+
 bool seg_ok(const gdn::Problem& p, const gdn_desc* d) {
   return gdn::fused_supported(p) && d->stop_after == 0 &&
          (long long)p.Ttot + p.N <= (1LL << 30);
@@ -156,7 +176,9 @@ bool recurrent_pays(const gdn::Problem& p, bool dense) {
 int resolve_variant(const gdn_desc* d, const gdn::Problem& p, bool dense, bool ws_check) {
   const bool fused_ok = gdn::fused_supported(p) && d->stop_after == 0;
   switch (d->variant) {
-    case GDN_VARIANT_FUSED: return fused_ok ? GDN_VARIANT_FUSED : -1;
+    case GDN_VARIANT_FUSED:
+      if (d->stop_after != 0) return fused_stop_ok(p, d) ? GDN_VARIANT_FUSED : -1;
+      return fused_ok ? GDN_VARIANT_FUSED : -1;
     case GDN_VARIANT_STAGED: return staged_ok(p) ? GDN_VARIANT_STAGED : -1;
     case GDN_VARIANT_SEGMENTED: return seg_ok(p, d) ? GDN_VARIANT_SEGMENTED : -1;
     case GDN_VARIANT_RECURRENT: return recurrent_ok(p, d) ? GDN_VARIANT_RECURRENT : -1;
@@ -198,6 +220,23 @@ void staged_layout(const gdn::Problem& p, Layout* L) {
   L->total = off;
 }
 
+// The fused stage stop's buffers: the staged layout at the fused chunk with only the chunk
+// table, the sequences' first chunks, h_c and v_new sized (the kernel forms nothing else).
+void fused_stop_layout(const gdn::Problem& p, Layout* L) {
+  gdn::Problem pc = p;
+  fused_stop_chunk(&pc);
+  staged_layout(pc, L);
+  size_t off = 0;
+  for (int i = 0; i < GDN_BUF_COUNT; ++i) {
+    const bool kept = i == GDN_BUF_CHUNK_TABLE || i == GDN_BUF_SEQ_CHUNKS ||
+                      i == GDN_BUF_H_C || i == GDN_BUF_V_NEW;
+    if (!kept) L->bytes[i] = 0;
+    L->off[i] = off;
+    off += align_up(L->bytes[i]);
+  }
+  L->total = off;
+}
+
 // The fused variant on a packed batch runs its sequences longest first when the workspace
 // holds their order (4 bytes per sequence): the order kernel's O(N^2) compares are cheap up
 // to this many sequences.  Without it, or beyond, they run in index order (same results).
@@ -212,6 +251,11 @@ size_t lpt_bytes(const gdn::Problem& p) { return align_up((size_t)p.N * sizeof(i
 // Workspace of the variant a call resolves to, for one reading of the descriptor.
 size_t workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
   const int v = resolve_variant(d, p, dense, false);
+  if (v == GDN_VARIANT_FUSED && fused_stop(d)) {
+    Layout L;
+    fused_stop_layout(p, &L);
+    return L.total;
+  }
   if (v == GDN_VARIANT_FUSED) return lpt_wanted(p, dense) ? lpt_bytes(p) : 0;
   if (v == GDN_VARIANT_RECURRENT || v < 0) return 0;
   if (v == GDN_VARIANT_SEGMENTED)
@@ -310,7 +354,12 @@ gdn_status gdn_stage_buffer(const gdn_desc* d, int32_t buf, size_t* offset, size
   if (s != GDN_OK) return s;
   if (buf < 0 || buf >= GDN_BUF_COUNT || !offset || !bytes) return GDN_ERR_INVALID_ARG;
   Layout L;
-  staged_layout(p, &L);
+  if (fused_stop(d)) {
+    if (!fused_stop_ok(p, d)) return GDN_ERR_UNSUPPORTED;
+    fused_stop_layout(p, &L);
+  } else {
+    staged_layout(p, &L);
+  }
   *offset = L.off[buf];
   *bytes = L.bytes[buf];
   return GDN_OK;
@@ -359,7 +408,26 @@ gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const 
     e = gdn::launch_recurrent(p, stream);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   }
-  if (variant == GDN_VARIANT_FUSED) {
+  if (variant == GDN_VARIANT_FUSED && fused_stop(d)) {
+    // the chunk table at the fused chunk, then the fused kernel storing h_c and v_new
+    Layout L;
+    fused_stop_layout(p, &L);
+    if (!d->workspace || d->workspace_bytes < L.total || !aligned(d->workspace, kAlign))
+      return GDN_ERR_WORKSPACE;
+    const gdn::Stages st = stages_at(static_cast<char*>(d->workspace), L);
+    gdn::Problem pf = p;
+    fused_stop_chunk(&pf);
+    e = gdn::launch_chunk_table(pf, st, stream);
+    if (e == hipSuccess) {
+      pf.o = nullptr;
+      pf.ht = nullptr;
+      pf.fused_flags = gdn::kFusedNoOutput;
+      pf.seq_chunks = st.seq_chunks;
+      pf.hc_out = st.h_c;
+      pf.vnew_out = st.v_new;
+      e = gdn::launch_fused(pf, stream);
+    }
+  } else if (variant == GDN_VARIANT_FUSED) {
     e = hipSuccess;
     if (lpt_wanted(p, cu_seqlens == nullptr) && d->workspace &&
         d->workspace_bytes >= lpt_bytes(p) && aligned(d->workspace, kAlign)) {

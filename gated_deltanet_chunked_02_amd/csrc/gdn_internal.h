@@ -60,6 +60,8 @@ struct Stages {
 };
 
 hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st);
+// Stage 0 alone: the chunk table and each sequence's first chunk at p.C.
+hipError_t launch_chunk_table(const Problem& p, const Stages& s, hipStream_t st);
 
 // Backward pass: the forward's chunk quantities (chunk table, Gc, T at C = 64, each chunk's
 // start state h_c and v_new; the staged layout) plus the gradient buffers.  dq, dk:

@@ -49,6 +49,8 @@ extern "C" gdn_status gdn_chunk_fwd_noalloc(const gdn_desc* d, const void* q, co
                                             float scale, void* o, float* ht,
                                             hipStream_t stream) {
   if (!d) return GDN_ERR_INVALID_ARG;
+  // a stage stop leaves its results in the workspace, here the library's own scratch
+  if (d->stop_after != 0) return GDN_ERR_INVALID_ARG;
   void* ws = nullptr;
   const gdn_status s = scratch_ptr(&ws);
   if (s != GDN_OK) return s;

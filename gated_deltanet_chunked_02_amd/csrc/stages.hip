@@ -820,4 +820,10 @@ hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipS
                : run_staged_d<bf16>(p, s, stop_after, st);
 }
 
+hipError_t launch_chunk_table(const Problem& p, const Stages& s, hipStream_t st) {
+  k_chunk_table<<<1, 1024, 0, st>>>(p.cu, p.N, p.T, p.Ttot, p.C, p.max_chunks, s.table,
+                                    s.seq_chunks);
+  return hipGetLastError();
+}
+
 }  // namespace gdn

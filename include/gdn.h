@@ -91,7 +91,9 @@ typedef enum gdn_variant {
                                 The gates arrive as g and beta, as in every variant.       */
 } gdn_variant;
 
-/* Intermediate buffers of the staged variant, readable through gdn_stage_buffer(). */
+/* Intermediate buffers of the staged variant, readable through gdn_stage_buffer().  The
+ * fused variant's stage stop (stop_after = 6 with GDN_VARIANT_FUSED) writes the chunk
+ * table, the sequences' first chunks, h_c and v_new only, at its own 64-token chunk. */
 typedef enum gdn_buffer {
   GDN_BUF_CHUNK_TABLE = 0, /* int32 [max_chunks, 4]: (sequence, first token, length, index
                               in sequence); unused rows have length 0                  */
@@ -122,7 +124,13 @@ typedef struct gdn_desc {
   int32_t qkv_dtype;  /* gdn_dtype of q, k, v, o                                          */
   int32_t beta_dtype; /* gdn_dtype of beta                                                */
   int32_t variant;    /* gdn_variant                                                      */
-  int32_t stop_after; /* staged only: 0 = all stages, k in 1..6 = stop after stage k      */
+  int32_t stop_after; /* 0 = the whole pass.  Staged: k in 1..6 stops after stage k (the
+                         page's section 7.4 debugging mode).  Fused: 6 only, and only for
+                         bf16 with D in {64, 128}: the kernel keeps every stage on chip and
+                         forms just the chunk-start states and v_new, which it then writes
+                         to the workspace (GDN_BUF_H_C, GDN_BUF_V_NEW, at 64-token chunks)
+                         instead of o; it never forms G, A, T, W or U, so 1..5 are refused
+                         (GDN_ERR_UNSUPPORTED), as is any stop for the other variants.    */
   void* workspace;    /* device memory for the staged and segmented variants and the fused
                          variant's longest-first order (256-byte aligned; may be NULL for
                          fused, see gdn_chunk_fwd_workspace_size)                         */
@@ -196,7 +204,8 @@ int32_t gdn_resolved_chunk(const gdn_desc* d, const int32_t* cu_seqlens);
  * is empty: ht = h0, or zeros, and nothing else is touched, whatever the variant); h0 (zero
  * state), cu_seqlens (dense batch) and ht (final state not written) may be NULL.  scale multiplies o (Dk^-0.5 is the
  * usual choice).  Pointers must be device pointers aligned to 16 bytes (g, beta, cu_seqlens:
- * 4 / 2 / 4 bytes).  With stop_after = k > 0 (staged only) o and ht are not written. */
+ * 4 / 2 / 4 bytes).  With stop_after = k > 0 (staged, or fused with k = 6) o and ht are
+ * not written. */
 gdn_status gdn_chunk_fwd(const gdn_desc* d, const void* q, const void* k, const void* v,
                          const float* g, const void* beta, const float* h0,
                          const int32_t* cu_seqlens, float scale, void* o, float* ht,
@@ -269,14 +278,18 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
  * that needs more returns GDN_ERR_WORKSPACE; AUTO picks among what fits, as it does for
  * any workspace.  Nothing is allocated and nothing needs clearing between calls.  Every
  * call on one GPU shares that GPU's scratch: calls that overlap on one GPU (other streams,
- * other host threads) race and give unspecified results. */
+ * other host threads) race and give unspecified results.  stop_after must be 0
+ * (GDN_ERR_INVALID_ARG otherwise): stage buffers in the scratch are out of the caller's
+ * reach. */
 gdn_status gdn_chunk_fwd_noalloc(const gdn_desc* d, const void* q, const void* k,
                                  const void* v, const float* g, const void* beta,
                                  const float* h0, const int32_t* cu_seqlens, float scale,
                                  void* o, float* ht, hipStream_t stream);
 
-/* Where intermediate `buf` lives inside the staged workspace (offset and size in bytes),
- * for stage-by-stage inspection (the page's section 7.4 debugging mode). */
+/* Where intermediate `buf` lives inside the workspace of a stage-stop call (offset and size
+ * in bytes), for stage-by-stage inspection (the page's section 7.4 debugging mode): the
+ * staged layout at C, or, for GDN_VARIANT_FUSED with stop_after = 6, the fused stop's
+ * layout at 64-token chunks, where the buffers it does not write have size 0. */
 gdn_status gdn_stage_buffer(const gdn_desc* d, int32_t buf, size_t* offset, size_t* bytes);
 
 /* Static, human-readable text for a status code. */

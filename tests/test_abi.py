@@ -77,6 +77,10 @@ def ws_status(d):
     (dict(variant=3, B=1, N=3), 0),      # packed batches segment too
     (dict(variant=3, stop_after=3), 2),
     (dict(variant=2, stop_after=3), 2),
+    (dict(variant=2, stop_after=6), 0),   # the fused stage stop: h_c and v_new only
+    (dict(variant=2, stop_after=6, Dk=64, Dv=64), 0),
+    (dict(variant=2, stop_after=6, Dk=256, Dv=256), 2),
+    (dict(variant=2, stop_after=6, qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, chunk=64), 2),
     (dict(variant=4), 0),
     (dict(variant=4, qkv_dtype=0, beta_dtype=0, Dk=256, Dv=256), 0),
     (dict(variant=4, stop_after=3), 2),
@@ -168,6 +172,36 @@ def test_staged_layout_is_aligned_and_disjoint(lib):
     assert sizes["h_c"] == max_chunks * H * D * D * 2
     with pytest.raises(gdn.GdnError):
         gdn.gdn_stage_buffer(d, 11)
+
+
+def test_fused_stop_layout_holds_only_what_the_kernel_forms(lib):
+    # C = 128 is requested; the fused kernel runs and lays out 64-token chunks
+    d = desc(variant=2, stop_after=6, B=1, T=1000, N=3, H=6, Hg=3, Dk=128, Dv=128, chunk=128)
+    total = gdn.gdn_chunk_fwd_workspace_size(d)
+    sizes = {n: gdn.gdn_stage_buffer(d, n) for n in gdn.BUFFERS}
+    Ttot, H, D = 1000, 6, 128
+    max_chunks = -(-Ttot // 64) + 3
+    kept = {"chunk_table": max_chunks * 16, "seq_chunks": 4 * 4,
+            "h_c": max_chunks * H * D * D * 2, "v_new": Ttot * H * D * 2}
+    for name, (off, nb) in sizes.items():
+        assert off % 256 == 0 and off + nb <= total
+        assert nb == kept.get(name, 0), name
+    spans = sorted((off, off + nb) for off, nb in sizes.values() if nb)
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert gdn.gdn_resolved_chunk(desc(variant=2, stop_after=6)) == 64
+    # stops the fused kernel does not have
+    for k in range(1, 6):
+        with pytest.raises(gdn.GdnError):
+            gdn.gdn_stage_buffer(desc(variant=2, stop_after=k), 5)
+
+
+def test_noalloc_refuses_a_stage_stop(lib):
+    A = 0x10000
+    for v, k in ((1, 3), (2, 6)):
+        d = desc(variant=v, stop_after=k)
+        assert gdn.load().gdn_chunk_fwd_noalloc(ctypes.byref(d), A, A, A, A, A, None, None,
+                                                1.0, A, None, None) == 1
 
 
 def test_chunk_fwd_rejects_bad_arguments_before_any_launch(lib):

@@ -223,6 +223,68 @@ def test_stop_after_leaves_outputs_untouched():
         assert torch.all(o == 7.0)
 
 
+@pytest.mark.parametrize("case", ["gqa_varlen_d128", "dense_d64"])
+def test_fused_stage_stop(case):
+    """The fused kernel's stage stop (stop_after = 6): its chunk-start states and v_new at
+    64-token chunks against the oracle's chunked stages at C = 64; o and ht untouched."""
+    import gated_deltanet_chunked_02_amd as gdn
+    from oracle import chunked
+    if case == "gqa_varlen_d128":
+        lens = [70, 128, 1, 300, 64]
+        w = gdn_inputs.small(H=4, Hg=2, Dk=128, C=128, seed=13, h0_std=0.05)
+        inp = gdn_inputs.draw(w.with_(B=1, T=sum(lens)), device="cpu")
+        inp["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]),
+                                         dtype=torch.int32)
+        inp["h0"] = torch.randn(len(lens), 4, 128, 128,
+                                generator=torch.Generator().manual_seed(6)) * 0.05
+    else:
+        inp = draw(B=2, T=333, H=2, Dk=64, C=64, seed=14, h0_std=0.05)
+    dev = torch.device("cuda")
+    q, k, v, g, beta = (inp[n].to(dev) for n in ("q", "k", "v", "g", "beta"))
+    h0 = None if inp["h0"] is None else inp["h0"].to(dev).float().contiguous()
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].to(dev)
+    desc = gdn.make_desc(q, v, beta, cu, 128, "fused", stop_after=6)
+    ws = torch.zeros(gdn.gdn_chunk_fwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+    desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+    o = torch.full_like(v, 7.0)
+    N, H, D = desc.N, v.shape[2], v.shape[3]
+    ht = torch.full((N, H, D, D), 7.0, device=dev)
+    print("fused stage stop", case, flush=True)
+    st = gdn.gdn_chunk_fwd(desc, q, k, v, g, beta, h0, cu, inp["scale"], o, ht)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.all(o == 7.0) and torch.all(ht == 7.0)
+    Ttot = q.shape[0] * q.shape[1]
+
+    def buf(name, dtype, shape):
+        off, nb = gdn.gdn_stage_buffer(desc, name)
+        return ws[off:off + nb].view(dtype).reshape(shape)
+
+    MC = gdn.gdn_stage_buffer(desc, "chunk_table")[1] // 16
+    table = buf("chunk_table", torch.int32, (MC, 4)).cpu().numpy()
+    h_c = to64(buf("h_c", torch.bfloat16, (MC, H, D, D)))
+    v_new = to64(buf("v_new", torch.bfloat16, (Ttot, H, D)))
+    for name in ("g_cum", "A", "Tinv", "W", "U"):
+        assert gdn.gdn_stage_buffer(desc, name)[1] == 0
+    ref = chunked.chunked(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), to64(inp["g"]),
+                          to64(inp["beta"]), None if inp["h0"] is None else to64(inp["h0"]),
+                          scale=inp["scale"],
+                          cu_seqlens=None if inp["cu_seqlens"] is None
+                          else inp["cu_seqlens"].numpy(), C=64)
+    NC = len(ref["table"])
+    exp_tab = np.array([(n, s0, L) for n, s0, L in ref["table"]], dtype=np.int64)
+    assert np.array_equal(table[:NC, :3], exp_tab)
+    eh = rel_l2(h_c[:NC], ref["h_c"])
+    ev = rel_l2(v_new, ref["v_new"])
+    # per chunk too, so that one wrong chunk of a packed batch is not diluted
+    worst = 0.0
+    for c in range(NC):
+        if np.any(ref["h_c"][c]):
+            worst = max(worst, rel_l2(h_c[c], ref["h_c"][c]))
+    log(test="fused_stage_stop", case=case, h_c_rel=eh, v_new_rel=ev, h_c_chunk_max=worst)
+    assert eh <= 1e-2 and ev <= 1e-2 and worst <= 1e-2, (eh, ev, worst)
+
+
 # ------------------------------------------------------------------ invariants
 def test_fused_and_staged_agree_and_are_deterministic():
     inp = draw(B=2, T=400, H=4, Hg=2, Dk=128, C=128, seed=21, h0_std=0.05)
