@@ -315,7 +315,8 @@ def bwd_bench(args, dev, gdn, w, inp):
     inp.update(gdn_inputs.draw_grads(w, q.shape[0], q.shape[1], N, device=dev,
                                      dht_std=None if h0 is None else 0.1))
     do, dht = inp["do"], inp["dht"]
-    desc = gdn.make_desc(q, v, beta, cu, 64, "staged")
+    desc = gdn.make_desc(q, v, beta, cu, 64, args.variant)
+    how = gdn.gdn_chunk_bwd_resolved_variant(desc, cu)
     ws = torch.empty(gdn.gdn_chunk_bwd_workspace_size(desc), device=dev, dtype=torch.uint8)
     desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
     f = dict(device=dev, dtype=torch.float32)
@@ -365,12 +366,16 @@ def bwd_bench(args, dev, gdn, w, inp):
         "dtype": "bf16" if q.dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": w.name, "pass": "backward", "B": int(q.shape[0]),
                    "T": int(q.shape[1]), "H": w.H, "Hg": w.Hg, "Dk": w.Dk, "Dv": w.Dv,
-                   "C": 64, "h0": h0 is not None, "parallelism": "single GPU"},
+                   "C": 64, "h0": h0 is not None, "variant": how,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "gdn_chunk_bwd whole call (%s, k_bwd_dh, k_bwd_chunk%s)" % (
-                         "staged stages 0-4, k_fused store mode" if q.dtype == torch.bfloat16
-                         else "staged stages 0-6", ", k_bwd_group_sum" if w.H != w.Hg else ""),
+                         {"segmented": "staged stages 0-4, per segment: k_fused maps, segment "
+                                       "scans, k_fused store mode, k_bwd_dh twice",
+                          "fused": "staged stages 0-4, k_fused store mode",
+                          "staged": "staged stages 0-6"}[how],
+                         ", k_bwd_group_sum" if w.H != w.Hg else ""),
                      "launch_ms": avg_ms, "algorithmic_bytes": by},
         "cpu_baseline": cpu,
     }

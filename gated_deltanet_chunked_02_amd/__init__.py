@@ -26,6 +26,7 @@ __all__ = [
     "GdnDesc", "GdnError", "load", "gdn_chunk_fwd", "gdn_chunk_fwd_workspace_size",
     "gdn_stage_buffer", "gdn_status_string", "gdn_version", "chunk_gated_delta_rule",
     "make_desc", "STATUS", "BUFFERS", "VARIANTS", "LIB_PATH", "gdn_resolved_variant",
+    "gdn_chunk_bwd_resolved_variant",
     "gdn_resolved_chunk", "gdn_chunk_fwd_noalloc", "gdn_fused_sigmoid_gating_delta_rule",
     "fused_sigmoid_gating_delta_rule", "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_size",
     "chunk_gated_delta_rule_bwd",
@@ -94,6 +95,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_version.argtypes = []
     lib.gdn_resolved_variant.restype = ctypes.c_int32
     lib.gdn_resolved_variant.argtypes = [ctypes.POINTER(GdnDesc), P]
+    lib.gdn_chunk_bwd_resolved_variant.restype = ctypes.c_int32
+    lib.gdn_chunk_bwd_resolved_variant.argtypes = [ctypes.POINTER(GdnDesc), P]
     lib.gdn_resolved_chunk.restype = ctypes.c_int32
     lib.gdn_resolved_chunk.argtypes = [ctypes.POINTER(GdnDesc), P]
     lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
@@ -128,6 +131,16 @@ def gdn_resolved_variant(desc: GdnDesc, cu_seqlens=None) -> str:
         if code == v and name != "auto":
             return name
     raise GdnError(1, "gdn_resolved_variant")
+
+
+def gdn_chunk_bwd_resolved_variant(desc: GdnDesc, cu_seqlens=None) -> str:
+    """How gdn_chunk_bwd runs with this descriptor: "segmented", "fused" (the fused
+    recompute, one reverse pass per sequence) or "staged" (the staged recompute)."""
+    v = int(load().gdn_chunk_bwd_resolved_variant(ctypes.byref(desc), _ptr(cu_seqlens)))
+    for name, code in VARIANTS.items():
+        if code == v and name != "auto":
+            return name
+    raise GdnError(1, "gdn_chunk_bwd_resolved_variant")
 
 
 def gdn_resolved_chunk(desc: GdnDesc, cu_seqlens=None) -> int:
@@ -398,12 +411,15 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
 
 
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, do, dht=None, scale=None,
-                               initial_state=None, cu_seqlens=None, workspace=None):
+                               initial_state=None, cu_seqlens=None, workspace=None,
+                               variant="auto"):
     """Gradients of chunk_gated_delta_rule's inputs on the current stream, given the
     gradient ``do`` of o [B, T, H, Dv] (q's dtype) and ``dht`` of the final state
     [N, H, Dk, Dv] (or None: zero).  Forward inputs as for chunk_gated_delta_rule.
     Returns fp32 (dq, dk [B, T, Hg, Dk], dv [B, T, H, Dv], dg, dbeta [B, T, H],
-    dh0 [N, H, Dk, Dv] or None when initial_state is None)."""
+    dh0 [N, H, Dk, Dv] or None when initial_state is None).  ``variant``: "auto" (long
+    sequences run per segment when that pays), "segmented" (always) or any other name (one
+    pass per sequence)."""
     import torch
     _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace, devices=False)
     _need(isinstance(do, torch.Tensor) and do.dtype == q.dtype, TypeError,
@@ -428,7 +444,7 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, do, dht=None, scale=None,
         initial_state = initial_state.to(torch.float32).contiguous()
     if dht is not None:
         dht = dht.to(torch.float32).contiguous()
-    desc = make_desc(q, v, beta, cu_seqlens, 64, "staged")
+    desc = make_desc(q, v, beta, cu_seqlens, 64, variant)
     if scale is None:
         scale = Dk ** -0.5
     f = dict(device=q.device, dtype=torch.float32)

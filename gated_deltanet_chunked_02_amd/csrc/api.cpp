@@ -309,6 +309,46 @@ BwdLayout bwd_layout(const gdn::Problem& p) {
   return L;
 }
 
+// Long sequences: the backward's two sequential passes (the recompute of the chunk-start
+// states and the reverse pass) run per segment, with the forward's segment plan.  After the
+// backward's own buffers: the segment table, the sequences' first segments, then b (reused
+// for each segment's own start gradient e), M and h_in (reused for each segment's end
+// gradient), as the segmented forward lays them out, and each segment's first chunk
+// [nseg + 1].
+struct BwdSegLayout {
+  SegPlan sp;
+  size_t base;  // offset of the segment buffers (the end of BwdLayout)
+  SegLayout seg;
+  size_t chunks, total;
+};
+
+// The plan a backward call runs with: segments only with the fused recompute (bf16), when
+// AUTO finds they pay off or GDN_VARIANT_SEGMENTED asks for them; any other variant keeps
+// one reverse pass per sequence.
+SegPlan bwd_seg_plan(const gdn_desc* d, const gdn::Problem& p, bool dense) {
+  if (p.f32 || !gdn::fused_supported(p) || (long long)p.Ttot + p.N > (1LL << 30))
+    return SegPlan();
+  if (d->variant != GDN_VARIANT_AUTO && d->variant != GDN_VARIANT_SEGMENTED) return SegPlan();
+  return seg_plan(p, d->variant == GDN_VARIANT_SEGMENTED, dense);
+}
+
+BwdSegLayout bwd_seg_layout(const gdn::Problem& p, const SegPlan& sp, size_t base) {
+  BwdSegLayout L;
+  L.sp = sp;
+  L.base = base;
+  L.seg = seg_layout(p, sp);
+  L.chunks = base + L.seg.total;
+  L.total = L.chunks + align_up(((size_t)sp.nseg + 1) * sizeof(int32_t));
+  return L;
+}
+
+// Workspace of a backward call for one reading of the descriptor (dense or packed).
+size_t bwd_workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
+  const BwdLayout L = bwd_layout(p);
+  const SegPlan sp = bwd_seg_plan(d, p, dense);
+  return sp.use ? bwd_seg_layout(p, sp, L.total).total : L.total;
+}
+
 gdn::Stages stages_at(char* ws, const Layout& L) {
   gdn::Stages st;
   st.table = reinterpret_cast<int32_t*>(ws + L.off[GDN_BUF_CHUNK_TABLE]);
@@ -547,10 +587,20 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_desc* d, gdn_status* status) {
   // N other than 0 or B is read as a packed batch; else the dense reading, whose chunk bound
   // ceil(B T / 64) + B also covers a packed batch of B = 1 and N = 1
   const bool packed = d && d->N != 0 && d->N != d->B;
-  const gdn_status s = bwd_problem(d, packed, &p);
+  gdn_status s = bwd_problem(d, packed, &p);
+  if (s == GDN_OK && d->variant == GDN_VARIANT_SEGMENTED && !bwd_seg_plan(d, p, !packed).use)
+    s = GDN_ERR_UNSUPPORTED;
   if (status) *status = s;
   if (s != GDN_OK) return 0;
-  return bwd_layout(p).total;
+  size_t need = bwd_workspace_for(d, p, !packed);
+  if (!packed && d->B == 1) {
+    // a single sequence may also come as a packed batch of one (cu_seqlens given)
+    gdn::Problem pp = p;
+    pp.N = 1;
+    const size_t alt = bwd_workspace_for(d, pp, false);
+    if (alt > need) need = alt;
+  }
+  return need;
 }
 
 gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const void* v,
@@ -590,8 +640,13 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
     pp.ht = dh0;
     return gdn::launch_recurrent(pp, stream) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   }
+  const bool dense = cu_seqlens == nullptr;
   const BwdLayout L = bwd_layout(p);
-  if (!d->workspace || d->workspace_bytes < L.total || !aligned(d->workspace, kAlign))
+  const SegPlan sp = bwd_seg_plan(d, p, dense);
+  if (d->variant == GDN_VARIANT_SEGMENTED && !sp.use) return GDN_ERR_UNSUPPORTED;
+  const BwdSegLayout SL = bwd_seg_layout(p, sp, L.total);
+  const size_t need = sp.use ? SL.total : L.total;
+  if (!d->workspace || d->workspace_bytes < need || !aligned(d->workspace, kAlign))
     return GDN_ERR_WORKSPACE;
   char* ws = static_cast<char*>(d->workspace);
   gdn::BwdBuffers b;
@@ -609,6 +664,67 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
   b.dqh = p.H != p.Hg ? reinterpret_cast<float*>(ws + L.dqh) : nullptr;
   b.dkh = p.H != p.Hg ? reinterpret_cast<float*>(ws + L.dkh) : nullptr;
   hipError_t e;
+  if (sp.use) {
+    // stages 0-4, then the segmented forward's maps (b, M) and each segment's true start
+    // state h_in, then h_c and v_new from the fused kernel per segment; the reverse pass per
+    // segment from a zero end gradient (each segment's own share e), the segments' end
+    // gradients composed last to first (dh_in = M^T dh_end + e), and the reverse pass per
+    // segment again from its true end gradient, writing dh' and dR
+    int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + SL.base + SL.seg.cu);
+    int32_t* seg_first = reinterpret_cast<int32_t*>(ws + SL.base + SL.seg.first);
+    float* bm = reinterpret_cast<float*>(ws + SL.base + SL.seg.b);
+    float* mm = reinterpret_cast<float*>(ws + SL.base + SL.seg.M);
+    float* hin = reinterpret_cast<float*>(ws + SL.base + SL.seg.h_in);
+    int32_t* seg_chunks = reinterpret_cast<int32_t*>(ws + SL.chunks);
+    const int nseg = (int)sp.nseg;
+    gdn::Problem ps = p;
+    ps.N = nseg;
+    ps.cu = cu_seg;
+    e = gdn::launch_staged(p, b.st, 4, stream);
+    if (e == hipSuccess)
+      e = dense ? gdn::launch_segment_table(cu_seg, p.N, p.T, sp.S, sp.Ls, stream)
+                : gdn::launch_segment_table_packed(p.cu, cu_seg, seg_first, p.N, p.Ttot, sp.Ls,
+                                                   nseg, stream);
+    if (e == hipSuccess)
+      e = gdn::launch_segment_chunks(b.st.seq_chunks, dense ? nullptr : seg_first, seg_chunks,
+                                     p.N, sp.S, sp.Ls / kBwdChunk, nseg, stream);
+    if (e == hipSuccess) {
+      gdn::Problem pb = ps;
+      pb.h0 = nullptr;
+      pb.ht = bm;
+      pb.fused_flags = gdn::kFusedNoOutput;
+      e = gdn::launch_fused(pb, stream);
+    }
+    if (e == hipSuccess) {
+      gdn::Problem pm = ps;
+      pm.h0 = nullptr;
+      pm.ht = mm;
+      pm.fused_flags = gdn::kFusedNoOutput | gdn::kFusedZeroV | gdn::kFusedH0Identity;
+      e = gdn::launch_fused(pm, stream);
+    }
+    const int32_t* first = dense ? nullptr : seg_first;
+    if (e == hipSuccess)
+      e = gdn::launch_segment_scan_ranges(mm, bm, p.h0, hin, nullptr, first, p.N, sp.S, p.H,
+                                          p.D, stream);
+    if (e == hipSuccess) {
+      gdn::Problem pf = ps;
+      pf.h0 = hin;
+      pf.ht = nullptr;
+      pf.fused_flags = gdn::kFusedNoOutput;
+      pf.seq_chunks = seg_chunks;
+      pf.hc_out = b.st.h_c;
+      pf.vnew_out = b.st.v_new;
+      e = gdn::launch_fused(pf, stream);
+    }
+    if (e == hipSuccess)
+      e = gdn::launch_bwd_dh(p, b, nseg, seg_chunks, nullptr, nullptr, nullptr, bm, stream);
+    if (e == hipSuccess)
+      e = gdn::launch_segment_rscan(mm, bm, dht, hin, dh0, first, p.N, sp.S, p.H, p.D, stream);
+    if (e == hipSuccess)
+      e = gdn::launch_bwd_dh(p, b, nseg, seg_chunks, hin, b.dH, b.dR, nullptr, stream);
+    if (e == hipSuccess) e = gdn::launch_bwd_chunk(p, b, stream);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
   if (gdn::fused_supported(p)) {
     // stages 0-4 (chunk table, Gc, T), then h_c and v_new from the fused kernel
     e = gdn::launch_staged(p, b.st, 4, stream);
@@ -684,6 +800,15 @@ int32_t gdn_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens) {
     return -1;
   }
   return resolve_variant(d, p, cu_seqlens == nullptr, true);
+}
+
+int32_t gdn_chunk_bwd_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens) {
+  gdn::Problem p;
+  if (bwd_problem(d, cu_seqlens != nullptr, &p) != GDN_OK) return -1;
+  const SegPlan sp = bwd_seg_plan(d, p, cu_seqlens == nullptr);
+  if (d->variant == GDN_VARIANT_SEGMENTED && !sp.use) return -1;
+  if (sp.use) return GDN_VARIANT_SEGMENTED;
+  return gdn::fused_supported(p) ? GDN_VARIANT_FUSED : GDN_VARIANT_STAGED;
 }
 
 int32_t gdn_resolved_chunk(const gdn_desc* d, const int32_t* cu_seqlens) {

@@ -25,8 +25,10 @@
 // Two kernels follow the staged forward's recomputation (chunk table, Gc, T, W, the chunk-start
 // states and v_new in the workspace):
 //   k_bwd_dh     one workgroup per (sequence, head, 64-column slab of the state): the chunks
-//                in reverse, dh kept in accumulator tiles; writes dh' of every chunk, dDelta,
-//                and dh0;
+//                in reverse, dh kept in accumulator tiles; writes dh' of every chunk, dR,
+//                and dh0.  Long sequences run it per segment (twice: once from a zero end
+//                gradient for each segment's own share, composed in reverse order across
+//                the segments, then from each segment's true end gradient);
 //   k_bwd_chunk  one workgroup per (chunk, head): everything else, in phases that stage their
 //                operands in LDS (each product C = A B^T with both operands k-contiguous).
 // Value heads that share a q/k head write their dq and dk to a per-head buffer that a last
@@ -257,20 +259,23 @@ __global__ __launch_bounds__(kBT, 2) void k_bwd_dh(const int32_t* __restrict__ t
       dr[tb] = zero4();
       mma_accB_T<TI, NT>(dr[tb], sT, LDC, 16 * tb, dd);
     }
-    // the chunk-end gradient dh' and dR, for the chunk-parallel kernel
-    const long coff = ((long)c * H + h) * D * D;
+    // the chunk-end gradient dh' and dR, for the chunk-parallel kernel (not written by the
+    // pass that only finds each segment's start gradient)
+    if (dH) {
+      const long coff = ((long)c * H + h) * D * D;
 #pragma unroll
-    for (int db = 0; db < NDK; ++db)
+      for (int db = 0; db < NDK; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dH[coff + (long)(16 * db + 4 * (l >> 4) + e) * D + col] = (TI)dh[db][e];
+        for (int e = 0; e < 4; ++e)
+          dH[coff + (long)(16 * db + 4 * (l >> 4) + e) * D + col] = (TI)dh[db][e];
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb)
+      for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * tb + 4 * (l >> 4) + e;
-        if (t < len) dRo[v0 + (long)t * H * D + col] = (TI)dr[tb][e];
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * tb + 4 * (l >> 4) + e;
+          if (t < len) dRo[v0 + (long)t * H * D + col] = (TI)dr[tb][e];
+        }
+    }
     // dh = gC dh' + scale Q^T diag(gam) dO - K^T diag(beta gam) dR
     f32x4 go[NT], nd[NT];
 #pragma unroll
@@ -696,18 +701,26 @@ hipError_t set_lds(F f, size_t bytes) {
   } while (0)
 
 template <typename TI, int D>
-hipError_t run_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st) {
+hipError_t run_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
+                      const int32_t* run_chunks, const float* dht, void* dH, void* dR,
+                      float* dh0, hipStream_t st) {
+  if (runs <= 0) return hipSuccess;
+  const size_t sm1 = dh_smem<TI, D>();
+  GDN_BTRY(set_lds(k_bwd_dh<TI, D>, sm1));
+  k_bwd_dh<TI, D><<<dim3(runs, p.H, D / 64), kBT, sm1, st>>>(
+      b.st.table, run_chunks, static_cast<const TI*>(p.q), static_cast<const TI*>(p.k),
+      static_cast<const TI*>(b.st.Tinv), p.beta, p.beta_f32 ? 1 : 0,
+      static_cast<const TI*>(b.dO), b.st.g_t, dht, static_cast<TI*>(dH), static_cast<TI*>(dR),
+      dh0, p.Ttot, p.H, p.Hg, p.scale);
+  return hipGetLastError();
+}
+
+template <typename TI, int D>
+hipError_t run_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st) {
   const TI* q = static_cast<const TI*>(p.q);
   const TI* k = static_cast<const TI*>(p.k);
   const TI* v = static_cast<const TI*>(p.v);
   const TI* dO = static_cast<const TI*>(b.dO);
-  const size_t sm1 = dh_smem<TI, D>();
-  GDN_BTRY(set_lds(k_bwd_dh<TI, D>, sm1));
-  k_bwd_dh<TI, D><<<dim3(p.N, p.H, D / 64), kBT, sm1, st>>>(
-      b.st.table, b.st.seq_chunks, q, k, static_cast<const TI*>(b.st.Tinv), p.beta,
-      p.beta_f32 ? 1 : 0, dO, b.st.g_t, b.dht, static_cast<TI*>(b.dH), static_cast<TI*>(b.dR),
-      b.dh0, p.Ttot, p.H, p.Hg, p.scale);
-  GDN_BTRY(hipGetLastError());
   const bool grouped = p.H != p.Hg;
   const size_t sm2 = ChunkLds<TI, D>::bytes;
   GDN_BTRY(set_lds(k_bwd_chunk<TI, D>, sm2));
@@ -734,9 +747,22 @@ bool bwd_supported(const Problem& p) {
   return p.f32 ? p.D == 64 : (p.D == 64 || p.D == 128);
 }
 
+hipError_t launch_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
+                         const int32_t* run_chunks, const float* dht, void* dH, void* dR,
+                         float* dh0, hipStream_t st) {
+  if (p.f32) return run_bwd_dh<float, 64>(p, b, runs, run_chunks, dht, dH, dR, dh0, st);
+  return p.D == 64 ? run_bwd_dh<bf16, 64>(p, b, runs, run_chunks, dht, dH, dR, dh0, st)
+                   : run_bwd_dh<bf16, 128>(p, b, runs, run_chunks, dht, dH, dR, dh0, st);
+}
+
+hipError_t launch_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st) {
+  if (p.f32) return run_bwd_chunk<float, 64>(p, b, st);
+  return p.D == 64 ? run_bwd_chunk<bf16, 64>(p, b, st) : run_bwd_chunk<bf16, 128>(p, b, st);
+}
+
 hipError_t launch_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st) {
-  if (p.f32) return run_bwd<float, 64>(p, b, st);
-  return p.D == 64 ? run_bwd<bf16, 64>(p, b, st) : run_bwd<bf16, 128>(p, b, st);
+  GDN_BTRY(launch_bwd_dh(p, b, p.N, b.st.seq_chunks, b.dht, b.dH, b.dR, b.dh0, st));
+  return launch_bwd_chunk(p, b, st);
 }
 
 }  // namespace gdn

@@ -85,7 +85,17 @@ struct BwdBuffers {
   float* dkh;
 };
 bool bwd_supported(const Problem& p);
+// Both backward kernels over the sequences (b.dht, b.dH, b.dR, b.dh0 as above).
 hipError_t launch_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st);
+// The reverse pass alone over `runs` runs of consecutive chunks (sequences, or segments of
+// them): run i covers chunks run_chunks[i] .. run_chunks[i + 1] - 1 of the chunk table and
+// starts from dht[i] ([runs, H, D, D] fp32; zero when null); dh0[i] receives the gradient
+// at its start (not written when null); dH and dR as above, not written when dH is null.
+hipError_t launch_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
+                         const int32_t* run_chunks, const float* dht, void* dH, void* dR,
+                         float* dh0, hipStream_t st);
+// The chunk-parallel kernel (and the group sum when H != Hg).
+hipError_t launch_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st);
 bool fused_supported(const Problem& p);
 hipError_t launch_fused(const Problem& p, hipStream_t st);
 // Longest-first order of a packed batch's sequences (order[rank] = sequence), for the fused

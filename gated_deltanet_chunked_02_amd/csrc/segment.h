@@ -21,4 +21,17 @@ hipError_t launch_segment_scan_ranges(const float* M, const float* b, const floa
                                       float* h_in, float* ht, const int32_t* seg_first, int N,
                                       int S, int H, int D, hipStream_t st);
 
+// The backward's composition, in reverse: for the segments of each sequence from last to
+// first, dh_end[s] = x and then x <- M_s^T x + e[s], from x = dht (zero when absent); dh0 (if
+// not null) receives the final x.  D = 64 or 128.
+hipError_t launch_segment_rscan(const float* M, const float* e, const float* dht,
+                                float* dh_end, float* dh0, const int32_t* seg_first, int N,
+                                int S, int H, int D, hipStream_t st);
+
+// seg_chunks[j] = the chunk-table index of segment j's first chunk (cps chunks per segment,
+// segments of sequence n as in launch_segment_scan_ranges); seg_chunks[nseg] = the total.
+hipError_t launch_segment_chunks(const int32_t* seq_chunks, const int32_t* seg_first,
+                                 int32_t* seg_chunks, int N, int S, int cps, int nseg,
+                                 hipStream_t st);
+
 }  // namespace gdn

@@ -81,7 +81,12 @@ __global__ __launch_bounds__(256) void k_segment_table_packed(const int32_t* __r
   for (int i = total + tid; i <= nseg; i += 256) cu_seg[i] = end;
 }
 
-template <int D>
+// REV: the backward's composition.  The gradient reaching a segment's start is affine in
+// the gradient at its end, dh_in = M^T dh_end + e (M^T is the adjoint of the segment's state
+// map; e the segment's own reverse pass from a zero end gradient).  The segments of each
+// sequence are then taken last to first, M is read transposed, h0 is the sequence's dht and
+// ht receives dh0; h_in[s] receives the gradient at segment s's end, and b holds e.
+template <int D, bool REV = false>
 __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ M,
                                                       const float* __restrict__ b,
                                                       const float* __restrict__ h0,
@@ -97,6 +102,7 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
   constexpr int TPW = NBLK * TPB;        // tiles per wave
   constexpr int LD = D + 4;              // padded LDS stride (floats)
   constexpr int NV = RB * D / 4 / 256;   // float4 of a row block of M per thread
+  static_assert(!REV || NBLK == 1, "the transposed composition stages M whole");
   __shared__ __align__(16) float ms[RB * LD];   // a row block of M: [row][k]
   __shared__ __align__(16) float hsT[16 * LD];  // h[k][col] stored as [col][k]
   const int nh = blockIdx.x, slab = blockIdx.y;
@@ -108,7 +114,8 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
   const long hbase = ((long)n * H + h) * DD;
   const int s0 = seg_first ? seg_first[n] : n * S;
   const int ns = seg_first ? seg_first[n + 1] - s0 : S;  // this sequence's segments
-  auto seg_off = [&](int s) { return (((long)s0 + s) * H + h) * DD; };
+  // step s takes segment s, or segment ns - 1 - s in reverse
+  auto seg_off = [&](int s) { return (((long)s0 + (REV ? ns - 1 - s : s)) * H + h) * DD; };
   // accumulator u of a wave: row block u / TPB, tile wave + 4 (u % TPB) within it
   auto tile_of = [&](int u) { return (u / TPB) * NTB + wave + 4 * (u % TPB); };
   auto row_of = [&](int u, int i) { return 16 * tile_of(u) + 4 * lg + i; };
@@ -170,11 +177,19 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
 #pragma unroll
         for (int j = 0; j < TPB; ++j) {
           const int u = bk * TPB + j;
-          const f32x4 av =
-              *reinterpret_cast<const f32x4*>(&ms[(16 * (wave + 4 * j) + lc) * LD + k0 + 4 * lg]);
+          if constexpr (REV) {
+            // M^T[row][k] = M[k][row]: four strided reads (rows 4 apart sit 16 banks apart)
+            const float* pm = &ms[(k0 + 4 * lg) * LD + 16 * (wave + 4 * j) + lc];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc[u], 0, 0, 0);
+            for (int q = 0; q < 4; ++q)
+              acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(pm[q * LD], bv[q], acc[u], 0, 0, 0);
+          } else {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(
+                &ms[(16 * (wave + 4 * j) + lc) * LD + k0 + 4 * lg]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc[u], 0, 0, 0);
+          }
         }
       }
       __syncthreads();  // ms (and, after the last block, hsT) is rewritten next
@@ -186,6 +201,25 @@ __global__ __launch_bounds__(256) void k_segment_scan(const float* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) ht[hbase + (long)row_of(u, i) * D + col] = acc[u][i];
   }
+}
+
+// The first chunk (of the chunk table) of every segment, and the total at [nseg]: segment s
+// of sequence n starts cps = Ls / C chunks after the previous one, clamped to the sequence's
+// chunks; the planned segments past the last real one start (and end) at the total.
+// Thread i takes sequence i (its segments) and table entry i past the real segments.
+__global__ void k_segment_chunks(const int32_t* __restrict__ seq_chunks,
+                                 const int32_t* __restrict__ seg_first,
+                                 int32_t* __restrict__ seg_chunks, int N, int S, int cps,
+                                 int nseg) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < N) {
+    const int j0 = seg_first ? seg_first[i] : i * S, j1 = seg_first ? seg_first[i + 1] : j0 + S;
+    const int c0 = seq_chunks[i], c1 = seq_chunks[i + 1];
+    for (int j = j0; j < j1 && j < nseg; ++j)
+      seg_chunks[j] = min(c0 + (j - j0) * cps, c1);
+  }
+  const int total = min(seg_first ? seg_first[N] : N * S, nseg);
+  if (i >= total && i <= nseg) seg_chunks[i] = seq_chunks[N];
 }
 
 }  // namespace
@@ -207,6 +241,29 @@ hipError_t launch_segment_scan_ranges(const float* M, const float* b, const floa
     k_segment_scan<128><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, seg_first, S, H);
   else
     k_segment_scan<256><<<grid, 256, 0, st>>>(M, b, h0, h_in, ht, seg_first, S, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_rscan(const float* M, const float* e, const float* dht,
+                                float* dh_end, float* dh0, const int32_t* seg_first, int N,
+                                int S, int H, int D, hipStream_t st) {
+  if (N * H == 0) return hipSuccess;
+  const dim3 grid(N * H, D / 16);
+  if (D == 64)
+    k_segment_scan<64, true><<<grid, 256, 0, st>>>(M, e, dht, dh_end, dh0, seg_first, S, H);
+  else if (D == 128)
+    k_segment_scan<128, true><<<grid, 256, 0, st>>>(M, e, dht, dh_end, dh0, seg_first, S, H);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_chunks(const int32_t* seq_chunks, const int32_t* seg_first,
+                                 int32_t* seg_chunks, int N, int S, int cps, int nseg,
+                                 hipStream_t st) {
+  const int n = (N > nseg + 1 ? N : nseg + 1);
+  k_segment_chunks<<<(n + 255) / 256, 256, 0, st>>>(seq_chunks, seg_first, seg_chunks, N, S,
+                                                     cps, nseg);
   return hipGetLastError();
 }
 

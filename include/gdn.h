@@ -235,6 +235,13 @@ gdn_status gdn_fused_sigmoid_gating_delta_rule(const gdn_desc* d, const void* q,
                                                float scale, void* o, float* ht,
                                                hipStream_t stream);
 
+/* How gdn_chunk_bwd(d, ..., cu_seqlens, ...) runs with this descriptor:
+ * GDN_VARIANT_SEGMENTED (both sequential passes per segment), GDN_VARIANT_FUSED (the fused
+ * kernel's recompute, one reverse pass per sequence), GDN_VARIANT_STAGED (the staged
+ * recompute: f32), or -1 if the call would be refused.  Only the nullness of cu_seqlens is
+ * used; host-only, no device work. */
+int32_t gdn_chunk_bwd_resolved_variant(const gdn_desc* d, const int32_t* cu_seqlens);
+
 /* Bytes of workspace gdn_chunk_bwd needs for this descriptor (N other than 0 or B reads as a
  * packed batch of N sequences, anything else as B dense sequences).  Host-only, no device
  * work.  Returns 0 and sets *status on an invalid or unsupported descriptor. */
@@ -244,8 +251,15 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_desc* d, gdn_status* status);
  * speed-ups of the chunked operator, section 4.3; none of the pages prints the backward's
  * formulas).  Given the forward's inputs and the gradients of its outputs, it writes the
  * gradients of its inputs: the exact derivative of the recurrence, computed chunk by chunk
- * (C = 64) from the WY form's quantities, which it recomputes into the workspace with the
- * staged forward's stages 0-6 (nothing of a forward call is kept).
+ * (C = 64) from the forward's chunk quantities, which it recomputes into the workspace
+ * (nothing of a forward call is kept): T = (I + A)^-1 by the staged stages 0-4, then the
+ * chunk-start states and v_new by the fused kernel (bf16), or stages 5-6 (f32).  The
+ * gradients of the chunk-end states then run back through each sequence's chunks in order.
+ * Few long sequences (AUTO: when segmenting pays, as for gdn_chunk_fwd's segmented variant;
+ * GDN_VARIANT_SEGMENTED: always, bf16 only) run both sequential passes per segment: the
+ * states from the segmented forward's maps, and the gradients by the adjoint map (a
+ * segment's start gradient is M^T times its end gradient plus its own share), composed last
+ * to first.  Any other variant keeps one pass per sequence.
  *   dout  [B, T, H, Dv]   qkv_dtype   gradient of o (required)
  *   dht   [N, H, Dk, Dv]  f32         gradient of ht, or NULL (zero)
  *   dq, dk [B, T, Hg, Dk] f32         the q/k heads' gradients (summed over the value heads
@@ -255,7 +269,7 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_desc* d, gdn_status* status);
  *   dh0   [N, H, Dk, Dv]  f32         gradient of h0, or NULL (not written)
  * Inputs, scale, cu_seqlens and their layouts as for gdn_chunk_fwd (h0 NULL = zero state).
  * Supported: bf16 with Dk = Dv in {64, 128}; f32 with Dk = Dv = 64 (else
- * GDN_ERR_UNSUPPORTED).  d->variant, d->chunk and d->stop_after are ignored.  The workspace
+ * GDN_ERR_UNSUPPORTED).  d->chunk and d->stop_after are ignored.  The workspace
  * (d->workspace, 256-byte aligned, gdn_chunk_bwd_workspace_size bytes) is required when
  * B*T > 0, else GDN_ERR_WORKSPACE.  Results do not depend on scheduling (no atomics).
  * Pointers are device pointers aligned to 16 bytes (g, beta, dg, dbeta, cu_seqlens: 4 / 2 /

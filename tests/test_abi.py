@@ -482,11 +482,40 @@ def test_bwd_workspace_covers_the_staged_stages_and_its_gradient_buffers(lib):
     assert bwd_ws(desc(qkv_dtype=0, Dk=128, Dv=128))[0] == 2
     assert bwd_ws(desc(qkv_dtype=0, Dk=64, Dv=64))[0] == 0
     assert bwd_ws(desc(Dk=64, Dv=64))[0] == 0
-    # the chunk, variant and stop_after fields do not change it
+    # the chunk and stop_after fields do not change it, nor a variant other than SEGMENTED
+    # where AUTO keeps one pass per sequence
     assert bwd_ws(desc(chunk=64, variant=2))[1] == n
+    assert bwd_ws(desc(stop_after=3))[1] == n
     # a packed batch of N sequences bounds its chunks by ceil(Ttot / 64) + N
     st, npk = bwd_ws(desc(B=1, T=512, N=5))
     assert st == 0 and npk > n
+
+
+def test_bwd_segments_few_long_sequences(lib):
+    # the long prompt: 32 (sequence, head) pairs, AUTO runs the passes per segment
+    long = desc(B=1, T=65536, N=0, H=32, Hg=16)
+    assert gdn.gdn_chunk_bwd_resolved_variant(long) == "segmented"
+    assert gdn.gdn_chunk_bwd_resolved_variant(desc(B=1, T=65536, N=0, H=32, Hg=16,
+                                                   variant=2)) == "fused"
+    st, nseg = bwd_ws(long)
+    st2, nflat = bwd_ws(desc(B=1, T=65536, N=0, H=32, Hg=16, variant=2))
+    assert st == 0 and st2 == 0 and nseg > nflat
+    # the segment buffers: 8 segments of 8192 tokens (256 segment-head pairs), b, M and h_in
+    # fp32 per (segment, head)
+    assert nseg - nflat >= 3 * 8 * 32 * 128 * 128 * 4
+    # many pairs: one pass per sequence; SEGMENTED forces segments (bf16 only)
+    assert gdn.gdn_chunk_bwd_resolved_variant(desc(B=16, T=8192, N=0, H=32, Hg=32)) == "fused"
+    assert gdn.gdn_chunk_bwd_resolved_variant(desc(variant=3)) == "segmented"
+    assert gdn.gdn_chunk_bwd_resolved_variant(
+        desc(qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64)) == "staged"
+    with pytest.raises(gdn.GdnError):
+        gdn.gdn_chunk_bwd_resolved_variant(desc(qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64,
+                                                variant=3))
+    assert bwd_ws(desc(qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64, variant=3))[0] == 2
+    # a dense single sequence may come packed: the query covers both readings
+    st, n1 = bwd_ws(desc(B=1, T=4096, N=0, H=32, Hg=16, variant=3))
+    st, n2 = bwd_ws(desc(B=1, T=4096, N=2, H=32, Hg=16, variant=3))
+    assert n1 > 0 and n2 > 0
 
 
 def test_bwd_rejects_bad_arguments_before_any_launch(lib):

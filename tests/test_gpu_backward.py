@@ -52,14 +52,14 @@ def oracle_bwd(inp):
                                         cu_seqlens=cu)
 
 
-def run_bwd(inp):
+def run_bwd(inp, variant="auto"):
     from gated_deltanet_chunked_02_amd import chunk_gated_delta_rule_bwd
     dev = torch.device("cuda")
     mv = lambda t: None if t is None else t.to(dev)
     out = chunk_gated_delta_rule_bwd(
         mv(inp["q"]), mv(inp["k"]), mv(inp["v"]), mv(inp["g"]), mv(inp["beta"]),
         mv(inp["do"]), dht=mv(inp["dht"]), scale=inp["scale"], initial_state=mv(inp["h0"]),
-        cu_seqlens=mv(inp["cu_seqlens"]))
+        cu_seqlens=mv(inp["cu_seqlens"]), variant=variant)
     torch.cuda.synchronize()
     return out
 
@@ -188,3 +188,77 @@ def test_backward_full_size_sampled_pairs():
         log(test="backward_fullsize", pair=[n, h], **errs)
         for name, e in errs.items():
             assert e <= tol("bf16", name), (n, h, name, e)
+
+
+# ------------------------------------------------------------------ segmented reverse pass
+SEG_CASES = [
+    # B, T, H, Hg, D, h0, dht, lens: forced segments of 64 tokens and more, ragged last ones
+    (1, 700, 2, 1, 128, True, True, None),
+    (2, 333, 2, 2, 64, False, True, None),
+    (1, 0, 4, 2, 128, True, True, [70, 0, 1, 300, 200, 64]),
+    (1, 0, 2, 2, 64, True, False, [513, 129]),
+]
+
+
+@pytest.mark.parametrize("B,T,H,Hg,D,h0,dht,lens", SEG_CASES)
+def test_backward_segmented_matches_oracle(B, T, H, Hg, D, h0, dht, lens):
+    """Both sequential passes per segment (the state maps of the segmented forward, the
+    adjoint maps composed last to first) against the oracle, and against the one-pass
+    backward on the same inputs."""
+    import gated_deltanet_chunked_02_amd as gdn
+    inp = draw(B=B, T=T, H=H, Hg=Hg, D=D, seed=B * 11 + T + D + H, h0=h0, dht=dht, lens=lens)
+    label = "segmented B%d T%d H%d Hg%d D%d lens %s" % (B, T, H, Hg, D, lens)
+    print(label, flush=True)
+    q, v, beta, cu = inp["q"], inp["v"], inp["beta"], inp["cu_seqlens"]
+    desc = gdn.make_desc(q, v, beta, cu, 64, "segmented")
+    assert gdn.gdn_chunk_bwd_resolved_variant(desc, cu) == "segmented"
+    got = run_bwd(inp, "segmented")
+    compare(inp, got, oracle_bwd(inp), "bf16", label)
+    flat = run_bwd(inp, "fused")
+    for name, x, y in zip(NAMES, got, flat):
+        if x is not None:
+            assert rel_l2(to64(x), to64(y)) <= 1e-2, (name, label)
+
+
+@pytest.mark.parametrize("decay", ["workload", "slow"])
+def test_backward_long_prompt_segments(decay):
+    """1 x 65536 tokens, H = 32 over Hg = 16, D = 128, bf16: AUTO runs the passes per
+    segment (8 segments of 8192 tokens); every gradient against the one-pass backward, and
+    one (sequence, head) pair's dv, dg, dbeta against the oracle (dq and dk sum the two value
+    heads of a q/k head).  With the workload's gates (about e^-0.05 per token) no trace of a
+    segment's start state survives 8192 tokens in fp32, so both paths agree bit for bit;
+    the slow decay (g / 500: about e^-0.8 over a segment) makes the composition across
+    segments carry real weight."""
+    import gated_deltanet_chunked_02_amd as gdn
+    from oracle import backward
+    w = gdn_inputs.WORKLOADS["long"].with_(T=65536)
+    inp = gdn_inputs.draw(w, device="cpu")
+    if decay == "slow":
+        inp["g"] = inp["g"] / 500.0
+    inp.update(gdn_inputs.draw_grads(w, w.B, w.T, w.B, dht_std=0.1))
+    desc = gdn.make_desc(inp["q"], inp["v"], inp["beta"], None, 64, "auto")
+    assert gdn.gdn_chunk_bwd_resolved_variant(desc) == "segmented"
+    print("long prompt backward, segmented", flush=True)
+    got = run_bwd(inp)
+    print("long prompt backward, one pass per sequence", flush=True)
+    flat = run_bwd(inp, "fused")
+    errs = {}
+    for name, x, y in zip(NAMES[:5], got[:5], flat[:5]):
+        errs[name] = rel_l2(to64(x), to64(y))
+    log(test="backward_long_segmented_vs_flat", decay=decay, **errs)
+    for name, e in errs.items():
+        assert e <= 1e-2, (name, e)
+    f = lambda x: x.double().numpy()
+    h = 5
+    sl = lambda x: f(x[:, :, h:h + 1])
+    hk = h // (w.H // w.Hg)
+    ref = backward.recurrence_backward(f(inp["q"][:, :, hk:hk + 1]), f(inp["k"][:, :, hk:hk + 1]),
+                                       sl(inp["v"]), sl(inp["g"]), sl(inp["beta"]), None,
+                                       inp["scale"], sl(inp["do"]), None if inp["dht"] is None
+                                       else f(inp["dht"][:, h:h + 1]))
+    perr = {}
+    for i, name in ((2, "dv"), (3, "dg"), (4, "dbeta")):
+        perr[name] = rel_l2(to64(got[i][:, :, h:h + 1]), ref[i])
+    log(test="backward_long_segmented_pair", decay=decay, head=h, **perr)
+    for name, e in perr.items():
+        assert e <= 1e-2, (name, e)

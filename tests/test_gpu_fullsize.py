@@ -103,3 +103,42 @@ def test_full_size_sampled(case):
     if LOG:
         with open(LOG, "a") as f:
             f.write(json.dumps(rec) + "\n")
+
+
+@pytest.mark.parametrize("T", [16384, 65536])
+def test_long_prompt_slow_decay_segments(T):
+    """The long prompt with its gates divided by 500 (about e^-0.1 per 1024 tokens instead
+    of e^-50): the workload's own gates leave no trace of a segment's start state after a
+    few hundred tokens, so its full-size check cannot see the composition of the segment
+    maps; here each segment keeps a large share of its start state, and the sampled pairs
+    against the oracle check h_in = M h_prev + b across every segment boundary."""
+    import gated_deltanet_chunked_02_amd as gdn
+    w = gdn_inputs.WORKLOADS["long"].with_(T=T)
+    inp = gdn_inputs.draw(w, device="cuda")
+    inp["g"] = inp["g"] / 500.0
+    desc = gdn.make_desc(inp["q"], inp["v"], inp["beta"], None, w.C, "auto")
+    wsb = gdn.gdn_chunk_fwd_workspace_size(desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    desc.workspace, desc.workspace_bytes = ws.data_ptr(), wsb
+    assert gdn.gdn_resolved_variant(desc) == "segmented"
+    print("[fullsize] long T=%d slow decay, segmented" % T, flush=True)
+    o, ht = gdn.chunk_gated_delta_rule(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                       scale=inp["scale"], initial_state=inp["h0"],
+                                       chunk_size=w.C, workspace=ws)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (0, 7), (0, 31)]
+    ref = oracle_pairs(inp, pairs, nthreads=3)
+    worst_o = worst_h = 0.0
+    for (n, h), (o_ref, ht_ref) in ref.items():
+        ts, b, _ = pair_slices(inp, n, h)
+        eo = rel_l2(o[b, ts, h].double().cpu().numpy(), o_ref)
+        eh = rel_l2(ht[n, h].double().cpu().numpy(), ht_ref)
+        assert eo <= TOL_BF16_O, (T, (n, h), eo)
+        assert eh <= TOL_BF16_HT, (T, (n, h), eh)
+        worst_o, worst_h = max(worst_o, eo), max(worst_h, eh)
+    rec = dict(test="full_size_slow_decay", T=T, pairs=len(ref), o_rel_max=worst_o,
+               ht_rel_max=worst_h)
+    print(json.dumps(rec), flush=True)
+    if LOG:
+        with open(LOG, "a") as f:
+            f.write(json.dumps(rec) + "\n")
