@@ -159,6 +159,26 @@ def cpu_baseline(inp, o_gpu, ht_gpu, budget_s: float):
     }
 
 
+def copy_rate(dev, warmup=10, launches=30):
+    """GB/s of a plain 1 GiB device copy (bf16; 1 GiB read + 1 GiB written per launch) on
+    the current stream: the bandwidth a streaming kernel can reach on this machine, measured in
+    the same process after the timed region."""
+    n = 1 << 29
+    a = torch.ones(n, device=dev, dtype=torch.bfloat16)
+    b = torch.empty_like(a)
+    for _ in range(warmup):
+        b.copy_(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(launches):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / launches
+    del a, b
+    return 4 * n / (ms * 1e-3) / 1e9
+
+
 def copy_reference(args, dev):
     """A plain copy of 1 GiB (bf16): 1 GiB read + 1 GiB written per launch."""
     n = 1 << 29
@@ -350,6 +370,7 @@ def bwd_bench(args, dev, gdn, w, inp):
     tokens = q.shape[0] * q.shape[1]
     by = bwd_algorithmic_bytes(inp)
     gbs = by / (avg_ms * 1e-3) / 1e9
+    copy_gbs = copy_rate(dev)
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] timing the oracle's backward on the host", file=sys.stderr, flush=True)
@@ -370,11 +391,13 @@ def bwd_bench(args, dev, gdn, w, inp):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "gdn_chunk_bwd whole call (%s, k_bwd_dh, k_bwd_chunk%s)" % (
-                         {"segmented": "staged stages 0-4, per segment: k_fused maps, segment "
-                                       "scans, k_fused store mode, k_bwd_dh twice",
-                          "fused": "staged stages 0-4, k_fused store mode",
-                          "staged": "staged stages 0-6"}[how],
+                     "copy_GBps": copy_gbs, "frac_of_copy": gbs / copy_gbs,
+                     "kernel": "gdn_chunk_bwd whole call (%s, k_bwd_chunk%s)" % (
+                         {"segmented": "staged stages 0-4; per segment: the k_fused maps and "
+                                       "segment scan, k_fused store mode, k_bwd_dh from zero, "
+                                       "the reverse segment scan, k_bwd_dh",
+                          "fused": "staged stages 0-4, k_fused store mode, k_bwd_dh",
+                          "staged": "staged stages 0-6, k_bwd_dh"}[how],
                          ", k_bwd_group_sum" if w.H != w.Hg else ""),
                      "launch_ms": avg_ms, "algorithmic_bytes": by},
         "cpu_baseline": cpu,
@@ -508,6 +531,9 @@ def main():
         roof = {"bound": "mfma", "achieved": tfl, "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": tfl / peak_tf}
     roof["traffic"] = pmc_traffic(w.name, variant)
+    if bound == "hbm":
+        roof["copy_GBps"] = copy_rate(dev)
+        roof["frac_of_copy"] = gbs / roof["copy_GBps"]
     roof["kernel"] = kernel
     roof["launch_ms"] = avg_ms
     roof["algorithmic_bytes"] = by
