@@ -148,7 +148,7 @@ constexpr size_t dh_smem() {
 }
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kBT, 2) void k_bwd_dh(const int32_t* __restrict__ table,
+__global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const int32_t* __restrict__ table,
                                                 const int32_t* __restrict__ seq_chunks,
                                                 const TI* __restrict__ q,
                                                 const TI* __restrict__ k,

@@ -535,14 +535,28 @@ __global__ __launch_bounds__(kThreads) void k_chunk_o(const int32_t* table, cons
   __syncthreads();
 
   const long hcoff = ((long)c * H + h) * D * D;
+#pragma unroll 1
   for (int p0 = 0; p0 < D; p0 += 64) {
     const int dv = p0 + 16 * w + (l & 15);
-    f32x4 hc[NDK];
+    // the Q h_c part of every row block first, so that h_c is dead before v_new is loaded
+    // (both together do not fit in registers at D = 256)
+    f32x4 acc[NT];
+    {
+      f32x4 hc[NDK];
 #pragma unroll
-    for (int db = 0; db < NDK; ++db)
+      for (int db = 0; db < NDK; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        hc[db][e] = (float)h_c[hcoff + (long)(16 * db + 4 * (l >> 4) + e) * D + dv];
+        for (int e = 0; e < 4; ++e)
+          hc[db][e] = (float)h_c[hcoff + (long)(16 * db + 4 * (l >> 4) + e) * D + dv];
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb) {
+        acc[tb] = zero4();
+        mma_accB<TI, NDK>(acc[tb], sQ, LDQ, tb * 16, 0, hc, NDK);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[tb][e] *= __expf(sG[tb * 16 + 4 * (l >> 4) + e]);
+        sched_fence();  // one row block's fragments at a time (no spills at D = 256)
+      }
+    }
     f32x4 vt[NT];
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb)
@@ -554,16 +568,13 @@ __global__ __launch_bounds__(kThreads) void k_chunk_o(const int32_t* table, cons
       }
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb) {
-      f32x4 acc = zero4();
-      mma_accB<TI, NDK>(acc, sQ, LDQ, tb * 16, 0, hc, NDK);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] *= __expf(sG[tb * 16 + 4 * (l >> 4) + e]);
-      mma_accB<TI, NT>(acc, sP, LDP, tb * 16, 0, vt, tb + 1);
+      mma_accB<TI, NT>(acc[tb], sP, LDP, tb * 16, 0, vt, tb + 1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = tb * 16 + 4 * (l >> 4) + e;
-        if (t < len) o[((long)(start + t) * H + h) * D + dv] = (TI)(scale * acc[e]);
+        if (t < len) o[((long)(start + t) * H + h) * D + dv] = (TI)(scale * acc[tb][e]);
       }
+      sched_fence();
     }
   }
 }

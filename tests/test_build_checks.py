@@ -81,3 +81,23 @@ def test_built_assembly_is_clean():
     for fn in files:
         text = open(fn).read()
         assert mfma_mixed_chains(text) == [], fn
+
+
+def test_no_kernel_uses_scratch():
+    """Every kernel of the build keeps its values in registers and LDS: the code-object
+    metadata gives each kernel's private (scratch) bytes per lane, which must be zero (a
+    spill or a stack array would put per-lane memory traffic into the hot loops)."""
+    import re
+    files = glob.glob(os.path.join(BUILD, "*.gfx950.s"))
+    if not files:
+        import pytest
+        pytest.skip("no build output")
+    seen = 0
+    for fn in files:
+        text = open(fn).read()
+        for blk in re.findall(r"- \.agpr_count:.*?\.vgpr_spill_count:\s*\d+", text, re.S):
+            name = re.search(r"\.name:\s+(\S+)", blk).group(1)
+            private = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", blk).group(1))
+            assert private == 0, (os.path.basename(fn), name, private)
+            seen += 1
+    assert seen > 20
