@@ -24,7 +24,7 @@
 //
 // Two kernels follow the staged forward's recomputation (chunk table, Gc, T, W, the chunk-start
 // states and v_new in the workspace):
-//   k_bwd_dh     one workgroup per (sequence, head, 64-column slab of the state): the chunks
+//   k_bwd_dh     one workgroup per (sequence, head), a wave per 16 state columns: the chunks
 //                in reverse, dh kept in accumulator tiles; writes dh' of every chunk, dR,
 //                and dh0.  Long sequences run it per segment (twice: once from a zero end
 //                gradient for each segment's own share, composed in reverse order across
@@ -41,30 +41,19 @@ namespace gdn {
 
 namespace {
 
-constexpr int kBT = 256;   // threads of the dh workgroup (4 waves)
 constexpr int kBT2 = 512;  // threads of the chunk workgroup (8 waves)
+
+// threads of the dh workgroup: one wave per 16 state columns
+template <int D>
+constexpr int dh_threads() { return 4 * D; }
 constexpr int kBC = 64;   // chunk length of the backward
 
 __device__ __forceinline__ int4 chunk_of(const int32_t* table, int c) {
   return reinterpret_cast<const int4*>(table)[c];
 }
 
-template <typename TI, int ROWS, int COLS, int NTH = kBT>
+template <typename TI, int ROWS, int COLS, int NTH>
 using Blk = TileCopy<TI, ROWS, COLS, NTH>;
-
-template <typename TI, int ROWS, int COLS, int NTH = kBT>
-__device__ __forceinline__ void ld_nat(TI* dst, int ld, const TI* src, long stride, int len) {
-  Blk<TI, ROWS, COLS, NTH> b;
-  b.load(src, stride, len);
-  b.store_nat(dst, ld);
-}
-
-template <typename TI, int ROWS, int COLS, int NTH = kBT>
-__device__ __forceinline__ void ld_tr(TI* dst, int ld, const TI* src, long stride, int len) {
-  Blk<TI, ROWS, COLS, NTH> b;
-  b.load(src, stride, len);
-  b.store_trn(dst, ld);
-}
 
 // Sum over the 16 lanes of a lane group (one accumulator row, its 16 columns).
 __device__ __forceinline__ float sum16(float x) {
@@ -138,17 +127,18 @@ __device__ __forceinline__ void mma_lds_Bn(f32x4& acc, const TI* A, int lda, int
 
 // With W = T diag(beta gam) K, the update's W^T dDelta is K^T diag(beta gam) dR, dR = T^T
 // dDelta: the pass reads rows of T (C x C) instead of W (C x D), and hands dR to the chunk
-// kernel.  Every tile sits in LDS in its natural layout (Q, K [C][LDD]; T, P^T [C][LDC];
-// this slab of dO [C][LDO]); the transposed operands Q^T, K^T, T^T and dO^T are read from
-// them directly.  About 63 KB at D = 128 in bf16.
+// kernel.  One workgroup per (sequence, head), wave w owning state columns 16 w .. 16 w + 15,
+// so Q, K and T are read and P is built once per chunk.  Every tile sits in LDS in its
+// natural layout (Q, K, dO [C][LDD]; T, P^T [C][LDC]); the transposed operands Q^T, K^T, T^T
+// and dO^T are read from them directly.  About 69 KB at D = 128 in bf16.
 template <typename TI, int D>
 constexpr size_t dh_smem() {
-  constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>(), LDO = 64 + pad_of<TI>();
-  return (2 * kBC * LDD + 2 * kBC * LDC + kBC * LDO) * sizeof(TI) + 2 * kBC * sizeof(float);
+  constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>();
+  return (3 * kBC * LDD + 2 * kBC * LDC) * sizeof(TI) + 2 * kBC * sizeof(float);
 }
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const int32_t* __restrict__ table,
+__global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __restrict__ table,
                                                 const int32_t* __restrict__ seq_chunks,
                                                 const TI* __restrict__ q,
                                                 const TI* __restrict__ k,
@@ -160,19 +150,18 @@ __global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const i
                                                 TI* __restrict__ dH, TI* __restrict__ dRo,
                                                 float* __restrict__ dh0, int Ttot, int H,
                                                 int Hg, float scale) {
-  constexpr int C = kBC, NDK = D / 16, NT = C / 16;
-  constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>(), LDO = 64 + pad_of<TI>();
+  constexpr int C = kBC, NDK = D / 16, NT = C / 16, NW = D / 16, NTH = dh_threads<D>();
+  constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>();
   const int n = blockIdx.x, h = blockIdx.y, hk = h / (H / Hg);
   const int w = wave_id(), l = lane_id();
-  const int scol = 16 * w + (l & 15);           // column within the 64-column slab
-  const int col = blockIdx.z * 64 + scol;       // state column
+  const int col = 16 * w + (l & 15);  // this lane's state column
   extern __shared__ __align__(16) char smem[];
   TI* sQ = reinterpret_cast<TI*>(smem);  // [C][LDD]
   TI* sK = sQ + C * LDD;                 // [C][LDD]
-  TI* sT = sK + C * LDD;                 // [C][LDC]  rows of T
+  TI* sO = sK + C * LDD;                 // [C][LDD]  dO
+  TI* sT = sO + C * LDD;                 // [C][LDC]  rows of T
   TI* sPt = sT + C * LDC;                // [C][LDC]  P^T
-  TI* sO = sPt + C * LDC;                // [C][LDO]  this slab of dO
-  float* sG = reinterpret_cast<float*>(sO + C * LDO);
+  float* sG = reinterpret_cast<float*>(sPt + C * LDC);
   float* sBeta = sG + C;
 
   // dh tile db: rows (key index) 16 db + 4 (l/16) + e, column col
@@ -187,9 +176,8 @@ __global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const i
   // the chunk's operands are loaded one chunk ahead (into registers) while the previous one
   // is computed
   const int c0 = seq_chunks[n], c1 = seq_chunks[n + 1];
-  Blk<TI, C, D> bq, bk;
-  Blk<TI, C, C> bt;
-  Blk<TI, C, 64> bo;
+  Blk<TI, C, D, NTH> bq, bk, bo;
+  Blk<TI, C, C, NTH> bt;
   float gt = 0.f, bet = 0.f;
   int glen = 0;
   auto fetch = [&](int c) {
@@ -199,7 +187,7 @@ __global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const i
     bq.load(q + qk0, (long)Hg * D, len);
     bk.load(k + qk0, (long)Hg * D, len);
     bt.load(Tinv + ((long)start * H + h) * C, (long)H * C, len);
-    bo.load(dO + v0 + blockIdx.z * 64, (long)H * D, len);
+    bo.load(dO + v0, (long)H * D, len);
     const int tt = min((int)threadIdx.x, len - 1);
     gt = g_t[(long)h * Ttot + start + tt];
     bet = load_beta(beta, beta_f32, (long)(start + tt) * H + h);
@@ -214,7 +202,7 @@ __global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const i
     bq.store_nat(sQ, LDD);
     bk.store_nat(sK, LDD);
     bt.store_nat(sT, LDC);
-    bo.store_nat(sO, LDO);
+    bo.store_nat(sO, LDD);
     if (threadIdx.x < C) {
       const bool in = (int)threadIdx.x < glen;
       sG[threadIdx.x] = in ? gt : 0.f;
@@ -223,10 +211,10 @@ __global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const i
     if (c > c0) fetch(c - 1);
     __syncthreads();
     // P^T: P[i][j] = scale (q_i . k_j) e^{Gc_i - Gc_j} for j <= i < len, stored at [j][i]
-    // (wave w: 4 of the 16 tiles)
+    // (wave w: tiles w, w + NW, ... of the 16)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int u = w + 4 * m, ti = u >> 2, tj = u & 3;
+    for (int m = 0; m < 16 / NW; ++m) {
+      const int u = w + NW * m, ti = u >> 2, tj = u & 3;
       f32x4 acc = zero4();
       if (ti >= tj) mma_lds<TI>(acc, sQ, LDD, 16 * ti, sK, LDD, 16 * tj, 0, D);
       const int j = 16 * tj + (l & 15);
@@ -244,7 +232,7 @@ __global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const i
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb) {
       f32x4 a = zero4(), x = zero4();
-      mma_lds_Bn<TI, C>(a, sPt, LDC, 16 * tb, sO, LDO, 16 * w);
+      mma_lds_Bn<TI, C>(a, sPt, LDC, 16 * tb, sO, LDD, 16 * w);
       mma_accB<TI, NDK>(x, sK, LDD, 16 * tb, 0, dh, NDK);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -284,7 +272,7 @@ __global__ __launch_bounds__(kBT, sizeof(TI) == 2 ? 2 : 1) void k_bwd_dh(const i
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * tb + 4 * (l >> 4) + e;
         const float gam = t < len ? __expf(sG[t]) : 0.f;
-        go[tb][e] = scale * gam * (float)sO[t * LDO + scol];
+        go[tb][e] = scale * gam * (float)sO[t * LDD + col];
         nd[tb][e] = -sBeta[t] * gam * dr[tb][e];
       }
 #pragma unroll
@@ -707,7 +695,7 @@ hipError_t run_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
   if (runs <= 0) return hipSuccess;
   const size_t sm1 = dh_smem<TI, D>();
   GDN_BTRY(set_lds(k_bwd_dh<TI, D>, sm1));
-  k_bwd_dh<TI, D><<<dim3(runs, p.H, D / 64), kBT, sm1, st>>>(
+  k_bwd_dh<TI, D><<<dim3(runs, p.H), dh_threads<D>(), sm1, st>>>(
       b.st.table, run_chunks, static_cast<const TI*>(p.q), static_cast<const TI*>(p.k),
       static_cast<const TI*>(b.st.Tinv), p.beta, p.beta_f32 ? 1 : 0,
       static_cast<const TI*>(b.dO), b.st.g_t, dht, static_cast<TI*>(dH), static_cast<TI*>(dR),
