@@ -41,7 +41,12 @@ namespace gdn {
 
 namespace {
 
-constexpr int kBT2 = 512;  // threads of the chunk workgroup (8 waves)
+// threads of the chunk workgroup: 8 waves, two 16-row blocks of the C x D outputs each.  The
+// kernel also runs with 16 waves of one row block each (1024 threads; at D = 128 in bf16 it
+// then holds 114 registers, four waves per SIMD), but the extra fragment reads made the
+// headline backward slower (10.4 against 10.0 ms).
+template <typename TI, int D>
+constexpr int chunk_threads() { return 512; }
 
 // threads of the dh workgroup: one wave per 16 state columns
 template <int D>
@@ -291,9 +296,10 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
 }
 
 // ------------------------------------------------------------------------- chunk gradients
-// One workgroup of 8 waves per (chunk, head).  Wave w = 4 rh + cw: in the C x D products it
-// owns the row blocks 2 rh, 2 rh + 1 and the column blocks cw + 4 m (m < D / 64); in the
-// C x C products the row block cw and the column blocks 2 rh, 2 rh + 1.  Every tile sits in
+// One workgroup of 4 RW waves per (chunk, head) (RW = 2 or 4 row groups, RPW = 4 / RW).
+// Wave w = 4 rh + cw: in the C x D products it owns the row blocks RPW rh .. RPW rh + RPW - 1
+// and the column blocks cw + 4 m (m < D / 64); in the C x C products the row block cw and
+// the column blocks RPW rh .. RPW rh + RPW - 1.  Every tile sits in
 // LDS in its natural layout and the transposed operands are read from it (frag_tr), so h
 // and dh' are each loaded once and every product that needs them runs while they are
 // resident.
@@ -309,7 +315,7 @@ struct ChunkLds {
 };
 
 template <typename TI, int D>
-__global__ __launch_bounds__(kBT2) void k_bwd_chunk(
+__global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
     const int32_t* __restrict__ table, const TI* __restrict__ q, const TI* __restrict__ k,
     const TI* __restrict__ v, const void* __restrict__ beta, int beta_f32,
     const float* __restrict__ g_t, const TI* __restrict__ h_c,
@@ -319,7 +325,9 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
     int Ttot, int H, int Hg, float scale) {
   typedef ChunkLds<TI, D> L;
   typedef Mma<TI> MM;
-  constexpr int C = kBC, CBW = D / 64, N2 = kBT2;  // column blocks per wave (C x D outputs)
+  constexpr int C = kBC, CBW = D / 64, N2 = chunk_threads<TI, D>();  // CBW: column blocks
+                                                                      // per wave
+  constexpr int RW = N2 / 256, RPW = 4 / RW;  // row groups of waves; row blocks per wave
   constexpr int LDD = L::LDD, LDC = L::LDC;
   const int c = blockIdx.x, h = blockIdx.y;
   const int4 ci = chunk_of(table, c);
@@ -342,17 +350,17 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   float* sG = reinterpret_cast<float*>(sDB + L::CC);
   float* sBeta = sG + C;
   // sPart [16 C]: the row dots' parts [quantity x][column wave][C] (x = 0..3); after they
-  // are summed: the last token's shares at 5 C, dGc at 6 C, rowsum(E) per row half at 8 C,
-  // rowsum(dA * KK * Gam) per row half at 10 C
+  // are summed: the last token's shares at 5 C, dGc at 6 C, rowsum(E) per row group of
+  // waves at 8 C, rowsum(dA * KK * Gam) per row group at 12 C (at most four groups each)
   float* sPart = sBeta + C;
   float* sRD = sPart + 16 * C;   // [4][C] the row dots (1: Delta.K dh', 2: dR.K h, 3: dR.V);
                                  // its first C floats hold the parts of <dh', h>
   float* sColE = sRD + 4 * C;    // [4 row blocks][C] partial colsum(E)
-  float* sHdh = sRD;
+  float* sHdh = sRD;              // one part per wave (at most C waves)
   float* sShare = sPart + 5 * C;
   float* sDgc = sPart + 6 * C;
   float* sRowE = sPart + 8 * C;
-  float* sRowB = sPart + 10 * C;
+  float* sRowB = sPart + 12 * C;
 
   const long qk0 = ((long)start * Hg + hk) * D, v0 = ((long)start * H + h) * D;
   const long hcoff = ((long)c * H + h) * D * D;
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   // fragment readers of the C x D products: rows 32 rh + 16 i of a [C][LD] panel; the
   // B operands of columns 16 (cw + 4 j): natural rows of a [.][LD] matrix, or M^T from M
   auto rows = [&](const TI* Pm, int ld) {
-    return [=](int i, int kk) { return frag_ld<TI>(Pm, ld, 32 * rh + 16 * i, kk); };
+    return [=](int i, int kk) { return frag_ld<TI>(Pm, ld, 16 * RPW * rh + 16 * i, kk); };
   };
   auto cols = [&](const TI* Pm, int ld) {
     return [=](int j, int kk) { return frag_ld<TI>(Pm, ld, 16 * (cw + 4 * j), kk); };
@@ -412,36 +420,38 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   };
 
   // ---- phase B, h resident: K h, dO h^T (into aq), dR h^T (into ak), row dots
-  f32x4 aq[2][CBW], ak[2][CBW];
+  f32x4 aq[RPW][CBW], ak[RPW][CBW];
   {
-    f32x4 Kh[2][CBW];
+    f32x4 Kh[RPW][CBW];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < RPW; ++b)
 #pragma unroll
       for (int m = 0; m < CBW; ++m) Kh[b][m] = aq[b][m] = ak[b][m] = zero4();
-    mma_steps<TI, D, 2, CBW>(rows(sK, LDD), colsT(sBig, LDD), [&](auto& fa, auto& fb) {
+    mma_steps<TI, D, RPW, CBW>(rows(sK, LDD), colsT(sBig, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < RPW; ++b)
 #pragma unroll
         for (int m = 0; m < CBW; ++m) Kh[b][m] = MM::mma(fa[b], fb[m], Kh[b][m]);
     });
-    mma_steps<TI, D, 4, CBW>(
-        [&](int i, int kk) { return frag_ld<TI>(i < 2 ? sO : sC, LDD, 32 * rh + 16 * (i & 1), kk); },
+    mma_steps<TI, D, 2 * RPW, CBW>(
+        [&](int i, int kk) {
+          return frag_ld<TI>(i < RPW ? sO : sC, LDD, 16 * RPW * rh + 16 * (i % RPW), kk);
+        },
         cols(sBig, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int b = 0; b < RPW; ++b)
 #pragma unroll
             for (int m = 0; m < CBW; ++m) {
               aq[b][m] = MM::mma(fa[b], fb[m], aq[b][m]);
-              ak[b][m] = MM::mma(fa[2 + b], fb[m], ak[b][m]);
+              ak[b][m] = MM::mma(fa[RPW + b], fb[m], ak[b][m]);
             }
         });
     // row dots over the wave's columns: dR.K h, dR.V, Q.(dO h^T) = dO.Q h
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < RPW; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        const int t = 16 * (RPW * rh + b) + 4 * lg + e;
         float p0 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
         for (int m = 0; m < CBW; ++m) {
@@ -479,28 +489,28 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   // ---- phase B', dh' resident: K dh' (row dot with Delta) and Delta dh'^T (into ak)
   const float gC = sG[len - 1];
   {
-    f32x4 Kd[2][CBW], X[2][CBW];
+    f32x4 Kd[RPW][CBW], X[RPW][CBW];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < RPW; ++b)
 #pragma unroll
       for (int m = 0; m < CBW; ++m) Kd[b][m] = X[b][m] = zero4();
-    mma_steps<TI, D, 2, CBW>(rows(sK, LDD), colsT(sBig, LDD), [&](auto& fa, auto& fb) {
+    mma_steps<TI, D, RPW, CBW>(rows(sK, LDD), colsT(sBig, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < RPW; ++b)
 #pragma unroll
         for (int m = 0; m < CBW; ++m) Kd[b][m] = MM::mma(fa[b], fb[m], Kd[b][m]);
     });
-    mma_steps<TI, D, 2, CBW>(rows(sDl, LDD), cols(sBig, LDD), [&](auto& fa, auto& fb) {
+    mma_steps<TI, D, RPW, CBW>(rows(sDl, LDD), cols(sBig, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < RPW; ++b)
 #pragma unroll
         for (int m = 0; m < CBW; ++m) X[b][m] = MM::mma(fa[b], fb[m], X[b][m]);
     });
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < RPW; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        const int t = 16 * (RPW * rh + b) + 4 * lg + e;
         float p1 = 0.f;
         const float r = __expf(gC - sG[t]);
 #pragma unroll
@@ -520,24 +530,25 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   }
 
   // ---- phase C: the C x C products and their elementwise terms
-  f32x4 KK[2], QK[2], E1[2], RD[2];
-  KK[0] = KK[1] = QK[0] = QK[1] = E1[0] = E1[1] = RD[0] = RD[1] = zero4();
-  mma_steps<TI, D, 2, 2>(
+  f32x4 KK[RPW], QK[RPW], E1[RPW], RD[RPW];
+#pragma unroll
+  for (int b = 0; b < RPW; ++b) KK[b] = QK[b] = E1[b] = RD[b] = zero4();
+  mma_steps<TI, D, 2, RPW>(
       [&](int i, int kk) { return frag_ld<TI>(i ? sQ : sK, LDD, 16 * cw, kk); },
-      [&](int j, int kk) { return frag_ld<TI>(sK, LDD, 32 * rh + 16 * j, kk); },
+      [&](int j, int kk) { return frag_ld<TI>(sK, LDD, 16 * RPW * rh + 16 * j, kk); },
       [&](auto& fa, auto& fb) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < RPW; ++b) {
           KK[b] = MM::mma(fa[0], fb[b], KK[b]);
           QK[b] = MM::mma(fa[1], fb[b], QK[b]);
         }
       });
-  mma_steps<TI, D, 2, 2>(
+  mma_steps<TI, D, 2, RPW>(
       [&](int i, int kk) { return frag_ld<TI>(i ? sC : sO, LDD, 16 * cw, kk); },
-      [&](int j, int kk) { return frag_ld<TI>(sDl, LDD, 32 * rh + 16 * j, kk); },
+      [&](int j, int kk) { return frag_ld<TI>(sDl, LDD, 16 * RPW * rh + 16 * j, kk); },
       [&](auto& fa, auto& fb) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < RPW; ++b) {
           E1[b] = MM::mma(fa[0], fb[b], E1[b]);
           RD[b] = MM::mma(fa[1], fb[b], RD[b]);
         }
@@ -545,8 +556,8 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   __syncthreads();  // the row-dot parts are summed before sRowE / sRowB reuse their space
   float rowE[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int j = 16 * (2 * rh + b) + lc;
+  for (int b = 0; b < RPW; ++b) {
+    const int j = 16 * (RPW * rh + b) + lc;
     float colE = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -577,44 +588,44 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
   __syncthreads();
 
   // ---- phase D: Mi K into aq; (DB + DB^T) K and Mi^T Q into ak
-  mma_steps<TI, C, 4, CBW>(
+  mma_steps<TI, C, 2 * RPW, CBW>(
       [&](int i, int kk) {
-        const TI* Pm = (i & 2) ? sDB : sMi;
-        return frag_ld<TI>(Pm, LDC, 32 * rh + 16 * (i & 1), kk);
+        const TI* Pm = i >= RPW ? sDB : sMi;
+        return frag_ld<TI>(Pm, LDC, 16 * RPW * rh + 16 * (i % RPW), kk);
       },
       colsT(sK, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < RPW; ++b)
 #pragma unroll
           for (int m = 0; m < CBW; ++m) {
             aq[b][m] = MM::mma(fa[b], fb[m], aq[b][m]);
-            ak[b][m] = MM::mma(fa[2 + b], fb[m], ak[b][m]);
+            ak[b][m] = MM::mma(fa[RPW + b], fb[m], ak[b][m]);
           }
       });
-  mma_steps<TI, C, 2, CBW>(
-      [&](int i, int kk) { return frag_tr<TI>(sDB, LDC, 32 * rh + 16 * i, kk); },  // DB^T
+  mma_steps<TI, C, RPW, CBW>(
+      [&](int i, int kk) { return frag_tr<TI>(sDB, LDC, 16 * RPW * rh + 16 * i, kk); },  // DB^T
       colsT(sK, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < RPW; ++b)
 #pragma unroll
           for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
       });
-  mma_steps<TI, C, 2, CBW>(
-      [&](int i, int kk) { return frag_tr<TI>(sMi, LDC, 32 * rh + 16 * i, kk); },  // Mi^T
+  mma_steps<TI, C, RPW, CBW>(
+      [&](int i, int kk) { return frag_tr<TI>(sMi, LDC, 16 * RPW * rh + 16 * i, kk); },  // Mi^T
       colsT(sQ, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < RPW; ++b)
 #pragma unroll
           for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
       });
   const long dq0 = ((long)start * qk_rows + hq) * D;
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < RPW; ++b)
 #pragma unroll
     for (int m = 0; m < CBW; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * (2 * rh + b) + 4 * lg + e;
+        const int t = 16 * (RPW * rh + b) + 4 * lg + e;
         if (t < len) {
           const long gi = dq0 + (long)t * qk_rows * D + 16 * (cw + 4 * m) + lc;
           dq[gi] = aq[b][m][e];
@@ -630,9 +641,14 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
       const float gam = __expf(sG[t]), r = __expf(gC - sG[t]);
       const float colE = sColE[t] + sColE[C + t] + sColE[2 * C + t] + sColE[3 * C + t];
       const float rq = sPart[t] + sPart[C + t] + sPart[2 * C + t] + sPart[3 * C + t];
-      db = sRD[3 * C + t] - gam * sRD[2 * C + t] + sRowB[t] + sRowB[C + t];
-      dgc = scale * gam * rq - r * sRD[C + t] - sBeta[t] * gam * sRD[2 * C + t] +
-            sRowE[t] + sRowE[C + t] - colE;
+      float rowB = 0.f, rowE = 0.f;
+#pragma unroll
+      for (int x = 0; x < RW; ++x) {
+        rowB += sRowB[x * C + t];
+        rowE += sRowE[x * C + t];
+      }
+      db = sRD[3 * C + t] - gam * sRD[2 * C + t] + rowB;
+      dgc = scale * gam * rq - r * sRD[C + t] - sBeta[t] * gam * sRD[2 * C + t] + rowE - colE;
       sShare[t] = r * sRD[C + t];  // the last token's share of h' = gC h + ...
     }
     sDgc[t] = dgc;
@@ -643,7 +659,7 @@ __global__ __launch_bounds__(kBT2) void k_bwd_chunk(
     // the last token: + sum_t (gC / gam_t) rowsum(Delta * K dh')_t + gC <dh', h>, then the
     // suffix sums in token order (fixed order: deterministic)
     float hdh = 0.f;
-    for (int i = 0; i < kBT2 / 64; ++i) hdh += sHdh[i];
+    for (int i = 0; i < chunk_threads<TI, D>() / 64; ++i) hdh += sHdh[i];
     float s = 0.f;
     for (int t = 0; t < len; ++t) s += sShare[t];
     sDgc[len - 1] += s + __expf(gC) * hdh;
@@ -712,7 +728,7 @@ hipError_t run_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st) 
   const bool grouped = p.H != p.Hg;
   const size_t sm2 = ChunkLds<TI, D>::bytes;
   GDN_BTRY(set_lds(k_bwd_chunk<TI, D>, sm2));
-  k_bwd_chunk<TI, D><<<dim3(p.max_chunks, p.H), kBT2, sm2, st>>>(
+  k_bwd_chunk<TI, D><<<dim3(p.max_chunks, p.H), chunk_threads<TI, D>(), sm2, st>>>(
       b.st.table, q, k, v, p.beta, p.beta_f32 ? 1 : 0, b.st.g_t,
       static_cast<const TI*>(b.st.h_c),
       static_cast<const TI*>(b.st.v_new), static_cast<const TI*>(b.dR),
