@@ -266,8 +266,9 @@ size_t workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
 }
 
 // The backward pass recomputes the forward's chunk quantities at C = 64 into the staged
-// layout at the front of its workspace (stages 0-4, then the chunk-start states and v_new
-// from the fused kernel's store mode in bf16, or from stages 5-6 in fp32), then keeps dR
+// layout at the front of its workspace, without A (stages 0-2, then T by one launch that
+// keeps A on chip, then the chunk-start states and v_new from the fused kernel's store mode
+// in bf16, or from stages 5-6 in fp32), then keeps dR
 // [Ttot, H, D] and each chunk's end-state gradient [max_chunks, H, D, D] in the q/k/v dtype
 // and (H != Hg) per-value-head dq and dk [Ttot, H, D] in fp32.
 constexpr int kBwdChunk = 64;
@@ -297,6 +298,14 @@ gdn_status bwd_problem(const gdn_desc* d, bool packed, gdn::Problem* p) {
 BwdLayout bwd_layout(const gdn::Problem& p) {
   BwdLayout L;
   staged_layout(p, &L.st);
+  // A stays on chip (stages 3 and 4 run as one launch): no room for it
+  L.st.bytes[GDN_BUF_A] = 0;
+  size_t off = 0;
+  for (int i = 0; i < GDN_BUF_COUNT; ++i) {
+    L.st.off[i] = off;
+    off += align_up(L.st.bytes[i]);
+  }
+  L.st.total = off;
   const size_t e = p.f32 ? 4 : 2;
   const size_t tok = (size_t)p.Ttot * p.H * p.D * sizeof(float);
   L.dR = L.st.total;
@@ -680,7 +689,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
     gdn::Problem ps = p;
     ps.N = nseg;
     ps.cu = cu_seg;
-    e = gdn::launch_staged(p, b.st, 4, stream);
+    e = gdn::launch_staged(p, b.st, 4, stream, true);
     if (e == hipSuccess)
       e = dense ? gdn::launch_segment_table(cu_seg, p.N, p.T, sp.S, sp.Ls, stream)
                 : gdn::launch_segment_table_packed(p.cu, cu_seg, seg_first, p.N, p.Ttot, sp.Ls,
@@ -727,7 +736,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
   }
   if (gdn::fused_supported(p)) {
     // stages 0-4 (chunk table, Gc, T), then h_c and v_new from the fused kernel
-    e = gdn::launch_staged(p, b.st, 4, stream);
+    e = gdn::launch_staged(p, b.st, 4, stream, true);
     if (e == hipSuccess) {
       gdn::Problem pf = p;
       pf.fused_flags = gdn::kFusedNoOutput;
@@ -737,7 +746,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
       e = gdn::launch_fused(pf, stream);
     }
   } else {
-    e = gdn::launch_staged(p, b.st, 6, stream);
+    e = gdn::launch_staged(p, b.st, 6, stream, true);
   }
   if (e == hipSuccess) e = gdn::launch_bwd(p, b, stream);
   return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;

@@ -59,7 +59,10 @@ struct Stages {
   void* v_new;          // [Ttot][H][D]
 };
 
-hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st);
+// fuse_kkt_solve (C = 64, D <= 128): stages 3 and 4 as one launch that keeps A on chip (A is
+// then not written); for callers that need only T, as the backward does.
+hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st,
+                         bool fuse_kkt_solve = false);
 // Stage 0 alone: the chunk table and each sequence's first chunk at p.C.
 hipError_t launch_chunk_table(const Problem& p, const Stages& s, hipStream_t st);
 

@@ -237,6 +237,30 @@ __global__ __launch_bounds__(kThreads) void k_kkt(const int32_t* table, const TI
 template <typename TI> struct SolveType { typedef f16 type; };
 template <> struct SolveType<float> { typedef float type; };
 
+// Rows t < len of T (lower triangle of sM [C][ld]; the upper part written as zeros) to dst
+// (row stride `stride` elements), eight elements per store.
+template <typename TI, int C, typename TS>
+__device__ __forceinline__ void store_T_rows(const TS* sM, int ld, TI* dst, long stride,
+                                             int len) {
+  constexpr int P8 = C / 8, OITER = (C * P8 + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int it = 0; it < OITER; ++it) {
+    const int i = threadIdx.x + it * kThreads;
+    const int t = i / P8, j0 = (i - t * P8) * 8;
+    if (i < C * P8 && t < len) {
+      union {
+        uint4 u[2];
+        TI e[8];
+      } o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o.e[e] = (TI)(j0 + e <= t ? (float)sM[t * ld + j0 + e] : 0.f);
+      uint4* d = reinterpret_cast<uint4*>(dst + (long)t * stride + j0);
+#pragma unroll
+      for (int q = 0; q < (int)sizeof(TI) / 2; ++q) d[q] = o.u[q];
+    }
+  }
+}
+
 template <typename TI, int C>
 __global__ __launch_bounds__(kThreads) void k_solve(const int32_t* table, const float* A,
                                                     TI* Tinv, int H) {
@@ -280,24 +304,63 @@ __global__ __launch_bounds__(kThreads) void k_solve(const int32_t* table, const 
   }
   __syncthreads();
   solve_tril<kWaves, C, TS>(sA, LD, sAd, sM, LD);
-  // rows of T, eight elements per store
-  constexpr int P8 = C / 8, OITER = (C * P8 + kThreads - 1) / kThreads;
+  store_T_rows<TI, C>(sM, LD, Tinv + ((long)start * H + h) * C, (long)H * C, len);
+}
+
+// The backward's stages 3 and 4 in one launch: A is built in LDS (the split of k_solve's
+// staging: the diagonal blocks in fp32, the rest in the solve's type) and inverted there, so
+// only T leaves the chip.  Same products and roundings as k_kkt followed by k_solve.
+template <typename TI, int D, int C>
+__global__ __launch_bounds__(kThreads) void k_kkt_solve(const int32_t* table, const TI* k,
+                                                        const float* g_t, const void* beta_t,
+                                                        int beta_f32, TI* Tinv, int Ttot,
+                                                        int H, int Hg) {
+  const int4 ci = load_chunk(table, blockIdx.x);
+  const int start = ci.y, len = ci.z;
+  if (len == 0) return;
+  const int h = blockIdx.y, hk = h / (H / Hg);
+  typedef typename SolveType<TI>::type TS;
+  constexpr int LDK = D + pad_of<TI>(), LD = C + pad_of<TS>(), NT = C / 16;
+  extern __shared__ __align__(16) char smem[];
+  TS* sA = reinterpret_cast<TS*>(smem);
+  TS* sM = sA + C * LD;
+  float* sAd = reinterpret_cast<float*>(sM + C * LD);
+  TI* sK = reinterpret_cast<TI*>(sAd + NT * 16 * kAdLd);
+  float* sG = reinterpret_cast<float*>(sK + C * LDK);
+  float* sB = sG + C;
+  stage_rows<TI, D, C>(sK, LDK, k + ((long)start * Hg + hk) * D, (long)Hg * D, len);
+  for (int t = threadIdx.x; t < C; t += kThreads) {
+    const long gi = (long)h * Ttot + start + t;
+    sG[t] = t < len ? g_t[gi] : 0.f;
+    sB[t] = t < len ? load_beta(beta_t, beta_f32, gi) : 0.f;
+  }
+  __syncthreads();
+  const int w = wave_id(), l = lane_id();
+  for (int tt = w; tt < NT * NT; tt += kWaves) {
+    const int ti = tt / NT, tj = tt % NT;
+    f32x4 acc = zero4();
+    if (ti >= tj) mma_lds<TI>(acc, sK, LDK, ti * 16, sK, LDK, tj * 16, 0, D);
+    const int j = tj * 16 + (l & 15);
 #pragma unroll
-  for (int it = 0; it < OITER; ++it) {
-    const int i = threadIdx.x + it * kThreads;
-    const int t = i / P8, j0 = (i - t * P8) * 8;
-    if (i < C * P8 && t < len) {
-      union {
-        uint4 u[2];
-        TI e[8];
-      } o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o.e[e] = (TI)(j0 + e <= t ? (float)sM[t * LD + j0 + e] : 0.f);
-      uint4* dst = reinterpret_cast<uint4*>(Tinv + ((long)(start + t) * H + h) * C + j0);
-#pragma unroll
-      for (int q = 0; q < (int)sizeof(TI) / 2; ++q) dst[q] = o.u[q];
+    for (int e = 0; e < 4; ++e) {
+      const int i = ti * 16 + 4 * (l >> 4) + e;
+      const float val = (i < len && i > j) ? sB[i] * __expf(sG[i] - sG[j]) * acc[e] : 0.f;
+      if (ti == tj)
+        sAd[ti * 16 * kAdLd + (i & 15) * kAdLd + (j & 15)] = val;
+      else
+        sA[i * LD + j] = (TS)val;
     }
   }
+  __syncthreads();
+  solve_tril<kWaves, C, TS>(sA, LD, sAd, sM, LD);
+  store_T_rows<TI, C>(sM, LD, Tinv + ((long)start * H + h) * C, (long)H * C, len);
+}
+
+template <typename TI, int D, int C>
+constexpr size_t kkt_solve_smem() {
+  typedef typename SolveType<TI>::type TS;
+  return 2 * C * (C + pad_of<TS>()) * sizeof(TS) + (C / 16) * 16 * kAdLd * 4 +
+         C * (D + pad_of<TI>()) * sizeof(TI) + 2 * C * sizeof(float);
 }
 
 // ------------------------------------------------------------------------- stage 5
@@ -716,7 +779,8 @@ hipError_t set_smem(K kernel, size_t bytes) {
   } while (0)
 
 template <typename TI, int D, int C>
-hipError_t run_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st) {
+hipError_t run_staged(const Problem& p, const Stages& s, int stop_after, bool fuse34,
+                      hipStream_t st) {
   const int MC = p.max_chunks;
   const TI* q = static_cast<const TI*>(p.q);
   const TI* k = static_cast<const TI*>(p.k);
@@ -751,7 +815,18 @@ hipError_t run_staged(const Problem& p, const Stages& s, int stop_after, hipStre
   }
   if (stop_after == 2) return hipSuccess;
 
-  {
+  if (fuse34) {
+    // the backward's shapes only (C = 64, D <= 128)
+    if constexpr (C == 64 && D <= 128) {
+      const size_t sm = kkt_solve_smem<TI, D, C>();
+      GDN_TRY(set_smem(k_kkt_solve<TI, D, C>, sm));
+      k_kkt_solve<TI, D, C><<<dim3(MC, p.H), kThreads, sm, st>>>(
+          s.table, k, s.g_t, s.beta_t, bf, Tinv, p.Ttot, p.H, p.Hg);
+      GDN_TRY(hipGetLastError());
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
     const size_t sm = C * (D + pad_of<TI>()) * sizeof(TI) + 2 * C * sizeof(float);
     GDN_TRY(set_smem(k_kkt<TI, D, C>, sm));
     k_kkt<TI, D, C><<<dim3(MC, p.H), kThreads, sm, st>>>(s.table, k, s.g_t, s.beta_t, bf, s.A,
@@ -760,7 +835,7 @@ hipError_t run_staged(const Problem& p, const Stages& s, int stop_after, hipStre
   }
   if (stop_after == 3) return hipSuccess;
 
-  {
+  if (!fuse34) {
     typedef typename SolveType<TI>::type TS;
     const size_t sm = 2 * C * (C + pad_of<TS>()) * sizeof(TS) + (C / 16) * 16 * kAdLd * 4;
     GDN_TRY(set_smem(k_solve<TI, C>, sm));
@@ -810,25 +885,28 @@ hipError_t run_staged(const Problem& p, const Stages& s, int stop_after, hipStre
 }
 
 template <typename TI, int D>
-hipError_t run_staged_c(const Problem& p, const Stages& s, int stop_after, hipStream_t st) {
-  return p.C == 64 ? run_staged<TI, D, 64>(p, s, stop_after, st)
-                   : run_staged<TI, D, 128>(p, s, stop_after, st);
+hipError_t run_staged_c(const Problem& p, const Stages& s, int stop_after, bool fuse34,
+                        hipStream_t st) {
+  return p.C == 64 ? run_staged<TI, D, 64>(p, s, stop_after, fuse34, st)
+                   : run_staged<TI, D, 128>(p, s, stop_after, fuse34, st);
 }
 
 template <typename TI>
-hipError_t run_staged_d(const Problem& p, const Stages& s, int stop_after, hipStream_t st) {
+hipError_t run_staged_d(const Problem& p, const Stages& s, int stop_after, bool fuse34,
+                        hipStream_t st) {
   switch (p.D) {
-    case 64: return run_staged_c<TI, 64>(p, s, stop_after, st);
-    case 128: return run_staged_c<TI, 128>(p, s, stop_after, st);
-    default: return run_staged_c<TI, 256>(p, s, stop_after, st);
+    case 64: return run_staged_c<TI, 64>(p, s, stop_after, fuse34, st);
+    case 128: return run_staged_c<TI, 128>(p, s, stop_after, fuse34, st);
+    default: return run_staged_c<TI, 256>(p, s, stop_after, fuse34, st);
   }
 }
 
 }  // namespace
 
-hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st) {
-  return p.f32 ? run_staged_d<float>(p, s, stop_after, st)
-               : run_staged_d<bf16>(p, s, stop_after, st);
+hipError_t launch_staged(const Problem& p, const Stages& s, int stop_after, hipStream_t st,
+                         bool fuse_kkt_solve) {
+  return p.f32 ? run_staged_d<float>(p, s, stop_after, fuse_kkt_solve, st)
+               : run_staged_d<bf16>(p, s, stop_after, fuse_kkt_solve, st);
 }
 
 hipError_t launch_chunk_table(const Problem& p, const Stages& s, hipStream_t st) {

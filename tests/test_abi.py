@@ -467,8 +467,9 @@ def test_bwd_workspace_covers_the_staged_stages_and_its_gradient_buffers(lib):
     d = desc(chunk=128)
     st, n = bwd_ws(d)
     assert st == 0
-    staged = gdn.gdn_chunk_fwd_workspace_size(desc(chunk=64, variant=1))
     Ttot, H, D = 512, 4, 128
+    # the staged layout without A (fp32 [Ttot, H, 64]: it stays on chip)
+    staged = gdn.gdn_chunk_fwd_workspace_size(desc(chunk=64, variant=1)) - Ttot * H * 64 * 4
     max_chunks = Ttot // 64 + 2
     tok = Ttot * H * D * 4
     # dDelta and dh' in bf16, the rest fp32
@@ -476,7 +477,8 @@ def test_bwd_workspace_covers_the_staged_stages_and_its_gradient_buffers(lib):
     # without grouped heads no per-value-head buffers
     st, n2 = bwd_ws(desc(Hg=4))
     assert st == 0 and n2 == gdn.gdn_chunk_fwd_workspace_size(
-        desc(Hg=4, chunk=64, variant=1)) + tok // 2 + max_chunks * H * D * D * 2
+        desc(Hg=4, chunk=64, variant=1)) - Ttot * H * 64 * 4 + tok // 2 + \
+        max_chunks * H * D * D * 2
     # supported: bf16 D 64 / 128, fp32 D 64
     assert bwd_ws(desc(Dk=256, Dv=256))[0] == 2
     assert bwd_ws(desc(qkv_dtype=0, Dk=128, Dv=128))[0] == 2
