@@ -350,15 +350,13 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   float* sG = reinterpret_cast<float*>(sDB + L::CC);
   float* sBeta = sG + C;
   // sPart [16 C]: the row dots' parts [quantity x][column wave][C] (x = 0..3); after they
-  // are summed: the last token's shares at 5 C, dGc at 6 C, rowsum(E) per row group of
-  // waves at 8 C, rowsum(dA * KK * Gam) per row group at 12 C (at most four groups each)
+  // are summed: rowsum(E) per row group of waves at 8 C, rowsum(dA * KK * Gam) per row
+  // group at 12 C (at most four groups each)
   float* sPart = sBeta + C;
   float* sRD = sPart + 16 * C;   // [4][C] the row dots (1: Delta.K dh', 2: dR.K h, 3: dR.V);
                                  // its first C floats hold the parts of <dh', h>
   float* sColE = sRD + 4 * C;    // [4 row blocks][C] partial colsum(E)
   float* sHdh = sRD;              // one part per wave (at most C waves)
-  float* sShare = sPart + 5 * C;
-  float* sDgc = sPart + 6 * C;
   float* sRowE = sPart + 8 * C;
   float* sRowB = sPart + 12 * C;
 
@@ -633,10 +631,13 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
         }
       }
 
-  // ---- dbeta and dg (one thread per token; dg is the suffix sum of dGc in the chunk)
-  if (threadIdx.x < C) {
-    const int t = threadIdx.x;
-    float dgc = 0.f, db = 0.f;
+  // ---- dbeta and dg: wave 0, lane t = token t (C = 64 = one wave).  dg is the suffix sum of
+  // dGc in the chunk; the last token's dGc also takes sum_t (gC / gam_t) rowsum(Delta * K
+  // dh')_t + gC <dh', h>.  Butterfly sums and a wave scan: a fixed order (deterministic).
+  static_assert(C == kWave, "one token per lane of wave 0");
+  if (w == 0) {
+    const int t = l;
+    float dgc = 0.f, db = 0.f, share = 0.f;
     if (t < len) {
       const float gam = __expf(sG[t]), r = __expf(gC - sG[t]);
       const float colE = sColE[t] + sColE[C + t] + sColE[2 * C + t] + sColE[3 * C + t];
@@ -649,25 +650,16 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
       }
       db = sRD[3 * C + t] - gam * sRD[2 * C + t] + rowB;
       dgc = scale * gam * rq - r * sRD[C + t] - sBeta[t] * gam * sRD[2 * C + t] + rowE - colE;
-      sShare[t] = r * sRD[C + t];  // the last token's share of h' = gC h + ...
+      share = r * sRD[C + t];  // the last token's share of h' = gC h + ...
+      dbeta[(long)(start + t) * H + h] = db;
     }
-    sDgc[t] = dgc;
-    if (t < len) dbeta[(long)(start + t) * H + h] = db;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    // the last token: + sum_t (gC / gam_t) rowsum(Delta * K dh')_t + gC <dh', h>, then the
-    // suffix sums in token order (fixed order: deterministic)
-    float hdh = 0.f;
-    for (int i = 0; i < chunk_threads<TI, D>() / 64; ++i) hdh += sHdh[i];
-    float s = 0.f;
-    for (int t = 0; t < len; ++t) s += sShare[t];
-    sDgc[len - 1] += s + __expf(gC) * hdh;
-    float acc = 0.f;
-    for (int t = len - 1; t >= 0; --t) {
-      acc += sDgc[t];
-      dg[(long)(start + t) * H + h] = acc;
-    }
+    const float hdh = t < N2 / 64 ? sHdh[t] : 0.f;
+    const float tot = sum4g(sum16(share)) + __expf(gC) * sum4g(sum16(hdh));
+    if (t == len - 1) dgc += tot;
+    // suffix sums: lane u scans token C - 1 - u, then each token takes its own
+    const float sc = wave_incl_scan(__shfl(dgc, C - 1 - t, kWave));
+    const float suf = __shfl(sc, C - 1 - t, kWave);
+    if (t < len) dg[(long)(start + t) * H + h] = suf;
   }
 }
 
