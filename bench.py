@@ -52,9 +52,9 @@ F32_PEAK_TFLOPS = 157.3
 # once they differ.
 PMC_TRAFFIC = {
     "workload": "bf16_16x8192_h32_d128_c128",
-    "fetch_kib": 1671912.73, "write_kib": 1081364.65,
+    "fetch_kib": 1671728.75, "write_kib": 1081375.18,
     "fetch_scale": 2.0, "write_scale": 1.0,
-    "sources_sha256": "1f68e0b6693d4e6122a765de6d3cac961471c9a2b821f2ef5da3f7b6de2acd76",
+    "sources_sha256": "6c5d8b72efa2e4523f2d85f532a2889ccf841e39db9bdf5f06909fb8762c25ff",
 }
 FUSED_SOURCES = ("fused.hip", "gdn_device.h", "gdn_internal.h")
 
