@@ -262,3 +262,25 @@ def test_backward_long_prompt_segments(decay):
     log(test="backward_long_segmented_pair", decay=decay, head=h, **perr)
     for name, e in perr.items():
         assert e <= 1e-2, (name, e)
+
+
+@pytest.mark.parametrize("kv,kd", [(-20, 0), (17, 0), (0, -20), (0, 17), (12, -12)])
+def test_backward_power_of_two_scaling(kv, kd):
+    """The gradients are linear in (do, dht) and, jointly with the forward, homogeneous in
+    (v, h0): scaling v and h0 by 2^kv scales dq, dk, dg and dbeta by 2^kv and leaves dv and dh0
+    alone; scaling do and dht by 2^kd scales every gradient by 2^kd.  Powers of two are exact
+    in binary floating point and every operand of the path is bf16 or fp32 (exponent range
+    of fp32), so the relations hold bit for bit far outside the range of fp16; a step that
+    kept any of these values in fp16 would overflow or flush them."""
+    inp = draw(B=1, T=200, H=4, Hg=2, D=128, seed=53)
+    base = run_bwd(inp)
+    s = dict(inp)
+    s["v"] = (inp["v"].float() * 2.0 ** kv).to(inp["v"].dtype)
+    s["h0"] = inp["h0"] * 2.0 ** kv
+    s["do"] = (inp["do"].float() * 2.0 ** kd).to(inp["do"].dtype)
+    s["dht"] = inp["dht"] * 2.0 ** kd
+    got = run_bwd(s)
+    for name, x, y in zip(NAMES, got, base):
+        f = 2.0 ** kd * (2.0 ** kv if name in ("dq", "dk", "dg", "dbeta") else 1.0)
+        assert torch.isfinite(x).all(), (name, kv, kd)
+        assert torch.equal(x, y * f), (name, kv, kd, rel_l2(to64(x), to64(y) * f))
