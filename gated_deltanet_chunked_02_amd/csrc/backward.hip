@@ -60,6 +60,25 @@ __device__ __forceinline__ int4 chunk_of(const int32_t* table, int c) {
 template <typename TI, int ROWS, int COLS, int NTH>
 using Blk = TileCopy<TI, ROWS, COLS, NTH>;
 
+// A buffer resource over `bytes` bytes from base: a store whose per-lane offset lies past the
+// end is dropped by the hardware (so rows past a chunk's end need no branch), and each
+// store's address is a 32-bit offset into the resource (no per-store 64-bit arithmetic).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+
+// One element of TI at byte offset voff + soff of the resource.
+template <typename TI>
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, float x, int voff,
+                                           int soff) {
+  if constexpr (sizeof(TI) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (TI)x), rs, voff,
+                                          soff, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), rs, voff, soff,
+                                          0);
+}
+
 // Sum over the 16 lanes of a lane group (one accumulator row, its 16 columns).
 __device__ __forceinline__ float sum16(float x) {
   x += __shfl_xor(x, 1);
@@ -255,19 +274,22 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
     // the chunk-end gradient dh' and dR, for the chunk-parallel kernel (not written by the
     // pass that only finds each segment's start gradient)
     if (dH) {
-      const long coff = ((long)c * H + h) * D * D;
+      constexpr int E = sizeof(TI);
+      const auto rh = out_rsrc(dH + ((long)c * H + h) * D * D, D * D * E);
+      const int hv = (4 * (l >> 4) * D + col) * E;
 #pragma unroll
       for (int db = 0; db < NDK; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dH[coff + (long)(16 * db + 4 * (l >> 4) + e) * D + col] = (TI)dh[db][e];
+        for (int e = 0; e < 4; ++e) store_elem<TI>(rh, dh[db][e], hv, (16 * db + e) * D * E);
+      // dR: the resource holds rows t < len; a store to a later row is dropped (its whole
+      // offset is in the per-lane part, which the bounds check covers)
+      const auto rr = out_rsrc(dRo + v0, (uint32_t)len * H * D * E);
+      const int rstep = H * D * E;
 #pragma unroll
       for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * tb + 4 * (l >> 4) + e;
-          if (t < len) dRo[v0 + (long)t * H * D + col] = (TI)dr[tb][e];
-        }
+        for (int e = 0; e < 4; ++e)
+          store_elem<TI>(rr, dr[tb][e], (16 * tb + 4 * (l >> 4) + e) * rstep + col * E, 0);
     }
     // dh = gC dh' + scale Q^T diag(gam) dO - K^T diag(beta gam) dR
     f32x4 go[NT], nd[NT];
