@@ -155,10 +155,18 @@ __device__ __forceinline__ void mma_lds_Bn(f32x4& acc, const TI* A, int lda, int
 // so Q, K and T are read and P is built once per chunk.  Every tile sits in LDS in its
 // natural layout (Q, K, dO [C][LDD]; T, P^T [C][LDC]); the transposed operands Q^T, K^T, T^T
 // and dO^T are read from them directly.  About 69 KB at D = 128 in bf16.
+// The tiles and gates of a chunk are double-buffered (one set per chunk parity), so storing
+// the next chunk's needs no barrier of its own; P^T is single.
+template <typename TI, int D>
+constexpr size_t dh_buf_bytes() {
+  constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>();
+  return (3 * kBC * LDD + kBC * LDC) * sizeof(TI) + 2 * kBC * sizeof(float);
+}
+
 template <typename TI, int D>
 constexpr size_t dh_smem() {
-  constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>();
-  return (3 * kBC * LDD + 2 * kBC * LDC) * sizeof(TI) + 2 * kBC * sizeof(float);
+  constexpr int LDC = kBC + pad_of<TI>();
+  return 2 * dh_buf_bytes<TI, D>() + kBC * LDC * sizeof(TI);
 }
 
 template <typename TI, int D>
@@ -180,13 +188,7 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
   const int w = wave_id(), l = lane_id();
   const int col = 16 * w + (l & 15);  // this lane's state column
   extern __shared__ __align__(16) char smem[];
-  TI* sQ = reinterpret_cast<TI*>(smem);  // [C][LDD]
-  TI* sK = sQ + C * LDD;                 // [C][LDD]
-  TI* sO = sK + C * LDD;                 // [C][LDD]  dO
-  TI* sT = sO + C * LDD;                 // [C][LDC]  rows of T
-  TI* sPt = sT + C * LDC;                // [C][LDC]  P^T
-  float* sG = reinterpret_cast<float*>(sPt + C * LDC);
-  float* sBeta = sG + C;
+  TI* sPt = reinterpret_cast<TI*>(smem + 2 * dh_buf_bytes<TI, D>());  // [C][LDC]  P^T
 
   // dh tile db: rows (key index) 16 db + 4 (l/16) + e, column col
   f32x4 dh[NDK];
@@ -222,7 +224,15 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
     const int4 ci = chunk_of(table, c);
     const int start = ci.y, len = ci.z;
     const long v0 = ((long)start * H + h) * D;
-    __syncthreads();  // the previous chunk is done with the LDS tiles
+    // this chunk's buffer set: the other set was read by the previous chunk, and the chunk
+    // before that, which read this one, finished before the previous chunk's first barrier
+    char* sb = smem + ((c1 - 1 - c) & 1) * dh_buf_bytes<TI, D>();
+    TI* sQ = reinterpret_cast<TI*>(sb);  // [C][LDD]
+    TI* sK = sQ + C * LDD;               // [C][LDD]
+    TI* sO = sK + C * LDD;               // [C][LDD]  dO
+    TI* sT = sO + C * LDD;               // [C][LDC]  rows of T
+    float* sG = reinterpret_cast<float*>(sT + C * LDC);
+    float* sBeta = sG + C;
     bq.store_nat(sQ, LDD);
     bk.store_nat(sK, LDD);
     bt.store_nat(sT, LDC);
