@@ -52,9 +52,9 @@ F32_PEAK_TFLOPS = 157.3
 # once they differ.
 PMC_TRAFFIC = {
     "workload": "bf16_16x8192_h32_d128_c128",
-    "fetch_kib": 1671728.75, "write_kib": 1081375.18,
+    "fetch_kib": 1671612.15, "write_kib": 1081381.53,
     "fetch_scale": 2.0, "write_scale": 1.0,
-    "sources_sha256": "6c5d8b72efa2e4523f2d85f532a2889ccf841e39db9bdf5f06909fb8762c25ff",
+    "sources_sha256": "8036437170e787a9b8b92198e0c0e8aba3efcd0cd35e4c0b40dd575462a0676f",
 }
 FUSED_SOURCES = ("fused.hip", "gdn_device.h", "gdn_internal.h")
 
@@ -398,7 +398,7 @@ def bwd_bench(args, dev, gdn, w, inp):
                                        "the reverse segment scan, k_bwd_dh",
                           "fused": "staged stages 0-4, k_fused store mode, k_bwd_dh",
                           "staged": "staged stages 0-6, k_bwd_dh"}[how],
-                         ", k_bwd_group_sum" if w.H != w.Hg else ""),
+                         " over each q/k head's value heads" if w.H != w.Hg else ""),
                      "launch_ms": avg_ms, "algorithmic_bytes": by},
         "cpu_baseline": cpu,
     }

@@ -269,13 +269,12 @@ size_t workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
 // layout at the front of its workspace, without A (stages 0-2, then T by one launch that
 // keeps A on chip, then the chunk-start states and v_new from the fused kernel's store mode
 // in bf16, or from stages 5-6 in fp32), then keeps dR
-// [Ttot, H, D] and each chunk's end-state gradient [max_chunks, H, D, D] in the q/k/v dtype
-// and (H != Hg) per-value-head dq and dk [Ttot, H, D] in fp32.
+// [Ttot, H, D] and each chunk's end-state gradient [max_chunks, H, D, D] in the q/k/v dtype.
 constexpr int kBwdChunk = 64;
 
 struct BwdLayout {
   Layout st;
-  size_t dR, dH, dqh, dkh, total;
+  size_t dR, dH, total;
 };
 
 // Shape part of a backward call: the forward's checks with the chunk set to 64 and N as the
@@ -307,14 +306,9 @@ BwdLayout bwd_layout(const gdn::Problem& p) {
   }
   L.st.total = off;
   const size_t e = p.f32 ? 4 : 2;
-  const size_t tok = (size_t)p.Ttot * p.H * p.D * sizeof(float);
   L.dR = L.st.total;
   L.dH = L.dR + align_up((size_t)p.Ttot * p.H * p.D * e);
-  const size_t hb = (size_t)p.max_chunks * p.H * p.D * p.D * e;
-  L.dqh = L.dH + align_up(hb);
-  const bool grouped = p.H != p.Hg;
-  L.dkh = L.dqh + (grouped ? align_up(tok) : 0);
-  L.total = L.dkh + (grouped ? align_up(tok) : 0);
+  L.total = L.dH + align_up((size_t)p.max_chunks * p.H * p.D * p.D * e);
   return L;
 }
 
@@ -670,8 +664,6 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
   b.dh0 = dh0;
   b.dR = ws + L.dR;
   b.dH = ws + L.dH;
-  b.dqh = p.H != p.Hg ? reinterpret_cast<float*>(ws + L.dqh) : nullptr;
-  b.dkh = p.H != p.Hg ? reinterpret_cast<float*>(ws + L.dkh) : nullptr;
   hipError_t e;
   if (sp.use) {
     // stages 0-4, then the segmented forward's maps (b, M) and each segment's true start

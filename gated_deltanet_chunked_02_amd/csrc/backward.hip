@@ -31,8 +31,9 @@
 //                the segments, then from each segment's true end gradient);
 //   k_bwd_chunk  one workgroup per (chunk, head): everything else, in phases that stage their
 //                operands in LDS (each product C = A B^T with both operands k-contiguous).
-// Value heads that share a q/k head write their dq and dk to a per-head buffer that a last
-// kernel sums (no float atomics: the results do not depend on scheduling).
+// Value heads that share a q/k head run in one workgroup of the chunk kernel, which sums
+// their dq and dk in registers in head order (no float atomics: the results do not depend
+// on scheduling).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_operands.h"
@@ -346,7 +347,7 @@ struct ChunkLds {
   static constexpr size_t bytes = (5 * P + BIG + 2 * CC) * sizeof(TI) + 26 * C * sizeof(float);
 };
 
-template <typename TI, int D>
+template <typename TI, int D, bool GRP>
 __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
     const int32_t* __restrict__ table, const TI* __restrict__ q, const TI* __restrict__ k,
     const TI* __restrict__ v, const void* __restrict__ beta, int beta_f32,
@@ -354,19 +355,22 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
     const TI* __restrict__ v_new, const TI* __restrict__ dR, const TI* __restrict__ dH,
     const TI* __restrict__ dO, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta, int qk_rows,
-    int Ttot, int H, int Hg, float scale) {
+    int gsz, int Ttot, int H, int Hg, float scale) {
   typedef ChunkLds<TI, D> L;
   typedef Mma<TI> MM;
   constexpr int C = kBC, CBW = D / 64, N2 = chunk_threads<TI, D>();  // CBW: column blocks
                                                                       // per wave
   constexpr int RW = N2 / 256, RPW = 4 / RW;  // row groups of waves; row blocks per wave
   constexpr int LDD = L::LDD, LDC = L::LDC;
-  const int c = blockIdx.x, h = blockIdx.y;
+  // GRP = false: blockIdx.y is a value head; GRP: blockIdx.y is a q/k head, whose gsz value
+  // heads run one after another on the resident K and Q, their dq and dk summed in registers
+  // (in head order: deterministic)
+  const int c = blockIdx.x;
   const int4 ci = chunk_of(table, c);
   const int start = ci.y, len = ci.z;
   if (len == 0) return;
-  const int hk = h / (H / Hg);
-  const int hq = qk_rows == H ? h : hk;  // the q/k row of dq and dk this head writes
+  const int hk = GRP ? (int)blockIdx.y : (int)blockIdx.y / (H / Hg);
+  const int hq = GRP ? hk : (qk_rows == H ? (int)blockIdx.y : hk);  // dq, dk row
   const int w = wave_id(), l = lane_id(), lg = l >> 4, lc = l & 15;
   const int cw = w & 3, rh = w >> 2;
   extern __shared__ __align__(16) char smem[];
@@ -392,27 +396,57 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   float* sRowE = sPart + 8 * C;
   float* sRowB = sPart + 12 * C;
 
-  const long qk0 = ((long)start * Hg + hk) * D, v0 = ((long)start * H + h) * D;
+  const long qk0 = ((long)start * Hg + hk) * D;
+  f32x4 aq[RPW][CBW], ak[RPW][CBW];  // dq and dk, summed over the value heads
+#pragma unroll
+  for (int b = 0; b < RPW; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m) aq[b][m] = ak[b][m] = zero4();
+  if constexpr (GRP) {
+    // K and Q once per workgroup (nothing reads them before the first barrier below)
+    Blk<TI, C, D, N2> bk, bq;
+    bk.load(k + qk0, (long)Hg * D, len);
+    bq.load(q + qk0, (long)Hg * D, len);
+    bk.store_nat(sK, LDD);
+    bq.store_nat(sQ, LDD);
+  }
+  const int nr = GRP ? gsz : 1;  // value heads of this workgroup (a loop only when grouped)
+#pragma unroll 1
+  for (int r = 0; r < nr; ++r) {
+  // grouped: lane and wave indices re-derived per head, so that the fragment addresses built
+  // from them are not hoisted out of the loop and kept live across it
+  int tid = threadIdx.x;
+  if constexpr (GRP) opaque(tid);
+  const int w = tid >> 6, l = tid & 63, lg = l >> 4, lc = l & 15;
+  const int cw = w & 3, rh = w >> 2;
+  const int h = GRP ? hk * gsz + r : (int)blockIdx.y;
+  const long v0 = ((long)start * H + h) * D;
   const long hcoff = ((long)c * H + h) * D * D;
+  if (r > 0) __syncthreads();  // the previous value head is done with the LDS
   if (threadIdx.x < C) {
     const int t = threadIdx.x;
     sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
     sBeta[t] = t < len ? load_beta(beta, beta_f32, (long)(start + t) * H + h) : 0.f;
   }
-  // every operand tile, loaded together (each thread holds its share in registers)
-  Blk<TI, C, D, N2> bdr, bk, bq, bdl, bv, bo;
+  // every operand tile of the head, loaded together (each thread holds its share in
+  // registers)
+  Blk<TI, C, D, N2> bdr, bdl, bv, bo, bk, bq;
   Blk<TI, D, D, N2> bh, bd;
   bdr.load(dR + v0, (long)H * D, len);
-  bk.load(k + qk0, (long)Hg * D, len);
-  bq.load(q + qk0, (long)Hg * D, len);
+  if constexpr (!GRP) {
+    bk.load(k + qk0, (long)Hg * D, len);
+    bq.load(q + qk0, (long)Hg * D, len);
+  }
   bdl.load(v_new + v0, (long)H * D, len);
   bv.load(v + v0, (long)H * D, len);
   bo.load(dO + v0, (long)H * D, len);
   bh.load(h_c + hcoff, D, D);
   __syncthreads();  // Gc and beta
   bdr.store_nat(sC, LDD);
-  bk.store_nat(sK, LDD);
-  bq.store_nat(sQ, LDD);
+  if constexpr (!GRP) {
+    bk.store_nat(sK, LDD);
+    bq.store_nat(sQ, LDD);
+  }
   bdl.store_nat(sDl, LDD);
   bv.store_nat(sV, LDD);
   bo.store_nat(sO, LDD);
@@ -449,14 +483,14 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
     return [=](int j, int kk) { return frag_tr<TI>(Pm, ld, 16 * (cw + 4 * j), kk); };
   };
 
-  // ---- phase B, h resident: K h, dO h^T (into aq), dR h^T (into ak), row dots
-  f32x4 aq[RPW][CBW], ak[RPW][CBW];
+  // ---- phase B, h resident: K h, dO h^T (into aq), dR h^T (into ak), row dots.  aq and ak
+  // carry dq and dk summed over the value heads of the workgroup
   {
-    f32x4 Kh[RPW][CBW];
+    f32x4 Kh[RPW][CBW], tq[RPW][CBW], tk[RPW][CBW];
 #pragma unroll
     for (int b = 0; b < RPW; ++b)
 #pragma unroll
-      for (int m = 0; m < CBW; ++m) Kh[b][m] = aq[b][m] = ak[b][m] = zero4();
+      for (int m = 0; m < CBW; ++m) Kh[b][m] = tq[b][m] = tk[b][m] = zero4();
     mma_steps<TI, D, RPW, CBW>(rows(sK, LDD), colsT(sBig, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
       for (int b = 0; b < RPW; ++b)
@@ -472,8 +506,8 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
           for (int b = 0; b < RPW; ++b)
 #pragma unroll
             for (int m = 0; m < CBW; ++m) {
-              aq[b][m] = MM::mma(fa[b], fb[m], aq[b][m]);
-              ak[b][m] = MM::mma(fa[RPW + b], fb[m], ak[b][m]);
+              tq[b][m] = MM::mma(fa[b], fb[m], tq[b][m]);
+              tk[b][m] = MM::mma(fa[RPW + b], fb[m], tk[b][m]);
             }
         });
     // row dots over the wave's columns: dR.K h, dR.V, Q.(dO h^T) = dO.Q h
@@ -489,7 +523,7 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
           const float r = (float)sC[gi];
           p2 += r * Kh[b][m][e];
           p3 += r * (float)sV[gi];
-          p0 += (float)sQ[gi] * aq[b][m][e];
+          p0 += (float)sQ[gi] * tq[b][m][e];
         }
         p0 = sum16(p0);
         p2 = sum16(p2);
@@ -502,8 +536,8 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
         const float gam = __expf(sG[t]);
 #pragma unroll
         for (int m = 0; m < CBW; ++m) {
-          aq[b][m][e] *= scale * gam;
-          ak[b][m][e] *= -sBeta[t] * gam;
+          aq[b][m][e] += scale * gam * tq[b][m][e];
+          ak[b][m][e] -= sBeta[t] * gam * tk[b][m][e];
         }
       }
   }
@@ -648,20 +682,6 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
 #pragma unroll
           for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
       });
-  const long dq0 = ((long)start * qk_rows + hq) * D;
-#pragma unroll
-  for (int b = 0; b < RPW; ++b)
-#pragma unroll
-    for (int m = 0; m < CBW; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * (RPW * rh + b) + 4 * lg + e;
-        if (t < len) {
-          const long gi = dq0 + (long)t * qk_rows * D + 16 * (cw + 4 * m) + lc;
-          dq[gi] = aq[b][m][e];
-          dk[gi] = ak[b][m][e];
-        }
-      }
 
   // ---- dbeta and dg: wave 0, lane t = token t (C = 64 = one wave).  dg is the suffix sum of
   // dGc in the chunk; the last token's dGc also takes sum_t (gC / gam_t) rowsum(Delta * K
@@ -693,27 +713,21 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
     const float suf = __shfl(sc, C - 1 - t, kWave);
     if (t < len) dg[(long)(start + t) * H + h] = suf;
   }
-}
-
-// dq[t][hk] = sum of the value heads' dq[t][hk G .. hk G + G - 1] (and dk the same).
-__global__ __launch_bounds__(256) void k_bwd_group_sum(const float* __restrict__ dqh,
-                                                       const float* __restrict__ dkh,
-                                                       float* __restrict__ dq,
-                                                       float* __restrict__ dk, long rows,
-                                                       int Hg, int G, int D) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // over rows * Hg * D
-  const long total = rows * Hg * D;
-  if (i >= total) return;
-  const long t = i / ((long)Hg * D);
-  const int rem = (int)(i - t * Hg * D), hk = rem / D, d = rem - hk * D;
-  float sq = 0.f, sk = 0.f;
-  for (int r = 0; r < G; ++r) {
-    const long j = (t * Hg * G + (long)hk * G + r) * D + d;
-    sq += dqh[j];
-    sk += dkh[j];
   }
-  dq[i] = sq;
-  dk[i] = sk;
+  const long dq0 = ((long)start * qk_rows + hq) * D;
+#pragma unroll
+  for (int b = 0; b < RPW; ++b)
+#pragma unroll
+    for (int m = 0; m < CBW; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * (RPW * rh + b) + 4 * lg + e;
+        if (t < len) {
+          const long gi = dq0 + (long)t * qk_rows * D + 16 * (cw + 4 * m) + lc;
+          dq[gi] = aq[b][m][e];
+          dk[gi] = ak[b][m][e];
+        }
+      }
 }
 
 template <typename F>
@@ -749,23 +763,19 @@ hipError_t run_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st) 
   const TI* k = static_cast<const TI*>(p.k);
   const TI* v = static_cast<const TI*>(p.v);
   const TI* dO = static_cast<const TI*>(b.dO);
-  const bool grouped = p.H != p.Hg;
+  // grouped heads: one workgroup per (chunk, q/k head) runs the group's value heads
+  const int gsz = p.H / p.Hg;
   const size_t sm2 = ChunkLds<TI, D>::bytes;
-  GDN_BTRY(set_lds(k_bwd_chunk<TI, D>, sm2));
-  k_bwd_chunk<TI, D><<<dim3(p.max_chunks, p.H), chunk_threads<TI, D>(), sm2, st>>>(
-      b.st.table, q, k, v, p.beta, p.beta_f32 ? 1 : 0, b.st.g_t,
-      static_cast<const TI*>(b.st.h_c),
-      static_cast<const TI*>(b.st.v_new), static_cast<const TI*>(b.dR),
-      static_cast<const TI*>(b.dH), dO, grouped ? b.dqh : b.dq,
-      grouped ? b.dkh : b.dk, b.dv, b.dg, b.dbeta, grouped ? p.H : p.Hg, p.Ttot, p.H, p.Hg,
-      p.scale);
-  GDN_BTRY(hipGetLastError());
-  if (grouped) {
-    const long total = (long)p.Ttot * p.Hg * D;
-    k_bwd_group_sum<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
-        b.dqh, b.dkh, b.dq, b.dk, p.Ttot, p.Hg, p.H / p.Hg, D);
-    GDN_BTRY(hipGetLastError());
-  }
+  auto launch = [&](auto kern) -> hipError_t {
+    GDN_BTRY(set_lds(kern, sm2));
+    kern<<<dim3(p.max_chunks, p.Hg), chunk_threads<TI, D>(), sm2, st>>>(
+        b.st.table, q, k, v, p.beta, p.beta_f32 ? 1 : 0, b.st.g_t,
+        static_cast<const TI*>(b.st.h_c), static_cast<const TI*>(b.st.v_new),
+        static_cast<const TI*>(b.dR), static_cast<const TI*>(b.dH), dO, b.dq, b.dk, b.dv,
+        b.dg, b.dbeta, p.Hg, gsz, p.Ttot, p.H, p.Hg, p.scale);
+    return hipGetLastError();
+  };
+  GDN_BTRY(gsz > 1 ? launch(k_bwd_chunk<TI, D, true>) : launch(k_bwd_chunk<TI, D, false>));
   return hipSuccess;
 }
 

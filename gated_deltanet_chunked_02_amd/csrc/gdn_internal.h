@@ -70,8 +70,7 @@ hipError_t launch_chunk_table(const Problem& p, const Stages& s, hipStream_t st)
 // start state h_c and v_new; the staged layout) plus the gradient buffers.  dq, dk:
 // [Ttot, Hg, D]; dv: [Ttot, H, D]; dg, dbeta: [Ttot, H]; dh0: [N, H, D, D] or NULL; all
 // fp32.  dR [Ttot, H, D] and dH [max_chunks, H, D, D] (the gradient of each chunk's end
-// state), in the q/k/v dtype, are workspace; dqh, dkh [Ttot, H, D] fp32 too when H != Hg
-// (per value head, summed over the group afterwards).
+// state), in the q/k/v dtype, are workspace.
 struct BwdBuffers {
   Stages st;
   const void* dO;
@@ -84,8 +83,6 @@ struct BwdBuffers {
   float* dh0;
   void* dR;
   void* dH;
-  float* dqh;
-  float* dkh;
 };
 bool bwd_supported(const Problem& p);
 // Both backward kernels over the sequences (b.dht, b.dH, b.dR, b.dh0 as above).
@@ -97,7 +94,7 @@ hipError_t launch_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st);
 hipError_t launch_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
                          const int32_t* run_chunks, const float* dht, void* dH, void* dR,
                          float* dh0, hipStream_t st);
-// The chunk-parallel kernel (and the group sum when H != Hg).
+// The chunk-parallel kernel (with grouped heads, one workgroup runs a group's value heads).
 hipError_t launch_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st);
 bool fused_supported(const Problem& p);
 hipError_t launch_fused(const Problem& p, hipStream_t st);
