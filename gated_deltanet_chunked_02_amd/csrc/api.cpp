@@ -297,8 +297,10 @@ gdn_status bwd_problem(const gdn_desc* d, bool packed, gdn::Problem* p) {
 BwdLayout bwd_layout(const gdn::Problem& p) {
   BwdLayout L;
   staged_layout(p, &L.st);
-  // A stays on chip (stages 3 and 4 run as one launch): no room for it
+  // A stays on chip (stages 3 and 4 run as one launch), and with the fused recompute (bf16)
+  // W and U are never formed: no room for them
   L.st.bytes[GDN_BUF_A] = 0;
+  if (gdn::fused_supported(p)) L.st.bytes[GDN_BUF_W] = L.st.bytes[GDN_BUF_U] = 0;
   size_t off = 0;
   for (int i = 0; i < GDN_BUF_COUNT; ++i) {
     L.st.off[i] = off;

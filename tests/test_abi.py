@@ -462,16 +462,18 @@ def bwd_ws(d):
 
 def test_bwd_workspace_covers_the_staged_stages_and_its_gradient_buffers(lib):
     # bf16 D = 128, dense B = 2, T = 256, H = 4, Hg = 2: the staged layout at C = 64 without
-    # A, then dR [Ttot, H, D] and the chunk-end state gradients [max_chunks, H, D, D] in bf16
-    # (grouped heads need nothing more: one workgroup sums a group's dq and dk)
+    # A, W and U, then dR [Ttot, H, D] and the chunk-end state gradients [max_chunks, H, D, D]
+    # in bf16 (grouped heads need nothing more: one workgroup sums a group's dq and dk)
     d = desc(chunk=128)
     st, n = bwd_ws(d)
     assert st == 0
     Ttot, H, D = 512, 4, 128
-    # the staged layout without A (fp32 [Ttot, H, 64]: it stays on chip)
-    staged = gdn.gdn_chunk_fwd_workspace_size(desc(chunk=64, variant=1)) - Ttot * H * 64 * 4
-    max_chunks = Ttot // 64 + 2
     tok = Ttot * H * D * 4
+    # the staged layout without A (fp32 [Ttot, H, 64]: it stays on chip) and without W and U
+    # (bf16 [Ttot, H, D] each: the fused recompute never forms them)
+    staged = (gdn.gdn_chunk_fwd_workspace_size(desc(chunk=64, variant=1)) - Ttot * H * 64 * 4
+              - 2 * (tok // 2))
+    max_chunks = Ttot // 64 + 2
     # dR and dh' in bf16
     assert n == staged + tok // 2 + max_chunks * H * D * D * 2
     # the same without grouped heads
@@ -480,7 +482,13 @@ def test_bwd_workspace_covers_the_staged_stages_and_its_gradient_buffers(lib):
     # supported: bf16 D 64 / 128, fp32 D 64
     assert bwd_ws(desc(Dk=256, Dv=256))[0] == 2
     assert bwd_ws(desc(qkv_dtype=0, Dk=128, Dv=128))[0] == 2
-    assert bwd_ws(desc(qkv_dtype=0, Dk=64, Dv=64))[0] == 0
+    # fp32 recomputes through the staged stages, so its workspace keeps W and U
+    st, n32 = bwd_ws(desc(qkv_dtype=0, Dk=64, Dv=64, beta_dtype=0))
+    tok32 = Ttot * H * 64 * 4
+    staged32 = (gdn.gdn_chunk_fwd_workspace_size(desc(qkv_dtype=0, Dk=64, Dv=64, beta_dtype=0,
+                                                      chunk=64, variant=1))
+                - Ttot * H * 64 * 4)
+    assert st == 0 and n32 == staged32 + tok32 + max_chunks * H * 64 * 64 * 4
     assert bwd_ws(desc(Dk=64, Dv=64))[0] == 0
     # the chunk and stop_after fields do not change it, nor a variant other than SEGMENTED
     # where AUTO keeps one pass per sequence
