@@ -22,15 +22,16 @@
 //            and at the last token also sum_t (gC / gam_t) rowsum(Delta * K dh')_t
 //            + gC <dh', h>;  dg = the in-chunk suffix sum of dGc.
 //
-// Two kernels follow the staged forward's recomputation (chunk table, Gc, T, W, the chunk-start
-// states and v_new in the workspace):
+// Two kernels follow the recomputation of the forward's chunk quantities (chunk table, Gc,
+// T, the chunk-start states and v_new in the workspace):
 //   k_bwd_dh     one workgroup per (sequence, head), a wave per 16 state columns: the chunks
 //                in reverse, dh kept in accumulator tiles; writes dh' of every chunk, dR,
 //                and dh0.  Long sequences run it per segment (twice: once from a zero end
 //                gradient for each segment's own share, composed in reverse order across
 //                the segments, then from each segment's true end gradient);
-//   k_bwd_chunk  one workgroup per (chunk, head): everything else, in phases that stage their
-//                operands in LDS (each product C = A B^T with both operands k-contiguous).
+//   k_bwd_chunk  one resident workgroup per CU walking the (chunk, head) items: everything
+//                else, in phases that stage their operands in LDS, with the next item's tiles
+//                copied in while the current item's last products run.
 // Value heads that share a q/k head run in one workgroup of the chunk kernel, which sums
 // their dq and dk in registers in head order (no float atomics: the results do not depend
 // on scheduling).
@@ -329,13 +330,80 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
 }
 
 // ------------------------------------------------------------------------- chunk gradients
-// One workgroup of 4 RW waves per (chunk, head) (RW = 2 or 4 row groups, RPW = 4 / RW).
+// One 16-byte copy per lane from global memory straight into LDS: lane l's 16 bytes land at
+// lds + 16 l (lds is the same for the whole wave; M0 carries it, and the wait state the
+// hardware needs between an M0 write and the copy that reads it is in the statement).  It is
+// inline assembly because the compiler, when it issues such a copy itself, waits for it to
+// land before every transposing LDS read that follows (it cannot tell those reads apart from
+// the copy's target), which would serialise the copies with the products they are meant to
+// overlap.  The compiler therefore does not know of the copy: the caller waits for it
+// (wait_loads) before the barrier that publishes the tile, and touches nothing of the tile
+// before then.
+__device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
+  const unsigned a = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(a) : "memory");
+}
+
+// Wave w's share (NW waves) of a direct HBM -> LDS copy of a ROWS x COLS tile of TI into the
+// padded natural layout [ROWS][COLS + pad_of<TI>()]: rows of PR 16-byte pieces and one pad
+// piece.  Each copy instruction writes 64 consecutive 16-byte LDS pieces, lane l the l-th, so
+// piece p of the tile is row p / (PR + 1), piece p % (PR + 1); the pad piece re-reads its
+// row's first piece.  Rows past len re-read row len - 1 (in bounds; every product masks those
+// rows).  No registers hold the data: the copy lands in LDS on its own, and a wait for the
+// wave's memory counter, then a barrier, make it visible to the workgroup.
+template <typename TI, int ROWS, int COLS, int NW>
+__device__ __forceinline__ void dma_tile(TI* dst, const TI* src, long stride, int len, int w,
+                                         int l) {
+  constexpr int VE = 16 / (int)sizeof(TI), PR = COLS / VE, PP = PR + 1;
+  static_assert(COLS + pad_of<TI>() == PP * VE, "one pad piece per row");
+  static_assert((ROWS * PP) % kWave == 0, "whole copy instructions");
+  constexpr int NI = ROWS * PP / kWave;
+#pragma unroll
+  for (int j0 = 0; j0 < NI; j0 += NW) {
+    const int j = j0 + w;
+    if (j < NI) {
+      const int p = kWave * j + l, r = p / PP, c = p % PP;
+      lds_copy16(src + (long)min(r, len - 1) * stride + (c < PR ? c : 0) * VE,
+                 dst + kWave * VE * j);
+    }
+  }
+}
+
+// A TileCopy whose load takes the thread index as an argument: a loop that passes an index the
+// compiler cannot see through recomputes the lane's addresses per call instead of holding
+// them in registers across the loop.
+template <typename TI, int ROWS, int COLS, int NTH>
+struct TileRegs : TileCopy<TI, ROWS, COLS, NTH> {
+  typedef TileCopy<TI, ROWS, COLS, NTH> B;
+  __device__ __forceinline__ void load_at(const TI* src, long stride, int len_, int tid) {
+    const int lo = tid & 63, hi = tid >> 6;
+    const int bc = (lo & 7) + 8 * (hi % (B::BC / 8)), br = (lo >> 3) + 8 * (hi / (B::BC / 8));
+    this->r0 = B::RB * br;
+    this->c0 = B::V * bc;
+    this->len = len_;
+#pragma unroll
+    for (int a = 0; a < B::RB; ++a)
+      this->in[a].u = *reinterpret_cast<const uint4*>(
+          src + (long)min(this->r0 + a, len_ - 1) * stride + this->c0);
+  }
+};
+
+// Wait until this wave's loads (copies into LDS included) have landed.
+__device__ __forceinline__ void wait_loads() {
+  // s_waitcnt with vmcnt = 0 and expcnt, lgkmcnt at their maxima (no wait on those)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// One workgroup of 4 RW waves per resident slot; it walks the (chunk, head) items b, b + G,
+// b + 2 G, ... (G workgroups, items with tokens only; RW = 2 or 4 row groups, RPW = 4 / RW).
 // Wave w = 4 rh + cw: in the C x D products it owns the row blocks RPW rh .. RPW rh + RPW - 1
 // and the column blocks cw + 4 m (m < D / 64); in the C x C products the row block cw and
-// the column blocks RPW rh .. RPW rh + RPW - 1.  Every tile sits in
-// LDS in its natural layout and the transposed operands are read from it (frag_tr), so h
-// and dh' are each loaded once and every product that needs them runs while they are
-// resident.
+// the column blocks RPW rh .. RPW rh + RPW - 1.  Every tile sits in LDS in its natural
+// layout and the transposed operands are read from it (frag_tr), so h and dh' are each
+// loaded once and every product that needs them runs while they are resident.  While one
+// item's last products run, the next item's h, dR, dO and Delta are copied into the LDS
+// tiles those products no longer read, and its K, Q and V load into registers.
 template <typename TI, int D>
 struct ChunkLds {
   static constexpr int C = kBC;
@@ -349,9 +417,9 @@ struct ChunkLds {
 
 template <typename TI, int D, bool GRP>
 __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
-    const int32_t* __restrict__ table, const TI* __restrict__ q, const TI* __restrict__ k,
-    const TI* __restrict__ v, const void* __restrict__ beta, int beta_f32,
-    const float* __restrict__ g_t, const TI* __restrict__ h_c,
+    const int32_t* __restrict__ table, int n_chunks, const TI* __restrict__ q,
+    const TI* __restrict__ k, const TI* __restrict__ v, const void* __restrict__ beta,
+    int beta_f32, const float* __restrict__ g_t, const TI* __restrict__ h_c,
     const TI* __restrict__ v_new, const TI* __restrict__ dR, const TI* __restrict__ dH,
     const TI* __restrict__ dO, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta, int qk_rows,
@@ -360,19 +428,16 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   typedef Mma<TI> MM;
   constexpr int C = kBC, CBW = D / 64, N2 = chunk_threads<TI, D>();  // CBW: column blocks
                                                                       // per wave
+  constexpr int NW = N2 / kWave;
   constexpr int RW = N2 / 256, RPW = 4 / RW;  // row groups of waves; row blocks per wave
   constexpr int LDD = L::LDD, LDC = L::LDC;
-  // GRP = false: blockIdx.y is a value head; GRP: blockIdx.y is a q/k head, whose gsz value
-  // heads run one after another on the resident K and Q, their dq and dk summed in registers
-  // (in head order: deterministic)
-  const int c = blockIdx.x;
-  const int4 ci = chunk_of(table, c);
-  const int start = ci.y, len = ci.z;
-  if (len == 0) return;
-  const int hk = GRP ? (int)blockIdx.y : (int)blockIdx.y / (H / Hg);
-  const int hq = GRP ? hk : (qk_rows == H ? (int)blockIdx.y : hk);  // dq, dk row
-  const int w = wave_id(), l = lane_id(), lg = l >> 4, lc = l & 15;
-  const int cw = w & 3, rh = w >> 2;
+  constexpr int VE = 16 / (int)sizeof(TI), PR = D / VE;  // 16-byte pieces of a D row
+  // GRP = false: an item is (chunk, value head); GRP: (chunk, q/k head), whose gsz value heads
+  // run one after another on the resident K and Q, their dq and dk summed in registers (in
+  // head order: deterministic)
+  const int Hy = GRP ? Hg : H;
+  const int n_items = n_chunks * Hy;
+  const int nr = GRP ? gsz : 1;
   extern __shared__ __align__(16) char smem[];
   TI* sK = reinterpret_cast<TI*>(smem);
   TI* sQ = sK + L::P;
@@ -396,72 +461,103 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   float* sRowE = sPart + 8 * C;
   float* sRowB = sPart + 12 * C;
 
-  const long qk0 = ((long)start * Hg + hk) * D;
+  // the next item at or after i (stride: the grid) that has tokens; n_items if none
+  auto next_item = [&](int i) {
+    while (i < n_items && chunk_of(table, i / Hy).z == 0) i += (int)gridDim.x;
+    return i < n_items ? i : n_items;
+  };
+  // the value head of unit r of item i, and the offsets of its token rows and h_c / dh'
+  auto value_head = [&](int i, int r) { return GRP ? (i % Hy) * gsz + r : i % Hy; };
+  // copies of a unit's h (part 0) or its dR, dO and Delta (part 1) into LDS (the tiles must be
+  // free)
+  auto copy_unit = [&](int i, int r, int part) {
+    const int cc = i / Hy, hv = value_head(i, r);
+    const int4 ti = chunk_of(table, cc);
+    int t = threadIdx.x;
+    opaque(t);
+    const int w = t >> 6, l = t & 63;
+    if (part == 0) {
+      dma_tile<TI, D, D, NW>(sBig, h_c + ((long)cc * H + hv) * D * D, D, D, w, l);
+    } else {
+      const long tv = ((long)ti.y * H + hv) * D;
+      dma_tile<TI, C, D, NW>(sC, dR + tv, (long)H * D, ti.z, w, l);
+      dma_tile<TI, C, D, NW>(sO, dO + tv, (long)H * D, ti.z, w, l);
+      dma_tile<TI, C, D, NW>(sDl, v_new + tv, (long)H * D, ti.z, w, l);
+    }
+  };
+  // K and Q (when the unit starts an item or heads are not grouped) and V of a unit, into
+  // registers
+  TileRegs<TI, C, D, N2> bk, bq, bv;
+  auto load_unit = [&](int i, int r) {
+    const int4 ti = chunk_of(table, i / Hy);
+    const int hk = GRP ? i % Hy : (i % Hy) / (H / Hg);
+    int t = threadIdx.x;
+    opaque(t);
+    if (!GRP || r == 0) {
+      const long o = ((long)ti.y * Hg + hk) * D;
+      bk.load_at(k + o, (long)Hg * D, ti.z, t);
+      bq.load_at(q + o, (long)Hg * D, ti.z, t);
+    }
+    bv.load_at(v + ((long)ti.y * H + value_head(i, r)) * D, (long)H * D, ti.z, t);
+  };
+
+  int it = next_item((int)blockIdx.x);
+  if (it >= n_items) return;
+  copy_unit(it, 0, 0);
+  copy_unit(it, 0, 1);
+  load_unit(it, 0);
+#pragma unroll 1
+  for (;;) {
+  const int c = it / Hy;
+  const int4 ci = chunk_of(table, c);
+  const int start = ci.y, len = ci.z;
+  const int hk = GRP ? it % Hy : (it % Hy) / (H / Hg);
+  const int hq = GRP ? hk : (qk_rows == H ? it % Hy : hk);  // dq, dk row
+  const int next_it = next_item(it + (int)gridDim.x);
   f32x4 aq[RPW][CBW], ak[RPW][CBW];  // dq and dk, summed over the value heads
 #pragma unroll
   for (int b = 0; b < RPW; ++b)
 #pragma unroll
     for (int m = 0; m < CBW; ++m) aq[b][m] = ak[b][m] = zero4();
-  if constexpr (GRP) {
-    // K and Q once per workgroup (nothing reads them before the first barrier below)
-    Blk<TI, C, D, N2> bk, bq;
-    bk.load(k + qk0, (long)Hg * D, len);
-    bq.load(q + qk0, (long)Hg * D, len);
-    bk.store_nat(sK, LDD);
-    bq.store_nat(sQ, LDD);
-  }
-  const int nr = GRP ? gsz : 1;  // value heads of this workgroup (a loop only when grouped)
 #pragma unroll 1
   for (int r = 0; r < nr; ++r) {
-  // grouped: lane and wave indices re-derived per head, so that the fragment addresses built
-  // from them are not hoisted out of the loop and kept live across it
+  // lane and wave indices re-derived per unit, so that the fragment addresses built from
+  // them are not hoisted out of the loops and kept live across them
   int tid = threadIdx.x;
-  if constexpr (GRP) opaque(tid);
+  opaque(tid);
   const int w = tid >> 6, l = tid & 63, lg = l >> 4, lc = l & 15;
   const int cw = w & 3, rh = w >> 2;
-  const int h = GRP ? hk * gsz + r : (int)blockIdx.y;
+  const int h = value_head(it, r);
+  // the next unit: the next value head of this item, or the next item's first
+  const int nit = r + 1 < nr ? it : next_it, nrr = r + 1 < nr ? r + 1 : 0;
   const long v0 = ((long)start * H + h) * D;
   const long hcoff = ((long)c * H + h) * D * D;
-  if (r > 0) __syncthreads();  // the previous value head is done with the LDS
-  if (threadIdx.x < C) {
-    const int t = threadIdx.x;
+  // the previous unit is done with the LDS, and this unit's copies have landed
+  wait_loads();
+  __syncthreads();
+  if (tid < C) {
+    const int t = tid;
     sG[t] = t < len ? g_t[(long)h * Ttot + start + t] : 0.f;
     sBeta[t] = t < len ? load_beta(beta, beta_f32, (long)(start + t) * H + h) : 0.f;
   }
-  // every operand tile of the head, loaded together (each thread holds its share in
-  // registers)
-  Blk<TI, C, D, N2> bdr, bdl, bv, bo, bk, bq;
-  Blk<TI, D, D, N2> bh, bd;
-  bdr.load(dR + v0, (long)H * D, len);
-  if constexpr (!GRP) {
-    bk.load(k + qk0, (long)Hg * D, len);
-    bq.load(q + qk0, (long)Hg * D, len);
-  }
-  bdl.load(v_new + v0, (long)H * D, len);
-  bv.load(v + v0, (long)H * D, len);
-  bo.load(dO + v0, (long)H * D, len);
-  bh.load(h_c + hcoff, D, D);
-  __syncthreads();  // Gc and beta
-  bdr.store_nat(sC, LDD);
-  if constexpr (!GRP) {
+  if (!GRP || r == 0) {
     bk.store_nat(sK, LDD);
     bq.store_nat(sQ, LDD);
   }
-  bdl.store_nat(sDl, LDD);
   bv.store_nat(sV, LDD);
-  bo.store_nat(sO, LDD);
-  bh.store_nat(sBig, LDD);
-  bd.load(dH + hcoff, D, D);
-  // dV = diag(beta) dR, from the registers that hold dR
-#pragma unroll
-  for (int a = 0; a < bdr.RB; ++a) {
-    const int t = bdr.r0 + a;
+  Blk<TI, D, D, N2> bd;
+  bd.load(dH + hcoff, D, D);  // dh', stored once h is no longer read
+  __syncthreads();  // Gc, beta, K, Q, V
+  // dV = diag(beta) dR, from the copied dR
+  for (int i = tid; i < C * PR; i += N2) {
+    const int t = i / PR, pc = i % PR;
     if (t < len) {
-      const typename Blk<TI, C, D, N2>::Vec x = bdr.row(a);
+      typename Blk<TI, C, D, N2>::Vec x;
+      x.u = *reinterpret_cast<const uint4*>(sC + t * LDD + pc * VE);
       const float bt = sBeta[t];
-      float* dst = dv + v0 + (long)t * H * D + bdr.c0;
+      float* dst = dv + v0 + (long)t * H * D + pc * VE;
 #pragma unroll
-      for (int q4 = 0; q4 < bdr.V / 4; ++q4) {
+      for (int q4 = 0; q4 < VE / 4; ++q4) {
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = bt * (float)x.e[4 * q4 + e];
@@ -469,7 +565,6 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
       }
     }
   }
-  __syncthreads();
 
   // fragment readers of the C x D products: rows 32 rh + 16 i of a [C][LD] panel; the
   // B operands of columns 16 (cw + 4 j): natural rows of a [.][LD] matrix, or M^T from M
@@ -484,7 +579,7 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   };
 
   // ---- phase B, h resident: K h, dO h^T (into aq), dR h^T (into ak), row dots.  aq and ak
-  // carry dq and dk summed over the value heads of the workgroup
+  // carry dq and dk summed over the value heads of the item
   {
     f32x4 Kh[RPW][CBW], tq[RPW][CBW], tk[RPW][CBW];
 #pragma unroll
@@ -586,9 +681,11 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
         if (lc == 0) sPart[(4 + cw) * C + t] = p1;
       }
   }
-  __syncthreads();  // row-dot parts complete; V read for the last time
-  if (threadIdx.x < 3 * C) {
-    const int x = 1 + threadIdx.x / C, t = threadIdx.x % C;
+  __syncthreads();  // row-dot parts complete; V and dh' read for the last time
+  // dh' is read no more in this unit: copy the next unit's h into its tile
+  if (nit < n_items) copy_unit(nit, nrr, 0);
+  if (tid < 3 * C) {
+    const int x = 1 + tid / C, t = tid % C;
     sRD[x * C + t] = sPart[(4 * x) * C + t] + sPart[(4 * x + 1) * C + t] +
                      sPart[(4 * x + 2) * C + t] + sPart[(4 * x + 3) * C + t];
   }
@@ -618,6 +715,8 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
         }
       });
   __syncthreads();  // the row-dot parts are summed before sRowE / sRowB reuse their space
+  // dR, dO and Delta are read no more in this unit: copy the next unit's into their tiles
+  if (nit < n_items) copy_unit(nit, nrr, 1);
   float rowE[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int b = 0; b < RPW; ++b) {
@@ -682,6 +781,8 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
 #pragma unroll
           for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
       });
+  // the next unit's K, Q and V into registers (stored once every wave is past phase D)
+  if (nit < n_items) load_unit(nit, nrr);
 
   // ---- dbeta and dg: wave 0, lane t = token t (C = 64 = one wave).  dg is the suffix sum of
   // dGc in the chunk; the last token's dGc also takes sum_t (gC / gam_t) rowsum(Delta * K
@@ -714,20 +815,27 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
     if (t < len) dg[(long)(start + t) * H + h] = suf;
   }
   }
-  const long dq0 = ((long)start * qk_rows + hq) * D;
+  {
+    const int w = wave_id(), l = lane_id(), lg = l >> 4, lc = l & 15;
+    const int cw = w & 3, rh = w >> 2;
+    const long dq0 = ((long)start * qk_rows + hq) * D;
 #pragma unroll
-  for (int b = 0; b < RPW; ++b)
+    for (int b = 0; b < RPW; ++b)
 #pragma unroll
-    for (int m = 0; m < CBW; ++m)
+      for (int m = 0; m < CBW; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * (RPW * rh + b) + 4 * lg + e;
-        if (t < len) {
-          const long gi = dq0 + (long)t * qk_rows * D + 16 * (cw + 4 * m) + lc;
-          dq[gi] = aq[b][m][e];
-          dk[gi] = ak[b][m][e];
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * (RPW * rh + b) + 4 * lg + e;
+          if (t < len) {
+            const long gi = dq0 + (long)t * qk_rows * D + 16 * (cw + 4 * m) + lc;
+            dq[gi] = aq[b][m][e];
+            dk[gi] = ak[b][m][e];
+          }
         }
-      }
+  }
+  it = next_it;
+  if (it >= n_items) break;
+  }
 }
 
 template <typename F>
@@ -766,10 +874,22 @@ hipError_t run_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st) 
   // grouped heads: one workgroup per (chunk, q/k head) runs the group's value heads
   const int gsz = p.H / p.Hg;
   const size_t sm2 = ChunkLds<TI, D>::bytes;
+  const long items = (long)p.max_chunks * (gsz > 1 ? p.Hg : p.H);
+  if (items == 0) return hipSuccess;
+  if (items > INT32_MAX) return hipErrorInvalidValue;
   auto launch = [&](auto kern) -> hipError_t {
     GDN_BTRY(set_lds(kern, sm2));
-    kern<<<dim3(p.max_chunks, p.Hg), chunk_threads<TI, D>(), sm2, st>>>(
-        b.st.table, q, k, v, p.beta, p.beta_f32 ? 1 : 0, b.st.g_t,
+    // persistent: as many workgroups as stay resident at once, each walking items with the
+    // grid as its stride
+    int dev = 0, cus = 0, per_cu = 0;
+    GDN_BTRY(hipGetDevice(&dev));
+    GDN_BTRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    GDN_BTRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern,
+                                                          chunk_threads<TI, D>(), sm2));
+    const long slots = (long)(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+    const int grid = (int)(items < slots ? items : slots);
+    kern<<<grid, chunk_threads<TI, D>(), sm2, st>>>(
+        b.st.table, p.max_chunks, q, k, v, p.beta, p.beta_f32 ? 1 : 0, b.st.g_t,
         static_cast<const TI*>(b.st.h_c), static_cast<const TI*>(b.st.v_new),
         static_cast<const TI*>(b.dR), static_cast<const TI*>(b.dH), dO, b.dq, b.dk, b.dv,
         b.dg, b.dbeta, p.Hg, gsz, p.Ttot, p.H, p.Hg, p.scale);
