@@ -81,13 +81,44 @@ __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, float x, i
                                           0);
 }
 
-// Sum over the 16 lanes of a lane group (one accumulator row, its 16 columns).
+// x from another lane of the same 16-lane row, by a DPP lane pattern (every source lane valid)
+template <int CTRL>
+__device__ __forceinline__ float dpp_from(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a lane group (one accumulator row, its 16 columns), in the VALU by
+// DPP (no LDS traffic): swaps within each quad of lanes, then the row rotated by 4 and by 8
+// lanes.  Every lane ends with the row's sum, in an order that depends on the lane (callers
+// take one lane's value).
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+  x += dpp_from<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_from<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_from<0x124>(x);  // row_ror 4
+  x += dpp_from<0x128>(x);  // row_ror 8
   return x;
+}
+
+// The elements of a row-major [.][ld] tile in the accumulator layout: lane l gets rows
+// r0 + 4 (l / 16) + e, e = 0..3, of column c0 + l % 16.  bf16: one transposing read (its
+// elements widened through 32-bit words); fp32: four reads.
+template <typename TI>
+__device__ __forceinline__ f32x4 acc_read(const TI* M, int ld, int r0, int c0, int lg,
+                                          int lc) {
+  f32x4 o;
+  if constexpr (sizeof(TI) == 2) {
+    const uint2 x = __builtin_bit_cast(uint2, read_tr4(M + (r0 + 4 * lg + (lc >> 2)) * ld + c0 +
+                                                       4 * (lc & 3)));
+    o[0] = __builtin_bit_cast(float, x.x << 16);
+    o[1] = __builtin_bit_cast(float, x.x & 0xFFFF0000u);
+    o[2] = __builtin_bit_cast(float, x.y << 16);
+    o[3] = __builtin_bit_cast(float, x.y & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)M[(r0 + 4 * lg + e) * ld + c0 + lc];
+  }
+  return o;
 }
 
 // Sum over the 4 lane groups (one accumulator column, 16 of its rows with the 4 elements).
@@ -607,18 +638,28 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
         });
     // row dots over the wave's columns: dR.K h, dR.V, Q.(dO h^T) = dO.Q h
 #pragma unroll
-    for (int b = 0; b < RPW; ++b)
+    for (int b = 0; b < RPW; ++b) {
+      f32x4 eC[CBW], eV[CBW], eQ[CBW];  // dR, V and Q in the accumulator layout
+#pragma unroll
+      for (int m = 0; m < CBW; ++m) {
+        const int r0 = 16 * (RPW * rh + b), c0 = 16 * (cw + 4 * m);
+        eC[m] = acc_read(sC, LDD, r0, c0, lg, lc);
+        eV[m] = acc_read(sV, LDD, r0, c0, lg, lc);
+        eQ[m] = acc_read(sQ, LDD, r0, c0, lg, lc);
+      }
+      // Gc and beta of the lane's four rows
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + 16 * (RPW * rh + b) + 4 * lg);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(sBeta + 16 * (RPW * rh + b) + 4 * lg);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * (RPW * rh + b) + 4 * lg + e;
         float p0 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
         for (int m = 0; m < CBW; ++m) {
-          const int gi = t * LDD + 16 * (cw + 4 * m) + lc;
-          const float r = (float)sC[gi];
+          const float r = eC[m][e];
           p2 += r * Kh[b][m][e];
-          p3 += r * (float)sV[gi];
-          p0 += (float)sQ[gi] * tq[b][m][e];
+          p3 += r * eV[m][e];
+          p0 += eQ[m][e] * tq[b][m][e];
         }
         p0 = sum16(p0);
         p2 = sum16(p2);
@@ -628,13 +669,14 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
           sPart[(8 + cw) * C + t] = p2;
           sPart[(12 + cw) * C + t] = p3;
         }
-        const float gam = __expf(sG[t]);
+        const float gam = __expf(g4[e]);
 #pragma unroll
         for (int m = 0; m < CBW; ++m) {
           aq[b][m][e] += scale * gam * tq[b][m][e];
-          ak[b][m][e] -= sBeta[t] * gam * tk[b][m][e];
+          ak[b][m][e] -= b4[e] * gam * tk[b][m][e];
         }
       }
+    }
   }
   {
     // <dh', h> from the held dh' blocks and the resident h (parts per wave, in order)
@@ -666,20 +708,26 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
         for (int m = 0; m < CBW; ++m) X[b][m] = MM::mma(fa[b], fb[m], X[b][m]);
     });
 #pragma unroll
-    for (int b = 0; b < RPW; ++b)
+    for (int b = 0; b < RPW; ++b) {
+      f32x4 eD[CBW];  // Delta in the accumulator layout
+#pragma unroll
+      for (int m = 0; m < CBW; ++m)
+        eD[m] = acc_read(sDl, LDD, 16 * (RPW * rh + b), 16 * (cw + 4 * m), lg, lc);
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + 16 * (RPW * rh + b) + 4 * lg);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * (RPW * rh + b) + 4 * lg + e;
         float p1 = 0.f;
-        const float r = __expf(gC - sG[t]);
+        const float r = __expf(gC - g4[e]);
 #pragma unroll
         for (int m = 0; m < CBW; ++m) {
-          p1 += (float)sDl[t * LDD + 16 * (cw + 4 * m) + lc] * Kd[b][m][e];
+          p1 += eD[m][e] * Kd[b][m][e];
           ak[b][m][e] += r * X[b][m][e];
         }
         p1 = sum16(p1);
         if (lc == 0) sPart[(4 + cw) * C + t] = p1;
       }
+    }
   }
   __syncthreads();  // row-dot parts complete; V and dh' read for the last time
   // dh' is read no more in this unit: copy the next unit's h into its tile
@@ -718,18 +766,22 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   // dR, dO and Delta are read no more in this unit: copy the next unit's into their tiles
   if (nit < n_items) copy_unit(nit, nrr, 1);
   float rowE[4] = {0.f, 0.f, 0.f, 0.f}, rowB[4] = {0.f, 0.f, 0.f, 0.f};
+  // Gc and beta of the lane's four rows i
+  const f32x4 gi4 = *reinterpret_cast<const f32x4*>(sG + 16 * cw + 4 * lg);
+  const f32x4 bi4 = *reinterpret_cast<const f32x4*>(sBeta + 16 * cw + 4 * lg);
 #pragma unroll
   for (int b = 0; b < RPW; ++b) {
     const int j = 16 * (RPW * rh + b) + lc;
+    const float gj = sG[j];
     float colE = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * cw + 4 * lg + e;
       const bool in = i < len && j < len;
-      const float gam = (in && i >= j) ? __expf(sG[i] - sG[j]) : 0.f;
+      const float gam = (in && i >= j) ? __expf(gi4[e] - gj) : 0.f;
       const float mi = (i >= j) ? scale * E1[b][e] * gam : 0.f;
       const float da = (in && i > j) ? -RD[b][e] : 0.f;
-      const float db = sBeta[i] * da * gam;
+      const float db = bi4[e] * da * gam;
       const float ee = mi * QK[b][e] + db * KK[b][e];
       rowE[e] += ee;
       rowB[e] += da * KK[b][e] * gam;
