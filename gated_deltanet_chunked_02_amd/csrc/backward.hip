@@ -121,6 +121,17 @@ __device__ __forceinline__ f32x4 acc_read(const TI* M, int ld, int r0, int c0, i
   return o;
 }
 
+// Four consecutive elements of TI from four floats (one 8- or 16-byte LDS store).
+template <typename TI>
+__device__ __forceinline__ void store4(TI* p, f32x4 v) {
+  if constexpr (sizeof(TI) == 2) {
+    const bf16x4 o = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(p) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
 // Sum over the 4 lane groups (one accumulator column, 16 of its rows with the 4 elements).
 __device__ __forceinline__ float sum4g(float x) {
   x += __shfl_xor(x, 16);
@@ -284,13 +295,16 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
       const int u = w + NW * m, ti = u >> 2, tj = u & 3;
       f32x4 acc = zero4();
       if (ti >= tj) mma_lds<TI>(acc, sQ, LDD, 16 * ti, sK, LDD, 16 * tj, 0, D);
-      const int j = 16 * tj + (l & 15);
+      const int j = 16 * tj + (l & 15), i0 = 16 * ti + 4 * (l >> 4);
+      const f32x4 gi = *reinterpret_cast<const f32x4*>(sG + i0);  // Gc of rows i0 .. i0 + 3
+      const float gj = sG[j];
+      f32x4 pv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * ti + 4 * (l >> 4) + e;
-        sPt[j * LDC + i] =
-            (TI)((i >= j && i < len) ? scale * acc[e] * __expf(sG[i] - sG[j]) : 0.f);
+        const int i = i0 + e;
+        pv[e] = (i >= j && i < len) ? scale * acc[e] * __expf(gi[e] - gj) : 0.f;
       }
+      store4<TI>(sPt + j * LDC + i0, pv);  // P^T row j, columns i0 .. i0 + 3
     }
     __syncthreads();
     const float gC = sG[len - 1], eC = __expf(gC);
@@ -301,10 +315,11 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
       f32x4 a = zero4(), x = zero4();
       mma_lds_Bn<TI, C>(a, sPt, LDC, 16 * tb, sO, LDD, 16 * w);
       mma_accB<TI, NDK>(x, sK, LDD, 16 * tb, 0, dh, NDK);
+      const f32x4 gt4 = *reinterpret_cast<const f32x4*>(sG + 16 * tb + 4 * (l >> 4));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * tb + 4 * (l >> 4) + e;
-        dd[tb][e] = t < len ? a[e] + __expf(gC - sG[t]) * x[e] : 0.f;
+        dd[tb][e] = t < len ? a[e] + __expf(gC - gt4[e]) * x[e] : 0.f;
       }
     }
     // dR = T^T dDelta
@@ -337,14 +352,19 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
     // dh = gC dh' + scale Q^T diag(gam) dO - K^T diag(beta gam) dR
     f32x4 go[NT], nd[NT];
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb)
+    for (int tb = 0; tb < NT; ++tb) {
+      const int t0 = 16 * tb + 4 * (l >> 4);
+      const f32x4 gt4 = *reinterpret_cast<const f32x4*>(sG + t0);
+      const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + t0);
+      const f32x4 o4 = acc_read(sO, LDD, 16 * tb, 16 * w, l >> 4, l & 15);  // dO[t][col]
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * tb + 4 * (l >> 4) + e;
-        const float gam = t < len ? __expf(sG[t]) : 0.f;
-        go[tb][e] = scale * gam * (float)sO[t * LDD + col];
-        nd[tb][e] = -sBeta[t] * gam * dr[tb][e];
+        const int t = t0 + e;
+        const float gam = t < len ? __expf(gt4[e]) : 0.f;
+        go[tb][e] = scale * gam * o4[e];
+        nd[tb][e] = -bt4[e] * gam * dr[tb][e];
       }
+    }
 #pragma unroll
     for (int db = 0; db < NDK; ++db) {
       dh[db] *= eC;
