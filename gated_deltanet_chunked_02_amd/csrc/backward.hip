@@ -496,6 +496,9 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   TI* sO = sC + L::P;            // dO
   TI* sDl = sO + L::P;           // Delta
   TI* sBig = sDl + L::P;         // h, then dh'
+  // Mi and DB are stored transposed (four elements per store) unless heads are grouped, where
+  // the four values held for those stores cost registers the grouped loop does not have
+  constexpr bool MT = !GRP;
   TI* sMi = sBig + L::BIG;       // V ([C][LDD] over both C x C tiles) in phase B, then Mi
   TI* sDB = sMi + L::CC;         // DB
   TI* sV = sMi;
@@ -794,6 +797,7 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
     const int j = 16 * (RPW * rh + b) + lc;
     const float gj = sG[j];
     float colE = 0.f;
+    f32x4 mi4, db4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * cw + 4 * lg + e;
@@ -806,8 +810,18 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
       rowE[e] += ee;
       rowB[e] += da * KK[b][e] * gam;
       colE += ee;
-      sMi[i * LDC + j] = (TI)mi;
-      sDB[i * LDC + j] = (TI)db;
+      if constexpr (MT) {
+        mi4[e] = mi;
+        db4[e] = db;
+      } else {
+        sMi[i * LDC + j] = (TI)mi;
+        sDB[i * LDC + j] = (TI)db;
+      }
+    }
+    if constexpr (MT) {
+      // stored transposed: the lane's four rows i are consecutive there
+      store4<TI>(sMi + j * LDC + 16 * cw + 4 * lg, mi4);
+      store4<TI>(sDB + j * LDC + 16 * cw + 4 * lg, db4);
     }
     colE = sum4g(colE);
     if (lg == 0) sColE[cw * C + j] = colE;
@@ -822,11 +836,15 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   }
   __syncthreads();
 
-  // ---- phase D: Mi K into aq; (DB + DB^T) K and Mi^T Q into ak
+  // ---- phase D: Mi K into aq; (DB + DB^T) K and Mi^T Q into ak.  Fragments of a matrix
+  // held as stored are natural reads, of its transpose transposing reads
+  auto frag_m = [&](const TI* Pm, int r0, int kk, bool transposed) {
+    return transposed == MT ? frag_ld<TI>(Pm, LDC, r0, kk) : frag_tr<TI>(Pm, LDC, r0, kk);
+  };
   mma_steps<TI, C, 2 * RPW, CBW>(
       [&](int i, int kk) {
         const TI* Pm = i >= RPW ? sDB : sMi;
-        return frag_ld<TI>(Pm, LDC, 16 * RPW * rh + 16 * (i % RPW), kk);
+        return frag_m(Pm, 16 * RPW * rh + 16 * (i % RPW), kk, false);
       },
       colsT(sK, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
@@ -838,7 +856,7 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
           }
       });
   mma_steps<TI, C, RPW, CBW>(
-      [&](int i, int kk) { return frag_tr<TI>(sDB, LDC, 16 * RPW * rh + 16 * i, kk); },  // DB^T
+      [&](int i, int kk) { return frag_m(sDB, 16 * RPW * rh + 16 * i, kk, true); },  // DB^T
       colsT(sK, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
         for (int b = 0; b < RPW; ++b)
@@ -846,7 +864,7 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
           for (int m = 0; m < CBW; ++m) ak[b][m] = MM::mma(fa[b], fb[m], ak[b][m]);
       });
   mma_steps<TI, C, RPW, CBW>(
-      [&](int i, int kk) { return frag_tr<TI>(sMi, LDC, 16 * RPW * rh + 16 * i, kk); },  // Mi^T
+      [&](int i, int kk) { return frag_m(sMi, 16 * RPW * rh + 16 * i, kk, true); },  // Mi^T
       colsT(sQ, LDD), [&](auto& fa, auto& fb) {
 #pragma unroll
         for (int b = 0; b < RPW; ++b)
