@@ -81,22 +81,15 @@ __device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t rs, float x, i
                                           0);
 }
 
-// x from another lane of the same 16-lane row, by a DPP lane pattern (every source lane valid)
-template <int CTRL>
-__device__ __forceinline__ float dpp_from(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               CTRL, 0xF, 0xF, false));
-}
-
 // Sum over the 16 lanes of a lane group (one accumulator row, its 16 columns), in the VALU by
 // DPP (no LDS traffic): swaps within each quad of lanes, then the row rotated by 4 and by 8
 // lanes.  Every lane ends with the row's sum, in an order that depends on the lane (callers
 // take one lane's value).
 __device__ __forceinline__ float sum16(float x) {
-  x += dpp_from<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-  x += dpp_from<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-  x += dpp_from<0x124>(x);  // row_ror 4
-  x += dpp_from<0x128>(x);  // row_ror 8
+  x += dpp_f<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x124>(x);  // row_ror 4
+  x += dpp_f<0x128>(x);  // row_ror 8
   return x;
 }
 

@@ -316,7 +316,8 @@ __global__ __launch_bounds__(DV * 4) void k_fused(
   auto make_gates = [&](int gb, float gv, uint32_t bvr) {
     const int t = lane_id();
     const float Gc = wave_incl_scan(gv) * kLog2e;
-    const float gend = __shfl(Gc, CS - 1, kWave);
+    const float gend =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gc), CS - 1));
     const float ef = __builtin_amdgcn_exp2f(Gc);
     if (t < CS) {
       SGC[gb][t] = Gc;

@@ -256,14 +256,24 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // not hoisted out of a loop (and kept live across it).
 template <typename T> __device__ __forceinline__ void opaque(T& x) { asm volatile("" : "+v"(x)); }
 
-// Inclusive prefix sum across a wave.
+// x from another lane by a DPP pattern (CTRL), in the rows (ROWS) and banks (BANKS) it
+// enables; lanes it leaves out, and lanes whose source lies outside the pattern, get 0.
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               CTRL, ROWS, BANKS, true));
+}
+
+// Inclusive prefix sum across a wave, in the VALU by DPP (no LDS traffic): a Hillis-Steele
+// scan within each 16-lane row (shifts by 1, 2, 4, 8 lanes), then the row totals carried
+// down: the last lane of rows 0 and 2 into rows 1 and 3, and lane 31 into rows 2 and 3.
 __device__ __forceinline__ float wave_incl_scan(float x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const float y = __shfl_up(x, d, kWave);
-    if (l >= d) x += y;
-  }
+  x += dpp_f<0x111>(x);        // row_shr 1
+  x += dpp_f<0x112>(x);        // row_shr 2
+  x += dpp_f<0x114>(x);        // row_shr 4
+  x += dpp_f<0x118>(x);        // row_shr 8
+  x += dpp_f<0x142, 0xA>(x);   // row_bcast 15, rows 1 and 3
+  x += dpp_f<0x143, 0xC>(x);   // row_bcast 31, rows 2 and 3
   return x;
 }
 
