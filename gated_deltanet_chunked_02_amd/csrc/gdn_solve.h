@@ -39,26 +39,28 @@ __device__ __forceinline__ void solve_diag_column(const float* sAd, TS* sM, int 
   {
     const int b = t >> 4, c = t & 15;
     const float* Ab = sAd + b * 16 * kAdLd;
-    // Forward substitution down column c; row i's entries are loaded two rows ahead so
-    // the dependent FMA chain does not wait on LDS.
+    // Forward substitution down column c, column-oriented: once x_m is final, every later
+    // row's sum takes its term -A[i][m] x_m at once (independent FMAs), so the dependent
+    // chain is one FMA per row rather than one per term.  Each row still sums its terms in
+    // the order m = 0, 1, ... from the identity's entry, as row-by-row substitution does.
+    // Columns of A are loaded two ahead.
     float x[16];
-    float ra[16], rb[16];
+    float ca[16], cb[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      ra[m] = m < 1 ? Ab[1 * kAdLd + m] : 0.f;
-      rb[m] = m < 2 ? Ab[2 * kAdLd + m] : 0.f;
+    for (int i = 0; i < 16; ++i) {
+      x[i] = (i == c) ? 1.f : 0.f;
+      ca[i] = i > 0 ? Ab[i * kAdLd + 0] : 0.f;
+      cb[i] = i > 1 ? Ab[i * kAdLd + 1] : 0.f;
     }
-    x[0] = (c == 0) ? 1.f : 0.f;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float s = (i == c) ? 1.f : 0.f;
+    for (int m = 0; m < 15; ++m) {
+      const float xm = x[m];
 #pragma unroll
-      for (int m = 0; m < i; ++m) s = fmaf(-ra[m], x[m], s);
-      x[i] = s;
+      for (int i = m + 1; i < 16; ++i) x[i] = fmaf(-ca[i], xm, x[i]);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        ra[m] = rb[m];
-        rb[m] = (i + 2 < 16 && m < i + 2) ? Ab[(i + 2) * kAdLd + m] : 0.f;
+      for (int i = 0; i < 16; ++i) {
+        ca[i] = cb[i];
+        cb[i] = (m + 2 < 16 && i > m + 2) ? Ab[i * kAdLd + m + 2] : 0.f;
       }
     }
     const int base = 16 * b;

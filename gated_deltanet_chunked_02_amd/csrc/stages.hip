@@ -40,6 +40,8 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* cu, int N, 
                                                       int C, int max_chunks, int32_t* table,
                                                       int32_t* seq_chunks) {
   __shared__ int s_part[16];
+  // this block of sequences: each one's first chunk, first token and length
+  __shared__ int s_off[1024], s_start[1024], s_len[1024];
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
   int4* tab = reinterpret_cast<int4*>(table);
   int carry = 0;
@@ -58,12 +60,23 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* cu, int N, 
       total += x;
     }
     const int off = carry + wbase + incl - nc;
-    if (n < N) {
-      seq_chunks[n] = min(off, max_chunks);
-      for (int m = 0; m < nc; ++m) {
-        const int idx = off + m;
-        if (idx < max_chunks) tab[idx] = make_int4(n, start + m * C, min(C, len - m * C), m);
+    if (n < N) seq_chunks[n] = min(off, max_chunks);
+    s_off[tid] = off;  // past the block's sequences: the end (no chunk lies there)
+    s_start[tid] = start;
+    s_len[tid] = len;
+    __syncthreads();
+    // every thread writes rows of the table: row idx belongs to the last sequence of the
+    // block whose first chunk is at or before idx (an empty sequence starts where the next
+    // one does, so the search passes over it)
+    const int cnt = min(1024, N - base);
+    for (int idx = carry + tid; idx < min(carry + total, max_chunks); idx += 1024) {
+      int lo = 0, hi = cnt - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= idx) lo = mid; else hi = mid - 1;
       }
+      const int m = idx - s_off[lo];
+      tab[idx] = make_int4(base + lo, s_start[lo] + m * C, min(C, s_len[lo] - m * C), m);
     }
     carry += total;
     __syncthreads();
@@ -252,8 +265,15 @@ __device__ __forceinline__ void store_T_rows(const TS* sM, int ld, TI* dst, long
         uint4 u[2];
         TI e[8];
       } o;
+      union {
+        uint4 u[sizeof(TS) / 2];
+        TS e[8];
+      } m;  // the row's 8 elements, one 16-byte LDS read per 16 bytes
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o.e[e] = (TI)(j0 + e <= t ? (float)sM[t * ld + j0 + e] : 0.f);
+      for (int q = 0; q < (int)sizeof(TS) / 2; ++q)
+        m.u[q] = reinterpret_cast<const uint4*>(sM + t * ld + j0)[q];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o.e[e] = (TI)(j0 + e <= t ? (float)m.e[e] : 0.f);
       uint4* d = reinterpret_cast<uint4*>(dst + (long)t * stride + j0);
 #pragma unroll
       for (int q = 0; q < (int)sizeof(TI) / 2; ++q) d[q] = o.u[q];
