@@ -50,9 +50,15 @@ namespace {
 template <typename TI, int D>
 constexpr int chunk_threads() { return 512; }
 
-// threads of the dh workgroup: one wave per 16 state columns
-template <int D>
-constexpr int dh_threads() { return 4 * D; }
+// Layout of the dh workgroup: each wave owns CB blocks of 16 state columns.  CB = 1: one
+// wave per block, the tiles double-buffered by chunk parity (133 KB of LDS at D = 128, one
+// workgroup per CU).  CB = 2 (bf16, D = 128, for grids of many (sequence, head) pairs): four
+// waves of two blocks and single-buffered tiles copied straight into LDS (71 KB, two
+// workgroups per CU, each one's barriers and loads hidden behind the other's work).
+template <int CB>
+constexpr bool dh_double() { return CB == 1; }
+template <int D, int CB>
+constexpr int dh_threads() { return 64 * D / (16 * CB); }
 constexpr int kBC = 64;   // chunk length of the backward
 
 __device__ __forceinline__ int4 chunk_of(const int32_t* table, int c) {
@@ -133,6 +139,52 @@ __device__ __forceinline__ float sum4g(float x) {
 }
 
 
+// One 16-byte copy per lane from global memory straight into LDS: lane l's 16 bytes land at
+// lds + 16 l (lds is the same for the whole wave; M0 carries it, and the wait state the
+// hardware needs between an M0 write and the copy that reads it is in the statement).  It is
+// inline assembly because the compiler, when it issues such a copy itself, waits for it to
+// land before every transposing LDS read that follows (it cannot tell those reads apart from
+// the copy's target), which would serialise the copies with the products they are meant to
+// overlap.  The compiler therefore does not know of the copy: the caller waits for it
+// (wait_loads) before the barrier that publishes the tile, and touches nothing of the tile
+// before then.
+__device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
+  const unsigned a = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) void*)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(a) : "memory");
+}
+
+// Wave w's share (NW waves) of a direct HBM -> LDS copy of a ROWS x COLS tile of TI into the
+// padded natural layout [ROWS][COLS + pad_of<TI>()]: rows of PR 16-byte pieces and one pad
+// piece.  Each copy instruction writes 64 consecutive 16-byte LDS pieces, lane l the l-th, so
+// piece p of the tile is row p / (PR + 1), piece p % (PR + 1); the pad piece re-reads its
+// row's first piece.  Rows past len re-read row len - 1 (in bounds; every product masks those
+// rows).  No registers hold the data: the copy lands in LDS on its own, and a wait for the
+// wave's memory counter, then a barrier, make it visible to the workgroup.
+template <typename TI, int ROWS, int COLS, int NW>
+__device__ __forceinline__ void dma_tile(TI* dst, const TI* src, long stride, int len, int w,
+                                         int l) {
+  constexpr int VE = 16 / (int)sizeof(TI), PR = COLS / VE, PP = PR + 1;
+  static_assert(COLS + pad_of<TI>() == PP * VE, "one pad piece per row");
+  static_assert((ROWS * PP) % kWave == 0, "whole copy instructions");
+  constexpr int NI = ROWS * PP / kWave;
+#pragma unroll
+  for (int j0 = 0; j0 < NI; j0 += NW) {
+    const int j = j0 + w;
+    if (j < NI) {
+      const int p = kWave * j + l, r = p / PP, c = p % PP;
+      lds_copy16(src + (long)min(r, len - 1) * stride + (c < PR ? c : 0) * VE,
+                 dst + kWave * VE * j);
+    }
+  }
+}
+
+// Wait until this wave's loads (copies into LDS included) have landed.
+__device__ __forceinline__ void wait_loads() {
+  // s_waitcnt with vmcnt = 0 and expcnt, lgkmcnt at their maxima (no wait on those)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // ------------------------------------------------------------------------- dh pass
 // acc += M^T[col0 .. col0 + 15][k] * Bt[k][.] over k < 16 NKB, with M row-major [k][col] in
 // LDS and Bt accumulator tiles whose rows run over k (the k order of mma_accB: 4 consecutive
@@ -188,61 +240,66 @@ __device__ __forceinline__ void mma_lds_Bn(f32x4& acc, const TI* A, int lda, int
 
 // With W = T diag(beta gam) K, the update's W^T dDelta is K^T diag(beta gam) dR, dR = T^T
 // dDelta: the pass reads rows of T (C x C) instead of W (C x D), and hands dR to the chunk
-// kernel.  One workgroup per (sequence, head), wave w owning state columns 16 w .. 16 w + 15,
-// so Q, K and T are read and P is built once per chunk.  Every tile sits in LDS in its
-// natural layout (Q, K, dO [C][LDD]; T, P^T [C][LDC]); the transposed operands Q^T, K^T, T^T
-// and dO^T are read from them directly.  About 69 KB at D = 128 in bf16.
-// The tiles and gates of a chunk are double-buffered (one set per chunk parity), so storing
-// the next chunk's needs no barrier of its own; P^T is single.
+// kernel.  One workgroup per (sequence, head), wave w owning the state columns of blocks
+// CB w .. CB w + CB - 1, so Q, K and T are read and P is built once per chunk.  Every tile
+// sits in LDS in its natural layout (Q, K, dO [C][LDD]; T, P^T [C][LDC]); the transposed
+// operands Q^T, K^T, T^T and dO^T are read from them directly.  Double-buffered (one tile set
+// per chunk parity), storing the next chunk's tiles needs no barrier of its own.
 template <typename TI, int D>
 constexpr size_t dh_buf_bytes() {
   constexpr int LDD = D + pad_of<TI>(), LDC = kBC + pad_of<TI>();
   return (3 * kBC * LDD + kBC * LDC) * sizeof(TI) + 2 * kBC * sizeof(float);
 }
 
-template <typename TI, int D>
+template <typename TI, int D, int CB>
 constexpr size_t dh_smem() {
   constexpr int LDC = kBC + pad_of<TI>();
-  return 2 * dh_buf_bytes<TI, D>() + kBC * LDC * sizeof(TI);
+  return (dh_double<CB>() ? 2 : 1) * dh_buf_bytes<TI, D>() + kBC * LDC * sizeof(TI);
 }
 
-template <typename TI, int D>
-__global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __restrict__ table,
-                                                const int32_t* __restrict__ seq_chunks,
-                                                const TI* __restrict__ q,
-                                                const TI* __restrict__ k,
-                                                const TI* __restrict__ Tinv,
-                                                const void* __restrict__ beta, int beta_f32,
-                                                const TI* __restrict__ dO,
-                                                const float* __restrict__ g_t,
-                                                const float* __restrict__ dht,
-                                                TI* __restrict__ dH, TI* __restrict__ dRo,
-                                                float* __restrict__ dh0, int Ttot, int H,
-                                                int Hg, float scale) {
-  constexpr int C = kBC, NDK = D / 16, NT = C / 16, NW = D / 16, NTH = dh_threads<D>();
+template <typename TI, int D, int CB>
+__global__ __launch_bounds__((dh_threads<D, CB>()), (dh_double<CB>() ? 1 : 2)) void k_bwd_dh(
+    const int32_t* __restrict__ table, const int32_t* __restrict__ seq_chunks,
+    const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ Tinv,
+    const void* __restrict__ beta, int beta_f32, const TI* __restrict__ dO,
+    const float* __restrict__ g_t, const float* __restrict__ dht, TI* __restrict__ dH,
+    TI* __restrict__ dRo, float* __restrict__ dh0, int Ttot, int H, int Hg, float scale) {
+  constexpr int C = kBC, NDK = D / 16, NT = C / 16, NW = D / (16 * CB);
+  constexpr int NTH = dh_threads<D, CB>();
+  constexpr bool DBUF = dh_double<CB>();
   constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>();
   const int n = blockIdx.x, h = blockIdx.y, hk = h / (H / Hg);
   const int w = wave_id(), l = lane_id();
-  const int col = 16 * w + (l & 15);  // this lane's state column
   extern __shared__ __align__(16) char smem[];
-  TI* sPt = reinterpret_cast<TI*>(smem + 2 * dh_buf_bytes<TI, D>());  // [C][LDC]  P^T
+  TI* sPt = reinterpret_cast<TI*>(smem + (DBUF ? 2 : 1) * dh_buf_bytes<TI, D>());  // P^T
 
-  // dh tile db: rows (key index) 16 db + 4 (l/16) + e, column col
-  f32x4 dh[NDK];
+  // dh tile (cb, db): rows (key index) 16 db + 4 (l/16) + e, column col(cb)
+  auto col_of = [&](int cb) { return 16 * (CB * w + cb) + (l & 15); };
+  f32x4 dh[CB][NDK];
   const long hoff = ((long)n * H + h) * D * D;
 #pragma unroll
-  for (int db = 0; db < NDK; ++db)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      dh[db][e] = dht ? dht[hoff + (long)(16 * db + 4 * (l >> 4) + e) * D + col] : 0.f;
+    for (int db = 0; db < NDK; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dh[cb][db][e] =
+            dht ? dht[hoff + (long)(16 * db + 4 * (l >> 4) + e) * D + col_of(cb)] : 0.f;
 
-  // the chunk's operands are loaded one chunk ahead (into registers) while the previous one
-  // is computed
+  // Double-buffered: the chunk's operands are loaded one chunk ahead (into registers) while
+  // the previous one is computed.  Single: they are copied straight into LDS at the chunk's
+  // start (no registers held; the other workgroup on the CU runs meanwhile).
   const int c0 = seq_chunks[n], c1 = seq_chunks[n + 1];
   Blk<TI, C, D, NTH> bq, bk, bo;
   Blk<TI, C, C, NTH> bt;
   float gt = 0.f, bet = 0.f;
   int glen = 0;
+  auto fetch_gates = [&](int start, int len) {
+    const int tt = min((int)threadIdx.x, len - 1);
+    gt = g_t[(long)h * Ttot + start + tt];
+    bet = load_beta(beta, beta_f32, (long)(start + tt) * H + h);
+    glen = len;
+  };
   auto fetch = [&](int c) {
     const int4 ci = chunk_of(table, c);
     const int start = ci.y, len = ci.z;
@@ -251,35 +308,50 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
     bk.load(k + qk0, (long)Hg * D, len);
     bt.load(Tinv + ((long)start * H + h) * C, (long)H * C, len);
     bo.load(dO + v0, (long)H * D, len);
-    const int tt = min((int)threadIdx.x, len - 1);
-    gt = g_t[(long)h * Ttot + start + tt];
-    bet = load_beta(beta, beta_f32, (long)(start + tt) * H + h);
-    glen = len;
+    fetch_gates(start, len);
   };
-  if (c1 > c0) fetch(c1 - 1);
+  if constexpr (DBUF)
+    if (c1 > c0) fetch(c1 - 1);
   for (int c = c1 - 1; c >= c0; --c) {
     const int4 ci = chunk_of(table, c);
     const int start = ci.y, len = ci.z;
     const long v0 = ((long)start * H + h) * D;
-    // this chunk's buffer set: the other set was read by the previous chunk, and the chunk
-    // before that, which read this one, finished before the previous chunk's first barrier
-    char* sb = smem + ((c1 - 1 - c) & 1) * dh_buf_bytes<TI, D>();
+    // this chunk's buffer set: double-buffered, the other set was read by the previous
+    // chunk, and the chunk before that, which read this one, finished before the previous
+    // chunk's first barrier; single, every wave must be done with the previous chunk first
+    if constexpr (!DBUF) __syncthreads();
+    char* sb = smem + (DBUF ? ((c1 - 1 - c) & 1) * dh_buf_bytes<TI, D>() : 0);
     TI* sQ = reinterpret_cast<TI*>(sb);  // [C][LDD]
     TI* sK = sQ + C * LDD;               // [C][LDD]
     TI* sO = sK + C * LDD;               // [C][LDD]  dO
     TI* sT = sO + C * LDD;               // [C][LDC]  rows of T
     float* sG = reinterpret_cast<float*>(sT + C * LDC);
     float* sBeta = sG + C;
-    bq.store_nat(sQ, LDD);
-    bk.store_nat(sK, LDD);
-    bt.store_nat(sT, LDC);
-    bo.store_nat(sO, LDD);
+    if constexpr (DBUF) {
+      bq.store_nat(sQ, LDD);
+      bk.store_nat(sK, LDD);
+      bt.store_nat(sT, LDC);
+      bo.store_nat(sO, LDD);
+    } else {
+      // rows past len re-read row len - 1; every use masks them (P^T, dDelta, the update's
+      // right-hand sides are zero there, T is zero above its diagonal)
+      const long qk0 = ((long)start * Hg + hk) * D;
+      dma_tile<TI, C, D, NW>(sQ, q + qk0, (long)Hg * D, len, w, l);
+      dma_tile<TI, C, D, NW>(sK, k + qk0, (long)Hg * D, len, w, l);
+      dma_tile<TI, C, C, NW>(sT, Tinv + ((long)start * H + h) * C, (long)H * C, len, w, l);
+      dma_tile<TI, C, D, NW>(sO, dO + v0, (long)H * D, len, w, l);
+      fetch_gates(start, len);
+    }
     if (threadIdx.x < C) {
       const bool in = (int)threadIdx.x < glen;
       sG[threadIdx.x] = in ? gt : 0.f;
       sBeta[threadIdx.x] = in ? bet : 0.f;
     }
-    if (c > c0) fetch(c - 1);
+    if constexpr (DBUF) {
+      if (c > c0) fetch(c - 1);
+    } else {
+      wait_loads();  // this wave's copies have landed
+    }
     __syncthreads();
     // P^T: P[i][j] = scale (q_i . k_j) e^{Gc_i - Gc_j} for j <= i < len, stored at [j][i]
     // (wave w: tiles w, w + NW, ... of the 16)
@@ -301,119 +373,89 @@ __global__ __launch_bounds__(dh_threads<D>()) void k_bwd_dh(const int32_t* __res
     }
     __syncthreads();
     const float gC = sG[len - 1], eC = __expf(gC);
-    // dDelta (rows t, this lane's column) = P^T dO + (gC / gam_t) (K dh')
-    f32x4 dd[NT];
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb) {
-      f32x4 a = zero4(), x = zero4();
-      mma_lds_Bn<TI, C>(a, sPt, LDC, 16 * tb, sO, LDD, 16 * w);
-      mma_accB<TI, NDK>(x, sK, LDD, 16 * tb, 0, dh, NDK);
-      const f32x4 gt4 = *reinterpret_cast<const f32x4*>(sG + 16 * tb + 4 * (l >> 4));
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = col_of(cb), cblk = 16 * (CB * w + cb);
+      // dDelta (rows t, this lane's column) = P^T dO + (gC / gam_t) (K dh')
+      f32x4 dd[NT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * tb + 4 * (l >> 4) + e;
-        dd[tb][e] = t < len ? a[e] + __expf(gC - gt4[e]) * x[e] : 0.f;
+      for (int tb = 0; tb < NT; ++tb) {
+        f32x4 a = zero4(), x = zero4();
+        mma_lds_Bn<TI, C>(a, sPt, LDC, 16 * tb, sO, LDD, cblk);
+        mma_accB<TI, NDK>(x, sK, LDD, 16 * tb, 0, dh[cb], NDK);
+        const f32x4 gt4 = *reinterpret_cast<const f32x4*>(sG + 16 * tb + 4 * (l >> 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * tb + 4 * (l >> 4) + e;
+          dd[tb][e] = t < len ? a[e] + __expf(gC - gt4[e]) * x[e] : 0.f;
+        }
       }
-    }
-    // dR = T^T dDelta
-    f32x4 dr[NT];
+      // dR = T^T dDelta
+      f32x4 dr[NT];
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb) {
-      dr[tb] = zero4();
-      mma_accB_T<TI, NT>(dr[tb], sT, LDC, 16 * tb, dd);
-    }
-    // the chunk-end gradient dh' and dR, for the chunk-parallel kernel (not written by the
-    // pass that only finds each segment's start gradient)
-    if (dH) {
-      constexpr int E = sizeof(TI);
-      const auto rh = out_rsrc(dH + ((long)c * H + h) * D * D, D * D * E);
-      const int hv = (4 * (l >> 4) * D + col) * E;
-#pragma unroll
-      for (int db = 0; db < NDK; ++db)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) store_elem<TI>(rh, dh[db][e], hv, (16 * db + e) * D * E);
-      // dR: the resource holds rows t < len; a store to a later row is dropped (its whole
-      // offset is in the per-lane part, which the bounds check covers)
-      const auto rr = out_rsrc(dRo + v0, (uint32_t)len * H * D * E);
-      const int rstep = H * D * E;
-#pragma unroll
-      for (int tb = 0; tb < NT; ++tb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          store_elem<TI>(rr, dr[tb][e], (16 * tb + 4 * (l >> 4) + e) * rstep + col * E, 0);
-    }
-    // dh = gC dh' + scale Q^T diag(gam) dO - K^T diag(beta gam) dR
-    f32x4 go[NT], nd[NT];
-#pragma unroll
-    for (int tb = 0; tb < NT; ++tb) {
-      const int t0 = 16 * tb + 4 * (l >> 4);
-      const f32x4 gt4 = *reinterpret_cast<const f32x4*>(sG + t0);
-      const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + t0);
-      const f32x4 o4 = acc_read(sO, LDD, 16 * tb, 16 * w, l >> 4, l & 15);  // dO[t][col]
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t0 + e;
-        const float gam = t < len ? __expf(gt4[e]) : 0.f;
-        go[tb][e] = scale * gam * o4[e];
-        nd[tb][e] = -bt4[e] * gam * dr[tb][e];
+      for (int tb = 0; tb < NT; ++tb) {
+        dr[tb] = zero4();
+        mma_accB_T<TI, NT>(dr[tb], sT, LDC, 16 * tb, dd);
       }
-    }
+      // the chunk-end gradient dh' and dR, for the chunk-parallel kernel (not written by the
+      // pass that only finds each segment's start gradient)
+      if (dH) {
+        constexpr int E = sizeof(TI);
+        const auto rh = out_rsrc(dH + ((long)c * H + h) * D * D, D * D * E);
+        const int hv = (4 * (l >> 4) * D + col) * E;
 #pragma unroll
-    for (int db = 0; db < NDK; ++db) {
-      dh[db] *= eC;
-      mma_accB_T<TI, NT>(dh[db], sQ, LDD, 16 * db, go);
-      mma_accB_T<TI, NT>(dh[db], sK, LDD, 16 * db, nd);
+        for (int db = 0; db < NDK; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            store_elem<TI>(rh, dh[cb][db][e], hv, (16 * db + e) * D * E);
+        // dR: the resource holds rows t < len; a store to a later row is dropped (its whole
+        // offset is in the per-lane part, which the bounds check covers)
+        const auto rr = out_rsrc(dRo + v0, (uint32_t)len * H * D * E);
+        const int rstep = H * D * E;
+#pragma unroll
+        for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            store_elem<TI>(rr, dr[tb][e], (16 * tb + 4 * (l >> 4) + e) * rstep + col * E, 0);
+      }
+      // dh = gC dh' + scale Q^T diag(gam) dO - K^T diag(beta gam) dR
+      f32x4 go[NT], nd[NT];
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb) {
+        const int t0 = 16 * tb + 4 * (l >> 4);
+        const f32x4 gt4 = *reinterpret_cast<const f32x4*>(sG + t0);
+        const f32x4 bt4 = *reinterpret_cast<const f32x4*>(sBeta + t0);
+        const f32x4 o4 = acc_read(sO, LDD, 16 * tb, cblk, l >> 4, l & 15);  // dO[t][col]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = t0 + e;
+          const float gam = t < len ? __expf(gt4[e]) : 0.f;
+          go[tb][e] = scale * gam * o4[e];
+          nd[tb][e] = -bt4[e] * gam * dr[tb][e];
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < NDK; ++db) {
+        dh[cb][db] *= eC;
+        mma_accB_T<TI, NT>(dh[cb][db], sQ, LDD, 16 * db, go);
+        mma_accB_T<TI, NT>(dh[cb][db], sK, LDD, 16 * db, nd);
+      }
+      // one column block at a time: its temporaries are dead before the next one's start
+      if constexpr (CB > 1) __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (dh0) {
 #pragma unroll
-    for (int db = 0; db < NDK; ++db)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dh0[hoff + (long)(16 * db + 4 * (l >> 4) + e) * D + col] = dh[db][e];
+      for (int db = 0; db < NDK; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dh0[hoff + (long)(16 * db + 4 * (l >> 4) + e) * D + col_of(cb)] = dh[cb][db][e];
   }
 }
 
 // ------------------------------------------------------------------------- chunk gradients
-// One 16-byte copy per lane from global memory straight into LDS: lane l's 16 bytes land at
-// lds + 16 l (lds is the same for the whole wave; M0 carries it, and the wait state the
-// hardware needs between an M0 write and the copy that reads it is in the statement).  It is
-// inline assembly because the compiler, when it issues such a copy itself, waits for it to
-// land before every transposing LDS read that follows (it cannot tell those reads apart from
-// the copy's target), which would serialise the copies with the products they are meant to
-// overlap.  The compiler therefore does not know of the copy: the caller waits for it
-// (wait_loads) before the barrier that publishes the tile, and touches nothing of the tile
-// before then.
-__device__ __forceinline__ void lds_copy16(const void* src, void* lds) {
-  const unsigned a = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(__attribute__((address_space(3))) void*)lds);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(a) : "memory");
-}
-
-// Wave w's share (NW waves) of a direct HBM -> LDS copy of a ROWS x COLS tile of TI into the
-// padded natural layout [ROWS][COLS + pad_of<TI>()]: rows of PR 16-byte pieces and one pad
-// piece.  Each copy instruction writes 64 consecutive 16-byte LDS pieces, lane l the l-th, so
-// piece p of the tile is row p / (PR + 1), piece p % (PR + 1); the pad piece re-reads its
-// row's first piece.  Rows past len re-read row len - 1 (in bounds; every product masks those
-// rows).  No registers hold the data: the copy lands in LDS on its own, and a wait for the
-// wave's memory counter, then a barrier, make it visible to the workgroup.
-template <typename TI, int ROWS, int COLS, int NW>
-__device__ __forceinline__ void dma_tile(TI* dst, const TI* src, long stride, int len, int w,
-                                         int l) {
-  constexpr int VE = 16 / (int)sizeof(TI), PR = COLS / VE, PP = PR + 1;
-  static_assert(COLS + pad_of<TI>() == PP * VE, "one pad piece per row");
-  static_assert((ROWS * PP) % kWave == 0, "whole copy instructions");
-  constexpr int NI = ROWS * PP / kWave;
-#pragma unroll
-  for (int j0 = 0; j0 < NI; j0 += NW) {
-    const int j = j0 + w;
-    if (j < NI) {
-      const int p = kWave * j + l, r = p / PP, c = p % PP;
-      lds_copy16(src + (long)min(r, len - 1) * stride + (c < PR ? c : 0) * VE,
-                 dst + kWave * VE * j);
-    }
-  }
-}
-
 // A TileCopy whose load takes the thread index as an argument: a loop that passes an index the
 // compiler cannot see through recomputes the lane's addresses per call instead of holding
 // them in registers across the loop.
@@ -433,11 +475,6 @@ struct TileRegs : TileCopy<TI, ROWS, COLS, NTH> {
   }
 };
 
-// Wait until this wave's loads (copies into LDS included) have landed.
-__device__ __forceinline__ void wait_loads() {
-  // s_waitcnt with vmcnt = 0 and expcnt, lgkmcnt at their maxima (no wait on those)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
 
 // One workgroup of 4 RW waves per resident slot; it walks the (chunk, head) items b, b + G,
 // b + 2 G, ... (G workgroups, items with tokens only; RW = 2 or 4 row groups, RPW = 4 / RW).
@@ -933,19 +970,35 @@ hipError_t set_lds(F f, size_t bytes) {
     if (e_ != hipSuccess) return e_;    \
   } while (0)
 
-template <typename TI, int D>
-hipError_t run_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
-                      const int32_t* run_chunks, const float* dht, void* dH, void* dR,
-                      float* dh0, hipStream_t st) {
-  if (runs <= 0) return hipSuccess;
-  const size_t sm1 = dh_smem<TI, D>();
-  GDN_BTRY(set_lds(k_bwd_dh<TI, D>, sm1));
-  k_bwd_dh<TI, D><<<dim3(runs, p.H), dh_threads<D>(), sm1, st>>>(
+template <typename TI, int D, int CB>
+hipError_t run_bwd_dh_cb(const Problem& p, const BwdBuffers& b, int runs,
+                         const int32_t* run_chunks, const float* dht, void* dH, void* dR,
+                         float* dh0, hipStream_t st) {
+  const size_t sm1 = dh_smem<TI, D, CB>();
+  GDN_BTRY(set_lds(k_bwd_dh<TI, D, CB>, sm1));
+  k_bwd_dh<TI, D, CB><<<dim3(runs, p.H), dh_threads<D, CB>(), sm1, st>>>(
       b.st.table, run_chunks, static_cast<const TI*>(p.q), static_cast<const TI*>(p.k),
       static_cast<const TI*>(b.st.Tinv), p.beta, p.beta_f32 ? 1 : 0,
       static_cast<const TI*>(b.dO), b.st.g_t, dht, static_cast<TI*>(dH), static_cast<TI*>(dR),
       dh0, p.Ttot, p.H, p.Hg, p.scale);
   return hipGetLastError();
+}
+
+template <typename TI, int D>
+hipError_t run_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
+                      const int32_t* run_chunks, const float* dht, void* dH, void* dR,
+                      float* dh0, hipStream_t st) {
+  if (runs <= 0) return hipSuccess;
+  if constexpr (sizeof(TI) == 2 && D == 128) {
+    // two workgroups per CU pay off once the pairs outnumber the CUs several times over
+    // (measured: 64 sequences x 64 heads gain 7 %; 512 or 256 pairs of equal length lose)
+    int dev = 0, cus = 0;
+    GDN_BTRY(hipGetDevice(&dev));
+    GDN_BTRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    if ((long)runs * p.H >= 8L * (cus > 0 ? cus : 1))
+      return run_bwd_dh_cb<TI, D, 2>(p, b, runs, run_chunks, dht, dH, dR, dh0, st);
+  }
+  return run_bwd_dh_cb<TI, D, 1>(p, b, runs, run_chunks, dht, dH, dR, dh0, st);
 }
 
 template <typename TI, int D>

@@ -116,6 +116,27 @@ def test_backward_varlen_with_empty_and_short_sequences(D, dtype):
         assert e <= tol(dtype, "dv"), (n, e)
 
 
+def test_backward_many_pairs_two_workgroups_per_cu():
+    # 72 sequences x 32 heads: enough (sequence, head) pairs (8 per CU) for the reverse pass
+    # to run its two-workgroups-per-CU layout (four waves of two column blocks, tiles copied
+    # straight into LDS); short sequences with empty and one-token ones among them
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(0, 41, size=72)]
+    lens[3], lens[10] = 0, 1
+    inp = draw(H=32, Hg=16, D=128, dtype="bf16", seed=53, lens=lens)
+    got = run_bwd(inp)
+    ref = oracle_bwd(inp)
+    compare(inp, got, ref, "bf16", "many pairs")
+    cu = inp["cu_seqlens"].numpy()
+    for n in range(len(lens)):
+        s0, s1 = int(cu[n]), int(cu[n + 1])
+        if s1 == s0:
+            continue
+        for i in (0, 2):  # dq and dv of the sequence
+            e = rel_l2(to64(got[i])[:, s0:s1], ref[i][:, s0:s1])
+            assert e <= tol("bf16", NAMES[i]), (n, NAMES[i], e)
+
+
 def test_backward_fp32_beta_with_bf16_inputs():
     inp = draw(B=1, T=100, H=2, Hg=2, D=128, seed=41, beta_dtype="f32")
     assert inp["beta"].dtype == torch.float32 and inp["q"].dtype == torch.bfloat16
