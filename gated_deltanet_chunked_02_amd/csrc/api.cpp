@@ -274,7 +274,7 @@ constexpr int kBwdChunk = 64;
 
 struct BwdLayout {
   Layout st;
-  size_t dR, dH, total;
+  size_t dR, dH, order, total;
 };
 
 // Shape part of a backward call: the forward's checks with the chunk set to 64 and N as the
@@ -294,7 +294,7 @@ gdn_status bwd_problem(const gdn_desc* d, bool packed, gdn::Problem* p) {
   return GDN_OK;
 }
 
-BwdLayout bwd_layout(const gdn::Problem& p) {
+BwdLayout bwd_layout(const gdn::Problem& p, bool dense) {
   BwdLayout L;
   staged_layout(p, &L.st);
   // A stays on chip (stages 3 and 4 run as one launch), and with the fused recompute (bf16)
@@ -310,7 +310,9 @@ BwdLayout bwd_layout(const gdn::Problem& p) {
   const size_t e = p.f32 ? 4 : 2;
   L.dR = L.st.total;
   L.dH = L.dR + align_up((size_t)p.Ttot * p.H * p.D * e);
-  L.total = L.dH + align_up((size_t)p.max_chunks * p.H * p.D * p.D * e);
+  // a packed batch's longest-first order, for the two passes over whole sequences
+  L.order = L.dH + align_up((size_t)p.max_chunks * p.H * p.D * p.D * e);
+  L.total = L.order + (lpt_wanted(p, dense) ? lpt_bytes(p) : 0);
   return L;
 }
 
@@ -349,7 +351,7 @@ BwdSegLayout bwd_seg_layout(const gdn::Problem& p, const SegPlan& sp, size_t bas
 
 // Workspace of a backward call for one reading of the descriptor (dense or packed).
 size_t bwd_workspace_for(const gdn_desc* d, const gdn::Problem& p, bool dense) {
-  const BwdLayout L = bwd_layout(p);
+  const BwdLayout L = bwd_layout(p, dense);
   const SegPlan sp = bwd_seg_plan(d, p, dense);
   return sp.use ? bwd_seg_layout(p, sp, L.total).total : L.total;
 }
@@ -646,7 +648,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
     return gdn::launch_recurrent(pp, stream) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   }
   const bool dense = cu_seqlens == nullptr;
-  const BwdLayout L = bwd_layout(p);
+  const BwdLayout L = bwd_layout(p, dense);
   const SegPlan sp = bwd_seg_plan(d, p, dense);
   if (d->variant == GDN_VARIANT_SEGMENTED && !sp.use) return GDN_ERR_UNSUPPORTED;
   const BwdSegLayout SL = bwd_seg_layout(p, sp, L.total);
@@ -728,11 +730,19 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
     if (e == hipSuccess) e = gdn::launch_bwd_chunk(p, b, stream);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
   }
+  // a packed batch runs its sequences longest first in the passes over whole sequences
+  if (lpt_wanted(p, dense)) {
+    int32_t* order = reinterpret_cast<int32_t*>(ws + L.order);
+    e = gdn::launch_lpt_order(p.cu, order, p.N, p.T, p.Ttot, stream);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    b.order = order;
+  }
   if (gdn::fused_supported(p)) {
     // stages 0-4 (chunk table, Gc, T), then h_c and v_new from the fused kernel
     e = gdn::launch_staged(p, b.st, 4, stream, true);
     if (e == hipSuccess) {
       gdn::Problem pf = p;
+      pf.order = b.order;
       pf.fused_flags = gdn::kFusedNoOutput;
       pf.seq_chunks = b.st.seq_chunks;
       pf.hc_out = b.st.h_c;

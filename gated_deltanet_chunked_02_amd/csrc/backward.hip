@@ -263,12 +263,22 @@ __global__ __launch_bounds__((dh_threads<D, CB>()), (dh_double<CB>() ? 1 : 2)) v
     const TI* __restrict__ q, const TI* __restrict__ k, const TI* __restrict__ Tinv,
     const void* __restrict__ beta, int beta_f32, const TI* __restrict__ dO,
     const float* __restrict__ g_t, const float* __restrict__ dht, TI* __restrict__ dH,
-    TI* __restrict__ dRo, float* __restrict__ dh0, int Ttot, int H, int Hg, float scale) {
+    TI* __restrict__ dRo, float* __restrict__ dh0, const int32_t* __restrict__ order, int Ttot,
+    int H, int Hg, float scale) {
   constexpr int C = kBC, NDK = D / 16, NT = C / 16, NW = D / (16 * CB);
   constexpr int NTH = dh_threads<D, CB>();
   constexpr bool DBUF = dh_double<CB>();
   constexpr int LDD = D + pad_of<TI>(), LDC = C + pad_of<TI>();
-  const int n = blockIdx.x, h = blockIdx.y, hk = h / (H / Hg);
+  // the run and head: with a longest-first order, workgroup rank (in launch order, heads
+  // innermost) r takes run order[r / H], so the longest runs start first and the grid ends
+  // with short ones; else run blockIdx.x, head blockIdx.y
+  int n = blockIdx.x, h = blockIdx.y;
+  if (order) {
+    const int lin = (int)(blockIdx.x + blockIdx.y * gridDim.x);
+    n = order[lin / H];
+    h = lin % H;
+  }
+  const int hk = h / (H / Hg);
   const int w = wave_id(), l = lane_id();
   extern __shared__ __align__(16) char smem[];
   TI* sPt = reinterpret_cast<TI*>(smem + (DBUF ? 2 : 1) * dh_buf_bytes<TI, D>());  // P^T
@@ -973,21 +983,21 @@ hipError_t set_lds(F f, size_t bytes) {
 template <typename TI, int D, int CB>
 hipError_t run_bwd_dh_cb(const Problem& p, const BwdBuffers& b, int runs,
                          const int32_t* run_chunks, const float* dht, void* dH, void* dR,
-                         float* dh0, hipStream_t st) {
+                         float* dh0, hipStream_t st, const int32_t* order) {
   const size_t sm1 = dh_smem<TI, D, CB>();
   GDN_BTRY(set_lds(k_bwd_dh<TI, D, CB>, sm1));
   k_bwd_dh<TI, D, CB><<<dim3(runs, p.H), dh_threads<D, CB>(), sm1, st>>>(
       b.st.table, run_chunks, static_cast<const TI*>(p.q), static_cast<const TI*>(p.k),
       static_cast<const TI*>(b.st.Tinv), p.beta, p.beta_f32 ? 1 : 0,
       static_cast<const TI*>(b.dO), b.st.g_t, dht, static_cast<TI*>(dH), static_cast<TI*>(dR),
-      dh0, p.Ttot, p.H, p.Hg, p.scale);
+      dh0, order, p.Ttot, p.H, p.Hg, p.scale);
   return hipGetLastError();
 }
 
 template <typename TI, int D>
 hipError_t run_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
                       const int32_t* run_chunks, const float* dht, void* dH, void* dR,
-                      float* dh0, hipStream_t st) {
+                      float* dh0, hipStream_t st, const int32_t* order) {
   if (runs <= 0) return hipSuccess;
   if constexpr (sizeof(TI) == 2 && D == 128) {
     // two workgroups per CU pay off once the pairs outnumber the CUs several times over
@@ -996,9 +1006,9 @@ hipError_t run_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
     GDN_BTRY(hipGetDevice(&dev));
     GDN_BTRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     if ((long)runs * p.H >= 8L * (cus > 0 ? cus : 1))
-      return run_bwd_dh_cb<TI, D, 2>(p, b, runs, run_chunks, dht, dH, dR, dh0, st);
+      return run_bwd_dh_cb<TI, D, 2>(p, b, runs, run_chunks, dht, dH, dR, dh0, st, order);
   }
-  return run_bwd_dh_cb<TI, D, 1>(p, b, runs, run_chunks, dht, dH, dR, dh0, st);
+  return run_bwd_dh_cb<TI, D, 1>(p, b, runs, run_chunks, dht, dH, dR, dh0, st, order);
 }
 
 template <typename TI, int D>
@@ -1043,10 +1053,11 @@ bool bwd_supported(const Problem& p) {
 
 hipError_t launch_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
                          const int32_t* run_chunks, const float* dht, void* dH, void* dR,
-                         float* dh0, hipStream_t st) {
-  if (p.f32) return run_bwd_dh<float, 64>(p, b, runs, run_chunks, dht, dH, dR, dh0, st);
-  return p.D == 64 ? run_bwd_dh<bf16, 64>(p, b, runs, run_chunks, dht, dH, dR, dh0, st)
-                   : run_bwd_dh<bf16, 128>(p, b, runs, run_chunks, dht, dH, dR, dh0, st);
+                         float* dh0, hipStream_t st, const int32_t* order) {
+  if (p.f32) return run_bwd_dh<float, 64>(p, b, runs, run_chunks, dht, dH, dR, dh0, st, order);
+  return p.D == 64
+             ? run_bwd_dh<bf16, 64>(p, b, runs, run_chunks, dht, dH, dR, dh0, st, order)
+             : run_bwd_dh<bf16, 128>(p, b, runs, run_chunks, dht, dH, dR, dh0, st, order);
 }
 
 hipError_t launch_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st) {
@@ -1055,7 +1066,7 @@ hipError_t launch_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t s
 }
 
 hipError_t launch_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st) {
-  GDN_BTRY(launch_bwd_dh(p, b, p.N, b.st.seq_chunks, b.dht, b.dH, b.dR, b.dh0, st));
+  GDN_BTRY(launch_bwd_dh(p, b, p.N, b.st.seq_chunks, b.dht, b.dH, b.dR, b.dh0, st, b.order));
   return launch_bwd_chunk(p, b, st);
 }
 

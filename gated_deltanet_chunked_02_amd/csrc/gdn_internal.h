@@ -83,6 +83,7 @@ struct BwdBuffers {
   float* dh0;
   void* dR;
   void* dH;
+  const int32_t* order = nullptr;  // a packed batch's longest-first order, or null
 };
 bool bwd_supported(const Problem& p);
 // Both backward kernels over the sequences (b.dht, b.dH, b.dR, b.dh0 as above).
@@ -91,9 +92,11 @@ hipError_t launch_bwd(const Problem& p, const BwdBuffers& b, hipStream_t st);
 // them): run i covers chunks run_chunks[i] .. run_chunks[i + 1] - 1 of the chunk table and
 // starts from dht[i] ([runs, H, D, D] fp32; zero when null); dh0[i] receives the gradient
 // at its start (not written when null); dH and dR as above, not written when dH is null.
+// With `order` (runs are a packed batch's sequences; order[rank] = sequence, longest first),
+// the workgroups take the runs longest first, heads innermost.
 hipError_t launch_bwd_dh(const Problem& p, const BwdBuffers& b, int runs,
                          const int32_t* run_chunks, const float* dht, void* dH, void* dR,
-                         float* dh0, hipStream_t st);
+                         float* dh0, hipStream_t st, const int32_t* order = nullptr);
 // The chunk-parallel kernel (with grouped heads, one workgroup runs a group's value heads).
 hipError_t launch_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st);
 bool fused_supported(const Problem& p);
