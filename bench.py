@@ -52,9 +52,9 @@ F32_PEAK_TFLOPS = 157.3
 # once they differ.
 PMC_TRAFFIC = {
     "workload": "bf16_16x8192_h32_d128_c128",
-    "fetch_kib": 1671612.15, "write_kib": 1081381.53,
+    "fetch_kib": 1672482.65, "write_kib": 1081369.97,
     "fetch_scale": 2.0, "write_scale": 1.0,
-    "sources_sha256": "8036437170e787a9b8b92198e0c0e8aba3efcd0cd35e4c0b40dd575462a0676f",
+    "sources_sha256": "0540c72bb97a55cdb85907811f007a574fe8939fb9744382f924ffba711f1323",
 }
 FUSED_SOURCES = ("fused.hip", "gdn_device.h", "gdn_internal.h")
 
