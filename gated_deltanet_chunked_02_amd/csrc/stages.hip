@@ -329,11 +329,9 @@ __global__ __launch_bounds__(kThreads) void k_solve(const int32_t* table, const 
 
 // The backward's stages 3 and 4 in one launch: A is built in LDS (the split of k_solve's
 // staging: the diagonal blocks in fp32, the rest in the solve's type) and inverted there, so
-// only T leaves the chip.  Same products and roundings as k_kkt followed by k_solve.  Four
-// workgroups per CU (40 KB of LDS each, at most 128 registers: a few bytes per lane spill,
-// and the chunks' load and solve latencies overlap better; 0.71 to 0.64 ms at 16 x 8192).
+// only T leaves the chip.  Same products and roundings as k_kkt followed by k_solve.
 template <typename TI, int D, int C>
-__global__ __launch_bounds__(kThreads, 4) void k_kkt_solve(const int32_t* table, const TI* k,
+__global__ __launch_bounds__(kThreads) void k_kkt_solve(const int32_t* table, const TI* k,
                                                         const float* g_t, const void* beta_t,
                                                         int beta_f32, TI* Tinv, int Ttot,
                                                         int H, int Hg) {
