@@ -24,11 +24,13 @@
 //
 // Two kernels follow the recomputation of the forward's chunk quantities (chunk table, Gc,
 // T, the chunk-start states and v_new in the workspace):
-//   k_bwd_dh     one workgroup per (sequence, head), a wave per 16 state columns: the chunks
-//                in reverse, dh kept in accumulator tiles; writes dh' of every chunk, dR,
-//                and dh0.  Long sequences run it per segment (twice: once from a zero end
-//                gradient for each segment's own share, composed in reverse order across
-//                the segments, then from each segment's true end gradient);
+//   k_bwd_dh     one workgroup per (sequence, head), a wave per 16 state columns (two per
+//                wave, two workgroups per CU, on grids of many pairs): the chunks in
+//                reverse, dh kept in accumulator tiles; writes dh' of every chunk, dR, and
+//                dh0.  A packed batch's sequences run longest first.  Long sequences run it
+//                per segment (twice: once from a zero end gradient for each segment's own
+//                share, composed in reverse order across the segments, then from each
+//                segment's true end gradient);
 //   k_bwd_chunk  one resident workgroup per CU walking the (chunk, head) items: everything
 //                else, in phases that stage their operands in LDS, with the next item's tiles
 //                copied in while the current item's last products run.
