@@ -211,6 +211,7 @@ def conv_bench(args, dev, gdn):
                            dtype=gdn._dtype_code(x), activation=gdn.ACTIVATIONS[w.activation],
                            state_lines=w.lines)
     stream = torch.cuda.current_stream()
+    st0 = None if st is None else st.clone()  # the drawn state lines, for the parity sample
 
     def step():
         rc = gdn.gdn_causal_conv1d_fwd(desc, x, wt, b, st, idx, None, None, y, stream)
@@ -251,7 +252,50 @@ def conv_bench(args, dev, gdn):
                      "launch_ms": avg_ms, "algorithmic_bytes": by},
         "cpu_baseline": None,
     }
+    if args.cpu_budget > 0:
+        # one more call from the drawn state lines, whose y the sample is checked against
+        if st is not None:
+            st.copy_(st0)
+        step()
+        torch.cuda.synchronize()
+        out["cpu_baseline"] = conv_cpu_baseline(w, inp, st0, y, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def conv_cpu_baseline(w, inp, st0, y_gpu, budget_s: float):
+    """The conv oracle (numpy, fp64, one thread) on a bounded sample: every sequence at full
+    length over a slice of the channels (the convolution is depthwise, so channels are
+    independent), doubled until it takes about a third of the budget; scaled by
+    channel-tokens to the whole job.  The sample doubles as a parity check of y."""
+    import oracle
+    from oracle import conv1d
+    C = w.channels
+    x = inp["x"]
+    wt, bias, idx = inp["weight"].cpu().double().numpy(), inp["bias"].cpu().double().numpy(), \
+        (None if inp["cache_indices"] is None else inp["cache_indices"].cpu().numpy())
+    st = None if st0 is None else st0.cpu().double().numpy()
+    nc, took, errs = 8, 0.0, []
+    while True:
+        sl = slice(0, nc)
+        xs = x[:, :, sl].float().cpu().double().numpy()
+        t0 = time.perf_counter()
+        ys, _ = conv1d.causal_conv1d(xs, wt[sl], bias[sl],
+                                     None if st is None else st[:, :, sl], idx,
+                                     activation=w.activation)
+        took = time.perf_counter() - t0
+        yg = y_gpu[:, :, sl].float().cpu().double().numpy()
+        errs = [float(np.linalg.norm(yg - ys) / max(np.linalg.norm(ys), 1e-30))]
+        if took >= budget_s / 3 or nc >= C:
+            break
+        nc = min(C, nc * 2)
+    scale = C / nc
+    return {"value": w.B * w.T / (took * scale), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "all %d sequences at full length over %d of %d channels, fp64 numpy "
+                      "(one thread), %.1f s; scaled by channel-tokens to the whole job"
+                      % (w.B, nc, C, took),
+            "cpu_model": oracle.cpu_model(), "sample_seconds": took,
+            "parity_sampled": {"channels": nc, "y_rel_l2": errs[0]}}
 
 
 def bwd_algorithmic_bytes(inp):
