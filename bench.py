@@ -298,10 +298,10 @@ def conv_cpu_baseline(w, inp, st0, y_gpu, budget_s: float):
             "parity_sampled": {"channels": nc, "y_rel_l2": errs[0]}}
 
 
-def bwd_algorithmic_bytes(inp):
+def bwd_algorithmic_bytes(inp, grad_bytes=4):
     """Bytes a perfect backward moves: the forward's inputs (q, k, v, g, beta, h0) and the
-    upstream gradients (do, dht) read once; dq, dk, dv, dg, dbeta (fp32) and dh0 written
-    once."""
+    upstream gradients (do, dht) read once; dq, dk, dv (grad_bytes each: fp32 or bf16), dg,
+    dbeta (fp32) and dh0 written once."""
     q, v = inp["q"], inp["v"]
     B, T, Hg, Dk = q.shape
     H, Dv = v.shape[2], v.shape[3]
@@ -310,7 +310,7 @@ def bwd_algorithmic_bytes(inp):
     nseq = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
     state = nseq * H * Dk * Dv * 4
     rd = toks * (2 * Hg * Dk + 2 * H * Dv) * el + toks * H * (4 + inp["beta"].element_size())
-    wr = toks * (2 * Hg * Dk + H * Dv) * 4 + toks * H * 8
+    wr = toks * (2 * Hg * Dk + H * Dv) * grad_bytes + toks * H * 8
     if inp["h0"] is not None:
         rd += state
         wr += state
@@ -384,7 +384,12 @@ def bwd_bench(args, dev, gdn, w, inp):
     ws = torch.empty(gdn.gdn_chunk_bwd_workspace_size(desc), device=dev, dtype=torch.uint8)
     desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
     f = dict(device=dev, dtype=torch.float32)
-    dq, dk, dv = torch.empty(q.shape, **f), torch.empty(k.shape, **f), torch.empty(v.shape, **f)
+    gbf = args.grad_dtype == "bf16"
+    if gbf and q.dtype != torch.bfloat16:
+        raise SystemExit("--grad-dtype bf16 needs bf16 inputs")
+    desc.grad_dtype = 1 if gbf else 0
+    fg = dict(device=dev, dtype=torch.bfloat16 if gbf else torch.float32)
+    dq, dk, dv = torch.empty(q.shape, **fg), torch.empty(k.shape, **fg), torch.empty(v.shape, **fg)
     dg, dbeta = torch.empty(g.shape, **f), torch.empty(g.shape, **f)
     dh0 = None if h0 is None else torch.empty(h0.shape, **f)
     stream = torch.cuda.current_stream()
@@ -412,7 +417,7 @@ def bwd_bench(args, dev, gdn, w, inp):
     avg_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
     ms_per_step = 1e3 * t_wall / args.steps
     tokens = q.shape[0] * q.shape[1]
-    by = bwd_algorithmic_bytes(inp)
+    by = bwd_algorithmic_bytes(inp, 2 if gbf else 4)
     gbs = by / (avg_ms * 1e-3) / 1e9
     copy_gbs = copy_rate(dev)
     cpu = None
@@ -432,7 +437,7 @@ def bwd_bench(args, dev, gdn, w, inp):
         "config": {"workload": w.name, "pass": "backward", "B": int(q.shape[0]),
                    "T": int(q.shape[1]), "H": w.H, "Hg": w.Hg, "Dk": w.Dk, "Dv": w.Dv,
                    "C": 64, "h0": h0 is not None, "variant": how,
-                   "parallelism": "single GPU"},
+                   "grad_dtype": "bf16" if gbf else "f32", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "copy_GBps": copy_gbs, "frac_of_copy": gbs / copy_gbs,
@@ -472,6 +477,8 @@ def main():
                          "(gdn_fused_sigmoid_gating_delta_rule) on the workload's tokens")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (gdn_chunk_bwd) on the workload")
+    ap.add_argument("--grad-dtype", default="f32", choices=["f32", "bf16"],
+                    help="--bwd: dtype of dq, dk, dv (bf16 needs bf16 inputs)")
     ap.add_argument("--mode", default="gdn", choices=["gdn", "copy"],
                     help="copy: time a plain 1 GiB device-to-device copy (the reference "
                          "kernel for scaling HBM byte counters)")

@@ -57,7 +57,8 @@ class GdnDesc(ctypes.Structure):
                 ("Dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("beta_dtype", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("stop_after", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("grad_dtype", ctypes.c_int32)]
 
 
 class GdnConvDesc(ctypes.Structure):
@@ -412,15 +413,21 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale=None, initial_state=None,
 
 def chunk_gated_delta_rule_bwd(q, k, v, g, beta, do, dht=None, scale=None,
                                initial_state=None, cu_seqlens=None, workspace=None,
-                               variant="auto"):
+                               variant="auto", grad_dtype=None):
     """Gradients of chunk_gated_delta_rule's inputs on the current stream, given the
     gradient ``do`` of o [B, T, H, Dv] (q's dtype) and ``dht`` of the final state
     [N, H, Dk, Dv] (or None: zero).  Forward inputs as for chunk_gated_delta_rule.
-    Returns fp32 (dq, dk [B, T, Hg, Dk], dv [B, T, H, Dv], dg, dbeta [B, T, H],
-    dh0 [N, H, Dk, Dv] or None when initial_state is None).  ``variant``: "auto" (long
-    sequences run per segment when that pays), "segmented" (always) or any other name (one
-    pass per sequence)."""
+    Returns (dq, dk [B, T, Hg, Dk], dv [B, T, H, Dv] in ``grad_dtype``: torch.float32 by
+    default, or torch.bfloat16 with bf16 inputs; dg, dbeta [B, T, H] and dh0 [N, H, Dk, Dv]
+    in fp32, dh0 None when initial_state is None).  ``variant``: "auto" (long sequences run
+    per segment when that pays), "segmented" (always) or any other name (one pass per
+    sequence)."""
     import torch
+    gdt = torch.float32 if grad_dtype is None else grad_dtype
+    _need(gdt in (torch.float32, torch.bfloat16), TypeError,
+          "grad_dtype must be torch.float32 or torch.bfloat16")
+    _need(gdt == torch.float32 or q.dtype == torch.bfloat16, TypeError,
+          "bf16 gradients need bf16 inputs")
     _validate_gdn(q, k, v, g, beta, initial_state, cu_seqlens, workspace, devices=False)
     _need(isinstance(do, torch.Tensor) and do.dtype == q.dtype, TypeError,
           "do must be a tensor of q's dtype")
@@ -448,8 +455,10 @@ def chunk_gated_delta_rule_bwd(q, k, v, g, beta, do, dht=None, scale=None,
     if scale is None:
         scale = Dk ** -0.5
     f = dict(device=q.device, dtype=torch.float32)
-    dq, dk = torch.empty(q.shape, **f), torch.empty(k.shape, **f)
-    dv = torch.empty(v.shape, **f)
+    fg = dict(device=q.device, dtype=gdt)
+    desc.grad_dtype = 1 if gdt == torch.bfloat16 else 0
+    dq, dk = torch.empty(q.shape, **fg), torch.empty(k.shape, **fg)
+    dv = torch.empty(v.shape, **fg)
     dg, dbeta = torch.empty(B, T, H, **f), torch.empty(B, T, H, **f)
     dh0 = torch.empty(N, H, Dk, Dv, **f) if initial_state is not None else None
     ws_bytes = gdn_chunk_bwd_workspace_size(desc)

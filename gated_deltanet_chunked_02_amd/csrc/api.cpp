@@ -613,11 +613,13 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_desc* d, gdn_status* status) {
 gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const void* v,
                          const float* g, const void* beta, const float* h0,
                          const int32_t* cu_seqlens, float scale, const void* dout,
-                         const float* dht, float* dq, float* dk, float* dv, float* dg,
+                         const float* dht, void* dq, void* dk, void* dv, float* dg,
                          float* dbeta, float* dh0, hipStream_t stream) {
   gdn::Problem p;
   const gdn_status s = bwd_problem(d, cu_seqlens != nullptr, &p);
   if (s != GDN_OK) return s;
+  if (d->grad_dtype != GDN_F32 && d->grad_dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (d->grad_dtype == GDN_BF16 && p.f32) return GDN_ERR_UNSUPPORTED;
   if (p.Ttot > 0 && (!q || !k || !v || !g || !beta || !dout || !dq || !dk || !dv || !dg ||
                      !dbeta))
     return GDN_ERR_INVALID_ARG;
@@ -663,6 +665,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const 
   b.dq = dq;
   b.dk = dk;
   b.dv = dv;
+  b.grad_bf16 = d->grad_dtype == GDN_BF16;
   b.dg = dg;
   b.dbeta = dbeta;
   b.dh0 = dh0;

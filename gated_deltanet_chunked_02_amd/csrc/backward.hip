@@ -514,9 +514,9 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
     const TI* __restrict__ k, const TI* __restrict__ v, const void* __restrict__ beta,
     int beta_f32, const float* __restrict__ g_t, const TI* __restrict__ h_c,
     const TI* __restrict__ v_new, const TI* __restrict__ dR, const TI* __restrict__ dH,
-    const TI* __restrict__ dO, float* __restrict__ dq, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta, int qk_rows,
-    int gsz, int Ttot, int H, int Hg, float scale) {
+    const TI* __restrict__ dO, void* __restrict__ dq, void* __restrict__ dk,
+    void* __restrict__ dv, float* __restrict__ dg, float* __restrict__ dbeta, int qk_rows,
+    int gsz, int Ttot, int H, int Hg, float scale, int grad_bf16) {
   typedef ChunkLds<TI, D> L;
   typedef Mma<TI> MM;
   constexpr int C = kBC, CBW = D / 64, N2 = chunk_threads<TI, D>();  // CBW: column blocks
@@ -644,20 +644,33 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
   Blk<TI, D, D, N2> bd;
   bd.load(dH + hcoff, D, D);  // dh', stored once h is no longer read
   __syncthreads();  // Gc, beta, K, Q, V
-  // dV = diag(beta) dR, from the copied dR
+  // dV = diag(beta) dR, from the copied dR (fp32, or rounded once to bf16)
   for (int i = tid; i < C * PR; i += N2) {
     const int t = i / PR, pc = i % PR;
     if (t < len) {
       typename Blk<TI, C, D, N2>::Vec x;
       x.u = *reinterpret_cast<const uint4*>(sC + t * LDD + pc * VE);
       const float bt = sBeta[t];
-      float* dst = dv + v0 + (long)t * H * D + pc * VE;
+      const long di = v0 + (long)t * H * D + pc * VE;
+      bool done = false;
+      if constexpr (sizeof(TI) == 2) {  // bf16 gradients come with bf16 inputs only
+        if (grad_bf16) {
+          typename Blk<bf16, C, D, N2>::Vec o;
 #pragma unroll
-      for (int q4 = 0; q4 < VE / 4; ++q4) {
-        f32x4 o;
+          for (int e = 0; e < VE; ++e) o.e[e] = (bf16)(bt * (float)x.e[e]);
+          *reinterpret_cast<uint4*>(static_cast<bf16*>(dv) + di) = o.u;
+          done = true;
+        }
+      }
+      if (!done) {
+        float* dst = static_cast<float*>(dv) + di;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = bt * (float)x.e[4 * q4 + e];
-        *reinterpret_cast<f32x4*>(dst + 4 * q4) = o;
+        for (int q4 = 0; q4 < VE / 4; ++q4) {
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = bt * (float)x.e[4 * q4 + e];
+          *reinterpret_cast<f32x4*>(dst + 4 * q4) = o;
+        }
       }
     }
   }
@@ -960,8 +973,13 @@ __global__ __launch_bounds__((chunk_threads<TI, D>())) void k_bwd_chunk(
           const int t = 16 * (RPW * rh + b) + 4 * lg + e;
           if (t < len) {
             const long gi = dq0 + (long)t * qk_rows * D + 16 * (cw + 4 * m) + lc;
-            dq[gi] = aq[b][m][e];
-            dk[gi] = ak[b][m][e];
+            if (grad_bf16) {
+              static_cast<bf16*>(dq)[gi] = (bf16)aq[b][m][e];
+              static_cast<bf16*>(dk)[gi] = (bf16)ak[b][m][e];
+            } else {
+              static_cast<float*>(dq)[gi] = aq[b][m][e];
+              static_cast<float*>(dk)[gi] = ak[b][m][e];
+            }
           }
         }
   }
@@ -1041,7 +1059,7 @@ hipError_t run_bwd_chunk(const Problem& p, const BwdBuffers& b, hipStream_t st) 
         b.st.table, p.max_chunks, q, k, v, p.beta, p.beta_f32 ? 1 : 0, b.st.g_t,
         static_cast<const TI*>(b.st.h_c), static_cast<const TI*>(b.st.v_new),
         static_cast<const TI*>(b.dR), static_cast<const TI*>(b.dH), dO, b.dq, b.dk, b.dv,
-        b.dg, b.dbeta, p.Hg, gsz, p.Ttot, p.H, p.Hg, p.scale);
+        b.dg, b.dbeta, p.Hg, gsz, p.Ttot, p.H, p.Hg, p.scale, b.grad_bf16 ? 1 : 0);
     return hipGetLastError();
   };
   GDN_BTRY(gsz > 1 ? launch(k_bwd_chunk<TI, D, true>) : launch(k_bwd_chunk<TI, D, false>));

@@ -75,15 +75,16 @@ struct BwdBuffers {
   Stages st;
   const void* dO;
   const float* dht;
-  float* dq;
-  float* dk;
-  float* dv;
+  void* dq;  // fp32, or bf16 when grad_bf16
+  void* dk;
+  void* dv;
   float* dg;
   float* dbeta;
   float* dh0;
   void* dR;
   void* dH;
   const int32_t* order = nullptr;  // a packed batch's longest-first order, or null
+  bool grad_bf16 = false;          // dq, dk, dv stored in bf16
 };
 bool bwd_supported(const Problem& p);
 // Both backward kernels over the sequences (b.dht, b.dH, b.dR, b.dh0 as above).

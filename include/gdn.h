@@ -135,6 +135,10 @@ typedef struct gdn_desc {
                          variant's longest-first order (256-byte aligned; may be NULL for
                          fused, see gdn_chunk_fwd_workspace_size)                         */
   size_t workspace_bytes;
+  int32_t grad_dtype; /* gdn_chunk_bwd only: gdn_dtype of dq, dk, dv.  GDN_F32 (0, the
+                         default) or, with bf16 inputs, GDN_BF16 (the gradients rounded
+                         once, at the store; half the bytes written).  Ignored by the
+                         forward entry points.                                            */
 } gdn_desc;
 
 /* Causal depthwise 1-D convolution with a decode state: the step before the gated delta
@@ -262,14 +266,14 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_desc* d, gdn_status* status);
  * to first.  Any other variant keeps one pass per sequence.
  *   dout  [B, T, H, Dv]   qkv_dtype   gradient of o (required)
  *   dht   [N, H, Dk, Dv]  f32         gradient of ht, or NULL (zero)
- *   dq, dk [B, T, Hg, Dk] f32         the q/k heads' gradients (summed over the value heads
- *                                     that share them)
- *   dv    [B, T, H, Dv]   f32
+ *   dq, dk [B, T, Hg, Dk] grad_dtype  the q/k heads' gradients (summed over the value heads
+ *                                     that share them; fp32 sums, rounded once at the store)
+ *   dv    [B, T, H, Dv]   grad_dtype
  *   dg, dbeta [B, T, H]   f32
  *   dh0   [N, H, Dk, Dv]  f32         gradient of h0, or NULL (not written)
  * Inputs, scale, cu_seqlens and their layouts as for gdn_chunk_fwd (h0 NULL = zero state).
- * Supported: bf16 with Dk = Dv in {64, 128}; f32 with Dk = Dv = 64 (else
- * GDN_ERR_UNSUPPORTED).  d->chunk and d->stop_after are ignored.  The workspace
+ * Supported: bf16 with Dk = Dv in {64, 128}; f32 with Dk = Dv = 64; d->grad_dtype GDN_F32, or
+ * GDN_BF16 with bf16 inputs (else GDN_ERR_UNSUPPORTED; another value: GDN_ERR_INVALID_ARG).  d->chunk and d->stop_after are ignored.  The workspace
  * (d->workspace, 256-byte aligned, gdn_chunk_bwd_workspace_size bytes) is required when
  * B*T > 0, else GDN_ERR_WORKSPACE.  Results do not depend on scheduling (no atomics).
  * Pointers are device pointers aligned to 16 bytes (g, beta, dg, dbeta, cu_seqlens: 4 / 2 /
@@ -277,7 +281,7 @@ size_t gdn_chunk_bwd_workspace_size(const gdn_desc* d, gdn_status* status);
 gdn_status gdn_chunk_bwd(const gdn_desc* d, const void* q, const void* k, const void* v,
                          const float* g, const void* beta, const float* h0,
                          const int32_t* cu_seqlens, float scale, const void* dout,
-                         const float* dht, float* dq, float* dk, float* dv, float* dg,
+                         const float* dht, void* dq, void* dk, void* dv, float* dg,
                          float* dbeta, float* dh0, hipStream_t stream);
 
 /* Bytes of device scratch the library holds on each GPU for gdn_chunk_fwd_noalloc. */

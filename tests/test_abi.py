@@ -552,6 +552,10 @@ def test_bwd_rejects_bad_arguments_before_any_launch(lib):
     assert call(desc(workspace=A + 16, workspace_bytes=1 << 40)) == 3  # misaligned
     assert call(desc(B=1, N=0, T=0), cu=A) == 0           # no sequences: nothing to do
     assert call(desc(T=0)) == 0                           # no tokens and no dh0: nothing
+    assert call(desc(grad_dtype=7)) == 1                  # unknown gradient dtype
+    assert call(desc(grad_dtype=1, qkv_dtype=0, beta_dtype=0, Dk=64, Dv=64)) == 2  # bf16
+    # gradients need bf16 inputs; with them they are accepted (and fail on the workspace)
+    assert call(desc(grad_dtype=1)) == 3
 
 
 def test_bwd_binding_validates_its_tensors(lib):
@@ -572,3 +576,14 @@ def test_bwd_binding_validates_its_tensors(lib):
         with pytest.raises(exc):
             gdn.chunk_gated_delta_rule_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["do"],
                                            dht=a["dht"], initial_state=a["initial_state"])
+    # the gradient dtype: fp32 or bf16, bf16 only with bf16 inputs (checked first)
+    a = gdn_args()
+    a.update(do=torch.zeros(1, 8, 4, 64, dtype=bf))
+    with pytest.raises(TypeError):
+        gdn.chunk_gated_delta_rule_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["do"],
+                                       grad_dtype=torch.float16)
+    f32 = {n: (t.float() if isinstance(t, torch.Tensor) and t.dtype == bf else t)
+           for n, t in a.items()}
+    with pytest.raises(TypeError):
+        gdn.chunk_gated_delta_rule_bwd(f32["q"], f32["k"], f32["v"], f32["g"], f32["beta"],
+                                       f32["do"], grad_dtype=torch.bfloat16)

@@ -52,14 +52,14 @@ def oracle_bwd(inp):
                                         cu_seqlens=cu)
 
 
-def run_bwd(inp, variant="auto"):
+def run_bwd(inp, variant="auto", grad_dtype=None):
     from gated_deltanet_chunked_02_amd import chunk_gated_delta_rule_bwd
     dev = torch.device("cuda")
     mv = lambda t: None if t is None else t.to(dev)
     out = chunk_gated_delta_rule_bwd(
         mv(inp["q"]), mv(inp["k"]), mv(inp["v"]), mv(inp["g"]), mv(inp["beta"]),
         mv(inp["do"]), dht=mv(inp["dht"]), scale=inp["scale"], initial_state=mv(inp["h0"]),
-        cu_seqlens=mv(inp["cu_seqlens"]), variant=variant)
+        cu_seqlens=mv(inp["cu_seqlens"]), variant=variant, grad_dtype=grad_dtype)
     torch.cuda.synchronize()
     return out
 
@@ -135,6 +135,23 @@ def test_backward_many_pairs_two_workgroups_per_cu():
         for i in (0, 2):  # dq and dv of the sequence
             e = rel_l2(to64(got[i])[:, s0:s1], ref[i][:, s0:s1])
             assert e <= tol("bf16", NAMES[i]), (n, NAMES[i], e)
+
+
+@pytest.mark.parametrize("lens", [None, [70, 0, 1, 64, 129, 5]])
+def test_backward_bf16_gradients_are_the_fp32_ones_rounded(lens):
+    # bf16 gradients round the kernel's fp32 values once, at the store: dq, dk and dv equal the
+    # fp32 gradients rounded to bf16 bit for bit, dg, dbeta and dh0 stay fp32 and unchanged,
+    # and all of them are within the bf16 tolerance of the oracle
+    inp = draw(B=2 if lens is None else 1, T=200, H=4, Hg=2, D=128, seed=61, lens=lens)
+    g32 = run_bwd(inp)
+    g16 = run_bwd(inp, grad_dtype=torch.bfloat16)
+    for i in (0, 1, 2):
+        assert g16[i].dtype == torch.bfloat16, NAMES[i]
+        assert torch.equal(g16[i], g32[i].to(torch.bfloat16)), NAMES[i]
+    for i in (3, 4, 5):
+        assert g16[i].dtype == torch.float32 and torch.equal(g16[i], g32[i]), NAMES[i]
+    compare(inp, g16, oracle_bwd(inp), "bf16", "bf16 gradients %s" % ("dense" if lens is None
+                                                                       else "varlen"))
 
 
 def test_backward_fp32_beta_with_bf16_inputs():
