@@ -52,9 +52,9 @@ F32_PEAK_TFLOPS = 157.3
 # once they differ.
 PMC_TRAFFIC = {
     "workload": "bf16_16x8192_h32_d128_c128",
-    "fetch_kib": 1671746.60, "write_kib": 1081361.75,
+    "fetch_kib": 1674309.08, "write_kib": 1081386.26,
     "fetch_scale": 2.0, "write_scale": 1.0,
-    "sources_sha256": "02f5a32e1cef1b36d413ea74230c20a93f26871527be0ea29e4e2a73e7ce6fe0",
+    "sources_sha256": "673222c874991f11d0fc932cf4041011c23f5b85bbbc8bd19474f11eb246b52b",
 }
 FUSED_SOURCES = ("fused.hip", "gdn_device.h", "gdn_internal.h")
 

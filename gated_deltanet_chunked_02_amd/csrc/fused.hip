@@ -105,8 +105,13 @@ __device__ __forceinline__ bf16x8 frag_swz(const bf16* m, int row0, int k0, int 
 // group g) as one 16-byte fragment, with the B operand built from the block pair in the
 // order (2p, 2p + 1) for even g and (2p + 1, 2p) for odd g; the transposing K^T reads of
 // the state update touch both 8-byte halves of the swizzled chunks and so every LDS bank.
+// That takes the four chunks of a pair to differ in their low four bits (an LDS bank cycle
+// is 16 chunks of 16 bytes): at D = 256 the far chunk is 8 away, not D/16 = 16 (which fell
+// on the same banks and made every K^T read a two-way conflict), and pairs p >= 4 take the
+// upper 16 chunks, 16 + 2 (p - 4) + a % 2 + 8 (a / 2).
 template <int D>
 __device__ __forceinline__ int kchunk(int p, int a) {
+  if constexpr (D == 256) return 2 * (p & 3) + (a & 1) + 8 * (a >> 1) + 16 * (p >> 2);
   return 2 * p + (a & 1) + (D / 16) * (a >> 1);
 }
 template <int D>
